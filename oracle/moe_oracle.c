@@ -1,0 +1,419 @@
+/*
+ * CPU oracle of the routed-expert MoE layer.
+ *
+ * TEST INFRASTRUCTURE.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  The product path (the
+ * HIP library and its Python binding) never links, imports or calls it, and
+ * this file shares no code, header or table with that path.
+ *
+ * Plain, single-threaded C11, built with -O2 -ffp-contract=off and without
+ * -ffast-math: every floating-point operation below is one IEEE-754 binary32
+ * operation rounded to nearest-even, and every fused multiply-add is an
+ * explicit fmaf().  Where the pages leave an operation order or a rounding
+ * rule open, the reading taken is stated at the function; the layer's output
+ * is then one exactly defined binary32 value per element.
+ *
+ * Sources, by page title and section:
+ *  [README]  colibrì README v1.0 (aihot.virxact.com mirror),
+ *            "What's implemented" and "The idea".
+ *  [ROUTER]  "Colibri (colibrì): GLM-5.2 local inference on 25 GB of RAM"
+ *            (ai-infrastructure.net), "How it works (validated core
+ *            mechanics)": the sigmoid noaux_tc router and its self-test.
+ *  [LAYOUT]  JustVugg/colibri (topgit.dev), the repository layout: the shared
+ *            routed-expert FFN kernel header (SwiGLU experts).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define OQ_OK 0
+#define OQ_EINVAL (-1)
+#define OQ_ENONFINITE (-2)
+#define OQ_ENOTRESIDENT (-4)
+#define OQ_ENOMEM (-6)
+
+/* ------------------------------------------------------------------------
+ * Exponential.  The pages do not say how exp is evaluated.  Reading: a
+ * Cody-Waite range reduction (Cody & Waite, "Software Manual for the
+ * Elementary Functions", 1980) and the degree-7 Taylor polynomial of e^r in
+ * Horner form, every step an explicit binary32 operation, so that any
+ * implementation following the same steps gets the same bits.
+ *   n = rint(x * log2(e));  r = x - n*ln2_hi (exact, one fma);  r -= n*ln2_lo
+ *   p = sum_{k=0..7} r^k / k!  (Horner, fmaf);  result = p * 2^n
+ * Constants come from the mathematics: ln2_hi = RN32(ln 2),
+ * ln2_lo = RN32(ln 2 - ln2_hi), log2e = RN32(1/ln 2), c_k = RN32(1/k!).
+ * Range: e^x rounds to +inf above x = 0x1.62e42ep+6 and to 0 below
+ * x = -0x1.9fe368p+6 (e^x < 2^-150 there).
+ * ---------------------------------------------------------------------- */
+static float pow2i(int n) { /* 2^n for -126 <= n <= 127 */
+    uint32_t bits = (uint32_t)(n + 127) << 23;
+    float f;
+    memcpy(&f, &bits, 4);
+    return f;
+}
+
+float oq_expf(float x) {
+    if (isnan(x)) return x;
+    if (x > 0x1.62e42ep+6f) return INFINITY;
+    if (x < -0x1.9fe368p+6f) return 0.0f;
+    const float log2e = 0x1.715476p+0f;
+    const float ln2_hi = 0x1.62e430p-1f;
+    const float ln2_lo = -0x1.05c610p-29f;
+    const float c2 = (float)(1.0 / 2.0), c3 = (float)(1.0 / 6.0), c4 = (float)(1.0 / 24.0);
+    const float c5 = (float)(1.0 / 120.0), c6 = (float)(1.0 / 720.0), c7 = (float)(1.0 / 5040.0);
+    float t = x * log2e;
+    float fn = rintf(t);
+    float r = fmaf(-fn, ln2_hi, x);
+    r = fmaf(-fn, ln2_lo, r);
+    float p = c7;
+    p = fmaf(p, r, c6);
+    p = fmaf(p, r, c5);
+    p = fmaf(p, r, c4);
+    p = fmaf(p, r, c3);
+    p = fmaf(p, r, c2);
+    p = fmaf(p, r, 1.0f);
+    p = fmaf(p, r, 1.0f);
+    int n = (int)fn;
+    if (n > 127) return (p * pow2i(127)) * pow2i(n - 127);
+    if (n < -126) return (p * pow2i(n + 64)) * pow2i(-64);
+    return p * pow2i(n);
+}
+
+/* Logistic function sigma(v) = 1 / (1 + e^-v), one correctly rounded division. */
+float oq_sigmoid(float v) { return 1.0f / (1.0f + oq_expf(-v)); }
+
+/* SwiGLU gate: silu(g) * u with silu(g) = g / (1 + e^-g)  [LAYOUT: SwiGLU experts].
+ * Reading: the division produces silu(g), which is then multiplied by u. */
+float oq_swiglu(float g, float u) { return (g / (1.0f + oq_expf(-g))) * u; }
+
+/* ------------------------------------------------------------------------
+ * Q8_0 activation quantisation  [README "What's implemented": integer-dot
+ * kernels over Q8_0-style int8 activations].  Blocks of 32 values, one
+ * binary32 scale per block.  The pages name the scheme only; reading (the
+ * usual Q8_0 block rule):
+ *   amax = max_j |v_j|;  d = amax / 127;
+ *   q_j = clamp(round_half_away_from_zero(v_j / d), -127, 127), q = 0 when d == 0.
+ * n must be a multiple of 32.
+ * ---------------------------------------------------------------------- */
+void oq_q8_0(const float *v, int n, int8_t *q, float *d) {
+    for (int b = 0; b < n / 32; ++b) {
+        const float *vb = v + 32 * b;
+        float amax = 0.0f;
+        for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(vb[j]));
+        float db = amax / 127.0f;
+        d[b] = db;
+        for (int j = 0; j < 32; ++j) {
+            float c = 0.0f;
+            if (db != 0.0f) {
+                c = roundf(vb[j] / db);
+                if (c > 127.0f) c = 127.0f;
+                if (c < -127.0f) c = -127.0f;
+            }
+            q[32 * b + j] = (int8_t)c;
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------
+ * Packed weight codes  [README "What's implemented": int8, packed int4 and
+ * packed int2 weights with per-row scales, dequantised on use, the packing
+ * identical to the int8 container].  Byte layout per 32-element block:
+ *   int8: 32 bytes, byte j = code j.
+ *   int4: 16 bytes, byte j = code j (bits 0-3) | code j+16 (bits 4-7).
+ *   int2:  8 bytes, byte j = code j+8i in bits 2i..2i+1, i = 0..3.
+ * Codes are two's complement: int4 in [-8, 7], int2 in [-2, 1].
+ * ---------------------------------------------------------------------- */
+void oq_unpack(const uint8_t *src, int n, int bits, int8_t *out) {
+    for (int b = 0; b < n / 32; ++b) {
+        for (int j = 0; j < 32; ++j) {
+            int v;
+            if (bits == 8) {
+                v = (int8_t)src[32 * b + j];
+            } else if (bits == 4) {
+                int byte = src[16 * b + (j % 16)];
+                int nib = (j < 16) ? (byte & 0xF) : (byte >> 4);
+                v = (nib >= 8) ? nib - 16 : nib;
+            } else {
+                int byte = src[8 * b + (j % 8)];
+                int f = (byte >> (2 * (j / 8))) & 3;
+                v = (f >= 2) ? f - 4 : f;
+            }
+            out[32 * b + j] = (int8_t)v;
+        }
+    }
+}
+
+/* Byte offsets of an expert blob: [gate codes][up codes][down codes]
+ * [gate scales][up scales][down scales], each section 256-byte aligned. */
+static uint64_t al256(uint64_t v) { return (v + 255u) & ~(uint64_t)255u; }
+
+void oq_blob_layout(int H, int I, int bits, uint64_t off[7]) {
+    uint64_t gate = (uint64_t)I * (uint64_t)H * (uint64_t)bits / 8u;
+    uint64_t down = (uint64_t)H * (uint64_t)I * (uint64_t)bits / 8u;
+    off[0] = 0;
+    off[1] = al256(off[0] + gate);
+    off[2] = al256(off[1] + gate);
+    off[3] = al256(off[2] + down);
+    off[4] = al256(off[3] + 4u * (uint64_t)I);
+    off[5] = al256(off[4] + 4u * (uint64_t)I);
+    off[6] = al256(off[5] + 4u * (uint64_t)H);
+}
+
+/* ------------------------------------------------------------------------
+ * Row dot product of an integer weight row with a Q8_0 vector.
+ * isum_b = sum_{j<32} w_{32b+j} * q_{32b+j} exactly in int32 (|isum| <=
+ * 32*128*127).  Reading for the floating-point part (the pages leave it
+ * open): acc = 0; for b ascending: acc = fmaf(d_b, (float)isum_b, acc);
+ * result = acc * row_scale.
+ * ---------------------------------------------------------------------- */
+int32_t oq_block_isum(const int8_t *w, const int8_t *q) {
+    int32_t s = 0;
+    for (int j = 0; j < 32; ++j) s += (int32_t)w[j] * (int32_t)q[j];
+    return s;
+}
+
+float oq_row_dot(const int8_t *w, const int8_t *q, const float *d, int n, float row_scale) {
+    float acc = 0.0f;
+    for (int b = 0; b < n / 32; ++b)
+        acc = fmaf(d[b], (float)oq_block_isum(w + 32 * b, q + 32 * b), acc);
+    return acc * row_scale;
+}
+
+/* ------------------------------------------------------------------------
+ * Router logit  [README "What's implemented" and [ROUTER]: logits of the
+ * hidden state against the router gate].  logit = sum_h x_h * w_h in
+ * binary32.  Reading for the order (the pages leave it open): 64 partial
+ * sums; partial l owns the elements h = 256j + 4l + c (j ascending, then
+ * c = 0..3) and accumulates them with fmaf from 0; then six rounds
+ * p_l <- p_l + p_{l xor o} for o = 32, 16, 8, 4, 2, 1; the logit is p_0.
+ * H must be a multiple of 256.
+ * ---------------------------------------------------------------------- */
+float oq_router_logit(const float *x, const float *w, int H) {
+    float p[64], t[64];
+    for (int l = 0; l < 64; ++l) {
+        float a = 0.0f;
+        for (int j = 0; j < H / 256; ++j)
+            for (int c = 0; c < 4; ++c) {
+                int h = 256 * j + 4 * l + c;
+                a = fmaf(x[h], w[h], a);
+            }
+        p[l] = a;
+    }
+    for (int o = 32; o >= 1; o >>= 1) {
+        for (int l = 0; l < 64; ++l) t[l] = p[l] + p[l ^ o];
+        memcpy(p, t, sizeof p);
+    }
+    return p[0];
+}
+
+/* ------------------------------------------------------------------------
+ * Selection and gate weights  [ROUTER]: the selection score is
+ * sigmoid(logit) + bias, the bias ranks experts only; the top K are ordered
+ * by (score descending, expert id ascending), so the lower id wins a tie;
+ * the combination weights are the unbiased sigmoids of the selected experts
+ * divided by their sum; routed_scaling_factor multiplies them afterwards
+ * ([README]: DeepSeek-V3-style sigmoid router with routed_scaling_factor).
+ * Readings: the sum runs over the K selected in rank order starting from
+ * the first; no epsilon is added; w_k = (sig_k / sum) * rsf; with
+ * norm == 0, w_k = sig_k * rsf.  Non-finite input is rejected [ROUTER].
+ * ---------------------------------------------------------------------- */
+int oq_select(const float *logit, const float *bias, int E, int K, float rsf, int norm,
+              int32_t *idx, float *w, float *sig_out) {
+    if (E <= 0 || K < 1 || K > E) return OQ_EINVAL;
+    float *sig = (float *)malloc(sizeof(float) * (size_t)E);
+    float *score = (float *)malloc(sizeof(float) * (size_t)E);
+    char *taken = (char *)calloc((size_t)E, 1);
+    if (!sig || !score || !taken) { free(sig); free(score); free(taken); return OQ_ENOMEM; }
+    int rc = OQ_OK;
+    for (int e = 0; e < E; ++e) {
+        float b = bias ? bias[e] : 0.0f;
+        if (!isfinite(logit[e]) || !isfinite(b)) rc = OQ_ENONFINITE;
+        sig[e] = oq_sigmoid(logit[e]);
+        score[e] = sig[e] + b;
+        if (sig_out) sig_out[e] = sig[e];
+    }
+    if (rc == OQ_OK) {
+        for (int k = 0; k < K; ++k) {
+            int best = -1;
+            for (int e = 0; e < E; ++e) {
+                if (taken[e]) continue;
+                if (best < 0 || score[e] > score[best]) best = e;
+            }
+            taken[best] = 1;
+            idx[k] = best;
+        }
+        if (norm) {
+            float denom = sig[idx[0]];
+            for (int k = 1; k < K; ++k) denom = denom + sig[idx[k]];
+            if (!(denom > 0.0f)) rc = OQ_ENONFINITE;
+            for (int k = 0; k < K; ++k) w[k] = (sig[idx[k]] / denom) * rsf;
+        } else {
+            for (int k = 0; k < K; ++k) w[k] = sig[idx[k]] * rsf;
+        }
+    }
+    free(sig);
+    free(score);
+    free(taken);
+    return rc;
+}
+
+/* ------------------------------------------------------------------------
+ * One SwiGLU expert on one token  [LAYOUT: routed-expert SwiGLU FFN;
+ * README: integer dots over Q8_0 activations, per-row scales].
+ *   g_i = row_dot(gate_i, qx, dx) , u_i = row_dot(up_i, qx, dx)   (i < I)
+ *   h_i = swiglu(g_i, u_i);  (qh, dh) = Q8_0(h)
+ *   y_r = row_dot(down_r, qh, dh)                                  (r < H)
+ * Reading: the down projection consumes Q8_0(h) like every other integer
+ * dot in the layer.  Optional debug outputs may be NULL.
+ * ---------------------------------------------------------------------- */
+int oq_expert(const uint8_t *blob, int H, int I, int bits, const int8_t *qx, const float *dx,
+              float *y, float *g_out, float *u_out, float *h_out, int8_t *qh_out, float *dh_out) {
+    uint64_t off[7];
+    oq_blob_layout(H, I, bits, off);
+    int n = H > I ? H : I;
+    int8_t *row = (int8_t *)malloc((size_t)n);
+    float *g = (float *)malloc(sizeof(float) * (size_t)I);
+    float *u = (float *)malloc(sizeof(float) * (size_t)I);
+    float *h = (float *)malloc(sizeof(float) * (size_t)I);
+    int8_t *qh = (int8_t *)malloc((size_t)I);
+    float *dh = (float *)malloc(sizeof(float) * (size_t)(I / 32));
+    if (!row || !g || !u || !h || !qh || !dh) {
+        free(row); free(g); free(u); free(h); free(qh); free(dh);
+        return OQ_ENOMEM;
+    }
+    const float *s_g = (const float *)(blob + off[3]);
+    const float *s_u = (const float *)(blob + off[4]);
+    const float *s_d = (const float *)(blob + off[5]);
+    uint64_t hrow = (uint64_t)H * (uint64_t)bits / 8u, irow = (uint64_t)I * (uint64_t)bits / 8u;
+    for (int i = 0; i < I; ++i) {
+        oq_unpack(blob + off[0] + (uint64_t)i * hrow, H, bits, row);
+        g[i] = oq_row_dot(row, qx, dx, H, s_g[i]);
+        oq_unpack(blob + off[1] + (uint64_t)i * hrow, H, bits, row);
+        u[i] = oq_row_dot(row, qx, dx, H, s_u[i]);
+        h[i] = oq_swiglu(g[i], u[i]);
+    }
+    oq_q8_0(h, I, qh, dh);
+    for (int r = 0; r < H; ++r) {
+        oq_unpack(blob + off[2] + (uint64_t)r * irow, I, bits, row);
+        y[r] = oq_row_dot(row, qh, dh, I, s_d[r]);
+    }
+    if (g_out) memcpy(g_out, g, sizeof(float) * (size_t)I);
+    if (u_out) memcpy(u_out, u, sizeof(float) * (size_t)I);
+    if (h_out) memcpy(h_out, h, sizeof(float) * (size_t)I);
+    if (qh_out) memcpy(qh_out, qh, (size_t)I);
+    if (dh_out) memcpy(dh_out, dh, sizeof(float) * (size_t)(I / 32));
+    free(row); free(g); free(u); free(h); free(qh); free(dh);
+    return OQ_OK;
+}
+
+static int dims_ok(int H, int I, int E, int K, int n_shared, int bits) {
+    if (H <= 0 || I <= 0 || H % 256 != 0 || I % 32 != 0) return 0;
+    if (E <= 0 || K < 1 || K > E) return 0;
+    if (n_shared != 0 && n_shared != 1) return 0;
+    if (bits != 8 && bits != 4 && bits != 2) return 0;
+    return 1;
+}
+
+static int all_finite(const float *v, size_t n) {
+    for (size_t i = 0; i < n; ++i)
+        if (!isfinite(v[i])) return 0;
+    return 1;
+}
+
+/* ------------------------------------------------------------------------
+ * Routing of S tokens: logits, selection and weights (see above).
+ * logits_out / sig_out ([S,E]) may be NULL.
+ * ---------------------------------------------------------------------- */
+int oq_moe_route(int H, int E, int K, float rsf, int norm, int S, const float *x,
+                 const float *router_w, const float *bias, int32_t *idx, float *w,
+                 float *logits_out, float *sig_out) {
+    if (H <= 0 || H % 256 != 0 || E <= 0 || K < 1 || K > E || S < 0) return OQ_EINVAL;
+    if (!all_finite(x, (size_t)S * (size_t)H) || !all_finite(router_w, (size_t)E * (size_t)H) ||
+        (bias && !all_finite(bias, (size_t)E)))
+        return OQ_ENONFINITE;
+    float *lg = (float *)malloc(sizeof(float) * (size_t)E);
+    if (!lg) return OQ_ENOMEM;
+    int rc = OQ_OK;
+    for (int t = 0; t < S && rc == OQ_OK; ++t) {
+        for (int e = 0; e < E; ++e)
+            lg[e] = oq_router_logit(x + (size_t)t * H, router_w + (size_t)e * H, H);
+        if (logits_out) memcpy(logits_out + (size_t)t * E, lg, sizeof(float) * (size_t)E);
+        rc = oq_select(lg, bias, E, K, rsf, norm, idx + (size_t)t * K, w + (size_t)t * K,
+                       sig_out ? sig_out + (size_t)t * E : NULL);
+    }
+    free(lg);
+    return rc;
+}
+
+/* ------------------------------------------------------------------------
+ * Expert FFNs and combine for S tokens with given routing.
+ *   out[t,r] = (fmaf chain over k in rank order of w[t,k] * y_{idx[t,k]}[r],
+ *               starting from 0) + y_shared[r]
+ * [README "What's implemented": DeepSeek-V3-style router with a shared
+ * expert; [ROUTER]: gate-weighted sum over the selected experts].  Readings:
+ * the shared expert has the routed experts' format and weight 1 and is added
+ * after the routed sum; without a shared expert out is the routed sum.
+ * blobs[e] == NULL marks expert e as not resident.
+ * ---------------------------------------------------------------------- */
+int oq_moe_forward(int H, int I, int E, int K, int n_shared, int bits, int S, const float *x,
+                   const int32_t *idx, const float *w, const uint8_t *const *blobs,
+                   const uint8_t *shared_blob, float *out) {
+    if (!dims_ok(H, I, E, K, n_shared, bits) || S < 0) return OQ_EINVAL;
+    if (n_shared && !shared_blob) return OQ_ENOTRESIDENT;
+    if (!all_finite(x, (size_t)S * (size_t)H) || !all_finite(w, (size_t)S * (size_t)K))
+        return OQ_ENONFINITE;
+    for (int t = 0; t < S; ++t)
+        for (int k = 0; k < K; ++k) {
+            int32_t e = idx[(size_t)t * K + k];
+            if (e < 0 || e >= E) return OQ_EINVAL;
+            for (int k2 = 0; k2 < k; ++k2)
+                if (idx[(size_t)t * K + k2] == e) return OQ_EINVAL;
+            if (!blobs[e]) return OQ_ENOTRESIDENT;
+        }
+    int8_t *qx = (int8_t *)malloc((size_t)H);
+    float *dx = (float *)malloc(sizeof(float) * (size_t)(H / 32));
+    float *y = (float *)malloc(sizeof(float) * (size_t)H * (size_t)K);
+    float *ysh = (float *)malloc(sizeof(float) * (size_t)H);
+    if (!qx || !dx || !y || !ysh) { free(qx); free(dx); free(y); free(ysh); return OQ_ENOMEM; }
+    int rc = OQ_OK;
+    for (int t = 0; t < S && rc == OQ_OK; ++t) {
+        oq_q8_0(x + (size_t)t * H, H, qx, dx);
+        for (int k = 0; k < K && rc == OQ_OK; ++k)
+            rc = oq_expert(blobs[idx[(size_t)t * K + k]], H, I, bits, qx, dx, y + (size_t)k * H,
+                           NULL, NULL, NULL, NULL, NULL);
+        if (rc == OQ_OK && n_shared)
+            rc = oq_expert(shared_blob, H, I, bits, qx, dx, ysh, NULL, NULL, NULL, NULL, NULL);
+        for (int r = 0; r < H && rc == OQ_OK; ++r) {
+            float acc = 0.0f;
+            for (int k = 0; k < K; ++k) acc = fmaf(w[(size_t)t * K + k], y[(size_t)k * H + r], acc);
+            out[(size_t)t * H + r] = n_shared ? acc + ysh[r] : acc;
+        }
+    }
+    free(qx); free(dx); free(y); free(ysh);
+    return rc;
+}
+
+/* Whole layer: routing then forward. */
+int oq_moe_layer(int H, int I, int E, int K, int n_shared, int bits, float rsf, int norm, int S,
+                 const float *x, const float *router_w, const float *bias,
+                 const uint8_t *const *blobs, const uint8_t *shared_blob, float *out,
+                 int32_t *idx, float *w) {
+    if (!dims_ok(H, I, E, K, n_shared, bits)) return OQ_EINVAL;
+    int rc = oq_moe_route(H, E, K, rsf, norm, S, x, router_w, bias, idx, w, NULL, NULL);
+    if (rc != OQ_OK) return rc;
+    return oq_moe_forward(H, I, E, K, n_shared, bits, S, x, idx, w, blobs, shared_blob, out);
+}
+
+/* Element-wise batch forms of the scalar functions above (for sweeps). */
+void oq_expf_n(const float *x, float *y, uint64_t n) {
+    for (uint64_t i = 0; i < n; ++i) y[i] = oq_expf(x[i]);
+}
+
+void oq_sigmoid_n(const float *x, float *y, uint64_t n) {
+    for (uint64_t i = 0; i < n; ++i) y[i] = oq_sigmoid(x[i]);
+}
+
+void oq_swiglu_n(const float *g, const float *u, float *h, uint64_t n) {
+    for (uint64_t i = 0; i < n; ++i) h[i] = oq_swiglu(g[i], u[i]);
+}

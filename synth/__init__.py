@@ -1,0 +1,361 @@
+"""Seeded synthetic inputs for the routed-expert MoE layer.
+
+This module only produces input bytes: hidden states, the router gate and
+bias, and expert weight blobs in the packed layout.  It holds none of the
+layer's own arithmetic (no activation quantisation, no routing, no expert
+FFN, no combine); the CPU oracle and the HIP library each consume exactly the
+bytes written here.  Routing-shaping constructions use only library linear
+algebra and sorting on target logits, never the layer's router.
+
+Random numbers come from SplitMix64 (Steele, Lea & Flood, OOPSLA 2014) used
+as a counter-based generator: value i of stream `key` is
+mix64(key + (i + 1) * GAMMA), and keys are derived by folding
+(seed, kind, indices...) through mix64.  The C helper `gen.c` implements the
+same stream for the large blobs.
+
+Two weight recipes:
+  * gaussian: w ~ N(0, sigma) per element (Box-Muller on the stream), then
+    the offline per-row quantiser (amax / qmax scale, round half away from
+    zero, clamp).  Used for small layers, where it is cheap.
+  * cdf: codes drawn i.i.d. from the distribution of that quantised Gaussian
+    (a 65536-entry inverse-CDF table with a nominal amax of 4 sigma), with a
+    per-row scale jittered +-5% around the nominal one.  Used for
+    GLM-5.2-shaped layers, where tens of gigabytes must be written quickly.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import math
+import os
+import subprocess
+
+import numpy as np
+
+GAMMA = 0x9E3779B97F4A7C15
+MASK64 = (1 << 64) - 1
+
+# stream kinds
+K_X = 1
+K_ROUTER_W = 2
+K_ROUTER_BIAS = 3
+K_WEIGHT = 4
+K_ROUTING = 5
+
+QRANGE = {8: (-127, 127), 4: (-7, 7), 2: (-2, 1)}
+QMAX = {8: 127, 4: 7, 2: 2}
+
+
+# --------------------------------------------------------------------------
+# counter-based random streams
+# --------------------------------------------------------------------------
+def _mix64_int(z: int) -> int:
+    z &= MASK64
+    z = ((z ^ (z >> 30)) * 0xBF58476D1CE4E5B9) & MASK64
+    z = ((z ^ (z >> 27)) * 0x94D049BB133111EB) & MASK64
+    return z ^ (z >> 31)
+
+
+def _mix64(z: np.ndarray) -> np.ndarray:
+    z = z.astype(np.uint64, copy=True)
+    z ^= z >> np.uint64(30)
+    z *= np.uint64(0xBF58476D1CE4E5B9)
+    z ^= z >> np.uint64(27)
+    z *= np.uint64(0x94D049BB133111EB)
+    z ^= z >> np.uint64(31)
+    return z
+
+
+def stream_key(seed: int, *parts: int) -> int:
+    """Folds (seed, parts...) into one 64-bit stream key."""
+    k = _mix64_int(seed + GAMMA)
+    for p in parts:
+        k = _mix64_int(k ^ _mix64_int((p & MASK64) + GAMMA))
+    return k
+
+
+def uniform_u64(key: int, n: int, offset: int = 0) -> np.ndarray:
+    """Values offset..offset+n-1 of the stream `key` as uint64."""
+    i = np.arange(offset + 1, offset + n + 1, dtype=np.uint64)
+    with np.errstate(over="ignore"):
+        z = np.uint64(key) + i * np.uint64(GAMMA)
+    return _mix64(z)
+
+
+def uniform01(key: int, n: int, offset: int = 0) -> np.ndarray:
+    """Uniform doubles in [0, 1) with 53 random bits."""
+    return (uniform_u64(key, n, offset) >> np.uint64(11)).astype(np.float64) * 2.0**-53
+
+
+def normal(key: int, n: int) -> np.ndarray:
+    """n standard normals (f64); value i uses stream values 2i and 2i+1."""
+    r = uniform_u64(key, 2 * n).reshape(n, 2)
+    u1 = ((r[:, 0] >> np.uint64(11)).astype(np.float64) + 0.5) * 2.0**-53
+    u2 = (r[:, 1] >> np.uint64(11)).astype(np.float64) * 2.0**-53
+    return np.sqrt(-2.0 * np.log(u1)) * np.cos(2.0 * math.pi * u2)
+
+
+# --------------------------------------------------------------------------
+# layer shapes
+# --------------------------------------------------------------------------
+@dataclasses.dataclass(frozen=True)
+class LayerSpec:
+    hidden: int
+    inter: int
+    n_experts: int
+    top_k: int
+    n_shared: int
+    wbits: int
+    routed_scaling_factor: float = 2.5
+    norm_topk_prob: int = 1
+
+    @property
+    def blob_bytes(self) -> int:
+        return blob_layout(self.hidden, self.inter, self.wbits)["total"]
+
+
+TINY = LayerSpec(hidden=256, inter=128, n_experts=16, top_k=2, n_shared=1, wbits=4)
+GLM = LayerSpec(hidden=6144, inter=2048, n_experts=256, top_k=8, n_shared=1, wbits=4)
+GLM_INT8 = dataclasses.replace(GLM, wbits=8)
+GLM_INT2 = dataclasses.replace(GLM, wbits=2)
+
+
+def blob_layout(hidden: int, inter: int, bits: int) -> dict:
+    """Byte offsets of the six sections of one expert blob.
+
+    [gate codes: inter rows x hidden*bits/8][up codes: same][down codes:
+    hidden rows x inter*bits/8][gate scales f32 x inter][up scales f32 x
+    inter][down scales f32 x hidden]; every section starts on a 256-byte
+    boundary and the total is rounded up to 256 bytes.
+    """
+    a = lambda n: (n + 255) // 256 * 256  # noqa: E731
+    gate = inter * hidden * bits // 8
+    down = hidden * inter * bits // 8
+    off = {"gate": 0}
+    off["up"] = a(gate)
+    off["down"] = a(off["up"] + gate)
+    off["s_gate"] = a(off["down"] + down)
+    off["s_up"] = a(off["s_gate"] + 4 * inter)
+    off["s_down"] = a(off["s_up"] + 4 * inter)
+    off["total"] = a(off["s_down"] + 4 * hidden)
+    return off
+
+
+# --------------------------------------------------------------------------
+# offline weight quantiser and packer (data preparation, not the layer)
+# --------------------------------------------------------------------------
+def _round_half_away(v: np.ndarray) -> np.ndarray:
+    return np.sign(v) * np.floor(np.abs(v) + 0.5)
+
+
+def quantize_rows(w: np.ndarray, bits: int) -> tuple[np.ndarray, np.ndarray]:
+    """Per-row symmetric quantiser: scale = amax/qmax, code = clamp(round(w/scale))."""
+    lo, hi = QRANGE[bits]
+    w = np.asarray(w, dtype=np.float64)
+    amax = np.max(np.abs(w), axis=1)
+    s = (amax / QMAX[bits]).astype(np.float32)
+    s64 = s.astype(np.float64)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = np.where(s64[:, None] > 0, _round_half_away(w / s64[:, None]), 0.0)
+    q = np.clip(q, lo, hi).astype(np.int8)
+    return q, s
+
+
+def pack_codes(codes: np.ndarray, bits: int) -> np.ndarray:
+    """Packs signed codes [rows, cols] into the blob byte layout.
+
+    Per 32-element block: int8 -> 32 bytes as is; int4 -> 16 bytes, byte j
+    holds element j in bits 0-3 and element j+16 in bits 4-7; int2 -> 8
+    bytes, byte j holds element j+8i in bits 2i..2i+1 (i = 0..3).  Codes are
+    stored in two's complement.
+    """
+    codes = np.asarray(codes, dtype=np.int8)
+    rows, cols = codes.shape
+    assert cols % 32 == 0
+    blk = codes.reshape(rows, cols // 32, 32).view(np.uint8)
+    if bits == 8:
+        return blk.reshape(rows, cols).copy()
+    if bits == 4:
+        lo = blk[:, :, :16] & 0x0F
+        hi = (blk[:, :, 16:] & 0x0F) << 4
+        return (lo | hi).astype(np.uint8).reshape(rows, cols // 2)
+    if bits == 2:
+        out = np.zeros((rows, cols // 32, 8), dtype=np.uint8)
+        for i in range(4):
+            out |= ((blk[:, :, 8 * i:8 * i + 8] & 0x03) << (2 * i)).astype(np.uint8)
+        return out.reshape(rows, cols // 4)
+    raise ValueError(bits)
+
+
+def assemble_blob(hidden, inter, bits, gate_codes, up_codes, down_codes, s_gate, s_up, s_down):
+    lay = blob_layout(hidden, inter, bits)
+    blob = np.zeros(lay["total"], dtype=np.uint8)
+
+    def put(name, arr):
+        b = np.ascontiguousarray(arr).view(np.uint8).ravel()
+        blob[lay[name]:lay[name] + b.size] = b
+
+    put("gate", pack_codes(gate_codes, bits))
+    put("up", pack_codes(up_codes, bits))
+    put("down", pack_codes(down_codes, bits))
+    put("s_gate", np.asarray(s_gate, np.float32))
+    put("s_up", np.asarray(s_up, np.float32))
+    put("s_down", np.asarray(s_down, np.float32))
+    return blob
+
+
+def gaussian_expert(seed: int, layer: int, expert: int, spec: LayerSpec, sigma: float = 0.02):
+    """Expert weights w ~ N(0, sigma), per-row quantised.
+
+    Returns (blob, parts) where parts holds the codes and scales of the
+    three matrices (gate/up [inter, hidden], down [hidden, inter]).
+    """
+    H, I, b = spec.hidden, spec.inter, spec.wbits
+    parts = {}
+    for m, (name, rows, cols) in enumerate((("gate", I, H), ("up", I, H), ("down", H, I))):
+        key = stream_key(seed, K_WEIGHT, layer, expert, m)
+        w = (normal(key, rows * cols) * sigma).astype(np.float32).reshape(rows, cols)
+        q, s = quantize_rows(w, b)
+        parts[name] = q
+        parts["s_" + name] = s
+    blob = assemble_blob(H, I, b, parts["gate"], parts["up"], parts["down"],
+                         parts["s_gate"], parts["s_up"], parts["s_down"])
+    return blob, parts
+
+
+# --------------------------------------------------------------------------
+# fast large-blob recipe (C helper)
+# --------------------------------------------------------------------------
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "_build", "libsynth.so")
+_lib = None
+
+
+def build_lib(force: bool = False) -> str:
+    """Compiles gen.c into synth/_build/libsynth.so."""
+    if force or not os.path.exists(_LIB_PATH):
+        os.makedirs(os.path.dirname(_LIB_PATH), exist_ok=True)
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-Wall",
+                               os.path.join(_HERE, "gen.c"), "-o", tmp])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        lib = ctypes.CDLL(build_lib())
+        lib.synth_fill_blob_cdf.restype = ctypes.c_uint64
+        lib.synth_fill_blob_cdf.argtypes = [
+            ctypes.POINTER(ctypes.c_uint64), ctypes.c_int, ctypes.c_int, ctypes.c_int,
+            ctypes.c_void_p, ctypes.c_float, ctypes.c_float, ctypes.c_void_p, ctypes.c_int]
+        _lib = lib
+    return _lib
+
+
+def _phi(z: float) -> float:
+    return 0.5 * (1.0 + math.erf(z / math.sqrt(2.0)))
+
+
+_TABLES: dict = {}
+
+
+def cdf_table(bits: int, amax_sigmas: float = 4.0) -> np.ndarray:
+    """65536-entry table mapping a 16-bit uniform to a code, distributed as
+    round(w/s) for w ~ N(0,1) and s = amax_sigmas/qmax, clamped to the code range."""
+    if bits in _TABLES:
+        return _TABLES[bits]
+    lo, hi = QRANGE[bits]
+    s = amax_sigmas / QMAX[bits]
+    ks = np.arange(lo, hi + 1)
+    upper = np.array([_phi((k + 0.5) * s) if k < hi else 1.0 for k in ks])
+    thresholds = np.round(upper * 65536.0).astype(np.int64)
+    u = np.arange(65536)
+    idx = np.searchsorted(thresholds, u, side="right")
+    table = (lo + np.minimum(idx, len(ks) - 1)).astype(np.int8)
+    _TABLES[bits] = table
+    return table
+
+
+def cdf_expert_into(out_ptr: int, seed: int, layer: int, expert: int, spec: LayerSpec,
+                    sigma: float = 0.02, threads: int | None = None) -> int:
+    """Writes one cdf-recipe blob at host address out_ptr; returns its size."""
+    lib = _load()
+    table = cdf_table(spec.wbits)
+    keys = (ctypes.c_uint64 * 6)(*[stream_key(seed, K_WEIGHT, layer, expert, m, part)
+                                   for m in range(3) for part in (0, 1)])
+    nominal = 4.0 * sigma / QMAX[spec.wbits]
+    if threads is None:
+        threads = min(16, os.cpu_count() or 1)
+    n = lib.synth_fill_blob_cdf(keys, spec.hidden, spec.inter, spec.wbits,
+                                table.ctypes.data, nominal, 0.1, out_ptr, threads)
+    if n != spec.blob_bytes:
+        raise RuntimeError("synth_fill_blob_cdf rejected the shape")
+    return int(n)
+
+
+def cdf_expert(seed: int, layer: int, expert: int, spec: LayerSpec, sigma: float = 0.02) -> np.ndarray:
+    blob = np.empty(spec.blob_bytes, dtype=np.uint8)
+    cdf_expert_into(blob.ctypes.data, seed, layer, expert, spec, sigma)
+    return blob
+
+
+def expert_blob(seed: int, layer: int, expert: int, spec: LayerSpec) -> np.ndarray:
+    """The blob of routed expert `expert` (or the shared expert, expert ==
+    n_experts) of `layer`, with the recipe chosen by size."""
+    if spec.hidden * spec.inter <= 1 << 20:
+        return gaussian_expert(seed, layer, expert, spec)[0]
+    return cdf_expert(seed, layer, expert, spec)
+
+
+# --------------------------------------------------------------------------
+# hidden states, router gate and bias
+# --------------------------------------------------------------------------
+def router_weights(seed: int, layer: int, spec: LayerSpec) -> np.ndarray:
+    """W_r [E, H] f32 ~ N(0, 1/H) so that logits are about N(0, 1)."""
+    key = stream_key(seed, K_ROUTER_W, layer)
+    w = normal(key, spec.n_experts * spec.hidden) / math.sqrt(spec.hidden)
+    return w.astype(np.float32).reshape(spec.n_experts, spec.hidden)
+
+
+def router_bias(seed: int, layer: int, spec: LayerSpec, std: float = 0.01) -> np.ndarray:
+    key = stream_key(seed, K_ROUTER_BIAS, layer)
+    return (normal(key, spec.n_experts) * std).astype(np.float32)
+
+
+def hidden_states(seed: int, layer: int, S: int, H: int, stream: int = 0) -> np.ndarray:
+    """x [S, H] f32 ~ N(0, 1)."""
+    key = stream_key(seed, K_X, layer, stream)
+    return normal(key, S * H).astype(np.float32).reshape(S, H)
+
+
+def shaped_hidden_states(W_r: np.ndarray, target_logits: np.ndarray, seed: int, layer: int,
+                         stream: int = 0) -> np.ndarray:
+    """x [S, H] with W_r @ x_t = target_logits[t] (least squares, f64) plus
+    N(0,1) noise projected onto the null space of W_r; stored as f32.
+
+    Lets a test or benchmark fix which experts a token prefers without
+    evaluating the layer's router: with zero bias the sigmoid is monotone,
+    so the top-k of the target logits is the intended selection."""
+    W = W_r.astype(np.float64)
+    S = target_logits.shape[0]
+    H = W.shape[1]
+    z = normal(stream_key(seed, K_ROUTING, layer, stream), S * H).reshape(S, H)
+    pinv = np.linalg.pinv(W)                     # [H, E]
+    x = target_logits.astype(np.float64) @ pinv.T
+    x += z - (z @ W.T) @ pinv.T
+    return x.astype(np.float32)
+
+
+def tiny_layer(seed: int = 0, S: int = 4, spec: LayerSpec = TINY, layer: int = 0) -> dict:
+    """All inputs of one small layer (gaussian recipe)."""
+    blobs = [gaussian_expert(seed, layer, e, spec)[0] for e in range(spec.n_experts + spec.n_shared)]
+    return {
+        "spec": spec,
+        "x": hidden_states(seed, layer, S, spec.hidden),
+        "router_w": router_weights(seed, layer, spec),
+        "bias": router_bias(seed, layer, spec),
+        "blobs": blobs[:spec.n_experts],
+        "shared": blobs[spec.n_experts] if spec.n_shared else None,
+    }

@@ -1,0 +1,111 @@
+/*
+ * Fast seeded generator for large synthetic expert blobs.
+ *
+ * Input-generation helper only: it writes packed weight codes and per-row
+ * scales in the expert-blob byte layout, and nothing else.  It contains no
+ * arithmetic of the MoE layer itself (no activation quantisation, routing,
+ * dot products or combine).  The CPU oracle and the HIP library both read
+ * the bytes it writes; neither links this file.
+ *
+ * Random numbers: SplitMix64 (Steele, Lea & Flood, "Fast splittable
+ * pseudorandom number generators", OOPSLA 2014) used as a counter-based
+ * generator: value i of stream `key` is mix(key + (i + 1) * GAMMA).
+ *
+ * Codes are drawn i.i.d. from a caller-supplied 65536-entry table that maps a
+ * 16-bit uniform to a signed code (the caller builds it from the CDF of a
+ * quantised Gaussian).  Row scales are nominal * (1 + jitter * (u - 0.5)).
+ */
+#include <stdint.h>
+#include <string.h>
+
+#define GAMMA 0x9E3779B97F4A7C15ULL
+
+static inline uint64_t mix64(uint64_t z) {
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ULL;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBULL;
+    return z ^ (z >> 31);
+}
+
+static inline uint64_t stream_at(uint64_t key, uint64_t i) {
+    return mix64(key + (i + 1) * GAMMA);
+}
+
+static uint64_t align256(uint64_t n) { return (n + 255u) & ~(uint64_t)255u; }
+
+/* Packs one row of codes (ncols, multiple of 32) into `dst`. */
+static void pack_row(const int8_t *q, int ncols, int bits, uint8_t *dst) {
+    int nb = ncols / 32;
+    for (int b = 0; b < nb; ++b) {
+        const int8_t *c = q + 32 * b;
+        if (bits == 8) {
+            memcpy(dst + 32 * b, c, 32);
+        } else if (bits == 4) {
+            uint8_t *o = dst + 16 * b;
+            for (int j = 0; j < 16; ++j)
+                o[j] = (uint8_t)(((uint8_t)c[j] & 0x0Fu) | (((uint8_t)c[j + 16] & 0x0Fu) << 4));
+        } else { /* bits == 2 */
+            uint8_t *o = dst + 8 * b;
+            for (int j = 0; j < 8; ++j) {
+                unsigned v = 0;
+                for (int i = 0; i < 4; ++i) v |= ((unsigned)(uint8_t)c[j + 8 * i] & 3u) << (2 * i);
+                o[j] = (uint8_t)v;
+            }
+        }
+    }
+}
+
+/*
+ * Fills one matrix section (rows x cols codes) and its scale section.
+ * key_codes / key_scales select the two random streams.
+ */
+static void fill_matrix(uint64_t key_codes, uint64_t key_scales, int rows, int cols, int bits,
+                        const int8_t *table, float scale_nominal, float scale_jitter,
+                        uint8_t *codes_out, float *scales_out, int nthreads) {
+    int row_bytes = cols * bits / 8;
+#pragma omp parallel for schedule(static) num_threads(nthreads)
+    for (int r = 0; r < rows; ++r) {
+        int8_t q[32768];
+        uint64_t base = (uint64_t)r * (uint64_t)(cols / 4);
+        for (int g = 0; g < cols / 4; ++g) {
+            uint64_t u = stream_at(key_codes, base + (uint64_t)g);
+            q[4 * g + 0] = table[(u >> 0) & 0xFFFF];
+            q[4 * g + 1] = table[(u >> 16) & 0xFFFF];
+            q[4 * g + 2] = table[(u >> 32) & 0xFFFF];
+            q[4 * g + 3] = table[(u >> 48) & 0xFFFF];
+        }
+        pack_row(q, cols, bits, codes_out + (uint64_t)r * (uint64_t)row_bytes);
+        uint64_t us = stream_at(key_scales, (uint64_t)r);
+        double uu = (double)(us >> 11) * (1.0 / 9007199254740992.0);
+        scales_out[r] = (float)((double)scale_nominal * (1.0 + (double)scale_jitter * (uu - 0.5)));
+    }
+}
+
+/*
+ * Writes one expert blob: [gate codes][up codes][down codes][s_gate][s_up][s_down],
+ * each section starting on a 256-byte boundary.  `keys` holds six stream keys:
+ * codes and scales for gate, up and down.  Returns the number of bytes written.
+ */
+uint64_t synth_fill_blob_cdf(const uint64_t *keys, int hidden, int inter, int bits,
+                             const int8_t *table, float scale_nominal, float scale_jitter,
+                             uint8_t *out, int nthreads) {
+    if (hidden <= 0 || inter <= 0 || hidden % 32 || inter % 32 || hidden > 32768 || inter > 32768)
+        return 0;
+    if (bits != 8 && bits != 4 && bits != 2) return 0;
+    uint64_t gate_bytes = (uint64_t)inter * (uint64_t)(hidden * bits / 8);
+    uint64_t down_bytes = (uint64_t)hidden * (uint64_t)(inter * bits / 8);
+    uint64_t off_g = 0;
+    uint64_t off_u = align256(off_g + gate_bytes);
+    uint64_t off_d = align256(off_u + gate_bytes);
+    uint64_t off_sg = align256(off_d + down_bytes);
+    uint64_t off_su = align256(off_sg + 4ull * (uint64_t)inter);
+    uint64_t off_sd = align256(off_su + 4ull * (uint64_t)inter);
+    uint64_t total = align256(off_sd + 4ull * (uint64_t)hidden);
+    memset(out, 0, total);
+    fill_matrix(keys[0], keys[1], inter, hidden, bits, table, scale_nominal, scale_jitter,
+                out + off_g, (float *)(out + off_sg), nthreads);
+    fill_matrix(keys[2], keys[3], inter, hidden, bits, table, scale_nominal, scale_jitter,
+                out + off_u, (float *)(out + off_su), nthreads);
+    fill_matrix(keys[4], keys[5], hidden, inter, bits, table, scale_nominal, scale_jitter,
+                out + off_d, (float *)(out + off_sd), nthreads);
+    return total;
+}
