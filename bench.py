@@ -1,0 +1,227 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed-expert MoE layer on one MI355X.
+
+Workload (default): GLM-5.2-shaped decode layer — hidden 6144, expert inter
+2048, 256 routed experts top-8 + 1 shared, int4 per-row-scaled experts
+(18.9 MB each), Q8_0 activations, random fp32 router gate — with 12 layers
+resident in HBM (about 58 GB).  A step is one token through one layer:
+coli_moe_route + coli_moe_forward; step s uses layer s mod 12 and its own
+hidden state, so expert reads do not hit in the 256 MB last-level cache.
+Steps are captured in a HIP graph and replayed.
+
+Prints one JSON line: MoE-layer tokens/s, the roofline of the dominant
+kernel (HIP-event kernel durations measured in this run), whole-layer HBM
+GB/s, and the CPU oracle timed on this host as a baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s + achieved HBM GB/s (decode), int8 TOPS (prefill)"
+HBM_PEAK_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2400)
+    ap.add_argument("--warmup", type=int, default=240)
+    ap.add_argument("--layers", type=int, default=12, help="resident GLM-shaped layers")
+    ap.add_argument("--graph-steps", type=int, default=240, help="steps per captured HIP graph")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU-oracle baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--seed", type=int, default=0)
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: --gpus {args.gpus} requested, but this layer build runs on exactly one GPU "
+              "(no collectives or sharding); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from quantized_expert_ffn_amd import build as hipbuild
+    if not os.path.exists(hipbuild.LIB):
+        hipbuild.build()
+    import quantized_expert_ffn_amd as q
+    import synth
+
+    torch.cuda.set_device(0)
+    spec = synth.GLM
+    dims = q.make_dims(spec)
+    H, E = spec.hidden, spec.n_experts
+    L = args.layers
+    bb = spec.blob_bytes
+    nblob = E + 1  # routed + shared, contiguous per layer
+
+    # ---- resident layers: generated on the host (pinned staging), copied to HBM
+    t0 = time.time()
+    layers = []
+    staging = [torch.empty(nblob * bb, dtype=torch.uint8, pin_memory=True) for _ in range(2)]
+    copy_stream = torch.cuda.Stream()
+    done = [None, None]
+    for l in range(L):
+        buf = staging[l % 2]
+        if done[l % 2] is not None:
+            done[l % 2].synchronize()
+        base = buf.data_ptr()
+        for e in range(nblob):
+            synth.cdf_expert_into(base + e * bb, args.seed, l, e, spec)
+        dev = torch.empty(nblob * bb, dtype=torch.uint8, device="cuda")
+        with torch.cuda.stream(copy_stream):
+            dev.copy_(buf, non_blocking=True)
+            ev = torch.cuda.Event()
+            ev.record(copy_stream)
+        done[l % 2] = ev
+        d = synth.layer_inputs(args.seed, l, spec, 1)
+        table = torch.tensor([dev.data_ptr() + e * bb for e in range(E)], dtype=torch.int64, device="cuda")
+        layers.append({"blobs": dev, "table": table, "shared": dev.data_ptr() + E * bb,
+                       "router_w": torch.from_numpy(d["router_w"]).cuda(),
+                       "bias": torch.from_numpy(d["bias"]).cuda()})
+        log(f"layer {l}: {nblob} experts generated and staged ({time.time() - t0:.1f} s)")
+    torch.cuda.synchronize()
+    del staging
+    G = max(1, min(args.graph_steps, args.steps))
+    xs_host = synth.hidden_states(args.seed, 1000, G, H)
+    xs = torch.from_numpy(xs_host).cuda()
+    ws = torch.zeros(q.coli_moe_workspace_bytes(dims, 1), dtype=torch.uint8, device="cuda")
+    idx = torch.empty((G, spec.top_k), dtype=torch.int32, device="cuda")
+    wts = torch.empty((G, spec.top_k), dtype=torch.float32, device="cuda")
+    out = torch.empty((G, H), dtype=torch.float32, device="cuda")
+    log(f"setup done in {time.time() - t0:.1f} s; {torch.cuda.memory_allocated() / 1e9:.1f} GB allocated")
+
+    def step(s):
+        lay = layers[s % L]
+        x = xs[s:s + 1]
+        q.coli_moe_route(dims, x, lay["router_w"], lay["bias"], idx[s:s + 1], wts[s:s + 1], ws)
+        q.coli_moe_forward(dims, x, idx[s:s + 1], wts[s:s + 1], lay["table"], lay["shared"],
+                           out[s:s + 1], ws)
+
+    # eager pass: correctness of the status word, kernel timing with HIP events
+    for s in range(G):
+        step(s)
+    rc = q.coli_moe_status(ws)
+    if rc != 0:
+        raise RuntimeError(f"device status {rc}: {q.coli_moe_last_error()}")
+    routed = idx.cpu().numpy()
+    q.coli_moe_timing_enable(True)
+    for s in range(G):
+        step(s)
+    torch.cuda.synchronize()
+    q.coli_moe_timing_enable(False)
+    kt = {k: q.coli_moe_timing_read(k) for k in (q.KIND_ROUTER_LOGITS, q.KIND_ROUTER_SELECT,
+                                                 q.KIND_GATEUP, q.KIND_DOWN)}
+    kernel_us = {name: 1e3 * kt[k][0] / max(kt[k][1], 1) for name, k in
+                 (("router_logits", 0), ("router_select", 1), ("gateup", 2), ("down_combine", 3))}
+
+    # captured steps
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.graph(graph, stream=cap):
+        for s in range(G):
+            step(s)
+    torch.cuda.synchronize()
+    reps_w = max(1, args.warmup // G)
+    reps = max(1, args.steps // G)
+    for _ in range(reps_w):
+        graph.replay()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(reps):
+        graph.replay()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t1
+    steps = reps * G
+    rc = q.coli_moe_status(ws)
+    if rc != 0:
+        raise RuntimeError(f"device status after replay {rc}: {q.coli_moe_last_error()}")
+    ms_per_step = 1e3 * elapsed / steps
+    tokens_per_s = steps / elapsed
+
+    # algorithmic bytes: each token-layer reads W_r, the 8 routed experts and the shared one once
+    lay_bytes = E * H * 4 + E * 4 + 9 * bb
+    gateup_bytes = 9 * (2 * spec.inter * H * spec.wbits // 8 + 2 * spec.inter * 4)
+    gu_us = kernel_us["gateup"]
+    achieved = gateup_bytes / (gu_us * 1e-6) / 1e9
+    layer_gbs = lay_bytes / (ms_per_step * 1e-3) / 1e9
+    res = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": reps_w * G,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8xi4->i32,f32",
+        "data": "synthetic (seeded; GLM-5.2-shaped random-code experts)",
+        "config": {
+            "workload": "GLM-5.2-shaped MoE decode layer, 1 token/step: hidden 6144, expert inter 2048, "
+                        "256 routed experts top-8 + 1 shared, int4 per-row-scaled weights (18.9 MB/expert), "
+                        "Q8_0 activations, fp32 router gate; 12 layers resident in HBM, step s uses layer s mod 12",
+            "layers_resident": L, "resident_gb": round(L * nblob * bb / 1e9, 1),
+            "tokens_per_step": 1, "graph_steps": G,
+        },
+        "roofline": {
+            "bound": "hbm", "kernel": "k_gateup<4,1>",
+            "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "algorithmic_bytes_per_launch": gateup_bytes, "avg_launch_us": round(gu_us, 3),
+        },
+        "layer_hbm_gbs": round(layer_gbs, 1),
+        "layer_hbm_frac": round(layer_gbs / HBM_PEAK_GBS, 4),
+        "kernel_avg_us": {k: round(v, 3) for k, v in kernel_us.items()},
+        "unique_experts_per_step": int(np.mean([len(set(r)) for r in routed])) + 1,
+    }
+
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(args, spec, xs_host, layers, L)
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline(args, spec, xs_host, layers, L):
+    """The CPU oracle (plain single-threaded C) on a bounded sample: whole
+    layer steps (route + 8 experts + shared + combine) of the same workload,
+    as many as fit the time budget."""
+    import numpy as np
+
+    import oracle
+    import synth
+    n, spent = 0, 0.0
+    while spent < args.cpu_seconds and n < xs_host.shape[0]:
+        l = n % L
+        d = synth.layer_inputs(args.seed, l, spec, 1)
+        x = xs_host[n:n + 1]
+        idx, w, _, _ = oracle.route(spec, x, d["router_w"], d["bias"])
+        blobs = [None] * spec.n_experts
+        for e in idx[0]:
+            blobs[int(e)] = synth.cdf_expert(args.seed, l, int(e), spec)
+        shared = synth.cdf_expert(args.seed, l, spec.n_experts, spec)
+        t = time.perf_counter()
+        oracle.layer(spec, x, d["router_w"], d["bias"], blobs, shared)
+        spent += time.perf_counter() - t
+        n += 1
+    return {"value": round(n / spent, 4), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n} token-layer steps of the same workload (route + 9 experts + combine), "
+                      f"{spent:.1f} s single-threaded; expert generation excluded"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,181 @@
+/*
+ * coli_moe.h — C ABI of the routed-expert MoE layer on MI355X (gfx950).
+ *
+ * The layer (colibrì README v1.0, "What's implemented": DeepSeek-V3-style
+ * sigmoid router with routed_scaling_factor and a shared expert; integer-dot
+ * kernels over Q8_0-style int8 activations; int8 / packed int4 / packed int2
+ * weights with per-row scales; batch-union MoE):
+ *
+ *   logits = W_r x                      (binary32, fixed reduction order)
+ *   sel    = top-K of sigmoid(logits) + bias, ties to the lower expert id
+ *   w_k    = sigmoid_k / sum(sigmoid_sel) * routed_scaling_factor
+ *   out    = sum_k w_k * FFN_{sel_k}(x) + FFN_shared(x)
+ *   FFN(x) = W_d Q8_0( silu(W_g Q8_0(x)) * (W_u Q8_0(x)) )
+ *
+ * Every binary32 operation happens in one defined order, so the results are
+ * bitwise reproducible and independent of the batch size.
+ *
+ * Conventions for every call:
+ *  - Pointers documented "device" are HIP device (or managed) memory; "host"
+ *    pointers are read before the call returns.  The library allocates no
+ *    device memory: scratch space is the caller's workspace.
+ *  - stream / event arguments are hipStream_t / hipEvent_t passed as void*;
+ *    NULL means the default stream.  Calls enqueue work and return without
+ *    synchronising, except coli_moe_status.
+ *  - Return value 0 on success or a negative COLI_E* code; the message of the
+ *    last failure on this thread is available from coli_moe_last_error().
+ *  - Conditions only the device can see (non-finite values, an out-of-range
+ *    or repeated expert index, a routed expert that is not resident) set bits
+ *    of a status word inside the workspace; they are sticky until
+ *    coli_moe_status() reads and clears them.  When the status is non-zero
+ *    the outputs of the calls since the last read are unspecified.
+ *  - There is no CPU fallback: without a usable gfx950 device every compute
+ *    call fails with COLI_EHIP.
+ */
+#ifndef COLI_MOE_H
+#define COLI_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define COLI_OK 0
+#define COLI_EINVAL (-1)        /* bad dimension, pointer, index or size */
+#define COLI_ENONFINITE (-2)    /* NaN/Inf in an input, or undefined gate weights */
+#define COLI_EHIP (-3)          /* a HIP runtime call failed */
+#define COLI_ENOTRESIDENT (-4)  /* a routed expert's blob pointer is NULL */
+#define COLI_EWORKSPACE (-5)    /* workspace too small for this call */
+
+/* Layer shape.  All fields are preconditions checked on every call. */
+typedef struct coli_moe_dims {
+    int32_t hidden;               /* H: multiple of 256 (router order) */
+    int32_t inter;                /* I: expert intermediate size, multiple of 32 */
+    int32_t n_experts;            /* E: routed experts, 1..1024 */
+    int32_t top_k;                /* K: 1..min(E, 32) */
+    int32_t n_shared;             /* 0 or 1 shared expert */
+    int32_t wbits;                /* 8, 4 or 2: weight code width */
+    float routed_scaling_factor;  /* multiplies the gate weights */
+    int32_t norm_topk_prob;       /* 1: weights renormalised over the K selected */
+} coli_moe_dims;
+
+/*
+ * Size in bytes of one expert blob.  Layout (row-major, reduction dimension
+ * contiguous, each section starting on a 256-byte boundary):
+ *   [gate codes: I rows x H*bits/8][up codes: I rows x H*bits/8]
+ *   [down codes: H rows x I*bits/8][gate scales: I f32][up scales: I f32]
+ *   [down scales: H f32]
+ * Codes per 32-element block: int8 as bytes; int4 16 bytes, byte j = code j
+ * (bits 0-3) | code j+16 (bits 4-7); int2 8 bytes, byte j = code j+8i in bits
+ * 2i..2i+1.  Two's complement.  (README v1.0 "The idea": about 19 MB per
+ * expert at int4; GLM-5.2 shape gives 18 915 328 bytes.)
+ * Returns 0 when dims are invalid.
+ */
+size_t coli_moe_expert_bytes(const coli_moe_dims *dims);
+
+/* Workspace bytes needed for calls with up to max_tokens tokens.  The
+ * workspace must be zero-filled once before its first use (the status word
+ * lives in it); afterwards the library keeps it consistent. 0 if invalid. */
+size_t coli_moe_workspace_bytes(const coli_moe_dims *dims, int32_t max_tokens);
+
+/*
+ * Router: logits, bias-corrected top-K and gate weights for n_tokens tokens
+ * ("Colibri (colibrì): GLM-5.2 local inference on 25 GB of RAM", "How it
+ * works (validated core mechanics)": the bias ranks only, weights are the
+ * unbiased sigmoids renormalised, lower id wins a tie; non-finite input is
+ * rejected).
+ *   x           device f32 [n_tokens, H]
+ *   router_w    device f32 [E, H]  (nn.Linear layout)
+ *   router_bias device f32 [E] or NULL (zeros)
+ *   topk_idx    device int32 [n_tokens, K] out, rank order
+ *   topk_w      device f32  [n_tokens, K] out, same order
+ * n_tokens == 0 is a no-op.  Non-finite x / W_r / bias / logits set
+ * COLI_ENONFINITE in the status word.
+ */
+int coli_moe_route(const coli_moe_dims *dims, int32_t n_tokens, const float *x,
+                   const float *router_w, const float *router_bias, int32_t *topk_idx,
+                   float *topk_w, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Expert FFNs and combine for n_tokens tokens with given routing (README
+ * v1.0 "What's implemented": SwiGLU experts on Q8_0 activations, shared
+ * expert, batch-union: each unique expert of the call is read once and
+ * applied to every token routed to it).
+ *   x            device f32 [n_tokens, H]
+ *   topk_idx     device int32 [n_tokens, K], topk_w device f32 [n_tokens, K]
+ *   expert_blobs device array [E] of device blob pointers; NULL = not resident
+ *   shared_blob  device blob, or NULL when n_shared == 0
+ *   pending_mask host uint8 [E] or NULL: experts whose blobs are still being
+ *                staged; they run after the stream waits for pending_ready
+ *                (a hipEvent_t, may be NULL), all others run before it
+ *   out          device f32 [n_tokens, H]; each element written once
+ */
+int coli_moe_forward(const coli_moe_dims *dims, int32_t n_tokens, const float *x,
+                     const int32_t *topk_idx, const float *topk_w,
+                     const void *const *expert_blobs, const void *shared_blob,
+                     const uint8_t *pending_mask, void *pending_ready, float *out, void *ws,
+                     size_t ws_bytes, void *stream);
+
+/*
+ * Expert staging (README v1.0 "What's implemented": async expert readahead —
+ * the next experts are fetched while the current ones are multiplied).
+ * Enqueues n host-to-device copies of bytes_each bytes, host_src[i] (pinned
+ * host memory) to dev_dst[i] (device), on copy_stream, then records
+ * done_event (may be NULL).  host_src / dev_dst are host arrays of pointers,
+ * read before return; the source memory must stay valid until the event
+ * completes.
+ */
+int coli_moe_stage_experts(int32_t n, const void *const *host_src, void *const *dev_dst,
+                           size_t bytes_each, void *copy_stream, void *done_event);
+
+/* Synchronises `stream`, returns the status recorded in the workspace since
+ * the last read (0 or the most severe COLI_E* code) and clears it. */
+int coli_moe_status(void *ws, void *stream);
+
+/* Message of the last failure on the calling thread ("" if none). */
+const char *coli_moe_last_error(void);
+
+/*
+ * Kernel timing.  While enabled, every kernel launched by the library is
+ * bracketed by events on its stream; coli_moe_timing_read() synchronises the
+ * recorded events and returns the accumulated milliseconds and launch count
+ * of one kernel kind (0 router logits, 1 router select, 2 gate/up,
+ * 3 down/combine, 4 prefill gate/up, 5 prefill down, 6 prefill combine,
+ * 7 prefill grouping), then resets that kind.  For measurement only.
+ */
+int coli_moe_timing_enable(int32_t enable);
+int coli_moe_timing_read(int32_t kind, double *total_ms, int64_t *launches);
+
+/* ---- test hooks: the same device functions as the production kernels ---- */
+
+/* Unpacks n_rows packed rows of `cols` codes (device src, row stride
+ * cols*bits/8 bytes) into device int8 out [n_rows, cols]. */
+int coli_moe_debug_unpack(int32_t bits, int32_t n_rows, int32_t cols, const void *src,
+                          int8_t *out, void *stream);
+
+/* Exact int32 block dot products isum[r, b] = sum_{j<32} w[r, 32b+j] * q[32b+j]
+ * of n_rows packed rows (device src) with a device int8 vector q [cols];
+ * out device int32 [n_rows, cols/32]. */
+int coli_moe_debug_block_dots(int32_t bits, int32_t n_rows, int32_t cols, const void *src,
+                              const int8_t *q, int32_t *out, void *stream);
+
+/* Router logits only: device f32 logits [n_tokens, E]. */
+int coli_moe_debug_logits(const coli_moe_dims *dims, int32_t n_tokens, const float *x,
+                          const float *router_w, float *logits, void *stream);
+
+/* The device exponential used by the router and SwiGLU, element-wise on
+ * device f32 arrays of n elements. */
+int coli_moe_debug_expf(int64_t n, const float *x, float *y, void *stream);
+
+/* Q8_0 of device f32 v [n_rows, cols] into device int8 q and f32 d
+ * [n_rows, cols/32], with the device quantiser the kernels use. */
+int coli_moe_debug_q8_0(int32_t n_rows, int32_t cols, const float *v, int8_t *q, float *d,
+                        void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* COLI_MOE_H */

@@ -1,0 +1,234 @@
+"""Python binding of libcolimoe, the routed-expert MoE layer for MI355X.
+
+Argument marshalling only: every function here has the name of the C entry
+point it calls (include/coli_moe.h), turns torch tensors into device
+pointers and the current torch stream into a hipStream_t, and raises
+ColiError on a non-zero return.  All computation happens in the HIP kernels.
+Importing fails if the library has not been built; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "_build", "libcolimoe.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python -m quantized_expert_ffn_amd.build` "
+        "(or __graft_entry__.build()); the MoE layer has no non-HIP implementation")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+COLI_OK, COLI_EINVAL, COLI_ENONFINITE, COLI_EHIP, COLI_ENOTRESIDENT, COLI_EWORKSPACE = 0, -1, -2, -3, -4, -5
+
+EXPORTS = (
+    "coli_moe_expert_bytes", "coli_moe_workspace_bytes", "coli_moe_route", "coli_moe_forward",
+    "coli_moe_stage_experts", "coli_moe_status", "coli_moe_last_error", "coli_moe_timing_enable",
+    "coli_moe_timing_read", "coli_moe_debug_unpack", "coli_moe_debug_block_dots",
+    "coli_moe_debug_logits", "coli_moe_debug_expf", "coli_moe_debug_q8_0",
+)
+
+KIND_ROUTER_LOGITS, KIND_ROUTER_SELECT, KIND_GATEUP, KIND_DOWN = 0, 1, 2, 3
+
+
+class coli_moe_dims(ctypes.Structure):
+    _fields_ = [
+        ("hidden", ctypes.c_int32), ("inter", ctypes.c_int32), ("n_experts", ctypes.c_int32),
+        ("top_k", ctypes.c_int32), ("n_shared", ctypes.c_int32), ("wbits", ctypes.c_int32),
+        ("routed_scaling_factor", ctypes.c_float), ("norm_topk_prob", ctypes.c_int32),
+    ]
+
+
+class ColiError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        msg = _lib.coli_moe_last_error().decode(errors="replace")
+        super().__init__(f"{where} failed ({code}): {msg}")
+        self.code = code
+
+
+_P = ctypes.c_void_p
+_SZ = ctypes.c_size_t
+_I32 = ctypes.c_int32
+_D = ctypes.POINTER(coli_moe_dims)
+_sigs = {
+    "coli_moe_expert_bytes": (_SZ, [_D]),
+    "coli_moe_workspace_bytes": (_SZ, [_D, _I32]),
+    "coli_moe_route": (ctypes.c_int, [_D, _I32, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "coli_moe_forward": (ctypes.c_int, [_D, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "coli_moe_stage_experts": (ctypes.c_int, [_I32, _P, _P, _SZ, _P, _P]),
+    "coli_moe_status": (ctypes.c_int, [_P, _P]),
+    "coli_moe_last_error": (ctypes.c_char_p, []),
+    "coli_moe_timing_enable": (ctypes.c_int, [_I32]),
+    "coli_moe_timing_read": (ctypes.c_int, [_I32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]),
+    "coli_moe_debug_unpack": (ctypes.c_int, [_I32, _I32, _I32, _P, _P, _P]),
+    "coli_moe_debug_block_dots": (ctypes.c_int, [_I32, _I32, _I32, _P, _P, _P, _P]),
+    "coli_moe_debug_logits": (ctypes.c_int, [_D, _I32, _P, _P, _P, _P]),
+    "coli_moe_debug_expf": (ctypes.c_int, [ctypes.c_int64, _P, _P, _P]),
+    "coli_moe_debug_q8_0": (ctypes.c_int, [_I32, _I32, _P, _P, _P, _P]),
+}
+for _name, (_res, _args) in _sigs.items():
+    _f = getattr(_lib, _name)
+    _f.restype = _res
+    _f.argtypes = _args
+
+
+# ---------------------------------------------------------------- marshalling
+def make_dims(spec) -> coli_moe_dims:
+    """coli_moe_dims from any object with the dims' field names."""
+    return coli_moe_dims(int(spec.hidden), int(spec.inter), int(spec.n_experts), int(spec.top_k),
+                         int(spec.n_shared), int(spec.wbits), float(spec.routed_scaling_factor),
+                         int(spec.norm_topk_prob))
+
+
+def _dims(d):
+    return ctypes.byref(d if isinstance(d, coli_moe_dims) else make_dims(d))
+
+
+def _ptr(t, dtype=None, what="tensor"):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{what}: expected a torch tensor or an address")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{what}: dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{what}: must be contiguous")
+    return t.data_ptr()
+
+
+def _dev(t, dtype, what):
+    import torch
+    if isinstance(t, torch.Tensor) and not t.is_cuda:
+        raise ValueError(f"{what}: must be a device tensor")
+    return _ptr(t, dtype, what)
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(rc, where):
+    if rc != COLI_OK:
+        raise ColiError(rc, where)
+
+
+def _nbytes(t):
+    return t.numel() * t.element_size()
+
+
+# ---------------------------------------------------------------- entry points
+def coli_moe_expert_bytes(dims) -> int:
+    return int(_lib.coli_moe_expert_bytes(_dims(dims)))
+
+
+def coli_moe_workspace_bytes(dims, max_tokens: int) -> int:
+    return int(_lib.coli_moe_workspace_bytes(_dims(dims), int(max_tokens)))
+
+
+def coli_moe_route(dims, x, router_w, router_bias, topk_idx, topk_w, ws, stream=None):
+    import torch
+    S = x.shape[0]
+    _check(_lib.coli_moe_route(
+        _dims(dims), S, _dev(x, torch.float32, "x"), _dev(router_w, torch.float32, "router_w"),
+        _dev(router_bias, torch.float32, "router_bias"), _dev(topk_idx, torch.int32, "topk_idx"),
+        _dev(topk_w, torch.float32, "topk_w"), _dev(ws, torch.uint8, "ws"), _nbytes(ws),
+        _stream(stream)), "coli_moe_route")
+
+
+def coli_moe_forward(dims, x, topk_idx, topk_w, expert_blobs, shared_blob, out, ws,
+                     pending_mask=None, pending_ready=None, stream=None):
+    """expert_blobs: device int64 tensor [E] of blob addresses (0 = not
+    resident); pending_mask: host sequence of E flags or None; pending_ready:
+    a torch.cuda.Event (or raw hipEvent_t address) or None."""
+    import numpy as np
+    import torch
+    S = x.shape[0]
+    mask_ptr = None
+    if pending_mask is not None:
+        mask = np.ascontiguousarray(np.asarray(pending_mask, dtype=np.uint8))
+        mask_ptr = mask.ctypes.data
+    ev = pending_ready
+    if ev is not None and not isinstance(ev, int):
+        ev = ev.cuda_event
+    _check(_lib.coli_moe_forward(
+        _dims(dims), S, _dev(x, torch.float32, "x"), _dev(topk_idx, torch.int32, "topk_idx"),
+        _dev(topk_w, torch.float32, "topk_w"), _dev(expert_blobs, torch.int64, "expert_blobs"),
+        _ptr(shared_blob, None, "shared_blob"), mask_ptr, ev, _dev(out, torch.float32, "out"),
+        _dev(ws, torch.uint8, "ws"), _nbytes(ws), _stream(stream)), "coli_moe_forward")
+
+
+def coli_moe_stage_experts(host_src, dev_dst, bytes_each: int, copy_stream=None, done_event=None):
+    n = len(host_src)
+    if len(dev_dst) != n:
+        raise ValueError("host_src and dev_dst differ in length")
+    src = (ctypes.c_void_p * max(n, 1))(*[_ptr(s, None, "host_src") for s in host_src])
+    dst = (ctypes.c_void_p * max(n, 1))(*[_ptr(d, None, "dev_dst") for d in dev_dst])
+    ev = done_event
+    if ev is not None and not isinstance(ev, int):
+        ev = ev.cuda_event
+    _check(_lib.coli_moe_stage_experts(n, src, dst, int(bytes_each), _stream(copy_stream), ev),
+           "coli_moe_stage_experts")
+
+
+def coli_moe_status(ws, stream=None) -> int:
+    """Synchronises the stream and returns (and clears) the device status code."""
+    return int(_lib.coli_moe_status(_ptr(ws, None, "ws"), _stream(stream)))
+
+
+def coli_moe_last_error() -> str:
+    return _lib.coli_moe_last_error().decode(errors="replace")
+
+
+def coli_moe_timing_enable(enable: bool) -> None:
+    _check(_lib.coli_moe_timing_enable(1 if enable else 0), "coli_moe_timing_enable")
+
+
+def coli_moe_timing_read(kind: int) -> tuple[float, int]:
+    ms = ctypes.c_double()
+    n = ctypes.c_int64()
+    _check(_lib.coli_moe_timing_read(int(kind), ctypes.byref(ms), ctypes.byref(n)), "coli_moe_timing_read")
+    return ms.value, n.value
+
+
+def coli_moe_debug_unpack(bits, n_rows, cols, src, out, stream=None):
+    import torch
+    _check(_lib.coli_moe_debug_unpack(bits, n_rows, cols, _ptr(src, None, "src"),
+                                      _dev(out, torch.int8, "out"), _stream(stream)), "coli_moe_debug_unpack")
+
+
+def coli_moe_debug_block_dots(bits, n_rows, cols, src, q, out, stream=None):
+    import torch
+    _check(_lib.coli_moe_debug_block_dots(bits, n_rows, cols, _ptr(src, None, "src"),
+                                          _dev(q, torch.int8, "q"), _dev(out, torch.int32, "out"),
+                                          _stream(stream)), "coli_moe_debug_block_dots")
+
+
+def coli_moe_debug_logits(dims, x, router_w, logits, stream=None):
+    import torch
+    _check(_lib.coli_moe_debug_logits(_dims(dims), x.shape[0], _dev(x, torch.float32, "x"),
+                                      _dev(router_w, torch.float32, "router_w"),
+                                      _dev(logits, torch.float32, "logits"), _stream(stream)),
+           "coli_moe_debug_logits")
+
+
+def coli_moe_debug_expf(x, y, stream=None):
+    import torch
+    _check(_lib.coli_moe_debug_expf(x.numel(), _dev(x, torch.float32, "x"), _dev(y, torch.float32, "y"),
+                                    _stream(stream)), "coli_moe_debug_expf")
+
+
+def coli_moe_debug_q8_0(v, q, d, stream=None):
+    import torch
+    rows, cols = v.shape
+    _check(_lib.coli_moe_debug_q8_0(rows, cols, _dev(v, torch.float32, "v"), _dev(q, torch.int8, "q"),
+                                    _dev(d, torch.float32, "d"), _stream(stream)), "coli_moe_debug_q8_0")

@@ -1,0 +1,344 @@
+// C-ABI entry points (include/coli_moe.h): argument checks, workspace
+// carve-up, kernel launches, staging copies, status and timing.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "coli_moe.h"
+#include "device_common.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+int hip_fail(hipError_t e, const char *what) {
+    return fail(COLI_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// The kernels are compiled for gfx950 only; refuse any other device.
+int check_device() {
+    static std::mutex mu;
+    static std::vector<int> ok;  // per device: 0 unknown, 1 ok, -1 refused
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    std::lock_guard<std::mutex> lk(mu);
+    if ((int)ok.size() <= dev) ok.resize(dev + 1, 0);
+    if (ok[dev] == 0) {
+        hipDeviceProp_t prop;
+        e = hipGetDeviceProperties(&prop, dev);
+        if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+        ok[dev] = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+    }
+    if (ok[dev] < 0) return fail(COLI_EHIP, "device %d is not gfx950; this library has no other code path", dev);
+    return COLI_OK;
+}
+
+int check_dims(const coli_moe_dims *d) {
+    if (!d) return fail(COLI_EINVAL, "dims is NULL");
+    if (d->hidden <= 0 || d->hidden % 256 != 0 || d->hidden > 16384)
+        return fail(COLI_EINVAL, "hidden=%d: must be a positive multiple of 256, at most 16384", d->hidden);
+    if (d->inter <= 0 || d->inter % 32 != 0 || d->inter > 16384)
+        return fail(COLI_EINVAL, "inter=%d: must be a positive multiple of 32, at most 16384", d->inter);
+    if (d->n_experts < 1 || d->n_experts > 1024)
+        return fail(COLI_EINVAL, "n_experts=%d: must be in 1..1024", d->n_experts);
+    if (d->top_k < 1 || d->top_k > d->n_experts || d->top_k > 32)
+        return fail(COLI_EINVAL, "top_k=%d: must be in 1..min(n_experts, 32)", d->top_k);
+    if (d->n_shared != 0 && d->n_shared != 1)
+        return fail(COLI_EINVAL, "n_shared=%d: must be 0 or 1", d->n_shared);
+    if (d->wbits != 8 && d->wbits != 4 && d->wbits != 2)
+        return fail(COLI_EINVAL, "wbits=%d: must be 8, 4 or 2", d->wbits);
+    return COLI_OK;
+}
+
+// ---- kernel timing ------------------------------------------------------
+struct Timing {
+    std::mutex mu;
+    bool on = false;
+    std::vector<hipEvent_t> free_events;
+    hipEvent_t open[coli::KK_COUNT] = {};
+    std::vector<std::pair<hipEvent_t, hipEvent_t>> done[coli::KK_COUNT];
+} g_timing;
+
+hipEvent_t take_event() {
+    if (!g_timing.free_events.empty()) {
+        hipEvent_t e = g_timing.free_events.back();
+        g_timing.free_events.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+}  // namespace
+
+namespace coli {
+
+void timing_before(int kind, hipStream_t st) {
+    std::lock_guard<std::mutex> lk(g_timing.mu);
+    if (!g_timing.on) return;
+    hipEvent_t e = take_event();
+    if (e && hipEventRecord(e, st) == hipSuccess) g_timing.open[kind] = e;
+}
+
+void timing_after(int kind, hipStream_t st) {
+    std::lock_guard<std::mutex> lk(g_timing.mu);
+    if (!g_timing.on || !g_timing.open[kind]) return;
+    hipEvent_t e = take_event();
+    if (e && hipEventRecord(e, st) == hipSuccess)
+        g_timing.done[kind].emplace_back(g_timing.open[kind], e);
+    g_timing.open[kind] = nullptr;
+}
+
+}  // namespace coli
+
+using namespace coli;
+
+extern "C" {
+
+size_t coli_moe_expert_bytes(const coli_moe_dims *d) {
+    if (check_dims(d) != COLI_OK) return 0;
+    return blob_layout(d->hidden, d->inter, d->wbits).total;
+}
+
+size_t coli_moe_workspace_bytes(const coli_moe_dims *d, int32_t max_tokens) {
+    if (check_dims(d) != COLI_OK || max_tokens < 0) return 0;
+    return ws_layout(d->hidden, d->inter, d->n_experts, d->top_k, max_tokens).total;
+}
+
+const char *coli_moe_last_error(void) { return g_err.c_str(); }
+
+int coli_moe_route(const coli_moe_dims *d, int32_t S, const float *x, const float *router_w,
+                   const float *router_bias, int32_t *topk_idx, float *topk_w, void *ws,
+                   size_t ws_bytes, void *stream) {
+    int rc = check_dims(d);
+    if (rc) return rc;
+    if (S < 0) return fail(COLI_EINVAL, "n_tokens=%d < 0", S);
+    if (S == 0) return COLI_OK;
+    if (!x || !router_w || !topk_idx || !topk_w || !ws)
+        return fail(COLI_EINVAL, "coli_moe_route: NULL pointer argument");
+    const WsLayout L = ws_layout(d->hidden, d->inter, d->n_experts, d->top_k, S);
+    if (ws_bytes < L.total)
+        return fail(COLI_EWORKSPACE, "workspace %zu bytes < %zu needed for %d tokens", ws_bytes, L.total, S);
+    if ((rc = check_device())) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    uint8_t *w8 = static_cast<uint8_t *>(ws);
+    uint32_t *status = reinterpret_cast<uint32_t *>(w8 + L.status);
+    float *logits = reinterpret_cast<float *>(w8 + L.logits);
+    timing_before(KK_ROUTER_LOGITS, st);
+    hipError_t e = launch_router_logits(x, router_w, logits, status, S, d->hidden, d->n_experts, st);
+    timing_after(KK_ROUTER_LOGITS, st);
+    if (e != hipSuccess) return hip_fail(e, "router logits launch");
+    timing_before(KK_ROUTER_SELECT, st);
+    e = launch_router_select(logits, router_bias, topk_idx, topk_w, status, S, d->n_experts, d->top_k,
+                             d->routed_scaling_factor, d->norm_topk_prob, st);
+    timing_after(KK_ROUTER_SELECT, st);
+    if (e != hipSuccess) return hip_fail(e, "router select launch");
+    return COLI_OK;
+}
+
+int coli_moe_forward(const coli_moe_dims *d, int32_t S, const float *x, const int32_t *topk_idx,
+                     const float *topk_w, const void *const *expert_blobs, const void *shared_blob,
+                     const uint8_t *pending_mask, void *pending_ready, float *out, void *ws,
+                     size_t ws_bytes, void *stream) {
+    int rc = check_dims(d);
+    if (rc) return rc;
+    if (S < 0) return fail(COLI_EINVAL, "n_tokens=%d < 0", S);
+    if (S == 0) return COLI_OK;
+    if (!x || !topk_idx || !topk_w || !expert_blobs || !out || !ws)
+        return fail(COLI_EINVAL, "coli_moe_forward: NULL pointer argument");
+    if (d->n_shared && !shared_blob)
+        return fail(COLI_ENOTRESIDENT, "n_shared=1 but shared_blob is NULL");
+    const WsLayout L = ws_layout(d->hidden, d->inter, d->n_experts, d->top_k, S);
+    if (ws_bytes < L.total)
+        return fail(COLI_EWORKSPACE, "workspace %zu bytes < %zu needed for %d tokens", ws_bytes, L.total, S);
+    const size_t smem = forward_smem_max(S, d->hidden, d->inter, d->n_experts, d->top_k, d->n_shared);
+    if (smem > 160 * 1024)
+        return fail(COLI_EINVAL, "shape needs %zu bytes of LDS per workgroup (> 160 KiB)", smem);
+    if ((rc = check_device())) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    uint8_t *w8 = static_cast<uint8_t *>(ws);
+    FwdArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.x = x;
+    a.idx = topk_idx;
+    a.w = topk_w;
+    a.blobs = reinterpret_cast<const uint8_t *const *>(expert_blobs);
+    a.shared = static_cast<const uint8_t *>(shared_blob);
+    a.qh = reinterpret_cast<int8_t *>(w8 + L.qh);
+    a.dh = reinterpret_cast<float *>(w8 + L.dh);
+    a.Y = reinterpret_cast<float *>(w8 + L.Y);
+    a.counters = reinterpret_cast<uint32_t *>(w8 + L.counters);
+    a.out = out;
+    a.status = reinterpret_cast<uint32_t *>(w8 + L.status);
+    a.S = S;
+    a.H = d->hidden;
+    a.I = d->inter;
+    a.E = d->n_experts;
+    a.K = d->top_k;
+    a.n_shared = d->n_shared;
+    bool any_pending = false;
+    if (pending_mask) {
+        for (int e = 0; e < d->n_experts; ++e)
+            if (pending_mask[e]) {
+                a.pend[e >> 5] |= 1u << (e & 31);
+                any_pending = true;
+            }
+    }
+    hipError_t e;
+    if (any_pending) {
+        a.pend_mode = 1;  // resident experts first
+        timing_before(KK_GATEUP, st);
+        e = launch_gateup(a, d->wbits, st);
+        timing_after(KK_GATEUP, st);
+        if (e != hipSuccess) return hip_fail(e, "gate/up launch");
+        if (pending_ready) {
+            e = hipStreamWaitEvent(st, static_cast<hipEvent_t>(pending_ready), 0);
+            if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+        }
+        a.pend_mode = 2;  // then the experts that were being staged
+    }
+    timing_before(KK_GATEUP, st);
+    e = launch_gateup(a, d->wbits, st);
+    timing_after(KK_GATEUP, st);
+    if (e != hipSuccess) return hip_fail(e, "gate/up launch");
+    timing_before(KK_DOWN, st);
+    e = launch_down(a, d->wbits, st);
+    timing_after(KK_DOWN, st);
+    if (e != hipSuccess) return hip_fail(e, "down/combine launch");
+    return COLI_OK;
+}
+
+int coli_moe_stage_experts(int32_t n, const void *const *host_src, void *const *dev_dst,
+                           size_t bytes_each, void *copy_stream, void *done_event) {
+    if (n < 0) return fail(COLI_EINVAL, "n=%d < 0", n);
+    if (n > 0 && (!host_src || !dev_dst)) return fail(COLI_EINVAL, "NULL pointer array");
+    for (int i = 0; i < n; ++i)
+        if (!host_src[i] || !dev_dst[i]) return fail(COLI_EINVAL, "NULL source or destination %d", i);
+    hipStream_t st = static_cast<hipStream_t>(copy_stream);
+    for (int i = 0; i < n; ++i) {
+        hipError_t e = hipMemcpyAsync(dev_dst[i], host_src[i], bytes_each, hipMemcpyHostToDevice, st);
+        if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync");
+    }
+    if (done_event) {
+        hipError_t e = hipEventRecord(static_cast<hipEvent_t>(done_event), st);
+        if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+    }
+    return COLI_OK;
+}
+
+int coli_moe_status(void *ws, void *stream) {
+    if (!ws) return fail(COLI_EINVAL, "workspace is NULL");
+    hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+    uint32_t s = 0;
+    e = hipMemcpy(&s, ws, sizeof s, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(e, "status read");
+    if (s == 0) return COLI_OK;
+    e = hipMemset(ws, 0, sizeof s);
+    if (e != hipSuccess) return hip_fail(e, "status clear");
+    if (s & ST_BADINDEX) return fail(COLI_EINVAL, "expert index out of range or repeated within a token (status 0x%x)", s);
+    if (s & ST_NONFINITE) return fail(COLI_ENONFINITE, "non-finite input or undefined gate weights (status 0x%x)", s);
+    return fail(COLI_ENOTRESIDENT, "a routed expert blob was NULL (status 0x%x)", s);
+}
+
+int coli_moe_timing_enable(int32_t enable) {
+    std::lock_guard<std::mutex> lk(g_timing.mu);
+    g_timing.on = enable != 0;
+    return COLI_OK;
+}
+
+int coli_moe_timing_read(int32_t kind, double *total_ms, int64_t *launches) {
+    if (kind < 0 || kind >= KK_COUNT || !total_ms || !launches)
+        return fail(COLI_EINVAL, "bad timing query");
+    std::lock_guard<std::mutex> lk(g_timing.mu);
+    double tot = 0.0;
+    int64_t n = 0;
+    for (auto &pr : g_timing.done[kind]) {
+        hipError_t e = hipEventSynchronize(pr.second);
+        if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+        float ms = 0.0f;
+        e = hipEventElapsedTime(&ms, pr.first, pr.second);
+        if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+        tot += ms;
+        ++n;
+        g_timing.free_events.push_back(pr.first);
+        g_timing.free_events.push_back(pr.second);
+    }
+    g_timing.done[kind].clear();
+    *total_ms = tot;
+    *launches = n;
+    return COLI_OK;
+}
+
+int coli_moe_debug_unpack(int32_t bits, int32_t n_rows, int32_t cols, const void *src, int8_t *out,
+                          void *stream) {
+    if ((bits != 8 && bits != 4 && bits != 2) || n_rows < 0 || cols <= 0 || cols % 32 || !src || !out)
+        return fail(COLI_EINVAL, "debug_unpack: bad arguments");
+    if (n_rows == 0) return COLI_OK;
+    int rc = check_device();
+    if (rc) return rc;
+    hipError_t e = launch_debug_unpack(bits, n_rows, cols, src, out, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? COLI_OK : hip_fail(e, "debug_unpack launch");
+}
+
+int coli_moe_debug_block_dots(int32_t bits, int32_t n_rows, int32_t cols, const void *src,
+                              const int8_t *q, int32_t *out, void *stream) {
+    if ((bits != 8 && bits != 4 && bits != 2) || n_rows < 0 || cols <= 0 || cols % 32 || !src || !q || !out)
+        return fail(COLI_EINVAL, "debug_block_dots: bad arguments");
+    if (n_rows == 0) return COLI_OK;
+    int rc = check_device();
+    if (rc) return rc;
+    hipError_t e = launch_debug_block_dots(bits, n_rows, cols, src, q, out, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? COLI_OK : hip_fail(e, "debug_block_dots launch");
+}
+
+int coli_moe_debug_logits(const coli_moe_dims *d, int32_t S, const float *x, const float *router_w,
+                          float *logits, void *stream) {
+    int rc = check_dims(d);
+    if (rc) return rc;
+    if (S < 0 || !x || !router_w || !logits) return fail(COLI_EINVAL, "debug_logits: bad arguments");
+    if (S == 0) return COLI_OK;
+    if ((rc = check_device())) return rc;
+    // no workspace here: the kernel skips its status report when given none
+    hipError_t e = launch_router_logits(x, router_w, logits, nullptr, S, d->hidden, d->n_experts,
+                                        static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? COLI_OK : hip_fail(e, "debug_logits launch");
+}
+
+int coli_moe_debug_expf(int64_t n, const float *x, float *y, void *stream) {
+    if (n < 0 || !x || !y) return fail(COLI_EINVAL, "debug_expf: bad arguments");
+    if (n == 0) return COLI_OK;
+    int rc = check_device();
+    if (rc) return rc;
+    hipError_t e = launch_debug_expf(n, x, y, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? COLI_OK : hip_fail(e, "debug_expf launch");
+}
+
+int coli_moe_debug_q8_0(int32_t n_rows, int32_t cols, const float *v, int8_t *q, float *d, void *stream) {
+    if (n_rows < 0 || cols <= 0 || cols % 32 || !v || !q || !d) return fail(COLI_EINVAL, "debug_q8_0: bad arguments");
+    if (n_rows == 0) return COLI_OK;
+    int rc = check_device();
+    if (rc) return rc;
+    hipError_t e = launch_debug_q8_0(n_rows, cols, v, q, d, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? COLI_OK : hip_fail(e, "debug_q8_0 launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,97 @@
+// Test hooks: thin kernels around the same device functions the forward
+// kernels use (packed-row unpacking and block dots, the exponential, Q8_0),
+// so their exact integer and binary32 results can be compared element by
+// element with the CPU oracle.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace coli {
+
+template <int BITS>
+__global__ __launch_bounds__(64) void k_debug_unpack(const uint8_t *__restrict__ src,
+                                                     int8_t *__restrict__ out, int cols) {
+    const int r = blockIdx.x;
+    const int nb = cols / 32;
+    const uint8_t *row = src + (size_t)r * cols * BITS / 8;
+    for (int b = threadIdx.x; b < nb; b += 64) {
+        const BlockBits<BITS> w = load_block<BITS>(row, b);
+#pragma unroll
+        for (int j = 0; j < 32; ++j) out[(size_t)r * cols + 32 * b + j] = block_code<BITS>(w, j);
+    }
+}
+
+template <int BITS>
+__global__ __launch_bounds__(64) void k_debug_block_dots(const uint8_t *__restrict__ src,
+                                                         const int8_t *__restrict__ q,
+                                                         int32_t *__restrict__ out, int cols) {
+    const int r = blockIdx.x;
+    const int nb = cols / 32;
+    const uint8_t *row = src + (size_t)r * cols * BITS / 8;
+    for (int b = threadIdx.x; b < nb; b += 64) {
+        const BlockBits<BITS> w = load_block<BITS>(row, b);
+        int32_t a[8];
+        for (int k = 0; k < 8; ++k) {
+            const int8_t *p = q + 32 * b + 4 * k;
+            a[k] = (int32_t)((uint32_t)(uint8_t)p[0] | ((uint32_t)(uint8_t)p[1] << 8) |
+                             ((uint32_t)(uint8_t)p[2] << 16) | ((uint32_t)(uint8_t)p[3] << 24));
+        }
+        out[(size_t)r * nb + b] = block_dot(w, a);
+    }
+}
+
+__global__ void k_debug_expf(const float *__restrict__ x, float *__restrict__ y, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) y[i] = exp_f32(x[i]);
+}
+
+// One wavefront per row; each half wave quantises one 32-element block.
+__global__ __launch_bounds__(64) void k_debug_q8_0(const float *__restrict__ v,
+                                                   int8_t *__restrict__ q, float *__restrict__ d,
+                                                   int cols) {
+    const int r = blockIdx.x;
+    const int lane = threadIdx.x;
+    for (int h0 = 0; h0 < cols; h0 += 64) {
+        const int h = h0 + lane;
+        if (h0 + (lane & 32) < cols) {  // whole half wave in or out
+            float dd;
+            const int8_t c = q8_0_lane(v[(size_t)r * cols + h], &dd);
+            q[(size_t)r * cols + h] = c;
+            if ((lane & 31) == 0) d[(size_t)r * (cols / 32) + (h >> 5)] = dd;
+        }
+    }
+}
+
+hipError_t launch_debug_unpack(int bits, int rows, int cols, const void *src, int8_t *out,
+                               hipStream_t st) {
+    const uint8_t *s = static_cast<const uint8_t *>(src);
+    if (bits == 8) hipLaunchKernelGGL(k_debug_unpack<8>, dim3(rows), dim3(64), 0, st, s, out, cols);
+    else if (bits == 4) hipLaunchKernelGGL(k_debug_unpack<4>, dim3(rows), dim3(64), 0, st, s, out, cols);
+    else hipLaunchKernelGGL(k_debug_unpack<2>, dim3(rows), dim3(64), 0, st, s, out, cols);
+    return hipGetLastError();
+}
+
+hipError_t launch_debug_block_dots(int bits, int rows, int cols, const void *src, const int8_t *q,
+                                   int32_t *out, hipStream_t st) {
+    const uint8_t *s = static_cast<const uint8_t *>(src);
+    if (bits == 8)
+        hipLaunchKernelGGL(k_debug_block_dots<8>, dim3(rows), dim3(64), 0, st, s, q, out, cols);
+    else if (bits == 4)
+        hipLaunchKernelGGL(k_debug_block_dots<4>, dim3(rows), dim3(64), 0, st, s, q, out, cols);
+    else
+        hipLaunchKernelGGL(k_debug_block_dots<2>, dim3(rows), dim3(64), 0, st, s, q, out, cols);
+    return hipGetLastError();
+}
+
+hipError_t launch_debug_expf(int64_t n, const float *x, float *y, hipStream_t st) {
+    const int64_t blocks = (n + 255) / 256;
+    hipLaunchKernelGGL(k_debug_expf, dim3((unsigned)blocks), dim3(256), 0, st, x, y, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_debug_q8_0(int rows, int cols, const float *v, int8_t *q, float *d,
+                             hipStream_t st) {
+    hipLaunchKernelGGL(k_debug_q8_0, dim3(rows), dim3(64), 0, st, v, q, d, cols);
+    return hipGetLastError();
+}
+
+}  // namespace coli

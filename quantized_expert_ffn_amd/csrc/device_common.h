@@ -1,0 +1,252 @@
+// Device building blocks shared by the MoE kernels and their test hooks.
+//
+// Floating point: this library is compiled with -ffp-contract=off and
+// correctly rounded binary32 division, so each expression below is exactly
+// the binary32 operation it spells, and every fused multiply-add is an
+// explicit __builtin_fmaf.  The operation orders are the layer's defined
+// orders (see the notes at each function); the integer parts are exact.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "coli_moe.h"
+
+namespace coli {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
+// ---- status word bits (first word of the workspace) ------------------------
+enum : uint32_t {
+    ST_NONFINITE = 1u,     // NaN/Inf in x, W_r, bias, logits or gate weights
+    ST_BADINDEX = 2u,      // expert index out of range or repeated in a token
+    ST_NOTRESIDENT = 4u,   // routed expert blob pointer is NULL
+};
+
+__device__ __forceinline__ void raise_status(uint32_t *status, uint32_t bit) {
+    // vector-memory atomic; the address is a plain global pointer
+    __hip_atomic_fetch_or(status, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ bool finite_f32(float v) {
+    return (__float_as_uint(v) & 0x7f800000u) != 0x7f800000u;
+}
+
+// ---- exponential -------------------------------------------------------
+// e^x by Cody-Waite reduction and the degree-7 Taylor polynomial of e^r
+// (Cody & Waite 1980): n = rint(x log2 e); r = x - n ln2_hi (exact under
+// fma) - n ln2_lo; p = Horner(1/k!, r); result p * 2^n, scaled in two steps
+// at the ends of the range.  Constants are the binary32 roundings of ln 2,
+// ln 2 - RN(ln 2), 1/ln 2 and 1/k!.  e^x rounds to +inf above 0x1.62e42ep+6
+// and to 0 below -0x1.9fe368p+6.
+__device__ __forceinline__ float pow2i(int n) {  // -126 <= n <= 127
+    return __uint_as_float((uint32_t)(n + 127) << 23);
+}
+
+__device__ __forceinline__ float exp_f32(float x) {
+    if (x != x) return x;
+    if (x > 0x1.62e42ep+6f) return __builtin_inff();
+    if (x < -0x1.9fe368p+6f) return 0.0f;
+    const float log2e = 0x1.715476p+0f;
+    const float ln2_hi = 0x1.62e430p-1f;
+    const float ln2_lo = -0x1.05c610p-29f;
+    const float t = x * log2e;
+    const float fn = __builtin_rintf(t);
+    float r = __builtin_fmaf(-fn, ln2_hi, x);
+    r = __builtin_fmaf(-fn, ln2_lo, r);
+    float p = (float)(1.0 / 5040.0);
+    p = __builtin_fmaf(p, r, (float)(1.0 / 720.0));
+    p = __builtin_fmaf(p, r, (float)(1.0 / 120.0));
+    p = __builtin_fmaf(p, r, (float)(1.0 / 24.0));
+    p = __builtin_fmaf(p, r, (float)(1.0 / 6.0));
+    p = __builtin_fmaf(p, r, 0.5f);
+    p = __builtin_fmaf(p, r, 1.0f);
+    p = __builtin_fmaf(p, r, 1.0f);
+    const int n = (int)fn;
+    if (n > 127) return (p * pow2i(127)) * pow2i(n - 127);
+    if (n < -126) return (p * pow2i(n + 64)) * pow2i(-64);
+    return p * pow2i(n);
+}
+
+// sigmoid(v) = 1 / (1 + e^-v), one correctly rounded division.
+__device__ __forceinline__ float sigmoid_f32(float v) { return 1.0f / (1.0f + exp_f32(-v)); }
+
+// SwiGLU: (g / (1 + e^-g)) * u.
+__device__ __forceinline__ float swiglu_f32(float g, float u) {
+    return (g / (1.0f + exp_f32(-g))) * u;
+}
+
+// ---- Q8_0 --------------------------------------------------------------
+// One 32-value block held by 32 consecutive lanes (a half wavefront): every
+// lane passes its value and gets its code; *d receives the block scale.
+// d = amax / 127, q = clamp(round-half-away(v / d), +-127), q = 0 if d == 0.
+__device__ __forceinline__ int8_t q8_0_lane(float v, float *d_out) {
+    float a = __builtin_fabsf(v);
+#pragma unroll
+    for (int o = 16; o >= 1; o >>= 1) a = __builtin_fmaxf(a, __shfl_xor(a, o, 64));
+    const float d = a / 127.0f;
+    *d_out = d;
+    float c = 0.0f;
+    if (d != 0.0f) {
+        c = __builtin_roundf(v / d);
+        c = __builtin_fminf(__builtin_fmaxf(c, -127.0f), 127.0f);
+    }
+    return (int8_t)(int)c;
+}
+
+// ---- packed rows: exact block dot products -----------------------------
+// A "block" is 32 consecutive codes of a row: 32 bytes (int8), 16 (int4) or
+// 8 (int2).  Activation codes arrive as 8 little-endian int32 words holding
+// the block's 32 int8 values in order.
+//
+// int4: byte j of the block holds code j in bits 0-3 and code j+16 in bits
+// 4-7.  Masking a nibble into the top half of its byte gives 16*code as a
+// signed byte, so four codes feed one v_dot4 with no sign extension; the sum
+// is then exactly divisible by 16.
+__device__ __forceinline__ int32_t block_dot_int4(u32x4 w, const int32_t a[8]) {
+    int32_t s = 0;
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const uint32_t lo = (ws[k] << 4) & 0xF0F0F0F0u;   // codes 4k..4k+3, x16
+        const uint32_t hi = ws[k] & 0xF0F0F0F0u;          // codes 16+4k.., x16
+        s = __builtin_amdgcn_sdot4((int)lo, a[k], s, false);
+        s = __builtin_amdgcn_sdot4((int)hi, a[4 + k], s, false);
+    }
+    return s >> 4;
+}
+
+// int2: byte j (of 8) holds code j+8i in bits 2i..2i+1.  Shifting field i
+// into the top two bits of each byte gives 64*code as a signed byte.
+// Word m (bytes 4m..4m+3) field i covers codes 8i+4m..8i+4m+3.
+__device__ __forceinline__ int32_t block_dot_int2(u32x2 w, const int32_t a[8]) {
+    int32_t s = 0;
+    const uint32_t ws[2] = {w.x, w.y};
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t f = (ws[m] << (6 - 2 * i)) & 0xC0C0C0C0u;
+            s = __builtin_amdgcn_sdot4((int)f, a[2 * i + m], s, false);
+        }
+    return s >> 6;
+}
+
+// int8: 32 codes in 8 words.
+__device__ __forceinline__ int32_t block_dot_int8(u32x4 w0, u32x4 w1, const int32_t a[8]) {
+    int32_t s = 0;
+    s = __builtin_amdgcn_sdot4((int)w0.x, a[0], s, false);
+    s = __builtin_amdgcn_sdot4((int)w0.y, a[1], s, false);
+    s = __builtin_amdgcn_sdot4((int)w0.z, a[2], s, false);
+    s = __builtin_amdgcn_sdot4((int)w0.w, a[3], s, false);
+    s = __builtin_amdgcn_sdot4((int)w1.x, a[4], s, false);
+    s = __builtin_amdgcn_sdot4((int)w1.y, a[5], s, false);
+    s = __builtin_amdgcn_sdot4((int)w1.z, a[6], s, false);
+    s = __builtin_amdgcn_sdot4((int)w1.w, a[7], s, false);
+    return s;
+}
+
+// Raw bytes of one block of a packed row, as loaded by one lane.
+template <int BITS>
+struct BlockBits;
+template <>
+struct BlockBits<8> {
+    u32x4 w0, w1;
+};
+template <>
+struct BlockBits<4> {
+    u32x4 w;
+};
+template <>
+struct BlockBits<2> {
+    u32x2 w;
+};
+
+// Weight rows live in global memory; loading through global-address-space
+// pointers gives global_load (not flat) instructions, marked non-temporal
+// because every weight byte is used once per call.
+typedef __attribute__((address_space(1))) const u32x4 g_u32x4;
+typedef __attribute__((address_space(1))) const u32x2 g_u32x2;
+
+template <int BITS>
+__device__ __forceinline__ BlockBits<BITS> load_block(const uint8_t *row, int b);
+
+template <>
+__device__ __forceinline__ BlockBits<8> load_block<8>(const uint8_t *row, int b) {
+    g_u32x4 *p = (g_u32x4 *)(row + 32 * b);
+    BlockBits<8> r;
+    r.w0 = __builtin_nontemporal_load(p);
+    r.w1 = __builtin_nontemporal_load(p + 1);
+    return r;
+}
+template <>
+__device__ __forceinline__ BlockBits<4> load_block<4>(const uint8_t *row, int b) {
+    BlockBits<4> r;
+    r.w = __builtin_nontemporal_load((g_u32x4 *)(row + 16 * b));
+    return r;
+}
+template <>
+__device__ __forceinline__ BlockBits<2> load_block<2>(const uint8_t *row, int b) {
+    BlockBits<2> r;
+    r.w = __builtin_nontemporal_load((g_u32x2 *)(row + 8 * b));
+    return r;
+}
+
+__device__ __forceinline__ int32_t block_dot(const BlockBits<8> &w, const int32_t a[8]) {
+    return block_dot_int8(w.w0, w.w1, a);
+}
+__device__ __forceinline__ int32_t block_dot(const BlockBits<4> &w, const int32_t a[8]) {
+    return block_dot_int4(w.w, a);
+}
+__device__ __forceinline__ int32_t block_dot(const BlockBits<2> &w, const int32_t a[8]) {
+    return block_dot_int2(w.w, a);
+}
+
+// Codes of one block (test hook for the unpacking): code j of the block.
+template <int BITS>
+__device__ __forceinline__ int8_t block_code(const BlockBits<BITS> &w, int j);
+template <>
+__device__ __forceinline__ int8_t block_code<8>(const BlockBits<8> &w, int j) {
+    const uint32_t ws[8] = {w.w0.x, w.w0.y, w.w0.z, w.w0.w, w.w1.x, w.w1.y, w.w1.z, w.w1.w};
+    return (int8_t)(ws[j >> 2] >> (8 * (j & 3)));
+}
+template <>
+__device__ __forceinline__ int8_t block_code<4>(const BlockBits<4> &w, int j) {
+    const uint32_t ws[4] = {w.w.x, w.w.y, w.w.z, w.w.w};
+    const int byte = j & 15;
+    const uint32_t word = ws[byte >> 2];
+    const uint32_t v = (j < 16) ? (word << 4) & 0xF0F0F0F0u : word & 0xF0F0F0F0u;
+    return (int8_t)((int8_t)(v >> (8 * (byte & 3))) >> 4);
+}
+template <>
+__device__ __forceinline__ int8_t block_code<2>(const BlockBits<2> &w, int j) {
+    const int byte = j & 7, i = j >> 3;
+    const uint32_t word = (byte < 4) ? w.w.x : w.w.y;
+    const uint32_t f = (word << (6 - 2 * i)) & 0xC0C0C0C0u;
+    return (int8_t)((int8_t)(f >> (8 * (byte & 3))) >> 6);
+}
+
+// ---- misc --------------------------------------------------------------
+__host__ __device__ constexpr size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+struct BlobLayout {
+    size_t gate, up, down, s_gate, s_up, s_down, total;
+};
+
+__host__ __device__ inline BlobLayout blob_layout(int H, int I, int bits) {
+    BlobLayout L;
+    const size_t gate = (size_t)I * (size_t)H * (size_t)bits / 8;
+    const size_t down = (size_t)H * (size_t)I * (size_t)bits / 8;
+    L.gate = 0;
+    L.up = align256(L.gate + gate);
+    L.down = align256(L.up + gate);
+    L.s_gate = align256(L.down + down);
+    L.s_up = align256(L.s_gate + 4 * (size_t)I);
+    L.s_down = align256(L.s_up + 4 * (size_t)I);
+    L.total = align256(L.s_down + 4 * (size_t)H);
+    return L;
+}
+
+}  // namespace coli

@@ -1,0 +1,79 @@
+// Private interface between the C-ABI entry points and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace coli {
+
+// Workspace carve-up for a call with S tokens.  status and counters sit at
+// fixed offsets (they persist between calls); the rest is per call.
+struct WsLayout {
+    size_t status, counters, logits, qh, dh, Y, total;
+};
+
+inline size_t al256h(size_t v) { return (v + 255) & ~(size_t)255; }
+
+inline WsLayout ws_layout(int H, int I, int E, int K, int S) {
+    WsLayout L;
+    const size_t slots = (size_t)S * (size_t)(K + 1);
+    L.status = 0;
+    L.counters = 256;
+    L.logits = al256h(L.counters + 4 * (size_t)(H / 64 + 1));
+    L.qh = al256h(L.logits + 4 * (size_t)S * (size_t)E);
+    L.dh = al256h(L.qh + slots * (size_t)I);
+    L.Y = al256h(L.dh + 4 * slots * (size_t)(I / 32));
+    L.total = al256h(L.Y + 4 * slots * (size_t)H);
+    return L;
+}
+
+// Arguments of the forward kernels (passed by value).
+struct FwdArgs {
+    const float *x;                // [S, H]
+    const int32_t *idx;            // [S, K]
+    const float *w;                // [S, K]
+    const uint8_t *const *blobs;   // device array [E]
+    const uint8_t *shared;         // shared expert blob or null
+    int8_t *qh;                    // [S*(K+1), I]   Q8_0(h) codes per pair slot
+    float *dh;                     // [S*(K+1), I/32]
+    float *Y;                      // [S*(K+1), H]   expert outputs per pair slot
+    uint32_t *counters;            // [H/64] arrival counters of the down row tiles
+    float *out;                    // [S, H]
+    uint32_t *status;
+    int S, H, I, E, K, n_shared;
+    int pend_mode;                 // 0: all units, 1: skip pending experts, 2: only pending
+    uint32_t pend[32];             // bit e: expert e pending
+};
+
+hipError_t launch_router_logits(const float *x, const float *W, float *logits, uint32_t *status,
+                                int S, int H, int E, hipStream_t st);
+hipError_t launch_router_select(const float *logits, const float *bias, int32_t *idx, float *w,
+                                uint32_t *status, int S, int E, int K, float rsf, int norm,
+                                hipStream_t st);
+
+// Kernel kinds for timing.
+enum KernelKind {
+    KK_ROUTER_LOGITS = 0,
+    KK_ROUTER_SELECT = 1,
+    KK_GATEUP = 2,
+    KK_DOWN = 3,
+    KK_COUNT = 8
+};
+
+// Timing hooks implemented by the API layer.
+void timing_before(int kind, hipStream_t st);
+void timing_after(int kind, hipStream_t st);
+
+hipError_t launch_gateup(const FwdArgs &a, int bits, hipStream_t st);
+hipError_t launch_down(const FwdArgs &a, int bits, hipStream_t st);
+size_t forward_smem_max(int S, int H, int I, int E, int K, int n_shared);
+
+hipError_t launch_debug_unpack(int bits, int rows, int cols, const void *src, int8_t *out,
+                               hipStream_t st);
+hipError_t launch_debug_block_dots(int bits, int rows, int cols, const void *src, const int8_t *q,
+                                   int32_t *out, hipStream_t st);
+hipError_t launch_debug_expf(int64_t n, const float *x, float *y, hipStream_t st);
+hipError_t launch_debug_q8_0(int rows, int cols, const float *v, int8_t *q, float *d,
+                             hipStream_t st);
+
+}  // namespace coli

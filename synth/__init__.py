@@ -359,3 +359,42 @@ def tiny_layer(seed: int = 0, S: int = 4, spec: LayerSpec = TINY, layer: int = 0
         "blobs": blobs[:spec.n_experts],
         "shared": blobs[spec.n_experts] if spec.n_shared else None,
     }
+
+
+def layer_inputs(seed: int, layer: int, spec: LayerSpec, S: int, x_stream: int = 0) -> dict:
+    """Hidden states, router gate and bias of one layer (blobs not included:
+    use expert_blob / cdf_expert_into for the experts that are needed)."""
+    return {
+        "spec": spec,
+        "x": hidden_states(seed, layer, S, spec.hidden, x_stream),
+        "router_w": router_weights(seed, layer, spec),
+        "bias": router_bias(seed, layer, spec),
+    }
+
+
+def verify_hidden_states(seed: int, layer: int, spec: LayerSpec, S: int, union_frac: float = 0.6) -> np.ndarray:
+    """Hidden states of S tokens that share experts: x_t = sqrt(rho) c +
+    sqrt(1 - rho) n_t with a common direction c, rho bisected so that the
+    top-K sets of the logits W_r x_t cover about union_frac * S * K distinct
+    experts.  Uses float64 logits and a sort only (bias ignored); the realised
+    union of the actual router is reported by whoever routes these tokens."""
+    W = router_weights(seed, layer, spec).astype(np.float64)
+    H, K = spec.hidden, spec.top_k
+    c = normal(stream_key(seed, K_ROUTING, layer, 100), H)
+    n = normal(stream_key(seed, K_ROUTING, layer, 101), S * H).reshape(S, H)
+
+    def make(rho):
+        return math.sqrt(rho) * c[None, :] + math.sqrt(1.0 - rho) * n
+
+    def union(rho):
+        top = np.argsort(-(make(rho) @ W.T), axis=1, kind="stable")[:, :K]
+        return len(set(top.ravel().tolist())) / (S * K)
+
+    lo, hi = 0.0, 1.0
+    for _ in range(40):
+        mid = 0.5 * (lo + hi)
+        if union(mid) > union_frac:
+            lo = mid
+        else:
+            hi = mid
+    return make(hi).astype(np.float32)

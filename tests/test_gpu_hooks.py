@@ -1,0 +1,107 @@
+"""GPU parity of the building blocks, through the C-ABI test hooks that run
+the production device functions: packed-row unpacking and int32 block dots
+(bit-exact), the exponential, Q8_0 and router logits (bit-exact binary32)."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.gpu_util import q, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as t
+    assert t.cuda.is_available(), "no GPU visible"
+    return t
+
+
+@pytest.mark.parametrize("bits", [8, 4, 2])
+@pytest.mark.parametrize("cols", [32, 96, 2048, 6144])
+def test_unpack_bitexact(torch, bits, cols):
+    say(f"unpack bits={bits} cols={cols}")
+    lo, hi = {8: (-128, 127), 4: (-8, 7), 2: (-2, 1)}[bits]
+    rng = np.random.default_rng(bits * 1000 + cols)
+    rows = 37
+    codes = rng.integers(lo, hi + 1, size=(rows, cols)).astype(np.int8)
+    codes[0, :] = np.resize(np.arange(lo, hi + 1), cols)
+    packed = synth.pack_codes(codes, bits)
+    src = torch.from_numpy(packed).cuda()
+    out = torch.empty((rows, cols), dtype=torch.int8, device="cuda")
+    q().coli_moe_debug_unpack(bits, rows, cols, src, out)
+    got = out.cpu().numpy()
+    want = np.stack([oracle.unpack(packed[r], cols, bits) for r in range(rows)])
+    assert np.array_equal(got, want)
+    assert np.array_equal(got, codes)
+
+
+@pytest.mark.parametrize("bits", [8, 4, 2])
+def test_block_dots_bitexact(torch, bits):
+    say(f"block dots bits={bits}")
+    lo, hi = {8: (-128, 127), 4: (-8, 7), 2: (-2, 1)}[bits]
+    rng = np.random.default_rng(50 + bits)
+    rows, cols = 64, 6144
+    codes = rng.integers(lo, hi + 1, size=(rows, cols)).astype(np.int8)
+    codes[1, :] = lo
+    qv = rng.integers(-127, 128, size=cols).astype(np.int8)
+    qv[:32] = -127
+    packed = synth.pack_codes(codes, bits)
+    out = torch.empty((rows, cols // 32), dtype=torch.int32, device="cuda")
+    q().coli_moe_debug_block_dots(bits, rows, cols, torch.from_numpy(packed).cuda(),
+                                  torch.from_numpy(qv).cuda(), out)
+    got = out.cpu().numpy()
+    for r in range(rows):
+        cr = oracle.unpack(packed[r], cols, bits)
+        want = [oracle.block_isum(cr[32 * b:32 * b + 32], qv[32 * b:32 * b + 32]) for b in range(cols // 32)]
+        assert got[r].tolist() == want
+
+
+def test_expf_bitexact_on_sweep(torch):
+    say("expf sweep")
+    bits = np.arange(-2 ** 31, 2 ** 31, 211, dtype=np.int64).astype(np.int32)
+    x = bits.view(np.float32)
+    x = np.concatenate([x[np.isfinite(x) & (np.abs(x) < 110)],
+                        np.float32([0.0, -0.0, np.inf, -np.inf, 88.72283172607422, 88.72283935546875,
+                                    -103.97207641601562, -103.97208404541016, -87.5, -100.0])])
+    xd = torch.from_numpy(x).cuda()
+    yd = torch.empty_like(xd)
+    q().coli_moe_debug_expf(xd, yd)
+    got = yd.cpu().numpy()
+    want = oracle.expf(x)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+def test_q8_0_bitexact(torch):
+    say("q8_0")
+    rng = np.random.default_rng(9)
+    v = (rng.normal(size=(64, 2048)) * rng.lognormal(size=(64, 1)) * 3).astype(np.float32)
+    v[0, :32] = 0.0                     # zero block
+    v[1, :32] = 0.5                     # constant block
+    v[2, :32] = np.float32(1e-40)       # denormal block
+    v[3, 5] = 127.0
+    v[3, 6:10] = [2.5, -2.5, 0.5, -0.5]  # half-way codes (amax 127 -> d = 1)
+    v[3, :5] = 0.0
+    v[3, 10:32] = 0.0
+    vd = torch.from_numpy(v).cuda()
+    qd = torch.empty((64, 2048), dtype=torch.int8, device="cuda")
+    dd = torch.empty((64, 64), dtype=torch.float32, device="cuda")
+    q().coli_moe_debug_q8_0(vd, qd, dd)
+    wq, wd = oracle.q8_0(v)
+    assert np.array_equal(qd.cpu().numpy(), wq)
+    assert np.array_equal(dd.cpu().numpy().view(np.uint32), wd.view(np.uint32))
+
+
+@pytest.mark.parametrize("spec", [synth.TINY, synth.GLM], ids=["tiny", "glm"])
+def test_router_logits_bitexact(torch, spec):
+    say(f"logits H={spec.hidden} E={spec.n_experts}")
+    d = synth.layer_inputs(3, 0, spec, 4)
+    x, W = d["x"], d["router_w"]
+    logits = torch.empty((4, spec.n_experts), dtype=torch.float32, device="cuda")
+    q().coli_moe_debug_logits(q().make_dims(spec), torch.from_numpy(x).cuda(), torch.from_numpy(W).cuda(), logits)
+    got = logits.cpu().numpy()
+    es = range(spec.n_experts) if spec.n_experts <= 16 else range(0, spec.n_experts, 7)
+    for t in range(4):
+        for e in es:
+            assert got[t, e].view(np.uint32) == oracle.router_logit(x[t], W[e]).view(np.uint32), (t, e)

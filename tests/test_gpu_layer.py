@@ -1,0 +1,289 @@
+"""GPU parity of the whole layer through the C ABI (coli_moe_route,
+coli_moe_forward, coli_moe_stage_experts) against the CPU oracle on the same
+seeded inputs: bit-exact routing, binary32 outputs within rel-L2 1e-5 and
+max-abs 1e-3 x RMS (and, by the layer's fixed operation order, bit-exact)."""
+import dataclasses
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.gpu_util import gpu_forward, gpu_route, parity, q, say, status, workspace
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as t
+    assert t.cuda.is_available(), "no GPU visible"
+    return t
+
+
+def _layer(spec, S, seed=0):
+    d = synth.tiny_layer(seed=seed, S=S, spec=spec)
+    return d
+
+
+def _run(torch, spec, d, S=None, dev=None):
+    from synth.device import upload_layer
+    dims = q().make_dims(spec)
+    dl = upload_layer(d) if dev is None else dev
+    S = d["x"].shape[0] if S is None else S
+    ws = workspace(dims, S)
+    idx, w = gpu_route(dims, dl, ws)
+    out = gpu_forward(dims, dl, idx, w, ws)
+    rc = status(ws)
+    return dims, dl, ws, idx.cpu().numpy(), w.cpu().numpy(), out.cpu().numpy(), rc
+
+
+def _oracle(spec, d):
+    out, idx, w = oracle.layer(spec, d["x"], d["router_w"], d["bias"], d["blobs"], d["shared"])
+    return out, idx, w
+
+
+def test_tiny_layer_bitexact(torch):
+    say("tiny layer S=4 int4")
+    spec = synth.TINY
+    d = _layer(spec, 4)
+    _, _, _, idx, w, out, rc = _run(torch, spec, d)
+    assert rc == 0, q().coli_moe_last_error()
+    o_out, o_idx, o_w = _oracle(spec, d)
+    assert np.array_equal(idx, o_idx)
+    assert np.array_equal(w.view(np.uint32), o_w.view(np.uint32))
+    parity(out, o_out)
+
+
+@pytest.mark.parametrize("S", [1, 2, 3, 5, 9, 17])
+def test_tiny_ragged_token_counts(torch, S):
+    say(f"tiny layer S={S}")
+    spec = synth.TINY
+    d = _layer(spec, S, seed=S)
+    _, _, _, idx, w, out, rc = _run(torch, spec, d)
+    assert rc == 0, q().coli_moe_last_error()
+    o_out, o_idx, o_w = _oracle(spec, d)
+    assert np.array_equal(idx, o_idx)
+    parity(out, o_out)
+
+
+@pytest.mark.parametrize("spec", [
+    dataclasses.replace(synth.TINY, wbits=8),
+    dataclasses.replace(synth.TINY, wbits=2),
+    dataclasses.replace(synth.TINY, top_k=1, n_shared=0, routed_scaling_factor=1.0),
+    dataclasses.replace(synth.TINY, n_experts=40, top_k=6, hidden=512, inter=96),
+    dataclasses.replace(synth.TINY, norm_topk_prob=0, routed_scaling_factor=1.5, n_experts=70, top_k=9),
+], ids=["int8", "int2", "k1-noshared", "e40-h512-i96", "nonorm-e70-k9"])
+def test_tiny_variants(torch, spec):
+    say(f"tiny variant {spec}")
+    d = _layer(spec, 5, seed=11)
+    _, _, _, idx, w, out, rc = _run(torch, spec, d)
+    assert rc == 0, q().coli_moe_last_error()
+    o_out, o_idx, o_w = _oracle(spec, d)
+    assert np.array_equal(idx, o_idx)
+    assert np.array_equal(w.view(np.uint32), o_w.view(np.uint32))
+    parity(out, o_out)
+
+
+def test_batch_invariance(torch):
+    """A token's output bits do not depend on which other tokens share the call."""
+    say("batch invariance")
+    from synth.device import upload_layer
+    spec = synth.TINY
+    d = _layer(spec, 6, seed=21)
+    dims = q().make_dims(spec)
+    dl = upload_layer(d)
+    ws = workspace(dims, 6)
+    idx, w = gpu_route(dims, dl, ws)
+    full = gpu_forward(dims, dl, idx, w, ws).cpu().numpy()
+    for t in range(6):
+        one = dict(dl)
+        one["x"] = dl["x"][t:t + 1].contiguous()
+        o = gpu_forward(dims, one, idx[t:t + 1].contiguous(), w[t:t + 1].contiguous(), ws).cpu().numpy()
+        assert np.array_equal(o[0].view(np.uint32), full[t].view(np.uint32))
+    assert status(ws) == 0
+
+
+def _one_hot_router(torch, logits_rows, K, bias=None):
+    """Routes tokens whose logits are given exactly: W_r rows are one-hot and
+    x carries the logits (the binary32 logit of a one-hot row is exact)."""
+    lg = np.asarray(logits_rows, np.float32)
+    S, E = lg.shape
+    spec = dataclasses.replace(synth.TINY, n_experts=E, top_k=K, routed_scaling_factor=1.0)
+    x = np.zeros((S, spec.hidden), np.float32)
+    x[:, :E] = lg
+    W = np.zeros((E, spec.hidden), np.float32)
+    W[np.arange(E), np.arange(E)] = 1.0
+    b = np.zeros(E, np.float32) if bias is None else np.asarray(bias, np.float32)
+    dims = q().make_dims(spec)
+    dl = {"x": torch.from_numpy(x).cuda(), "router_w": torch.from_numpy(W).cuda(), "bias": torch.from_numpy(b).cuda()}
+    ws = workspace(dims, S)
+    idx, w = gpu_route(dims, dl, ws)
+    return idx.cpu().numpy(), w.cpu().numpy(), status(ws)
+
+
+def test_router_worked_examples_through_the_abi(torch):
+    import json
+    import os
+    say("router worked examples")
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "router_worked_examples.json")))
+    ex = g["tie_break"]
+    idx, _, rc = _one_hot_router(torch, [ex["logits"]], ex["top_k"], ex["bias"])
+    assert rc == 0
+    assert sorted(idx[0].tolist()) == ex["expected_sorted_set"] and idx[0, -1] == ex["expected_last"]
+    ex = g["near_tie"]
+    lg = np.array(ex["logits"], np.float64)
+    nudged = lg.copy()
+    nudged[ex["nudge_expert"]] += ex["nudge"]
+    idx, _, rc = _one_hot_router(torch, [lg, nudged], ex["top_k"], ex["bias"])
+    assert rc == 0
+    assert idx[0, -1] == ex["expected_last_before"] and idx[1, -1] == ex["expected_last_after"]
+    bad = np.zeros((1, 8), np.float32)
+    bad[0, 3] = np.nan
+    _, _, rc = _one_hot_router(torch, bad, 5)
+    assert rc == q().COLI_ENONFINITE
+
+
+def test_error_contract(torch):
+    say("error contract")
+    from synth.device import upload_layer
+    qm = q()
+    spec = synth.TINY
+    d = _layer(spec, 4, seed=5)
+    dims = qm.make_dims(spec)
+    dl = upload_layer(d)
+    ws = workspace(dims, 4)
+    idx, w = gpu_route(dims, dl, ws)
+    assert status(ws) == 0
+    # non-finite hidden state
+    dl2 = dict(dl)
+    dl2["x"] = dl["x"].clone()
+    dl2["x"][1, 3] = float("nan")
+    gpu_forward(dims, dl2, idx, w, ws)
+    assert status(ws) == qm.COLI_ENONFINITE
+    gpu_route(dims, dl2, ws)
+    assert status(ws) == qm.COLI_ENONFINITE
+    # routed expert not resident
+    table = dl["table"].clone()
+    table[int(idx[0, 0])] = 0
+    dl3 = dict(dl)
+    dl3["table"] = table
+    gpu_forward(dims, dl3, idx, w, ws)
+    assert status(ws) == qm.COLI_ENOTRESIDENT
+    # index out of range, repeated index
+    i2 = idx.clone()
+    i2[2, 1] = spec.n_experts
+    gpu_forward(dims, dl, i2, w, ws)
+    assert status(ws) == qm.COLI_EINVAL
+    i3 = idx.clone()
+    i3[3, 1] = i3[3, 0]
+    gpu_forward(dims, dl, i3, w, ws)
+    assert status(ws) == qm.COLI_EINVAL
+    # status cleared, normal call fine again
+    gpu_forward(dims, dl, idx, w, ws)
+    assert status(ws) == 0
+    # host-side checks
+    small = ws[: 1024]
+    with pytest.raises(qm.ColiError) as e:
+        gpu_forward(dims, dl, idx, w, small)
+    assert e.value.code == qm.COLI_EWORKSPACE
+    bad = qm.make_dims(spec)
+    bad.wbits = 3
+    with pytest.raises(qm.ColiError) as e:
+        gpu_route(bad, dl, ws)
+    assert e.value.code == qm.COLI_EINVAL
+    # zero tokens: no-op
+    empty = dict(dl)
+    empty["x"] = dl["x"][:0]
+    o = gpu_forward(dims, empty, idx[:0], w[:0], ws)
+    assert o.shape == (0, spec.hidden) and status(ws) == 0
+
+
+def test_pending_experts_run_after_the_event(torch):
+    say("pending mask")
+    from synth.device import upload_layer
+    spec = synth.TINY
+    d = _layer(spec, 4, seed=8)
+    dims = q().make_dims(spec)
+    dl = upload_layer(d)
+    ws = workspace(dims, 4)
+    idx, w = gpu_route(dims, dl, ws)
+    ref = gpu_forward(dims, dl, idx, w, ws).cpu().numpy()
+    mask = np.zeros(spec.n_experts, np.uint8)
+    mask[idx[0].cpu().numpy()] = 1
+    ev = torch.cuda.Event()
+    ev.record()
+    out = gpu_forward(dims, dl, idx, w, ws, pending_mask=mask, pending_ready=ev).cpu().numpy()
+    assert status(ws) == 0
+    assert np.array_equal(out.view(np.uint32), ref.view(np.uint32))
+
+
+def test_stage_experts_copies_bytes(torch):
+    say("stage experts")
+    spec = synth.TINY
+    n = 5
+    host = [torch.from_numpy(synth.gaussian_expert(2, 0, e, spec)[0]).pin_memory() for e in range(n)]
+    dev = [torch.empty(spec.blob_bytes, dtype=torch.uint8, device="cuda") for _ in range(n)]
+    s = torch.cuda.Stream()
+    ev = torch.cuda.Event()
+    q().coli_moe_stage_experts(host, dev, spec.blob_bytes, s, ev)
+    ev.synchronize()
+    for h, dv in zip(host, dev):
+        assert torch.equal(h, dv.cpu())
+
+
+def _glm_layer_for_tokens(torch, spec, S, seed, x=None, layer=0):
+    """GLM-shaped layer with only the experts the tokens route to resident."""
+    from synth.device import blob_table
+    d = synth.layer_inputs(seed, layer, spec, S)
+    if x is not None:
+        d["x"] = x
+    dims = q().make_dims(spec)
+    dl = {"x": torch.from_numpy(d["x"]).cuda(), "router_w": torch.from_numpy(d["router_w"]).cuda(),
+          "bias": torch.from_numpy(d["bias"]).cuda()}
+    ws = workspace(dims, S)
+    idx, w = gpu_route(dims, dl, ws)
+    assert status(ws) == 0
+    used = sorted(set(idx.cpu().numpy().ravel().tolist()))
+    host = {e: synth.expert_blob(seed, layer, e, spec) for e in used}
+    shared = synth.expert_blob(seed, layer, spec.n_experts, spec)
+    blobs = [torch.from_numpy(host[e]).cuda() if e in host else None for e in range(spec.n_experts)]
+    dl["blobs"] = blobs
+    dl["table"] = blob_table(blobs, spec.n_experts)
+    dl["shared"] = torch.from_numpy(shared).cuda()
+    d["blobs"] = [host.get(e) for e in range(spec.n_experts)]
+    d["shared"] = shared
+    return d, dims, dl, ws, idx, w, used
+
+
+def test_glm_decode_one_token(torch):
+    """GLM-5.2-shaped decode layer (H 6144, I 2048, 256 experts top-8 + shared,
+    int4, 1 token) in the launch configuration the benchmark times."""
+    say("glm decode S=1 int4")
+    spec = synth.GLM
+    d, dims, dl, ws, idx, w, used = _glm_layer_for_tokens(torch, spec, 1, seed=0)
+    o_idx, o_w, _, _ = oracle.route(spec, d["x"], d["router_w"], d["bias"])
+    assert np.array_equal(idx.cpu().numpy(), o_idx)
+    assert np.array_equal(w.cpu().numpy().view(np.uint32), o_w.view(np.uint32))
+    out = gpu_forward(dims, dl, idx, w, ws).cpu().numpy()
+    assert status(ws) == 0
+    want = oracle.forward(spec, d["x"], o_idx, o_w, d["blobs"], d["shared"])
+    r = parity(out, want)
+    say("glm decode parity", r)
+
+
+def test_glm_verify_four_tokens_int8(torch):
+    """Speculative-verify batch: S=4 tokens routed jointly, int8 experts,
+    tokens sharing experts (batch-union)."""
+    say("glm verify S=4 int8")
+    spec = synth.GLM_INT8
+    x = synth.verify_hidden_states(0, 0, spec, 4)
+    d, dims, dl, ws, idx, w, used = _glm_layer_for_tokens(torch, spec, 4, seed=0, x=x)
+    say("unique experts", len(used))
+    assert len(used) < 32
+    o_idx, o_w, _, _ = oracle.route(spec, d["x"], d["router_w"], d["bias"])
+    assert np.array_equal(idx.cpu().numpy(), o_idx)
+    out = gpu_forward(dims, dl, idx, w, ws).cpu().numpy()
+    assert status(ws) == 0
+    want = oracle.forward(spec, d["x"], o_idx, o_w, d["blobs"], d["shared"])
+    parity(out, want)
