@@ -123,10 +123,12 @@ def main():
         step(s)
     torch.cuda.synchronize()
     q.coli_moe_timing_enable(False)
-    kt = {k: q.coli_moe_timing_read(k) for k in (q.KIND_ROUTER_LOGITS, q.KIND_ROUTER_SELECT,
-                                                 q.KIND_GATEUP, q.KIND_DOWN)}
-    kernel_us = {name: 1e3 * kt[k][0] / max(kt[k][1], 1) for name, k in
-                 (("router_logits", 0), ("router_select", 1), ("gateup", 2), ("down_combine", 3))}
+    kinds = (("router_logits", q.KIND_ROUTER_LOGITS), ("router_select", q.KIND_ROUTER_SELECT),
+             ("gateup", q.KIND_GATEUP), ("down", q.KIND_DOWN), ("combine", q.KIND_COMBINE))
+    kernel_us = {}
+    for name, k in kinds:
+        ms, n = q.coli_moe_timing_read(k)
+        kernel_us[name] = 1e3 * ms / max(n, 1)
 
     # captured steps
     graph = torch.cuda.CUDAGraph()

@@ -141,9 +141,8 @@ const char *coli_moe_last_error(void);
  * Kernel timing.  While enabled, every kernel launched by the library is
  * bracketed by events on its stream; coli_moe_timing_read() synchronises the
  * recorded events and returns the accumulated milliseconds and launch count
- * of one kernel kind (0 router logits, 1 router select, 2 gate/up,
- * 3 down/combine, 4 prefill gate/up, 5 prefill down, 6 prefill combine,
- * 7 prefill grouping), then resets that kind.  For measurement only.
+ * of one kernel kind (0 router logits, 1 router select, 2 gate/up, 3 down,
+ * 4 combine), then resets that kind.  For measurement only.
  */
 int coli_moe_timing_enable(int32_t enable);
 int coli_moe_timing_read(int32_t kind, double *total_ms, int64_t *launches);

@@ -30,7 +30,7 @@ EXPORTS = (
     "coli_moe_debug_logits", "coli_moe_debug_expf", "coli_moe_debug_q8_0",
 )
 
-KIND_ROUTER_LOGITS, KIND_ROUTER_SELECT, KIND_GATEUP, KIND_DOWN = 0, 1, 2, 3
+KIND_ROUTER_LOGITS, KIND_ROUTER_SELECT, KIND_GATEUP, KIND_DOWN, KIND_COMBINE = 0, 1, 2, 3, 4
 
 
 class coli_moe_dims(ctypes.Structure):

@@ -185,7 +185,6 @@ int coli_moe_forward(const coli_moe_dims *d, int32_t S, const float *x, const in
     a.qh = reinterpret_cast<int8_t *>(w8 + L.qh);
     a.dh = reinterpret_cast<float *>(w8 + L.dh);
     a.Y = reinterpret_cast<float *>(w8 + L.Y);
-    a.counters = reinterpret_cast<uint32_t *>(w8 + L.counters);
     a.out = out;
     a.status = reinterpret_cast<uint32_t *>(w8 + L.status);
     a.S = S;
@@ -222,7 +221,11 @@ int coli_moe_forward(const coli_moe_dims *d, int32_t S, const float *x, const in
     timing_before(KK_DOWN, st);
     e = launch_down(a, d->wbits, st);
     timing_after(KK_DOWN, st);
-    if (e != hipSuccess) return hip_fail(e, "down/combine launch");
+    if (e != hipSuccess) return hip_fail(e, "down launch");
+    timing_before(KK_COMBINE, st);
+    e = launch_combine(a, st);
+    timing_after(KK_COMBINE, st);
+    if (e != hipSuccess) return hip_fail(e, "combine launch");
     return COLI_OK;
 }
 
@@ -290,7 +293,8 @@ int coli_moe_timing_read(int32_t kind, double *total_ms, int64_t *launches) {
 
 int coli_moe_debug_unpack(int32_t bits, int32_t n_rows, int32_t cols, const void *src, int8_t *out,
                           void *stream) {
-    if ((bits != 8 && bits != 4 && bits != 2) || n_rows < 0 || cols <= 0 || cols % 32 || !src || !out)
+    if ((bits != 8 && bits != 4 && bits != 2) || n_rows < 0 || cols <= 0 || cols % 32 || !src || !out ||
+        (uint64_t)n_rows * (uint64_t)cols * (uint64_t)bits / 8 >= (1ull << 31))
         return fail(COLI_EINVAL, "debug_unpack: bad arguments");
     if (n_rows == 0) return COLI_OK;
     int rc = check_device();
@@ -301,7 +305,8 @@ int coli_moe_debug_unpack(int32_t bits, int32_t n_rows, int32_t cols, const void
 
 int coli_moe_debug_block_dots(int32_t bits, int32_t n_rows, int32_t cols, const void *src,
                               const int8_t *q, int32_t *out, void *stream) {
-    if ((bits != 8 && bits != 4 && bits != 2) || n_rows < 0 || cols <= 0 || cols % 32 || !src || !q || !out)
+    if ((bits != 8 && bits != 4 && bits != 2) || n_rows < 0 || cols <= 0 || cols % 32 || !src || !q || !out ||
+        (uint64_t)n_rows * (uint64_t)cols * (uint64_t)bits / 8 >= (1ull << 31))
         return fail(COLI_EINVAL, "debug_block_dots: bad arguments");
     if (n_rows == 0) return COLI_OK;
     int rc = check_device();

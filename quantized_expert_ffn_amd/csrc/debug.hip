@@ -12,9 +12,10 @@ __global__ __launch_bounds__(64) void k_debug_unpack(const uint8_t *__restrict__
                                                      int8_t *__restrict__ out, int cols) {
     const int r = blockIdx.x;
     const int nb = cols / 32;
-    const uint8_t *row = src + (size_t)r * cols * BITS / 8;
+    const uint32_t row_bytes = (uint32_t)cols * BITS / 8;
+    const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(src, row_bytes * gridDim.x);
     for (int b = threadIdx.x; b < nb; b += 64) {
-        const BlockBits<BITS> w = load_block<BITS>(row, b);
+        const BlockBits<BITS> w = load_block<BITS>(rsrc, (uint32_t)r * row_bytes, b);
 #pragma unroll
         for (int j = 0; j < 32; ++j) out[(size_t)r * cols + 32 * b + j] = block_code<BITS>(w, j);
     }
@@ -26,9 +27,10 @@ __global__ __launch_bounds__(64) void k_debug_block_dots(const uint8_t *__restri
                                                          int32_t *__restrict__ out, int cols) {
     const int r = blockIdx.x;
     const int nb = cols / 32;
-    const uint8_t *row = src + (size_t)r * cols * BITS / 8;
+    const uint32_t row_bytes = (uint32_t)cols * BITS / 8;
+    const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(src, row_bytes * gridDim.x);
     for (int b = threadIdx.x; b < nb; b += 64) {
-        const BlockBits<BITS> w = load_block<BITS>(row, b);
+        const BlockBits<BITS> w = load_block<BITS>(rsrc, (uint32_t)r * row_bytes, b);
         int32_t a[8];
         for (int k = 0; k < 8; ++k) {
             const int8_t *p = q + 32 * b + 4 * k;

@@ -17,6 +17,7 @@ namespace coli {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // ---- status word bits (first word of the workspace) ------------------------
 enum : uint32_t {
@@ -164,34 +165,41 @@ struct BlockBits<2> {
     u32x2 w;
 };
 
-// Weight rows live in global memory; loading through global-address-space
-// pointers gives global_load (not flat) instructions, marked non-temporal
-// because every weight byte is used once per call.
-typedef __attribute__((address_space(1))) const u32x4 g_u32x4;
-typedef __attribute__((address_space(1))) const u32x2 g_u32x2;
+// Weight rows are read through a buffer resource covering the whole blob:
+// the row's byte offset is a scalar, the lane's offset a single VGPR, and
+// every access is range-checked by the hardware (reads past num_records
+// return zeros).  Loads are marked non-temporal: each weight byte is used
+// once per call.
+constexpr uint32_t RSRC_WORD3 = 0x00020000u;  // raw (untyped) buffer on gfx9-family GPUs
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             (int)RSRC_WORD3);
+}
+
+constexpr int BUF_NT = 2;  // cache-policy bits: non-temporal
 
 template <int BITS>
-__device__ __forceinline__ BlockBits<BITS> load_block(const uint8_t *row, int b);
+__device__ __forceinline__ BlockBits<BITS> load_block(__amdgpu_buffer_rsrc_t r, uint32_t row_off, int b);
 
 template <>
-__device__ __forceinline__ BlockBits<8> load_block<8>(const uint8_t *row, int b) {
-    g_u32x4 *p = (g_u32x4 *)(row + 32 * b);
-    BlockBits<8> r;
-    r.w0 = __builtin_nontemporal_load(p);
-    r.w1 = __builtin_nontemporal_load(p + 1);
-    return r;
+__device__ __forceinline__ BlockBits<8> load_block<8>(__amdgpu_buffer_rsrc_t r, uint32_t row_off, int b) {
+    BlockBits<8> v;
+    v.w0 = __builtin_amdgcn_raw_buffer_load_b128(r, 32 * b, row_off, BUF_NT);
+    v.w1 = __builtin_amdgcn_raw_buffer_load_b128(r, 32 * b + 16, row_off, BUF_NT);
+    return v;
 }
 template <>
-__device__ __forceinline__ BlockBits<4> load_block<4>(const uint8_t *row, int b) {
-    BlockBits<4> r;
-    r.w = __builtin_nontemporal_load((g_u32x4 *)(row + 16 * b));
-    return r;
+__device__ __forceinline__ BlockBits<4> load_block<4>(__amdgpu_buffer_rsrc_t r, uint32_t row_off, int b) {
+    BlockBits<4> v;
+    v.w = __builtin_amdgcn_raw_buffer_load_b128(r, 16 * b, row_off, BUF_NT);
+    return v;
 }
 template <>
-__device__ __forceinline__ BlockBits<2> load_block<2>(const uint8_t *row, int b) {
-    BlockBits<2> r;
-    r.w = __builtin_nontemporal_load((g_u32x2 *)(row + 8 * b));
-    return r;
+__device__ __forceinline__ BlockBits<2> load_block<2>(__amdgpu_buffer_rsrc_t r, uint32_t row_off, int b) {
+    BlockBits<2> v;
+    v.w = __builtin_amdgcn_raw_buffer_load_b64(r, 8 * b, row_off, BUF_NT);
+    return v;
 }
 
 __device__ __forceinline__ int32_t block_dot(const BlockBits<8> &w, const int32_t a[8]) {

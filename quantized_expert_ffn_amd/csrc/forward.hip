@@ -32,13 +32,29 @@
 namespace coli {
 
 constexpr int ROWS_PER_WAVE = 16;
-constexpr int ISUM_PITCH = 65;  // padded: thread `row` reads a row of LDS without bank conflicts
+constexpr int ISUM_PITCH = 68;  // padded row of block dots: 16-byte aligned, few bank conflicts
 
 struct SmemPlan {
     size_t cnt, ustart, fill, uexp, uoff, pairs, misc, vq, vd, isum, gu, total;
 };
 
 __host__ __device__ inline size_t a16(size_t v) { return (v + 15) & ~(size_t)15; }
+
+// Values read from LDS that are the same in every lane: moving them to a
+// scalar register lets the compiler address weights with scalar bases.
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+template <typename T>
+__device__ __forceinline__ T *uniform_ptr(T *p) {
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return reinterpret_cast<T *>(((uint64_t)hi << 32) | lo);
+}
+
+// Per-vector stride of the staged block scales (a multiple of 4 so every
+// chunk of 64 scales starts 16-byte aligned).
+__host__ __device__ inline int vd_stride(int nb) { return (nb + 3) & ~3; }
 
 __host__ __device__ inline SmemPlan smem_plan(int S, int K, int E, int NT, int vlen) {
     SmemPlan p;
@@ -53,7 +69,7 @@ __host__ __device__ inline SmemPlan smem_plan(int S, int K, int E, int NT, int v
     p.misc = a16(p.pairs + 4 * (size_t)(P + S));
     p.vq = a16(p.misc + 16);
     p.vd = a16(p.vq + (size_t)NT * vlen);
-    p.isum = a16(p.vd + 4 * (size_t)NT * (vlen / 32));
+    p.isum = a16(p.vd + 4 * (size_t)NT * vd_stride(vlen / 32));
     p.gu = a16(p.isum + 4 * (size_t)NT * 64 * ISUM_PITCH);
     p.total = a16(p.gu + 4 * (size_t)NT * 64);
     return p;
@@ -159,44 +175,99 @@ __device__ __forceinline__ void load_act(const int8_t *vq, int b, int32_t a[8]) 
     a[4] = hi.x; a[5] = hi.y; a[6] = hi.z; a[7] = hi.w;
 }
 
-// Streams this wave's 16 rows for the ng staged vectors and leaves, in
-// `acc` of thread (row = tid & 63, vector = tid >> 6), the chain
-// fmaf(d_b, isum_b, acc) over all blocks of the row in ascending order.
-template <int BITS, int NT>
-__device__ __forceinline__ float stream_rows(const uint8_t *const rowp[ROWS_PER_WAVE], int nb,
+// Makes this wave's LDS writes visible to its own later reads (LDS
+// operations of one wave complete in order; the fence orders them for the
+// compiler and waits for outstanding LDS traffic).
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
+// Binary32 chain of one chunk for one (row, vector): acc = fmaf(d_b, isum_b,
+// acc) for the chunk's blocks in ascending order.  A full chunk is unrolled
+// with 16-byte LDS reads so the reads are all in flight before the chain.
+__device__ __forceinline__ float chain_chunk(float acc, const int32_t *is, const float *dv, int nbc) {
+    if (nbc == 64) {
+        // four quarters of 16 blocks; within a quarter all LDS reads are issued first
+#pragma unroll 1
+        for (int qq = 0; qq < 64; qq += 16) {
+            i32x4 iv[4];
+            f32x4 dd[4];
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                iv[q4] = *reinterpret_cast<const i32x4 *>(is + qq + 4 * q4);
+                dd[q4] = *reinterpret_cast<const f32x4 *>(dv + qq + 4 * q4);
+            }
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                acc = __builtin_fmaf(dd[q4].x, (float)iv[q4].x, acc);
+                acc = __builtin_fmaf(dd[q4].y, (float)iv[q4].y, acc);
+                acc = __builtin_fmaf(dd[q4].z, (float)iv[q4].z, acc);
+                acc = __builtin_fmaf(dd[q4].w, (float)iv[q4].w, acc);
+            }
+        }
+    } else {
+        for (int bb = 0; bb < nbc; ++bb) acc = __builtin_fmaf(dv[bb], (float)is[bb], acc);
+    }
+    return acc;
+}
+
+// Streams this wave's 16 rows for the ng staged vectors.  Returns, in lane
+// (row = lane & 15, vector = lane >> 4), the chain fmaf(d_b, isum_b, acc)
+// over all blocks of that row in ascending order.  `stage()` fills the LDS
+// vectors and ends with a workgroup barrier; it runs after the first chunk's
+// weight loads are issued so that their latency overlaps it.  Each wave then
+// works alone on its own LDS region; for int4 / int2 the next chunk's
+// weights are in flight while the current chunk is reduced.
+template <int BITS, int NT, typename Stage>
+__device__ __forceinline__ float stream_rows(__amdgpu_buffer_rsrc_t rsrc,
+                                             const uint32_t rowoff[ROWS_PER_WAVE], int nb,
                                              int ng, const int8_t *vq, const float *vd,
-                                             int32_t *isum, int vlen) {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int crow = tid & 63, cvec = tid >> 6;
+                                             int32_t *isum_wave, int vlen, Stage stage) {
+    constexpr bool PREFETCH = BITS < 8;
+    const int lane = threadIdx.x & 63;
+    const int crow = lane & 15, cvec = lane >> 4;
+    const int vds = vd_stride(nb);
     float acc = 0.0f;
     const int nchunks = (nb + 63) / 64;
+    BlockBits<BITS> cur[ROWS_PER_WAVE];
+    if (lane < nb) {
+#pragma unroll
+        for (int j = 0; j < ROWS_PER_WAVE; ++j) cur[j] = load_block<BITS>(rsrc, rowoff[j], lane);
+    }
+    stage();
     for (int c = 0; c < nchunks; ++c) {
         const int b = c * 64 + lane;
         const bool act = b < nb;
-        BlockBits<BITS> wv[ROWS_PER_WAVE];
-        if (act) {
+        BlockBits<BITS> nxt[ROWS_PER_WAVE];
+        if (PREFETCH && b + 64 < nb) {
 #pragma unroll
-            for (int j = 0; j < ROWS_PER_WAVE; ++j) wv[j] = load_block<BITS>(rowp[j], b);
+            for (int j = 0; j < ROWS_PER_WAVE; ++j) nxt[j] = load_block<BITS>(rsrc, rowoff[j], b + 64);
         }
 #pragma unroll
         for (int it = 0; it < NT; ++it) {
             if (it < ng) {
                 int32_t av[8] = {0, 0, 0, 0, 0, 0, 0, 0};
                 if (act) load_act(vq + (size_t)it * vlen, b, av);
-                int32_t *dst = isum + (it * 64 + wave * ROWS_PER_WAVE) * ISUM_PITCH + lane;
+                int32_t *dst = isum_wave + it * ROWS_PER_WAVE * ISUM_PITCH + lane;
 #pragma unroll
                 for (int j = 0; j < ROWS_PER_WAVE; ++j)
-                    dst[j * ISUM_PITCH] = act ? block_dot(wv[j], av) : 0;
+                    dst[j * ISUM_PITCH] = act ? block_dot(cur[j], av) : 0;
             }
         }
-        __syncthreads();
-        if (cvec < ng) {
-            const int nbc = min(64, nb - c * 64);
-            const int32_t *is = isum + (cvec * 64 + crow) * ISUM_PITCH;
-            const float *dv = vd + cvec * nb + c * 64;
-            for (int bb = 0; bb < nbc; ++bb) acc = __builtin_fmaf(dv[bb], (float)is[bb], acc);
+        wave_lds_sync();
+        if (cvec < ng)
+            acc = chain_chunk(acc, isum_wave + (cvec * ROWS_PER_WAVE + crow) * ISUM_PITCH,
+                              vd + cvec * vds + c * 64, min(64, nb - c * 64));
+        wave_lds_sync();
+        if (PREFETCH) {
+#pragma unroll
+            for (int j = 0; j < ROWS_PER_WAVE; ++j) cur[j] = nxt[j];
+        } else if (c + 1 < nchunks && b + 64 < nb) {
+#pragma unroll
+            for (int j = 0; j < ROWS_PER_WAVE; ++j) cur[j] = load_block<BITS>(rsrc, rowoff[j], b + 64);
         }
-        __syncthreads();
     }
     return acc;
 }
@@ -204,7 +275,7 @@ __device__ __forceinline__ float stream_rows(const uint8_t *const rowp[ROWS_PER_
 template <int BITS, int NT>
 __global__ __launch_bounds__(256) void k_gateup(const FwdArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
     const int S = a.S, K = a.K, E = a.E, H = a.H, I = a.I, P = S * K;
     const SmemPlan L = smem_plan(S, K, E, NT, H);
     build_units(a.idx, S, K, E, a.n_shared, smem, L, a.status,
@@ -212,61 +283,61 @@ __global__ __launch_bounds__(256) void k_gateup(const FwdArgs a) {
     const int *uexp = reinterpret_cast<const int *>(smem + L.uexp);
     const int *uoff = reinterpret_cast<const int *>(smem + L.uoff);
     const int *pairs = reinterpret_cast<const int *>(smem + L.pairs);
-    const int n_units = reinterpret_cast<const int *>(smem + L.misc)[0];
+    const int n_units = uniform(reinterpret_cast<const int *>(smem + L.misc)[0]);
     const int u = blockIdx.y;
     if (u >= n_units) return;
-    const int e = uexp[u];
+    const int e = uniform(uexp[u]);
     if (e >= 0 && a.pend_mode != 0) {
         const bool pend = (a.pend[e >> 5] >> (e & 31)) & 1u;
         if ((a.pend_mode == 1) == pend) return;
     }
-    const uint8_t *blob = e < 0 ? a.shared : a.blobs[e];
+    const uint8_t *blob = uniform_ptr(e < 0 ? a.shared : a.blobs[e]);
     if (blob == nullptr) {
         if (tid == 0) raise_status(a.status, ST_NOTRESIDENT);
         return;
     }
     int8_t *vq = reinterpret_cast<int8_t *>(smem + L.vq);
     float *vd = reinterpret_cast<float *>(smem + L.vd);
-    int32_t *isum = reinterpret_cast<int32_t *>(smem + L.isum);
+    int32_t *isum_wave = reinterpret_cast<int32_t *>(smem + L.isum) + wave * NT * ROWS_PER_WAVE * ISUM_PITCH;
     float *gu = reinterpret_cast<float *>(smem + L.gu);
     const BlobLayout BL = blob_layout(H, I, BITS);
     const size_t row_bytes = (size_t)H * BITS / 8;
     const int i0 = blockIdx.x * 32;
     const int half = wave & 1;            // rows 0-15 or 16-31 of the tile
     const size_t mat = wave < 2 ? BL.gate : BL.up;
-    const uint8_t *rowp[ROWS_PER_WAVE];
+    const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(blob, (uint32_t)BL.total);
+    uint32_t rowoff[ROWS_PER_WAVE];
 #pragma unroll
     for (int j = 0; j < ROWS_PER_WAVE; ++j)
-        rowp[j] = blob + mat + (size_t)(i0 + 16 * half + j) * row_bytes;
-    const float *s_gate = reinterpret_cast<const float *>(blob + BL.s_gate);
-    const float *s_up = reinterpret_cast<const float *>(blob + BL.s_up);
+        rowoff[j] = (uint32_t)(mat + (size_t)(i0 + 16 * half + j) * row_bytes);
+    const float *scale = reinterpret_cast<const float *>(blob + (wave < 2 ? BL.s_gate : BL.s_up));
     const int nb = H / 32;
-    const int p0 = uoff[u], np = uoff[u + 1] - p0;
+    const int p0 = uniform(uoff[u]), np = uniform(uoff[u + 1]) - p0;
     const bool check_x = blockIdx.x == 0;
+    const int crow = lane & 15, cvec = lane >> 4;
+    const int vds = vd_stride(nb);
     for (int g0 = 0; g0 < np; g0 += NT) {
         const int ng = min(NT, np - g0);
         // Q8_0 of the hidden states of this group's tokens.  Lanes 0-31 and
         // 32-63 of a wave each hold one 32-element block.
-        for (int it = 0; it < ng; ++it) {
-            const int v = pairs[p0 + g0 + it];
-            const int t = v < P ? v / K : v - P;
-            const float *xr = a.x + (size_t)t * H;
-            for (int h = tid; h < H; h += 256) {
-                const float xv = xr[h];
-                if (check_x && !finite_f32(xv)) raise_status(a.status, ST_NONFINITE);
-                float d;
-                const int8_t q = q8_0_lane(xv, &d);
-                vq[it * H + h] = q;
-                if ((lane & 31) == 0) vd[it * nb + (h >> 5)] = d;
+        auto stage = [&]() {
+            for (int it = 0; it < ng; ++it) {
+                const int v = pairs[p0 + g0 + it];
+                const int t = v < P ? v / K : v - P;
+                const float *xr = a.x + (size_t)t * H;
+                for (int h = tid; h < H; h += 256) {
+                    const float xv = xr[h];
+                    if (check_x && !finite_f32(xv)) raise_status(a.status, ST_NONFINITE);
+                    float d;
+                    const int8_t q = q8_0_lane(xv, &d);
+                    vq[it * H + h] = q;
+                    if ((lane & 31) == 0) vd[it * vds + (h >> 5)] = d;
+                }
             }
-        }
-        __syncthreads();
-        const float acc = stream_rows<BITS, NT>(rowp, nb, ng, vq, vd, isum, H);
-        const int crow = tid & 63, cvec = tid >> 6;
-        if (cvec < ng) {
-            const float s = crow < 32 ? s_gate[i0 + crow] : s_up[i0 + crow - 32];
-            gu[cvec * 64 + crow] = acc * s;
-        }
+            __syncthreads();
+        };
+        const float acc = stream_rows<BITS, NT>(rsrc, rowoff, nb, ng, vq, vd, isum_wave, H, stage);
+        if (cvec < ng) gu[cvec * 64 + wave * ROWS_PER_WAVE + crow] = acc * scale[i0 + 16 * half + crow];
         __syncthreads();
         // SwiGLU and Q8_0(h): half-wave (tid >> 5) handles one vector's 32 rows.
         const int vv = tid >> 5, i = tid & 31;
@@ -282,91 +353,87 @@ __global__ __launch_bounds__(256) void k_gateup(const FwdArgs a) {
     }
 }
 
+// Down projection: 64 rows of one unit per workgroup, y written to the
+// pair's slot of the workspace (the combine kernel reads it after this
+// kernel has finished, so no cross-workgroup signalling is needed).
 template <int BITS, int NT>
 __global__ __launch_bounds__(256) void k_down(const FwdArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    __shared__ int is_last;
-    const int tid = threadIdx.x, wave = tid >> 6;
-    const int S = a.S, K = a.K, E = a.E, H = a.H, I = a.I, P = S * K;
+    const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
+    const int S = a.S, K = a.K, E = a.E, H = a.H, I = a.I;
     const SmemPlan L = smem_plan(S, K, E, NT, I);
     build_units(a.idx, S, K, E, a.n_shared, smem, L, a.status, false);
     const int *uexp = reinterpret_cast<const int *>(smem + L.uexp);
     const int *uoff = reinterpret_cast<const int *>(smem + L.uoff);
     const int *pairs = reinterpret_cast<const int *>(smem + L.pairs);
-    const int n_units = reinterpret_cast<const int *>(smem + L.misc)[0];
+    const int n_units = uniform(reinterpret_cast<const int *>(smem + L.misc)[0]);
     const int u = blockIdx.y;
     if (u >= n_units) return;
-    const int e = uexp[u];
-    const uint8_t *blob = e < 0 ? a.shared : a.blobs[e];
+    const int e = uniform(uexp[u]);
+    const uint8_t *blob = uniform_ptr(e < 0 ? a.shared : a.blobs[e]);
     const int r0 = blockIdx.x * 64;
-    const int p0 = uoff[u], np = uoff[u + 1] - p0;
-    const int crow = tid & 63, cvec = tid >> 6;
-    if (blob != nullptr) {
-        int8_t *vq = reinterpret_cast<int8_t *>(smem + L.vq);
-        float *vd = reinterpret_cast<float *>(smem + L.vd);
-        int32_t *isum = reinterpret_cast<int32_t *>(smem + L.isum);
-        const BlobLayout BL = blob_layout(H, I, BITS);
-        const size_t row_bytes = (size_t)I * BITS / 8;
-        const uint8_t *rowp[ROWS_PER_WAVE];
-#pragma unroll
-        for (int j = 0; j < ROWS_PER_WAVE; ++j)
-            rowp[j] = blob + BL.down + (size_t)(r0 + wave * ROWS_PER_WAVE + j) * row_bytes;
-        const float *s_down = reinterpret_cast<const float *>(blob + BL.s_down);
-        const int nb = I / 32;
-        for (int g0 = 0; g0 < np; g0 += NT) {
-            const int ng = min(NT, np - g0);
-            for (int it = 0; it < ng; ++it) {
-                const int slot = pairs[p0 + g0 + it];
-                const i32x4 *src = reinterpret_cast<const i32x4 *>(a.qh + (size_t)slot * I);
-                i32x4 *dst = reinterpret_cast<i32x4 *>(vq + (size_t)it * I);
-                for (int q = tid; q < I / 16; q += 256) dst[q] = src[q];
-                for (int q = tid; q < nb; q += 256) vd[it * nb + q] = a.dh[(size_t)slot * nb + q];
-            }
-            __syncthreads();
-            const float acc = stream_rows<BITS, NT>(rowp, nb, ng, vq, vd, isum, I);
-            if (cvec < ng) {
-                const int slot = pairs[p0 + g0 + cvec];
-                a.Y[(size_t)slot * H + r0 + crow] = acc * s_down[r0 + crow];
-            }
-            __syncthreads();
-        }
-    } else {
+    const int p0 = uniform(uoff[u]), np = uniform(uoff[u + 1]) - p0;
+    if (blob == nullptr) {
         if (tid == 0) raise_status(a.status, ST_NOTRESIDENT);
         for (int q = tid; q < np * 64; q += 256) {
             const int slot = pairs[p0 + (q >> 6)];
             a.Y[(size_t)slot * H + r0 + (q & 63)] = 0.0f;
         }
+        return;
     }
-    // Arrival: the last unit workgroup of this row tile combines it.
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) {
-        const uint32_t prev = __hip_atomic_fetch_add(&a.counters[blockIdx.x], 1u, __ATOMIC_ACQ_REL,
-                                                     __HIP_MEMORY_SCOPE_AGENT);
-        const int last = prev == (uint32_t)(n_units - 1);
-        if (last)
-            __hip_atomic_store(&a.counters[blockIdx.x], 0u, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-        is_last = last;
-    }
-    __syncthreads();
-    if (!is_last) return;
-    __threadfence();
-    for (int q = tid; q < S * 64; q += 256) {
-        const int t = q >> 6, r = r0 + (q & 63);
-        float acc = 0.0f;
-        for (int k = 0; k < K; ++k) {
-            const float wk = a.w[(size_t)t * K + k];
-            if (r == r0 && !finite_f32(wk)) raise_status(a.status, ST_NONFINITE);
-            const float yk = __hip_atomic_load(&a.Y[(size_t)(t * K + k) * H + r], __ATOMIC_RELAXED,
-                                               __HIP_MEMORY_SCOPE_AGENT);
-            acc = __builtin_fmaf(wk, yk, acc);
+    int8_t *vq = reinterpret_cast<int8_t *>(smem + L.vq);
+    float *vd = reinterpret_cast<float *>(smem + L.vd);
+    int32_t *isum_wave = reinterpret_cast<int32_t *>(smem + L.isum) + wave * NT * ROWS_PER_WAVE * ISUM_PITCH;
+    const BlobLayout BL = blob_layout(H, I, BITS);
+    const size_t row_bytes = (size_t)I * BITS / 8;
+    const int rw = r0 + wave * ROWS_PER_WAVE;
+    const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(blob, (uint32_t)BL.total);
+    uint32_t rowoff[ROWS_PER_WAVE];
+#pragma unroll
+    for (int j = 0; j < ROWS_PER_WAVE; ++j) rowoff[j] = (uint32_t)(BL.down + (size_t)(rw + j) * row_bytes);
+    const float *s_down = reinterpret_cast<const float *>(blob + BL.s_down);
+    const int nb = I / 32;
+    const int vds = vd_stride(nb);
+    const int crow = lane & 15, cvec = lane >> 4;
+    for (int g0 = 0; g0 < np; g0 += NT) {
+        const int ng = min(NT, np - g0);
+        auto stage = [&]() {
+            for (int it = 0; it < ng; ++it) {
+                const int slot = pairs[p0 + g0 + it];
+                const i32x4 *src = reinterpret_cast<const i32x4 *>(a.qh + (size_t)slot * I);
+                i32x4 *dst = reinterpret_cast<i32x4 *>(vq + (size_t)it * I);
+                for (int q = tid; q < I / 16; q += 256) dst[q] = src[q];
+                for (int q = tid; q < nb; q += 256) vd[it * vds + q] = a.dh[(size_t)slot * nb + q];
+            }
+            __syncthreads();
+        };
+        const float acc = stream_rows<BITS, NT>(rsrc, rowoff, nb, ng, vq, vd, isum_wave, I, stage);
+        if (cvec < ng) {
+            const int slot = pairs[p0 + g0 + cvec];
+            a.Y[(size_t)slot * H + rw + crow] = acc * s_down[rw + crow];
         }
-        if (a.n_shared)
-            acc = acc + __hip_atomic_load(&a.Y[(size_t)(P + t) * H + r], __ATOMIC_RELAXED,
-                                          __HIP_MEMORY_SCOPE_AGENT);
-        a.out[(size_t)t * H + r] = acc;
+        __syncthreads();
     }
+}
+
+// Combine: out[t, r] = (fmaf chain over k in rank order of w[t,k] * y[t,k][r]
+// from 0) + y_shared[t][r].  One thread per output element, one writer.
+// Grid (H / 256, S).
+__global__ __launch_bounds__(256) void k_combine(const FwdArgs a) {
+    const int t = blockIdx.y;
+    const int r = blockIdx.x * 256 + threadIdx.x;
+    const int K = a.K, H = a.H, P = a.S * a.K;
+    const float *w = a.w + (size_t)t * K;
+    float acc = 0.0f;
+    bool ok = true;
+    for (int k = 0; k < K; ++k) {
+        const float wk = w[k];
+        ok = ok && finite_f32(wk);
+        acc = __builtin_fmaf(wk, a.Y[(size_t)(t * K + k) * H + r], acc);
+    }
+    if (a.n_shared) acc = acc + a.Y[(size_t)(P + t) * H + r];
+    a.out[(size_t)t * H + r] = acc;
+    if (!ok && r == 0) raise_status(a.status, ST_NONFINITE);
 }
 
 // ---- launchers -----------------------------------------------------------
@@ -422,6 +489,11 @@ hipError_t launch_gateup(const FwdArgs &a, int bits, hipStream_t st) {
     if (bits == 8) return gateup_bits<8>(a, st);
     if (bits == 4) return gateup_bits<4>(a, st);
     return gateup_bits<2>(a, st);
+}
+
+hipError_t launch_combine(const FwdArgs &a, hipStream_t st) {
+    hipLaunchKernelGGL(k_combine, dim3(a.H / 256, a.S), dim3(256), 0, st, a);
+    return hipGetLastError();
 }
 
 hipError_t launch_down(const FwdArgs &a, int bits, hipStream_t st) {

@@ -6,10 +6,10 @@
 
 namespace coli {
 
-// Workspace carve-up for a call with S tokens.  status and counters sit at
-// fixed offsets (they persist between calls); the rest is per call.
+// Workspace carve-up for a call with S tokens.  The status word sits at a
+// fixed offset (it persists between calls); the rest is per call.
 struct WsLayout {
-    size_t status, counters, logits, qh, dh, Y, total;
+    size_t status, logits, qh, dh, Y, total;
 };
 
 inline size_t al256h(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -18,8 +18,7 @@ inline WsLayout ws_layout(int H, int I, int E, int K, int S) {
     WsLayout L;
     const size_t slots = (size_t)S * (size_t)(K + 1);
     L.status = 0;
-    L.counters = 256;
-    L.logits = al256h(L.counters + 4 * (size_t)(H / 64 + 1));
+    L.logits = 256;
     L.qh = al256h(L.logits + 4 * (size_t)S * (size_t)E);
     L.dh = al256h(L.qh + slots * (size_t)I);
     L.Y = al256h(L.dh + 4 * slots * (size_t)(I / 32));
@@ -37,7 +36,6 @@ struct FwdArgs {
     int8_t *qh;                    // [S*(K+1), I]   Q8_0(h) codes per pair slot
     float *dh;                     // [S*(K+1), I/32]
     float *Y;                      // [S*(K+1), H]   expert outputs per pair slot
-    uint32_t *counters;            // [H/64] arrival counters of the down row tiles
     float *out;                    // [S, H]
     uint32_t *status;
     int S, H, I, E, K, n_shared;
@@ -57,6 +55,7 @@ enum KernelKind {
     KK_ROUTER_SELECT = 1,
     KK_GATEUP = 2,
     KK_DOWN = 3,
+    KK_COMBINE = 4,
     KK_COUNT = 8
 };
 
@@ -66,6 +65,7 @@ void timing_after(int kind, hipStream_t st);
 
 hipError_t launch_gateup(const FwdArgs &a, int bits, hipStream_t st);
 hipError_t launch_down(const FwdArgs &a, int bits, hipStream_t st);
+hipError_t launch_combine(const FwdArgs &a, hipStream_t st);
 size_t forward_smem_max(int S, int H, int I, int E, int K, int n_shared);
 
 hipError_t launch_debug_unpack(int bits, int rows, int cols, const void *src, int8_t *out,

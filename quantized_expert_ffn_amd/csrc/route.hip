@@ -8,13 +8,14 @@
 
 namespace coli {
 
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // One wavefront per (token, expert).  Lane l accumulates, with fmaf from 0,
 // the elements h = 256 j + 4 l + c for j ascending and c = 0..3 (a float4
 // per lane per step, so each step reads 1 KB of the gate row coalesced);
 // then six xor-butterfly additions p_l + p_{l^o}, o = 32..1, leave the logit
-// in every lane.  Grid: (E, S), 64 threads.
+// in every lane.  Up to MAXJ steps the whole row is loaded before the chain;
+// longer rows go in chunks of MAXJ.  Grid: (E, S), 64 threads.
+template <int MAXJ>
 __global__ __launch_bounds__(64) void k_router_logits(const float *__restrict__ x,
                                                       const float *__restrict__ W,
                                                       float *__restrict__ logits,
@@ -25,19 +26,29 @@ __global__ __launch_bounds__(64) void k_router_logits(const float *__restrict__ 
     const int t = blockIdx.y;
     const f32x4 *xr = reinterpret_cast<const f32x4 *>(x + (size_t)t * H);
     const f32x4 *wr = reinterpret_cast<const f32x4 *>(W + (size_t)e * H);
+    const int steps = H / 256;
     float p = 0.0f;
     bool ok = true;
-    const int steps = H / 256;
-#pragma unroll 8
-    for (int j = 0; j < steps; ++j) {
-        const f32x4 xv = xr[64 * j + lane];
-        const f32x4 wv = wr[64 * j + lane];
-        p = __builtin_fmaf(xv.x, wv.x, p);
-        p = __builtin_fmaf(xv.y, wv.y, p);
-        p = __builtin_fmaf(xv.z, wv.z, p);
-        p = __builtin_fmaf(xv.w, wv.w, p);
-        ok = ok && finite_f32(xv.x) && finite_f32(xv.y) && finite_f32(xv.z) && finite_f32(xv.w) &&
-             finite_f32(wv.x) && finite_f32(wv.y) && finite_f32(wv.z) && finite_f32(wv.w);
+    for (int j0 = 0; j0 < steps; j0 += MAXJ) {
+        f32x4 xv[MAXJ], wv[MAXJ];
+#pragma unroll
+        for (int jj = 0; jj < MAXJ; ++jj)
+            if (j0 + jj < steps) {
+                wv[jj] = __builtin_nontemporal_load(wr + 64 * (j0 + jj) + lane);
+                xv[jj] = xr[64 * (j0 + jj) + lane];
+            }
+#pragma unroll
+        for (int jj = 0; jj < MAXJ; ++jj) {
+            if (j0 + jj < steps) {
+                p = __builtin_fmaf(xv[jj].x, wv[jj].x, p);
+                p = __builtin_fmaf(xv[jj].y, wv[jj].y, p);
+                p = __builtin_fmaf(xv[jj].z, wv[jj].z, p);
+                p = __builtin_fmaf(xv[jj].w, wv[jj].w, p);
+                ok = ok && finite_f32(xv[jj].x) && finite_f32(xv[jj].y) && finite_f32(xv[jj].z) &&
+                     finite_f32(xv[jj].w) && finite_f32(wv[jj].x) && finite_f32(wv[jj].y) &&
+                     finite_f32(wv[jj].z) && finite_f32(wv[jj].w);
+            }
+        }
     }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) p = p + __shfl_xor(p, o, 64);
@@ -45,11 +56,39 @@ __global__ __launch_bounds__(64) void k_router_logits(const float *__restrict__ 
     if (lane == 0) logits[(size_t)t * E + e] = p;
 }
 
+// ---- wavefront reductions through DPP (result uniform across the wave) ----
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ int dpp(int v) {
+    return __builtin_amdgcn_update_dpp(v, v, CTRL, ROWS, 0xF, false);
+}
+
+__device__ __forceinline__ float wave_max_f32(float v) {
+    int i = __float_as_int(v);
+    i = __float_as_int(__builtin_fmaxf(__int_as_float(i), __int_as_float(dpp<0xB1>(i))));  // quad [1,0,3,2]
+    i = __float_as_int(__builtin_fmaxf(__int_as_float(i), __int_as_float(dpp<0x4E>(i))));  // quad [2,3,0,1]
+    i = __float_as_int(__builtin_fmaxf(__int_as_float(i), __int_as_float(dpp<0x141>(i)))); // row half mirror
+    i = __float_as_int(__builtin_fmaxf(__int_as_float(i), __int_as_float(dpp<0x140>(i)))); // row mirror
+    i = __float_as_int(__builtin_fmaxf(__int_as_float(i), __int_as_float(dpp<0x142, 0xA>(i))));  // row bcast 15
+    i = __float_as_int(__builtin_fmaxf(__int_as_float(i), __int_as_float(dpp<0x143, 0xC>(i))));  // row bcast 31
+    return __int_as_float(__builtin_amdgcn_readlane(i, 63));
+}
+
+__device__ __forceinline__ int wave_min_i32(int v) {
+    v = min(v, dpp<0xB1>(v));
+    v = min(v, dpp<0x4E>(v));
+    v = min(v, dpp<0x141>(v));
+    v = min(v, dpp<0x140>(v));
+    v = min(v, dpp<0x142, 0xA>(v));
+    v = min(v, dpp<0x143, 0xC>(v));
+    return __builtin_amdgcn_readlane(v, 63);
+}
+
 // One wavefront per token.  Lane l owns experts l, l+64, ...; sig = sigmoid,
-// score = sig + bias.  K rounds of a wavefront argmax under the total order
-// (score desc, id asc) pick the experts in rank order; the gate weights are
-// (sig_k / ((sig_0 + sig_1) + ...)) * rsf, or sig_k * rsf without
-// renormalisation.  E <= 1024, K <= 32.
+// score = sig + bias.  K rounds pick the experts in rank order under the
+// total order (score desc, id asc): the wavefront maximum of the lanes' best
+// remaining scores, then the smallest id holding that score.  The gate
+// weights are (sig_k / ((sig_0 + sig_1) + ...)) * rsf, or sig_k * rsf
+// without renormalisation.  E <= 1024, K <= 32.
 __global__ __launch_bounds__(64) void k_router_select(const float *__restrict__ logits,
                                                       const float *__restrict__ bias,
                                                       int32_t *__restrict__ idx_out,
@@ -57,60 +96,48 @@ __global__ __launch_bounds__(64) void k_router_select(const float *__restrict__ 
                                                       uint32_t *__restrict__ status, int E, int K,
                                                       float rsf, int norm) {
     constexpr int MAXM = 16;
+    __shared__ float sig_s[1024];
     __shared__ float sel_sig[32];
     const int lane = threadIdx.x;
     const int t = blockIdx.x;
-    float sig[MAXM], score[MAXM];
+    const int mcount = (E + 63) / 64;
+    float score[MAXM];
     uint32_t taken = 0;
     bool ok = true;
 #pragma unroll
     for (int m = 0; m < MAXM; ++m) {
         const int e = lane + 64 * m;
-        sig[m] = 0.0f;
         score[m] = -__builtin_inff();
-        if (e < E) {
+        if (m < mcount && e < E) {
             const float l = logits[(size_t)t * E + e];
             const float b = bias ? bias[e] : 0.0f;
             ok = ok && finite_f32(l) && finite_f32(b);
-            sig[m] = sigmoid_f32(l);
-            score[m] = sig[m] + b;
+            const float sg = sigmoid_f32(l);
+            sig_s[e] = sg;
+            score[m] = sg + b;
         }
     }
     if (!ok) raise_status(status, ST_NONFINITE);
+    __syncthreads();
     for (int k = 0; k < K; ++k) {
         float bs = -__builtin_inff();
         int be = 0x7fffffff;
-        float bsig = 0.0f;
 #pragma unroll
         for (int m = 0; m < MAXM; ++m) {
-            const int e = lane + 64 * m;
-            if (e < E && !((taken >> m) & 1u)) {
-                if (score[m] > bs || (score[m] == bs && e < be)) {
-                    bs = score[m];
-                    be = e;
-                    bsig = sig[m];
-                }
+            if (m < mcount && !((taken >> m) & 1u) && score[m] > bs) {
+                bs = score[m];
+                be = lane + 64 * m;
             }
         }
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) {
-            const float os = __shfl_xor(bs, o, 64);
-            const int oe = __shfl_xor(be, o, 64);
-            const float osig = __shfl_xor(bsig, o, 64);
-            if (os > bs || (os == bs && oe < be)) {
-                bs = os;
-                be = oe;
-                bsig = osig;
-            }
+        const float M = wave_max_f32(bs);
+        int sel = wave_min_i32(bs == M ? be : 0x7fffffff);
+        if (sel >= E) {  // only reachable with NaN scores, already flagged
+            sel = k;
         }
-        if (be >= E) {  // only reachable with NaN scores, already flagged
-            be = k;
-            bsig = 0.0f;
-        }
-        if ((be & 63) == lane) taken |= 1u << (be >> 6);
+        if ((sel & 63) == lane) taken |= 1u << (sel >> 6);
         if (lane == 0) {
-            idx_out[(size_t)t * K + k] = be;
-            sel_sig[k] = bsig;
+            idx_out[(size_t)t * K + k] = sel;
+            sel_sig[k] = sig_s[sel];
         }
     }
     __syncthreads();
@@ -128,7 +155,10 @@ __global__ __launch_bounds__(64) void k_router_select(const float *__restrict__ 
 
 hipError_t launch_router_logits(const float *x, const float *W, float *logits, uint32_t *status,
                                 int S, int H, int E, hipStream_t st) {
-    hipLaunchKernelGGL(k_router_logits, dim3(E, S), dim3(64), 0, st, x, W, logits, status, H, E);
+    if (H <= 24 * 256)
+        hipLaunchKernelGGL(k_router_logits<24>, dim3(E, S), dim3(64), 0, st, x, W, logits, status, H, E);
+    else
+        hipLaunchKernelGGL(k_router_logits<16>, dim3(E, S), dim3(64), 0, st, x, W, logits, status, H, E);
     return hipGetLastError();
 }
 
