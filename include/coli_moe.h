@@ -119,6 +119,18 @@ int coli_moe_forward(const coli_moe_dims *dims, int32_t n_tokens, const float *x
                      size_t ws_bytes, void *stream);
 
 /*
+ * The whole layer in one call: the result of coli_moe_route followed by
+ * coli_moe_forward (same bits), with the routing also written to topk_idx /
+ * topk_w.  For up to 8 tokens it runs as one persistent kernel (router,
+ * gate/up and down+combine phases separated by grid barriers inside the
+ * launch); otherwise it makes the two calls.  Arguments as for those calls.
+ */
+int coli_moe_layer(const coli_moe_dims *dims, int32_t n_tokens, const float *x,
+                   const float *router_w, const float *router_bias,
+                   const void *const *expert_blobs, const void *shared_blob, int32_t *topk_idx,
+                   float *topk_w, float *out, void *ws, size_t ws_bytes, void *stream);
+
+/*
  * Expert staging (README v1.0 "What's implemented": async expert readahead —
  * the next experts are fetched while the current ones are multiplied).
  * Enqueues n host-to-device copies of bytes_each bytes, host_src[i] (pinned
@@ -142,12 +154,19 @@ const char *coli_moe_last_error(void);
  * bracketed by events on its stream; coli_moe_timing_read() synchronises the
  * recorded events and returns the accumulated milliseconds and launch count
  * of one kernel kind (0 router logits, 1 router select, 2 gate/up, 3 down,
- * 4 combine), then resets that kind.  For measurement only.
+ * 4 combine, 5 persistent layer, 6 persistent forward), then resets that
+ * kind.  For measurement only.
  */
 int coli_moe_timing_enable(int32_t enable);
 int coli_moe_timing_read(int32_t kind, double *total_ms, int64_t *launches);
 
 /* ---- test hooks: the same device functions as the production kernels ---- */
+
+/* Kernel family for subsequent calls in this process: 0 automatic (default),
+ * 1 multi-launch kernels only, 2 persistent (single-launch) kernels only —
+ * a forced persistent kernel fails with COLI_EINVAL where it does not
+ * apply (pending experts, more than 8 tokens). */
+int coli_moe_debug_force_path(int32_t path);
 
 /* Unpacks n_rows packed rows of `cols` codes (device src, row stride
  * cols*bits/8 bytes) into device int8 out [n_rows, cols]. */

@@ -28,9 +28,12 @@ EXPORTS = (
     "coli_moe_stage_experts", "coli_moe_status", "coli_moe_last_error", "coli_moe_timing_enable",
     "coli_moe_timing_read", "coli_moe_debug_unpack", "coli_moe_debug_block_dots",
     "coli_moe_debug_logits", "coli_moe_debug_expf", "coli_moe_debug_q8_0",
+    "coli_moe_debug_force_path", "coli_moe_layer",
 )
 
 KIND_ROUTER_LOGITS, KIND_ROUTER_SELECT, KIND_GATEUP, KIND_DOWN, KIND_COMBINE = 0, 1, 2, 3, 4
+KIND_LAYER, KIND_FORWARD_PERSISTENT = 5, 6
+PATH_AUTO, PATH_MULTI, PATH_PERSISTENT = 0, 1, 2
 
 
 class coli_moe_dims(ctypes.Structure):
@@ -67,6 +70,8 @@ _sigs = {
     "coli_moe_debug_logits": (ctypes.c_int, [_D, _I32, _P, _P, _P, _P]),
     "coli_moe_debug_expf": (ctypes.c_int, [ctypes.c_int64, _P, _P, _P]),
     "coli_moe_debug_q8_0": (ctypes.c_int, [_I32, _I32, _P, _P, _P, _P]),
+    "coli_moe_debug_force_path": (ctypes.c_int, [_I32]),
+    "coli_moe_layer": (ctypes.c_int, [_D, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
 }
 for _name, (_res, _args) in _sigs.items():
     _f = getattr(_lib, _name)
@@ -167,6 +172,19 @@ def coli_moe_forward(dims, x, topk_idx, topk_w, expert_blobs, shared_blob, out, 
         _dev(ws, torch.uint8, "ws"), _nbytes(ws), _stream(stream)), "coli_moe_forward")
 
 
+def coli_moe_layer(dims, x, router_w, router_bias, expert_blobs, shared_blob, topk_idx, topk_w, out, ws,
+                   stream=None):
+    """Route + forward in one call (persistent kernel for up to 8 tokens)."""
+    import torch
+    S = x.shape[0]
+    _check(_lib.coli_moe_layer(
+        _dims(dims), S, _dev(x, torch.float32, "x"), _dev(router_w, torch.float32, "router_w"),
+        _dev(router_bias, torch.float32, "router_bias"), _dev(expert_blobs, torch.int64, "expert_blobs"),
+        _ptr(shared_blob, None, "shared_blob"), _dev(topk_idx, torch.int32, "topk_idx"),
+        _dev(topk_w, torch.float32, "topk_w"), _dev(out, torch.float32, "out"), _dev(ws, torch.uint8, "ws"),
+        _nbytes(ws), _stream(stream)), "coli_moe_layer")
+
+
 def coli_moe_stage_experts(host_src, dev_dst, bytes_each: int, copy_stream=None, done_event=None):
     n = len(host_src)
     if len(dev_dst) != n:
@@ -232,3 +250,7 @@ def coli_moe_debug_q8_0(v, q, d, stream=None):
     rows, cols = v.shape
     _check(_lib.coli_moe_debug_q8_0(rows, cols, _dev(v, torch.float32, "v"), _dev(q, torch.int8, "q"),
                                     _dev(d, torch.float32, "d"), _stream(stream)), "coli_moe_debug_q8_0")
+
+
+def coli_moe_debug_force_path(path: int) -> None:
+    _check(_lib.coli_moe_debug_force_path(int(path)), "coli_moe_debug_force_path")

@@ -5,6 +5,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <map>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -87,6 +88,15 @@ hipEvent_t take_event() {
     return e;
 }
 
+// 0: automatic, 1: multi-launch kernels only, 2: persistent kernels only.
+int g_force_path = 0;
+
+// The persistent kernel handles small batches whose experts are all resident.
+bool use_persistent(const coli_moe_dims *d, int S, bool pending) {
+    if (g_force_path == 1 || pending || S > 8) return false;
+    return coli::layer_smem(S, d->hidden, d->inter, d->n_experts, d->top_k, d->n_shared) <= 160 * 1024;
+}
+
 }  // namespace
 
 namespace coli {
@@ -105,6 +115,17 @@ void timing_after(int kind, hipStream_t st) {
     if (e && hipEventRecord(e, st) == hipSuccess)
         g_timing.done[kind].emplace_back(g_timing.open[kind], e);
     g_timing.open[kind] = nullptr;
+}
+
+hipError_t ensure_dyn_smem(const void *kern, size_t smem) {
+    static std::mutex mu;
+    static std::map<const void *, size_t> raised;
+    std::lock_guard<std::mutex> lk(mu);
+    size_t &have = raised[kern];
+    if (smem <= have) return hipSuccess;
+    const hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    if (e == hipSuccess) have = smem;
+    return e;
 }
 
 }  // namespace coli
@@ -142,8 +163,9 @@ int coli_moe_route(const coli_moe_dims *d, int32_t S, const float *x, const floa
     uint8_t *w8 = static_cast<uint8_t *>(ws);
     uint32_t *status = reinterpret_cast<uint32_t *>(w8 + L.status);
     float *logits = reinterpret_cast<float *>(w8 + L.logits);
+    hipError_t e;
     timing_before(KK_ROUTER_LOGITS, st);
-    hipError_t e = launch_router_logits(x, router_w, logits, status, S, d->hidden, d->n_experts, st);
+    e = launch_router_logits(x, router_w, logits, status, S, d->hidden, d->n_experts, st);
     timing_after(KK_ROUTER_LOGITS, st);
     if (e != hipSuccess) return hip_fail(e, "router logits launch");
     timing_before(KK_ROUTER_SELECT, st);
@@ -202,6 +224,21 @@ int coli_moe_forward(const coli_moe_dims *d, int32_t S, const float *x, const in
             }
     }
     hipError_t e;
+    if (g_force_path == 2 && !use_persistent(d, S, any_pending))
+        return fail(COLI_EINVAL, "persistent kernel forced but the call has pending experts, more than 8 tokens "
+                                 "or a shape beyond its LDS budget");
+    if (use_persistent(d, S, any_pending)) {
+        LayerArgs l;
+        std::memset(&l, 0, sizeof l);
+        l.qx = reinterpret_cast<int8_t *>(w8 + L.qx);
+        l.dx = reinterpret_cast<float *>(w8 + L.dx);
+        l.sync = reinterpret_cast<uint32_t *>(w8) + WS_SYNC_LAYER;
+        timing_before(KK_FORWARD_PERSISTENT, st);
+        e = launch_layer(a, l, false, d->wbits, st);
+        timing_after(KK_FORWARD_PERSISTENT, st);
+        if (e != hipSuccess) return hip_fail(e, "forward launch");
+        return COLI_OK;
+    }
     if (any_pending) {
         a.pend_mode = 1;  // resident experts first
         timing_before(KK_GATEUP, st);
@@ -226,6 +263,68 @@ int coli_moe_forward(const coli_moe_dims *d, int32_t S, const float *x, const in
     e = launch_combine(a, st);
     timing_after(KK_COMBINE, st);
     if (e != hipSuccess) return hip_fail(e, "combine launch");
+    return COLI_OK;
+}
+
+int coli_moe_layer(const coli_moe_dims *d, int32_t S, const float *x, const float *router_w,
+                   const float *router_bias, const void *const *expert_blobs, const void *shared_blob,
+                   int32_t *topk_idx, float *topk_w, float *out, void *ws, size_t ws_bytes, void *stream) {
+    int rc = check_dims(d);
+    if (rc) return rc;
+    if (S < 0) return fail(COLI_EINVAL, "n_tokens=%d < 0", S);
+    if (S == 0) return COLI_OK;
+    if (!x || !router_w || !expert_blobs || !topk_idx || !topk_w || !out || !ws)
+        return fail(COLI_EINVAL, "coli_moe_layer: NULL pointer argument");
+    if (d->n_shared && !shared_blob) return fail(COLI_ENOTRESIDENT, "n_shared=1 but shared_blob is NULL");
+    const WsLayout L = ws_layout(d->hidden, d->inter, d->n_experts, d->top_k, S);
+    if (ws_bytes < L.total)
+        return fail(COLI_EWORKSPACE, "workspace %zu bytes < %zu needed for %d tokens", ws_bytes, L.total, S);
+    if (g_force_path == 2 && !use_persistent(d, S, false))
+        return fail(COLI_EINVAL, "persistent kernel forced but the call has more than 8 tokens or a shape beyond "
+                                 "its LDS budget");
+    if (!use_persistent(d, S, false)) {
+        rc = coli_moe_route(d, S, x, router_w, router_bias, topk_idx, topk_w, ws, ws_bytes, stream);
+        if (rc) return rc;
+        return coli_moe_forward(d, S, x, topk_idx, topk_w, expert_blobs, shared_blob, nullptr, nullptr, out, ws,
+                                ws_bytes, stream);
+    }
+    if ((rc = check_device())) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    uint8_t *w8 = static_cast<uint8_t *>(ws);
+    FwdArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.x = x;
+    a.idx = topk_idx;
+    a.w = topk_w;
+    a.blobs = reinterpret_cast<const uint8_t *const *>(expert_blobs);
+    a.shared = static_cast<const uint8_t *>(shared_blob);
+    a.qh = reinterpret_cast<int8_t *>(w8 + L.qh);
+    a.dh = reinterpret_cast<float *>(w8 + L.dh);
+    a.Y = reinterpret_cast<float *>(w8 + L.Y);
+    a.out = out;
+    a.status = reinterpret_cast<uint32_t *>(w8 + L.status);
+    a.S = S;
+    a.H = d->hidden;
+    a.I = d->inter;
+    a.E = d->n_experts;
+    a.K = d->top_k;
+    a.n_shared = d->n_shared;
+    LayerArgs l;
+    std::memset(&l, 0, sizeof l);
+    l.router_w = router_w;
+    l.bias = router_bias;
+    l.idx_out = topk_idx;
+    l.w_out = topk_w;
+    l.logits = reinterpret_cast<float *>(w8 + L.logits);
+    l.rsf = d->routed_scaling_factor;
+    l.norm = d->norm_topk_prob;
+    l.qx = reinterpret_cast<int8_t *>(w8 + L.qx);
+    l.dx = reinterpret_cast<float *>(w8 + L.dx);
+    l.sync = reinterpret_cast<uint32_t *>(w8) + WS_SYNC_LAYER;
+    timing_before(KK_LAYER, st);
+    hipError_t e = launch_layer(a, l, true, d->wbits, st);
+    timing_after(KK_LAYER, st);
+    if (e != hipSuccess) return hip_fail(e, "layer launch");
     return COLI_OK;
 }
 
@@ -257,6 +356,8 @@ int coli_moe_status(void *ws, void *stream) {
     if (s == 0) return COLI_OK;
     e = hipMemset(ws, 0, sizeof s);
     if (e != hipSuccess) return hip_fail(e, "status clear");
+    if (s & ST_TIMEOUT)
+        return fail(COLI_EHIP, "a persistent kernel's grid barrier timed out: not all workgroups were resident (status 0x%x)", s);
     if (s & ST_BADINDEX) return fail(COLI_EINVAL, "expert index out of range or repeated within a token (status 0x%x)", s);
     if (s & ST_NONFINITE) return fail(COLI_ENONFINITE, "non-finite input or undefined gate weights (status 0x%x)", s);
     return fail(COLI_ENOTRESIDENT, "a routed expert blob was NULL (status 0x%x)", s);
@@ -288,6 +389,12 @@ int coli_moe_timing_read(int32_t kind, double *total_ms, int64_t *launches) {
     g_timing.done[kind].clear();
     *total_ms = tot;
     *launches = n;
+    return COLI_OK;
+}
+
+int coli_moe_debug_force_path(int32_t path) {
+    if (path < 0 || path > 2) return fail(COLI_EINVAL, "path must be 0, 1 or 2");
+    g_force_path = path;
     return COLI_OK;
 }
 

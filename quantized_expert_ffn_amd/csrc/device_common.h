@@ -24,6 +24,7 @@ enum : uint32_t {
     ST_NONFINITE = 1u,     // NaN/Inf in x, W_r, bias, logits or gate weights
     ST_BADINDEX = 2u,      // expert index out of range or repeated in a token
     ST_NOTRESIDENT = 4u,   // routed expert blob pointer is NULL
+    ST_TIMEOUT = 8u,       // a grid barrier of a persistent kernel gave up waiting
 };
 
 __device__ __forceinline__ void raise_status(uint32_t *status, uint32_t bit) {
@@ -199,6 +200,33 @@ template <>
 __device__ __forceinline__ BlockBits<2> load_block<2>(__amdgpu_buffer_rsrc_t r, uint32_t row_off, int b) {
     BlockBits<2> v;
     v.w = __builtin_amdgcn_raw_buffer_load_b64(r, 8 * b, row_off, BUF_NT);
+    return v;
+}
+
+// The same blocks read through a plain global pointer (row start + block).
+typedef __attribute__((address_space(1))) const u32x4 g_u32x4;
+typedef __attribute__((address_space(1))) const u32x2 g_u32x2;
+
+template <int BITS>
+__device__ __forceinline__ BlockBits<BITS> load_block_ptr(const uint8_t *row, int b);
+template <>
+__device__ __forceinline__ BlockBits<8> load_block_ptr<8>(const uint8_t *row, int b) {
+    g_u32x4 *p = (g_u32x4 *)(row + 32 * b);
+    BlockBits<8> v;
+    v.w0 = __builtin_nontemporal_load(p);
+    v.w1 = __builtin_nontemporal_load(p + 1);
+    return v;
+}
+template <>
+__device__ __forceinline__ BlockBits<4> load_block_ptr<4>(const uint8_t *row, int b) {
+    BlockBits<4> v;
+    v.w = __builtin_nontemporal_load((g_u32x4 *)(row + 16 * b));
+    return v;
+}
+template <>
+__device__ __forceinline__ BlockBits<2> load_block_ptr<2>(const uint8_t *row, int b) {
+    BlockBits<2> v;
+    v.w = __builtin_nontemporal_load((g_u32x2 *)(row + 8 * b));
     return v;
 }
 

@@ -28,249 +28,9 @@
 
 #include "device_common.h"
 #include "kernels.h"
+#include "stream.h"
 
 namespace coli {
-
-constexpr int ROWS_PER_WAVE = 16;
-constexpr int ISUM_PITCH = 68;  // padded row of block dots: 16-byte aligned, few bank conflicts
-
-struct SmemPlan {
-    size_t cnt, ustart, fill, uexp, uoff, pairs, misc, vq, vd, isum, gu, total;
-};
-
-__host__ __device__ inline size_t a16(size_t v) { return (v + 15) & ~(size_t)15; }
-
-// Values read from LDS that are the same in every lane: moving them to a
-// scalar register lets the compiler address weights with scalar bases.
-__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
-
-template <typename T>
-__device__ __forceinline__ T *uniform_ptr(T *p) {
-    const uint64_t v = reinterpret_cast<uint64_t>(p);
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-    return reinterpret_cast<T *>(((uint64_t)hi << 32) | lo);
-}
-
-// Per-vector stride of the staged block scales (a multiple of 4 so every
-// chunk of 64 scales starts 16-byte aligned).
-__host__ __device__ inline int vd_stride(int nb) { return (nb + 3) & ~3; }
-
-__host__ __device__ inline SmemPlan smem_plan(int S, int K, int E, int NT, int vlen) {
-    SmemPlan p;
-    const int P = S * K;
-    const int umax = (P < E ? P : E) + 1;
-    p.cnt = 0;
-    p.ustart = a16(p.cnt + 4 * (size_t)E);
-    p.fill = a16(p.ustart + 4 * (size_t)E);
-    p.uexp = a16(p.fill + 4 * (size_t)E);
-    p.uoff = a16(p.uexp + 4 * (size_t)umax);
-    p.pairs = a16(p.uoff + 4 * (size_t)(umax + 1));
-    p.misc = a16(p.pairs + 4 * (size_t)(P + S));
-    p.vq = a16(p.misc + 16);
-    p.vd = a16(p.vq + (size_t)NT * vlen);
-    p.isum = a16(p.vd + 4 * (size_t)NT * vd_stride(vlen / 32));
-    p.gu = a16(p.isum + 4 * (size_t)NT * 64 * ISUM_PITCH);
-    p.total = a16(p.gu + 4 * (size_t)NT * 64);
-    return p;
-}
-
-// Builds the unit table in LDS.  Pair p = t*K + k is routed pair (t, k); the
-// shared expert's entry for token t is P + t.  Units: experts present in
-// topk_idx in ascending id, then the shared expert.  The order of pairs
-// inside a unit does not affect any value (every pair has its own output
-// slot and its own chain).  With `validate`, out-of-range and repeated
-// indices are flagged in the status word.
-__device__ void build_units(const int32_t *__restrict__ idx, int S, int K, int E, int n_shared,
-                            uint8_t *smem, const SmemPlan &L, uint32_t *status, bool validate) {
-    int *cnt = reinterpret_cast<int *>(smem + L.cnt);
-    int *ustart = reinterpret_cast<int *>(smem + L.ustart);
-    int *fill = reinterpret_cast<int *>(smem + L.fill);
-    int *uexp = reinterpret_cast<int *>(smem + L.uexp);
-    int *uoff = reinterpret_cast<int *>(smem + L.uoff);
-    int *pairs = reinterpret_cast<int *>(smem + L.pairs);
-    int *misc = reinterpret_cast<int *>(smem + L.misc);
-    const int tid = threadIdx.x, nthr = blockDim.x;
-    const int P = S * K;
-    for (int e = tid; e < E; e += nthr) {
-        cnt[e] = 0;
-        fill[e] = 0;
-    }
-    __syncthreads();
-    for (int p = tid; p < P; p += nthr) {
-        const int e = idx[p];
-        if (e >= 0 && e < E) {
-            atomicAdd(&cnt[e], 1);
-            if (validate) {
-                const int t0 = (p / K) * K;
-                for (int q = t0; q < p; ++q)
-                    if (idx[q] == e) raise_status(status, ST_BADINDEX);
-            }
-        } else if (validate) {
-            raise_status(status, ST_BADINDEX);
-        }
-    }
-    __syncthreads();
-    if (tid < 64) {
-        const int per = (E + 63) / 64;
-        const int e0 = tid * per;
-        int sp = 0, su = 0;
-        for (int i = 0; i < per; ++i) {
-            const int e = e0 + i;
-            if (e < E) {
-                sp += cnt[e];
-                su += cnt[e] > 0 ? 1 : 0;
-            }
-        }
-        int ip = sp, iu = su;
-        for (int o = 1; o < 64; o <<= 1) {
-            const int a = __shfl_up(ip, o, 64);
-            const int b = __shfl_up(iu, o, 64);
-            if (tid >= o) {
-                ip += a;
-                iu += b;
-            }
-        }
-        int xp = ip - sp, xu = iu - su;
-        for (int i = 0; i < per; ++i) {
-            const int e = e0 + i;
-            if (e < E) {
-                ustart[e] = xp;
-                if (cnt[e] > 0) {
-                    uexp[xu] = e;
-                    uoff[xu] = xp;
-                    ++xu;
-                }
-                xp += cnt[e];
-            }
-        }
-        if (tid == 63) {
-            misc[1] = iu;  // routed units
-            misc[2] = ip;  // valid routed pairs
-        }
-    }
-    __syncthreads();
-    for (int p = tid; p < P; p += nthr) {
-        const int e = idx[p];
-        if (e >= 0 && e < E) pairs[ustart[e] + atomicAdd(&fill[e], 1)] = p;
-    }
-    const int nr = misc[1], pv = misc[2];
-    if (n_shared)
-        for (int t = tid; t < S; t += nthr) pairs[pv + t] = P + t;
-    if (tid == 0) {
-        uoff[nr] = pv;
-        if (n_shared) {
-            uexp[nr] = -1;
-            uoff[nr + 1] = pv + S;
-        }
-        misc[0] = nr + (n_shared ? 1 : 0);
-    }
-    __syncthreads();
-}
-
-__device__ __forceinline__ void load_act(const int8_t *vq, int b, int32_t a[8]) {
-    const i32x4 *p = reinterpret_cast<const i32x4 *>(vq + 32 * b);
-    const i32x4 lo = p[0], hi = p[1];
-    a[0] = lo.x; a[1] = lo.y; a[2] = lo.z; a[3] = lo.w;
-    a[4] = hi.x; a[5] = hi.y; a[6] = hi.z; a[7] = hi.w;
-}
-
-// Makes this wave's LDS writes visible to its own later reads (LDS
-// operations of one wave complete in order; the fence orders them for the
-// compiler and waits for outstanding LDS traffic).
-__device__ __forceinline__ void wave_lds_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-}
-
-// Binary32 chain of one chunk for one (row, vector): acc = fmaf(d_b, isum_b,
-// acc) for the chunk's blocks in ascending order.  A full chunk is unrolled
-// with 16-byte LDS reads so the reads are all in flight before the chain.
-__device__ __forceinline__ float chain_chunk(float acc, const int32_t *is, const float *dv, int nbc) {
-    if (nbc == 64) {
-        // four quarters of 16 blocks; within a quarter all LDS reads are issued first
-#pragma unroll 1
-        for (int qq = 0; qq < 64; qq += 16) {
-            i32x4 iv[4];
-            f32x4 dd[4];
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                iv[q4] = *reinterpret_cast<const i32x4 *>(is + qq + 4 * q4);
-                dd[q4] = *reinterpret_cast<const f32x4 *>(dv + qq + 4 * q4);
-            }
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                acc = __builtin_fmaf(dd[q4].x, (float)iv[q4].x, acc);
-                acc = __builtin_fmaf(dd[q4].y, (float)iv[q4].y, acc);
-                acc = __builtin_fmaf(dd[q4].z, (float)iv[q4].z, acc);
-                acc = __builtin_fmaf(dd[q4].w, (float)iv[q4].w, acc);
-            }
-        }
-    } else {
-        for (int bb = 0; bb < nbc; ++bb) acc = __builtin_fmaf(dv[bb], (float)is[bb], acc);
-    }
-    return acc;
-}
-
-// Streams this wave's 16 rows for the ng staged vectors.  Returns, in lane
-// (row = lane & 15, vector = lane >> 4), the chain fmaf(d_b, isum_b, acc)
-// over all blocks of that row in ascending order.  `stage()` fills the LDS
-// vectors and ends with a workgroup barrier; it runs after the first chunk's
-// weight loads are issued so that their latency overlaps it.  Each wave then
-// works alone on its own LDS region; for int4 / int2 the next chunk's
-// weights are in flight while the current chunk is reduced.
-template <int BITS, int NT, typename Stage>
-__device__ __forceinline__ float stream_rows(__amdgpu_buffer_rsrc_t rsrc,
-                                             const uint32_t rowoff[ROWS_PER_WAVE], int nb,
-                                             int ng, const int8_t *vq, const float *vd,
-                                             int32_t *isum_wave, int vlen, Stage stage) {
-    constexpr bool PREFETCH = BITS < 8;
-    const int lane = threadIdx.x & 63;
-    const int crow = lane & 15, cvec = lane >> 4;
-    const int vds = vd_stride(nb);
-    float acc = 0.0f;
-    const int nchunks = (nb + 63) / 64;
-    BlockBits<BITS> cur[ROWS_PER_WAVE];
-    if (lane < nb) {
-#pragma unroll
-        for (int j = 0; j < ROWS_PER_WAVE; ++j) cur[j] = load_block<BITS>(rsrc, rowoff[j], lane);
-    }
-    stage();
-    for (int c = 0; c < nchunks; ++c) {
-        const int b = c * 64 + lane;
-        const bool act = b < nb;
-        BlockBits<BITS> nxt[ROWS_PER_WAVE];
-        if (PREFETCH && b + 64 < nb) {
-#pragma unroll
-            for (int j = 0; j < ROWS_PER_WAVE; ++j) nxt[j] = load_block<BITS>(rsrc, rowoff[j], b + 64);
-        }
-#pragma unroll
-        for (int it = 0; it < NT; ++it) {
-            if (it < ng) {
-                int32_t av[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-                if (act) load_act(vq + (size_t)it * vlen, b, av);
-                int32_t *dst = isum_wave + it * ROWS_PER_WAVE * ISUM_PITCH + lane;
-#pragma unroll
-                for (int j = 0; j < ROWS_PER_WAVE; ++j)
-                    dst[j * ISUM_PITCH] = act ? block_dot(cur[j], av) : 0;
-            }
-        }
-        wave_lds_sync();
-        if (cvec < ng)
-            acc = chain_chunk(acc, isum_wave + (cvec * ROWS_PER_WAVE + crow) * ISUM_PITCH,
-                              vd + cvec * vds + c * 64, min(64, nb - c * 64));
-        wave_lds_sync();
-        if (PREFETCH) {
-#pragma unroll
-            for (int j = 0; j < ROWS_PER_WAVE; ++j) cur[j] = nxt[j];
-        } else if (c + 1 < nchunks && b + 64 < nb) {
-#pragma unroll
-            for (int j = 0; j < ROWS_PER_WAVE; ++j) cur[j] = load_block<BITS>(rsrc, rowoff[j], b + 64);
-        }
-    }
-    return acc;
-}
 
 template <int BITS, int NT>
 __global__ __launch_bounds__(256) void k_gateup(const FwdArgs a) {
@@ -336,7 +96,9 @@ __global__ __launch_bounds__(256) void k_gateup(const FwdArgs a) {
             }
             __syncthreads();
         };
-        const float acc = stream_rows<BITS, NT>(rsrc, rowoff, nb, ng, vq, vd, isum_wave, H, stage);
+        BlockBits<BITS> cur[ROWS_PER_WAVE];
+        prime_rows<BITS, ROWS_PER_WAVE>(rsrc, rowoff, nb, cur);
+        const float acc = stream_rows<BITS, NT, ROWS_PER_WAVE>(rsrc, rowoff, nb, ng, vq, vd, isum_wave, H, stage, cur);
         if (cvec < ng) gu[cvec * 64 + wave * ROWS_PER_WAVE + crow] = acc * scale[i0 + 16 * half + crow];
         __syncthreads();
         // SwiGLU and Q8_0(h): half-wave (tid >> 5) handles one vector's 32 rows.
@@ -407,7 +169,9 @@ __global__ __launch_bounds__(256) void k_down(const FwdArgs a) {
             }
             __syncthreads();
         };
-        const float acc = stream_rows<BITS, NT>(rsrc, rowoff, nb, ng, vq, vd, isum_wave, I, stage);
+        BlockBits<BITS> cur[ROWS_PER_WAVE];
+        prime_rows<BITS, ROWS_PER_WAVE>(rsrc, rowoff, nb, cur);
+        const float acc = stream_rows<BITS, NT, ROWS_PER_WAVE>(rsrc, rowoff, nb, ng, vq, vd, isum_wave, I, stage, cur);
         if (cvec < ng) {
             const int slot = pairs[p0 + g0 + cvec];
             a.Y[(size_t)slot * H + rw + crow] = acc * s_down[rw + crow];
@@ -445,18 +209,10 @@ size_t forward_smem_max(int S, int H, int I, int E, int K, int n_shared) {
     return std::max(smem_plan(S, K, E, nt, H).total, smem_plan(S, K, E, nt, I).total);
 }
 
-// Raises a kernel's dynamic-LDS limit once to the largest size it has been
-// launched with (so that later launches, including ones under stream capture,
-// only enqueue work).  Calls come from one host thread at a time per kernel.
 template <typename F>
 static hipError_t launch_dyn(F kern, dim3 grid, size_t smem, hipStream_t st, const FwdArgs &a) {
-    static size_t raised = 0;
-    if (smem > raised) {
-        hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-        if (err != hipSuccess) return err;
-        raised = smem;
-    }
+    const hipError_t err = ensure_dyn_smem(reinterpret_cast<const void *>(kern), smem);
+    if (err != hipSuccess) return err;
     hipLaunchKernelGGL(kern, grid, dim3(256), smem, st, a);
     return hipGetLastError();
 }

@@ -9,8 +9,12 @@ namespace coli {
 // Workspace carve-up for a call with S tokens.  The status word sits at a
 // fixed offset (it persists between calls); the rest is per call.
 struct WsLayout {
-    size_t status, logits, qh, dh, Y, total;
+    size_t status, logits, qx, dx, qh, dh, Y, total;
 };
+
+// Word index, inside the first 256 bytes of the workspace, of the three
+// barrier words of the persistent layer kernel.
+constexpr int WS_SYNC_LAYER = 32;
 
 inline size_t al256h(size_t v) { return (v + 255) & ~(size_t)255; }
 
@@ -19,7 +23,9 @@ inline WsLayout ws_layout(int H, int I, int E, int K, int S) {
     const size_t slots = (size_t)S * (size_t)(K + 1);
     L.status = 0;
     L.logits = 256;
-    L.qh = al256h(L.logits + 4 * (size_t)S * (size_t)E);
+    L.qx = al256h(L.logits + 4 * (size_t)S * (size_t)E);
+    L.dx = al256h(L.qx + (size_t)S * (size_t)H);
+    L.qh = al256h(L.dx + 4 * (size_t)S * (size_t)(H / 32));
     L.dh = al256h(L.qh + slots * (size_t)I);
     L.Y = al256h(L.dh + 4 * slots * (size_t)(I / 32));
     L.total = al256h(L.Y + 4 * slots * (size_t)H);
@@ -56,12 +62,36 @@ enum KernelKind {
     KK_GATEUP = 2,
     KK_DOWN = 3,
     KK_COMBINE = 4,
+    KK_LAYER = 5,
+    KK_FORWARD_PERSISTENT = 6,
     KK_COUNT = 8
 };
 
 // Timing hooks implemented by the API layer.
+// Raises `kern`'s dynamic-LDS limit to at least `smem` bytes (once per
+// kernel and size, so launches under stream capture only enqueue work).
+hipError_t ensure_dyn_smem(const void *kern, size_t smem);
 void timing_before(int kind, hipStream_t st);
 void timing_after(int kind, hipStream_t st);
+
+// Extra arguments of the persistent layer kernel.
+struct LayerArgs {
+    const float *router_w;   // [E, H]   (routing computed in the kernel)
+    const float *bias;       // [E] or null
+    int32_t *idx_out;        // [S, K]   routing written by the kernel
+    float *w_out;            // [S, K]
+    float *logits;           // [S, E]   workspace
+    float rsf;
+    int norm;
+    int8_t *qx;              // [S, H]   workspace: Q8_0(x)
+    float *dx;               // [S, H/32]
+    uint32_t *sync;          // 3 barrier words in the workspace
+};
+
+// The persistent layer kernel: route = true computes the routing itself
+// (coli_moe_layer); route = false takes it from the arguments (coli_moe_forward).
+hipError_t launch_layer(const FwdArgs &a, const LayerArgs &l, bool route, int bits, hipStream_t st);
+size_t layer_smem(int S, int H, int I, int E, int K, int n_shared);
 
 hipError_t launch_gateup(const FwdArgs &a, int bits, hipStream_t st);
 hipError_t launch_down(const FwdArgs &a, int bits, hipStream_t st);

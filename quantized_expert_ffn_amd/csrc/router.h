@@ -1,0 +1,156 @@
+// Router device routines ("Colibri (colibrì): GLM-5.2 local inference on
+// 25 GB of RAM", "How it works (validated core mechanics)"; colibrì README
+// v1.0 "What's implemented": DeepSeek-V3-style sigmoid router with
+// routed_scaling_factor): one router logit per wavefront in the layer's fixed
+// order, and the bias-corrected top-K selection with renormalised weights.
+#pragma once
+
+#include "device_common.h"
+
+namespace coli {
+
+// Logit of one (token, expert) by one wavefront.  Lane l accumulates, with
+// fmaf from 0, the elements h = 256 j + 4 l + c for j ascending and c = 0..3
+// (a float4 per lane per step: each step reads 1 KB of the gate row
+// coalesced); then six xor-butterfly additions p_l + p_{l^o}, o = 32..1,
+// leave the logit in every lane.  Up to MAXJ steps of the row are loaded
+// before the chain starts.  *ok is cleared on a non-finite input.
+template <int MAXJ>
+__device__ __forceinline__ float logit_wave(const float *__restrict__ xrow,
+                                            const float *__restrict__ wrow, int H, bool *ok) {
+    const int lane = threadIdx.x & 63;
+    const f32x4 *xr = reinterpret_cast<const f32x4 *>(xrow);
+    const f32x4 *wr = reinterpret_cast<const f32x4 *>(wrow);
+    const int steps = H / 256;
+    float p = 0.0f;
+    bool good = true;
+    for (int j0 = 0; j0 < steps; j0 += MAXJ) {
+        f32x4 xv[MAXJ], wv[MAXJ];
+#pragma unroll
+        for (int jj = 0; jj < MAXJ; ++jj)
+            if (j0 + jj < steps) {
+                wv[jj] = __builtin_nontemporal_load(wr + 64 * (j0 + jj) + lane);
+                xv[jj] = xr[64 * (j0 + jj) + lane];
+            }
+#pragma unroll
+        for (int jj = 0; jj < MAXJ; ++jj) {
+            if (j0 + jj < steps) {
+                p = __builtin_fmaf(xv[jj].x, wv[jj].x, p);
+                p = __builtin_fmaf(xv[jj].y, wv[jj].y, p);
+                p = __builtin_fmaf(xv[jj].z, wv[jj].z, p);
+                p = __builtin_fmaf(xv[jj].w, wv[jj].w, p);
+                good = good && finite_f32(xv[jj].x) && finite_f32(xv[jj].y) &&
+                       finite_f32(xv[jj].z) && finite_f32(xv[jj].w) && finite_f32(wv[jj].x) &&
+                       finite_f32(wv[jj].y) && finite_f32(wv[jj].z) && finite_f32(wv[jj].w);
+            }
+        }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) p = p + __shfl_xor(p, o, 64);
+    *ok = good && finite_f32(p);
+    return p;
+}
+
+// ---- wavefront reductions through DPP (result uniform across the wave) ----
+// LDS writes of this wave made visible to its own later reads.
+__device__ __forceinline__ void wave_and_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ int dpp(int v) {
+    return __builtin_amdgcn_update_dpp(v, v, CTRL, ROWS, 0xF, false);
+}
+
+__device__ __forceinline__ float wave_max_f32(float v) {
+    int i = __float_as_int(v);
+    i = __float_as_int(__builtin_fmaxf(__int_as_float(i), __int_as_float(dpp<0xB1>(i))));  // quad [1,0,3,2]
+    i = __float_as_int(__builtin_fmaxf(__int_as_float(i), __int_as_float(dpp<0x4E>(i))));  // quad [2,3,0,1]
+    i = __float_as_int(__builtin_fmaxf(__int_as_float(i), __int_as_float(dpp<0x141>(i)))); // row half mirror
+    i = __float_as_int(__builtin_fmaxf(__int_as_float(i), __int_as_float(dpp<0x140>(i)))); // row mirror
+    i = __float_as_int(__builtin_fmaxf(__int_as_float(i), __int_as_float(dpp<0x142, 0xA>(i))));  // row bcast 15
+    i = __float_as_int(__builtin_fmaxf(__int_as_float(i), __int_as_float(dpp<0x143, 0xC>(i))));  // row bcast 31
+    return __int_as_float(__builtin_amdgcn_readlane(i, 63));
+}
+
+__device__ __forceinline__ int wave_min_i32(int v) {
+    v = min(v, dpp<0xB1>(v));
+    v = min(v, dpp<0x4E>(v));
+    v = min(v, dpp<0x141>(v));
+    v = min(v, dpp<0x140>(v));
+    v = min(v, dpp<0x142, 0xA>(v));
+    v = min(v, dpp<0x143, 0xC>(v));
+    return __builtin_amdgcn_readlane(v, 63);
+}
+
+// Selection for one token by one wavefront (sig_s: LDS scratch of E floats,
+// sel_sig: LDS scratch of K floats).  Lane l owns experts l, l+64, ...;
+// sig = sigmoid(logit), score = sig + bias.  K rounds pick the experts in
+// rank order under the total order (score desc, id asc): the wavefront
+// maximum of the lanes' best remaining scores, then the smallest id holding
+// it.  Gate weights: (sig_k / ((sig_0 + sig_1) + ...)) * rsf, or sig_k * rsf
+// without renormalisation.  load_logit(e) returns the token's logit e.
+// E <= 1024, K <= 32.  Returns false on a non-finite input or zero weights.
+template <typename LoadLogit>
+__device__ __forceinline__ bool select_wave(LoadLogit load_logit, const float *__restrict__ bias,
+                                            int E, int K, float rsf, int norm,
+                                            int32_t *__restrict__ idx_out,
+                                            float *__restrict__ w_out, float *sig_s,
+                                            float *sel_sig) {
+    constexpr int MAXM = 16;
+    const int lane = threadIdx.x & 63;
+    const int mcount = (E + 63) / 64;
+    float score[MAXM];
+    uint32_t taken = 0;
+    bool ok = true;
+#pragma unroll
+    for (int m = 0; m < MAXM; ++m) {
+        const int e = lane + 64 * m;
+        score[m] = -__builtin_inff();
+        if (m < mcount && e < E) {
+            const float l = load_logit(e);
+            const float b = bias ? bias[e] : 0.0f;
+            ok = ok && finite_f32(l) && finite_f32(b);
+            const float sg = sigmoid_f32(l);
+            sig_s[e] = sg;
+            score[m] = sg + b;
+        }
+    }
+    wave_and_lds_sync();
+    for (int k = 0; k < K; ++k) {
+        float bs = -__builtin_inff();
+        int be = 0x7fffffff;
+#pragma unroll
+        for (int m = 0; m < MAXM; ++m) {
+            if (m < mcount && !((taken >> m) & 1u) && score[m] > bs) {
+                bs = score[m];
+                be = lane + 64 * m;
+            }
+        }
+        const float M = wave_max_f32(bs);
+        int sel = wave_min_i32(bs == M ? be : 0x7fffffff);
+        if (sel >= E) sel = k;  // only reachable with NaN scores, flagged below
+        if ((sel & 63) == lane) taken |= 1u << (sel >> 6);
+        if (lane == 0) {
+            idx_out[k] = sel;
+            sel_sig[k] = sig_s[sel];
+        }
+    }
+    wave_and_lds_sync();
+    bool wok = true;
+    if (lane == 0) {
+        if (norm) {
+            float denom = sel_sig[0];
+            for (int k = 1; k < K; ++k) denom = denom + sel_sig[k];
+            wok = denom > 0.0f && finite_f32(denom);
+            for (int k = 0; k < K; ++k) w_out[k] = (sel_sig[k] / denom) * rsf;
+        } else {
+            for (int k = 0; k < K; ++k) w_out[k] = sel_sig[k] * rsf;
+        }
+    }
+    return __builtin_amdgcn_readfirstlane((int)(ok && wok)) != 0;
+}
+
+}  // namespace coli

@@ -21,6 +21,15 @@ def torch():
     return t
 
 
+@pytest.fixture(params=["multi", "persistent"])
+def path(request, torch):
+    """Runs a test with the multi-launch kernels or the persistent ones."""
+    qm = q()
+    qm.coli_moe_debug_force_path(qm.PATH_MULTI if request.param == "multi" else qm.PATH_PERSISTENT)
+    yield request.param
+    qm.coli_moe_debug_force_path(qm.PATH_AUTO)
+
+
 def _layer(spec, S, seed=0):
     d = synth.tiny_layer(seed=seed, S=S, spec=spec)
     return d
@@ -43,8 +52,8 @@ def _oracle(spec, d):
     return out, idx, w
 
 
-def test_tiny_layer_bitexact(torch):
-    say("tiny layer S=4 int4")
+def test_tiny_layer_bitexact(torch, path):
+    say(f"tiny layer S=4 int4 [{path}]")
     spec = synth.TINY
     d = _layer(spec, 4)
     _, _, _, idx, w, out, rc = _run(torch, spec, d)
@@ -55,9 +64,11 @@ def test_tiny_layer_bitexact(torch):
     parity(out, o_out)
 
 
-@pytest.mark.parametrize("S", [1, 2, 3, 5, 9, 17])
-def test_tiny_ragged_token_counts(torch, S):
-    say(f"tiny layer S={S}")
+@pytest.mark.parametrize("S", [1, 2, 3, 5, 8, 9, 17])
+def test_tiny_ragged_token_counts(torch, path, S):
+    if path == "persistent" and S > 8:
+        pytest.skip("the persistent forward takes at most 8 tokens")
+    say(f"tiny layer S={S} [{path}]")
     spec = synth.TINY
     d = _layer(spec, S, seed=S)
     _, _, _, idx, w, out, rc = _run(torch, spec, d)
@@ -74,8 +85,8 @@ def test_tiny_ragged_token_counts(torch, S):
     dataclasses.replace(synth.TINY, n_experts=40, top_k=6, hidden=512, inter=96),
     dataclasses.replace(synth.TINY, norm_topk_prob=0, routed_scaling_factor=1.5, n_experts=70, top_k=9),
 ], ids=["int8", "int2", "k1-noshared", "e40-h512-i96", "nonorm-e70-k9"])
-def test_tiny_variants(torch, spec):
-    say(f"tiny variant {spec}")
+def test_tiny_variants(torch, path, spec):
+    say(f"tiny variant {spec} [{path}]")
     d = _layer(spec, 5, seed=11)
     _, _, _, idx, w, out, rc = _run(torch, spec, d)
     assert rc == 0, q().coli_moe_last_error()
@@ -85,9 +96,9 @@ def test_tiny_variants(torch, spec):
     parity(out, o_out)
 
 
-def test_batch_invariance(torch):
+def test_batch_invariance(torch, path):
     """A token's output bits do not depend on which other tokens share the call."""
-    say("batch invariance")
+    say(f"batch invariance [{path}]")
     from synth.device import upload_layer
     spec = synth.TINY
     d = _layer(spec, 6, seed=21)
@@ -144,8 +155,8 @@ def test_router_worked_examples_through_the_abi(torch):
     assert rc == q().COLI_ENONFINITE
 
 
-def test_error_contract(torch):
-    say("error contract")
+def test_error_contract(torch, path):
+    say(f"error contract [{path}]")
     from synth.device import upload_layer
     qm = q()
     spec = synth.TINY
@@ -256,10 +267,11 @@ def _glm_layer_for_tokens(torch, spec, S, seed, x=None, layer=0):
     return d, dims, dl, ws, idx, w, used
 
 
-def test_glm_decode_one_token(torch):
+def test_glm_decode_one_token(torch, path):
     """GLM-5.2-shaped decode layer (H 6144, I 2048, 256 experts top-8 + shared,
-    int4, 1 token) in the launch configuration the benchmark times."""
-    say("glm decode S=1 int4")
+    int4, 1 token); the persistent kernels are the launch configuration the
+    benchmark times."""
+    say(f"glm decode S=1 int4 [{path}]")
     spec = synth.GLM
     d, dims, dl, ws, idx, w, used = _glm_layer_for_tokens(torch, spec, 1, seed=0)
     o_idx, o_w, _, _ = oracle.route(spec, d["x"], d["router_w"], d["bias"])
@@ -272,10 +284,10 @@ def test_glm_decode_one_token(torch):
     say("glm decode parity", r)
 
 
-def test_glm_verify_four_tokens_int8(torch):
+def test_glm_verify_four_tokens_int8(torch, path):
     """Speculative-verify batch: S=4 tokens routed jointly, int8 experts,
     tokens sharing experts (batch-union)."""
-    say("glm verify S=4 int8")
+    say(f"glm verify S=4 int8 [{path}]")
     spec = synth.GLM_INT8
     x = synth.verify_hidden_states(0, 0, spec, 4)
     d, dims, dl, ws, idx, w, used = _glm_layer_for_tokens(torch, spec, 4, seed=0, x=x)
@@ -287,3 +299,140 @@ def test_glm_verify_four_tokens_int8(torch):
     assert status(ws) == 0
     want = oracle.forward(spec, d["x"], o_idx, o_w, d["blobs"], d["shared"])
     parity(out, want)
+
+
+def test_paths_agree_bitwise(torch):
+    """Multi-launch and persistent kernels give the same bits (S = 1..8)."""
+    from synth.device import upload_layer
+    qm = q()
+    spec = synth.TINY
+    for S in (1, 3, 8):
+        say(f"path agreement S={S}")
+        d = _layer(spec, S, seed=40 + S)
+        dims = qm.make_dims(spec)
+        dl = upload_layer(d)
+        ws = workspace(dims, S)
+        outs = []
+        for p in (qm.PATH_MULTI, qm.PATH_PERSISTENT):
+            qm.coli_moe_debug_force_path(p)
+            idx, w = gpu_route(dims, dl, ws)
+            outs.append((idx.cpu().numpy(), gpu_forward(dims, dl, idx, w, ws).cpu().numpy()))
+            assert status(ws) == 0
+        qm.coli_moe_debug_force_path(qm.PATH_AUTO)
+        assert np.array_equal(outs[0][0], outs[1][0])
+        assert np.array_equal(outs[0][1].view(np.uint32), outs[1][1].view(np.uint32))
+
+
+def gpu_layer(torch, dims, dl, ws):
+    S = dl["x"].shape[0]
+    idx = torch.full((S, dims.top_k), -7, dtype=torch.int32, device="cuda")
+    w = torch.full((S, dims.top_k), float("nan"), dtype=torch.float32, device="cuda")
+    out = torch.full((S, dims.hidden), float("nan"), dtype=torch.float32, device="cuda")
+    q().coli_moe_layer(dims, dl["x"], dl["router_w"], dl["bias"], dl["table"], dl["shared"], idx, w, out, ws)
+    return idx.cpu().numpy(), w.cpu().numpy(), out.cpu().numpy()
+
+
+@pytest.mark.parametrize("S", [1, 2, 4, 7, 8, 13])
+def test_layer_entry_tiny(torch, path, S):
+    """coli_moe_layer (router + experts + combine in one call) against the
+    oracle, ragged token counts; above 8 tokens it runs route + forward."""
+    from synth.device import upload_layer
+    say(f"coli_moe_layer tiny S={S} [{path}]")
+    spec = synth.TINY
+    d = _layer(spec, S, seed=70 + S)
+    dims = q().make_dims(spec)
+    dl = upload_layer(d)
+    ws = workspace(dims, S)
+    idx, w, out = gpu_layer(torch, dims, dl, ws)
+    assert status(ws) == 0, q().coli_moe_last_error()
+    o_out, o_idx, o_w = _oracle(spec, d)
+    assert np.array_equal(idx, o_idx)
+    assert np.array_equal(w.view(np.uint32), o_w.view(np.uint32))
+    parity(out, o_out)
+
+
+@pytest.mark.parametrize("spec", [
+    dataclasses.replace(synth.TINY, wbits=8),
+    dataclasses.replace(synth.TINY, wbits=2, n_shared=0, top_k=3),
+    dataclasses.replace(synth.TINY, n_experts=70, top_k=9, hidden=512, inter=96, norm_topk_prob=0),
+], ids=["int8", "int2-k3-noshared", "e70-k9-h512-i96-nonorm"])
+def test_layer_entry_variants(torch, path, spec):
+    from synth.device import upload_layer
+    say(f"coli_moe_layer variant {spec} [{path}]")
+    d = _layer(spec, 5, seed=3)
+    dims = q().make_dims(spec)
+    dl = upload_layer(d)
+    ws = workspace(dims, 5)
+    idx, w, out = gpu_layer(torch, dims, dl, ws)
+    assert status(ws) == 0, q().coli_moe_last_error()
+    o_out, o_idx, o_w = _oracle(spec, d)
+    assert np.array_equal(idx, o_idx)
+    assert np.array_equal(w.view(np.uint32), o_w.view(np.uint32))
+    parity(out, o_out)
+
+
+def _glm_resident_for_oracle_routing(torch, spec, S, seed, x=None, layer=0):
+    """GLM-shaped layer whose resident experts are the ones the oracle routes
+    the tokens to (the others are null in the table)."""
+    from synth.device import blob_table
+    d = synth.layer_inputs(seed, layer, spec, S)
+    if x is not None:
+        d["x"] = x
+    o_idx, o_w, _, _ = oracle.route(spec, d["x"], d["router_w"], d["bias"])
+    used = sorted(set(o_idx.ravel().tolist()))
+    host = {e: synth.expert_blob(seed, layer, e, spec) for e in used}
+    shared = synth.expert_blob(seed, layer, spec.n_experts, spec)
+    blobs = [torch.from_numpy(host[e]).cuda() if e in host else None for e in range(spec.n_experts)]
+    dl = {"x": torch.from_numpy(d["x"]).cuda(), "router_w": torch.from_numpy(d["router_w"]).cuda(),
+          "bias": torch.from_numpy(d["bias"]).cuda(), "blobs": blobs,
+          "table": blob_table(blobs, spec.n_experts), "shared": torch.from_numpy(shared).cuda()}
+    d["blobs"] = [host.get(e) for e in range(spec.n_experts)]
+    d["shared"] = shared
+    return d, dl, o_idx, o_w, used
+
+
+@pytest.mark.parametrize("case", ["decode-s1-int4", "verify-s4-int8"])
+def test_layer_entry_glm(torch, path, case):
+    """The benchmarked call at its full shape: GLM-5.2-shaped layer through
+    coli_moe_layer, every output element against the oracle."""
+    say(f"coli_moe_layer glm {case} [{path}]")
+    if case == "decode-s1-int4":
+        spec, S, x = synth.GLM, 1, None
+    else:
+        spec, S = synth.GLM_INT8, 4
+        x = synth.verify_hidden_states(0, 0, spec, S)
+    d, dl, o_idx, o_w, used = _glm_resident_for_oracle_routing(torch, spec, S, seed=0, x=x)
+    dims = q().make_dims(spec)
+    ws = workspace(dims, S)
+    idx, w, out = gpu_layer(torch, dims, dl, ws)
+    assert status(ws) == 0, q().coli_moe_last_error()
+    assert np.array_equal(idx, o_idx)
+    assert np.array_equal(w.view(np.uint32), o_w.view(np.uint32))
+    want = oracle.forward(spec, d["x"], o_idx, o_w, d["blobs"], d["shared"])
+    say("glm layer parity", parity(out, want))
+
+
+def test_layer_entry_repeat_calls_reset_the_grid_barrier(torch):
+    """Back-to-back persistent launches on one workspace: each one leaves the
+    barrier words at zero for the next (alternating layers and token counts)."""
+    from synth.device import upload_layer
+    qm = q()
+    spec = synth.TINY
+    dims = qm.make_dims(spec)
+    ws = workspace(dims, 8)
+    cases = []
+    for i, S in enumerate((3, 8, 1, 6, 2)):
+        d = _layer(spec, S, seed=90 + i)
+        cases.append((d, upload_layer(d)))
+    qm.coli_moe_debug_force_path(qm.PATH_PERSISTENT)
+    try:
+        for rep in range(3):
+            for d, dl in cases:
+                say(f"repeat {rep} S={d['x'].shape[0]}")
+                idx, w, out = gpu_layer(torch, dims, dl, ws)
+                assert status(ws) == 0, qm.coli_moe_last_error()
+                o_out, o_idx, _ = _oracle(spec, d)
+                assert np.array_equal(idx, o_idx)
+                parity(out, o_out)
+    finally:
+        qm.coli_moe_debug_force_path(qm.PATH_AUTO)
