@@ -5,9 +5,14 @@ Workload (default): GLM-5.2-shaped decode layer — hidden 6144, expert inter
 2048, 256 routed experts top-8 + 1 shared, int4 per-row-scaled experts
 (18.9 MB each), Q8_0 activations, random fp32 router gate — with 12 layers
 resident in HBM (about 58 GB).  A step is one token through one layer:
-coli_moe_route + coli_moe_forward; step s uses layer s mod 12 and its own
-hidden state, so expert reads do not hit in the 256 MB last-level cache.
-Steps are captured in a HIP graph and replayed.
+coli_moe_layer (router, Q8_0, 8 routed experts + shared, combine); step s
+uses layer s mod 12 and its own hidden state, so expert reads do not hit in
+the 256 MB last-level cache.  Steps are captured in a HIP graph and
+replayed.
+
+--copy-calibration MB runs only a device-to-device copy of MB megabytes
+(torch copy_) ten times: the reference for scaling rocprofv3's
+FETCH_SIZE / WRITE_SIZE counters to bytes.
 
 Prints one JSON line: MoE-layer tokens/s, the roofline of the dominant
 kernel (HIP-event kernel durations measured in this run), whole-layer HBM
@@ -42,8 +47,12 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU-oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
+                    help="only run a device copy of MB megabytes ten times (counter calibration)")
     ap.add_argument("--path", choices=("layer", "split"), default="layer",
                     help="layer: one coli_moe_layer launch per step; split: coli_moe_route + coli_moe_forward")
+    ap.add_argument("--kernels", choices=("auto", "multi", "persistent"), default="auto",
+                    help="kernel set: the library's choice, the multi-launch kernels or the persistent one")
     return ap.parse_args()
 
 
@@ -56,6 +65,16 @@ def main():
     import numpy as np
     import torch
 
+    if args.copy_calibration:
+        n = args.copy_calibration * 1000 * 1000
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(10):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "copies": 10}), flush=True)
+        return
+
     from quantized_expert_ffn_amd import build as hipbuild
     if not os.path.exists(hipbuild.LIB):
         hipbuild.build()
@@ -65,6 +84,7 @@ def main():
     torch.cuda.set_device(0)
     spec = synth.GLM
     dims = q.make_dims(spec)
+    q.coli_moe_debug_force_path({"auto": q.PATH_AUTO, "multi": q.PATH_MULTI, "persistent": q.PATH_PERSISTENT}[args.kernels])
     H, E = spec.hidden, spec.n_experts
     L = args.layers
     bb = spec.blob_bytes
@@ -197,7 +217,7 @@ def main():
                         "256 routed experts top-8 + 1 shared, int4 per-row-scaled weights (18.9 MB/expert), "
                         "Q8_0 activations, fp32 router gate; 12 layers resident in HBM, step s uses layer s mod 12",
             "layers_resident": L, "resident_gb": round(L * nblob * bb / 1e9, 1),
-            "tokens_per_step": 1, "graph_steps": G, "entry": args.path,
+            "tokens_per_step": 1, "graph_steps": G, "entry": args.path, "kernels": args.kernels,
         },
         "roofline": {
             "bound": "hbm", "kernel": dom_kernel,

@@ -121,9 +121,12 @@ int coli_moe_forward(const coli_moe_dims *dims, int32_t n_tokens, const float *x
 /*
  * The whole layer in one call: the result of coli_moe_route followed by
  * coli_moe_forward (same bits), with the routing also written to topk_idx /
- * topk_w.  For up to 8 tokens it runs as one persistent kernel (router,
- * gate/up and down+combine phases separated by grid barriers inside the
- * launch); otherwise it makes the two calls.  Arguments as for those calls.
+ * topk_w.  By default it runs the multi-launch kernels of those two calls,
+ * with Q8_0(x) produced once by the router-logit launch.  A persistent
+ * single-launch kernel (router, gate/up and down+combine phases separated
+ * by grid barriers) serves up to 8 tokens when selected with
+ * coli_moe_debug_force_path.  Arguments as for coli_moe_route and
+ * coli_moe_forward.
  */
 int coli_moe_layer(const coli_moe_dims *dims, int32_t n_tokens, const float *x,
                    const float *router_w, const float *router_bias,
@@ -154,7 +157,8 @@ const char *coli_moe_last_error(void);
  * bracketed by events on its stream; coli_moe_timing_read() synchronises the
  * recorded events and returns the accumulated milliseconds and launch count
  * of one kernel kind (0 router logits, 1 router select, 2 gate/up, 3 down,
- * 4 combine, 5 persistent layer, 6 persistent forward), then resets that
+ * 4 combine, 5 persistent layer, 6 persistent forward, 7 Q8_0 of the
+ * hidden states), then resets that
  * kind.  For measurement only.
  */
 int coli_moe_timing_enable(int32_t enable);
@@ -162,10 +166,11 @@ int coli_moe_timing_read(int32_t kind, double *total_ms, int64_t *launches);
 
 /* ---- test hooks: the same device functions as the production kernels ---- */
 
-/* Kernel family for subsequent calls in this process: 0 automatic (default),
- * 1 multi-launch kernels only, 2 persistent (single-launch) kernels only —
- * a forced persistent kernel fails with COLI_EINVAL where it does not
- * apply (pending experts, more than 8 tokens). */
+/* Kernel family for subsequent calls in this process: 0 automatic (default:
+ * the multi-launch kernels), 1 multi-launch kernels only, 2 persistent
+ * (single-launch) kernels — a forced persistent kernel fails with
+ * COLI_EINVAL where it does not apply (pending experts, more than 8 tokens,
+ * a shape beyond 160 KiB of LDS). */
 int coli_moe_debug_force_path(int32_t path);
 
 /* Unpacks n_rows packed rows of `cols` codes (device src, row stride

@@ -32,7 +32,7 @@ EXPORTS = (
 )
 
 KIND_ROUTER_LOGITS, KIND_ROUTER_SELECT, KIND_GATEUP, KIND_DOWN, KIND_COMBINE = 0, 1, 2, 3, 4
-KIND_LAYER, KIND_FORWARD_PERSISTENT = 5, 6
+KIND_LAYER, KIND_FORWARD_PERSISTENT, KIND_QUANT_X = 5, 6, 7
 PATH_AUTO, PATH_MULTI, PATH_PERSISTENT = 0, 1, 2
 
 

@@ -91,10 +91,16 @@ hipEvent_t take_event() {
 // 0: automatic, 1: multi-launch kernels only, 2: persistent kernels only.
 int g_force_path = 0;
 
-// The persistent kernel handles small batches whose experts are all resident.
-bool use_persistent(const coli_moe_dims *d, int S, bool pending) {
-    if (g_force_path == 1 || pending || S > 8) return false;
+// The persistent kernel takes small batches whose experts are all resident.
+bool persistent_fits(const coli_moe_dims *d, int S, bool pending) {
+    if (pending || S > 8) return false;
     return coli::layer_smem(S, d->hidden, d->inter, d->n_experts, d->top_k, d->n_shared) <= 160 * 1024;
+}
+
+// The automatic choice is the multi-launch kernel set (the faster one on
+// MI355X for the shapes measured); the persistent kernel runs when forced.
+bool use_persistent(const coli_moe_dims *d, int S, bool pending) {
+    return g_force_path == 2 && persistent_fits(d, S, pending);
 }
 
 }  // namespace
@@ -132,6 +138,94 @@ hipError_t ensure_dyn_smem(const void *kern, size_t smem) {
 
 using namespace coli;
 
+namespace {
+
+FwdArgs fwd_args(const coli_moe_dims *d, int S, const float *x, const int32_t *idx, const float *w,
+                 const void *const *expert_blobs, const void *shared_blob, float *out, uint8_t *w8,
+                 const WsLayout &L) {
+    FwdArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.x = x;
+    a.idx = idx;
+    a.w = w;
+    a.blobs = reinterpret_cast<const uint8_t *const *>(expert_blobs);
+    a.shared = static_cast<const uint8_t *>(shared_blob);
+    a.qx = reinterpret_cast<const int8_t *>(w8 + L.qx);
+    a.dx = reinterpret_cast<const float *>(w8 + L.dx);
+    a.qh = reinterpret_cast<int8_t *>(w8 + L.qh);
+    a.dh = reinterpret_cast<float *>(w8 + L.dh);
+    a.Y = reinterpret_cast<float *>(w8 + L.Y);
+    a.out = out;
+    a.status = reinterpret_cast<uint32_t *>(w8 + L.status);
+    a.S = S;
+    a.H = d->hidden;
+    a.I = d->inter;
+    a.E = d->n_experts;
+    a.K = d->top_k;
+    a.n_shared = d->n_shared;
+    return a;
+}
+
+// Router logits (with Q8_0(x) into the workspace when quant_x) and selection.
+int route_launches(const coli_moe_dims *d, int S, const float *x, const float *router_w,
+                   const float *router_bias, int32_t *topk_idx, float *topk_w, uint8_t *w8,
+                   const WsLayout &L, bool quant_x, hipStream_t st) {
+    uint32_t *status = reinterpret_cast<uint32_t *>(w8 + L.status);
+    float *logits = reinterpret_cast<float *>(w8 + L.logits);
+    timing_before(KK_ROUTER_LOGITS, st);
+    hipError_t e = launch_router_logits(x, router_w, logits, status, S, d->hidden, d->n_experts,
+                                        quant_x ? reinterpret_cast<int8_t *>(w8 + L.qx) : nullptr,
+                                        quant_x ? reinterpret_cast<float *>(w8 + L.dx) : nullptr, st);
+    timing_after(KK_ROUTER_LOGITS, st);
+    if (e != hipSuccess) return hip_fail(e, "router logits launch");
+    timing_before(KK_ROUTER_SELECT, st);
+    e = launch_router_select(logits, router_bias, topk_idx, topk_w, status, S, d->n_experts, d->top_k,
+                             d->routed_scaling_factor, d->norm_topk_prob, st);
+    timing_after(KK_ROUTER_SELECT, st);
+    if (e != hipSuccess) return hip_fail(e, "router select launch");
+    return COLI_OK;
+}
+
+// The multi-launch forward: [Q8_0(x)], gate/up (resident experts first when
+// some are pending, then the pending ones after pending_ready), down, combine.
+int forward_launches(FwdArgs &a, int bits, bool any_pending, void *pending_ready, bool qx_ready,
+                     hipStream_t st) {
+    hipError_t e;
+    if (!qx_ready) {
+        timing_before(KK_QUANT_X, st);
+        e = launch_quant_x(a.x, const_cast<int8_t *>(a.qx), const_cast<float *>(a.dx), a.status, a.S, a.H, st);
+        timing_after(KK_QUANT_X, st);
+        if (e != hipSuccess) return hip_fail(e, "Q8_0(x) launch");
+    }
+    if (any_pending) {
+        a.pend_mode = 1;  // resident experts first
+        timing_before(KK_GATEUP, st);
+        e = launch_gateup(a, bits, st);
+        timing_after(KK_GATEUP, st);
+        if (e != hipSuccess) return hip_fail(e, "gate/up launch");
+        if (pending_ready) {
+            e = hipStreamWaitEvent(st, static_cast<hipEvent_t>(pending_ready), 0);
+            if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+        }
+        a.pend_mode = 2;  // then the experts that were being staged
+    }
+    timing_before(KK_GATEUP, st);
+    e = launch_gateup(a, bits, st);
+    timing_after(KK_GATEUP, st);
+    if (e != hipSuccess) return hip_fail(e, "gate/up launch");
+    timing_before(KK_DOWN, st);
+    e = launch_down(a, bits, st);
+    timing_after(KK_DOWN, st);
+    if (e != hipSuccess) return hip_fail(e, "down launch");
+    timing_before(KK_COMBINE, st);
+    e = launch_combine(a, st);
+    timing_after(KK_COMBINE, st);
+    if (e != hipSuccess) return hip_fail(e, "combine launch");
+    return COLI_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 size_t coli_moe_expert_bytes(const coli_moe_dims *d) {
@@ -159,21 +253,8 @@ int coli_moe_route(const coli_moe_dims *d, int32_t S, const float *x, const floa
     if (ws_bytes < L.total)
         return fail(COLI_EWORKSPACE, "workspace %zu bytes < %zu needed for %d tokens", ws_bytes, L.total, S);
     if ((rc = check_device())) return rc;
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    uint8_t *w8 = static_cast<uint8_t *>(ws);
-    uint32_t *status = reinterpret_cast<uint32_t *>(w8 + L.status);
-    float *logits = reinterpret_cast<float *>(w8 + L.logits);
-    hipError_t e;
-    timing_before(KK_ROUTER_LOGITS, st);
-    e = launch_router_logits(x, router_w, logits, status, S, d->hidden, d->n_experts, st);
-    timing_after(KK_ROUTER_LOGITS, st);
-    if (e != hipSuccess) return hip_fail(e, "router logits launch");
-    timing_before(KK_ROUTER_SELECT, st);
-    e = launch_router_select(logits, router_bias, topk_idx, topk_w, status, S, d->n_experts, d->top_k,
-                             d->routed_scaling_factor, d->norm_topk_prob, st);
-    timing_after(KK_ROUTER_SELECT, st);
-    if (e != hipSuccess) return hip_fail(e, "router select launch");
-    return COLI_OK;
+    return route_launches(d, S, x, router_w, router_bias, topk_idx, topk_w, static_cast<uint8_t *>(ws), L,
+                          false, static_cast<hipStream_t>(stream));
 }
 
 int coli_moe_forward(const coli_moe_dims *d, int32_t S, const float *x, const int32_t *topk_idx,
@@ -197,24 +278,7 @@ int coli_moe_forward(const coli_moe_dims *d, int32_t S, const float *x, const in
     if ((rc = check_device())) return rc;
     hipStream_t st = static_cast<hipStream_t>(stream);
     uint8_t *w8 = static_cast<uint8_t *>(ws);
-    FwdArgs a;
-    std::memset(&a, 0, sizeof a);
-    a.x = x;
-    a.idx = topk_idx;
-    a.w = topk_w;
-    a.blobs = reinterpret_cast<const uint8_t *const *>(expert_blobs);
-    a.shared = static_cast<const uint8_t *>(shared_blob);
-    a.qh = reinterpret_cast<int8_t *>(w8 + L.qh);
-    a.dh = reinterpret_cast<float *>(w8 + L.dh);
-    a.Y = reinterpret_cast<float *>(w8 + L.Y);
-    a.out = out;
-    a.status = reinterpret_cast<uint32_t *>(w8 + L.status);
-    a.S = S;
-    a.H = d->hidden;
-    a.I = d->inter;
-    a.E = d->n_experts;
-    a.K = d->top_k;
-    a.n_shared = d->n_shared;
+    FwdArgs a = fwd_args(d, S, x, topk_idx, topk_w, expert_blobs, shared_blob, out, w8, L);
     bool any_pending = false;
     if (pending_mask) {
         for (int e = 0; e < d->n_experts; ++e)
@@ -224,7 +288,7 @@ int coli_moe_forward(const coli_moe_dims *d, int32_t S, const float *x, const in
             }
     }
     hipError_t e;
-    if (g_force_path == 2 && !use_persistent(d, S, any_pending))
+    if (g_force_path == 2 && !persistent_fits(d, S, any_pending))
         return fail(COLI_EINVAL, "persistent kernel forced but the call has pending experts, more than 8 tokens "
                                  "or a shape beyond its LDS budget");
     if (use_persistent(d, S, any_pending)) {
@@ -239,31 +303,7 @@ int coli_moe_forward(const coli_moe_dims *d, int32_t S, const float *x, const in
         if (e != hipSuccess) return hip_fail(e, "forward launch");
         return COLI_OK;
     }
-    if (any_pending) {
-        a.pend_mode = 1;  // resident experts first
-        timing_before(KK_GATEUP, st);
-        e = launch_gateup(a, d->wbits, st);
-        timing_after(KK_GATEUP, st);
-        if (e != hipSuccess) return hip_fail(e, "gate/up launch");
-        if (pending_ready) {
-            e = hipStreamWaitEvent(st, static_cast<hipEvent_t>(pending_ready), 0);
-            if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
-        }
-        a.pend_mode = 2;  // then the experts that were being staged
-    }
-    timing_before(KK_GATEUP, st);
-    e = launch_gateup(a, d->wbits, st);
-    timing_after(KK_GATEUP, st);
-    if (e != hipSuccess) return hip_fail(e, "gate/up launch");
-    timing_before(KK_DOWN, st);
-    e = launch_down(a, d->wbits, st);
-    timing_after(KK_DOWN, st);
-    if (e != hipSuccess) return hip_fail(e, "down launch");
-    timing_before(KK_COMBINE, st);
-    e = launch_combine(a, st);
-    timing_after(KK_COMBINE, st);
-    if (e != hipSuccess) return hip_fail(e, "combine launch");
-    return COLI_OK;
+    return forward_launches(a, d->wbits, any_pending, pending_ready, false, st);
 }
 
 int coli_moe_layer(const coli_moe_dims *d, int32_t S, const float *x, const float *router_w,
@@ -279,36 +319,21 @@ int coli_moe_layer(const coli_moe_dims *d, int32_t S, const float *x, const floa
     const WsLayout L = ws_layout(d->hidden, d->inter, d->n_experts, d->top_k, S);
     if (ws_bytes < L.total)
         return fail(COLI_EWORKSPACE, "workspace %zu bytes < %zu needed for %d tokens", ws_bytes, L.total, S);
-    if (g_force_path == 2 && !use_persistent(d, S, false))
+    if (g_force_path == 2 && !persistent_fits(d, S, false))
         return fail(COLI_EINVAL, "persistent kernel forced but the call has more than 8 tokens or a shape beyond "
                                  "its LDS budget");
-    if (!use_persistent(d, S, false)) {
-        rc = coli_moe_route(d, S, x, router_w, router_bias, topk_idx, topk_w, ws, ws_bytes, stream);
-        if (rc) return rc;
-        return coli_moe_forward(d, S, x, topk_idx, topk_w, expert_blobs, shared_blob, nullptr, nullptr, out, ws,
-                                ws_bytes, stream);
-    }
     if ((rc = check_device())) return rc;
     hipStream_t st = static_cast<hipStream_t>(stream);
     uint8_t *w8 = static_cast<uint8_t *>(ws);
-    FwdArgs a;
-    std::memset(&a, 0, sizeof a);
-    a.x = x;
-    a.idx = topk_idx;
-    a.w = topk_w;
-    a.blobs = reinterpret_cast<const uint8_t *const *>(expert_blobs);
-    a.shared = static_cast<const uint8_t *>(shared_blob);
-    a.qh = reinterpret_cast<int8_t *>(w8 + L.qh);
-    a.dh = reinterpret_cast<float *>(w8 + L.dh);
-    a.Y = reinterpret_cast<float *>(w8 + L.Y);
-    a.out = out;
-    a.status = reinterpret_cast<uint32_t *>(w8 + L.status);
-    a.S = S;
-    a.H = d->hidden;
-    a.I = d->inter;
-    a.E = d->n_experts;
-    a.K = d->top_k;
-    a.n_shared = d->n_shared;
+    FwdArgs a = fwd_args(d, S, x, topk_idx, topk_w, expert_blobs, shared_blob, out, w8, L);
+    if (!use_persistent(d, S, false)) {
+        const size_t smem = forward_smem_max(S, d->hidden, d->inter, d->n_experts, d->top_k, d->n_shared);
+        if (smem > 160 * 1024)
+            return fail(COLI_EINVAL, "shape needs %zu bytes of LDS per workgroup (> 160 KiB)", smem);
+        rc = route_launches(d, S, x, router_w, router_bias, topk_idx, topk_w, w8, L, true, st);
+        if (rc) return rc;
+        return forward_launches(a, d->wbits, false, nullptr, true, st);
+    }
     LayerArgs l;
     std::memset(&l, 0, sizeof l);
     l.router_w = router_w;
@@ -430,8 +455,8 @@ int coli_moe_debug_logits(const coli_moe_dims *d, int32_t S, const float *x, con
     if (S == 0) return COLI_OK;
     if ((rc = check_device())) return rc;
     // no workspace here: the kernel skips its status report when given none
-    hipError_t e = launch_router_logits(x, router_w, logits, nullptr, S, d->hidden, d->n_experts,
-                                        static_cast<hipStream_t>(stream));
+    hipError_t e = launch_router_logits(x, router_w, logits, nullptr, S, d->hidden, d->n_experts, nullptr,
+                                        nullptr, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? COLI_OK : hip_fail(e, "debug_logits launch");
 }
 

@@ -98,6 +98,47 @@ __device__ __forceinline__ int8_t q8_0_lane(float v, float *d_out) {
     return (int8_t)(int)c;
 }
 
+// The same quantisation with one lane holding a whole 32-value block: reads
+// x[0..31], writes the 32 codes to q[0..31] (16-byte aligned) and returns d.
+// *ok is cleared on a non-finite input.
+__device__ __forceinline__ float q8_0_block_lane(const float *__restrict__ x, int8_t *__restrict__ q, bool *ok) {
+    float v[32];
+    const f32x4 *xv = reinterpret_cast<const f32x4 *>(x);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const f32x4 t = xv[i];
+        v[4 * i] = t.x; v[4 * i + 1] = t.y; v[4 * i + 2] = t.z; v[4 * i + 3] = t.w;
+    }
+    float a = 0.0f;
+    bool good = true;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+        good = good && finite_f32(v[i]);
+        a = __builtin_fmaxf(a, __builtin_fabsf(v[i]));
+    }
+    *ok = good;
+    const float d = a / 127.0f;
+    uint32_t w[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            float c = 0.0f;
+            if (d != 0.0f) {
+                c = __builtin_roundf(v[4 * i + j] / d);
+                c = __builtin_fminf(__builtin_fmaxf(c, -127.0f), 127.0f);
+            }
+            word |= (uint32_t)(uint8_t)(int8_t)(int)c << (8 * j);
+        }
+        w[i] = word;
+    }
+    u32x4 *qv = reinterpret_cast<u32x4 *>(q);
+    qv[0] = u32x4{w[0], w[1], w[2], w[3]};
+    qv[1] = u32x4{w[4], w[5], w[6], w[7]};
+    return d;
+}
+
 // ---- packed rows: exact block dot products -----------------------------
 // A "block" is 32 consecutive codes of a row: 32 bytes (int8), 16 (int4) or
 // 8 (int2).  Activation codes arrive as 8 little-endian int32 words holding

@@ -73,26 +73,19 @@ __global__ __launch_bounds__(256) void k_gateup(const FwdArgs a) {
     const float *scale = reinterpret_cast<const float *>(blob + (wave < 2 ? BL.s_gate : BL.s_up));
     const int nb = H / 32;
     const int p0 = uniform(uoff[u]), np = uniform(uoff[u + 1]) - p0;
-    const bool check_x = blockIdx.x == 0;
     const int crow = lane & 15, cvec = lane >> 4;
     const int vds = vd_stride(nb);
     for (int g0 = 0; g0 < np; g0 += NT) {
         const int ng = min(NT, np - g0);
-        // Q8_0 of the hidden states of this group's tokens.  Lanes 0-31 and
-        // 32-63 of a wave each hold one 32-element block.
+        // Q8_0(x) of this group's tokens (computed once per call) into LDS
         auto stage = [&]() {
             for (int it = 0; it < ng; ++it) {
                 const int v = pairs[p0 + g0 + it];
                 const int t = v < P ? v / K : v - P;
-                const float *xr = a.x + (size_t)t * H;
-                for (int h = tid; h < H; h += 256) {
-                    const float xv = xr[h];
-                    if (check_x && !finite_f32(xv)) raise_status(a.status, ST_NONFINITE);
-                    float d;
-                    const int8_t q = q8_0_lane(xv, &d);
-                    vq[it * H + h] = q;
-                    if ((lane & 31) == 0) vd[it * vds + (h >> 5)] = d;
-                }
+                const i32x4 *src = reinterpret_cast<const i32x4 *>(a.qx + (size_t)t * H);
+                i32x4 *dst = reinterpret_cast<i32x4 *>(vq + (size_t)it * H);
+                for (int q = tid; q < H / 16; q += 256) dst[q] = src[q];
+                for (int q = tid; q < nb; q += 256) vd[it * vds + q] = a.dx[(size_t)t * nb + q];
             }
             __syncthreads();
         };

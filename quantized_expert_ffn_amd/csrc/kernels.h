@@ -39,6 +39,8 @@ struct FwdArgs {
     const float *w;                // [S, K]
     const uint8_t *const *blobs;   // device array [E]
     const uint8_t *shared;         // shared expert blob or null
+    const int8_t *qx;              // [S, H]   Q8_0(x) codes
+    const float *dx;               // [S, H/32]
     int8_t *qh;                    // [S*(K+1), I]   Q8_0(h) codes per pair slot
     float *dh;                     // [S*(K+1), I/32]
     float *Y;                      // [S*(K+1), H]   expert outputs per pair slot
@@ -49,8 +51,11 @@ struct FwdArgs {
     uint32_t pend[32];             // bit e: expert e pending
 };
 
+// Router logits; with qx non-null the same launch writes Q8_0(x) to qx / dx.
 hipError_t launch_router_logits(const float *x, const float *W, float *logits, uint32_t *status,
-                                int S, int H, int E, hipStream_t st);
+                                int S, int H, int E, int8_t *qx, float *dx, hipStream_t st);
+hipError_t launch_quant_x(const float *x, int8_t *qx, float *dx, uint32_t *status, int S, int H,
+                          hipStream_t st);
 hipError_t launch_router_select(const float *logits, const float *bias, int32_t *idx, float *w,
                                 uint32_t *status, int S, int E, int K, float rsf, int norm,
                                 hipStream_t st);
@@ -64,6 +69,7 @@ enum KernelKind {
     KK_COMBINE = 4,
     KK_LAYER = 5,
     KK_FORWARD_PERSISTENT = 6,
+    KK_QUANT_X = 7,
     KK_COUNT = 8
 };
 

@@ -218,8 +218,10 @@ __global__ __launch_bounds__(LT) void k_layer(const FwdArgs a, const LayerArgs l
         bool ok = true;
         for (int t = wave; t < S; t += LW) {
             float *lg = l.logits + (size_t)t * E;
-            ok = select_wave([&](int e) { return ld_dev(lg + e); }, l.bias, E, K, l.rsf, l.norm,
-                             idx_l + t * K, w_l + t * K, sig_s, selsig) && ok;
+            auto ld = [&](int e) { return ld_dev(lg + e); };
+            ok = (E <= 256 ? select_wave<4>(ld, l.bias, E, K, l.rsf, l.norm, idx_l + t * K, w_l + t * K, sig_s, selsig)
+                           : select_wave<16>(ld, l.bias, E, K, l.rsf, l.norm, idx_l + t * K, w_l + t * K, sig_s,
+                                             selsig)) && ok;
         }
         if (!ok && lane == 0 && blockIdx.x == 0) raise_status(a.status, ST_NONFINITE);
         __syncthreads();

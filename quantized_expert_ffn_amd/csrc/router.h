@@ -92,30 +92,37 @@ __device__ __forceinline__ int wave_min_i32(int v) {
 // maximum of the lanes' best remaining scores, then the smallest id holding
 // it.  Gate weights: (sig_k / ((sig_0 + sig_1) + ...)) * rsf, or sig_k * rsf
 // without renormalisation.  load_logit(e) returns the token's logit e.
-// E <= 1024, K <= 32.  Returns false on a non-finite input or zero weights.
-template <typename LoadLogit>
+// E <= 64 * MAXM, K <= 32.  Returns false on a non-finite input or zero
+// weights.
+template <int MAXM, typename LoadLogit>
 __device__ __forceinline__ bool select_wave(LoadLogit load_logit, const float *__restrict__ bias,
                                             int E, int K, float rsf, int norm,
                                             int32_t *__restrict__ idx_out,
                                             float *__restrict__ w_out, float *sig_s,
                                             float *sel_sig) {
-    constexpr int MAXM = 16;
     const int lane = threadIdx.x & 63;
     const int mcount = (E + 63) / 64;
-    float score[MAXM];
+    float score[MAXM], lv[MAXM], bv[MAXM];
     uint32_t taken = 0;
     bool ok = true;
+    // all loads first (in flight together), then the arithmetic
+#pragma unroll
+    for (int m = 0; m < MAXM; ++m) {
+        const int e = min(lane + 64 * m, E - 1);
+        if (m < mcount) {
+            lv[m] = load_logit(e);
+            bv[m] = bias ? bias[e] : 0.0f;
+        }
+    }
 #pragma unroll
     for (int m = 0; m < MAXM; ++m) {
         const int e = lane + 64 * m;
         score[m] = -__builtin_inff();
         if (m < mcount && e < E) {
-            const float l = load_logit(e);
-            const float b = bias ? bias[e] : 0.0f;
-            ok = ok && finite_f32(l) && finite_f32(b);
-            const float sg = sigmoid_f32(l);
+            ok = ok && finite_f32(lv[m]) && finite_f32(bv[m]);
+            const float sg = sigmoid_f32(lv[m]);
             sig_s[e] = sg;
-            score[m] = sg + b;
+            score[m] = sg + bv[m];
         }
     }
     wave_and_lds_sync();

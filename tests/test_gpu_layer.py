@@ -337,6 +337,8 @@ def test_layer_entry_tiny(torch, path, S):
     """coli_moe_layer (router + experts + combine in one call) against the
     oracle, ragged token counts; above 8 tokens it runs route + forward."""
     from synth.device import upload_layer
+    if path == "persistent" and S > 8:
+        pytest.skip("the persistent kernel takes at most 8 tokens (forcing it above is an error)")
     say(f"coli_moe_layer tiny S={S} [{path}]")
     spec = synth.TINY
     d = _layer(spec, S, seed=70 + S)
