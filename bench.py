@@ -144,28 +144,21 @@ def main():
     if rc != 0:
         raise RuntimeError(f"device status {rc}: {q.coli_moe_last_error()}")
     routed = idx.cpu().numpy()
-    q.coli_moe_timing_enable(True)
-    for s in range(G):
-        step(s)
-    torch.cuda.synchronize()
-    q.coli_moe_timing_enable(False)
-    kinds = (("router_logits", q.KIND_ROUTER_LOGITS), ("router_select", q.KIND_ROUTER_SELECT),
-             ("gateup", q.KIND_GATEUP), ("down", q.KIND_DOWN), ("combine", q.KIND_COMBINE),
-             ("layer", q.KIND_LAYER), ("forward_persistent", q.KIND_FORWARD_PERSISTENT))
-    kernel_us, launches = {}, {}
-    for name, k in kinds:
-        ms, n = q.coli_moe_timing_read(k)
-        if n:
-            kernel_us[name] = 1e3 * ms / n
-            launches[name] = n
 
-    # captured steps
-    graph = torch.cuda.CUDAGraph()
+    # captured steps: the timed graph, and a second capture of the same steps
+    # with a HIP event pair around every kernel (per-kernel durations)
     cap = torch.cuda.Stream()
     cap.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph, stream=cap):
         for s in range(G):
             step(s)
+    q.coli_moe_timing_enable(True)
+    tgraph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(tgraph, stream=cap):
+        for s in range(G):
+            step(s)
+    q.coli_moe_timing_enable(False)
     torch.cuda.synchronize()
     reps_w = max(1, args.warmup // G)
     reps = max(1, args.steps // G)
@@ -184,14 +177,29 @@ def main():
     ms_per_step = 1e3 * elapsed / steps
     tokens_per_s = steps / elapsed
 
+    # per-kernel durations: one replay of the event-bracketed graph (the
+    # events hold the timestamps of its last replay)
+    tgraph.replay()
+    torch.cuda.synchronize()
+    kinds = (("router_logits", q.KIND_ROUTER_LOGITS), ("router_select", q.KIND_ROUTER_SELECT),
+             ("quant_x", q.KIND_QUANT_X), ("gateup", q.KIND_GATEUP), ("down", q.KIND_DOWN),
+             ("combine", q.KIND_COMBINE), ("layer", q.KIND_LAYER),
+             ("forward_persistent", q.KIND_FORWARD_PERSISTENT))
+    kernel_us, launches = {}, {}
+    for name, k in kinds:
+        ms, n = q.coli_moe_timing_read(k)
+        if n:
+            kernel_us[name] = 1e3 * ms / n
+            launches[name] = n
+
     # algorithmic bytes: each token-layer reads W_r, the 8 routed experts and the shared one once
     n_units = int(np.mean([len(set(r)) for r in routed])) + spec.n_shared
     lay_bytes = E * H * 4 + E * 4 + n_units * bb
     if "layer" in kernel_us:
-        dom, dom_kernel = "layer", "k_layer<4> (router + gate/up + SwiGLU + down + combine, one launch)"
+        dom, dom_kernel = "layer", "k_layer<4,1,1,24>"
         dom_bytes = lay_bytes
     elif "forward_persistent" in kernel_us:
-        dom, dom_kernel = "forward_persistent", "k_layer<4> (given routing: gate/up + SwiGLU + down + combine)"
+        dom, dom_kernel = "forward_persistent", "k_layer<4,1,0,24>"
         dom_bytes = n_units * bb
     else:
         dom, dom_kernel = "gateup", "k_gateup<4,1>"
@@ -222,7 +230,7 @@ def main():
         "roofline": {
             "bound": "hbm", "kernel": dom_kernel,
             "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": counted_traffic(dom_kernel),
             "algorithmic_bytes_per_launch": dom_bytes, "avg_launch_us": round(dom_us, 3),
         },
         "layer_hbm_gbs": round(layer_gbs, 1),
@@ -234,6 +242,29 @@ def main():
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(args, spec, xs_host, layers, L)
     print(json.dumps(res), flush=True)
+
+
+def counted_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary (FETCH_SIZE + WRITE_SIZE, scaled by a device copy), or None when
+    there is none or the kernel's sources changed since it was taken."""
+    import glob
+    import hashlib
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        with open(path) as f:
+            for line in f:
+                if not line.startswith("traffic_json: "):
+                    continue
+                rec = json.loads(line[len("traffic_json: "):])
+                if rec.get("kernel") != kernel:
+                    continue
+                h = hashlib.sha256()
+                for src in rec["sources"]:
+                    with open(os.path.join(ROOT, src), "rb") as s:
+                        h.update(s.read())
+                if h.hexdigest() == rec["sha256"]:
+                    return int(rec["read_bytes"]) + int(rec["write_bytes"])
+    return None
 
 
 def cpu_baseline(args, spec, xs_host, layers, L):
