@@ -145,20 +145,31 @@ def main():
         raise RuntimeError(f"device status {rc}: {q.coli_moe_last_error()}")
     routed = idx.cpu().numpy()
 
-    # captured steps: the timed graph, and a second capture of the same steps
-    # with a HIP event pair around every kernel (per-kernel durations)
+    # per-kernel durations: every launch of an eager pass carries a HIP event
+    # pair recorded at the kernel's own start and end
+    q.coli_moe_timing_enable(True)
+    for s in range(G):
+        step(s)
+    torch.cuda.synchronize()
+    q.coli_moe_timing_enable(False)
+    kinds = (("router_logits", q.KIND_ROUTER_LOGITS), ("router_select", q.KIND_ROUTER_SELECT),
+             ("quant_x", q.KIND_QUANT_X), ("gateup", q.KIND_GATEUP), ("down", q.KIND_DOWN),
+             ("combine", q.KIND_COMBINE), ("layer", q.KIND_LAYER),
+             ("forward_persistent", q.KIND_FORWARD_PERSISTENT))
+    kernel_us, launches = {}, {}
+    for name, k in kinds:
+        ms, n = q.coli_moe_timing_read(k)
+        if n:
+            kernel_us[name] = 1e3 * ms / n
+            launches[name] = n
+
+    # captured steps
     cap = torch.cuda.Stream()
     cap.wait_stream(torch.cuda.current_stream())
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph, stream=cap):
         for s in range(G):
             step(s)
-    q.coli_moe_timing_enable(True)
-    tgraph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(tgraph, stream=cap):
-        for s in range(G):
-            step(s)
-    q.coli_moe_timing_enable(False)
     torch.cuda.synchronize()
     reps_w = max(1, args.warmup // G)
     reps = max(1, args.steps // G)
@@ -176,21 +187,6 @@ def main():
         raise RuntimeError(f"device status after replay {rc}: {q.coli_moe_last_error()}")
     ms_per_step = 1e3 * elapsed / steps
     tokens_per_s = steps / elapsed
-
-    # per-kernel durations: one replay of the event-bracketed graph (the
-    # events hold the timestamps of its last replay)
-    tgraph.replay()
-    torch.cuda.synchronize()
-    kinds = (("router_logits", q.KIND_ROUTER_LOGITS), ("router_select", q.KIND_ROUTER_SELECT),
-             ("quant_x", q.KIND_QUANT_X), ("gateup", q.KIND_GATEUP), ("down", q.KIND_DOWN),
-             ("combine", q.KIND_COMBINE), ("layer", q.KIND_LAYER),
-             ("forward_persistent", q.KIND_FORWARD_PERSISTENT))
-    kernel_us, launches = {}, {}
-    for name, k in kinds:
-        ms, n = q.coli_moe_timing_read(k)
-        if n:
-            kernel_us[name] = 1e3 * ms / n
-            launches[name] = n
 
     # algorithmic bytes: each token-layer reads W_r, the 8 routed experts and the shared one once
     n_units = int(np.mean([len(set(r)) for r in routed])) + spec.n_shared

@@ -153,8 +153,9 @@ int coli_moe_status(void *ws, void *stream);
 const char *coli_moe_last_error(void);
 
 /*
- * Kernel timing.  While enabled, every kernel launched by the library is
- * bracketed by events on its stream; coli_moe_timing_read() synchronises the
+ * Kernel timing.  While enabled, every kernel launched by the library
+ * carries a pair of HIP events that the runtime records at the kernel's own
+ * start and end (hipExtLaunchKernel); coli_moe_timing_read() synchronises the
  * recorded events and returns the accumulated milliseconds and launch count
  * of one kernel kind (0 router logits, 1 router select, 2 gate/up, 3 down,
  * 4 combine, 5 persistent layer, 6 persistent forward, 7 Q8_0 of the

@@ -73,7 +73,6 @@ struct Timing {
     std::mutex mu;
     bool on = false;
     std::vector<hipEvent_t> free_events;
-    hipEvent_t open[coli::KK_COUNT] = {};
     std::vector<std::pair<hipEvent_t, hipEvent_t>> done[coli::KK_COUNT];
 } g_timing;
 
@@ -107,20 +106,23 @@ bool use_persistent(const coli_moe_dims *d, int S, bool pending) {
 
 namespace coli {
 
-void timing_before(int kind, hipStream_t st) {
-    std::lock_guard<std::mutex> lk(g_timing.mu);
-    if (!g_timing.on) return;
-    hipEvent_t e = take_event();
-    if (e && hipEventRecord(e, st) == hipSuccess) g_timing.open[kind] = e;
-}
+// The kind of the launches the calling thread is making (-1: none).
+thread_local int tl_kind = -1;
 
-void timing_after(int kind, hipStream_t st) {
+void timing_before(int kind, hipStream_t) { tl_kind = kind; }
+
+void timing_after(int, hipStream_t) { tl_kind = -1; }
+
+bool timing_pair(hipEvent_t *start, hipEvent_t *stop) {
+    if (tl_kind < 0) return false;
     std::lock_guard<std::mutex> lk(g_timing.mu);
-    if (!g_timing.on || !g_timing.open[kind]) return;
-    hipEvent_t e = take_event();
-    if (e && hipEventRecord(e, st) == hipSuccess)
-        g_timing.done[kind].emplace_back(g_timing.open[kind], e);
-    g_timing.open[kind] = nullptr;
+    if (!g_timing.on) return false;
+    hipEvent_t e0 = take_event(), e1 = take_event();
+    if (!e0 || !e1) return false;
+    g_timing.done[tl_kind].emplace_back(e0, e1);
+    *start = e0;
+    *stop = e1;
+    return true;
 }
 
 hipError_t ensure_dyn_smem(const void *kern, size_t smem) {
@@ -166,10 +168,11 @@ FwdArgs fwd_args(const coli_moe_dims *d, int S, const float *x, const int32_t *i
     return a;
 }
 
-// Router logits (with Q8_0(x) into the workspace when quant_x) and selection.
+// Router logits (with Q8_0(x) into the workspace when quant_x) and, with
+// select, the top-K selection.
 int route_launches(const coli_moe_dims *d, int S, const float *x, const float *router_w,
                    const float *router_bias, int32_t *topk_idx, float *topk_w, uint8_t *w8,
-                   const WsLayout &L, bool quant_x, hipStream_t st) {
+                   const WsLayout &L, bool quant_x, bool select, hipStream_t st) {
     uint32_t *status = reinterpret_cast<uint32_t *>(w8 + L.status);
     float *logits = reinterpret_cast<float *>(w8 + L.logits);
     timing_before(KK_ROUTER_LOGITS, st);
@@ -178,6 +181,7 @@ int route_launches(const coli_moe_dims *d, int S, const float *x, const float *r
                                         quant_x ? reinterpret_cast<float *>(w8 + L.dx) : nullptr, st);
     timing_after(KK_ROUTER_LOGITS, st);
     if (e != hipSuccess) return hip_fail(e, "router logits launch");
+    if (!select) return COLI_OK;
     timing_before(KK_ROUTER_SELECT, st);
     e = launch_router_select(logits, router_bias, topk_idx, topk_w, status, S, d->n_experts, d->top_k,
                              d->routed_scaling_factor, d->norm_topk_prob, st);
@@ -213,6 +217,13 @@ int forward_launches(FwdArgs &a, int bits, bool any_pending, void *pending_ready
     e = launch_gateup(a, bits, st);
     timing_after(KK_GATEUP, st);
     if (e != hipSuccess) return hip_fail(e, "gate/up launch");
+    if (a.S <= 8 && down_rows_smem(a.S, a.I, a.E, a.K, a.n_shared) <= 64 * 1024) {
+        timing_before(KK_DOWN, st);
+        e = launch_down_rows(a, bits, st);
+        timing_after(KK_DOWN, st);
+        if (e != hipSuccess) return hip_fail(e, "down+combine launch");
+        return COLI_OK;
+    }
     timing_before(KK_DOWN, st);
     e = launch_down(a, bits, st);
     timing_after(KK_DOWN, st);
@@ -254,7 +265,7 @@ int coli_moe_route(const coli_moe_dims *d, int32_t S, const float *x, const floa
         return fail(COLI_EWORKSPACE, "workspace %zu bytes < %zu needed for %d tokens", ws_bytes, L.total, S);
     if ((rc = check_device())) return rc;
     return route_launches(d, S, x, router_w, router_bias, topk_idx, topk_w, static_cast<uint8_t *>(ws), L,
-                          false, static_cast<hipStream_t>(stream));
+                          false, true, static_cast<hipStream_t>(stream));
 }
 
 int coli_moe_forward(const coli_moe_dims *d, int32_t S, const float *x, const int32_t *topk_idx,
@@ -330,8 +341,19 @@ int coli_moe_layer(const coli_moe_dims *d, int32_t S, const float *x, const floa
         const size_t smem = forward_smem_max(S, d->hidden, d->inter, d->n_experts, d->top_k, d->n_shared);
         if (smem > 160 * 1024)
             return fail(COLI_EINVAL, "shape needs %zu bytes of LDS per workgroup (> 160 KiB)", smem);
-        rc = route_launches(d, S, x, router_w, router_bias, topk_idx, topk_w, w8, L, true, st);
+        // up to 8 tokens: the gate/up kernel selects the routing from the logits
+        const bool fused = S <= 8 &&
+                           gateup_route_smem(S, d->hidden, d->n_experts, d->top_k) <= 160 * 1024;
+        rc = route_launches(d, S, x, router_w, router_bias, topk_idx, topk_w, w8, L, true, !fused, st);
         if (rc) return rc;
+        if (fused) {
+            a.logits = reinterpret_cast<const float *>(w8 + L.logits);
+            a.bias = router_bias;
+            a.idx_out = topk_idx;
+            a.w_out = topk_w;
+            a.rsf = d->routed_scaling_factor;
+            a.norm = d->norm_topk_prob;
+        }
         return forward_launches(a, d->wbits, false, nullptr, true, st);
     }
     LayerArgs l;

@@ -207,6 +207,12 @@ struct BlockBits<2> {
     u32x2 w;
 };
 
+// Vector-memory instructions that load one block per lane.
+template <int BITS>
+struct BlockLoads {
+    static constexpr int N = BITS == 8 ? 2 : 1;
+};
+
 // Weight rows are read through a buffer resource covering the whole blob:
 // the row's byte offset is a scalar, the lane's offset a single VGPR, and
 // every access is range-checked by the hardware (reads past num_records

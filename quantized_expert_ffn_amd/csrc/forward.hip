@@ -28,25 +28,88 @@
 
 #include "device_common.h"
 #include "kernels.h"
+#include "router.h"
 #include "stream.h"
 
 namespace coli {
 
-template <int BITS, int NT>
+// LDS of the in-kernel routing (after the gate/up plan): per-wave sigmoid
+// scratch [4][E], selected sigmoids [4][32], top-K indices and weights [S*K].
+struct RoutePlan {
+    size_t sig, selsig, idx, w, total;
+};
+__host__ __device__ inline RoutePlan route_plan(size_t base, int S, int K, int E) {
+    RoutePlan r;
+    r.sig = a16(base);
+    r.selsig = a16(r.sig + 4 * 4 * (size_t)E);
+    r.idx = a16(r.selsig + 4 * 4 * 32);
+    r.w = a16(r.idx + 4 * (size_t)S * K);
+    r.total = a16(r.w + 4 * (size_t)S * K);
+    return r;
+}
+
+// Gate/up of one (32-row tile, unit).  With ROUTE the routing is taken from
+// the router logits here: grid row y = 0 is the shared expert (its pairs do
+// not depend on the routing, so it starts at once); every other workgroup
+// selects the top-K of every token itself (one wavefront per token, the
+// same bits in every workgroup), builds the unit table and takes routed
+// unit y - 1; workgroup (0, 1) writes the routing out.
+template <int BITS, int NT, bool ROUTE>
 __global__ __launch_bounds__(256) void k_gateup(const FwdArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
     const int S = a.S, K = a.K, E = a.E, H = a.H, I = a.I, P = S * K;
     const SmemPlan L = smem_plan(S, K, E, NT, H);
-    build_units(a.idx, S, K, E, a.n_shared, smem, L, a.status,
-                blockIdx.x == 0 && blockIdx.y == 0 && a.pend_mode != 2);
     const int *uexp = reinterpret_cast<const int *>(smem + L.uexp);
     const int *uoff = reinterpret_cast<const int *>(smem + L.uoff);
     const int *pairs = reinterpret_cast<const int *>(smem + L.pairs);
-    const int n_units = uniform(reinterpret_cast<const int *>(smem + L.misc)[0]);
-    const int u = blockIdx.y;
-    if (u >= n_units) return;
-    const int e = uniform(uexp[u]);
+    int u = blockIdx.y, e;
+    if (ROUTE && a.n_shared && blockIdx.y == 0) {
+        int *pw = reinterpret_cast<int *>(smem + L.pairs);
+        int *ow = reinterpret_cast<int *>(smem + L.uoff);
+        for (int t = tid; t < S; t += 256) pw[t] = P + t;
+        if (tid == 0) {
+            ow[0] = 0;
+            ow[1] = S;
+        }
+        __syncthreads();
+        u = 0;
+        e = -1;
+    } else {
+        const int32_t *idx = a.idx;
+        if (ROUTE) {
+            const RoutePlan R = route_plan(L.total, S, K, E);
+            int32_t *idx_l = reinterpret_cast<int32_t *>(smem + R.idx);
+            float *w_l = reinterpret_cast<float *>(smem + R.w);
+            float *sig_s = reinterpret_cast<float *>(smem + R.sig) + wave * E;
+            float *selsig = reinterpret_cast<float *>(smem + R.selsig) + wave * 32;
+            bool ok = true;
+            for (int t = wave; t < S; t += 4) {
+                const float *lg = a.logits + (size_t)t * E;
+                auto ld = [&](int q) { return lg[q]; };
+                ok = (E <= 256 ? select_wave<4>(ld, a.bias, E, K, a.rsf, a.norm, idx_l + t * K, w_l + t * K, sig_s,
+                                                selsig)
+                               : select_wave<16>(ld, a.bias, E, K, a.rsf, a.norm, idx_l + t * K, w_l + t * K,
+                                                 sig_s, selsig)) && ok;
+            }
+            __syncthreads();
+            if (blockIdx.x == 0 && blockIdx.y == (a.n_shared ? 1 : 0)) {
+                if (!ok && lane == 0) raise_status(a.status, ST_NONFINITE);
+                for (int q = tid; q < P; q += 256) {
+                    a.idx_out[q] = idx_l[q];
+                    a.w_out[q] = w_l[q];
+                }
+            }
+            idx = idx_l;
+            u = blockIdx.y - (a.n_shared ? 1 : 0);
+        }
+        build_units(idx, S, K, E, a.n_shared, smem, L, a.status,
+                    !ROUTE && blockIdx.x == 0 && blockIdx.y == 0 && a.pend_mode != 2);
+        const int n_units = uniform(reinterpret_cast<const int *>(smem + L.misc)[0]);
+        const int n_routed = uniform(reinterpret_cast<const int *>(smem + L.misc)[1]);
+        if (u >= (ROUTE ? n_routed : n_units)) return;
+        e = uniform(uexp[u]);
+    }
     if (e >= 0 && a.pend_mode != 0) {
         const bool pend = (a.pend[e >> 5] >> (e & 31)) & 1u;
         if ((a.pend_mode == 1) == pend) return;
@@ -77,15 +140,31 @@ __global__ __launch_bounds__(256) void k_gateup(const FwdArgs a) {
     const int vds = vd_stride(nb);
     for (int g0 = 0; g0 < np; g0 += NT) {
         const int ng = min(NT, np - g0);
-        // Q8_0(x) of this group's tokens (computed once per call) into LDS
+        // Q8_0(x) of this group's tokens (computed once per call) into LDS:
+        // direct global-to-LDS loads (1 KB of codes or 64 scales per
+        // wavefront instruction) when the rows split into whole chunks
         auto stage = [&]() {
-            for (int it = 0; it < ng; ++it) {
-                const int v = pairs[p0 + g0 + it];
-                const int t = v < P ? v / K : v - P;
-                const i32x4 *src = reinterpret_cast<const i32x4 *>(a.qx + (size_t)t * H);
-                i32x4 *dst = reinterpret_cast<i32x4 *>(vq + (size_t)it * H);
-                for (int q = tid; q < H / 16; q += 256) dst[q] = src[q];
-                for (int q = tid; q < nb; q += 256) vd[it * vds + q] = a.dx[(size_t)t * nb + q];
+            if (H % 2048 == 0) {
+                const int qch = H / 1024, dch = nb / 64;
+                for (int j = wave; j < ng * (qch + dch); j += 4) {
+                    const int it = j / (qch + dch), ch = j - it * (qch + dch);
+                    const int v = pairs[p0 + g0 + it];
+                    const int t = v < P ? v / K : v - P;
+                    if (ch < qch)
+                        lds_dma16(a.qx + (size_t)t * H + ch * 1024 + 16 * lane, vq + (size_t)it * H + ch * 1024);
+                    else
+                        lds_dma4(a.dx + (size_t)t * nb + (ch - qch) * 64 + lane, vd + it * vds + (ch - qch) * 64);
+                }
+                drain_vm();
+            } else {
+                for (int it = 0; it < ng; ++it) {
+                    const int v = pairs[p0 + g0 + it];
+                    const int t = v < P ? v / K : v - P;
+                    const i32x4 *src = reinterpret_cast<const i32x4 *>(a.qx + (size_t)t * H);
+                    i32x4 *dst = reinterpret_cast<i32x4 *>(vq + (size_t)it * H);
+                    for (int q = tid; q < H / 16; q += 256) dst[q] = src[q];
+                    for (int q = tid; q < nb; q += 256) vd[it * vds + q] = a.dx[(size_t)t * nb + q];
+                }
             }
             __syncthreads();
         };
@@ -206,20 +285,24 @@ template <typename F>
 static hipError_t launch_dyn(F kern, dim3 grid, size_t smem, hipStream_t st, const FwdArgs &a) {
     const hipError_t err = ensure_dyn_smem(reinterpret_cast<const void *>(kern), smem);
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(kern, grid, dim3(256), smem, st, a);
-    return hipGetLastError();
+    return launch(kern, grid, dim3(256), smem, st, a);
 }
 
-template <int BITS>
+template <int BITS, bool ROUTE>
 static hipError_t gateup_bits(const FwdArgs &a, hipStream_t st) {
     const int P = a.S * a.K;
     const int umax = std::min(P, a.E) + a.n_shared;
     const dim3 grid(a.I / 32, umax);
     const int nt = pick_nt(a.S);
-    const size_t smem = smem_plan(a.S, a.K, a.E, nt, a.H).total;
-    if (nt == 1) return launch_dyn(k_gateup<BITS, 1>, grid, smem, st, a);
-    if (nt == 2) return launch_dyn(k_gateup<BITS, 2>, grid, smem, st, a);
-    return launch_dyn(k_gateup<BITS, 4>, grid, smem, st, a);
+    const size_t base = smem_plan(a.S, a.K, a.E, nt, a.H).total;
+    const size_t smem = ROUTE ? route_plan(base, a.S, a.K, a.E).total : base;
+    if (nt == 1) return launch_dyn(k_gateup<BITS, 1, ROUTE>, grid, smem, st, a);
+    if (nt == 2) return launch_dyn(k_gateup<BITS, 2, ROUTE>, grid, smem, st, a);
+    return launch_dyn(k_gateup<BITS, 4, ROUTE>, grid, smem, st, a);
+}
+
+size_t gateup_route_smem(int S, int H, int E, int K) {
+    return route_plan(smem_plan(S, K, E, pick_nt(S), H).total, S, K, E).total;
 }
 
 template <int BITS>
@@ -235,14 +318,14 @@ static hipError_t down_bits(const FwdArgs &a, hipStream_t st) {
 }
 
 hipError_t launch_gateup(const FwdArgs &a, int bits, hipStream_t st) {
-    if (bits == 8) return gateup_bits<8>(a, st);
-    if (bits == 4) return gateup_bits<4>(a, st);
-    return gateup_bits<2>(a, st);
+    const bool route = a.logits != nullptr;
+    if (bits == 8) return route ? gateup_bits<8, true>(a, st) : gateup_bits<8, false>(a, st);
+    if (bits == 4) return route ? gateup_bits<4, true>(a, st) : gateup_bits<4, false>(a, st);
+    return route ? gateup_bits<2, true>(a, st) : gateup_bits<2, false>(a, st);
 }
 
 hipError_t launch_combine(const FwdArgs &a, hipStream_t st) {
-    hipLaunchKernelGGL(k_combine, dim3(a.H / 256, a.S), dim3(256), 0, st, a);
-    return hipGetLastError();
+    return launch(k_combine, dim3(a.H / 256, a.S), dim3(256), 0, st, a);
 }
 
 hipError_t launch_down(const FwdArgs &a, int bits, hipStream_t st) {

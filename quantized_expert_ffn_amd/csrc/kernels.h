@@ -1,8 +1,11 @@
 // Private interface between the C-ABI entry points and the kernel launchers.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <utility>
 
 namespace coli {
 
@@ -49,6 +52,13 @@ struct FwdArgs {
     int S, H, I, E, K, n_shared;
     int pend_mode;                 // 0: all units, 1: skip pending experts, 2: only pending
     uint32_t pend[32];             // bit e: expert e pending
+    // routing inside the gate/up kernel (coli_moe_layer): logits in, top-K out
+    const float *logits;           // [S, E]
+    const float *bias;             // [E] or null
+    int32_t *idx_out;              // [S, K]
+    float *w_out;                  // [S, K]
+    float rsf;
+    int norm;
 };
 
 // Router logits; with qx non-null the same launch writes Q8_0(x) to qx / dx.
@@ -74,6 +84,23 @@ enum KernelKind {
 };
 
 // Timing hooks implemented by the API layer.
+// While kernel timing is on and a timed kind is open on this thread, hands
+// out a start / stop event pair for the next launch (recorded by the
+// runtime at the kernel's own start and end) and files it under that kind.
+bool timing_pair(hipEvent_t *start, hipEvent_t *stop);
+
+// Every kernel of the library is launched through here.
+template <typename... KArgs, typename... Args>
+inline hipError_t launch(void (*kern)(KArgs...), dim3 grid, dim3 block, size_t smem, hipStream_t st,
+                         Args &&...args) {
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    if (timing_pair(&e0, &e1))
+        hipExtLaunchKernelGGL(kern, grid, block, (uint32_t)smem, st, e0, e1, 0, std::forward<Args>(args)...);
+    else
+        hipLaunchKernelGGL(kern, grid, block, smem, st, std::forward<Args>(args)...);
+    return hipGetLastError();
+}
+
 // Raises `kern`'s dynamic-LDS limit to at least `smem` bytes (once per
 // kernel and size, so launches under stream capture only enqueue work).
 hipError_t ensure_dyn_smem(const void *kern, size_t smem);
@@ -96,6 +123,11 @@ struct LayerArgs {
 
 // The persistent layer kernel: route = true computes the routing itself
 // (coli_moe_layer); route = false takes it from the arguments (coli_moe_forward).
+// LDS of the gate/up kernel when it also selects the routing.
+size_t gateup_route_smem(int S, int H, int E, int K);
+// Down projection + combine by output-row tiles (up to 8 tokens).
+hipError_t launch_down_rows(const FwdArgs &a, int bits, hipStream_t st);
+size_t down_rows_smem(int S, int I, int E, int K, int n_shared);
 hipError_t launch_layer(const FwdArgs &a, const LayerArgs &l, bool route, int bits, hipStream_t st);
 size_t layer_smem(int S, int H, int I, int E, int K, int n_shared);
 

@@ -477,8 +477,7 @@ static hipError_t layer_launch(const FwdArgs &a, const LayerArgs &l, hipStream_t
     const int umax = std::min(a.S * a.K, a.E) + a.n_shared;
     const int want = std::max(umax * (a.I / 32), a.H / ROWS2);
     const int G = std::max(1, std::min(want, cap));
-    hipLaunchKernelGGL((k_layer<BITS, NT, ROUTE, MAXJ>), dim3(G), dim3(LT), smem, st, a, l);
-    return hipGetLastError();
+    return launch(k_layer<BITS, NT, ROUTE, MAXJ>, dim3(G), dim3(LT), smem, st, a, l);
 }
 
 template <int BITS, bool ROUTE>

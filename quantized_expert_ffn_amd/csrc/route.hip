@@ -70,29 +70,21 @@ __global__ __launch_bounds__(64) void k_quant_x(const float *__restrict__ x, int
 hipError_t launch_router_logits(const float *x, const float *W, float *logits, uint32_t *status,
                                 int S, int H, int E, int8_t *qx, float *dx, hipStream_t st) {
     const int gx = E + (qx ? (H / 32 + 63) / 64 : 0);
-    if (H <= 24 * 256)
-        hipLaunchKernelGGL(k_router_logits<24>, dim3(gx, S), dim3(64), 0, st, x, W, logits, status, H, E, qx, dx);
-    else
-        hipLaunchKernelGGL(k_router_logits<16>, dim3(gx, S), dim3(64), 0, st, x, W, logits, status, H, E, qx, dx);
-    return hipGetLastError();
+    if (H <= 24 * 256) return launch(k_router_logits<24>, dim3(gx, S), dim3(64), 0, st, x, W, logits, status, H, E, qx, dx);
+    return launch(k_router_logits<16>, dim3(gx, S), dim3(64), 0, st, x, W, logits, status, H, E, qx, dx);
 }
 
 hipError_t launch_quant_x(const float *x, int8_t *qx, float *dx, uint32_t *status, int S, int H,
                           hipStream_t st) {
-    hipLaunchKernelGGL(k_quant_x, dim3((H / 32 + 63) / 64, S), dim3(64), 0, st, x, qx, dx, status, H);
-    return hipGetLastError();
+    return launch(k_quant_x, dim3((H / 32 + 63) / 64, S), dim3(64), 0, st, x, qx, dx, status, H);
 }
 
 hipError_t launch_router_select(const float *logits, const float *bias, int32_t *idx, float *w,
                                 uint32_t *status, int S, int E, int K, float rsf, int norm,
                                 hipStream_t st) {
     if (E <= 256)
-        hipLaunchKernelGGL(k_router_select<4>, dim3(S), dim3(64), 0, st, logits, bias, idx, w, status, E,
-                           K, rsf, norm);
-    else
-        hipLaunchKernelGGL(k_router_select<16>, dim3(S), dim3(64), 0, st, logits, bias, idx, w, status, E,
-                           K, rsf, norm);
-    return hipGetLastError();
+        return launch(k_router_select<4>, dim3(S), dim3(64), 0, st, logits, bias, idx, w, status, E, K, rsf, norm);
+    return launch(k_router_select<16>, dim3(S), dim3(64), 0, st, logits, bias, idx, w, status, E, K, rsf, norm);
 }
 
 }  // namespace coli

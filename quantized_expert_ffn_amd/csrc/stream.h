@@ -144,6 +144,51 @@ __device__ inline void build_units(const int32_t *__restrict__ idx, int S, int K
     __syncthreads();
 }
 
+// Staging of device words into LDS in rounds: in round r a thread loads up
+// to MW words of an array (word i from src(i), indices clamped into range,
+// n >= 1) into registers, and later stores them (to dst(i)).  Callers issue
+// the loads of every array of a round before any store, so a round costs a
+// single memory latency.
+template <int MW, typename T, typename Src>
+__device__ __forceinline__ void stage_load(T (&v)[MW], int round, int n, Src src) {
+    const int nthr = blockDim.x, base = round * MW * nthr + (int)threadIdx.x;
+#pragma unroll
+    for (int k = 0; k < MW; ++k) v[k] = *src(min(base + k * nthr, n - 1));
+}
+template <int MW, typename T, typename Dst>
+__device__ __forceinline__ void stage_store(const T (&v)[MW], int round, int n, Dst dst) {
+    const int nthr = blockDim.x, base = round * MW * nthr + (int)threadIdx.x;
+#pragma unroll
+    for (int k = 0; k < MW; ++k)
+        if (base + k * nthr < n) *dst(base + k * nthr) = v[k];
+}
+__device__ __forceinline__ int stage_rounds(int n, int per_round) { return (n + per_round - 1) / per_round; }
+
+// Direct global-to-LDS loads (no registers): lane l of the wavefront reads
+// 16 (or 4) bytes at its own src and the hardware writes them to
+// lds_wave + 16 l (or + 4 l); lds_wave must be the same in every lane.
+// Completion is tracked by the vector-memory counter: wait for it, then a
+// workgroup barrier, before the LDS data is read.
+__device__ __forceinline__ void lds_dma16(const void *src, void *lds_wave) {
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
+                                     (__attribute__((address_space(3))) void *)lds_wave, 16, 0, 0);
+}
+__device__ __forceinline__ void lds_dma4(const void *src, void *lds_wave) {
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
+                                     (__attribute__((address_space(3))) void *)lds_wave, 4, 0, 0);
+}
+__host__ __device__ inline int round_up(int v, int m) { return (v + m - 1) / m * m; }
+
+// Waits until at most N of this thread's vector-memory operations are
+// outstanding (they complete in issue order); gfx9 s_waitcnt encoding, with
+// expcnt and lgkmcnt left at their maxima.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+__device__ __forceinline__ void drain_vm() { wait_vm<0>(); }
+
 __device__ __forceinline__ void load_act(const int8_t *vq, int b, int32_t a[8]) {
     const i32x4 *p = reinterpret_cast<const i32x4 *>(vq + 32 * b);
     const i32x4 lo = p[0], hi = p[1];
