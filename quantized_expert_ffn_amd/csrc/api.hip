@@ -308,6 +308,7 @@ int coli_moe_forward(const coli_moe_dims *d, int32_t S, const float *x, const in
         l.qx = reinterpret_cast<int8_t *>(w8 + L.qx);
         l.dx = reinterpret_cast<float *>(w8 + L.dx);
         l.sync = reinterpret_cast<uint32_t *>(w8) + WS_SYNC_LAYER;
+        l.flags = w8 + L.flags;
         timing_before(KK_FORWARD_PERSISTENT, st);
         e = launch_layer(a, l, false, d->wbits, st);
         timing_after(KK_FORWARD_PERSISTENT, st);
@@ -341,19 +342,40 @@ int coli_moe_layer(const coli_moe_dims *d, int32_t S, const float *x, const floa
         const size_t smem = forward_smem_max(S, d->hidden, d->inter, d->n_experts, d->top_k, d->n_shared);
         if (smem > 160 * 1024)
             return fail(COLI_EINVAL, "shape needs %zu bytes of LDS per workgroup (> 160 KiB)", smem);
-        // up to 8 tokens: the gate/up kernel selects the routing from the logits
-        const bool fused = S <= 8 &&
-                           gateup_route_smem(S, d->hidden, d->n_experts, d->top_k) <= 160 * 1024;
-        rc = route_launches(d, S, x, router_w, router_bias, topk_idx, topk_w, w8, L, true, !fused, st);
-        if (rc) return rc;
-        if (fused) {
-            a.logits = reinterpret_cast<const float *>(w8 + L.logits);
-            a.bias = router_bias;
-            a.idx_out = topk_idx;
-            a.w_out = topk_w;
-            a.rsf = d->routed_scaling_factor;
-            a.norm = d->norm_topk_prob;
+        // up to ROUTE_FUSE_MAX tokens: one router launch also selects the
+        // routing and writes the call's unit table, which the expert kernels read
+        if (S <= ROUTE_FUSE_MAX && route_fused_smem(S, d->top_k, d->n_experts) <= 64 * 1024) {
+            RouteArgs r;
+            std::memset(&r, 0, sizeof r);
+            r.x = x;
+            r.W = router_w;
+            r.bias = router_bias;
+            r.logits = reinterpret_cast<float *>(w8 + L.logits);
+            r.status = reinterpret_cast<uint32_t *>(w8 + L.status);
+            r.qx = reinterpret_cast<int8_t *>(w8 + L.qx);
+            r.dx = reinterpret_cast<float *>(w8 + L.dx);
+            r.idx_out = topk_idx;
+            r.w_out = topk_w;
+            r.blobs = reinterpret_cast<const uint8_t *const *>(expert_blobs);
+            r.shared = static_cast<const uint8_t *>(shared_blob);
+            r.units = w8 + L.units;
+            r.sync = reinterpret_cast<uint32_t *>(w8) + WS_SYNC_ROUTE;
+            r.S = S;
+            r.H = d->hidden;
+            r.E = d->n_experts;
+            r.K = d->top_k;
+            r.n_shared = d->n_shared;
+            r.norm = d->norm_topk_prob;
+            r.rsf = d->routed_scaling_factor;
+            timing_before(KK_ROUTER_LOGITS, st);
+            const hipError_t e = launch_route_fused(r, st);
+            timing_after(KK_ROUTER_LOGITS, st);
+            if (e != hipSuccess) return hip_fail(e, "router launch");
+            a.units = w8 + L.units;
+            return forward_launches(a, d->wbits, false, nullptr, true, st);
         }
+        rc = route_launches(d, S, x, router_w, router_bias, topk_idx, topk_w, w8, L, true, true, st);
+        if (rc) return rc;
         return forward_launches(a, d->wbits, false, nullptr, true, st);
     }
     LayerArgs l;
@@ -368,6 +390,7 @@ int coli_moe_layer(const coli_moe_dims *d, int32_t S, const float *x, const floa
     l.qx = reinterpret_cast<int8_t *>(w8 + L.qx);
     l.dx = reinterpret_cast<float *>(w8 + L.dx);
     l.sync = reinterpret_cast<uint32_t *>(w8) + WS_SYNC_LAYER;
+    l.flags = w8 + L.flags;
     timing_before(KK_LAYER, st);
     hipError_t e = launch_layer(a, l, true, d->wbits, st);
     timing_after(KK_LAYER, st);

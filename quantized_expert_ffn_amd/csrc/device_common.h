@@ -27,6 +27,28 @@ enum : uint32_t {
     ST_TIMEOUT = 8u,       // a grid barrier of a persistent kernel gave up waiting
 };
 
+// Device-scope (all L2 slices) relaxed accesses, for data exchanged between
+// workgroups inside one launch; a writer drains its stores (drain()) before
+// it signals through an atomic.
+__device__ __forceinline__ void st_dev(uint32_t *p, uint32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev(int32_t *p, int32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev(float *p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_dev(const float *p) {
+    return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int32_t ld_dev(const int32_t *p) {
+    return __hip_atomic_load(const_cast<int32_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Waits for every outstanding memory operation of this thread.
+__device__ __forceinline__ void drain() { __builtin_amdgcn_s_waitcnt(0); }
+
 __device__ __forceinline__ void raise_status(uint32_t *status, uint32_t bit) {
     // vector-memory atomic; the address is a plain global pointer
     __hip_atomic_fetch_or(status, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -99,9 +121,9 @@ __device__ __forceinline__ int8_t q8_0_lane(float v, float *d_out) {
 }
 
 // The same quantisation with one lane holding a whole 32-value block: reads
-// x[0..31], writes the 32 codes to q[0..31] (16-byte aligned) and returns d.
-// *ok is cleared on a non-finite input.
-__device__ __forceinline__ float q8_0_block_lane(const float *__restrict__ x, int8_t *__restrict__ q, bool *ok) {
+// x[0..31] (16-byte aligned), returns d and the 32 codes as 8 little-endian
+// words in w.  *ok is cleared on a non-finite input.
+__device__ __forceinline__ float q8_0_block_words(const float *__restrict__ x, uint32_t w[8], bool *ok) {
     float v[32];
     const f32x4 *xv = reinterpret_cast<const f32x4 *>(x);
 #pragma unroll
@@ -118,7 +140,6 @@ __device__ __forceinline__ float q8_0_block_lane(const float *__restrict__ x, in
     }
     *ok = good;
     const float d = a / 127.0f;
-    uint32_t w[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         uint32_t word = 0;
@@ -133,6 +154,13 @@ __device__ __forceinline__ float q8_0_block_lane(const float *__restrict__ x, in
         }
         w[i] = word;
     }
+    return d;
+}
+
+// As q8_0_block_words, storing the codes to q[0..31] (16-byte aligned).
+__device__ __forceinline__ float q8_0_block_lane(const float *__restrict__ x, int8_t *__restrict__ q, bool *ok) {
+    uint32_t w[8];
+    const float d = q8_0_block_words(x, w, ok);
     u32x4 *qv = reinterpret_cast<u32x4 *>(q);
     qv[0] = u32x4{w[0], w[1], w[2], w[3]};
     qv[1] = u32x4{w[4], w[5], w[6], w[7]};

@@ -1,0 +1,276 @@
+// Down projection and combine of one tile of 8 output rows for every unit of
+// a decode / speculative-verify call (colibrì README v1.0, "What's
+// implemented": SwiGLU experts on Q8_0 activations, shared expert,
+// batch-union MoE).  Used by the down+combine kernel and by the down phase
+// of the persistent layer kernel.
+//
+// The workgroup that owns rows r0 .. r0+7 (2 per wavefront) holds every term
+// of those output elements and combines them itself: one writer per element,
+// no floating-point atomics.  Per batch of units (up to UB units and
+// DR_MAXPB pair slots): lane b loads block c*64 + b of its wavefront's two
+// rows for each unit (one straight run of loads; slots past the batch read
+// through an empty buffer resource, which returns zeros without touching
+// memory), the batch's Q8_0(h) vectors and block scales are staged in LDS,
+// the exact int32 block dots go to LDS, and lane (row, pair) runs the
+// binary32 chain acc = fmaf(d_b, isum_b, acc) over the blocks in ascending
+// order; y = acc * s_down[row].  The combine is the fmaf chain over k in rank
+// order of w[t,k] * y[t,k][row] from 0, plus the shared expert's y.
+#pragma once
+
+#include <type_traits>
+
+#include "device_common.h"
+#include "kernels.h"
+#include "stream.h"
+
+namespace coli {
+
+constexpr int DR_T = 256;                // threads per workgroup
+constexpr int DR_W = DR_T / 64;          // wavefronts
+constexpr int DR_RPW = 2;                // rows per wavefront
+constexpr int DR_ROWS = DR_W * DR_RPW;   // rows per workgroup
+constexpr int DR_MAXPB = 16;             // pair slots per batch (chain lanes: DR_RPW x DR_MAXPB)
+constexpr int DR_MQ = 5, DR_MD = 3;      // staging words per thread and round (codes, scales)
+constexpr int CPOL_SC1 = 16;             // buffer cache policy: device-scope coherent
+
+template <int BITS>
+struct DownRowsBatch {
+    static constexpr int UB = BITS == 8 ? 4 : (BITS == 4 ? 9 : 16);  // units per batch
+};
+
+// LDS of one down tile (from `base`).
+struct DownTilePlan {
+    size_t qh, dh, isum, sdn, y, end;
+};
+__host__ __device__ inline DownTilePlan down_tile_plan(size_t base, int S, int K, int E, int n_shared, int I) {
+    DownTilePlan p;
+    const int P = S * K;
+    const int umax = (P < E ? P : E) + 1;
+    const int slots = P + S * n_shared;
+    const int mpb = slots < DR_MAXPB ? slots : DR_MAXPB;
+    p.qh = a16(base);
+    p.dh = a16(p.qh + (size_t)mpb * round_up(I, 1024));
+    p.isum = a16(p.dh + 4 * (size_t)mpb * round_up(I / 32, 64));
+    p.sdn = a16(p.isum + 4 * (size_t)DR_W * DR_RPW * mpb * ISUM_PITCH);
+    p.y = a16(p.sdn + 4 * (size_t)umax * DR_ROWS);
+    p.end = a16(p.y + 4 * (size_t)slots * DR_ROWS);
+    return p;
+}
+
+// One down tile.  COHERENT: Q8_0(h) was written earlier in the same launch
+// by other workgroups, so it is read with device-scope loads.
+template <int BITS, bool ONE_TOKEN, bool COHERENT>
+struct DownTile {
+    static constexpr int UB = DownRowsBatch<BITS>::UB;
+    const FwdArgs &a;
+    uint8_t *smem;
+    DownTilePlan D;
+    const int *uoff, *pairs;
+    const uint8_t *const *ublob;   // LDS, [n_units]
+    const float *w;                // routing weights [S*K] (LDS or device)
+    int n_units, rt, mpb, nbi, nch, qpitch, dpitch;
+    uint32_t m16, mnb;             // reciprocals for i / (I / 16) and i / nbi (fast_div)
+    size_t ro, irow;
+    BlobLayout BL;
+    BlockBits<BITS> wv[UB][DR_RPW];
+
+    __device__ __forceinline__ DownTile(const FwdArgs &a_, uint8_t *smem_, const DownTilePlan &D_, const int *uoff_,
+                        const int *pairs_, const uint8_t *const *ublob_, const float *w_, int n_units_, int rt_)
+        : a(a_), smem(smem_), D(D_), uoff(uoff_), pairs(pairs_), ublob(ublob_), w(w_), n_units(n_units_), rt(rt_) {
+        const int slots = a.S * a.K + a.S * a.n_shared;
+        mpb = slots < DR_MAXPB ? slots : DR_MAXPB;
+        nbi = a.I / 32;
+        nch = (nbi + 63) / 64;
+        qpitch = round_up(a.I, 1024);
+        dpitch = round_up(nbi, 64);
+        m16 = fast_div_magic(a.I / 16);
+        mnb = fast_div_magic(nbi);
+        BL = blob_layout(a.H, a.I, BITS);
+        irow = (size_t)a.I * BITS / 8;
+        ro = BL.down + (size_t)(rt * DR_ROWS + uniform(threadIdx.x >> 6) * DR_RPW) * irow;
+    }
+
+    __device__ __forceinline__ int batch_end(int u0) const {
+        int u1 = u0, npb = 0;
+        while (u1 < n_units && u1 - u0 < UB) {
+            const int np = uoff[u1 + 1] - uoff[u1];
+            if (npb + np > mpb && u1 > u0) break;
+            npb += np;
+            ++u1;
+        }
+        return uniform(u1);
+    }
+
+    // All units in one batch, rows of one chunk, staging in one round: the
+    // straight-line case (the weights can be issued ahead, see issue()).
+    __device__ __forceinline__ bool single() const {
+        const int all_pairs = uniform(uoff[n_units]) - uniform(uoff[0]);
+        return nch == 1 && batch_end(0) == n_units && all_pairs * (a.I / 16) <= DR_MQ * DR_T &&
+               all_pairs * nbi <= DR_MD * DR_T;
+    }
+
+    // Weight loads of units [u0, u1), chunk c, in one straight run.
+    __device__ __forceinline__ void issue(int u0, int u1, int c) {
+        const int b = c * 64 + (int)(threadIdx.x & 63);
+#pragma unroll
+        for (int ui = 0; ui < UB; ++ui) {
+            const int uu = u0 + ui;
+            const uint8_t *blob = uniform_ptr(ublob[min(uu, n_units - 1)]);
+            const __amdgpu_buffer_rsrc_t rs = make_rsrc(blob, (uu < u1 && blob) ? (uint32_t)BL.total : 0u);
+#pragma unroll
+            for (int r = 0; r < DR_RPW; ++r) wv[ui][r] = load_block<BITS>(rs, (uint32_t)(ro + r * irow), b);
+        }
+    }
+
+    __device__ __forceinline__ i32x4 ld_qh(uint32_t off) const {
+        if (COHERENT) {
+            const uint32_t bytes = (uint32_t)(a.S * a.K + a.S * a.n_shared) * (uint32_t)a.I;
+            const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.qh, bytes);
+            return __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, CPOL_SC1));
+        }
+        return *reinterpret_cast<const i32x4 *>(a.qh + off);
+    }
+    __device__ __forceinline__ float ld_dh(size_t i) const { return COHERENT ? ld_dev(a.dh + i) : a.dh[i]; }
+
+    // One batch of units [u0, u1); ONE: single() holds and, with issued,
+    // the batch's weights were issued ahead by issue(0, n_units, 0).
+    template <bool ONE>
+    __device__ __forceinline__ int batch(int u0, bool issued) {
+        const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
+        const int I = a.I, r0 = rt * DR_ROWS;
+        int8_t *qh_l = reinterpret_cast<int8_t *>(smem + D.qh);
+        float *dh_l = reinterpret_cast<float *>(smem + D.dh);
+        int32_t *isum = reinterpret_cast<int32_t *>(smem + D.isum) + wave * DR_RPW * mpb * ISUM_PITCH;
+        float *sdn = reinterpret_cast<float *>(smem + D.sdn);
+        float *y_l = reinterpret_cast<float *>(smem + D.y);
+        const int u1 = ONE ? n_units : batch_end(u0);
+        const int pbase = uniform(uoff[u0]);
+        const int npb = uniform(uoff[u1]) - pbase;
+        const int cr = lane >> 4 >= DR_RPW ? 0 : lane >> 4, cp = lane & 15;   // chain lane (row, pair)
+        const bool chain_lane = lane < DR_RPW * 16;
+        float acc = 0.0f;
+        // Q8_0(h) of the batch's pairs, their block scales and the down-row
+        // scales of its units; the first round is issued before the weights
+        // so that it arrives first (staged through registers: reading LDS
+        // written by direct global-to-LDS loads would make the compiler wait
+        // for every load)
+        const int w16 = I / 16;
+        const int nq = npb * w16, nd = npb * nbi, ns = (u1 - u0) * DR_ROWS;
+        auto q_src = [&](int i) {
+            const int pb = fast_div(i, m16);
+            return ld_qh((uint32_t)pairs[pbase + pb] * (uint32_t)I + 16u * (uint32_t)(i - pb * w16));
+        };
+        auto q_dst = [&](int i) {
+            const int pb = fast_div(i, m16);
+            return reinterpret_cast<i32x4 *>(qh_l + (size_t)pb * qpitch) + (i - pb * w16);
+        };
+        auto d_src = [&](int i) {
+            const int pb = fast_div(i, mnb);
+            return ld_dh((size_t)pairs[pbase + pb] * nbi + (i - pb * nbi));
+        };
+        auto d_dst = [&](int i) {
+            const int pb = fast_div(i, mnb);
+            return dh_l + pb * dpitch + (i - pb * nbi);
+        };
+        auto s_src = [&](int i) {
+            const uint8_t *blob = ublob[u0 + i / DR_ROWS];
+            return blob ? reinterpret_cast<const float *>(blob + BL.s_down)[r0 + i % DR_ROWS] : 0.0f;
+        };
+        auto s_dst = [&](int i) { return sdn + u0 * DR_ROWS + i; };
+        const int nr = max(stage_rounds(nq, DR_MQ * DR_T), max(stage_rounds(nd, DR_MD * DR_T), stage_rounds(ns, DR_T)));
+        i32x4 qv[DR_MQ];
+        float dv[DR_MD], sv[1];
+        stage_fetch(qv, 0, nq, q_src);
+        stage_fetch(dv, 0, nd, d_src);
+        stage_fetch(sv, 0, ns, s_src);
+        __builtin_amdgcn_sched_barrier(0);
+        for (int c = 0; c < (ONE ? 1 : nch); ++c) {
+            const int b = c * 64 + lane;
+            const bool act = b < nbi;
+            if (!(ONE && issued)) issue(u0, u1, c);
+            if (c == 0) {
+                // the staged data are in once no more than the weight loads
+                // issued after them are outstanding
+                __builtin_amdgcn_sched_barrier(0);
+                if (ONE && issued)
+                    wait_vm<0>();
+                else
+                    wait_vm<UB * DR_RPW * BlockLoads<BITS>::N>();
+                stage_store(qv, 0, nq, q_dst);
+                stage_store(dv, 0, nd, d_dst);
+                stage_store(sv, 0, ns, s_dst);
+                for (int rd = 1; !ONE && rd < nr; ++rd) {
+                    stage_fetch(qv, rd, nq, q_src);
+                    stage_fetch(dv, rd, nd, d_src);
+                    stage_fetch(sv, rd, ns, s_src);
+                    stage_store(qv, rd, nq, q_dst);
+                    stage_store(dv, rd, nd, d_dst);
+                    stage_store(sv, rd, ns, s_dst);
+                }
+                __syncthreads();
+            }
+#pragma unroll
+            for (int ui = 0; ui < UB; ++ui) {
+                if (u0 + ui < u1) {
+                    const bool live = ublob[u0 + ui] != nullptr;
+                    const int q0 = uniform(uoff[u0 + ui]);
+                    const int q1 = ONE_TOKEN ? q0 + 1 : uniform(uoff[u0 + ui + 1]);
+#pragma unroll
+                    for (int q = q0; q < q1; ++q) {
+                        int32_t av[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+                        if (act) load_act(qh_l + (size_t)(q - pbase) * qpitch, b, av);
+#pragma unroll
+                        for (int r = 0; r < DR_RPW; ++r)
+                            isum[(r * mpb + (q - pbase)) * ISUM_PITCH + lane] =
+                                (act && live) ? block_dot(wv[ui][r], av) : 0;
+                    }
+                }
+            }
+            wave_lds_sync();
+            if (chain_lane && cp < npb)
+                acc = chain_chunk(acc, isum + (cr * mpb + cp) * ISUM_PITCH, dh_l + cp * dpitch + c * 64,
+                                  min(64, nbi - c * 64));
+            wave_lds_sync();
+        }
+        if (chain_lane && cp < npb) {
+            int ub = u0;   // the pair's unit: the last one whose first pair is at or before it
+            while (ub + 1 < u1 && uoff[ub + 1] <= pbase + cp) ++ub;
+            const int slot = pairs[pbase + cp];
+            const int rl = wave * DR_RPW + cr;
+            y_l[slot * DR_ROWS + rl] = ublob[ub] ? acc * sdn[ub * DR_ROWS + rl] : 0.0f;
+        }
+        __syncthreads();   // the next batch restages qh_l / dh_l
+        return u1;
+    }
+
+    // Every unit of the tile, then the combine.  issued: single() holds and
+    // issue(0, n_units, 0) was called.
+    __device__ __forceinline__ void run(bool issued) {
+        const int tid = threadIdx.x;
+        const int S = a.S, K = a.K, P = S * K, slots = P + S * a.n_shared;
+        float *y_l = reinterpret_cast<float *>(smem + D.y);
+        __syncthreads();   // a previous tile's combine may still be reading y_l
+        for (int q = tid; q < slots * DR_ROWS; q += DR_T) y_l[q] = 0.0f;
+        if (issued) {
+            batch<true>(0, true);
+        } else if (single()) {
+            batch<true>(0, false);
+        } else {
+            for (int u0 = 0; u0 < n_units;) u0 = batch<false>(u0, false);
+        }
+        const int r0 = rt * DR_ROWS;
+        for (int q = tid; q < S * DR_ROWS; q += DR_T) {
+            const int t = q / DR_ROWS, rl = q - t * DR_ROWS;
+            float acc = 0.0f;
+            for (int k = 0; k < K; ++k) {
+                const float wk = w[t * K + k];
+                if (rt == 0 && rl == 0 && !finite_f32(wk)) raise_status(a.status, ST_NONFINITE);
+                acc = __builtin_fmaf(wk, y_l[(t * K + k) * DR_ROWS + rl], acc);
+            }
+            if (a.n_shared) acc = acc + y_l[(P + t) * DR_ROWS + rl];
+            a.out[(size_t)t * a.H + r0 + rl] = acc;
+        }
+    }
+};
+
+}  // namespace coli

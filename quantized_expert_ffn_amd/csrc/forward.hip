@@ -28,33 +28,28 @@
 
 #include "device_common.h"
 #include "kernels.h"
-#include "router.h"
 #include "stream.h"
 
 namespace coli {
 
-// LDS of the in-kernel routing (after the gate/up plan): per-wave sigmoid
-// scratch [4][E], selected sigmoids [4][32], top-K indices and weights [S*K].
-struct RoutePlan {
-    size_t sig, selsig, idx, w, total;
-};
-__host__ __device__ inline RoutePlan route_plan(size_t base, int S, int K, int E) {
-    RoutePlan r;
-    r.sig = a16(base);
-    r.selsig = a16(r.sig + 4 * 4 * (size_t)E);
-    r.idx = a16(r.selsig + 4 * 4 * 32);
-    r.w = a16(r.idx + 4 * (size_t)S * K);
-    r.total = a16(r.w + 4 * (size_t)S * K);
-    return r;
+// Copies the unit table of the call (workspace, built by the router
+// launch) into LDS words at `tab`; returns the blob pointer of unit u (or
+// null when u is past the table).  One memory latency.
+__device__ __forceinline__ const uint8_t *load_unit_table(const uint8_t *units, const UnitTable &U, int *tab,
+                                                          int u) {
+    const int32_t *src = reinterpret_cast<const int32_t *>(units);
+    for (int q = threadIdx.x; q < U.words; q += blockDim.x) tab[q] = src[q];
+    const uint8_t *blob = u < U.umax ? reinterpret_cast<const uint8_t *const *>(units + U.ublob)[u] : nullptr;
+    __syncthreads();
+    return blob;
 }
 
-// Gate/up of one (32-row tile, unit).  With ROUTE the routing is taken from
-// the router logits here: grid row y = 0 is the shared expert (its pairs do
-// not depend on the routing, so it starts at once); every other workgroup
-// selects the top-K of every token itself (one wavefront per token, the
-// same bits in every workgroup), builds the unit table and takes routed
-// unit y - 1; workgroup (0, 1) writes the routing out.
-template <int BITS, int NT, bool ROUTE>
+// Gate/up of one (32-row tile, unit).  With TABLE the units come from the
+// call's unit table (coli_moe_layer): grid row y = 0 is the shared expert
+// (its pairs do not depend on the routing, so it needs no table) and row
+// y > 0 routed unit y - 1.  Otherwise every workgroup builds the unit table
+// from topk_idx and takes unit y.
+template <int BITS, int NT, bool TABLE>
 __global__ __launch_bounds__(256) void k_gateup(const FwdArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
@@ -64,7 +59,8 @@ __global__ __launch_bounds__(256) void k_gateup(const FwdArgs a) {
     const int *uoff = reinterpret_cast<const int *>(smem + L.uoff);
     const int *pairs = reinterpret_cast<const int *>(smem + L.pairs);
     int u = blockIdx.y, e;
-    if (ROUTE && a.n_shared && blockIdx.y == 0) {
+    const uint8_t *tblob = nullptr;
+    if (TABLE && a.n_shared && blockIdx.y == 0) {
         int *pw = reinterpret_cast<int *>(smem + L.pairs);
         int *ow = reinterpret_cast<int *>(smem + L.uoff);
         for (int t = tid; t < S; t += 256) pw[t] = P + t;
@@ -75,46 +71,31 @@ __global__ __launch_bounds__(256) void k_gateup(const FwdArgs a) {
         __syncthreads();
         u = 0;
         e = -1;
+        tblob = a.shared;
+    } else if (TABLE) {
+        // the table's words go to the start of LDS (the region this kernel
+        // otherwise uses to build its unit table, which is at least as large)
+        const UnitTable U = unit_table(S, K, E);
+        int *tab = reinterpret_cast<int *>(smem);
+        u = blockIdx.y - (a.n_shared ? 1 : 0);
+        tblob = load_unit_table(a.units, U, tab, u);
+        uexp = tab + U.uexp;
+        uoff = tab + U.uoff;
+        pairs = tab + U.pairs;
+        if (u >= uniform(tab[1])) return;
+        e = uniform(uexp[u]);
     } else {
-        const int32_t *idx = a.idx;
-        if (ROUTE) {
-            const RoutePlan R = route_plan(L.total, S, K, E);
-            int32_t *idx_l = reinterpret_cast<int32_t *>(smem + R.idx);
-            float *w_l = reinterpret_cast<float *>(smem + R.w);
-            float *sig_s = reinterpret_cast<float *>(smem + R.sig) + wave * E;
-            float *selsig = reinterpret_cast<float *>(smem + R.selsig) + wave * 32;
-            bool ok = true;
-            for (int t = wave; t < S; t += 4) {
-                const float *lg = a.logits + (size_t)t * E;
-                auto ld = [&](int q) { return lg[q]; };
-                ok = (E <= 256 ? select_wave<4>(ld, a.bias, E, K, a.rsf, a.norm, idx_l + t * K, w_l + t * K, sig_s,
-                                                selsig)
-                               : select_wave<16>(ld, a.bias, E, K, a.rsf, a.norm, idx_l + t * K, w_l + t * K,
-                                                 sig_s, selsig)) && ok;
-            }
-            __syncthreads();
-            if (blockIdx.x == 0 && blockIdx.y == (a.n_shared ? 1 : 0)) {
-                if (!ok && lane == 0) raise_status(a.status, ST_NONFINITE);
-                for (int q = tid; q < P; q += 256) {
-                    a.idx_out[q] = idx_l[q];
-                    a.w_out[q] = w_l[q];
-                }
-            }
-            idx = idx_l;
-            u = blockIdx.y - (a.n_shared ? 1 : 0);
-        }
-        build_units(idx, S, K, E, a.n_shared, smem, L, a.status,
-                    !ROUTE && blockIdx.x == 0 && blockIdx.y == 0 && a.pend_mode != 2);
+        build_units(a.idx, S, K, E, a.n_shared, smem, L, a.status,
+                    blockIdx.x == 0 && blockIdx.y == 0 && a.pend_mode != 2);
         const int n_units = uniform(reinterpret_cast<const int *>(smem + L.misc)[0]);
-        const int n_routed = uniform(reinterpret_cast<const int *>(smem + L.misc)[1]);
-        if (u >= (ROUTE ? n_routed : n_units)) return;
+        if (u >= n_units) return;
         e = uniform(uexp[u]);
     }
     if (e >= 0 && a.pend_mode != 0) {
         const bool pend = (a.pend[e >> 5] >> (e & 31)) & 1u;
         if ((a.pend_mode == 1) == pend) return;
     }
-    const uint8_t *blob = uniform_ptr(e < 0 ? a.shared : a.blobs[e]);
+    const uint8_t *blob = uniform_ptr(TABLE ? tblob : (e < 0 ? a.shared : a.blobs[e]));
     if (blob == nullptr) {
         if (tid == 0) raise_status(a.status, ST_NOTRESIDENT);
         return;
@@ -288,21 +269,16 @@ static hipError_t launch_dyn(F kern, dim3 grid, size_t smem, hipStream_t st, con
     return launch(kern, grid, dim3(256), smem, st, a);
 }
 
-template <int BITS, bool ROUTE>
+template <int BITS, bool TABLE>
 static hipError_t gateup_bits(const FwdArgs &a, hipStream_t st) {
     const int P = a.S * a.K;
     const int umax = std::min(P, a.E) + a.n_shared;
     const dim3 grid(a.I / 32, umax);
     const int nt = pick_nt(a.S);
-    const size_t base = smem_plan(a.S, a.K, a.E, nt, a.H).total;
-    const size_t smem = ROUTE ? route_plan(base, a.S, a.K, a.E).total : base;
-    if (nt == 1) return launch_dyn(k_gateup<BITS, 1, ROUTE>, grid, smem, st, a);
-    if (nt == 2) return launch_dyn(k_gateup<BITS, 2, ROUTE>, grid, smem, st, a);
-    return launch_dyn(k_gateup<BITS, 4, ROUTE>, grid, smem, st, a);
-}
-
-size_t gateup_route_smem(int S, int H, int E, int K) {
-    return route_plan(smem_plan(S, K, E, pick_nt(S), H).total, S, K, E).total;
+    const size_t smem = smem_plan(a.S, a.K, a.E, nt, a.H).total;
+    if (nt == 1) return launch_dyn(k_gateup<BITS, 1, TABLE>, grid, smem, st, a);
+    if (nt == 2) return launch_dyn(k_gateup<BITS, 2, TABLE>, grid, smem, st, a);
+    return launch_dyn(k_gateup<BITS, 4, TABLE>, grid, smem, st, a);
 }
 
 template <int BITS>
@@ -318,10 +294,10 @@ static hipError_t down_bits(const FwdArgs &a, hipStream_t st) {
 }
 
 hipError_t launch_gateup(const FwdArgs &a, int bits, hipStream_t st) {
-    const bool route = a.logits != nullptr;
-    if (bits == 8) return route ? gateup_bits<8, true>(a, st) : gateup_bits<8, false>(a, st);
-    if (bits == 4) return route ? gateup_bits<4, true>(a, st) : gateup_bits<4, false>(a, st);
-    return route ? gateup_bits<2, true>(a, st) : gateup_bits<2, false>(a, st);
+    const bool table = a.units != nullptr;
+    if (bits == 8) return table ? gateup_bits<8, true>(a, st) : gateup_bits<8, false>(a, st);
+    if (bits == 4) return table ? gateup_bits<4, true>(a, st) : gateup_bits<4, false>(a, st);
+    return table ? gateup_bits<2, true>(a, st) : gateup_bits<2, false>(a, st);
 }
 
 hipError_t launch_combine(const FwdArgs &a, hipStream_t st) {

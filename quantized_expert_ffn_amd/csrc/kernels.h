@@ -12,21 +12,56 @@ namespace coli {
 // Workspace carve-up for a call with S tokens.  The status word sits at a
 // fixed offset (it persists between calls); the rest is per call.
 struct WsLayout {
-    size_t status, logits, qx, dx, qh, dh, Y, total;
+    size_t status, flags, logits, units, qx, dx, qh, dh, Y, total;
 };
 
-// Word index, inside the first 256 bytes of the workspace, of the three
+// Release flags of the persistent kernel's barriers: one per workgroup
+// (FLAG_COPIES of them, FLAG_STRIDE bytes apart), so that every waiting
+// workgroup polls a word of its own.
+constexpr int FLAG_COPIES = 2048;
+constexpr int FLAG_STRIDE = 64;
+constexpr int N_FLAGS = 3;   // barrier A, Q8_0(x) published, barrier B
+
+// Word index, inside the first 256 bytes of the workspace, of the four
 // barrier words of the persistent layer kernel.
 constexpr int WS_SYNC_LAYER = 32;
+// Word index of the router launch's arrival counters: one per token (up to
+// ROUTE_FUSE_MAX tokens), then one for the tokens whose selection is done.
+constexpr int WS_SYNC_ROUTE = 48;
+constexpr int ROUTE_FUSE_MAX = 8;
 
 inline size_t al256h(size_t v) { return (v + 255) & ~(size_t)255; }
+
+// Unit table of a call, as int32 words: [0] units, [1] routed units,
+// [2] valid routed pairs, [3] 0, then uexp[umax] (expert id, -1 = shared),
+// uoff[umax + 1] (first pair of each unit), pairs[P + S] (pair slots grouped
+// by unit); then, 16-byte aligned, ublob[umax] (blob pointers).
+struct UnitTable {
+    int umax, words;      // units at most; int32 words before ublob
+    int uexp, uoff, pairs;
+    size_t ublob, total;  // byte offsets
+};
+__host__ __device__ inline UnitTable unit_table(int S, int K, int E) {
+    UnitTable u;
+    const int P = S * K;
+    u.umax = (P < E ? P : E) + 1;
+    u.uexp = 4;
+    u.uoff = u.uexp + u.umax;
+    u.pairs = u.uoff + u.umax + 1;
+    u.words = u.pairs + P + S;
+    u.ublob = ((size_t)4 * u.words + 15) & ~(size_t)15;
+    u.total = u.ublob + (size_t)8 * u.umax;
+    return u;
+}
 
 inline WsLayout ws_layout(int H, int I, int E, int K, int S) {
     WsLayout L;
     const size_t slots = (size_t)S * (size_t)(K + 1);
     L.status = 0;
-    L.logits = 256;
-    L.qx = al256h(L.logits + 4 * (size_t)S * (size_t)E);
+    L.flags = 256;
+    L.logits = L.flags + (size_t)N_FLAGS * FLAG_COPIES * FLAG_STRIDE;
+    L.units = al256h(L.logits + 4 * (size_t)S * (size_t)E);
+    L.qx = al256h(L.units + unit_table(S, K, E).total);
     L.dx = al256h(L.qx + (size_t)S * (size_t)H);
     L.qh = al256h(L.dx + 4 * (size_t)S * (size_t)(H / 32));
     L.dh = al256h(L.qh + slots * (size_t)I);
@@ -44,6 +79,7 @@ struct FwdArgs {
     const uint8_t *shared;         // shared expert blob or null
     const int8_t *qx;              // [S, H]   Q8_0(x) codes
     const float *dx;               // [S, H/32]
+    const uint8_t *units;          // unit table of the call (workspace), or null: built per workgroup
     int8_t *qh;                    // [S*(K+1), I]   Q8_0(h) codes per pair slot
     float *dh;                     // [S*(K+1), I/32]
     float *Y;                      // [S*(K+1), H]   expert outputs per pair slot
@@ -52,14 +88,27 @@ struct FwdArgs {
     int S, H, I, E, K, n_shared;
     int pend_mode;                 // 0: all units, 1: skip pending experts, 2: only pending
     uint32_t pend[32];             // bit e: expert e pending
-    // routing inside the gate/up kernel (coli_moe_layer): logits in, top-K out
-    const float *logits;           // [S, E]
-    const float *bias;             // [E] or null
-    int32_t *idx_out;              // [S, K]
-    float *w_out;                  // [S, K]
-    float rsf;
-    int norm;
 };
+
+// Router launch of coli_moe_layer for up to ROUTE_FUSE_MAX tokens: logits,
+// Q8_0(x), the top-K of each token (by the last workgroup to finish its
+// logits) and the unit table (by the last token to be selected).
+struct RouteArgs {
+    const float *x, *W, *bias;
+    float *logits;
+    uint32_t *status;
+    int8_t *qx;
+    float *dx;
+    int32_t *idx_out;
+    float *w_out;
+    const uint8_t *const *blobs;
+    const uint8_t *shared;
+    uint8_t *units;
+    uint32_t *sync;
+    int S, H, E, K, n_shared, norm;
+    float rsf;
+};
+hipError_t launch_route_fused(const RouteArgs &r, hipStream_t st);
 
 // Router logits; with qx non-null the same launch writes Q8_0(x) to qx / dx.
 hipError_t launch_router_logits(const float *x, const float *W, float *logits, uint32_t *status,
@@ -118,13 +167,13 @@ struct LayerArgs {
     int norm;
     int8_t *qx;              // [S, H]   workspace: Q8_0(x)
     float *dx;               // [S, H/32]
-    uint32_t *sync;          // 3 barrier words in the workspace
+    uint32_t *sync;          // 4 barrier words in the workspace
+    uint8_t *flags;          // release flags (N_FLAGS x FLAG_COPIES, FLAG_STRIDE apart)
 };
 
 // The persistent layer kernel: route = true computes the routing itself
 // (coli_moe_layer); route = false takes it from the arguments (coli_moe_forward).
-// LDS of the gate/up kernel when it also selects the routing.
-size_t gateup_route_smem(int S, int H, int E, int K);
+size_t route_fused_smem(int S, int K, int E);
 // Down projection + combine by output-row tiles (up to 8 tokens).
 hipError_t launch_down_rows(const FwdArgs &a, int bits, hipStream_t st);
 size_t down_rows_smem(int S, int I, int E, int K, int n_shared);

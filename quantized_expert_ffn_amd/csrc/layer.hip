@@ -4,30 +4,35 @@
 // batch-union MoE; "Colibri (colibrì): GLM-5.2 local inference on 25 GB of
 // RAM", "How it works (validated core mechanics)": the router).
 //
-// One launch runs the phases of the layer, separated by grid barriers
-// instead of kernel boundaries:
-//   R  router logits (one wavefront each) and Q8_0(x), one 32-block per half
-//      wave; skipped logits when the routing is given;
-//   -- barrier --
-//      every workgroup selects the top-K of every token itself (same bits
-//      everywhere) and builds the unit table of the batch union;
-//   1  gate/up items (unit, 32-row tile): 4 waves x 16 rows, SwiGLU and
-//      Q8_0(h) in the epilogue;
-//   -- barrier --
-//   2  down items of 8 output rows (2 per wave) for every unit, then the
-//      combine of those rows in the same workgroup (one writer each).
-// A workgroup drains its own stores (s_waitcnt) before it issues the next
-// phase's weight loads and arrives at the barrier, so the loads are in
-// flight during the wait.  Data crossing workgroups (logits, Q8_0(x),
-// Q8_0(h)) is written and read with device-scope (sc1) accesses, coherent
-// across the L2 slices of the GPU.  Barrier waits are bounded: a grid that
-// could not be fully resident ends with a status error, never a hang; the
-// host sizes the grid from the kernel's occupancy.
+// One launch runs the layer's phases; grid barriers replace kernel
+// boundaries, and every workgroup's work is laid out so that each phase's
+// memory traffic starts as early as its inputs allow:
+//   R  router logits, one wavefront each, on the highest-numbered
+//      workgroups (those with no gate/up item), published with device-scope
+//      stores; every workgroup with a possible gate/up item quantises x
+//      (Q8_0) into its own LDS;
+//   -- barrier A: the logits --
+//      routing: every workgroup selects the top-K of every token itself (the
+//      same bits everywhere, at raised wave priority) and builds the unit
+//      table of the batch union;
+//   1  gate/up items (unit, 32-row tile), shared expert first: its
+//      workgroups stream before barrier A, since its pairs do not depend on
+//      the routing; 4 waves x 16 rows, SwiGLU and Q8_0(h) in the epilogue,
+//      published with device-scope stores;
+//      each workgroup then issues the weight loads of its down tile;
+//   -- barrier B: Q8_0(h) --
+//   2  down tiles of 8 output rows for every unit, combined in the
+//      workgroup (one writer per output element).
+// A workgroup drains its stores (s_waitcnt) before it arrives at a barrier.
+// Barrier waits are bounded: a grid that could not be fully resident ends
+// with a status error, never a hang; the host sizes the grid from the
+// kernel's occupancy.
 #include <algorithm>
 #include <map>
 #include <mutex>
 
 #include "device_common.h"
+#include "down_rows.h"
 #include "kernels.h"
 #include "router.h"
 #include "stream.h"
@@ -37,33 +42,44 @@ namespace coli {
 constexpr uint32_t SPIN_LIMIT = 1u << 22;
 constexpr int LT = 256;         // threads per workgroup
 constexpr int LW = LT / 64;     // waves per workgroup
-constexpr int RW2 = 2;          // down rows per wave
-constexpr int ROWS2 = LW * RW2; // down rows per item
-constexpr int MAXPB = 32;       // pairs per down batch (chain lanes: RW2 x MAXPB)
-constexpr int CPOL_SC1 = 16;    // buffer cache policy: device-scope coherent
+constexpr int LMAXJ = 12;       // router row steps loaded per round
 
-__device__ __forceinline__ void st_dev(uint32_t *p, uint32_t v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_dev(float *p, float v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float ld_dev(float *p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Barriers: an arrival counter per barrier, and a release flag per
+// workgroup that the last arrival sets.  Each waiting workgroup polls its
+// own word: when hundreds of workgroups poll one word, the requests queue at
+// that word's memory channel and slow every other access to the channel.
+__device__ __forceinline__ uint32_t *flag_word(uint8_t *flags, int k, int copy) {
+    return reinterpret_cast<uint32_t *>(flags + ((size_t)k * FLAG_COPIES + copy) * FLAG_STRIDE);
 }
 
-// Waits for every outstanding memory operation of this thread.
-__device__ __forceinline__ void drain() { __builtin_amdgcn_s_waitcnt(0); }
+// Releases flag k of every workgroup (all lanes of the calling wave).
+__device__ __forceinline__ void release(uint8_t *flags, int k) {
+    const int lane = threadIdx.x & 63;
+    for (int c = lane; c < (int)gridDim.x; c += 64) st_dev(flag_word(flags, k, c), 1u);
+}
 
-// Grid barrier; callers drain() their stores first (loads issued after the
-// drain stay in flight).
-__device__ __forceinline__ void arrive_wait(uint32_t *ctr, uint32_t nwg, uint32_t *status) {
+// Counts one arrival of the calling wave at counter k; the arrival that
+// completes `target` releases flag k.
+__device__ __forceinline__ void signal(uint32_t *sync, uint8_t *flags, int k, uint32_t target) {
+    uint32_t prev = 0;
+    if ((threadIdx.x & 63) == 0)
+        prev = __hip_atomic_fetch_add(&sync[k], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (__builtin_amdgcn_readfirstlane(prev) == target - 1) release(flags, k);
+}
+
+// Workgroup arrival at barrier k (callers drain() their stores first).
+__device__ __forceinline__ void arrive(uint32_t *sync, uint8_t *flags, int k, uint32_t nwg) {
     __syncthreads();
+    if (threadIdx.x < 64) signal(sync, flags, k, nwg);
+}
+
+// Waits (bounded) until this workgroup's flag k is released.
+__device__ __forceinline__ void wait_flag(uint8_t *flags, int k, uint32_t *status) {
     if (threadIdx.x == 0) {
-        __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        uint32_t *f = flag_word(flags, k, blockIdx.x);
         uint32_t spins = 0;
-        while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < nwg) {
-            __builtin_amdgcn_s_sleep(1);
+        while (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
+            __builtin_amdgcn_s_sleep(2);
             if (++spins >= SPIN_LIMIT) {
                 raise_status(status, ST_TIMEOUT);
                 break;
@@ -73,219 +89,236 @@ __device__ __forceinline__ void arrive_wait(uint32_t *ctr, uint32_t nwg, uint32_
     __syncthreads();
 }
 
-// The last workgroup to leave resets the barrier words for the next launch.
-__device__ __forceinline__ void grid_exit(uint32_t *sync, int nbar, uint32_t nwg) {
+// The last workgroup to leave resets the counters and flags for the next
+// launch (counter `nbar` counts the departures).
+__device__ __forceinline__ void grid_exit(uint32_t *sync, uint8_t *flags, int nbar, uint32_t nwg) {
+    __shared__ int last;
     __syncthreads();
-    if (threadIdx.x == 0) {
-        const uint32_t prev =
-            __hip_atomic_fetch_add(&sync[nbar], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (prev == nwg - 1)
-            for (int i = 0; i <= nbar; ++i) st_dev(&sync[i], 0u);
+    if (threadIdx.x == 0)
+        last = __hip_atomic_fetch_add(&sync[nbar], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nwg - 1;
+    __syncthreads();
+    if (last) {
+        for (int c = threadIdx.x; c < N_FLAGS * (int)nwg; c += blockDim.x)
+            st_dev(flag_word(flags, c / (int)nwg, c % (int)nwg), 0u);
+        if ((int)threadIdx.x <= nbar) st_dev(&sync[threadIdx.x], 0u);
     }
 }
 
-template <int BITS>
-struct DownBatch {
-    static constexpr int UB = BITS == 8 ? 4 : 8;  // units per batch
-};
-
 struct LayerPlan {
-    size_t cnt, ustart, fill, uexp, uoff, pairs, misc;   // unit table
-    size_t idx, w, ublob, sig, selsig;                   // routing
-    size_t vq, vd, isum, gu;                             // phase 1
-    size_t qh, dh, isum2, sdn, y, total;                 // phase 2
+    SmemPlan T;                   // unit table
+    size_t idx, w, ublob;         // routing [P], weights [P], unit blob pointers [umax]
+    size_t xq, xd;                // Q8_0(x) of every token: codes [S][H], scales [S][vds]
+    size_t vq, vd;                // group staging when NT > 1
+    size_t isum, gu;              // block dots per wave, gate/up results
+    DownTilePlan tile;            // phase 2 (over the phase-1 region)
+    size_t total;
 };
 
 __host__ __device__ inline LayerPlan layer_plan(int S, int K, int E, int n_shared, int NT, int H, int I) {
     LayerPlan p;
     const int P = S * K;
     const int umax = (P < E ? P : E) + 1;
-    const int slots = P + S * n_shared;
-    const int mpb = slots < MAXPB ? slots : MAXPB;
-    p.cnt = 0;
-    p.ustart = a16(p.cnt + 4 * (size_t)E);
-    p.fill = a16(p.ustart + 4 * (size_t)E);
-    p.uexp = a16(p.fill + 4 * (size_t)E);
-    p.uoff = a16(p.uexp + 4 * (size_t)umax);
-    p.pairs = a16(p.uoff + 4 * (size_t)(umax + 1));
-    p.misc = a16(p.pairs + 4 * (size_t)(P + S));
-    p.idx = a16(p.misc + 16);
+    const int vds = vd_stride(H / 32);
+    p.T = smem_plan(S, K, E, 0, 0);
+    p.idx = a16(p.T.total);
     p.w = a16(p.idx + 4 * (size_t)P);
     p.ublob = a16(p.w + 4 * (size_t)P);
-    p.sig = a16(p.ublob + 8 * (size_t)umax);
-    p.selsig = a16(p.sig + 4 * (size_t)LW * E);
-    const size_t base = a16(p.selsig + 4 * (size_t)LW * 32);
-    p.vq = base;
-    p.vd = a16(p.vq + (size_t)NT * H);
-    p.isum = a16(p.vd + 4 * (size_t)NT * vd_stride(H / 32));
+    const size_t base = a16(p.ublob + 8 * (size_t)umax);
+    p.xq = base;
+    p.xd = a16(p.xq + (size_t)S * H);
+    p.vq = a16(p.xd + 4 * (size_t)S * vds);
+    p.vd = a16(p.vq + (NT > 1 ? (size_t)NT * H : 0));
+    p.isum = a16(p.vd + (NT > 1 ? 4 * (size_t)NT * vds : 0));
     p.gu = a16(p.isum + 4 * (size_t)LW * NT * ROWS_PER_WAVE * ISUM_PITCH);
     const size_t end1 = a16(p.gu + 4 * (size_t)NT * 64);
-    p.qh = base;
-    p.dh = a16(p.qh + (size_t)mpb * I);
-    p.isum2 = a16(p.dh + 4 * (size_t)mpb * vd_stride(I / 32));
-    p.sdn = a16(p.isum2 + 4 * (size_t)LW * RW2 * mpb * ISUM_PITCH);
-    p.y = a16(p.sdn + 4 * (size_t)umax * ROWS2);
-    const size_t end2 = a16(p.y + 4 * (size_t)slots * ROWS2);
-    p.total = end1 > end2 ? end1 : end2;
+    p.tile = down_tile_plan(base, S, K, E, n_shared, I);
+    p.total = end1 > p.tile.end ? end1 : p.tile.end;
     return p;
 }
 
-template <int BITS, int NT, bool ROUTE, int MAXJ>
+// ONE_PASS: the grid has a workgroup for every gate/up item and every down
+// tile, so each workgroup takes at most one of each (straight-line code,
+// which keeps the register count low enough for 3 workgroups per CU).
+// FAST: one token, and the grid has a workgroup for every gate/up item and
+// every down tile, with the tile's units in a single batch (the host checks
+// the worst case): straight-line code with only the decode path in it, so
+// that the kernel's code stays small in the instruction cache and its
+// register count allows 3 workgroups per CU.  MAXM: router selection width
+// (E <= 64 * MAXM).
+template <int BITS, int NT, bool ROUTE, bool FAST, int MAXM>
 __global__ __launch_bounds__(LT) void k_layer(const FwdArgs a, const LayerArgs l) {
+    static_assert(!FAST || NT == 1, "FAST is the one-token path");
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
     const int S = a.S, K = a.K, E = a.E, H = a.H, I = a.I, P = S * K;
-    const int G = gridDim.x;
+    const int G = gridDim.x, wg = blockIdx.x;
     const LayerPlan L = layer_plan(S, K, E, a.n_shared, NT, H, I);
-    SmemPlan T;
-    T.cnt = L.cnt; T.ustart = L.ustart; T.fill = L.fill; T.uexp = L.uexp;
-    T.uoff = L.uoff; T.pairs = L.pairs; T.misc = L.misc;
+    const int nbx = H / 32, vds = vd_stride(nbx), ntile = I / 32;
+    const int umax = min(P, E) + a.n_shared;
+    const int n_it1_max = umax * ntile;
+    const int n_q8 = (S * nbx + 63) / 64;   // Q8_0(x) wavefront items
     int32_t *idx_l = reinterpret_cast<int32_t *>(smem + L.idx);
     float *w_l = reinterpret_cast<float *>(smem + L.w);
     const uint8_t **ublob = reinterpret_cast<const uint8_t **>(smem + L.ublob);
-    const int *uexp = reinterpret_cast<const int *>(smem + L.uexp);
-    const int *uoff = reinterpret_cast<const int *>(smem + L.uoff);
-    const int *pairs = reinterpret_cast<const int *>(smem + L.pairs);
-    const int nbx = H / 32;
-    const BlobLayout BL = blob_layout(H, I, BITS);
+    const int *uexp = reinterpret_cast<const int *>(smem + L.T.uexp);
+    const int *uoff = reinterpret_cast<const int *>(smem + L.T.uoff);
+    const int *pairs = reinterpret_cast<const int *>(smem + L.T.pairs);
+    const int *misc = reinterpret_cast<const int *>(smem + L.T.misc);
+    int8_t *xq = reinterpret_cast<int8_t *>(smem + L.xq);
+    float *xd = reinterpret_cast<float *>(smem + L.xd);
 
-    // ---- phase R: router logits and Q8_0(x)
-    if (ROUTE) {
-        for (int it = blockIdx.x * LW + wave; it < S * E; it += G * LW) {
-            const int t = it / E, e = it - t * E;
-            bool ok;
-            const float p = logit_wave<MAXJ>(a.x + (size_t)t * H, l.router_w + (size_t)e * H, H, &ok);
-            if (!ok) raise_status(a.status, ST_NONFINITE);
-            if (lane == 0) st_dev(&l.logits[it], p);
+    // ---- phase R, on wavefronts counted from the last workgroup down: the
+    // router logits (with routing computed here), then Q8_0(x) in items of
+    // 64 blocks (one per lane), published with device-scope stores and
+    // counted in sync[2]
+    {
+        const int n_lg = ROUTE ? S * E : 0;
+        for (int i = (G - 1 - wg) * LW + wave; i < n_lg + n_q8; i += G * LW) {
+            if (i < n_lg) {
+                const int t = i / E, e = i - t * E;
+                bool ok;
+                const float p = logit_wave<LMAXJ>(a.x + (size_t)t * H, l.router_w + (size_t)e * H, H, &ok);
+                if (!ok) raise_status(a.status, ST_NONFINITE);
+                if (lane == 0) st_dev(&l.logits[i], p);
+            } else {
+                const int j = (i - n_lg) * 64 + lane;
+                if (j < S * nbx) {
+                    const int t = j / nbx, b = j - t * nbx;
+                    bool ok;
+                    uint32_t w[8];
+                    const float d = q8_0_block_words(a.x + (size_t)t * H + 32 * b, w, &ok);
+                    if (!ok) raise_status(a.status, ST_NONFINITE);
+                    uint32_t *q = reinterpret_cast<uint32_t *>(l.qx + (size_t)t * H + 32 * b);
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) st_dev(q + k, w[k]);
+                    st_dev(l.dx + (size_t)t * nbx + b, d);
+                }
+                drain();
+                signal(l.sync, l.flags, 2, (uint32_t)n_q8);
+            }
         }
     }
-    for (int j = blockIdx.x * (LT / 32) + (tid >> 5); j < S * nbx; j += G * (LT / 32)) {
-        const int t = j / nbx, b = j - t * nbx;
-        const int h = 32 * b + (tid & 31);
-        const float v = a.x[(size_t)t * H + h];
-        if (!finite_f32(v)) raise_status(a.status, ST_NONFINITE);
-        float dd;
-        const uint32_t c = (uint8_t)q8_0_lane(v, &dd);
-        const uint32_t c1 = __shfl_down(c, 1, 64), c2 = __shfl_down(c, 2, 64), c3 = __shfl_down(c, 3, 64);
-        if ((tid & 3) == 0)
-            st_dev(reinterpret_cast<uint32_t *>(l.qx + (size_t)t * H + h), c | (c1 << 8) | (c2 << 16) | (c3 << 24));
-        if ((tid & 31) == 0) st_dev(l.dx + (size_t)t * nbx + b, dd);
-    }
-
-    // ---- routing: the unit table (given routing: before the barrier)
-    auto make_units = [&](const int32_t *idx, bool validate) {
-        build_units(idx, S, K, E, a.n_shared, smem, T, a.status, validate);
-        const int nu = reinterpret_cast<const int *>(smem + L.misc)[0];
+    // unit blob pointers; with given routing, the unit table now
+    auto fill_blobs = [&]() {
+        const int nu = misc[0];
         for (int u = tid; u < nu; u += LT) {
             const int e = uexp[u];
             ublob[u] = e < 0 ? a.shared : a.blobs[e];
         }
         __syncthreads();
     };
-    if (!ROUTE) make_units(a.idx, blockIdx.x == 0);
-
-    // first gate/up item of this workgroup: rows and their first chunk
-    const int ntile = I / 32;
-    const size_t hrow = (size_t)H * BITS / 8;
-    const int half = wave & 1;
-    const size_t mat = wave < 2 ? BL.gate : BL.up;
-    BlockBits<BITS> cur[ROWS_PER_WAVE];
-    bool primed = false;
-    auto rows1 = [&](int it, uint32_t rowoff[ROWS_PER_WAVE]) {
-        const int i0 = (it % ntile) * 32;
-#pragma unroll
-        for (int j = 0; j < ROWS_PER_WAVE; ++j)
-            rowoff[j] = (uint32_t)(mat + (size_t)(i0 + 16 * half + j) * hrow);
-    };
-    auto prime1 = [&](int n_units) {
-        if ((int)blockIdx.x < n_units * ntile) {
-            const uint8_t *blob = uniform_ptr(ublob[uniform(blockIdx.x / ntile)]);
-            if (blob) {
-                uint32_t rowoff[ROWS_PER_WAVE];
-                rows1(blockIdx.x, rowoff);
-                prime_rows<BITS, ROWS_PER_WAVE>(make_rsrc(blob, (uint32_t)BL.total), rowoff, nbx, cur);
-                primed = true;
-            }
-        }
-    };
+    if (!ROUTE) {
+        build_units(a.idx, S, K, E, a.n_shared, smem, L.T, a.status, wg == 0);
+        fill_blobs();
+    }
     drain();
-    if (!ROUTE) prime1(uniform(reinterpret_cast<const int *>(smem + L.misc)[0]));
-    arrive_wait(&l.sync[0], G, a.status);   // logits and Q8_0(x) complete
+    if (ROUTE) arrive(l.sync, l.flags, 0, G);
 
-    if (ROUTE) {
-        float *sig_s = reinterpret_cast<float *>(smem + L.sig) + wave * E;
-        float *selsig = reinterpret_cast<float *>(smem + L.selsig) + wave * 32;
+    // Q8_0(x) of every token into LDS, once it is published (device-scope
+    // loads; the codes come in 16-byte pieces)
+    auto load_x = [&]() {
+        wait_flag(l.flags, 2, a.status);   // Q8_0(x) published
+        const __amdgpu_buffer_rsrc_t qrs = make_rsrc(l.qx, (uint32_t)((size_t)S * H));
+        for (int q = tid; q < S * H / 16; q += LT)
+            reinterpret_cast<u32x4 *>(xq)[q] = __builtin_amdgcn_raw_buffer_load_b128(qrs, 16 * q, 0, CPOL_SC1);
+        for (int j = tid; j < S * nbx; j += LT) {
+            const int t = j / nbx, b = j - t * nbx;
+            xd[t * vds + b] = ld_dev(l.dx + j);
+        }
+        __syncthreads();
+    };
+    auto route = [&]() {
+        wait_flag(l.flags, 0, a.status);   // every logit published
+        __builtin_amdgcn_s_setprio(2);
         bool ok = true;
         for (int t = wave; t < S; t += LW) {
-            float *lg = l.logits + (size_t)t * E;
+            const float *lg = l.logits + (size_t)t * E;
             auto ld = [&](int e) { return ld_dev(lg + e); };
-            ok = (E <= 256 ? select_wave<4>(ld, l.bias, E, K, l.rsf, l.norm, idx_l + t * K, w_l + t * K, sig_s, selsig)
-                           : select_wave<16>(ld, l.bias, E, K, l.rsf, l.norm, idx_l + t * K, w_l + t * K, sig_s,
-                                             selsig)) && ok;
+            int32_t si;
+            float sw;
+            ok = select_wave<MAXM>(ld, l.bias, E, K, l.rsf, l.norm, &si, &sw) && ok;
+            if (lane < K) {
+                idx_l[t * K + lane] = si;
+                w_l[t * K + lane] = sw;
+            }
         }
-        if (!ok && lane == 0 && blockIdx.x == 0) raise_status(a.status, ST_NONFINITE);
+        if (!ok && lane == 0 && wg == 0) raise_status(a.status, ST_NONFINITE);
         __syncthreads();
-        if (blockIdx.x == 0)
+        if (wg == 0)
             for (int q = tid; q < P; q += LT) {
                 l.idx_out[q] = idx_l[q];
                 l.w_out[q] = w_l[q];
             }
-        make_units(idx_l, false);
-        prime1(uniform(reinterpret_cast<const int *>(smem + L.misc)[0]));
-    }
-    const int n_units = uniform(reinterpret_cast<const int *>(smem + L.misc)[0]);
-    const float *wts = ROUTE ? w_l : a.w;
+        build_units(idx_l, S, K, E, a.n_shared, smem, L.T, a.status, false);
+        fill_blobs();
+        __builtin_amdgcn_s_setprio(0);
+    };
 
-    // ---- phase 1: gate/up items (unit, 32-row tile)
+    // ---- phase 1: gate/up items (unit, 32-row tile); item order puts the
+    // shared expert first, then the routed units in table order
+    const size_t hrow = (size_t)H * BITS / 8;
+    const int half = wave & 1;
+    const BlobLayout BL = blob_layout(H, I, BITS);
+    const size_t mat = wave < 2 ? BL.gate : BL.up;
     int8_t *vq = reinterpret_cast<int8_t *>(smem + L.vq);
     float *vd = reinterpret_cast<float *>(smem + L.vd);
     int32_t *isum_wave = reinterpret_cast<int32_t *>(smem + L.isum) + wave * NT * ROWS_PER_WAVE * ISUM_PITCH;
     float *gu = reinterpret_cast<float *>(smem + L.gu);
-    const int n_it1 = n_units * ntile;
-    const int vds = vd_stride(nbx);
     const int crow = lane & 15, cvec = lane >> 4;
-    const __amdgpu_buffer_rsrc_t qx_rs = make_rsrc(l.qx, (uint32_t)((size_t)S * H));
-    for (int it = blockIdx.x; it < n_it1; it += G) {
-        const int u = uniform(it / ntile);
-        const uint8_t *blob = uniform_ptr(ublob[u]);
+    auto item = [&](int it, bool shared_item) {
+        const int uo = it / ntile, i0 = (it - uo * ntile) * 32;
+        const int ut = shared_item ? -1 : uo - a.n_shared;   // routed unit (table order)
+        const uint8_t *blob = uniform_ptr(shared_item ? a.shared : ublob[ut]);
         if (!blob) {
+            // a call with a non-resident expert fails as a whole (status word)
             if (tid == 0) raise_status(a.status, ST_NOTRESIDENT);
-            primed = false;
-            continue;
+            return false;
         }
+        const int p0 = shared_item ? 0 : uniform(uoff[ut]);
+        const int np = shared_item ? S : uniform(uoff[ut + 1]) - p0;
+        auto pair_at = [&](int i) { return shared_item ? P + i : pairs[p0 + i]; };
         const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(blob, (uint32_t)BL.total);
         uint32_t rowoff[ROWS_PER_WAVE];
-        rows1(it, rowoff);
+#pragma unroll
+        for (int j = 0; j < ROWS_PER_WAVE; ++j) rowoff[j] = (uint32_t)(mat + (size_t)(i0 + 16 * half + j) * hrow);
         const float *scale = reinterpret_cast<const float *>(blob + (wave < 2 ? BL.s_gate : BL.s_up));
-        const int i0 = (it % ntile) * 32;
-        const int p0 = uniform(uoff[u]), np = uniform(uoff[u + 1]) - p0;
         for (int g0 = 0; g0 < np; g0 += NT) {
             const int ng = min(NT, np - g0);
-            if (!primed) prime_rows<BITS, ROWS_PER_WAVE>(rsrc, rowoff, nbx, cur);
-            primed = false;
+            const int8_t *gq = vq;
+            const float *gd = vd;
+            if (NT == 1) {
+                const int v = pair_at(g0);
+                const int t = v < P ? v / K : v - P;
+                gq = xq + (size_t)t * H;
+                gd = xd + t * vds;
+            }
             auto stage = [&]() {
-                for (int itk = 0; itk < ng; ++itk) {
-                    const int v = pairs[p0 + g0 + itk];
-                    const int t = v < P ? v / K : v - P;
-                    u32x4 *dst = reinterpret_cast<u32x4 *>(vq + (size_t)itk * H);
-                    for (int q = tid; q < H / 16; q += LT)
-                        dst[q] = __builtin_amdgcn_raw_buffer_load_b128(qx_rs, (t * H) + 16 * q, 0, CPOL_SC1);
-                    for (int q = tid; q < nbx; q += LT) vd[itk * vds + q] = ld_dev(l.dx + (size_t)t * nbx + q);
+                if (NT > 1) {
+                    // this group's tokens, copied from the per-token Q8_0(x) in LDS
+                    for (int itk = 0; itk < ng; ++itk) {
+                        const int v = pair_at(g0 + itk);
+                        const int t = v < P ? v / K : v - P;
+                        const i32x4 *src = reinterpret_cast<const i32x4 *>(xq + (size_t)t * H);
+                        i32x4 *dst = reinterpret_cast<i32x4 *>(vq + (size_t)itk * H);
+                        for (int q = tid; q < H / 16; q += LT) dst[q] = src[q];
+                        for (int q = tid; q < nbx; q += LT) vd[itk * vds + q] = xd[t * vds + q];
+                    }
+                    __syncthreads();
                 }
-                __syncthreads();
             };
-            const float acc = stream_rows<BITS, NT, ROWS_PER_WAVE>(rsrc, rowoff, nbx, ng, vq, vd, isum_wave, H, stage, cur);
+            BlockBits<BITS> cur[ROWS_PER_WAVE];
+            prime_rows<BITS, ROWS_PER_WAVE>(rsrc, rowoff, nbx, cur);
+            const float acc = stream_rows<BITS, NT, ROWS_PER_WAVE>(rsrc, rowoff, nbx, ng, gq, gd, isum_wave, H, stage, cur);
             if (cvec < ng) gu[cvec * 64 + wave * ROWS_PER_WAVE + crow] = acc * scale[i0 + 16 * half + crow];
             __syncthreads();
-            // SwiGLU and Q8_0(h): half wave (tid >> 5) handles one vector's 32 rows.
+            // SwiGLU and Q8_0(h): half wave (tid >> 5) handles one vector's 32 rows
             const int vv = tid >> 5, i = tid & 31;
             if (vv < ng) {
                 const float h = swiglu_f32(gu[vv * 64 + i], gu[vv * 64 + 32 + i]);
                 float d;
                 const uint32_t c = (uint8_t)q8_0_lane(h, &d);
-                const uint32_t c1 = __shfl_down(c, 1, 64), c2 = __shfl_down(c, 2, 64),
-                               c3 = __shfl_down(c, 3, 64);
-                const int slot = pairs[p0 + g0 + vv];
+                const uint32_t c1 = __shfl_down(c, 1, 64), c2 = __shfl_down(c, 2, 64), c3 = __shfl_down(c, 3, 64);
+                const int slot = pair_at(g0 + vv);
                 if ((i & 3) == 0)
                     st_dev(reinterpret_cast<uint32_t *>(a.qh + (size_t)slot * I + i0 + i),
                            c | (c1 << 8) | (c2 << 16) | (c3 << 24));
@@ -293,139 +326,59 @@ __global__ __launch_bounds__(LT) void k_layer(const FwdArgs a, const LayerArgs l
             }
             __syncthreads();
         }
+        return true;
+    };
+
+    const bool first_shared = a.n_shared && wg < ntile;   // this workgroup's first item is the shared expert's
+    if (FAST) {
+        // at most one item per workgroup; the shared expert's workgroups
+        // stream it before routing, the others route first (one call site
+        // for the item keeps the code small)
+        if (ROUTE && !first_shared) route();
+        if (first_shared || (wg < n_it1_max && wg < uniform(misc[0]) * ntile)) {
+            load_x();
+            item(wg, first_shared);
+        }
+        if (ROUTE && first_shared) route();
+    } else {
+        bool routed = !ROUTE, have_x = false;
+        for (int it = wg; it < n_it1_max; it += G) {
+            const bool shared_item = a.n_shared && it < ntile;
+            if (!shared_item && !routed) {
+                route();
+                routed = true;
+            }
+            if (routed && it >= uniform(misc[0]) * ntile) break;
+            if (!have_x) {
+                load_x();
+                have_x = true;
+            }
+            if (!item(it, shared_item)) break;
+        }
+        if (!routed) route();
     }
 
-    // ---- phase 2: two down rows per wave for every unit, then the combine
-    constexpr int UB = DownBatch<BITS>::UB;
-    const int nbi = I / 32;
-    const int nch2 = (nbi + 63) / 64;
-    const int vds2 = vd_stride(nbi);
-    const size_t irow = (size_t)I * BITS / 8;
-    const int slots = P + S * a.n_shared;
-    const int mpb = slots < MAXPB ? slots : MAXPB;
-    const int n_it2 = H / ROWS2;
-    int8_t *qh_l = reinterpret_cast<int8_t *>(smem + L.qh);
-    float *dh_l = reinterpret_cast<float *>(smem + L.dh);
-    int32_t *isum2 = reinterpret_cast<int32_t *>(smem + L.isum2) + wave * RW2 * mpb * ISUM_PITCH;
-    float *sdn = reinterpret_cast<float *>(smem + L.sdn);
-    float *y_l = reinterpret_cast<float *>(smem + L.y);
-    auto batch_end = [&](int u0) {
-        int u1 = u0, npb = 0;
-        while (u1 < n_units && u1 - u0 < UB) {
-            const int np = uoff[u1 + 1] - uoff[u1];
-            if (npb + np > mpb && u1 > u0) break;
-            npb += np;
-            ++u1;
-        }
-        return uniform(u1);
-    };
-    BlockBits<BITS> wv[UB][RW2];
-    auto load_batch = [&](int rt, int u0, int u1, int c) {
-        const int b = c * 64 + lane;
-        const size_t ro = BL.down + (size_t)(rt * ROWS2 + wave * RW2) * irow;
-#pragma unroll
-        for (int ui = 0; ui < UB; ++ui) {
-            if (u0 + ui < u1) {
-                const uint8_t *blob = uniform_ptr(ublob[u0 + ui]);
-                if (blob && b < nbi) {
-#pragma unroll
-                    for (int r = 0; r < RW2; ++r) wv[ui][r] = load_block_ptr<BITS>(blob + ro + r * irow, b);
-                }
-            }
-        }
-    };
-    // down scales of this item's rows for every unit (LDS)
-    auto load_scales = [&](int rt) {
-        for (int q = tid; q < n_units * ROWS2; q += LT) {
-            const int u = q / ROWS2, r = q - u * ROWS2;
-            const uint8_t *blob = ublob[u];
-            sdn[q] = blob ? reinterpret_cast<const float *>(blob + BL.s_down)[rt * ROWS2 + r] : 0.0f;
-        }
-    };
+    // ---- phase 2: down tiles
     drain();
-    bool primed2 = false;
-    if ((int)blockIdx.x < n_it2 && n_units > 0) {
-        load_batch(blockIdx.x, 0, batch_end(0), 0);
-        primed2 = true;
+    const int n_units = uniform(misc[0]);
+    const int n_tiles = H / DR_ROWS;
+    const float *wts = ROUTE ? w_l : a.w;
+    if (FAST) {
+        // the tile's weights are issued before the barrier
+        DownTile<BITS, true, true> tile(a, smem, L.tile, uoff, pairs, ublob, wts, n_units, wg);
+        if (wg < n_tiles) tile.issue(0, n_units, 0);
+        arrive(l.sync, l.flags, 1, G);
+        wait_flag(l.flags, 1, a.status);   // every Q8_0(h) published
+        if (wg < n_tiles) tile.run(true);
+    } else {
+        arrive(l.sync, l.flags, 1, G);
+        wait_flag(l.flags, 1, a.status);
+        for (int rt = wg; rt < n_tiles; rt += G) {
+            DownTile<BITS, NT == 1, true> tile(a, smem, L.tile, uoff, pairs, ublob, wts, n_units, rt);
+            tile.run(false);
+        }
     }
-    arrive_wait(&l.sync[1], G, a.status);   // Q8_0(h) complete
-    const __amdgpu_buffer_rsrc_t qh_rs = make_rsrc(a.qh, (uint32_t)((size_t)slots * I));
-    auto stage_pairs = [&](int pbase, int npb) {
-        for (int pb = 0; pb < npb; ++pb) {
-            const int sl = pairs[pbase + pb];
-            u32x4 *dst = reinterpret_cast<u32x4 *>(qh_l + (size_t)pb * I);
-            for (int q = tid; q < I / 16; q += LT)
-                dst[q] = __builtin_amdgcn_raw_buffer_load_b128(qh_rs, sl * I + 16 * q, 0, CPOL_SC1);
-            for (int q = tid; q < nbi; q += LT) dh_l[pb * vds2 + q] = ld_dev(a.dh + (size_t)sl * nbi + q);
-        }
-    };
-    const bool one_batch = batch_end(0) == n_units;
-    if (one_batch && (int)blockIdx.x < n_it2) stage_pairs(0, uniform(uoff[n_units]));
-    for (int rt = blockIdx.x; rt < n_it2; rt += G) {
-        const int r0 = rt * ROWS2;
-        load_scales(rt);
-        __syncthreads();
-        for (int u0 = 0; u0 < n_units;) {
-            const int u1 = batch_end(u0);
-            const int pbase = uniform(uoff[u0]);
-            const int npb = uniform(uoff[u1]) - pbase;
-            if (!one_batch) {
-                __syncthreads();
-                stage_pairs(pbase, npb);
-                __syncthreads();
-            }
-            const int cr = lane >> 5, cp = lane & 31;   // chain lane: (row, pair)
-            float acc = 0.0f;
-            for (int c = 0; c < nch2; ++c) {
-                if (!primed2) load_batch(rt, u0, u1, c);
-                primed2 = false;
-                const int b = c * 64 + lane;
-                const bool act = b < nbi;
-#pragma unroll
-                for (int ui = 0; ui < UB; ++ui) {
-                    if (u0 + ui < u1) {
-                        const bool live = ublob[u0 + ui] != nullptr;
-                        const int q0 = uniform(uoff[u0 + ui]), q1 = uniform(uoff[u0 + ui + 1]);
-                        for (int q = q0; q < q1; ++q) {
-                            int32_t av[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-                            if (act) load_act(qh_l + (size_t)(q - pbase) * I, b, av);
-#pragma unroll
-                            for (int r = 0; r < RW2; ++r)
-                                isum2[(r * mpb + (q - pbase)) * ISUM_PITCH + lane] =
-                                    (act && live) ? block_dot(wv[ui][r], av) : 0;
-                        }
-                    }
-                }
-                wave_lds_sync();
-                if (cp < npb)
-                    acc = chain_chunk(acc, isum2 + (cr * mpb + cp) * ISUM_PITCH, dh_l + cp * vds2 + c * 64,
-                                      min(64, nbi - c * 64));
-                wave_lds_sync();
-            }
-            if (cp < npb) {
-                int ub = u0;   // the pair's unit: the last one whose first pair is at or before it
-                while (ub + 1 < u1 && uoff[ub + 1] <= pbase + cp) ++ub;
-                const int slot = pairs[pbase + cp];
-                const int rl = wave * RW2 + cr;
-                y_l[slot * ROWS2 + rl] = ublob[ub] ? acc * sdn[ub * ROWS2 + rl] : 0.0f;
-            }
-            u0 = u1;
-        }
-        __syncthreads();
-        for (int q = tid; q < S * ROWS2; q += LT) {
-            const int t = q / ROWS2, rl = q - t * ROWS2;
-            float acc = 0.0f;
-            for (int k = 0; k < K; ++k) {
-                const float wk = wts[t * K + k];
-                if (!ROUTE && rt == 0 && rl == 0 && !finite_f32(wk)) raise_status(a.status, ST_NONFINITE);
-                acc = __builtin_fmaf(wk, y_l[(t * K + k) * ROWS2 + rl], acc);
-            }
-            if (a.n_shared) acc = acc + y_l[(P + t) * ROWS2 + rl];
-            a.out[(size_t)t * H + r0 + rl] = acc;
-        }
-        __syncthreads();
-    }
-    grid_exit(l.sync, 2, G);
+    grid_exit(l.sync, l.flags, 3, G);
 }
 
 // ---- launchers ----------------------------------------------------------
@@ -468,25 +421,53 @@ size_t layer_smem(int S, int H, int I, int E, int K, int n_shared) {
     return layer_plan(S, K, E, n_shared, pick_nt_layer(S), H, I).total;
 }
 
-template <int BITS, int NT, bool ROUTE, int MAXJ>
+// Whether the one-token fast instantiation covers a call: every gate/up item
+// and down tile gets its own workgroup, and the down tile's units fit one
+// batch in the worst case.
+static bool layer_fast(const FwdArgs &a, int cap) {
+    const int umax = std::min(a.S * a.K, a.E) + a.n_shared;
+    const int slots = a.S * a.K + a.S * a.n_shared;
+    const int want = std::max(umax * (a.I / 32), a.H / DR_ROWS);
+    return a.S == 1 && want <= cap && a.I <= 2048 && slots <= DR_MAXPB &&
+           slots * (a.I / 16) <= DR_MQ * DR_T && slots * (a.I / 32) <= DR_MD * DR_T;
+}
+
+template <int BITS, int NT, bool ROUTE, bool FAST, int MAXM>
+static hipError_t layer_go(const FwdArgs &a, const LayerArgs &l, size_t smem, int G, hipStream_t st) {
+    const void *kern = reinterpret_cast<const void *>(k_layer<BITS, NT, ROUTE, FAST, MAXM>);
+    const hipError_t e = ensure_dyn_smem(kern, smem);
+    if (e != hipSuccess) return e;
+    return launch(k_layer<BITS, NT, ROUTE, FAST, MAXM>, dim3(G), dim3(LT), smem, st, a, l);
+}
+
+template <int BITS, int NT, bool ROUTE>
 static hipError_t layer_launch(const FwdArgs &a, const LayerArgs &l, hipStream_t st) {
     const size_t smem = layer_plan(a.S, a.K, a.E, a.n_shared, NT, a.H, a.I).total;
-    int cap = 0;
-    hipError_t e = resident_blocks(reinterpret_cast<const void *>(k_layer<BITS, NT, ROUTE, MAXJ>), smem, &cap);
-    if (e != hipSuccess) return e;
     const int umax = std::min(a.S * a.K, a.E) + a.n_shared;
-    const int want = std::max(umax * (a.I / 32), a.H / ROWS2);
-    const int G = std::max(1, std::min(want, cap));
-    return launch(k_layer<BITS, NT, ROUTE, MAXJ>, dim3(G), dim3(LT), smem, st, a, l);
+    const int want = std::max(umax * (a.I / 32), a.H / DR_ROWS);
+    int cap = 0;
+    const auto fits = [](int c) { return std::min(c, FLAG_COPIES); };   // one release flag per workgroup
+    if (NT == 1) {
+        hipError_t e = resident_blocks(reinterpret_cast<const void *>(k_layer<BITS, 1, ROUTE, true, 4>), smem, &cap);
+        if (e != hipSuccess) return e;
+        cap = fits(cap);
+        if (DownRowsBatch<BITS>::UB >= umax && layer_fast(a, cap)) {
+            if (a.E <= 256) return layer_go<BITS, 1, ROUTE, true, 4>(a, l, smem, want, st);
+            return layer_go<BITS, 1, ROUTE, true, 16>(a, l, smem, want, st);
+        }
+    }
+    hipError_t e = resident_blocks(reinterpret_cast<const void *>(k_layer<BITS, NT, ROUTE, false, 16>), smem, &cap);
+    if (e != hipSuccess) return e;
+    cap = fits(cap);
+    return layer_go<BITS, NT, ROUTE, false, 16>(a, l, smem, std::max(1, std::min(want, cap)), st);
 }
 
 template <int BITS, bool ROUTE>
 static hipError_t layer_bits(const FwdArgs &a, const LayerArgs &l, hipStream_t st) {
-    const bool short_rows = a.H <= 24 * 256;
     switch (pick_nt_layer(a.S)) {
-        case 4: return short_rows ? layer_launch<BITS, 4, ROUTE, 24>(a, l, st) : layer_launch<BITS, 4, ROUTE, 16>(a, l, st);
-        case 2: return short_rows ? layer_launch<BITS, 2, ROUTE, 24>(a, l, st) : layer_launch<BITS, 2, ROUTE, 16>(a, l, st);
-        default: return short_rows ? layer_launch<BITS, 1, ROUTE, 24>(a, l, st) : layer_launch<BITS, 1, ROUTE, 16>(a, l, st);
+        case 4: return layer_launch<BITS, 4, ROUTE>(a, l, st);
+        case 2: return layer_launch<BITS, 2, ROUTE>(a, l, st);
+        default: return layer_launch<BITS, 1, ROUTE>(a, l, st);
     }
 }
 

@@ -1,8 +1,11 @@
-// Router kernels for the two-launch path (logits, then selection); the
-// device routines are in router.h.
+// Router kernels: logits and selection as two launches (coli_moe_route), or
+// one launch that also selects and builds the unit table of the call
+// (coli_moe_layer, up to ROUTE_FUSE_MAX tokens).  The device routines are
+// in router.h.
 #include "device_common.h"
 #include "kernels.h"
 #include "router.h"
+#include "stream.h"
 
 namespace coli {
 
@@ -51,13 +54,119 @@ __global__ __launch_bounds__(64) void k_router_select(const float *__restrict__ 
                                                       float *__restrict__ w_out,
                                                       uint32_t *__restrict__ status, int E, int K,
                                                       float rsf, int norm) {
-    __shared__ float sig_s[1024];
-    __shared__ float sel_sig[32];
-    const int t = blockIdx.x;
+    const int t = blockIdx.x, lane = threadIdx.x;
     const float *lg = logits + (size_t)t * E;
-    const bool ok = select_wave<MAXM>([&](int e) { return lg[e]; }, bias, E, K, rsf, norm,
-                                idx_out + (size_t)t * K, w_out + (size_t)t * K, sig_s, sel_sig);
-    if (!ok && threadIdx.x == 0) raise_status(status, ST_NONFINITE);
+    int32_t si;
+    float sw;
+    const bool ok = select_wave<MAXM>([&](int e) { return lg[e]; }, bias, E, K, rsf, norm, &si, &sw);
+    if (lane < K) {
+        idx_out[(size_t)t * K + lane] = si;
+        w_out[(size_t)t * K + lane] = sw;
+    }
+    if (!ok && lane == 0) raise_status(status, ST_NONFINITE);
+}
+
+// The fused router launch.  Grid (E + ceil(H / 2048), S), 64 threads.
+// Workgroup (e < E, t) computes logit (t, e), publishes it with a
+// device-scope store, drains it and counts itself in the token's arrival
+// counter; the workgroup that arrives last selects the token's top-K from
+// the published logits (device-scope loads) and counts the token as done;
+// the last token to be done builds the unit table of the batch in LDS and
+// writes it to the workspace.  Each counter is reset by its last arriver,
+// so the next launch starts from zero.  Workgroups e >= E quantise x.
+template <int MAXJ>
+__global__ __launch_bounds__(64) void k_route_fused(const RouteArgs r) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int e = blockIdx.x, t = blockIdx.y, lane = threadIdx.x;
+    const int E = r.E, K = r.K, S = r.S, H = r.H;
+    if (e >= E) {
+        quant_x_wave(r.x, r.qx, r.dx, r.status, H, t, e - E);
+        return;
+    }
+    bool ok;
+    const float p = logit_wave<MAXJ>(r.x + (size_t)t * H, r.W + (size_t)e * H, H, &ok);
+    if (!ok) raise_status(r.status, ST_NONFINITE);
+    if (lane == 0) st_dev(&r.logits[(size_t)t * E + e], p);
+    drain();
+    uint32_t prev = 0;
+    if (lane == 0) prev = __hip_atomic_fetch_add(&r.sync[t], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (__builtin_amdgcn_readlane((int)prev, 0) != E - 1) return;
+
+    // last logit of token t: select (the blob pointers of the first 256
+    // experts are fetched meanwhile, for the unit table)
+    const uint8_t *bl[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) bl[m] = r.blobs[min(lane + 64 * m, E - 1)];
+    const float *lg = r.logits + (size_t)t * E;
+    auto ld = [&](int q) { return ld_dev(lg + q); };
+    int32_t si;
+    float sw;
+    const bool sok = E <= 256 ? select_wave<4>(ld, r.bias, E, K, r.rsf, r.norm, &si, &sw)
+                              : select_wave<16>(ld, r.bias, E, K, r.rsf, r.norm, &si, &sw);
+    if (!sok && lane == 0) raise_status(r.status, ST_NONFINITE);
+    const int P = S * K;
+    const SmemPlan T = smem_plan(S, K, E, 0, 0);
+    int32_t *idx_l = reinterpret_cast<int32_t *>(smem + T.total);
+    const uint8_t **btab = reinterpret_cast<const uint8_t **>(smem + a16(T.total + 4 * (size_t)P));
+    if (lane == 0) st_dev(&r.sync[t], 0u);
+    if (S == 1) {
+        // one token: its selection is the whole routing; no second count
+        if (lane < K) {
+            r.idx_out[lane] = si;
+            r.w_out[lane] = sw;
+            idx_l[lane] = si;
+        }
+    } else {
+        if (lane < K) {
+            st_dev(&r.idx_out[(size_t)t * K + lane], si);
+            st_dev(&r.w_out[(size_t)t * K + lane], sw);
+        }
+        drain();
+        if (lane == 0)
+            prev = __hip_atomic_fetch_add(&r.sync[ROUTE_FUSE_MAX], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (__builtin_amdgcn_readlane((int)prev, 0) != S - 1) return;
+        // last token selected: the unit table
+        for (int q = lane; q < P; q += 64) idx_l[q] = ld_dev(r.idx_out + q);
+        if (lane == 0) st_dev(&r.sync[ROUTE_FUSE_MAX], 0u);
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+        if (lane + 64 * m < E) btab[lane + 64 * m] = bl[m];
+    __syncthreads();
+    build_units(idx_l, S, K, E, r.n_shared, smem, T, r.status, false);
+    const UnitTable U = unit_table(S, K, E);
+    int32_t *tab = reinterpret_cast<int32_t *>(r.units);
+    const int *misc = reinterpret_cast<const int *>(smem + T.misc);
+    const int *uexp = reinterpret_cast<const int *>(smem + T.uexp);
+    const int *uoff = reinterpret_cast<const int *>(smem + T.uoff);
+    const int *pairs = reinterpret_cast<const int *>(smem + T.pairs);
+    const int n_units = misc[0];
+    if (lane < 4) tab[lane] = lane < 3 ? misc[lane] : 0;
+    for (int q = lane; q < n_units; q += 64) {
+        const int ex = uexp[q];
+        tab[U.uexp + q] = ex;
+        reinterpret_cast<const uint8_t **>(r.units + U.ublob)[q] =
+            ex < 0 ? r.shared : (ex < 256 ? btab[ex] : r.blobs[ex]);
+    }
+    for (int q = lane; q <= n_units; q += 64) tab[U.uoff + q] = uoff[q];
+    for (int q = lane; q < P + S * r.n_shared; q += 64) tab[U.pairs + q] = pairs[q];
+}
+
+size_t route_fused_smem(int S, int K, int E) {
+    return a16(a16(smem_plan(S, K, E, 0, 0).total + 4 * (size_t)S * K) + 8 * (size_t)(E < 256 ? E : 256));
+}
+
+hipError_t launch_route_fused(const RouteArgs &r, hipStream_t st) {
+    const dim3 grid(r.E + (r.H / 32 + 63) / 64, r.S);
+    const size_t smem = route_fused_smem(r.S, r.K, r.E);
+    if (r.H <= 24 * 256) {
+        const hipError_t e = ensure_dyn_smem(reinterpret_cast<const void *>(k_route_fused<24>), smem);
+        if (e != hipSuccess) return e;
+        return launch(k_route_fused<24>, grid, dim3(64), smem, st, r);
+    }
+    const hipError_t e = ensure_dyn_smem(reinterpret_cast<const void *>(k_route_fused<16>), smem);
+    if (e != hipSuccess) return e;
+    return launch(k_route_fused<16>, grid, dim3(64), smem, st, r);
 }
 
 // Q8_0 of the hidden states alone.  Grid: (ceil(H / 2048), S), 64 threads.

@@ -52,12 +52,6 @@ __device__ __forceinline__ float logit_wave(const float *__restrict__ xrow,
 }
 
 // ---- wavefront reductions through DPP (result uniform across the wave) ----
-// LDS writes of this wave made visible to its own later reads.
-__device__ __forceinline__ void wave_and_lds_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-}
 
 template <int CTRL, int ROWS = 0xF>
 __device__ __forceinline__ int dpp(int v) {
@@ -85,24 +79,21 @@ __device__ __forceinline__ int wave_min_i32(int v) {
     return __builtin_amdgcn_readlane(v, 63);
 }
 
-// Selection for one token by one wavefront (sig_s: LDS scratch of E floats,
-// sel_sig: LDS scratch of K floats).  Lane l owns experts l, l+64, ...;
-// sig = sigmoid(logit), score = sig + bias.  K rounds pick the experts in
-// rank order under the total order (score desc, id asc): the wavefront
+// Selection for one token by one wavefront.  Lane l owns experts l, l+64,
+// ...; sig = sigmoid(logit), score = sig + bias.  K rounds pick the experts
+// in rank order under the total order (score desc, id asc): the wavefront
 // maximum of the lanes' best remaining scores, then the smallest id holding
-// it.  Gate weights: (sig_k / ((sig_0 + sig_1) + ...)) * rsf, or sig_k * rsf
-// without renormalisation.  load_logit(e) returns the token's logit e.
-// E <= 64 * MAXM, K <= 32.  Returns false on a non-finite input or zero
-// weights.
+// it (a ballot settles the usual single-holder case; exact ties take a
+// minimum reduction).  Gate weights: (sig_k / ((sig_0 + sig_1) + ...)) * rsf,
+// or sig_k * rsf without renormalisation.  Lane k < K receives the k-th pick
+// in *idx / *w.  load_logit(e) returns the token's logit e.  E <= 64 * MAXM,
+// K <= 32.  Returns false on a non-finite input or zero weights.
 template <int MAXM, typename LoadLogit>
 __device__ __forceinline__ bool select_wave(LoadLogit load_logit, const float *__restrict__ bias,
-                                            int E, int K, float rsf, int norm,
-                                            int32_t *__restrict__ idx_out,
-                                            float *__restrict__ w_out, float *sig_s,
-                                            float *sel_sig) {
+                                            int E, int K, float rsf, int norm, int32_t *idx, float *w) {
     const int lane = threadIdx.x & 63;
     const int mcount = (E + 63) / 64;
-    float score[MAXM], lv[MAXM], bv[MAXM];
+    float score[MAXM], sig[MAXM], lv[MAXM], bv[MAXM];
     uint32_t taken = 0;
     bool ok = true;
     // all loads first (in flight together), then the arithmetic
@@ -118,45 +109,51 @@ __device__ __forceinline__ bool select_wave(LoadLogit load_logit, const float *_
     for (int m = 0; m < MAXM; ++m) {
         const int e = lane + 64 * m;
         score[m] = -__builtin_inff();
+        sig[m] = 0.0f;
         if (m < mcount && e < E) {
             ok = ok && finite_f32(lv[m]) && finite_f32(bv[m]);
-            const float sg = sigmoid_f32(lv[m]);
-            sig_s[e] = sg;
-            score[m] = sg + bv[m];
+            sig[m] = sigmoid_f32(lv[m]);
+            score[m] = sig[m] + bv[m];
         }
     }
-    wave_and_lds_sync();
+    int32_t my_idx = 0;
+    float my_sig = 0.0f;
     for (int k = 0; k < K; ++k) {
-        float bs = -__builtin_inff();
+        float bs = -__builtin_inff(), bsig = 0.0f;
         int be = 0x7fffffff;
 #pragma unroll
         for (int m = 0; m < MAXM; ++m) {
             if (m < mcount && !((taken >> m) & 1u) && score[m] > bs) {
                 bs = score[m];
+                bsig = sig[m];
                 be = lane + 64 * m;
             }
         }
         const float M = wave_max_f32(bs);
-        int sel = wave_min_i32(bs == M ? be : 0x7fffffff);
+        const uint64_t hit = __builtin_amdgcn_ballot_w64(bs == M);
+        int sel;
+        if (__builtin_popcountll(hit) == 1)
+            sel = __builtin_amdgcn_readlane(be, (int)__builtin_ctzll(hit));
+        else
+            sel = wave_min_i32(bs == M ? be : 0x7fffffff);
         if (sel >= E) sel = k;  // only reachable with NaN scores, flagged below
+        const float s = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bsig), sel & 63));
         if ((sel & 63) == lane) taken |= 1u << (sel >> 6);
-        if (lane == 0) {
-            idx_out[k] = sel;
-            sel_sig[k] = sig_s[sel];
+        if (lane == k) {
+            my_idx = sel;
+            my_sig = s;
         }
     }
-    wave_and_lds_sync();
     bool wok = true;
-    if (lane == 0) {
-        if (norm) {
-            float denom = sel_sig[0];
-            for (int k = 1; k < K; ++k) denom = denom + sel_sig[k];
-            wok = denom > 0.0f && finite_f32(denom);
-            for (int k = 0; k < K; ++k) w_out[k] = (sel_sig[k] / denom) * rsf;
-        } else {
-            for (int k = 0; k < K; ++k) w_out[k] = sel_sig[k] * rsf;
-        }
+    float denom = 1.0f;
+    if (norm) {
+        denom = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_sig), 0));
+        for (int k = 1; k < K; ++k)
+            denom = denom + __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_sig), k));
+        wok = denom > 0.0f && finite_f32(denom);
     }
+    *idx = my_idx;
+    *w = norm ? (my_sig / denom) * rsf : my_sig * rsf;
     return __builtin_amdgcn_readfirstlane((int)(ok && wok)) != 0;
 }
 

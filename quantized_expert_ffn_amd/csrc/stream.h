@@ -162,6 +162,13 @@ __device__ __forceinline__ void stage_store(const T (&v)[MW], int round, int n, 
     for (int k = 0; k < MW; ++k)
         if (base + k * nthr < n) *dst(base + k * nthr) = v[k];
 }
+// As stage_load, with src(i) returning the word itself.
+template <int MW, typename T, typename Src>
+__device__ __forceinline__ void stage_fetch(T (&v)[MW], int round, int n, Src src) {
+    const int nthr = blockDim.x, base = round * MW * nthr + (int)threadIdx.x;
+#pragma unroll
+    for (int k = 0; k < MW; ++k) v[k] = src(min(base + k * nthr, n - 1));
+}
 __device__ __forceinline__ int stage_rounds(int n, int per_round) { return (n + per_round - 1) / per_round; }
 
 // Direct global-to-LDS loads (no registers): lane l of the wavefront reads
@@ -178,6 +185,12 @@ __device__ __forceinline__ void lds_dma4(const void *src, void *lds_wave) {
                                      (__attribute__((address_space(3))) void *)lds_wave, 4, 0, 0);
 }
 __host__ __device__ inline int round_up(int v, int m) { return (v + m - 1) / m * m; }
+
+// i / d by a multiply-high for 0 <= i < 2^16, 1 <= d < 2^16: with
+// m = floor(2^32 / d) + 1 (2^32 / d when d is a power of two),
+// (i * m) >> 32 == floor(i / d); d = 1 is kept as m = 0.
+__device__ __forceinline__ uint32_t fast_div_magic(int d) { return d == 1 ? 0u : 0xFFFFFFFFu / (uint32_t)d + 1u; }
+__device__ __forceinline__ int fast_div(int i, uint32_t m) { return m ? (int)__umulhi((uint32_t)i, m) : i; }
 
 // Waits until at most N of this thread's vector-memory operations are
 // outstanding (they complete in issue order); gfx9 s_waitcnt encoding, with
