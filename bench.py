@@ -75,7 +75,7 @@ def main():
         print(json.dumps({"copy_calibration_bytes": n, "copies": 10}), flush=True)
         return
 
-    from quantized_expert_ffn_amd import build as hipbuild
+    hipbuild = _hipbuild()
     if not os.path.exists(hipbuild.LIB):
         hipbuild.build()
     import quantized_expert_ffn_amd as q
@@ -238,6 +238,17 @@ def main():
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(args, spec, xs_host, layers, L)
     print(json.dumps(res), flush=True)
+
+
+def _hipbuild():
+    """The library's build module, loaded by path: importing the package
+    itself needs the built library."""
+    import importlib.util
+    path = os.path.join(ROOT, "quantized_expert_ffn_amd", "build.py")
+    spec = importlib.util.spec_from_file_location("coli_moe_hip_build", path)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
 
 
 def counted_traffic(kernel):

@@ -109,8 +109,16 @@ int coli_moe_route(const coli_moe_dims *dims, int32_t n_tokens, const float *x,
  *   shared_blob  device blob, or NULL when n_shared == 0
  *   pending_mask host uint8 [E] or NULL: experts whose blobs are still being
  *                staged; they run after the stream waits for pending_ready
- *                (a hipEvent_t, may be NULL), all others run before it
+ *                (a hipEvent_t, may be NULL), all others run before it;
+ *                batches of 9 or more tokens wait for the event first
  *   out          device f32 [n_tokens, H]; each element written once
+ * Batches of up to 8 tokens run the decode kernels (GEMV-shaped, bound by
+ * HBM bandwidth).  Larger batches run the grouped kernels: one launch builds
+ * the unit table and its tiles of up to 32 (token, expert) pairs of one
+ * expert, then gate/up and down are int8 matrix-core products per (32-row
+ * tile, pair tile) with the exact per-block f32 chains, then the combine.
+ * Their grouping launch holds the pair list in LDS, which limits n_tokens to
+ * about 4400 at top_k = 8 (COLI_EINVAL beyond 160 KiB).
  */
 int coli_moe_forward(const coli_moe_dims *dims, int32_t n_tokens, const float *x,
                      const int32_t *topk_idx, const float *topk_w,
@@ -159,8 +167,8 @@ const char *coli_moe_last_error(void);
  * recorded events and returns the accumulated milliseconds and launch count
  * of one kernel kind (0 router logits, 1 router select, 2 gate/up, 3 down,
  * 4 combine, 5 persistent layer, 6 persistent forward, 7 Q8_0 of the
- * hidden states), then resets that
- * kind.  For measurement only.
+ * hidden states, 8 grouping of the grouped kernels), then resets that kind.
+ * For measurement only.
  */
 int coli_moe_timing_enable(int32_t enable);
 int coli_moe_timing_read(int32_t kind, double *total_ms, int64_t *launches);
@@ -168,10 +176,11 @@ int coli_moe_timing_read(int32_t kind, double *total_ms, int64_t *launches);
 /* ---- test hooks: the same device functions as the production kernels ---- */
 
 /* Kernel family for subsequent calls in this process: 0 automatic (default:
- * the multi-launch kernels), 1 multi-launch kernels only, 2 persistent
+ * the multi-launch decode kernels up to 8 tokens, the grouped kernels
+ * beyond), 1 multi-launch decode kernels at any batch size, 2 persistent
  * (single-launch) kernels — a forced persistent kernel fails with
  * COLI_EINVAL where it does not apply (pending experts, more than 8 tokens,
- * a shape beyond 160 KiB of LDS). */
+ * a shape beyond 160 KiB of LDS) — 3 grouped kernels at any batch size. */
 int coli_moe_debug_force_path(int32_t path);
 
 /* Unpacks n_rows packed rows of `cols` codes (device src, row stride
@@ -192,6 +201,12 @@ int coli_moe_debug_logits(const coli_moe_dims *dims, int32_t n_tokens, const flo
 /* The device exponential used by the router and SwiGLU, element-wise on
  * device f32 arrays of n elements. */
 int coli_moe_debug_expf(int64_t n, const float *x, float *y, void *stream);
+
+/* One v_mfma_i32_32x32x32_i8 on raw lane registers: lane l (of 64) takes
+ * its A and B registers from bytes 16 l .. 16 l + 15 of device a and b and
+ * writes its 16 int32 result registers to device c[16 l .. 16 l + 15] (the
+ * lane layout of the prefill kernels is checked against a host matmul). */
+int coli_moe_debug_mfma_i8(const int8_t *a, const int8_t *b, int32_t *c, void *stream);
 
 /* Q8_0 of device f32 v [n_rows, cols] into device int8 q and f32 d
  * [n_rows, cols/32], with the device quantiser the kernels use. */

@@ -28,12 +28,12 @@ EXPORTS = (
     "coli_moe_stage_experts", "coli_moe_status", "coli_moe_last_error", "coli_moe_timing_enable",
     "coli_moe_timing_read", "coli_moe_debug_unpack", "coli_moe_debug_block_dots",
     "coli_moe_debug_logits", "coli_moe_debug_expf", "coli_moe_debug_q8_0",
-    "coli_moe_debug_force_path", "coli_moe_layer",
+    "coli_moe_debug_force_path", "coli_moe_layer", "coli_moe_debug_mfma_i8",
 )
 
 KIND_ROUTER_LOGITS, KIND_ROUTER_SELECT, KIND_GATEUP, KIND_DOWN, KIND_COMBINE = 0, 1, 2, 3, 4
-KIND_LAYER, KIND_FORWARD_PERSISTENT, KIND_QUANT_X = 5, 6, 7
-PATH_AUTO, PATH_MULTI, PATH_PERSISTENT = 0, 1, 2
+KIND_LAYER, KIND_FORWARD_PERSISTENT, KIND_QUANT_X, KIND_GROUP = 5, 6, 7, 8
+PATH_AUTO, PATH_MULTI, PATH_PERSISTENT, PATH_GROUPED = 0, 1, 2, 3
 
 
 class coli_moe_dims(ctypes.Structure):
@@ -72,6 +72,7 @@ _sigs = {
     "coli_moe_debug_q8_0": (ctypes.c_int, [_I32, _I32, _P, _P, _P, _P]),
     "coli_moe_debug_force_path": (ctypes.c_int, [_I32]),
     "coli_moe_layer": (ctypes.c_int, [_D, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "coli_moe_debug_mfma_i8": (ctypes.c_int, [_P, _P, _P, _P]),
 }
 for _name, (_res, _args) in _sigs.items():
     _f = getattr(_lib, _name)
@@ -254,3 +255,12 @@ def coli_moe_debug_q8_0(v, q, d, stream=None):
 
 def coli_moe_debug_force_path(path: int) -> None:
     _check(_lib.coli_moe_debug_force_path(int(path)), "coli_moe_debug_force_path")
+
+
+def coli_moe_debug_mfma_i8(a, b, c, stream=None):
+    """a, b: device int8 [64, 16] raw lane registers; c: device int32 [64, 16]."""
+    import torch
+    if a.numel() != 1024 or b.numel() != 1024 or c.numel() != 1024:
+        raise ValueError("a, b and c hold 64 lanes x 16 registers")
+    _check(_lib.coli_moe_debug_mfma_i8(_dev(a, torch.int8, "a"), _dev(b, torch.int8, "b"),
+                                       _dev(c, torch.int32, "c"), _stream(stream)), "coli_moe_debug_mfma_i8")

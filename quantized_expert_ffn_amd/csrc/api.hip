@@ -87,8 +87,21 @@ hipEvent_t take_event() {
     return e;
 }
 
-// 0: automatic, 1: multi-launch kernels only, 2: persistent kernels only.
+// 0: automatic, 1: multi-launch decode kernels at any batch size,
+// 2: persistent kernels only, 3: grouped (matrix-core) kernels at any batch
+// size.
 int g_force_path = 0;
+
+// Batches of more than GROUPED_MIN_S - 1 tokens take the grouped kernels.
+constexpr int GROUPED_MIN_S = 9;
+
+bool use_grouped(int S) { return g_force_path == 3 || (g_force_path == 0 && S >= GROUPED_MIN_S); }
+
+// LDS of the kernels a forward of S tokens launches.
+size_t forward_lds(const coli_moe_dims *d, int S) {
+    if (use_grouped(S)) return coli::pf_group_smem(S, d->top_k, d->n_experts);
+    return coli::forward_smem_max(S, d->hidden, d->inter, d->n_experts, d->top_k, d->n_shared);
+}
 
 // The persistent kernel takes small batches whose experts are all resident.
 bool persistent_fits(const coli_moe_dims *d, int S, bool pending) {
@@ -157,6 +170,7 @@ FwdArgs fwd_args(const coli_moe_dims *d, int S, const float *x, const int32_t *i
     a.qh = reinterpret_cast<int8_t *>(w8 + L.qh);
     a.dh = reinterpret_cast<float *>(w8 + L.dh);
     a.Y = reinterpret_cast<float *>(w8 + L.Y);
+    a.tiles = reinterpret_cast<int32_t *>(w8 + L.tiles);
     a.out = out;
     a.status = reinterpret_cast<uint32_t *>(w8 + L.status);
     a.S = S;
@@ -175,12 +189,28 @@ int route_launches(const coli_moe_dims *d, int S, const float *x, const float *r
                    const WsLayout &L, bool quant_x, bool select, hipStream_t st) {
     uint32_t *status = reinterpret_cast<uint32_t *>(w8 + L.status);
     float *logits = reinterpret_cast<float *>(w8 + L.logits);
-    timing_before(KK_ROUTER_LOGITS, st);
-    hipError_t e = launch_router_logits(x, router_w, logits, status, S, d->hidden, d->n_experts,
-                                        quant_x ? reinterpret_cast<int8_t *>(w8 + L.qx) : nullptr,
-                                        quant_x ? reinterpret_cast<float *>(w8 + L.dx) : nullptr, st);
-    timing_after(KK_ROUTER_LOGITS, st);
-    if (e != hipSuccess) return hip_fail(e, "router logits launch");
+    hipError_t e;
+    if (S > ROUTE_FUSE_MAX) {
+        // many tokens: a wavefront per 8 tokens x 8 experts, Q8_0(x) apart
+        timing_before(KK_ROUTER_LOGITS, st);
+        e = launch_logits_tiled(x, router_w, logits, status, S, d->hidden, d->n_experts, st);
+        timing_after(KK_ROUTER_LOGITS, st);
+        if (e != hipSuccess) return hip_fail(e, "router logits launch");
+        if (quant_x) {
+            timing_before(KK_QUANT_X, st);
+            e = launch_quant_x(x, reinterpret_cast<int8_t *>(w8 + L.qx), reinterpret_cast<float *>(w8 + L.dx),
+                               status, S, d->hidden, st);
+            timing_after(KK_QUANT_X, st);
+            if (e != hipSuccess) return hip_fail(e, "Q8_0(x) launch");
+        }
+    } else {
+        timing_before(KK_ROUTER_LOGITS, st);
+        e = launch_router_logits(x, router_w, logits, status, S, d->hidden, d->n_experts,
+                                 quant_x ? reinterpret_cast<int8_t *>(w8 + L.qx) : nullptr,
+                                 quant_x ? reinterpret_cast<float *>(w8 + L.dx) : nullptr, st);
+        timing_after(KK_ROUTER_LOGITS, st);
+        if (e != hipSuccess) return hip_fail(e, "router logits launch");
+    }
     if (!select) return COLI_OK;
     timing_before(KK_ROUTER_SELECT, st);
     e = launch_router_select(logits, router_bias, topk_idx, topk_w, status, S, d->n_experts, d->top_k,
@@ -193,13 +223,40 @@ int route_launches(const coli_moe_dims *d, int S, const float *x, const float *r
 // The multi-launch forward: [Q8_0(x)], gate/up (resident experts first when
 // some are pending, then the pending ones after pending_ready), down, combine.
 int forward_launches(FwdArgs &a, int bits, bool any_pending, void *pending_ready, bool qx_ready,
-                     hipStream_t st) {
+                     uint8_t *units_ws, hipStream_t st) {
     hipError_t e;
     if (!qx_ready) {
         timing_before(KK_QUANT_X, st);
         e = launch_quant_x(a.x, const_cast<int8_t *>(a.qx), const_cast<float *>(a.dx), a.status, a.S, a.H, st);
         timing_after(KK_QUANT_X, st);
         if (e != hipSuccess) return hip_fail(e, "Q8_0(x) launch");
+    }
+    if (use_grouped(a.S)) {
+        // grouped kernels: the unit table and tiles, then gate/up and down as
+        // int8 matrix-core products per (rows, tile), then the combine.  They
+        // do not split resident from pending experts: all wait for the copies.
+        if (any_pending && pending_ready) {
+            e = hipStreamWaitEvent(st, static_cast<hipEvent_t>(pending_ready), 0);
+            if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+        }
+        a.units = units_ws;
+        timing_before(KK_GROUP, st);
+        e = launch_group(a.idx, a.S, a.K, a.E, a.n_shared, units_ws, a.tiles, a.status, st);
+        timing_after(KK_GROUP, st);
+        if (e != hipSuccess) return hip_fail(e, "grouping launch");
+        timing_before(KK_GATEUP, st);
+        e = launch_pf_gateup(a, a.tiles, bits, st);
+        timing_after(KK_GATEUP, st);
+        if (e != hipSuccess) return hip_fail(e, "gate/up launch");
+        timing_before(KK_DOWN, st);
+        e = launch_pf_down(a, a.tiles, bits, st);
+        timing_after(KK_DOWN, st);
+        if (e != hipSuccess) return hip_fail(e, "down launch");
+        timing_before(KK_COMBINE, st);
+        e = launch_combine(a, st);
+        timing_after(KK_COMBINE, st);
+        if (e != hipSuccess) return hip_fail(e, "combine launch");
+        return COLI_OK;
     }
     if (any_pending) {
         a.pend_mode = 1;  // resident experts first
@@ -283,7 +340,7 @@ int coli_moe_forward(const coli_moe_dims *d, int32_t S, const float *x, const in
     const WsLayout L = ws_layout(d->hidden, d->inter, d->n_experts, d->top_k, S);
     if (ws_bytes < L.total)
         return fail(COLI_EWORKSPACE, "workspace %zu bytes < %zu needed for %d tokens", ws_bytes, L.total, S);
-    const size_t smem = forward_smem_max(S, d->hidden, d->inter, d->n_experts, d->top_k, d->n_shared);
+    const size_t smem = forward_lds(d, S);
     if (smem > 160 * 1024)
         return fail(COLI_EINVAL, "shape needs %zu bytes of LDS per workgroup (> 160 KiB)", smem);
     if ((rc = check_device())) return rc;
@@ -315,7 +372,7 @@ int coli_moe_forward(const coli_moe_dims *d, int32_t S, const float *x, const in
         if (e != hipSuccess) return hip_fail(e, "forward launch");
         return COLI_OK;
     }
-    return forward_launches(a, d->wbits, any_pending, pending_ready, false, st);
+    return forward_launches(a, d->wbits, any_pending, pending_ready, false, w8 + L.units, st);
 }
 
 int coli_moe_layer(const coli_moe_dims *d, int32_t S, const float *x, const float *router_w,
@@ -339,12 +396,12 @@ int coli_moe_layer(const coli_moe_dims *d, int32_t S, const float *x, const floa
     uint8_t *w8 = static_cast<uint8_t *>(ws);
     FwdArgs a = fwd_args(d, S, x, topk_idx, topk_w, expert_blobs, shared_blob, out, w8, L);
     if (!use_persistent(d, S, false)) {
-        const size_t smem = forward_smem_max(S, d->hidden, d->inter, d->n_experts, d->top_k, d->n_shared);
+        const size_t smem = forward_lds(d, S);
         if (smem > 160 * 1024)
             return fail(COLI_EINVAL, "shape needs %zu bytes of LDS per workgroup (> 160 KiB)", smem);
         // up to ROUTE_FUSE_MAX tokens: one router launch also selects the
         // routing and writes the call's unit table, which the expert kernels read
-        if (S <= ROUTE_FUSE_MAX && route_fused_smem(S, d->top_k, d->n_experts) <= 64 * 1024) {
+        if (S <= ROUTE_FUSE_MAX && !use_grouped(S) && route_fused_smem(S, d->top_k, d->n_experts) <= 64 * 1024) {
             RouteArgs r;
             std::memset(&r, 0, sizeof r);
             r.x = x;
@@ -372,11 +429,11 @@ int coli_moe_layer(const coli_moe_dims *d, int32_t S, const float *x, const floa
             timing_after(KK_ROUTER_LOGITS, st);
             if (e != hipSuccess) return hip_fail(e, "router launch");
             a.units = w8 + L.units;
-            return forward_launches(a, d->wbits, false, nullptr, true, st);
+            return forward_launches(a, d->wbits, false, nullptr, true, w8 + L.units, st);
         }
         rc = route_launches(d, S, x, router_w, router_bias, topk_idx, topk_w, w8, L, true, true, st);
         if (rc) return rc;
-        return forward_launches(a, d->wbits, false, nullptr, true, st);
+        return forward_launches(a, d->wbits, false, nullptr, true, w8 + L.units, st);
     }
     LayerArgs l;
     std::memset(&l, 0, sizeof l);
@@ -463,7 +520,7 @@ int coli_moe_timing_read(int32_t kind, double *total_ms, int64_t *launches) {
 }
 
 int coli_moe_debug_force_path(int32_t path) {
-    if (path < 0 || path > 2) return fail(COLI_EINVAL, "path must be 0, 1 or 2");
+    if (path < 0 || path > 3) return fail(COLI_EINVAL, "path must be 0, 1, 2 or 3");
     g_force_path = path;
     return COLI_OK;
 }
@@ -521,6 +578,14 @@ int coli_moe_debug_q8_0(int32_t n_rows, int32_t cols, const float *v, int8_t *q,
     if (rc) return rc;
     hipError_t e = launch_debug_q8_0(n_rows, cols, v, q, d, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? COLI_OK : hip_fail(e, "debug_q8_0 launch");
+}
+
+int coli_moe_debug_mfma_i8(const int8_t *a, const int8_t *b, int32_t *c, void *stream) {
+    if (!a || !b || !c) return fail(COLI_EINVAL, "debug_mfma_i8: NULL pointer argument");
+    int rc = check_device();
+    if (rc) return rc;
+    hipError_t e = launch_debug_mfma_i8(a, b, c, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? COLI_OK : hip_fail(e, "debug_mfma_i8 launch");
 }
 
 }  // extern "C"

@@ -3,6 +3,7 @@
 // so their exact integer and binary32 results can be compared element by
 // element with the CPU oracle.
 #include "device_common.h"
+#include "mfma.h"
 #include "kernels.h"
 
 namespace coli {
@@ -87,6 +88,24 @@ hipError_t launch_debug_block_dots(int bits, int rows, int cols, const void *src
 hipError_t launch_debug_expf(int64_t n, const float *x, float *y, hipStream_t st) {
     const int64_t blocks = (n + 255) / 256;
     hipLaunchKernelGGL(k_debug_expf, dim3((unsigned)blocks), dim3(256), 0, st, x, y, n);
+    return hipGetLastError();
+}
+
+// One int8 MFMA on raw lane registers: lane l's A and B registers are
+// bytes 16 l .. 16 l + 15 of a and b; its 16 result registers go to
+// c[16 l .. 16 l + 15].
+__global__ __launch_bounds__(64) void k_debug_mfma_i8(const int8_t *__restrict__ a, const int8_t *__restrict__ b,
+                                                       int32_t *__restrict__ c) {
+    const int l = threadIdx.x;
+    const i32x4 av = reinterpret_cast<const i32x4 *>(a)[l];
+    const i32x4 bv = reinterpret_cast<const i32x4 *>(b)[l];
+    const i32x16 cv = mfma_i8_32x32x32(av, bv);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) c[16 * l + r] = cv[r];
+}
+
+hipError_t launch_debug_mfma_i8(const int8_t *a, const int8_t *b, int32_t *c, hipStream_t st) {
+    hipLaunchKernelGGL(k_debug_mfma_i8, dim3(1), dim3(64), 0, st, a, b, c);
     return hipGetLastError();
 }
 

@@ -12,8 +12,18 @@ namespace coli {
 // Workspace carve-up for a call with S tokens.  The status word sits at a
 // fixed offset (it persists between calls); the rest is per call.
 struct WsLayout {
-    size_t status, flags, logits, units, qx, dx, qh, dh, Y, total;
+    size_t status, flags, logits, units, tiles, qx, dx, qh, dh, Y, total;
 };
+
+// Tiles of the batch-union kernels for large batches: up to PF_TOK pairs of
+// one unit.  A unit of n pairs makes ceil(n / PF_TOK) tiles, so a call makes
+// at most floor(pairs / PF_TOK) + units of them.
+constexpr int PF_TOK = 32;
+__host__ __device__ inline int pf_tile_bound(int S, int K, int E, int n_shared) {
+    const int P = S * K;
+    const int umax = (P < E ? P : E) + n_shared;
+    return (P + S * n_shared) / PF_TOK + umax;
+}
 
 // Release flags of the persistent kernel's barriers: one per workgroup
 // (FLAG_COPIES of them, FLAG_STRIDE bytes apart), so that every waiting
@@ -61,7 +71,8 @@ inline WsLayout ws_layout(int H, int I, int E, int K, int S) {
     L.flags = 256;
     L.logits = L.flags + (size_t)N_FLAGS * FLAG_COPIES * FLAG_STRIDE;
     L.units = al256h(L.logits + 4 * (size_t)S * (size_t)E);
-    L.qx = al256h(L.units + unit_table(S, K, E).total);
+    L.tiles = al256h(L.units + unit_table(S, K, E).total);
+    L.qx = al256h(L.tiles + 16 * (size_t)(1 + pf_tile_bound(S, K, E, 1)));
     L.dx = al256h(L.qx + (size_t)S * (size_t)H);
     L.qh = al256h(L.dx + 4 * (size_t)S * (size_t)(H / 32));
     L.dh = al256h(L.qh + slots * (size_t)I);
@@ -83,6 +94,7 @@ struct FwdArgs {
     int8_t *qh;                    // [S*(K+1), I]   Q8_0(h) codes per pair slot
     float *dh;                     // [S*(K+1), I/32]
     float *Y;                      // [S*(K+1), H]   expert outputs per pair slot
+    int32_t *tiles;                // tile list of the grouped kernels (workspace)
     float *out;                    // [S, H]
     uint32_t *status;
     int S, H, I, E, K, n_shared;
@@ -129,7 +141,8 @@ enum KernelKind {
     KK_LAYER = 5,
     KK_FORWARD_PERSISTENT = 6,
     KK_QUANT_X = 7,
-    KK_COUNT = 8
+    KK_GROUP = 8,
+    KK_COUNT = 9
 };
 
 // Timing hooks implemented by the API layer.
@@ -183,6 +196,13 @@ size_t layer_smem(int S, int H, int I, int E, int K, int n_shared);
 hipError_t launch_gateup(const FwdArgs &a, int bits, hipStream_t st);
 hipError_t launch_down(const FwdArgs &a, int bits, hipStream_t st);
 hipError_t launch_combine(const FwdArgs &a, hipStream_t st);
+hipError_t launch_logits_tiled(const float *x, const float *W, float *logits, uint32_t *status, int S, int H, int E,
+                               hipStream_t st);
+hipError_t launch_group(const int32_t *idx, int S, int K, int E, int n_shared, uint8_t *units, int32_t *tiles,
+                        uint32_t *status, hipStream_t st);
+size_t pf_group_smem(int S, int K, int E);
+hipError_t launch_pf_gateup(const FwdArgs &a, const int32_t *tiles, int bits, hipStream_t st);
+hipError_t launch_pf_down(const FwdArgs &a, const int32_t *tiles, int bits, hipStream_t st);
 size_t forward_smem_max(int S, int H, int I, int E, int K, int n_shared);
 
 hipError_t launch_debug_unpack(int bits, int rows, int cols, const void *src, int8_t *out,
@@ -190,6 +210,7 @@ hipError_t launch_debug_unpack(int bits, int rows, int cols, const void *src, in
 hipError_t launch_debug_block_dots(int bits, int rows, int cols, const void *src, const int8_t *q,
                                    int32_t *out, hipStream_t st);
 hipError_t launch_debug_expf(int64_t n, const float *x, float *y, hipStream_t st);
+hipError_t launch_debug_mfma_i8(const int8_t *a, const int8_t *b, int32_t *c, hipStream_t st);
 hipError_t launch_debug_q8_0(int rows, int cols, const float *v, int8_t *q, float *d,
                              hipStream_t st);
 

@@ -19,7 +19,11 @@ def _declared():
 
 @pytest.fixture(scope="module")
 def lib():
-    from quantized_expert_ffn_amd import build as b
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "coli_moe_hip_build", os.path.join(ROOT, "quantized_expert_ffn_amd", "build.py"))
+    b = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(b)
     if not os.path.exists(b.LIB):
         b.build()
     return ctypes.CDLL(b.LIB)

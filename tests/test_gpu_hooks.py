@@ -105,3 +105,29 @@ def test_router_logits_bitexact(torch, spec):
     for t in range(4):
         for e in es:
             assert got[t, e].view(np.uint32) == oracle.router_logit(x[t], W[e]).view(np.uint32), (t, e)
+
+
+def test_mfma_i8_lane_layout(torch):
+    """The lane layout the prefill kernels assume for v_mfma_i32_32x32x32_i8
+    reproduces a host int matmul of the matrices it implies."""
+    say("mfma i8 32x32x32 lane layout")
+    rng = np.random.default_rng(11)
+    a_raw = rng.integers(-128, 128, size=(64, 16), dtype=np.int8)
+    b_raw = rng.integers(-128, 128, size=(64, 16), dtype=np.int8)
+    c = torch.zeros((64, 16), dtype=torch.int32, device="cuda")
+    q().coli_moe_debug_mfma_i8(torch.from_numpy(a_raw).cuda(), torch.from_numpy(b_raw).cuda(), c)
+    got = c.cpu().numpy()
+    A = np.zeros((32, 32), np.int64)
+    B = np.zeros((32, 32), np.int64)
+    for lane in range(64):
+        for j in range(16):
+            A[lane % 32, 16 * (lane // 32) + j] = a_raw[lane, j]
+            B[16 * (lane // 32) + j, lane % 32] = b_raw[lane, j]
+    C = A @ B
+    want = np.zeros((64, 16), np.int64)
+    for lane in range(64):
+        for r in range(16):
+            want[lane, r] = C[8 * (r // 4) + 4 * (lane // 32) + r % 4, lane % 32]
+    if not np.array_equal(got, want):
+        np.save("gpurun_out/mfma_raw.npy", np.stack([a_raw.astype(np.int32), b_raw.astype(np.int32), got]))
+    assert np.array_equal(got, want)

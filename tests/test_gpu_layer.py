@@ -21,11 +21,14 @@ def torch():
     return t
 
 
-@pytest.fixture(params=["multi", "persistent"])
+@pytest.fixture(params=["multi", "persistent", "grouped"])
 def path(request, torch):
-    """Runs a test with the multi-launch kernels or the persistent ones."""
+    """Runs a test with the multi-launch decode kernels, the persistent ones
+    or the grouped matrix-core kernels (each forced at every batch size the
+    family takes)."""
     qm = q()
-    qm.coli_moe_debug_force_path(qm.PATH_MULTI if request.param == "multi" else qm.PATH_PERSISTENT)
+    qm.coli_moe_debug_force_path({"multi": qm.PATH_MULTI, "persistent": qm.PATH_PERSISTENT,
+                                  "grouped": qm.PATH_GROUPED}[request.param])
     yield request.param
     qm.coli_moe_debug_force_path(qm.PATH_AUTO)
 
@@ -302,7 +305,7 @@ def test_glm_verify_four_tokens_int8(torch, path):
 
 
 def test_paths_agree_bitwise(torch):
-    """Multi-launch and persistent kernels give the same bits (S = 1..8)."""
+    """Multi-launch, persistent and grouped kernels give the same bits (S = 1..8)."""
     from synth.device import upload_layer
     qm = q()
     spec = synth.TINY
@@ -313,14 +316,15 @@ def test_paths_agree_bitwise(torch):
         dl = upload_layer(d)
         ws = workspace(dims, S)
         outs = []
-        for p in (qm.PATH_MULTI, qm.PATH_PERSISTENT):
+        for p in (qm.PATH_MULTI, qm.PATH_PERSISTENT, qm.PATH_GROUPED):
             qm.coli_moe_debug_force_path(p)
             idx, w = gpu_route(dims, dl, ws)
             outs.append((idx.cpu().numpy(), gpu_forward(dims, dl, idx, w, ws).cpu().numpy()))
             assert status(ws) == 0
         qm.coli_moe_debug_force_path(qm.PATH_AUTO)
-        assert np.array_equal(outs[0][0], outs[1][0])
-        assert np.array_equal(outs[0][1].view(np.uint32), outs[1][1].view(np.uint32))
+        for o in outs[1:]:
+            assert np.array_equal(outs[0][0], o[0])
+            assert np.array_equal(outs[0][1].view(np.uint32), o[1].view(np.uint32))
 
 
 def gpu_layer(torch, dims, dl, ws):
