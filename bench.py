@@ -10,6 +10,12 @@ uses layer s mod 12 and its own hidden state, so expert reads do not hit in
 the 256 MB last-level cache.  Steps are captured in a HIP graph and
 replayed.
 
+--workload prefill times the batch-union prefill instead: the same layer
+shape with all 257 experts resident, a step being one batch of 2048 tokens
+whose routing has a Zipf(1.1) skew over expert popularity (the grouped
+int8 matrix-core kernels); its roofline is the gate/up kernel's int8
+TOPS against the MI355X dense int8 peak.
+
 --copy-calibration MB runs only a device-to-device copy of MB megabytes
 (torch copy_) ten times: the reference for scaling rocprofv3's
 FETCH_SIZE / WRITE_SIZE counters to bytes.
@@ -40,8 +46,10 @@ def log(*a):
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=2400)
-    ap.add_argument("--warmup", type=int, default=240)
+    ap.add_argument("--workload", choices=("decode", "prefill"), default="decode")
+    ap.add_argument("--steps", type=int, default=None, help="timed steps (decode 2400, prefill 200)")
+    ap.add_argument("--warmup", type=int, default=None, help="untimed steps (decode 240, prefill 20)")
+    ap.add_argument("--tokens", type=int, default=2048, help="tokens per prefill step")
     ap.add_argument("--layers", type=int, default=12, help="resident GLM-shaped layers")
     ap.add_argument("--graph-steps", type=int, default=240, help="steps per captured HIP graph")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU-oracle baseline")
@@ -51,9 +59,19 @@ def parse():
                     help="only run a device copy of MB megabytes ten times (counter calibration)")
     ap.add_argument("--path", choices=("layer", "split"), default="layer",
                     help="layer: one coli_moe_layer launch per step; split: coli_moe_route + coli_moe_forward")
-    ap.add_argument("--kernels", choices=("auto", "multi", "persistent"), default="auto",
-                    help="kernel set: the library's choice, the multi-launch kernels or the persistent one")
-    return ap.parse_args()
+    ap.add_argument("--kernels", choices=("auto", "multi", "persistent", "grouped"), default="auto",
+                    help="kernel set: the library's choice, the multi-launch decode kernels, the persistent "
+                         "one or the grouped matrix-core kernels")
+    a = ap.parse_args()
+    if a.steps is None:
+        a.steps = 2400 if a.workload == "decode" else 200
+    if a.warmup is None:
+        a.warmup = 240 if a.workload == "decode" else 20
+    return a
+
+
+PATHS = {"auto": 0, "multi": 1, "persistent": 2, "grouped": 3}
+INT8_PEAK_TOPS = 5000.0   # MI355X dense int8 matrix-core peak
 
 
 def main():
@@ -82,9 +100,12 @@ def main():
     import synth
 
     torch.cuda.set_device(0)
+    q.coli_moe_debug_force_path(PATHS[args.kernels])
+    if args.workload == "prefill":
+        run_prefill(args, q, synth)
+        return
     spec = synth.GLM
     dims = q.make_dims(spec)
-    q.coli_moe_debug_force_path({"auto": q.PATH_AUTO, "multi": q.PATH_MULTI, "persistent": q.PATH_PERSISTENT}[args.kernels])
     H, E = spec.hidden, spec.n_experts
     L = args.layers
     bb = spec.blob_bytes
@@ -147,21 +168,7 @@ def main():
 
     # per-kernel durations: every launch of an eager pass carries a HIP event
     # pair recorded at the kernel's own start and end
-    q.coli_moe_timing_enable(True)
-    for s in range(G):
-        step(s)
-    torch.cuda.synchronize()
-    q.coli_moe_timing_enable(False)
-    kinds = (("router_logits", q.KIND_ROUTER_LOGITS), ("router_select", q.KIND_ROUTER_SELECT),
-             ("quant_x", q.KIND_QUANT_X), ("gateup", q.KIND_GATEUP), ("down", q.KIND_DOWN),
-             ("combine", q.KIND_COMBINE), ("layer", q.KIND_LAYER),
-             ("forward_persistent", q.KIND_FORWARD_PERSISTENT))
-    kernel_us, launches = {}, {}
-    for name, k in kinds:
-        ms, n = q.coli_moe_timing_read(k)
-        if n:
-            kernel_us[name] = 1e3 * ms / n
-            launches[name] = n
+    kernel_us, launches = kernel_times(q, lambda: [step(s) for s in range(G)])
 
     # captured steps
     cap = torch.cuda.Stream()
@@ -238,6 +245,161 @@ def main():
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(args, spec, xs_host, layers, L)
     print(json.dumps(res), flush=True)
+
+
+KINDS = (("router_logits", 0), ("router_select", 1), ("quant_x", 7), ("group", 8), ("gateup", 2), ("down", 3),
+         ("combine", 4), ("layer", 5), ("forward_persistent", 6))
+
+
+def kernel_times(q, run):
+    """Average duration (us) and launch count per kernel kind over one eager
+    call of run(), every launch bracketed by HIP events recorded at the
+    kernel's own start and end."""
+    import torch
+    q.coli_moe_timing_enable(True)
+    run()
+    torch.cuda.synchronize()
+    q.coli_moe_timing_enable(False)
+    us, n_l = {}, {}
+    for name, k in KINDS:
+        ms, n = q.coli_moe_timing_read(k)
+        if n:
+            us[name] = 1e3 * ms / n
+            n_l[name] = n
+    return us, n_l
+
+
+def run_prefill(args, q, synth):
+    """Batch-union prefill: GLM-5.2-shaped layer, all experts resident, one
+    step = coli_moe_layer over a batch of args.tokens Zipf-routed tokens
+    (two batches alternate)."""
+    import numpy as np
+    import torch
+
+    spec = synth.GLM
+    dims = q.make_dims(spec)
+    S, H, I, E, K = args.tokens, spec.hidden, spec.inter, spec.n_experts, spec.top_k
+    bb = spec.blob_bytes
+    t0 = time.time()
+    host = torch.empty((E + 1) * bb, dtype=torch.uint8, pin_memory=True)
+    for e in range(E + 1):
+        synth.cdf_expert_into(host.data_ptr() + e * bb, args.seed, 0, e, spec)
+    dev = host.cuda()
+    table = torch.tensor([dev.data_ptr() + e * bb for e in range(E)], dtype=torch.int64, device="cuda")
+    shared = dev.data_ptr() + E * bb
+    d = synth.layer_inputs(args.seed, 0, spec, 1)
+    W = torch.from_numpy(d["router_w"]).cuda()
+    bias = torch.zeros(E, dtype=torch.float32, device="cuda")
+    xs_host = [synth.prefill_hidden_states(args.seed, 0, spec, S, batch=b) for b in range(2)]
+    xs = [torch.from_numpy(x).cuda() for x in xs_host]
+    ws = torch.zeros(q.coli_moe_workspace_bytes(dims, S), dtype=torch.uint8, device="cuda")
+    idx = [torch.empty((S, K), dtype=torch.int32, device="cuda") for _ in range(2)]
+    wts = [torch.empty((S, K), dtype=torch.float32, device="cuda") for _ in range(2)]
+    out = [torch.empty((S, H), dtype=torch.float32, device="cuda") for _ in range(2)]
+    log(f"prefill setup: {E + 1} experts resident, 2 batches of {S} tokens ({time.time() - t0:.1f} s)")
+
+    def step(s):
+        b = s % 2
+        q.coli_moe_layer(dims, xs[b], W, bias, table, shared, idx[b], wts[b], out[b], ws)
+
+    step(0)
+    step(1)
+    rc = q.coli_moe_status(ws)
+    if rc != 0:
+        raise RuntimeError(f"device status {rc}: {q.coli_moe_last_error()}")
+    routed = [i.cpu().numpy() for i in idx]
+    counts = np.bincount(routed[0].ravel(), minlength=E)
+    kernel_us, launches = kernel_times(q, lambda: [step(s) for s in range(2)])
+
+    G = 10
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=cap):
+        for s in range(G):
+            step(s)
+    torch.cuda.synchronize()
+    reps_w = max(1, args.warmup // G)
+    reps = max(1, args.steps // G)
+    for _ in range(reps_w):
+        graph.replay()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(reps):
+        graph.replay()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t1
+    steps = reps * G
+    rc = q.coli_moe_status(ws)
+    if rc != 0:
+        raise RuntimeError(f"device status after replay {rc}: {q.coli_moe_last_error()}")
+    ms_per_step = 1e3 * elapsed / steps
+
+    # algorithmic work: every (token, expert) pair of the batch, shared expert
+    # included, costs 2 H I MACs in gate/up and H I in down (2 ops a MAC)
+    pairs = S * K + S * spec.n_shared
+    ops_gateup = 2 * 2 * H * I * pairs
+    ops_layer = 3 * 2 * H * I * pairs
+    g_us = kernel_us["gateup"]
+    achieved = ops_gateup / (g_us * 1e-6) / 1e12
+    layer_tops = ops_layer / (ms_per_step * 1e-3) / 1e12
+    hbm_bytes = (E + 1) * bb + E * H * 4
+    res = {
+        "metric": METRIC,
+        "value": round(S / (ms_per_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": reps_w * G,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8xi4->i32,f32",
+        "data": "synthetic (seeded; GLM-5.2-shaped random-code experts, Zipf(1.1)-routed tokens)",
+        "config": {
+            "workload": f"GLM-5.2-shaped MoE prefill layer, {S} tokens/step: hidden 6144, expert inter 2048, "
+                        "256 routed experts top-8 + 1 shared, int4 per-row-scaled weights, Q8_0 activations, "
+                        "fp32 router gate, zero bias; Zipf(1.1) expert popularity; all 257 experts resident",
+            "tokens_per_step": S, "graph_steps": G, "kernels": args.kernels,
+            "routing": {"unique": int((counts > 0).sum()), "min": int(counts[counts > 0].min()),
+                        "median": float(np.median(counts[counts > 0])), "max": int(counts.max())},
+        },
+        "roofline": {
+            "bound": "mfma", "kernel": "k_pf_gateup<4,2>",
+            "achieved": round(achieved, 1), "peak": INT8_PEAK_TOPS, "unit": "TOPS",
+            "frac": round(achieved / INT8_PEAK_TOPS, 4), "traffic": counted_traffic("k_pf_gateup<4,2>"),
+            "algorithmic_ops_per_launch": ops_gateup, "avg_launch_us": round(g_us, 3),
+        },
+        "layer_int8_tops": round(layer_tops, 1),
+        "layer_int8_frac": round(layer_tops / INT8_PEAK_TOPS, 4),
+        "layer_hbm_gbs": round(hbm_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+        "kernel_avg_us": {k: round(v, 3) for k, v in kernel_us.items()},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_prefill(args, spec, xs_host[0], d, host.numpy(), routed[0])
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline_prefill(args, spec, x, d, host, routed):
+    """The CPU oracle on the first tokens of the prefill batch, as many as fit
+    the time budget (each token's output depends on that token only)."""
+    import numpy as np
+
+    import oracle
+    E, bb = spec.n_experts, spec.blob_bytes
+    blobs = [host[e * bb:(e + 1) * bb] for e in range(E)]
+    shared = host[E * bb:(E + 1) * bb]
+    bias = np.zeros(E, np.float32)
+    n, spent = 0, 0.0
+    while spent < args.cpu_seconds and n < x.shape[0]:
+        t = time.perf_counter()
+        oracle.layer(spec, x[n:n + 1], d["router_w"], bias, blobs, shared)
+        spent += time.perf_counter() - t
+        n += 1
+    return {"value": round(n / spent, 4), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {n} tokens of the 2048-token batch, one at a time (route + 9 experts + combine), "
+                      f"{spent:.1f} s single-threaded"}
 
 
 def _hipbuild():

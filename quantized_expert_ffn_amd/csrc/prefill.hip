@@ -137,50 +137,61 @@ __global__ __launch_bounds__(1024) void k_group(const int32_t *__restrict__ idx,
     }
 }
 
-// ---- weights and activations as matrix-core operands --------------------
-// The product of the 16 codes of a lane's weight operand with its 16
-// activation codes sums to 2^SHIFT times the true integer sum: int8 codes
-// are used as they are, int4 codes as 16 * code (the nibble masked into the
-// top of a byte) and int2 codes as 64 * code.
+// ---- staging of weight rows and activations through LDS -----------------
+// A workgroup computes PF_ROWS rows of each of its NM matrices (gate and up,
+// or down) for the 32 pairs of a tile; wave w owns rows 32 w .. 32 w + 31.
+// The K dimension advances in stages of 128 bytes of every weight row
+// (C = 32 / BITS blocks): each stage is loaded with whole 128-byte segments
+// per row (coalesced, every byte fetched once per workgroup) into registers
+// while the previous stage is computed from LDS, then written to LDS.
 //
-// Inside a block the order of the 32 products is free (the sum is exact), so
-// lane half h may take any 16 of the block's codes, with its activation codes
-// in the same order:
-//   int8: codes 16 h .. 16 h + 15 (bytes 16 h .. of the block);
-//   int4: the low, then the high nibbles of bytes 8 h .. 8 h + 7, i.e. codes
-//         8 h .. 8 h + 7 then 16 + 8 h .. 16 + 8 h + 7, so that a lane reads
-//         only its own 8 bytes of the row;
-//   int2: fields 2 h and 2 h + 1 of the 8 bytes, codes 16 h .. 16 h + 15.
-// Rows and activations are read through buffer resources: the lane's row
-// (or vector) offset is its VGPR offset, the block's offset a scalar.
-template <int BITS>
-struct Operand {
+// LDS holds 16-byte pieces with their index xor-ed with the row (or token)
+// index mod 8, so that the 8 lanes of a read phase hit 8 different 16-byte
+// bank groups.
+constexpr int PF_ROWS = 128;
+
+template <int BITS, int NM>
+struct PfStage {
+    static constexpr int C = 32 / BITS;           // blocks per stage
+    static constexpr int WPIECES = 8;             // 16-byte pieces of a row per stage
+    static constexpr int APIECES = 2 * C;         // 16-byte pieces of a token per stage
+    static constexpr int W_CHUNKS = NM * PF_ROWS * WPIECES / PF_T;   // per thread
+    static constexpr int A_CHUNKS = 32 * APIECES / PF_T;             // per thread (1, 2, 4)
+    static constexpr int D_WORDS = (32 * C + PF_T - 1) / PF_T;       // per thread (1, 1, 2)
+    static constexpr int W_BYTES = NM * PF_ROWS * 128;
+    static constexpr int A_BYTES = 32 * 32 * C;
+    static constexpr int D_BYTES = 32 * C * 4;
+    static constexpr int LDS = W_BYTES + A_BYTES + D_BYTES;
     static constexpr int SHIFT = BITS == 8 ? 0 : (BITS == 4 ? 4 : 6);
-    static constexpr int BLOCK = 4 * BITS;  // bytes of a packed 32-code block
-    // byte offset of lane half h inside a block of a packed row
-    __device__ static int lane_off(int h) { return BITS == 8 ? 16 * h : (BITS == 4 ? 8 * h : 0); }
 };
 
+__device__ __forceinline__ int swz(int piece, int row) { return piece ^ (row & 7); }
+
+// Weight operand of block j of the stage for lane half h, from the row's
+// 128 LDS bytes.  The 16 codes of lane half h, times 2^SHIFT as signed
+// bytes: int8 codes 16 h .. 16 h + 15; int4 the low nibbles (h = 0, codes
+// 0 .. 15) or high nibbles (h = 1, codes 16 .. 31) of the block's 16 bytes;
+// int2 fields 2 h and 2 h + 1 of its 8 bytes (codes 16 h .. 16 h + 15).
 template <int BITS>
-__device__ __forceinline__ i32x4 weight_operand(__amdgpu_buffer_rsrc_t r, uint32_t voff, int b, int h);
+__device__ __forceinline__ i32x4 lds_weight(const uint8_t *row_lds, int row, int j, int h);
 template <>
-__device__ __forceinline__ i32x4 weight_operand<8>(__amdgpu_buffer_rsrc_t r, uint32_t voff, int b, int) {
-    const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(r, voff, 32 * b, BUF_NT);
-    return i32x4{(int)w.x, (int)w.y, (int)w.z, (int)w.w};
+__device__ __forceinline__ i32x4 lds_weight<8>(const uint8_t *row_lds, int row, int j, int h) {
+    return *reinterpret_cast<const i32x4 *>(row_lds + 16 * swz(2 * j + h, row));
 }
 template <>
-__device__ __forceinline__ i32x4 weight_operand<4>(__amdgpu_buffer_rsrc_t r, uint32_t voff, int b, int) {
-    const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(r, voff, 16 * b, BUF_NT);
+__device__ __forceinline__ i32x4 lds_weight<4>(const uint8_t *row_lds, int row, int j, int h) {
+    const u32x4 w = *reinterpret_cast<const u32x4 *>(row_lds + 16 * swz(j, row));
+    const int s = 4 - 4 * h;
     i32x4 o;
-    o.x = (int)((w.x << 4) & 0xF0F0F0F0u);
-    o.y = (int)((w.y << 4) & 0xF0F0F0F0u);
-    o.z = (int)(w.x & 0xF0F0F0F0u);
-    o.w = (int)(w.y & 0xF0F0F0F0u);
+    o.x = (int)((w.x << s) & 0xF0F0F0F0u);
+    o.y = (int)((w.y << s) & 0xF0F0F0F0u);
+    o.z = (int)((w.z << s) & 0xF0F0F0F0u);
+    o.w = (int)((w.w << s) & 0xF0F0F0F0u);
     return o;
 }
 template <>
-__device__ __forceinline__ i32x4 weight_operand<2>(__amdgpu_buffer_rsrc_t r, uint32_t voff, int b, int h) {
-    const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(r, voff, 8 * b, BUF_NT);
+__device__ __forceinline__ i32x4 lds_weight<2>(const uint8_t *row_lds, int row, int j, int h) {
+    const u32x2 w = *reinterpret_cast<const u32x2 *>(row_lds + 16 * swz(j >> 1, row) + 8 * (j & 1));
     const int s0 = 6 - 4 * h, s1 = 4 - 4 * h;  // fields 2 h and 2 h + 1 to bits 6-7
     i32x4 o;
     o.x = (int)((w.x << s0) & 0xC0C0C0C0u);
@@ -190,31 +201,11 @@ __device__ __forceinline__ i32x4 weight_operand<2>(__amdgpu_buffer_rsrc_t r, uin
     return o;
 }
 
-// Activation operand of block b; voff = byte offset of the Q8_0 vector.
-template <int BITS>
-__device__ __forceinline__ i32x4 act_operand(__amdgpu_buffer_rsrc_t r, uint32_t voff, int b, int h) {
-    if (BITS == 4) {
-        const u32x2 lo = __builtin_amdgcn_raw_buffer_load_b64(r, voff + 8 * h, 32 * b, 0);
-        const u32x2 hi = __builtin_amdgcn_raw_buffer_load_b64(r, voff + 16 + 8 * h, 32 * b, 0);
-        return i32x4{(int)lo.x, (int)lo.y, (int)hi.x, (int)hi.y};
-    }
-    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff + 16 * h, 32 * b, 0);
-    return i32x4{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
-}
-
-__device__ __forceinline__ float scale_at(__amdgpu_buffer_rsrc_t r, uint32_t voff, int b) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, 4 * b, 0));
-}
-
 // The tile of workgroup row blockIdx.y: unit, first pair, pairs.
 struct Tile {
     int u, p_first, n;
 };
 
-// Slot of column n of the tile (-1 past its pairs).
-__device__ __forceinline__ int tile_slot(const int32_t *pairs, const Tile &tl, int n) {
-    return n < tl.n ? pairs[tl.p_first + n] : -1;
-}
 __device__ __forceinline__ int slot_token(int slot, int P, int K) { return slot < P ? slot / K : slot - P; }
 
 // Whether d * 2^-SHIFT is exact for the nb block scales d[0 .. nb) of every
@@ -232,77 +223,144 @@ __device__ __forceinline__ bool scales_fold(const float *d, int nb) {
     return __builtin_amdgcn_ballot_w64(!ok) == 0;
 }
 
-// Chains one 32 x 32 product into the lane's 16 accumulators: with FOLD the
-// scale is pre-multiplied by 2^-SHIFT, otherwise the sums are shifted.
-template <int SHIFT, bool FOLD>
-__device__ __forceinline__ void chain16(float (&acc)[16], const i32x16 &c, float d) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] = __builtin_fmaf(d, (float)(FOLD ? c[r] : c[r] >> SHIFT), acc[r]);
-}
+// Operands of a tile: NM weight matrices at byte offsets mat[m] of the blob
+// (rows of rb bytes, row0 = first row of the workgroup, n_rows valid rows of
+// the matrix), the Q8_0 vectors of the tile's 32 columns (codes at
+// voff[col] of ra, scales at doff[col] of rd, vec_bytes per vector).
+template <int NM>
+struct PfSrc {
+    __amdgpu_buffer_rsrc_t rw, ra, rd;
+    uint32_t mat[NM];
+    uint32_t rb;
+    int row0, n_rows, nb;
+};
 
-template <int SHIFT, bool FOLD>
-__device__ __forceinline__ float chain_scale(float d) {
-    return FOLD ? d * (1.0f / (float)(1 << SHIFT)) : d;
-}
+// Stage registers of one thread.
+template <int BITS, int NM>
+struct PfRegs {
+    u32x4 w[PfStage<BITS, NM>::W_CHUNKS];
+    u32x4 a[PfStage<BITS, NM>::A_CHUNKS];
+    uint32_t d[PfStage<BITS, NM>::D_WORDS];
+};
 
-// Accumulators of NM matrices x RT row tiles over nb blocks for the lane's
-// column: acc[m][t][r] = chain over b of d_b * isum_b of row
-// r0 + 32 t + mfma_c_row(lane, r) of matrix m (wv[m][t] = the row's offset).
-template <int BITS, int NM, int RT, bool FOLD>
-__device__ __forceinline__ void pf_chains(float (&acc)[NM][RT][16], __amdgpu_buffer_rsrc_t rw,
-                                          const uint32_t (&wv)[NM][RT], __amdgpu_buffer_rsrc_t ra, uint32_t av,
-                                          __amdgpu_buffer_rsrc_t rd, uint32_t dv, int nb, int h) {
-    constexpr int SH = Operand<BITS>::SHIFT;
-    i32x4 wa[NM][RT];
+template <int BITS, int NM>
+__device__ __forceinline__ void pf_load(PfRegs<BITS, NM> &R, const PfSrc<NM> &src, const uint32_t *col_voff,
+                                        const uint32_t *col_doff, int stage) {
+    using ST = PfStage<BITS, NM>;
+    const int tid = threadIdx.x;
 #pragma unroll
-    for (int m = 0; m < NM; ++m)
+    for (int i = 0; i < ST::W_CHUNKS; ++i) {
+        // a matrix spans PF_ROWS * 8 / PF_T = 4 chunks of every thread
+        constexpr int PER_M = PF_ROWS * 8 / PF_T;
+        const int m = i / PER_M, row = ((i % PER_M) * PF_T + tid) / 8, piece = tid % 8;
+        const int r = min(src.row0 + row, src.n_rows - 1);
+        const uint32_t off = src.mat[m] + (uint32_t)r * src.rb + 128u * stage + 16u * piece;
+        R.w[i] = __builtin_amdgcn_raw_buffer_load_b128(src.rw, off, 0, BUF_NT);
+    }
 #pragma unroll
-        for (int t = 0; t < RT; ++t) wa[m][t] = weight_operand<BITS>(rw, wv[m][t], 0, h);
-    i32x4 xa = act_operand<BITS>(ra, av, 0, h);
-    float d = scale_at(rd, dv, 0);
-    for (int b = 0; b < nb; ++b) {
-        // block b + 1's operands load while block b computes (the last
-        // iteration reloads block b, in range)
-        const int bn = b + 1 < nb ? b + 1 : b;
-        i32x4 wn[NM][RT];
+    for (int i = 0; i < ST::A_CHUNKS; ++i) {
+        const int g = i * PF_T + tid;
+        const int col = g / ST::APIECES, piece = g % ST::APIECES;
+        R.a[i] = __builtin_amdgcn_raw_buffer_load_b128(src.ra, col_voff[col] + 32u * ST::C * stage + 16u * piece, 0, 0);
+    }
 #pragma unroll
-        for (int m = 0; m < NM; ++m)
-#pragma unroll
-            for (int t = 0; t < RT; ++t) wn[m][t] = weight_operand<BITS>(rw, wv[m][t], bn, h);
-        const i32x4 xn = act_operand<BITS>(ra, av, bn, h);
-        const float dn = scale_at(rd, dv, bn);
-        const float ds = chain_scale<SH, FOLD>(d);
-        // all products of the block first, then their chains
-        i32x16 c[NM][RT];
-#pragma unroll
-        for (int t = 0; t < RT; ++t)
-#pragma unroll
-            for (int m = 0; m < NM; ++m) c[m][t] = mfma_i8_32x32x32(wa[m][t], xa);
-#pragma unroll
-        for (int t = 0; t < RT; ++t)
-#pragma unroll
-            for (int m = 0; m < NM; ++m) chain16<SH, FOLD>(acc[m][t], c[m][t], ds);
-#pragma unroll
-        for (int m = 0; m < NM; ++m)
-#pragma unroll
-            for (int t = 0; t < RT; ++t) wa[m][t] = wn[m][t];
-        xa = xn;
-        d = dn;
+    for (int i = 0; i < ST::D_WORDS; ++i) {
+        const int g = i * PF_T + tid;
+        const int col = min(g / ST::C, 31), c = g % ST::C;
+        R.d[i] = __builtin_amdgcn_raw_buffer_load_b32(src.rd, col_doff[col] + 4u * (ST::C * stage + c), 0, 0);
     }
 }
 
+template <int BITS, int NM>
+__device__ __forceinline__ void pf_store(const PfRegs<BITS, NM> &R, uint8_t *lds) {
+    using ST = PfStage<BITS, NM>;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < ST::W_CHUNKS; ++i) {
+        const int g = i * PF_T + tid;
+        const int mrow = g / 8, piece = g % 8;  // row index over all matrices
+        *reinterpret_cast<u32x4 *>(lds + 128 * mrow + 16 * swz(piece, mrow)) = R.w[i];
+    }
+    uint8_t *la = lds + ST::W_BYTES;
+#pragma unroll
+    for (int i = 0; i < ST::A_CHUNKS; ++i) {
+        const int g = i * PF_T + tid;
+        const int col = g / ST::APIECES, piece = g % ST::APIECES;
+        *reinterpret_cast<u32x4 *>(la + 32 * ST::C * col + 16 * swz(piece, col)) = R.a[i];
+    }
+    uint32_t *ld = reinterpret_cast<uint32_t *>(lds + ST::W_BYTES + ST::A_BYTES);
+#pragma unroll
+    for (int i = 0; i < ST::D_WORDS; ++i) {
+        const int g = i * PF_T + tid;
+        if (g < 32 * ST::C) ld[g] = R.d[i];
+    }
+}
+
+// The staged product loop: acc[m][r] = chain over the nb blocks of
+// d_b * isum_b for row 32 w + mfma_c_row(lane, r) of matrix m and the lane's
+// column.  Every wave runs the loads and barriers; `active` waves compute.
+template <int BITS, int NM, bool FOLD>
+__device__ __forceinline__ void pf_run(float (&acc)[NM][16], uint8_t *lds, const PfSrc<NM> &src,
+                                       const uint32_t *col_voff, const uint32_t *col_doff, bool active) {
+    using ST = PfStage<BITS, NM>;
+    constexpr int SH = ST::SHIFT;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, h = lane >> 5, n = lane & 31;
+    const int n_stages = (src.nb + ST::C - 1) / ST::C;
+    PfRegs<BITS, NM> R;
+    pf_load<BITS, NM>(R, src, col_voff, col_doff, 0);
+    const uint8_t *la = lds + ST::W_BYTES + 32 * ST::C * n;
+    const float *ld = reinterpret_cast<const float *>(lds + ST::W_BYTES + ST::A_BYTES) + ST::C * n;
+    for (int s = 0; s < n_stages; ++s) {
+        if (s > 0) __syncthreads();  // every wave is done with the previous stage
+        pf_store<BITS, NM>(R, lds);
+        __syncthreads();
+        if (s + 1 < n_stages) pf_load<BITS, NM>(R, src, col_voff, col_doff, s + 1);
+        if (!active) continue;
+        const int nblk = min(ST::C, src.nb - ST::C * s);
+        for (int j = 0; j < nblk; ++j) {
+            const i32x4 xb = *reinterpret_cast<const i32x4 *>(la + 16 * swz(2 * j + h, n));
+            const float d = ld[j];
+            const float ds = FOLD ? d * (1.0f / (float)(1 << SH)) : d;
+            i32x16 c[NM];
+#pragma unroll
+            for (int m = 0; m < NM; ++m) {
+                const int row = m * PF_ROWS + 32 * wave + n;
+                c[m] = mfma_i8_32x32x32(lds_weight<BITS>(lds + 128 * row, row, j, h), xb);
+            }
+#pragma unroll
+            for (int m = 0; m < NM; ++m)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    acc[m][r] = __builtin_fmaf(ds, (float)(FOLD ? c[m][r] : c[m][r] >> SH), acc[m][r]);
+        }
+    }
+}
+
+// Columns of the tile: the slot of pair n (the tile's first pair past its
+// end) and that slot's token.
+struct PfCols {
+    int slot, tok;
+    bool live;
+};
+__device__ __forceinline__ PfCols pf_col(const int32_t *pairs, const Tile &tl, int n, int P, int K) {
+    PfCols c;
+    c.live = n < tl.n;
+    c.slot = pairs[tl.p_first + (c.live ? n : 0)];
+    c.tok = slot_token(c.slot, P, K);
+    return c;
+}
+
 // ---- gate/up ------------------------------------------------------------
-// Grid (ceil(I / (128 RT)), tile bound); wave w takes rows
-// 128 RT x + 32 RT w .. + 32 RT - 1 (RT row tiles of 32) for the tile's
-// pairs, lane column n = lane % 32, lane half h = lane / 32.  Columns past
-// the tile's pairs compute on a copy of its first pair and store nothing.
-template <int BITS, int RT>
+// Grid (ceil(I / PF_ROWS), tile bound).  Epilogue: row scales, SwiGLU and
+// Q8_0 over each wave's 32 rows (one block of h) for every live column.
+template <int BITS>
 __global__ __launch_bounds__(PF_T) void k_pf_gateup(const FwdArgs a, const int32_t *__restrict__ tiles) {
-    constexpr int SH = Operand<BITS>::SHIFT;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    using ST = PfStage<BITS, 2>;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[ST::LDS];
+    __shared__ uint32_t col_voff[32], col_doff[32];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, h = lane >> 5, n = lane & 31;
     const int H = a.H, I = a.I, P = a.S * a.K, nb = H / 32;
-    const int i0 = (blockIdx.x * 4 + wave) * 32 * RT;
-    if (i0 >= I || (int)blockIdx.y >= tiles[0]) return;
+    if ((int)blockIdx.y >= tiles[0]) return;
     const i32x4 td = reinterpret_cast<const i32x4 *>(tiles + 4)[blockIdx.y];
     const Tile tl{td.x, td.y, td.z};
     const UnitTable U = unit_table(a.S, a.K, a.E);
@@ -314,78 +372,76 @@ __global__ __launch_bounds__(PF_T) void k_pf_gateup(const FwdArgs a, const int32
         return;
     }
     const BlobLayout BL = blob_layout(H, I, BITS);
-    const uint32_t rb = (uint32_t)H * BITS / 8;
-    const int h = lane >> 5, n = lane & 31;
-    const __amdgpu_buffer_rsrc_t rw = make_rsrc(blob, (uint32_t)BL.total);
-    uint32_t wv[2][RT];
-#pragma unroll
-    for (int t = 0; t < RT; ++t) {
-        const uint32_t row = (uint32_t)(i0 + 32 * t + n) * rb + Operand<BITS>::lane_off(h);
-        wv[0][t] = (uint32_t)BL.gate + row;
-        wv[1][t] = (uint32_t)BL.up + row;
+    const PfCols col = pf_col(tab + U.pairs, tl, n, P, a.K);
+    if (threadIdx.x < 32) {
+        col_voff[n] = (uint32_t)col.tok * (uint32_t)H;
+        col_doff[n] = (uint32_t)col.tok * (uint32_t)nb * 4u;
     }
-    const int slot = tile_slot(tab + U.pairs, tl, n);
-    const bool live = slot >= 0;
-    const int tok = slot_token(live ? slot : tab[U.pairs + tl.p_first], P, a.K);
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.qx, (uint32_t)a.S * (uint32_t)H);
-    const __amdgpu_buffer_rsrc_t rd = make_rsrc(a.dx, (uint32_t)a.S * (uint32_t)nb * 4u);
-    float acc[2][RT][16];
+    PfSrc<2> src;
+    src.rw = make_rsrc(blob, (uint32_t)BL.total);
+    src.ra = make_rsrc(a.qx, (uint32_t)a.S * (uint32_t)H);
+    src.rd = make_rsrc(a.dx, (uint32_t)a.S * (uint32_t)nb * 4u);
+    src.mat[0] = (uint32_t)BL.gate;
+    src.mat[1] = (uint32_t)BL.up;
+    src.rb = (uint32_t)H * BITS / 8;
+    src.row0 = blockIdx.x * PF_ROWS;
+    src.n_rows = I;
+    src.nb = nb;
+    __syncthreads();
+    const int i0 = src.row0 + 32 * wave;
+    const bool active = i0 < I;
+    float acc[2][16];
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
-        for (int t = 0; t < RT; ++t)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[m][t][r] = 0.0f;
-    if (scales_fold<SH>(a.dx + (size_t)tok * nb, nb))
-        pf_chains<BITS, 2, RT, true>(acc, rw, wv, ra, (uint32_t)tok * H, rd, (uint32_t)tok * nb * 4u, nb, h);
+        for (int r = 0; r < 16; ++r) acc[m][r] = 0.0f;
+    // every wave has the same 32 columns, hence the same choice
+    if (scales_fold<ST::SHIFT>(a.dx + (size_t)col.tok * nb, nb))
+        pf_run<BITS, 2, true>(acc, lds, src, col_voff, col_doff, active);
     else
-        pf_chains<BITS, 2, RT, false>(acc, rw, wv, ra, (uint32_t)tok * H, rd, (uint32_t)tok * nb * 4u, nb, h);
-    if (!live) return;
-    // epilogue per row tile: register r of the lane is row 8 (r / 4) + 4 h + r % 4
+        pf_run<BITS, 2, false>(acc, lds, src, col_voff, col_doff, active);
+    if (!active || !col.live) return;
+    const float *sg = reinterpret_cast<const float *>(blob + BL.s_gate) + i0;
+    const float *su = reinterpret_cast<const float *>(blob + BL.s_up) + i0;
+    float hv[16], amax = 0.0f;
 #pragma unroll
-    for (int t = 0; t < RT; ++t) {
-        const int r0 = i0 + 32 * t;
-        const float *sg = reinterpret_cast<const float *>(blob + BL.s_gate) + r0;
-        const float *su = reinterpret_cast<const float *>(blob + BL.s_up) + r0;
-        float hv[16], amax = 0.0f;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int row = mfma_c_row(lane, r);
-            hv[r] = swiglu_f32(acc[0][t][r] * sg[row], acc[1][t][r] * su[row]);
-            amax = __builtin_fmaxf(amax, __builtin_fabsf(hv[r]));
-        }
-        // Q8_0 over the 32 rows of the column, held by lanes n and n + 32
-        amax = __builtin_fmaxf(amax, __shfl_xor(amax, 32, 64));
-        const float dq = amax / 127.0f;
-        int8_t *qrow = a.qh + (size_t)slot * I + r0;
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            uint32_t word = 0;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                float c = 0.0f;
-                if (dq != 0.0f) {
-                    c = __builtin_roundf(hv[4 * g + q] / dq);
-                    c = __builtin_fminf(__builtin_fmaxf(c, -127.0f), 127.0f);
-                }
-                word |= (uint32_t)(uint8_t)(int8_t)(int)c << (8 * q);
-            }
-            *reinterpret_cast<uint32_t *>(qrow + 8 * g + 4 * h) = word;
-        }
-        if (h == 0) a.dh[(size_t)slot * (I / 32) + r0 / 32] = dq;
+    for (int r = 0; r < 16; ++r) {
+        const int row = mfma_c_row(lane, r);
+        hv[r] = swiglu_f32(acc[0][r] * sg[row], acc[1][r] * su[row]);
+        amax = __builtin_fmaxf(amax, __builtin_fabsf(hv[r]));
     }
+    // Q8_0 over the 32 rows of the column, held by lanes n and n + 32
+    amax = __builtin_fmaxf(amax, __shfl_xor(amax, 32, 64));
+    const float dq = amax / 127.0f;
+    int8_t *qrow = a.qh + (size_t)col.slot * I + i0;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            float c = 0.0f;
+            if (dq != 0.0f) {
+                c = __builtin_roundf(hv[4 * g + q] / dq);
+                c = __builtin_fminf(__builtin_fmaxf(c, -127.0f), 127.0f);
+            }
+            word |= (uint32_t)(uint8_t)(int8_t)(int)c << (8 * q);
+        }
+        *reinterpret_cast<uint32_t *>(qrow + 8 * g + 4 * h) = word;
+    }
+    if (h == 0) a.dh[(size_t)col.slot * (I / 32) + i0 / 32] = dq;
 }
 
 // ---- down ---------------------------------------------------------------
-// Grid (ceil(H / (128 RT)), tile bound): Y[slot][row] = s_d[row] * chain over
+// Grid (ceil(H / PF_ROWS), tile bound): Y[slot][row] = s_d[row] * chain over
 // the I / 32 blocks of Q8_0(h) of the slot.
-template <int BITS, int RT>
+template <int BITS>
 __global__ __launch_bounds__(PF_T) void k_pf_down(const FwdArgs a, const int32_t *__restrict__ tiles) {
-    constexpr int SH = Operand<BITS>::SHIFT;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int H = a.H, I = a.I, nb = I / 32;
-    const int r0 = (blockIdx.x * 4 + wave) * 32 * RT;
-    if (r0 >= H || (int)blockIdx.y >= tiles[0]) return;
+    using ST = PfStage<BITS, 1>;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[ST::LDS];
+    __shared__ uint32_t col_voff[32], col_doff[32];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, h = lane >> 5, n = lane & 31;
+    const int H = a.H, I = a.I, P = a.S * a.K, nb = I / 32;
+    if ((int)blockIdx.y >= tiles[0]) return;
     const i32x4 td = reinterpret_cast<const i32x4 *>(tiles + 4)[blockIdx.y];
     const Tile tl{td.x, td.y, td.z};
     const UnitTable U = unit_table(a.S, a.K, a.E);
@@ -394,44 +450,43 @@ __global__ __launch_bounds__(PF_T) void k_pf_down(const FwdArgs a, const int32_t
     const uint8_t *blob = e < 0 ? a.shared : a.blobs[e];
     if (!blob) return;  // reported by the gate/up kernel
     const BlobLayout BL = blob_layout(H, I, BITS);
-    const uint32_t rb = (uint32_t)I * BITS / 8;
-    const int h = lane >> 5, n = lane & 31;
-    const __amdgpu_buffer_rsrc_t rw = make_rsrc(blob, (uint32_t)BL.total);
-    uint32_t wv[1][RT];
-#pragma unroll
-    for (int t = 0; t < RT; ++t)
-        wv[0][t] = (uint32_t)BL.down + (uint32_t)(r0 + 32 * t + n) * rb + Operand<BITS>::lane_off(h);
-    const int slot = tile_slot(tab + U.pairs, tl, n);
-    const bool live = slot >= 0;
-    const int src = live ? slot : tab[U.pairs + tl.p_first];
+    const PfCols col = pf_col(tab + U.pairs, tl, n, P, a.K);
+    if (threadIdx.x < 32) {
+        col_voff[n] = (uint32_t)col.slot * (uint32_t)I;
+        col_doff[n] = (uint32_t)col.slot * (uint32_t)nb * 4u;
+    }
     const uint32_t slots = (uint32_t)a.S * (uint32_t)(a.K + 1);
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.qh, slots * (uint32_t)I);
-    const __amdgpu_buffer_rsrc_t rd = make_rsrc(a.dh, slots * (uint32_t)nb * 4u);
-    float acc[1][RT][16];
+    PfSrc<1> src;
+    src.rw = make_rsrc(blob, (uint32_t)BL.total);
+    src.ra = make_rsrc(a.qh, slots * (uint32_t)I);
+    src.rd = make_rsrc(a.dh, slots * (uint32_t)nb * 4u);
+    src.mat[0] = (uint32_t)BL.down;
+    src.rb = (uint32_t)I * BITS / 8;
+    src.row0 = blockIdx.x * PF_ROWS;
+    src.n_rows = H;
+    src.nb = nb;
+    __syncthreads();
+    const int r0 = src.row0 + 32 * wave;
+    const bool active = r0 < H;
+    float acc[1][16];
 #pragma unroll
-    for (int t = 0; t < RT; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[0][t][r] = 0.0f;
-    if (scales_fold<SH>(a.dh + (size_t)src * nb, nb))
-        pf_chains<BITS, 1, RT, true>(acc, rw, wv, ra, (uint32_t)src * I, rd, (uint32_t)src * nb * 4u, nb, h);
+    for (int r = 0; r < 16; ++r) acc[0][r] = 0.0f;
+    if (scales_fold<ST::SHIFT>(a.dh + (size_t)col.slot * nb, nb))
+        pf_run<BITS, 1, true>(acc, lds, src, col_voff, col_doff, active);
     else
-        pf_chains<BITS, 1, RT, false>(acc, rw, wv, ra, (uint32_t)src * I, rd, (uint32_t)src * nb * 4u, nb, h);
-    if (!live) return;
+        pf_run<BITS, 1, false>(acc, lds, src, col_voff, col_doff, active);
+    if (!active || !col.live) return;
+    const float *sd = reinterpret_cast<const float *>(blob + BL.s_down) + r0;
+    float *yrow = a.Y + (size_t)col.slot * H + r0;
 #pragma unroll
-    for (int t = 0; t < RT; ++t) {
-        const int rt0 = r0 + 32 * t;
-        const float *sd = reinterpret_cast<const float *>(blob + BL.s_down) + rt0;
-        float *yrow = a.Y + (size_t)slot * H + rt0;
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const int rr = 8 * g + 4 * h;
-            f32x4 v;
-            v.x = acc[0][t][4 * g + 0] * sd[rr + 0];
-            v.y = acc[0][t][4 * g + 1] * sd[rr + 1];
-            v.z = acc[0][t][4 * g + 2] * sd[rr + 2];
-            v.w = acc[0][t][4 * g + 3] * sd[rr + 3];
-            *reinterpret_cast<f32x4 *>(yrow + rr) = v;
-        }
+    for (int g = 0; g < 4; ++g) {
+        const int rr = 8 * g + 4 * h;
+        f32x4 v;
+        v.x = acc[0][4 * g + 0] * sd[rr + 0];
+        v.y = acc[0][4 * g + 1] * sd[rr + 1];
+        v.z = acc[0][4 * g + 2] * sd[rr + 2];
+        v.w = acc[0][4 * g + 3] * sd[rr + 3];
+        *reinterpret_cast<f32x4 *>(yrow + rr) = v;
     }
 }
 
@@ -454,18 +509,14 @@ hipError_t launch_group(const int32_t *idx, int S, int K, int E, int n_shared, u
 
 template <int BITS>
 static hipError_t pf_gateup_bits(const FwdArgs &a, const int32_t *tiles, hipStream_t st) {
-    const int ty = pf_tile_bound(a.S, a.K, a.E, a.n_shared);
-    if (a.I % 64 == 0)
-        return launch(k_pf_gateup<BITS, 2>, dim3((a.I + 255) / 256, ty), dim3(PF_T), 0, st, a, tiles);
-    return launch(k_pf_gateup<BITS, 1>, dim3((a.I + 127) / 128, ty), dim3(PF_T), 0, st, a, tiles);
+    const dim3 grid((a.I + PF_ROWS - 1) / PF_ROWS, pf_tile_bound(a.S, a.K, a.E, a.n_shared));
+    return launch(k_pf_gateup<BITS>, grid, dim3(PF_T), 0, st, a, tiles);
 }
 
 template <int BITS>
 static hipError_t pf_down_bits(const FwdArgs &a, const int32_t *tiles, hipStream_t st) {
-    const int ty = pf_tile_bound(a.S, a.K, a.E, a.n_shared);
-    if (a.H % 64 == 0)
-        return launch(k_pf_down<BITS, 2>, dim3((a.H + 255) / 256, ty), dim3(PF_T), 0, st, a, tiles);
-    return launch(k_pf_down<BITS, 1>, dim3((a.H + 127) / 128, ty), dim3(PF_T), 0, st, a, tiles);
+    const dim3 grid((a.H + PF_ROWS - 1) / PF_ROWS, pf_tile_bound(a.S, a.K, a.E, a.n_shared));
+    return launch(k_pf_down<BITS>, grid, dim3(PF_T), 0, st, a, tiles);
 }
 
 hipError_t launch_pf_gateup(const FwdArgs &a, const int32_t *tiles, int bits, hipStream_t st) {

@@ -372,33 +372,37 @@ def layer_inputs(seed: int, layer: int, spec: LayerSpec, S: int, x_stream: int =
     }
 
 
-def zipf_target_logits(seed: int, layer: int, spec: LayerSpec, S: int, exponent: float = 1.1) -> np.ndarray:
+def zipf_target_logits(seed: int, layer: int, spec: LayerSpec, S: int, exponent: float = 1.1,
+                       batch: int = 0) -> np.ndarray:
     """Target router logits [S, E] (f64) for a Zipf-skewed prefill batch.
 
     Expert popularity p_e is proportional to rank^-exponent, the ranks being
     a seeded permutation of the expert ids; token t's targets are
     log p + Gumbel(0, 1) noise, so that the top-K of a row is a draw of K
     experts without replacement with probabilities proportional to p
-    (the Gumbel-top-k construction)."""
+    (the Gumbel-top-k construction).  `batch` selects an independent draw of
+    the noise (same popularity)."""
     E = spec.n_experts
     perm = np.argsort(uniform01(stream_key(seed, K_ROUTING, layer, 200), E), kind="stable")
     rank = np.empty(E, np.int64)
     rank[perm] = np.arange(1, E + 1)
     logp = -exponent * np.log(rank.astype(np.float64))
     logp -= np.log(np.sum(np.exp(logp)))
-    u = uniform01(stream_key(seed, K_ROUTING, layer, 201), S * E).reshape(S, E)
+    u = uniform01(stream_key(seed, K_ROUTING, layer, 201, batch), S * E).reshape(S, E)
     u = np.clip(u, 1e-300, 1.0 - 1e-16)
     gumbel = -np.log(-np.log(u))
     return logp[None, :] + gumbel
 
 
-def prefill_hidden_states(seed: int, layer: int, spec: LayerSpec, S: int, exponent: float = 1.1) -> np.ndarray:
+def prefill_hidden_states(seed: int, layer: int, spec: LayerSpec, S: int, exponent: float = 1.1,
+                          batch: int = 0) -> np.ndarray:
     """Hidden states [S, H] f32 whose router logits are the Zipf targets of
     zipf_target_logits (pseudo-inverse construction of
     shaped_hidden_states; with zero router bias the sigmoid router then
     selects the Gumbel-top-K)."""
     W = router_weights(seed, layer, spec)
-    return shaped_hidden_states(W, zipf_target_logits(seed, layer, spec, S, exponent), seed, layer, stream=7)
+    return shaped_hidden_states(W, zipf_target_logits(seed, layer, spec, S, exponent, batch), seed, layer,
+                                stream=7 + batch)
 
 
 def verify_hidden_states(seed: int, layer: int, spec: LayerSpec, S: int, union_frac: float = 0.6) -> np.ndarray:
