@@ -145,9 +145,10 @@ __global__ __launch_bounds__(1024) void k_group(const int32_t *__restrict__ idx,
 // per row (coalesced, every byte fetched once per workgroup) into registers
 // while the previous stage is computed from LDS, then written to LDS.
 //
-// LDS holds 16-byte pieces with their index xor-ed with the row (or token)
-// index mod 8, so that the 8 lanes of a read phase hit 8 different 16-byte
-// bank groups.
+// LDS rows (weight rows, activation vectors) are padded by 16 bytes, so the
+// 16-byte pieces that 8 consecutive rows read at one block offset fall on 8
+// different 16-byte bank groups and every block offset is an immediate.
+// Scales are stored block-major, one word per column.
 constexpr int PF_ROWS = 128;
 
 template <int BITS, int NM>
@@ -158,49 +159,28 @@ struct PfStage {
     static constexpr int W_CHUNKS = NM * PF_ROWS * WPIECES / PF_T;   // per thread
     static constexpr int A_CHUNKS = 32 * APIECES / PF_T;             // per thread (1, 2, 4)
     static constexpr int D_WORDS = (32 * C + PF_T - 1) / PF_T;       // per thread (1, 1, 2)
-    static constexpr int W_BYTES = NM * PF_ROWS * 128;
-    static constexpr int A_BYTES = 32 * 32 * C;
+    static constexpr int WS = 128 + 16;           // LDS bytes of a weight row
+    static constexpr int AS = 32 * C + 16;        // LDS bytes of an activation vector
+    static constexpr int W_BYTES = NM * PF_ROWS * WS;
+    static constexpr int A_BYTES = 32 * AS;
     static constexpr int D_BYTES = 32 * C * 4;
     static constexpr int LDS = W_BYTES + A_BYTES + D_BYTES;
     static constexpr int SHIFT = BITS == 8 ? 0 : (BITS == 4 ? 4 : 6);
 };
 
-__device__ __forceinline__ int swz(int piece, int row) { return piece ^ (row & 7); }
-
 // Weight operand of block j of the stage for lane half h, from the row's
-// 128 LDS bytes.  The 16 codes of lane half h, times 2^SHIFT as signed
-// bytes: int8 codes 16 h .. 16 h + 15; int4 the low nibbles (h = 0, codes
-// 0 .. 15) or high nibbles (h = 1, codes 16 .. 31) of the block's 16 bytes;
-// int2 fields 2 h and 2 h + 1 of its 8 bytes (codes 16 h .. 16 h + 15).
-template <int BITS>
-__device__ __forceinline__ i32x4 lds_weight(const uint8_t *row_lds, int row, int j, int h);
-template <>
-__device__ __forceinline__ i32x4 lds_weight<8>(const uint8_t *row_lds, int row, int j, int h) {
-    return *reinterpret_cast<const i32x4 *>(row_lds + 16 * swz(2 * j + h, row));
-}
-template <>
-__device__ __forceinline__ i32x4 lds_weight<4>(const uint8_t *row_lds, int row, int j, int h) {
-    const u32x4 w = *reinterpret_cast<const u32x4 *>(row_lds + 16 * swz(j, row));
-    const int s = 4 - 4 * h;
-    i32x4 o;
-    o.x = (int)((w.x << s) & 0xF0F0F0F0u);
-    o.y = (int)((w.y << s) & 0xF0F0F0F0u);
-    o.z = (int)((w.z << s) & 0xF0F0F0F0u);
-    o.w = (int)((w.w << s) & 0xF0F0F0F0u);
-    return o;
-}
-template <>
-__device__ __forceinline__ i32x4 lds_weight<2>(const uint8_t *row_lds, int row, int j, int h) {
-    const u32x2 w = *reinterpret_cast<const u32x2 *>(row_lds + 16 * swz(j >> 1, row) + 8 * (j & 1));
-    const int s0 = 6 - 4 * h, s1 = 4 - 4 * h;  // fields 2 h and 2 h + 1 to bits 6-7
-    i32x4 o;
-    o.x = (int)((w.x << s0) & 0xC0C0C0C0u);
-    o.y = (int)((w.y << s0) & 0xC0C0C0C0u);
-    o.z = (int)((w.x << s1) & 0xC0C0C0C0u);
-    o.w = (int)((w.y << s1) & 0xC0C0C0C0u);
-    return o;
-}
-
+// LDS bytes (lds_raw, unpack_raw below): 16 codes of the block, times
+// 2^SHIFT, as signed bytes.  Inside
+// a block the order of the 32 products is free (their sum is exact), so a
+// lane half may take any 16 codes as long as its activation operand holds
+// the matching activation codes in the same order:
+//   int8: codes 16 h .. 16 h + 15 (bytes 16 h .. 16 h + 15), as they are;
+//   int4: the low nibbles of bytes 8 h .. 8 h + 7 (codes 8 h .. 8 h + 7),
+//         then their high nibbles (codes 16 + 8 h ..), each masked into the
+//         top of a byte (16 * code); the activations of a block are stored
+//         in LDS in the order 0-7, 16-23, 8-15, 24-31 to match;
+//   int2: fields 2 h and 2 h + 1 of the block's 8 bytes (codes 16 h ..
+//         16 h + 15), shifted into the top two bits (64 * code).
 // The tile of workgroup row blockIdx.y: unit, first pair, pairs.
 struct Tile {
     int u, p_first, n;
@@ -212,13 +192,24 @@ __device__ __forceinline__ int slot_token(int slot, int P, int K) { return slot 
 // lane of the wave (true unless some scale lies within 2^SHIFT of the
 // denormal range).  Then d * 2^-SHIFT times the 2^SHIFT-scaled sum is the
 // same product as d times the true sum, and the chain needs no shift.
+// A scale that is 0 or at least 2^-120 qualifies (for SHIFT <= 6 its
+// product with 2^-SHIFT is a normal number or 0); smaller ones take the
+// shifting path, which is exact for every scale.
 template <int SHIFT>
 __device__ __forceinline__ bool scales_fold(const float *d, int nb) {
     if (SHIFT == 0) return true;
+    constexpr float LOW = 0x1p-120f;
     bool ok = true;
-    for (int b = 0; b < nb; ++b) {
-        const float v = d[b];
-        ok = ok && (v * (1.0f / (float)(1 << SHIFT))) * (float)(1 << SHIFT) == v;
+    if ((nb & 3) == 0 && (reinterpret_cast<uintptr_t>(d) & 15) == 0) {
+        const f32x4 *v4 = reinterpret_cast<const f32x4 *>(d);
+#pragma unroll 8
+        for (int b = 0; b < nb / 4; ++b) {
+            const f32x4 v = v4[b];
+            ok = ok && (v.x == 0.0f || v.x >= LOW) && (v.y == 0.0f || v.y >= LOW) && (v.z == 0.0f || v.z >= LOW) &&
+                 (v.w == 0.0f || v.w >= LOW);
+        }
+    } else {
+        for (int b = 0; b < nb; ++b) ok = ok && (d[b] == 0.0f || d[b] >= LOW);
     }
     return __builtin_amdgcn_ballot_w64(!ok) == 0;
 }
@@ -255,7 +246,8 @@ __device__ __forceinline__ void pf_load(PfRegs<BITS, NM> &R, const PfSrc<NM> &sr
         const int m = i / PER_M, row = ((i % PER_M) * PF_T + tid) / 8, piece = tid % 8;
         const int r = min(src.row0 + row, src.n_rows - 1);
         const uint32_t off = src.mat[m] + (uint32_t)r * src.rb + 128u * stage + 16u * piece;
-        R.w[i] = __builtin_amdgcn_raw_buffer_load_b128(src.rw, off, 0, BUF_NT);
+        // default cache policy: the tiles of one expert share these lines in L2
+        R.w[i] = __builtin_amdgcn_raw_buffer_load_b128(src.rw, off, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < ST::A_CHUNKS; ++i) {
@@ -271,7 +263,8 @@ __device__ __forceinline__ void pf_load(PfRegs<BITS, NM> &R, const PfSrc<NM> &sr
     }
 }
 
-template <int BITS, int NM>
+// FOLD: the scales are stored times 2^-SHIFT.
+template <int BITS, int NM, bool FOLD>
 __device__ __forceinline__ void pf_store(const PfRegs<BITS, NM> &R, uint8_t *lds) {
     using ST = PfStage<BITS, NM>;
     const int tid = threadIdx.x;
@@ -279,20 +272,105 @@ __device__ __forceinline__ void pf_store(const PfRegs<BITS, NM> &R, uint8_t *lds
     for (int i = 0; i < ST::W_CHUNKS; ++i) {
         const int g = i * PF_T + tid;
         const int mrow = g / 8, piece = g % 8;  // row index over all matrices
-        *reinterpret_cast<u32x4 *>(lds + 128 * mrow + 16 * swz(piece, mrow)) = R.w[i];
+        *reinterpret_cast<u32x4 *>(lds + ST::WS * mrow + 16 * piece) = R.w[i];
     }
     uint8_t *la = lds + ST::W_BYTES;
 #pragma unroll
     for (int i = 0; i < ST::A_CHUNKS; ++i) {
         const int g = i * PF_T + tid;
         const int col = g / ST::APIECES, piece = g % ST::APIECES;
-        *reinterpret_cast<u32x4 *>(la + 32 * ST::C * col + 16 * swz(piece, col)) = R.a[i];
+        uint8_t *dst = la + ST::AS * col + 16 * piece;
+        if (BITS == 4) {
+            // bytes 8 k .. 8 k + 7 of a block go to 8 (k / 2) + 16 (k % 2)
+            uint8_t *blk = la + ST::AS * col + 32 * (piece >> 1) + 8 * (piece & 1);
+            *reinterpret_cast<u32x2 *>(blk) = u32x2{R.a[i].x, R.a[i].y};
+            *reinterpret_cast<u32x2 *>(blk + 16) = u32x2{R.a[i].z, R.a[i].w};
+        } else {
+            *reinterpret_cast<u32x4 *>(dst) = R.a[i];
+        }
     }
-    uint32_t *ld = reinterpret_cast<uint32_t *>(lds + ST::W_BYTES + ST::A_BYTES);
+    float *ld = reinterpret_cast<float *>(lds + ST::W_BYTES + ST::A_BYTES);
 #pragma unroll
     for (int i = 0; i < ST::D_WORDS; ++i) {
         const int g = i * PF_T + tid;
-        if (g < 32 * ST::C) ld[g] = R.d[i];
+        const float d = __builtin_bit_cast(float, R.d[i]);
+        if (g < 32 * ST::C) ld[32 * (g % ST::C) + g / ST::C] = FOLD ? d * (1.0f / (float)(1 << ST::SHIFT)) : d;
+    }
+}
+
+// Raw LDS words of a block's weight operand (8 or 16 bytes of the row).
+template <int BITS>
+struct RawW {
+    typedef u32x2 T;
+};
+template <>
+struct RawW<8> {
+    typedef u32x4 T;
+};
+
+template <int BITS>
+__device__ __forceinline__ typename RawW<BITS>::T lds_raw(const uint8_t *row_lds, int j, int h) {
+    if constexpr (BITS == 8) return *reinterpret_cast<const u32x4 *>(row_lds + 32 * j + 16 * h);
+    else if constexpr (BITS == 4) return *reinterpret_cast<const u32x2 *>(row_lds + 16 * j + 8 * h);
+    else return *reinterpret_cast<const u32x2 *>(row_lds + 8 * j);
+}
+
+// The operand from the raw words (see lds_weight).
+template <int BITS>
+__device__ __forceinline__ i32x4 unpack_raw(typename RawW<BITS>::T w, int h) {
+    i32x4 o;
+    if constexpr (BITS == 8) {
+        o = i32x4{(int)w.x, (int)w.y, (int)w.z, (int)w.w};
+    } else if constexpr (BITS == 4) {
+        o.x = (int)((w.x << 4) & 0xF0F0F0F0u);
+        o.y = (int)((w.y << 4) & 0xF0F0F0F0u);
+        o.z = (int)(w.x & 0xF0F0F0F0u);
+        o.w = (int)(w.y & 0xF0F0F0F0u);
+    } else {
+        const int s0 = 6 - 4 * h, s1 = 4 - 4 * h;
+        o.x = (int)((w.x << s0) & 0xC0C0C0C0u);
+        o.y = (int)((w.y << s0) & 0xC0C0C0C0u);
+        o.z = (int)((w.x << s1) & 0xC0C0C0C0u);
+        o.w = (int)((w.y << s1) & 0xC0C0C0C0u);
+    }
+    return o;
+}
+
+// Blocks 0 .. nblk - 1 of a stage in LDS (all C of them when FULL).  The
+// raw operands of block j + 1 are read before the chains of block j and
+// unpacked after them, so the LDS latency overlaps the chains.
+template <int BITS, int NM, bool FOLD, int C, bool FULL>
+__device__ __forceinline__ void pf_blocks(float (&acc)[NM][16], const uint8_t *lw, const uint8_t *la,
+                                          const float *ld, int h, int nblk) {
+    using ST = PfStage<BITS, NM>;
+    constexpr int SH = ST::SHIFT;
+    typename RawW<BITS>::T wr[NM];
+    i32x4 xa;
+    float da;
+#pragma unroll
+    for (int m = 0; m < NM; ++m) wr[m] = lds_raw<BITS>(lw + m * PF_ROWS * ST::WS, 0, h);
+    xa = *reinterpret_cast<const i32x4 *>(la);
+    da = ld[0];
+#pragma unroll
+    for (int j = 0; j < C; ++j) {
+        if (!FULL && j >= nblk) break;
+        i32x16 c[NM];
+#pragma unroll
+        for (int m = 0; m < NM; ++m) c[m] = mfma_i8_32x32x32(unpack_raw<BITS>(wr[m], h), xa);
+        const float d = da;
+        if (j + 1 < C && (FULL || j + 1 < nblk)) {
+#pragma unroll
+            for (int m = 0; m < NM; ++m) wr[m] = lds_raw<BITS>(lw + m * PF_ROWS * ST::WS, j + 1, h);
+            xa = *reinterpret_cast<const i32x4 *>(la + 32 * (j + 1));
+            da = ld[32 * (j + 1)];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int m = 0; m < NM; ++m)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                acc[m][r] = __builtin_fmaf(d, (float)(FOLD ? c[m][r] : c[m][r] >> SH), acc[m][r]);
+        __builtin_amdgcn_sched_barrier(0);
     }
 }
 
@@ -308,30 +386,32 @@ __device__ __forceinline__ void pf_run(float (&acc)[NM][16], uint8_t *lds, const
     const int n_stages = (src.nb + ST::C - 1) / ST::C;
     PfRegs<BITS, NM> R;
     pf_load<BITS, NM>(R, src, col_voff, col_doff, 0);
-    const uint8_t *la = lds + ST::W_BYTES + 32 * ST::C * n;
-    const float *ld = reinterpret_cast<const float *>(lds + ST::W_BYTES + ST::A_BYTES) + ST::C * n;
+    const uint8_t *la = lds + ST::W_BYTES + ST::AS * n + 16 * h;
+    const float *ld = reinterpret_cast<const float *>(lds + ST::W_BYTES + ST::A_BYTES) + n;
+    const uint8_t *lw = lds + ST::WS * (32 * wave + n);
     for (int s = 0; s < n_stages; ++s) {
         if (s > 0) __syncthreads();  // every wave is done with the previous stage
-        pf_store<BITS, NM>(R, lds);
+        pf_store<BITS, NM, FOLD>(R, lds);
         __syncthreads();
         if (s + 1 < n_stages) pf_load<BITS, NM>(R, src, col_voff, col_doff, s + 1);
         if (!active) continue;
         const int nblk = min(ST::C, src.nb - ST::C * s);
-        for (int j = 0; j < nblk; ++j) {
-            const i32x4 xb = *reinterpret_cast<const i32x4 *>(la + 16 * swz(2 * j + h, n));
-            const float d = ld[j];
-            const float ds = FOLD ? d * (1.0f / (float)(1 << SH)) : d;
-            i32x16 c[NM];
+        if (nblk == ST::C) {
+            pf_blocks<BITS, NM, FOLD, ST::C, true>(acc, lw, la, ld, h, ST::C);
+        } else {
+            // the short last stage of a K that is no multiple of the stage
+            for (int j = 0; j < nblk; ++j) {
+                const i32x4 xb = *reinterpret_cast<const i32x4 *>(la + 32 * j);
+                const float d = ld[32 * j];
 #pragma unroll
-            for (int m = 0; m < NM; ++m) {
-                const int row = m * PF_ROWS + 32 * wave + n;
-                c[m] = mfma_i8_32x32x32(lds_weight<BITS>(lds + 128 * row, row, j, h), xb);
+                for (int m = 0; m < NM; ++m) {
+                    const i32x16 c = mfma_i8_32x32x32(
+                        unpack_raw<BITS>(lds_raw<BITS>(lw + m * PF_ROWS * ST::WS, j, h), h), xb);
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        acc[m][r] = __builtin_fmaf(d, (float)(FOLD ? c[r] : c[r] >> SH), acc[m][r]);
+                }
             }
-#pragma unroll
-            for (int m = 0; m < NM; ++m)
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    acc[m][r] = __builtin_fmaf(ds, (float)(FOLD ? c[m][r] : c[m][r] >> SH), acc[m][r]);
         }
     }
 }
@@ -354,7 +434,7 @@ __device__ __forceinline__ PfCols pf_col(const int32_t *pairs, const Tile &tl, i
 // Grid (ceil(I / PF_ROWS), tile bound).  Epilogue: row scales, SwiGLU and
 // Q8_0 over each wave's 32 rows (one block of h) for every live column.
 template <int BITS>
-__global__ __launch_bounds__(PF_T) void k_pf_gateup(const FwdArgs a, const int32_t *__restrict__ tiles) {
+__global__ __launch_bounds__(PF_T, 3) void k_pf_gateup(const FwdArgs a, const int32_t *__restrict__ tiles) {
     using ST = PfStage<BITS, 2>;
     __shared__ __attribute__((aligned(16))) uint8_t lds[ST::LDS];
     __shared__ uint32_t col_voff[32], col_doff[32];
@@ -435,7 +515,7 @@ __global__ __launch_bounds__(PF_T) void k_pf_gateup(const FwdArgs a, const int32
 // Grid (ceil(H / PF_ROWS), tile bound): Y[slot][row] = s_d[row] * chain over
 // the I / 32 blocks of Q8_0(h) of the slot.
 template <int BITS>
-__global__ __launch_bounds__(PF_T) void k_pf_down(const FwdArgs a, const int32_t *__restrict__ tiles) {
+__global__ __launch_bounds__(PF_T, 4) void k_pf_down(const FwdArgs a, const int32_t *__restrict__ tiles) {
     using ST = PfStage<BITS, 1>;
     __shared__ __attribute__((aligned(16))) uint8_t lds[ST::LDS];
     __shared__ uint32_t col_voff[32], col_doff[32];
