@@ -16,6 +16,10 @@ whose routing has a Zipf(1.1) skew over expert popularity (the grouped
 int8 matrix-core kernels); its roofline is the gate/up kernel's int8
 TOPS against the MI355X dense int8 peak.
 
+--workload verify times the speculative-verify batch: 4 tokens per step
+routed jointly through int8 layers (12 resident, about 116 GB), the tokens
+sharing about 40% of their experts.
+
 --copy-calibration MB runs only a device-to-device copy of MB megabytes
 (torch copy_) ten times: the reference for scaling rocprofv3's
 FETCH_SIZE / WRITE_SIZE counters to bytes.
@@ -46,7 +50,7 @@ def log(*a):
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--workload", choices=("decode", "prefill"), default="decode")
+    ap.add_argument("--workload", choices=("decode", "verify", "prefill"), default="decode")
     ap.add_argument("--steps", type=int, default=None, help="timed steps (decode 2400, prefill 200)")
     ap.add_argument("--warmup", type=int, default=None, help="untimed steps (decode 240, prefill 20)")
     ap.add_argument("--tokens", type=int, default=2048, help="tokens per prefill step")
@@ -64,9 +68,9 @@ def parse():
                          "one or the grouped matrix-core kernels")
     a = ap.parse_args()
     if a.steps is None:
-        a.steps = 2400 if a.workload == "decode" else 200
+        a.steps = {"decode": 2400, "verify": 1200, "prefill": 200}[a.workload]
     if a.warmup is None:
-        a.warmup = 240 if a.workload == "decode" else 20
+        a.warmup = {"decode": 240, "verify": 120, "prefill": 20}[a.workload]
     return a
 
 
@@ -104,7 +108,9 @@ def main():
     if args.workload == "prefill":
         run_prefill(args, q, synth)
         return
-    spec = synth.GLM
+    verify = args.workload == "verify"
+    spec = synth.GLM_INT8 if verify else synth.GLM
+    S = 4 if verify else 1  # tokens per step
     dims = q.make_dims(spec)
     H, E = spec.hidden, spec.n_experts
     L = args.layers
@@ -133,30 +139,36 @@ def main():
         d = synth.layer_inputs(args.seed, l, spec, 1)
         table = torch.tensor([dev.data_ptr() + e * bb for e in range(E)], dtype=torch.int64, device="cuda")
         layers.append({"blobs": dev, "table": table, "shared": dev.data_ptr() + E * bb,
-                       "router_w": torch.from_numpy(d["router_w"]).cuda(),
+                       "router_w": torch.from_numpy(d["router_w"]).cuda(), "router_w_host": d["router_w"],
                        "bias": torch.from_numpy(d["bias"]).cuda()})
         log(f"layer {l}: {nblob} experts generated and staged ({time.time() - t0:.1f} s)")
     torch.cuda.synchronize()
     del staging
     G = max(1, min(args.graph_steps, args.steps))
-    xs_host = synth.hidden_states(args.seed, 1000, G, H)
+    if verify:
+        # step s: 4 tokens of layer s mod L sharing experts (independent draws per step)
+        xs_host = np.concatenate([synth.verify_hidden_states(args.seed, s % L, spec, S, batch=1 + s // L,
+                                                             W=layers[s % L]["router_w_host"])
+                                  for s in range(G)])
+    else:
+        xs_host = synth.hidden_states(args.seed, 1000, G, H)
     xs = torch.from_numpy(xs_host).cuda()
-    ws = torch.zeros(q.coli_moe_workspace_bytes(dims, 1), dtype=torch.uint8, device="cuda")
-    idx = torch.empty((G, spec.top_k), dtype=torch.int32, device="cuda")
-    wts = torch.empty((G, spec.top_k), dtype=torch.float32, device="cuda")
-    out = torch.empty((G, H), dtype=torch.float32, device="cuda")
+    ws = torch.zeros(q.coli_moe_workspace_bytes(dims, S), dtype=torch.uint8, device="cuda")
+    idx = torch.empty((G * S, spec.top_k), dtype=torch.int32, device="cuda")
+    wts = torch.empty((G * S, spec.top_k), dtype=torch.float32, device="cuda")
+    out = torch.empty((G * S, H), dtype=torch.float32, device="cuda")
     log(f"setup done in {time.time() - t0:.1f} s; {torch.cuda.memory_allocated() / 1e9:.1f} GB allocated")
 
     def step(s):
         lay = layers[s % L]
-        x = xs[s:s + 1]
+        r = slice(s * S, (s + 1) * S)
+        x = xs[r]
         if args.path == "layer":
             q.coli_moe_layer(dims, x, lay["router_w"], lay["bias"], lay["table"], lay["shared"],
-                             idx[s:s + 1], wts[s:s + 1], out[s:s + 1], ws)
+                             idx[r], wts[r], out[r], ws)
         else:
-            q.coli_moe_route(dims, x, lay["router_w"], lay["bias"], idx[s:s + 1], wts[s:s + 1], ws)
-            q.coli_moe_forward(dims, x, idx[s:s + 1], wts[s:s + 1], lay["table"], lay["shared"],
-                               out[s:s + 1], ws)
+            q.coli_moe_route(dims, x, lay["router_w"], lay["bias"], idx[r], wts[r], ws)
+            q.coli_moe_forward(dims, x, idx[r], wts[r], lay["table"], lay["shared"], out[r], ws)
 
     # eager pass: correctness of the status word, kernel timing with HIP events
     for s in range(G):
@@ -193,19 +205,21 @@ def main():
     if rc != 0:
         raise RuntimeError(f"device status after replay {rc}: {q.coli_moe_last_error()}")
     ms_per_step = 1e3 * elapsed / steps
-    tokens_per_s = steps / elapsed
+    tokens_per_s = steps * S / elapsed
 
-    # algorithmic bytes: each token-layer reads W_r, the 8 routed experts and the shared one once
-    n_units = int(np.mean([len(set(r)) for r in routed])) + spec.n_shared
+    # algorithmic bytes: each step reads W_r and each unique expert of its
+    # tokens (8 routed + shared for one token) once
+    uniq = [len(set(routed[s * S:(s + 1) * S].ravel().tolist())) for s in range(G)]
+    n_units = float(np.mean(uniq)) + spec.n_shared
     lay_bytes = E * H * 4 + E * 4 + n_units * bb
     if "layer" in kernel_us:
-        dom, dom_kernel = "layer", "k_layer<4,1,1,24>"
+        dom, dom_kernel = "layer", "k_layer<%d,%d,1,24>" % (spec.wbits, S)
         dom_bytes = lay_bytes
     elif "forward_persistent" in kernel_us:
-        dom, dom_kernel = "forward_persistent", "k_layer<4,1,0,24>"
+        dom, dom_kernel = "forward_persistent", "k_layer<%d,%d,0,24>" % (spec.wbits, S)
         dom_bytes = n_units * bb
     else:
-        dom, dom_kernel = "gateup", "k_gateup<4,1>"
+        dom, dom_kernel = "gateup", "k_gateup<%d,%d>" % (spec.wbits, min(S, 4))
         dom_bytes = n_units * (2 * spec.inter * H * spec.wbits // 8 + 2 * spec.inter * 4)
     dom_us = kernel_us[dom]
     achieved = dom_bytes / (dom_us * 1e-6) / 1e9
@@ -221,14 +235,19 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "i8xi4->i32,f32",
+        "dtype": "i8xi8->i32,f32" if verify else "i8xi4->i32,f32",
         "data": "synthetic (seeded; GLM-5.2-shaped random-code experts)",
         "config": {
-            "workload": "GLM-5.2-shaped MoE decode layer, 1 token/step: hidden 6144, expert inter 2048, "
-                        "256 routed experts top-8 + 1 shared, int4 per-row-scaled weights (18.9 MB/expert), "
-                        "Q8_0 activations, fp32 router gate; 12 layers resident in HBM, step s uses layer s mod 12",
+            "workload": ("GLM-5.2-shaped speculative-verify batch, 4 tokens/step routed jointly (about 40% "
+                         "shared experts): hidden 6144, expert inter 2048, 256 routed experts top-8 + 1 shared, "
+                         "int8 per-row-scaled weights (37.8 MB/expert), Q8_0 activations, fp32 router gate; "
+                         f"{L} layers resident in HBM, step s uses layer s mod {L}") if verify else
+                        ("GLM-5.2-shaped MoE decode layer, 1 token/step: hidden 6144, expert inter 2048, "
+                         "256 routed experts top-8 + 1 shared, int4 per-row-scaled weights (18.9 MB/expert), "
+                         f"Q8_0 activations, fp32 router gate; {L} layers resident in HBM, step s uses layer "
+                         f"s mod {L}"),
             "layers_resident": L, "resident_gb": round(L * nblob * bb / 1e9, 1),
-            "tokens_per_step": 1, "graph_steps": G, "entry": args.path, "kernels": args.kernels,
+            "tokens_per_step": S, "graph_steps": G, "entry": args.path, "kernels": args.kernels,
         },
         "roofline": {
             "bound": "hbm", "kernel": dom_kernel,
@@ -243,7 +262,7 @@ def main():
     }
 
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(args, spec, xs_host, layers, L)
+        res["cpu_baseline"] = cpu_baseline(args, spec, xs_host, layers, L, S)
     print(json.dumps(res), flush=True)
 
 
@@ -366,9 +385,9 @@ def run_prefill(args, q, synth):
                         "median": float(np.median(counts[counts > 0])), "max": int(counts.max())},
         },
         "roofline": {
-            "bound": "mfma", "kernel": "k_pf_gateup<4,2>",
+            "bound": "mfma", "kernel": "k_pf_gateup<4>",
             "achieved": round(achieved, 1), "peak": INT8_PEAK_TOPS, "unit": "TOPS",
-            "frac": round(achieved / INT8_PEAK_TOPS, 4), "traffic": counted_traffic("k_pf_gateup<4,2>"),
+            "frac": round(achieved / INT8_PEAK_TOPS, 4), "traffic": counted_traffic("k_pf_gateup<4>"),
             "algorithmic_ops_per_launch": ops_gateup, "avg_launch_us": round(g_us, 3),
         },
         "layer_int8_tops": round(layer_tops, 1),
@@ -436,7 +455,7 @@ def counted_traffic(kernel):
     return None
 
 
-def cpu_baseline(args, spec, xs_host, layers, L):
+def cpu_baseline(args, spec, xs_host, layers, L, S=1):
     """The CPU oracle (plain single-threaded C) on a bounded sample: whole
     layer steps (route + 8 experts + shared + combine) of the same workload,
     as many as fit the time budget."""
@@ -446,7 +465,7 @@ def cpu_baseline(args, spec, xs_host, layers, L):
     import synth
     n, spent = 0, 0.0
     while spent < args.cpu_seconds and n < xs_host.shape[0]:
-        l = n % L
+        l = (n // S) % L
         d = synth.layer_inputs(args.seed, l, spec, 1)
         x = xs_host[n:n + 1]
         idx, w, _, _ = oracle.route(spec, x, d["router_w"], d["bias"])

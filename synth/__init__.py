@@ -405,22 +405,29 @@ def prefill_hidden_states(seed: int, layer: int, spec: LayerSpec, S: int, expone
                                 stream=7 + batch)
 
 
-def verify_hidden_states(seed: int, layer: int, spec: LayerSpec, S: int, union_frac: float = 0.6) -> np.ndarray:
+def verify_hidden_states(seed: int, layer: int, spec: LayerSpec, S: int, union_frac: float = 0.6,
+                         batch: int = 0, W: np.ndarray | None = None) -> np.ndarray:
     """Hidden states of S tokens that share experts: x_t = sqrt(rho) c +
     sqrt(1 - rho) n_t with a common direction c, rho bisected so that the
     top-K sets of the logits W_r x_t cover about union_frac * S * K distinct
     experts.  Uses float64 logits and a sort only (bias ignored); the realised
-    union of the actual router is reported by whoever routes these tokens."""
-    W = router_weights(seed, layer, spec).astype(np.float64)
+    union of the actual router is reported by whoever routes these tokens.
+    `batch` selects an independent draw; W (the layer's router gate) may be
+    passed to skip regenerating it."""
+    if W is None:
+        W = router_weights(seed, layer, spec)
+    W = W.astype(np.float64)
     H, K = spec.hidden, spec.top_k
-    c = normal(stream_key(seed, K_ROUTING, layer, 100), H)
-    n = normal(stream_key(seed, K_ROUTING, layer, 101), S * H).reshape(S, H)
+    extra = (batch,) if batch else ()
+    c = normal(stream_key(seed, K_ROUTING, layer, 100, *extra), H)
+    n = normal(stream_key(seed, K_ROUTING, layer, 101, *extra), S * H).reshape(S, H)
+    lc, ln = W @ c, n @ W.T
 
     def make(rho):
         return math.sqrt(rho) * c[None, :] + math.sqrt(1.0 - rho) * n
 
     def union(rho):
-        top = np.argsort(-(make(rho) @ W.T), axis=1, kind="stable")[:, :K]
+        top = np.argsort(-(math.sqrt(rho) * lc[None, :] + math.sqrt(1.0 - rho) * ln), axis=1, kind="stable")[:, :K]
         return len(set(top.ravel().tolist())) / (S * K)
 
     lo, hi = 0.0, 1.0
