@@ -20,6 +20,13 @@ TOPS against the MI355X dense int8 peak.
 routed jointly through int8 layers (12 resident, about 116 GB), the tokens
 sharing about 40% of their experts.
 
+--workload tiered streams GLM-5.2-shaped layers (75 by default, int4 or,
+with --tier-bits 2, int2) through a 48 GB HBM expert cache split into
+per-layer LRUs, the other experts staged from pinned host memory by
+hipMemcpyAsync on a side stream while the resident experts compute; one
+token per step through every layer, routed by a seeded trace in which each
+of the 8 slots reuses the previous step's expert with probability 0.6.
+
 --copy-calibration MB runs only a device-to-device copy of MB megabytes
 (torch copy_) ten times: the reference for scaling rocprofv3's
 FETCH_SIZE / WRITE_SIZE counters to bytes.
@@ -50,7 +57,12 @@ def log(*a):
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--workload", choices=("decode", "verify", "prefill"), default="decode")
+    ap.add_argument("--workload", choices=("decode", "verify", "prefill", "tiered"), default="decode")
+    ap.add_argument("--tier-bits", type=int, choices=(4, 2), default=4, help="tiered: expert width")
+    ap.add_argument("--tier-layers", type=int, default=75, help="tiered: layers streamed")
+    ap.add_argument("--host-layers", type=int, default=8,
+                    help="tiered: distinct layers of expert bytes in pinned host memory (reused cyclically)")
+    ap.add_argument("--cache-gb", type=float, default=48.0, help="tiered: HBM expert cache, split over the layers")
     ap.add_argument("--steps", type=int, default=None, help="timed steps (decode 2400, prefill 200)")
     ap.add_argument("--warmup", type=int, default=None, help="untimed steps (decode 240, prefill 20)")
     ap.add_argument("--tokens", type=int, default=2048, help="tokens per prefill step")
@@ -68,9 +80,9 @@ def parse():
                          "one or the grouped matrix-core kernels")
     a = ap.parse_args()
     if a.steps is None:
-        a.steps = {"decode": 2400, "verify": 1200, "prefill": 200}[a.workload]
+        a.steps = {"decode": 2400, "verify": 1200, "prefill": 200, "tiered": 64}[a.workload]
     if a.warmup is None:
-        a.warmup = {"decode": 240, "verify": 120, "prefill": 20}[a.workload]
+        a.warmup = {"decode": 240, "verify": 120, "prefill": 20, "tiered": 8}[a.workload]
     return a
 
 
@@ -107,6 +119,9 @@ def main():
     q.coli_moe_debug_force_path(PATHS[args.kernels])
     if args.workload == "prefill":
         run_prefill(args, q, synth)
+        return
+    if args.workload == "tiered":
+        run_tiered(args, q, synth)
         return
     verify = args.workload == "verify"
     spec = synth.GLM_INT8 if verify else synth.GLM
@@ -397,6 +412,163 @@ def run_prefill(args, q, synth):
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_prefill(args, spec, xs_host[0], d, host.numpy(), routed[0])
+    print(json.dumps(res), flush=True)
+
+
+PCIE_PEAK_GBS = 64.0  # PCIe Gen5 x16, one direction
+
+
+def run_tiered(args, q, synth):
+    """Tiered streaming decode: every step routes one token through all
+    layers; each layer's experts beyond its HBM slots come from pinned host
+    memory through coli_moe_stage_experts, the forward running the resident
+    experts first (pending mask) and the copied ones after the copy event."""
+    import numpy as np
+    import torch
+
+    from quantized_expert_ffn_amd.tier import ExpertTier
+
+    spec = synth.GLM if args.tier_bits == 4 else synth.GLM_INT2
+    dims = q.make_dims(spec)
+    L, HL = args.tier_layers, min(args.host_layers, args.tier_layers)
+    H, E, K = spec.hidden, spec.n_experts, spec.top_k
+    bb = spec.blob_bytes
+    spl = int(args.cache_gb * 1e9 // bb) // L
+    if spl < K:
+        raise SystemExit(f"{spl} cache slots per layer is fewer than top-{K}")
+    n_steps = args.warmup + args.steps
+    t0 = time.time()
+    host = torch.empty(HL * E * bb, dtype=torch.uint8, pin_memory=True)
+    hp = host.data_ptr()
+    for hl in range(HL):
+        for e in range(E):
+            synth.cdf_expert_into(hp + (hl * E + e) * bb, args.seed, hl, e, spec)
+    log(f"tiered: {HL} layers x {E} experts in pinned host memory ({HL * E * bb / 1e9:.1f} GB, "
+        f"{time.time() - t0:.1f} s)")
+    tmp = torch.empty(bb, dtype=torch.uint8, pin_memory=True)
+    shared = torch.empty(L * bb, dtype=torch.uint8, device="cuda")
+    for l in range(L):
+        synth.cdf_expert_into(tmp.data_ptr(), args.seed, l % HL, E, spec)
+        shared[l * bb:(l + 1) * bb].copy_(tmp)
+    cache = torch.empty(L * spl * bb, dtype=torch.uint8, device="cuda")
+    Ws, biases, xs = [], [], []
+    for l in range(L):
+        W = synth.router_weights(args.seed, l, spec)
+        trace = synth.reuse_trace(args.seed, l, spec, n_steps)
+        x = synth.shaped_hidden_states(W, synth.trace_target_logits(args.seed, l, spec, trace), args.seed, l,
+                                       stream=11)
+        Ws.append(torch.from_numpy(W).cuda())
+        biases.append(torch.from_numpy(synth.router_bias(args.seed, l, spec)).cuda())
+        xs.append(torch.from_numpy(x).cuda())
+    torch.cuda.synchronize()
+    log(f"tiered setup: {L} layers, {spl} HBM slots each ({L * spl * bb / 1e9:.1f} GB cache), "
+        f"{time.time() - t0:.1f} s")
+
+    cp = cache.data_ptr()
+    tier = ExpertTier(L, E, spl, bb, slot_addr=lambda l, s: cp + (l * spl + s) * bb,
+                      host_addr=lambda l, e: hp + ((l % HL) * E + e) * bb)
+    ws = torch.zeros(q.coli_moe_workspace_bytes(dims, 1), dtype=torch.uint8, device="cuda")
+    idx = torch.empty((1, K), dtype=torch.int32, device="cuda")
+    wts = torch.empty((1, K), dtype=torch.float32, device="cuda")
+    out = torch.empty((1, H), dtype=torch.float32, device="cuda")
+    idx_host = torch.empty((1, K), dtype=torch.int32, pin_memory=True)
+    R = 16
+    ring = torch.empty((R, E), dtype=torch.int64, pin_memory=True)
+    ring_ev = [None] * R
+    dev_tab = torch.zeros((L, E), dtype=torch.int64, device="cuda")
+    copy = torch.cuda.Stream()
+    comp = torch.cuda.current_stream()
+    got = torch.cuda.Event()
+    copies_timed = []
+    state = {"r": 0, "bytes": 0, "copies": 0, "layer_steps": 0}
+
+    def layer_step(s, l, timed):
+        q.coli_moe_route(dims, xs[l][s:s + 1], Ws[l], biases[l], idx, wts, ws)
+        idx_host.copy_(idx, non_blocking=True)
+        got.record(comp)
+        got.synchronize()
+        table, copies = tier.plan(l, idx_host[0].tolist())
+        ev = None
+        mask = None
+        if copies:
+            c0, c1, ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True), torch.cuda.Event()
+            copy.wait_stream(comp)
+            c0.record(copy)
+            q.coli_moe_stage_experts([c[1] for c in copies], [c[2] for c in copies], bb, copy, ev)
+            c1.record(copy)
+            mask = np.zeros(E, np.uint8)
+            mask[[c[0] for c in copies]] = 1
+            if timed:
+                copies_timed.append((c0, c1, len(copies)))
+                state["bytes"] += len(copies) * bb
+                state["copies"] += len(copies)
+        r = state["r"]
+        state["r"] = (r + 1) % R
+        if ring_ev[r] is not None:
+            ring_ev[r].synchronize()
+        ring[r].copy_(torch.tensor(table, dtype=torch.int64))
+        dev_tab[l].copy_(ring[r], non_blocking=True)
+        ring_ev[r] = torch.cuda.Event()
+        ring_ev[r].record(comp)
+        q.coli_moe_forward(dims, xs[l][s:s + 1], idx, wts, dev_tab[l], shared.data_ptr() + l * bb, out, ws,
+                           pending_mask=mask, pending_ready=ev)
+        if timed:
+            state["layer_steps"] += 1
+
+    for s in range(args.warmup):
+        for l in range(L):
+            layer_step(s, l, False)
+    torch.cuda.synchronize()
+    rc = q.coli_moe_status(ws)
+    if rc != 0:
+        raise RuntimeError(f"device status {rc}: {q.coli_moe_last_error()}")
+    h0, m0 = tier.hits, tier.misses
+    t1 = time.perf_counter()
+    for s in range(args.warmup, n_steps):
+        for l in range(L):
+            layer_step(s, l, True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t1
+    rc = q.coli_moe_status(ws)
+    if rc != 0:
+        raise RuntimeError(f"device status after the timed steps {rc}: {q.coli_moe_last_error()}")
+    hits, misses = tier.hits - h0, tier.misses - m0
+    copy_ms = sum(a.elapsed_time(b) for a, b, _ in copies_timed)
+    staged = state["bytes"]
+    copy_gbs = staged / (copy_ms * 1e-3) / 1e9 if copy_ms > 0 else 0.0
+    steps = args.steps
+    res = {
+        "metric": METRIC,
+        "value": round(steps / elapsed, 3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(1e3 * elapsed / steps, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8xi%d->i32,f32" % spec.wbits,
+        "data": "synthetic (seeded; GLM-5.2-shaped random-code experts, 60%-reuse routing trace)",
+        "config": {
+            "workload": f"tiered streaming decode: {L} GLM-5.2-shaped layers (int{spec.wbits}, "
+                        f"{bb / 1e6:.2f} MB/expert, {L * (E + 1) * bb / 1e9:.0f} GB in all), 1 token/step through "
+                        f"every layer, {args.cache_gb:g} GB HBM cache as {spl} LRU slots per layer, other experts "
+                        "in pinned host memory staged by hipMemcpyAsync on a side stream, shared experts resident",
+            "layers": L, "slots_per_layer": spl, "host_layers_distinct": HL,
+        },
+        "roofline": {
+            "bound": "pcie", "kernel": "coli_moe_stage_experts (hipMemcpyAsync host to device)",
+            "achieved": round(copy_gbs, 2), "peak": PCIE_PEAK_GBS, "unit": "GB/s",
+            "frac": round(copy_gbs / PCIE_PEAK_GBS, 4), "traffic": staged / max(1, len(copies_timed)),
+            "copy_batches": len(copies_timed), "copy_busy_ms": round(copy_ms, 3),
+        },
+        "staged_gb_per_token": round(staged / steps / 1e9, 3),
+        "pcie_gbs_wall": round(staged / elapsed / 1e9, 2),
+        "hit_rate": round(hits / max(1, hits + misses), 4),
+        "misses_per_layer_step": round(misses / max(1, state["layer_steps"]), 3),
+        "layer_step_ms": round(1e3 * elapsed / max(1, state["layer_steps"]), 4),
+    }
     print(json.dumps(res), flush=True)
 
 

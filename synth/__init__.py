@@ -332,19 +332,22 @@ def hidden_states(seed: int, layer: int, S: int, H: int, stream: int = 0) -> np.
 
 def shaped_hidden_states(W_r: np.ndarray, target_logits: np.ndarray, seed: int, layer: int,
                          stream: int = 0) -> np.ndarray:
-    """x [S, H] with W_r @ x_t = target_logits[t] (least squares, f64) plus
-    N(0,1) noise projected onto the null space of W_r; stored as f32.
+    """x [S, H] with W_r @ x_t = target_logits[t] (the minimum-norm solution,
+    f64) plus N(0,1) noise projected onto the null space of W_r; stored as
+    f32.
 
     Lets a test or benchmark fix which experts a token prefers without
     evaluating the layer's router: with zero bias the sigmoid is monotone,
-    so the top-k of the target logits is the intended selection."""
+    so the top-k of the target logits is the intended selection.  W_r has
+    full row rank (E < H, Gaussian), so the pseudo-inverse is
+    W^T (W W^T)^-1, applied through one E x E solve."""
     W = W_r.astype(np.float64)
     S = target_logits.shape[0]
     H = W.shape[1]
     z = normal(stream_key(seed, K_ROUTING, layer, stream), S * H).reshape(S, H)
-    pinv = np.linalg.pinv(W)                     # [H, E]
-    x = target_logits.astype(np.float64) @ pinv.T
-    x += z - (z @ W.T) @ pinv.T
+    G = W @ W.T                                  # [E, E]
+    rhs = target_logits.astype(np.float64).T - W @ z.T
+    x = z + (W.T @ np.linalg.solve(G, rhs)).T   # z - P z + W^+ t
     return x.astype(np.float32)
 
 
@@ -403,6 +406,38 @@ def prefill_hidden_states(seed: int, layer: int, spec: LayerSpec, S: int, expone
     W = router_weights(seed, layer, spec)
     return shaped_hidden_states(W, zipf_target_logits(seed, layer, spec, S, exponent, batch), seed, layer,
                                 stream=7 + batch)
+
+
+def reuse_trace(seed: int, layer: int, spec: LayerSpec, steps: int, reuse: float = 0.6) -> np.ndarray:
+    """Expert sets [steps, K] of one layer over decode steps: slot k keeps the
+    previous step's expert of slot k with probability `reuse` (when no
+    earlier slot of the step took it), else draws uniformly from the experts
+    outside the previous step's set and the step's earlier picks."""
+    E, K = spec.n_experts, spec.top_k
+    u = uniform01(stream_key(seed, K_ROUTING, layer, 300), steps * K * 2).reshape(steps, K, 2)
+    out = np.zeros((steps, K), np.int64)
+    prev: list[int] = []
+    for s in range(steps):
+        cur: list[int] = []
+        for k in range(K):
+            if prev and u[s, k, 0] < reuse and prev[k] not in cur:
+                cur.append(prev[k])
+                continue
+            pool = [e for e in range(E) if e not in cur and e not in prev]
+            cur.append(pool[int(u[s, k, 1] * len(pool))])
+        out[s] = cur
+        prev = cur
+    return out
+
+
+def trace_target_logits(seed: int, layer: int, spec: LayerSpec, trace: np.ndarray) -> np.ndarray:
+    """Target logits [steps, E] whose top-K is the trace's set: the set's
+    experts at 4.0, 3.75, ... in slot order, the others N(-2, 0.5)."""
+    steps, K = trace.shape
+    t = -2.0 + 0.5 * normal(stream_key(seed, K_ROUTING, layer, 301), steps * spec.n_experts).reshape(steps, -1)
+    for k in range(K):
+        t[np.arange(steps), trace[:, k]] = 4.0 - 0.25 * k
+    return t
 
 
 def verify_hidden_states(seed: int, layer: int, spec: LayerSpec, S: int, union_frac: float = 0.6,
