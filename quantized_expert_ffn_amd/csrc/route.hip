@@ -110,12 +110,46 @@ __global__ __launch_bounds__(64) void k_route_fused(const RouteArgs r) {
     const uint8_t **btab = reinterpret_cast<const uint8_t **>(smem + a16(T.total + 4 * (size_t)P));
     if (lane == 0) st_dev(&r.sync[t], 0u);
     if (S == 1) {
-        // one token: its selection is the whole routing; no second count
+        // One token: its selection is the whole routing.  The unit table is
+        // written straight from the selection: unit j is the selected expert
+        // of rank j in ascending id (its one pair is slot k, the lane that
+        // selected it), then the shared expert with slot K.
+        const UnitTable U = unit_table(1, K, E);
+        int32_t *tab = reinterpret_cast<int32_t *>(r.units);
+        const uint8_t **ublob = reinterpret_cast<const uint8_t **>(r.units + U.ublob);
+        int rank = 0;
+        for (int j = 0; j < K; ++j) rank += __builtin_amdgcn_readlane(si, j) < si ? 1 : 0;
+        // blob pointer of expert si: prefetched by lane si % 64 in bl[si / 64]
+        const uint8_t *mine = nullptr;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const uint8_t *v = reinterpret_cast<const uint8_t *>(
+                __shfl(reinterpret_cast<uintptr_t>(bl[m]), si & 63, 64));
+            if ((si >> 6) == m) mine = v;
+        }
         if (lane < K) {
             r.idx_out[lane] = si;
             r.w_out[lane] = sw;
-            idx_l[lane] = si;
+            tab[U.uexp + rank] = si;
+            tab[U.uoff + rank] = rank;
+            tab[U.pairs + rank] = lane;
+            ublob[rank] = si < 256 ? mine : r.blobs[si];
         }
+        if (lane == 0) {
+            const int ns = r.n_shared;
+            tab[0] = K + ns;
+            tab[1] = K;
+            tab[2] = K;
+            tab[3] = 0;
+            if (ns) {
+                tab[U.uexp + K] = -1;
+                tab[U.uoff + K] = K;
+                tab[U.pairs + K] = K;
+                ublob[K] = r.shared;
+            }
+            tab[U.uoff + K + ns] = K + ns;
+        }
+        return;
     } else {
         if (lane < K) {
             st_dev(&r.idx_out[(size_t)t * K + lane], si);
