@@ -442,3 +442,71 @@ def test_layer_entry_repeat_calls_reset_the_grid_barrier(torch):
                 parity(out, o_out)
     finally:
         qm.coli_moe_debug_force_path(qm.PATH_AUTO)
+
+
+def _layer_any(spec, S, seed):
+    """Layer inputs with blobs by size (cdf recipe for large matrices)."""
+    d = synth.layer_inputs(seed, 0, spec, S)
+    d["blobs"] = [synth.expert_blob(seed, 0, e, spec) for e in range(spec.n_experts)]
+    d["shared"] = synth.expert_blob(seed, 0, spec.n_experts, spec) if spec.n_shared else None
+    return d
+
+
+@pytest.mark.parametrize("spec", [
+    dataclasses.replace(synth.TINY, n_experts=1024, top_k=32, hidden=256, inter=32),
+    dataclasses.replace(synth.TINY, n_experts=8, top_k=2, hidden=16384, inter=64),
+    dataclasses.replace(synth.TINY, n_experts=4, top_k=1, hidden=256, inter=16384, wbits=8),
+], ids=["e1024-k32", "h16384", "i16384-int8"])
+def test_layer_entry_limits(torch, path, spec):
+    """The largest dimensions the boundary accepts (1024 experts with top-32,
+    hidden 16384, inter 16384) through every kernel family."""
+    from synth.device import upload_layer
+    S = 3
+    say(f"coli_moe_layer limits {spec} [{path}]")
+    d = _layer_any(spec, S, seed=17)
+    dims = q().make_dims(spec)
+    dl = upload_layer(d)
+    ws = workspace(dims, S)
+    qm = q()
+    try:
+        idx, w, out = gpu_layer(torch, dims, dl, ws)
+    except qm.ColiError as err:
+        # the persistent kernel refuses shapes beyond its LDS budget
+        assert path == "persistent" and err.code == qm.COLI_EINVAL, str(err)
+        return
+    assert status(ws) == 0, qm.coli_moe_last_error()
+    o_out, o_idx, o_w = oracle.layer(spec, d["x"], d["router_w"], d["bias"], d["blobs"], d["shared"])
+    assert np.array_equal(idx, o_idx)
+    assert np.array_equal(w.view(np.uint32), o_w.view(np.uint32))
+    parity(out, o_out)
+
+
+def test_grouped_batch_limit(torch):
+    """The grouped kernels' pair list lives in LDS: a batch beyond 160 KiB of
+    it is refused on the host (no launch), a large one within it runs."""
+    from synth.device import upload_layer
+    qm = q()
+    spec = synth.TINY
+    S = 2500
+    say(f"grouped large batch S={S}")
+    d = synth.tiny_layer(seed=23, S=S, spec=spec)
+    dims = qm.make_dims(spec)
+    dl = upload_layer(d)
+    ws = workspace(dims, S)
+    idx, w, out = gpu_layer(torch, dims, dl, ws)
+    assert status(ws) == 0, qm.coli_moe_last_error()
+    o_out, o_idx, _ = oracle.layer(spec, d["x"], d["router_w"], d["bias"], d["blobs"], d["shared"])
+    assert np.array_equal(idx, o_idx)
+    parity(out, o_out)
+    big = dataclasses.replace(spec, n_experts=64, top_k=32)
+    Sb = 1400  # (32 + 1) * 1400 pair words > 160 KiB
+    dims_b = qm.make_dims(big)
+    x = torch.zeros((Sb, big.hidden), dtype=torch.float32, device="cuda")
+    wsb = workspace(dims_b, Sb)
+    table = torch.zeros(big.n_experts, dtype=torch.int64, device="cuda")
+    idx_b = torch.zeros((Sb, big.top_k), dtype=torch.int32, device="cuda")
+    w_b = torch.zeros((Sb, big.top_k), dtype=torch.float32, device="cuda")
+    o_b = torch.zeros((Sb, big.hidden), dtype=torch.float32, device="cuda")
+    with pytest.raises(qm.ColiError) as e:
+        qm.coli_moe_forward(dims_b, x, idx_b, w_b, table, dl["shared"], o_b, wsb)
+    assert e.value.code == qm.COLI_EINVAL
