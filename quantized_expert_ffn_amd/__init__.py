@@ -175,7 +175,7 @@ def coli_moe_forward(dims, x, topk_idx, topk_w, expert_blobs, shared_blob, out, 
 
 def coli_moe_layer(dims, x, router_w, router_bias, expert_blobs, shared_blob, topk_idx, topk_w, out, ws,
                    stream=None):
-    """Route + forward in one call (persistent kernel for up to 8 tokens)."""
+    """Route + forward in one call (the kernel family is chosen as the header describes)."""
     import torch
     S = x.shape[0]
     _check(_lib.coli_moe_layer(

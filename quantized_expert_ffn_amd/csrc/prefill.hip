@@ -377,7 +377,7 @@ __device__ __forceinline__ void pf_blocks(float (&acc)[NM][16], const uint8_t *l
 // The staged product loop: acc[m][r] = chain over the nb blocks of
 // d_b * isum_b for row 32 w + mfma_c_row(lane, r) of matrix m and the lane's
 // column.  Every wave runs the loads and barriers; `active` waves compute.
-template <int BITS, int NM, bool FOLD>
+template <int BITS, int NM, bool FOLD, bool TAIL>
 __device__ __forceinline__ void pf_run(float (&acc)[NM][16], uint8_t *lds, const PfSrc<NM> &src,
                                        const uint32_t *col_voff, const uint32_t *col_doff, bool active) {
     using ST = PfStage<BITS, NM>;
@@ -389,17 +389,22 @@ __device__ __forceinline__ void pf_run(float (&acc)[NM][16], uint8_t *lds, const
     const uint8_t *la = lds + ST::W_BYTES + ST::AS * n + 16 * h;
     const float *ld = reinterpret_cast<const float *>(lds + ST::W_BYTES + ST::A_BYTES) + n;
     const uint8_t *lw = lds + ST::WS * (32 * wave + n);
-    for (int s = 0; s < n_stages; ++s) {
+    // full stages; a short last stage (K no multiple of the stage) after the
+    // loop, so that the loop body has a single path for the accumulators
+    const int n_full = src.nb / ST::C;
+    for (int s = 0; s < n_full; ++s) {
         if (s > 0) __syncthreads();  // every wave is done with the previous stage
         pf_store<BITS, NM, FOLD>(R, lds);
         __syncthreads();
         if (s + 1 < n_stages) pf_load<BITS, NM>(R, src, col_voff, col_doff, s + 1);
-        if (!active) continue;
-        const int nblk = min(ST::C, src.nb - ST::C * s);
-        if (nblk == ST::C) {
-            pf_blocks<BITS, NM, FOLD, ST::C, true>(acc, lw, la, ld, h, ST::C);
-        } else {
-            // the short last stage of a K that is no multiple of the stage
+        if (active) pf_blocks<BITS, NM, FOLD, ST::C, true>(acc, lw, la, ld, h, ST::C);
+    }
+    if (TAIL && n_full < n_stages) {
+        if (n_full > 0) __syncthreads();
+        pf_store<BITS, NM, FOLD>(R, lds);
+        __syncthreads();
+        const int nblk = src.nb - ST::C * n_full;
+        if (active) {
             for (int j = 0; j < nblk; ++j) {
                 const i32x4 xb = *reinterpret_cast<const i32x4 *>(la + 32 * j);
                 const float d = ld[32 * j];
@@ -414,6 +419,17 @@ __device__ __forceinline__ void pf_run(float (&acc)[NM][16], uint8_t *lds, const
             }
         }
     }
+}
+
+// pf_run with the folded or the shifting chain (FOLD is the same for every
+// wave of a workgroup: they share the tile's columns).
+template <int BITS, int NM, bool TAIL>
+__device__ __forceinline__ void pf_dispatch(bool fold, float (&acc)[NM][16], uint8_t *lds, const PfSrc<NM> &src,
+                                            const uint32_t *col_voff, const uint32_t *col_doff, bool active) {
+    if (fold)
+        pf_run<BITS, NM, true, TAIL>(acc, lds, src, col_voff, col_doff, active);
+    else
+        pf_run<BITS, NM, false, TAIL>(acc, lds, src, col_voff, col_doff, active);
 }
 
 // Columns of the tile: the slot of pair n (the tile's first pair past its
@@ -476,10 +492,11 @@ __global__ __launch_bounds__(PF_T, 3) void k_pf_gateup(const FwdArgs a, const in
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[m][r] = 0.0f;
     // every wave has the same 32 columns, hence the same choice
-    if (scales_fold<ST::SHIFT>(a.dx + (size_t)col.tok * nb, nb))
-        pf_run<BITS, 2, true>(acc, lds, src, col_voff, col_doff, active);
+    const bool fold = scales_fold<ST::SHIFT>(a.dx + (size_t)col.tok * nb, nb);
+    if (nb % ST::C != 0)
+        pf_dispatch<BITS, 2, true>(fold, acc, lds, src, col_voff, col_doff, active);
     else
-        pf_run<BITS, 2, false>(acc, lds, src, col_voff, col_doff, active);
+        pf_dispatch<BITS, 2, false>(fold, acc, lds, src, col_voff, col_doff, active);
     if (!active || !col.live) return;
     const float *sg = reinterpret_cast<const float *>(blob + BL.s_gate) + i0;
     const float *su = reinterpret_cast<const float *>(blob + BL.s_up) + i0;
@@ -551,10 +568,11 @@ __global__ __launch_bounds__(PF_T, 4) void k_pf_down(const FwdArgs a, const int3
     float acc[1][16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[0][r] = 0.0f;
-    if (scales_fold<ST::SHIFT>(a.dh + (size_t)col.slot * nb, nb))
-        pf_run<BITS, 1, true>(acc, lds, src, col_voff, col_doff, active);
+    const bool fold = scales_fold<ST::SHIFT>(a.dh + (size_t)col.slot * nb, nb);
+    if (nb % ST::C != 0)
+        pf_dispatch<BITS, 1, true>(fold, acc, lds, src, col_voff, col_doff, active);
     else
-        pf_run<BITS, 1, false>(acc, lds, src, col_voff, col_doff, active);
+        pf_dispatch<BITS, 1, false>(fold, acc, lds, src, col_voff, col_doff, active);
     if (!active || !col.live) return;
     const float *sd = reinterpret_cast<const float *>(blob + BL.s_down) + r0;
     float *yrow = a.Y + (size_t)col.slot * H + r0;

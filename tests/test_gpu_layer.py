@@ -510,3 +510,43 @@ def test_grouped_batch_limit(torch):
     with pytest.raises(qm.ColiError) as e:
         qm.coli_moe_forward(dims_b, x, idx_b, w_b, table, dl["shared"], o_b, wsb)
     assert e.value.code == qm.COLI_EINVAL
+
+
+@pytest.mark.parametrize("S", [1, 4, 40])
+def test_graph_replay_matches_eager(torch, path, S):
+    """The benchmark replays coli_moe_layer calls from a captured HIP graph:
+    every replay (with eager work and synchronisations in between) must give
+    the eager call's bits, for each kernel family."""
+    from synth.device import upload_layer
+    if path == "persistent" and S > 8:
+        pytest.skip("the persistent kernel takes at most 8 tokens")
+    say(f"graph replay S={S} [{path}]")
+    qm = q()
+    spec = synth.TINY
+    d = _layer(spec, S, seed=90 + S)
+    dims = qm.make_dims(spec)
+    dl = upload_layer(d)
+    ws = workspace(dims, S)
+    ref_idx, ref_w, ref_out = gpu_layer(torch, dims, dl, ws)
+    assert status(ws) == 0, qm.coli_moe_last_error()
+    idx = torch.full((S, spec.top_k), -1, dtype=torch.int32, device="cuda")
+    w = torch.zeros((S, spec.top_k), dtype=torch.float32, device="cuda")
+    out = torch.zeros((S, spec.hidden), dtype=torch.float32, device="cuda")
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=cap):
+        qm.coli_moe_layer(dims, dl["x"], dl["router_w"], dl["bias"], dl["table"], dl["shared"], idx, w, out, ws,
+                          stream=cap)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        out.fill_(float("nan"))
+        idx.fill_(-1)
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(idx.cpu().numpy(), ref_idx)
+        assert np.array_equal(w.cpu().numpy().view(np.uint32), ref_w.view(np.uint32))
+        assert np.array_equal(out.cpu().numpy().view(np.uint32), ref_out.view(np.uint32)), f"replay {rep}"
+        # eager work between replays
+        gpu_layer(torch, dims, dl, ws)
+    assert status(ws) == 0, qm.coli_moe_last_error()
