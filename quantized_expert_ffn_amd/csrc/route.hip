@@ -66,50 +66,68 @@ __global__ __launch_bounds__(64) void k_router_select(const float *__restrict__ 
     if (!ok && lane == 0) raise_status(status, ST_NONFINITE);
 }
 
-// The fused router launch.  Grid (E + ceil(H / 2048), S), 64 threads.
-// Workgroup (e < E, t) computes logit (t, e), publishes it with a
-// device-scope store, drains it and counts itself in the token's arrival
-// counter; the workgroup that arrives last selects the token's top-K from
-// the published logits (device-scope loads) and counts the token as done;
-// the last token to be done builds the unit table of the batch in LDS and
-// writes it to the workspace.  Each counter is reset by its last arriver,
-// so the next launch starts from zero.  Workgroups e >= E quantise x.
+// The fused router launch.  Grid (ceil(E / RF_W) [+ ceil(ceil(H / 2048) /
+// RF_W) with qx], S), RF_W wavefronts per workgroup.  Wave w of workgroup
+// (x < ceil(E / RF_W), t) computes logit (t, RF_W x + w) and publishes it
+// with a device-scope store; once all of its waves have drained their
+// stores, the workgroup counts itself in the token's arrival counter (one
+// atomic per workgroup).  In the workgroup that arrives last, wave 0 selects
+// the token's top-K from the published logits (device-scope loads); for one
+// token it writes the unit table straight from the selection, otherwise the
+// token counts itself done and the last token's workgroup builds the unit
+// table of the batch in LDS.  Each counter is reset by its last arriver, so
+// the next launch starts from zero.  Workgroups past the logits quantise x
+// (one 2048-element slice per wave).
+constexpr int RF_W = 4;
+
 template <int MAXJ>
-__global__ __launch_bounds__(64) void k_route_fused(const RouteArgs r) {
+__global__ __launch_bounds__(64 * RF_W) void k_route_fused(const RouteArgs r) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    const int e = blockIdx.x, t = blockIdx.y, lane = threadIdx.x;
+    __shared__ int s_last;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, t = blockIdx.y;
     const int E = r.E, K = r.K, S = r.S, H = r.H;
-    if (e >= E) {
-        quant_x_wave(r.x, r.qx, r.dx, r.status, H, t, e - E);
+    const int n_lw = (E + RF_W - 1) / RF_W;
+    if ((int)blockIdx.x >= n_lw) {
+        quant_x_wave(r.x, r.qx, r.dx, r.status, H, t, ((int)blockIdx.x - n_lw) * RF_W + wave);
         return;
     }
-    bool ok;
-    const float p = logit_wave<MAXJ>(r.x + (size_t)t * H, r.W + (size_t)e * H, H, &ok);
-    if (!ok) raise_status(r.status, ST_NONFINITE);
-    if (lane == 0) st_dev(&r.logits[(size_t)t * E + e], p);
+    const int e = (int)blockIdx.x * RF_W + wave;
+    if (e < E) {
+        bool ok;
+        const float p = logit_wave<MAXJ>(r.x + (size_t)t * H, r.W + (size_t)e * H, H, &ok);
+        if (!ok) raise_status(r.status, ST_NONFINITE);
+        if (lane == 0) st_dev(&r.logits[(size_t)t * E + e], p);
+    }
     drain();
-    uint32_t prev = 0;
-    if (lane == 0) prev = __hip_atomic_fetch_add(&r.sync[t], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (__builtin_amdgcn_readlane((int)prev, 0) != E - 1) return;
+    __syncthreads();
+    if (tid == 0) {
+        const uint32_t prev = __hip_atomic_fetch_add(&r.sync[t], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = prev == (uint32_t)(n_lw - 1);
+        if (s_last) st_dev(&r.sync[t], 0u);
+    }
+    __syncthreads();
+    if (!s_last) return;
 
-    // last logit of token t: select (the blob pointers of the first 256
-    // experts are fetched meanwhile, for the unit table)
-    const uint8_t *bl[4];
-#pragma unroll
-    for (int m = 0; m < 4; ++m) bl[m] = r.blobs[min(lane + 64 * m, E - 1)];
-    const float *lg = r.logits + (size_t)t * E;
-    auto ld = [&](int q) { return ld_dev(lg + q); };
-    int32_t si;
-    float sw;
-    const bool sok = E <= 256 ? select_wave<4>(ld, r.bias, E, K, r.rsf, r.norm, &si, &sw)
-                              : select_wave<16>(ld, r.bias, E, K, r.rsf, r.norm, &si, &sw);
-    if (!sok && lane == 0) raise_status(r.status, ST_NONFINITE);
+    // last workgroup of token t: wave 0 selects (the blob pointers of the
+    // first 256 experts are fetched meanwhile, for the unit table)
     const int P = S * K;
     const SmemPlan T = smem_plan(S, K, E, 0, 0);
     int32_t *idx_l = reinterpret_cast<int32_t *>(smem + T.total);
     const uint8_t **btab = reinterpret_cast<const uint8_t **>(smem + a16(T.total + 4 * (size_t)P));
-    if (lane == 0) st_dev(&r.sync[t], 0u);
+    const uint8_t *bl[4];
+    int32_t si = 0;
+    float sw = 0.0f;
+    if (wave == 0) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) bl[m] = r.blobs[min(lane + 64 * m, E - 1)];
+        const float *lg = r.logits + (size_t)t * E;
+        auto ld = [&](int q) { return ld_dev(lg + q); };
+        const bool sok = E <= 256 ? select_wave<4>(ld, r.bias, E, K, r.rsf, r.norm, &si, &sw)
+                                  : select_wave<16>(ld, r.bias, E, K, r.rsf, r.norm, &si, &sw);
+        if (!sok && lane == 0) raise_status(r.status, ST_NONFINITE);
+    }
     if (S == 1) {
+        if (wave != 0) return;
         // One token: its selection is the whole routing.  The unit table is
         // written straight from the selection: unit j is the selected expert
         // of rank j in ascending id (its one pair is slot k, the lane that
@@ -150,22 +168,28 @@ __global__ __launch_bounds__(64) void k_route_fused(const RouteArgs r) {
             tab[U.uoff + K + ns] = K + ns;
         }
         return;
-    } else {
-        if (lane < K) {
-            st_dev(&r.idx_out[(size_t)t * K + lane], si);
-            st_dev(&r.w_out[(size_t)t * K + lane], sw);
-        }
-        drain();
-        if (lane == 0)
-            prev = __hip_atomic_fetch_add(&r.sync[ROUTE_FUSE_MAX], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (__builtin_amdgcn_readlane((int)prev, 0) != S - 1) return;
-        // last token selected: the unit table
-        for (int q = lane; q < P; q += 64) idx_l[q] = ld_dev(r.idx_out + q);
-        if (lane == 0) st_dev(&r.sync[ROUTE_FUSE_MAX], 0u);
     }
+    if (wave == 0 && lane < K) {
+        st_dev(&r.idx_out[(size_t)t * K + lane], si);
+        st_dev(&r.w_out[(size_t)t * K + lane], sw);
+    }
+    drain();
+    __syncthreads();
+    if (tid == 0) {
+        const uint32_t prev =
+            __hip_atomic_fetch_add(&r.sync[ROUTE_FUSE_MAX], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = prev == (uint32_t)(S - 1);
+        if (s_last) st_dev(&r.sync[ROUTE_FUSE_MAX], 0u);
+    }
+    __syncthreads();
+    if (!s_last) return;
+    // last token selected: the unit table of the batch
+    for (int q = tid; q < P; q += blockDim.x) idx_l[q] = ld_dev(r.idx_out + q);
+    if (wave == 0) {
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
-        if (lane + 64 * m < E) btab[lane + 64 * m] = bl[m];
+        for (int m = 0; m < 4; ++m)
+            if (lane + 64 * m < E) btab[lane + 64 * m] = bl[m];
+    }
     __syncthreads();
     build_units(idx_l, S, K, E, r.n_shared, smem, T, r.status, false);
     const UnitTable U = unit_table(S, K, E);
@@ -175,15 +199,15 @@ __global__ __launch_bounds__(64) void k_route_fused(const RouteArgs r) {
     const int *uoff = reinterpret_cast<const int *>(smem + T.uoff);
     const int *pairs = reinterpret_cast<const int *>(smem + T.pairs);
     const int n_units = misc[0];
-    if (lane < 4) tab[lane] = lane < 3 ? misc[lane] : 0;
-    for (int q = lane; q < n_units; q += 64) {
+    if (tid < 4) tab[tid] = tid < 3 ? misc[tid] : 0;
+    for (int q = tid; q < n_units; q += blockDim.x) {
         const int ex = uexp[q];
         tab[U.uexp + q] = ex;
         reinterpret_cast<const uint8_t **>(r.units + U.ublob)[q] =
             ex < 0 ? r.shared : (ex < 256 ? btab[ex] : r.blobs[ex]);
     }
-    for (int q = lane; q <= n_units; q += 64) tab[U.uoff + q] = uoff[q];
-    for (int q = lane; q < P + S * r.n_shared; q += 64) tab[U.pairs + q] = pairs[q];
+    for (int q = tid; q <= n_units; q += blockDim.x) tab[U.uoff + q] = uoff[q];
+    for (int q = tid; q < P + S * r.n_shared; q += blockDim.x) tab[U.pairs + q] = pairs[q];
 }
 
 size_t route_fused_smem(int S, int K, int E) {
@@ -191,16 +215,17 @@ size_t route_fused_smem(int S, int K, int E) {
 }
 
 hipError_t launch_route_fused(const RouteArgs &r, hipStream_t st) {
-    const dim3 grid(r.E + (r.H / 32 + 63) / 64, r.S);
+    const int n_lw = (r.E + RF_W - 1) / RF_W, n_q = ((r.H / 32 + 63) / 64 + RF_W - 1) / RF_W;
+    const dim3 grid(n_lw + (r.qx ? n_q : 0), r.S);
     const size_t smem = route_fused_smem(r.S, r.K, r.E);
     if (r.H <= 24 * 256) {
         const hipError_t e = ensure_dyn_smem(reinterpret_cast<const void *>(k_route_fused<24>), smem);
         if (e != hipSuccess) return e;
-        return launch(k_route_fused<24>, grid, dim3(64), smem, st, r);
+        return launch(k_route_fused<24>, grid, dim3(64 * RF_W), smem, st, r);
     }
     const hipError_t e = ensure_dyn_smem(reinterpret_cast<const void *>(k_route_fused<16>), smem);
     if (e != hipSuccess) return e;
-    return launch(k_route_fused<16>, grid, dim3(64), smem, st, r);
+    return launch(k_route_fused<16>, grid, dim3(64 * RF_W), smem, st, r);
 }
 
 // Q8_0 of the hidden states alone.  Grid: (ceil(H / 2048), S), 64 threads.
