@@ -234,8 +234,13 @@ def main():
         dom, dom_kernel = "forward_persistent", "k_layer<%d,%d,0,24>" % (spec.wbits, S)
         dom_bytes = n_units * bb
     else:
+        # for up to 2 tokens with at most 256 KiB of shared gate/up rows per
+        # 32-row tile, the layer call runs the shared expert's gate/up in its
+        # router launch; the gate/up launch then reads the routed experts only
+        in_router = args.path == "layer" and S <= 2 and 64 * H * spec.wbits // 8 <= 256 * 1024
+        gu_units = n_units - (spec.n_shared if in_router else 0)
         dom, dom_kernel = "gateup", "k_gateup<%d,%d>" % (spec.wbits, min(S, 4))
-        dom_bytes = n_units * (2 * spec.inter * H * spec.wbits // 8 + 2 * spec.inter * 4)
+        dom_bytes = gu_units * (2 * spec.inter * H * spec.wbits // 8 + 2 * spec.inter * 4)
     dom_us = kernel_us[dom]
     achieved = dom_bytes / (dom_us * 1e-6) / 1e9
     layer_gbs = lay_bytes / (ms_per_step * 1e-3) / 1e9

@@ -401,7 +401,7 @@ int coli_moe_layer(const coli_moe_dims *d, int32_t S, const float *x, const floa
             return fail(COLI_EINVAL, "shape needs %zu bytes of LDS per workgroup (> 160 KiB)", smem);
         // up to ROUTE_FUSE_MAX tokens: one router launch also selects the
         // routing and writes the call's unit table, which the expert kernels read
-        if (S <= ROUTE_FUSE_MAX && !use_grouped(S) && route_fused_smem(S, d->top_k, d->n_experts) <= 64 * 1024) {
+        if (S <= ROUTE_FUSE_MAX && !use_grouped(S)) {
             RouteArgs r;
             std::memset(&r, 0, sizeof r);
             r.x = x;
@@ -424,12 +424,24 @@ int coli_moe_layer(const coli_moe_dims *d, int32_t S, const float *x, const floa
             r.n_shared = d->n_shared;
             r.norm = d->norm_topk_prob;
             r.rsf = d->routed_scaling_factor;
-            timing_before(KK_ROUTER_LOGITS, st);
-            const hipError_t e = launch_route_fused(r, st);
-            timing_after(KK_ROUTER_LOGITS, st);
-            if (e != hipSuccess) return hip_fail(e, "router launch");
-            a.units = w8 + L.units;
-            return forward_launches(a, d->wbits, false, nullptr, true, w8 + L.units, st);
+            r.qh = a.qh;
+            r.dh = a.dh;
+            r.I = d->inter;
+            r.bits = d->wbits;
+            // the shared expert's gate/up tiles run in the router launch when
+            // they are short enough to finish beside it (one pass over at
+            // most 256 KiB of rows per workgroup) and their LDS fits there
+            r.sg = d->n_shared && route_shared_fits(S, d->hidden, d->wbits) ? 1 : 0;
+            if (route_fused_lds(r) > 64 * 1024) r.sg = 0;
+            if (route_fused_lds(r) <= 64 * 1024) {
+                timing_before(KK_ROUTER_LOGITS, st);
+                const hipError_t e = launch_route_fused(r, st);
+                timing_after(KK_ROUTER_LOGITS, st);
+                if (e != hipSuccess) return hip_fail(e, "router launch");
+                a.units = w8 + L.units;
+                a.shared_done = r.sg;
+                return forward_launches(a, d->wbits, false, nullptr, true, w8 + L.units, st);
+            }
         }
         rc = route_launches(d, S, x, router_w, router_bias, topk_idx, topk_w, w8, L, true, true, st);
         if (rc) return rc;

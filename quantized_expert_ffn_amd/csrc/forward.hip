@@ -27,6 +27,7 @@
 #include <algorithm>
 
 #include "device_common.h"
+#include "gateup.h"
 #include "kernels.h"
 #include "stream.h"
 
@@ -45,10 +46,11 @@ __device__ __forceinline__ const uint8_t *load_unit_table(const uint8_t *units, 
 }
 
 // Gate/up of one (32-row tile, unit).  With TABLE the units come from the
-// call's unit table (coli_moe_layer): grid row y = 0 is the shared expert
-// (its pairs do not depend on the routing, so it needs no table) and row
-// y > 0 routed unit y - 1.  Otherwise every workgroup builds the unit table
-// from topk_idx and takes unit y.
+// call's unit table (coli_moe_layer): row y = 0 is the shared expert (its
+// pairs do not depend on the routing, so it needs no table) and row y > 0
+// routed unit y - 1, where y = blockIdx.y + shared_done (the router launch
+// may already have run the shared expert's tiles).  Otherwise every
+// workgroup builds the unit table from topk_idx and takes unit blockIdx.y.
 template <int BITS, int NT, bool TABLE>
 __global__ __launch_bounds__(256) void k_gateup(const FwdArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -58,9 +60,10 @@ __global__ __launch_bounds__(256) void k_gateup(const FwdArgs a) {
     const int *uexp = reinterpret_cast<const int *>(smem + L.uexp);
     const int *uoff = reinterpret_cast<const int *>(smem + L.uoff);
     const int *pairs = reinterpret_cast<const int *>(smem + L.pairs);
-    int u = blockIdx.y, e;
+    const int y = (int)blockIdx.y + (TABLE ? a.shared_done : 0);
+    int u = y, e;
     const uint8_t *tblob = nullptr;
-    if (TABLE && a.n_shared && blockIdx.y == 0) {
+    if (TABLE && a.n_shared && y == 0) {
         int *pw = reinterpret_cast<int *>(smem + L.pairs);
         int *ow = reinterpret_cast<int *>(smem + L.uoff);
         for (int t = tid; t < S; t += 256) pw[t] = P + t;
@@ -77,7 +80,7 @@ __global__ __launch_bounds__(256) void k_gateup(const FwdArgs a) {
         // otherwise uses to build its unit table, which is at least as large)
         const UnitTable U = unit_table(S, K, E);
         int *tab = reinterpret_cast<int *>(smem);
-        u = blockIdx.y - (a.n_shared ? 1 : 0);
+        u = y - (a.n_shared ? 1 : 0);
         tblob = load_unit_table(a.units, U, tab, u);
         uexp = tab + U.uexp;
         uoff = tab + U.uoff;
@@ -100,72 +103,39 @@ __global__ __launch_bounds__(256) void k_gateup(const FwdArgs a) {
         if (tid == 0) raise_status(a.status, ST_NOTRESIDENT);
         return;
     }
-    int8_t *vq = reinterpret_cast<int8_t *>(smem + L.vq);
-    float *vd = reinterpret_cast<float *>(smem + L.vd);
-    int32_t *isum_wave = reinterpret_cast<int32_t *>(smem + L.isum) + wave * NT * ROWS_PER_WAVE * ISUM_PITCH;
-    float *gu = reinterpret_cast<float *>(smem + L.gu);
-    const BlobLayout BL = blob_layout(H, I, BITS);
-    const size_t row_bytes = (size_t)H * BITS / 8;
-    const int i0 = blockIdx.x * 32;
-    const int half = wave & 1;            // rows 0-15 or 16-31 of the tile
-    const size_t mat = wave < 2 ? BL.gate : BL.up;
-    const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(blob, (uint32_t)BL.total);
-    uint32_t rowoff[ROWS_PER_WAVE];
-#pragma unroll
-    for (int j = 0; j < ROWS_PER_WAVE; ++j)
-        rowoff[j] = (uint32_t)(mat + (size_t)(i0 + 16 * half + j) * row_bytes);
-    const float *scale = reinterpret_cast<const float *>(blob + (wave < 2 ? BL.s_gate : BL.s_up));
-    const int nb = H / 32;
+    const int nb = H / 32, vds = vd_stride(nb);
     const int p0 = uniform(uoff[u]), np = uniform(uoff[u + 1]) - p0;
-    const int crow = lane & 15, cvec = lane >> 4;
-    const int vds = vd_stride(nb);
-    for (int g0 = 0; g0 < np; g0 += NT) {
-        const int ng = min(NT, np - g0);
-        // Q8_0(x) of this group's tokens (computed once per call) into LDS:
-        // direct global-to-LDS loads (1 KB of codes or 64 scales per
-        // wavefront instruction) when the rows split into whole chunks
-        auto stage = [&]() {
-            if (H % 2048 == 0) {
-                const int qch = H / 1024, dch = nb / 64;
-                for (int j = wave; j < ng * (qch + dch); j += 4) {
-                    const int it = j / (qch + dch), ch = j - it * (qch + dch);
-                    const int v = pairs[p0 + g0 + it];
-                    const int t = v < P ? v / K : v - P;
-                    if (ch < qch)
-                        lds_dma16(a.qx + (size_t)t * H + ch * 1024 + 16 * lane, vq + (size_t)it * H + ch * 1024);
-                    else
-                        lds_dma4(a.dx + (size_t)t * nb + (ch - qch) * 64 + lane, vd + it * vds + (ch - qch) * 64);
-                }
-                drain_vm();
-            } else {
-                for (int it = 0; it < ng; ++it) {
-                    const int v = pairs[p0 + g0 + it];
-                    const int t = v < P ? v / K : v - P;
-                    const i32x4 *src = reinterpret_cast<const i32x4 *>(a.qx + (size_t)t * H);
-                    i32x4 *dst = reinterpret_cast<i32x4 *>(vq + (size_t)it * H);
-                    for (int q = tid; q < H / 16; q += 256) dst[q] = src[q];
-                    for (int q = tid; q < nb; q += 256) vd[it * vds + q] = a.dx[(size_t)t * nb + q];
-                }
+    // Q8_0(x) of a group's tokens (computed once per call) into LDS: direct
+    // global-to-LDS loads (1 KB of codes or 64 scales per wavefront
+    // instruction) when the rows split into whole chunks
+    auto stage = [&](int g0, int ng) {
+        int8_t *vq = reinterpret_cast<int8_t *>(smem + L.vq);
+        float *vd = reinterpret_cast<float *>(smem + L.vd);
+        if (H % 2048 == 0) {
+            const int qch = H / 1024, dch = nb / 64;
+            for (int j = wave; j < ng * (qch + dch); j += 4) {
+                const int it = j / (qch + dch), ch = j - it * (qch + dch);
+                const int v = pairs[p0 + g0 + it];
+                const int t = v < P ? v / K : v - P;
+                if (ch < qch)
+                    lds_dma16(a.qx + (size_t)t * H + ch * 1024 + 16 * lane, vq + (size_t)it * H + ch * 1024);
+                else
+                    lds_dma4(a.dx + (size_t)t * nb + (ch - qch) * 64 + lane, vd + it * vds + (ch - qch) * 64);
             }
-            __syncthreads();
-        };
-        BlockBits<BITS> cur[ROWS_PER_WAVE];
-        prime_rows<BITS, ROWS_PER_WAVE>(rsrc, rowoff, nb, cur);
-        const float acc = stream_rows<BITS, NT, ROWS_PER_WAVE>(rsrc, rowoff, nb, ng, vq, vd, isum_wave, H, stage, cur);
-        if (cvec < ng) gu[cvec * 64 + wave * ROWS_PER_WAVE + crow] = acc * scale[i0 + 16 * half + crow];
-        __syncthreads();
-        // SwiGLU and Q8_0(h): half-wave (tid >> 5) handles one vector's 32 rows.
-        const int vv = tid >> 5, i = tid & 31;
-        if (vv < ng) {
-            const float h = swiglu_f32(gu[vv * 64 + i], gu[vv * 64 + 32 + i]);
-            float d;
-            const int8_t q = q8_0_lane(h, &d);
-            const int slot = pairs[p0 + g0 + vv];
-            a.qh[(size_t)slot * I + i0 + i] = q;
-            if (i == 0) a.dh[(size_t)slot * (I / 32) + i0 / 32] = d;
+            drain_vm();
+        } else {
+            for (int it = 0; it < ng; ++it) {
+                const int v = pairs[p0 + g0 + it];
+                const int t = v < P ? v / K : v - P;
+                const i32x4 *src = reinterpret_cast<const i32x4 *>(a.qx + (size_t)t * H);
+                i32x4 *dst = reinterpret_cast<i32x4 *>(vq + (size_t)it * H);
+                for (int q = tid; q < H / 16; q += 256) dst[q] = src[q];
+                for (int q = tid; q < nb; q += 256) vd[it * vds + q] = a.dx[(size_t)t * nb + q];
+            }
         }
         __syncthreads();
-    }
+    };
+    gateup_unit<BITS, NT>(blob, H, I, blockIdx.x * 32, pairs + p0, np, smem, L, a.qh, a.dh, stage);
 }
 
 // Down projection: 64 rows of one unit per workgroup, y written to the
@@ -272,7 +242,7 @@ static hipError_t launch_dyn(F kern, dim3 grid, size_t smem, hipStream_t st, con
 template <int BITS, bool TABLE>
 static hipError_t gateup_bits(const FwdArgs &a, hipStream_t st) {
     const int P = a.S * a.K;
-    const int umax = std::min(P, a.E) + a.n_shared;
+    const int umax = std::min(P, a.E) + a.n_shared - (TABLE ? a.shared_done : 0);
     const dim3 grid(a.I / 32, umax);
     const int nt = pick_nt(a.S);
     const size_t smem = smem_plan(a.S, a.K, a.E, nt, a.H).total;

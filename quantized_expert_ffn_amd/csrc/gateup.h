@@ -1,0 +1,65 @@
+// Gate/up of one 32-row tile of one unit (colibrì README v1.0, "What's
+// implemented": SwiGLU experts over packed per-row-scaled weights with
+// integer dots over Q8_0 activations).  Used by the gate/up kernel for every
+// unit, and by the router launch of a layer call, whose extra workgroups run
+// the shared expert's tiles while the routing is being decided (the shared
+// expert's pairs do not depend on it).
+#pragma once
+
+#include "device_common.h"
+#include "stream.h"
+
+namespace coli {
+
+// Rows i0 .. i0+31 of the gate and up matrices of `blob` for the np pair
+// slots slots[0 .. np): waves 0-1 stream 16 gate rows each, waves 2-3 the
+// matching up rows.  Vectors go NT at a time: stage(g0, ng) puts the Q8_0
+// codes and block scales of slots g0 .. g0+ng-1 into vq (H codes per
+// vector) and vd (vd_stride(H / 32) scales per vector) and ends with a
+// workgroup barrier; it runs while the first weights are in flight.  Then
+// SwiGLU of each row pair and Q8_0(h) of the 32 values (one block), written
+// to qh / dh at the slot.  256 threads.
+template <int BITS, int NT, typename Stage>
+__device__ __forceinline__ void gateup_unit(const uint8_t *blob, int H, int I, int i0, const int *slots, int np,
+                                            uint8_t *smem, const SmemPlan &L, int8_t *__restrict__ qh,
+                                            float *__restrict__ dh, Stage stage) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
+    int8_t *vq = reinterpret_cast<int8_t *>(smem + L.vq);
+    float *vd = reinterpret_cast<float *>(smem + L.vd);
+    int32_t *isum_wave = reinterpret_cast<int32_t *>(smem + L.isum) + wave * NT * ROWS_PER_WAVE * ISUM_PITCH;
+    float *gu = reinterpret_cast<float *>(smem + L.gu);
+    const BlobLayout BL = blob_layout(H, I, BITS);
+    const size_t row_bytes = (size_t)H * BITS / 8;
+    const int half = wave & 1;            // rows 0-15 or 16-31 of the tile
+    const size_t mat = wave < 2 ? BL.gate : BL.up;
+    const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(blob, (uint32_t)BL.total);
+    uint32_t rowoff[ROWS_PER_WAVE];
+#pragma unroll
+    for (int j = 0; j < ROWS_PER_WAVE; ++j)
+        rowoff[j] = (uint32_t)(mat + (size_t)(i0 + 16 * half + j) * row_bytes);
+    const float *scale = reinterpret_cast<const float *>(blob + (wave < 2 ? BL.s_gate : BL.s_up));
+    const int nb = H / 32;
+    const int crow = lane & 15, cvec = lane >> 4;
+    for (int g0 = 0; g0 < np; g0 += NT) {
+        const int ng = min(NT, np - g0);
+        BlockBits<BITS> cur[ROWS_PER_WAVE];
+        prime_rows<BITS, ROWS_PER_WAVE>(rsrc, rowoff, nb, cur);
+        const float acc = stream_rows<BITS, NT, ROWS_PER_WAVE>(rsrc, rowoff, nb, ng, vq, vd, isum_wave, H,
+                                                              [&]() { stage(g0, ng); }, cur);
+        if (cvec < ng) gu[cvec * 64 + wave * ROWS_PER_WAVE + crow] = acc * scale[i0 + 16 * half + crow];
+        __syncthreads();
+        // SwiGLU and Q8_0(h): half-wave (tid >> 5) handles one vector's 32 rows.
+        const int vv = tid >> 5, i = tid & 31;
+        if (vv < ng) {
+            const float h = swiglu_f32(gu[vv * 64 + i], gu[vv * 64 + 32 + i]);
+            float d;
+            const int8_t q = q8_0_lane(h, &d);
+            const int slot = slots[g0 + vv];
+            qh[(size_t)slot * I + i0 + i] = q;
+            if (i == 0) dh[(size_t)slot * (I / 32) + i0 / 32] = d;
+        }
+        __syncthreads();
+    }
+}
+
+}  // namespace coli

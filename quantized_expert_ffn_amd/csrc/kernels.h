@@ -99,6 +99,7 @@ struct FwdArgs {
     uint32_t *status;
     int S, H, I, E, K, n_shared;
     int pend_mode;                 // 0: all units, 1: skip pending experts, 2: only pending
+    int shared_done;               // 1: the router launch wrote the shared expert's Q8_0(h)
     uint32_t pend[32];             // bit e: expert e pending
 };
 
@@ -117,10 +118,20 @@ struct RouteArgs {
     const uint8_t *shared;
     uint8_t *units;
     uint32_t *sync;
+    int8_t *qh;                    // with sg: the shared expert's Q8_0(h), slots S*K + t
+    float *dh;
     int S, H, E, K, n_shared, norm;
+    int I, bits;                   // expert shape and code width (for sg)
+    int sg;                        // 1: the launch also runs the shared expert's gate/up tiles
     float rsf;
 };
 hipError_t launch_route_fused(const RouteArgs &r, hipStream_t st);
+size_t route_fused_lds(const RouteArgs &r);
+// Shared-expert tiles in the router launch: up to two tokens (one pass of
+// the tile's 64 rows) and at most 256 KiB of those rows per workgroup.
+inline bool route_shared_fits(int S, int H, int bits) {
+    return S <= 2 && (size_t)64 * H * bits / 8 <= 256 * 1024;
+}
 
 // Router logits; with qx non-null the same launch writes Q8_0(x) to qx / dx.
 hipError_t launch_router_logits(const float *x, const float *W, float *logits, uint32_t *status,

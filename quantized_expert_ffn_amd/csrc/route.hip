@@ -3,6 +3,7 @@
 // (coli_moe_layer, up to ROUTE_FUSE_MAX tokens).  The device routines are
 // in router.h.
 #include "device_common.h"
+#include "gateup.h"
 #include "kernels.h"
 #include "router.h"
 #include "stream.h"
@@ -78,20 +79,54 @@ __global__ __launch_bounds__(64) void k_router_select(const float *__restrict__ 
 // table of the batch in LDS.  Each counter is reset by its last arriver, so
 // the next launch starts from zero.  Workgroups past the logits quantise x
 // (one 2048-element slice per wave).
+//
+// With sg, the first I / 32 workgroups of grid row 0 (ahead of the logits,
+// being the longest) run the shared expert's gate/up tiles for all S tokens
+// — its pairs do not depend on the routing — quantising x into their own
+// LDS with the same Q8_0 as the workspace copy; the gate/up launch then
+// skips the shared expert.
 constexpr int RF_W = 4;
 
-template <int MAXJ>
+// Shared expert, gate/up rows 32 tile .. 32 tile + 31, every token.
+template <int BITS, int NT>
+__device__ __forceinline__ void shared_gateup_tile(const RouteArgs &r, uint8_t *smem, int tile) {
+    const int tid = threadIdx.x, S = r.S, H = r.H, P = S * r.K;
+    const SmemPlan L = smem_plan(S, r.K, r.E, NT, H);
+    int *slots = reinterpret_cast<int *>(smem + L.pairs);
+    for (int t = tid; t < S; t += blockDim.x) slots[t] = P + t;
+    __syncthreads();
+    const int nb = H / 32, vds = vd_stride(nb);
+    auto stage = [&](int g0, int ng) {
+        int8_t *vq = reinterpret_cast<int8_t *>(smem + L.vq);
+        float *vd = reinterpret_cast<float *>(smem + L.vd);
+        for (int j = tid; j < ng * nb; j += blockDim.x) {
+            const int it = j / nb, b = j - it * nb;
+            bool ok;
+            vd[it * vds + b] = q8_0_block_lane(r.x + (size_t)(g0 + it) * H + 32 * b, vq + (size_t)it * H + 32 * b, &ok);
+        }
+        __syncthreads();
+    };
+    gateup_unit<BITS, NT>(uniform_ptr(r.shared), H, r.I, 32 * tile, slots, S, smem, L, r.qh, r.dh, stage);
+}
+
+template <int MAXJ, int BITS, int NT>
 __global__ __launch_bounds__(64 * RF_W) void k_route_fused(const RouteArgs r) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     __shared__ int s_last;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, t = blockIdx.y;
     const int E = r.E, K = r.K, S = r.S, H = r.H;
-    const int n_lw = (E + RF_W - 1) / RF_W;
-    if ((int)blockIdx.x >= n_lw) {
-        quant_x_wave(r.x, r.qx, r.dx, r.status, H, t, ((int)blockIdx.x - n_lw) * RF_W + wave);
+    const int n_sg = r.sg ? r.I / 32 : 0;
+    if ((int)blockIdx.x < n_sg) {
+        if (t == 0) shared_gateup_tile<BITS, NT>(r, smem, blockIdx.x);
         return;
     }
-    const int e = (int)blockIdx.x * RF_W + wave;
+    const int bx = (int)blockIdx.x - n_sg;
+    const int n_lw = (E + RF_W - 1) / RF_W;
+    if (bx >= n_lw) {
+        quant_x_wave(r.x, r.qx, r.dx, r.status, H, t, (bx - n_lw) * RF_W + wave);
+        return;
+    }
+    const int e = bx * RF_W + wave;
     if (e < E) {
         bool ok;
         const float p = logit_wave<MAXJ>(r.x + (size_t)t * H, r.W + (size_t)e * H, H, &ok);
@@ -214,18 +249,43 @@ size_t route_fused_smem(int S, int K, int E) {
     return a16(a16(smem_plan(S, K, E, 0, 0).total + 4 * (size_t)S * K) + 8 * (size_t)(E < 256 ? E : 256));
 }
 
+// Vectors per pass of the shared tiles: two at most, so that their LDS fits
+// beside the router's for the decode shapes (later passes re-read the
+// tile's rows from L2).
+static int route_nt(int S) { return S >= 2 ? 2 : 1; }
+
+size_t route_fused_lds(const RouteArgs &r) {
+    const size_t sel = route_fused_smem(r.S, r.K, r.E);
+    if (!r.sg) return sel;
+    const size_t tile = smem_plan(r.S, r.K, r.E, route_nt(r.S), r.H).total;
+    return sel > tile ? sel : tile;
+}
+
+template <int MAXJ, int BITS>
+static hipError_t route_fused_bits(const RouteArgs &r, dim3 grid, size_t smem, hipStream_t st) {
+    auto go = [&](auto kern) {
+        const hipError_t e = ensure_dyn_smem(reinterpret_cast<const void *>(kern), smem);
+        if (e != hipSuccess) return e;
+        return launch(kern, grid, dim3(64 * RF_W), smem, st, r);
+    };
+    if (route_nt(r.S) == 1) return go(k_route_fused<MAXJ, BITS, 1>);
+    return go(k_route_fused<MAXJ, BITS, 2>);
+}
+
+template <int MAXJ>
+static hipError_t route_fused_maxj(const RouteArgs &r, dim3 grid, size_t smem, hipStream_t st) {
+    if (r.bits == 8) return route_fused_bits<MAXJ, 8>(r, grid, smem, st);
+    if (r.bits == 2) return route_fused_bits<MAXJ, 2>(r, grid, smem, st);
+    return route_fused_bits<MAXJ, 4>(r, grid, smem, st);
+}
+
 hipError_t launch_route_fused(const RouteArgs &r, hipStream_t st) {
     const int n_lw = (r.E + RF_W - 1) / RF_W, n_q = ((r.H / 32 + 63) / 64 + RF_W - 1) / RF_W;
-    const dim3 grid(n_lw + (r.qx ? n_q : 0), r.S);
-    const size_t smem = route_fused_smem(r.S, r.K, r.E);
-    if (r.H <= 24 * 256) {
-        const hipError_t e = ensure_dyn_smem(reinterpret_cast<const void *>(k_route_fused<24>), smem);
-        if (e != hipSuccess) return e;
-        return launch(k_route_fused<24>, grid, dim3(64 * RF_W), smem, st, r);
-    }
-    const hipError_t e = ensure_dyn_smem(reinterpret_cast<const void *>(k_route_fused<16>), smem);
-    if (e != hipSuccess) return e;
-    return launch(k_route_fused<16>, grid, dim3(64 * RF_W), smem, st, r);
+    const int n_sg = r.sg ? r.I / 32 : 0;
+    const dim3 grid(n_sg + n_lw + (r.qx ? n_q : 0), r.S);
+    const size_t smem = route_fused_lds(r);
+    if (r.H <= 24 * 256) return route_fused_maxj<24>(r, grid, smem, st);
+    return route_fused_maxj<16>(r, grid, smem, st);
 }
 
 // Q8_0 of the hidden states alone.  Grid: (ceil(H / 2048), S), 64 threads.

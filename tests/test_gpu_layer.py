@@ -362,13 +362,16 @@ def test_layer_entry_tiny(torch, path, S):
     dataclasses.replace(synth.TINY, wbits=2, n_shared=0, top_k=3),
     dataclasses.replace(synth.TINY, n_experts=70, top_k=9, hidden=512, inter=96, norm_topk_prob=0),
 ], ids=["int8", "int2-k3-noshared", "e70-k9-h512-i96-nonorm"])
-def test_layer_entry_variants(torch, path, spec):
+@pytest.mark.parametrize("S", [2, 5])
+def test_layer_entry_variants(torch, path, spec, S):
+    """Up to two tokens the router launch also runs the shared expert's
+    gate/up tiles; more tokens leave them to the gate/up launch."""
     from synth.device import upload_layer
-    say(f"coli_moe_layer variant {spec} [{path}]")
-    d = _layer(spec, 5, seed=3)
+    say(f"coli_moe_layer variant {spec} S={S} [{path}]")
+    d = _layer(spec, S, seed=3)
     dims = q().make_dims(spec)
     dl = upload_layer(d)
-    ws = workspace(dims, 5)
+    ws = workspace(dims, S)
     idx, w, out = gpu_layer(torch, dims, dl, ws)
     assert status(ws) == 0, q().coli_moe_last_error()
     o_out, o_idx, o_w = _oracle(spec, d)
