@@ -283,11 +283,54 @@ def main():
 
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(args, spec, xs_host, layers, L, S)
+    add_measured_roof(res, q, "hbm")
     print(json.dumps(res), flush=True)
 
 
 KINDS = (("router_logits", 0), ("router_select", 1), ("quant_x", 7), ("group", 8), ("gateup", 2), ("down", 3),
          ("combine", 4), ("layer", 5), ("forward_persistent", 6))
+
+
+def add_measured_roof(res, q, kind):
+    """Adds to res["roofline"] the ceiling of the same kind measured on this
+    GPU in this run, and the dominant kernel's fraction of it:
+      hbm   a streaming read of 4 GiB (coli_moe_roof_stream_read), GB/s;
+      mfma  the int8 matrix cores alone (coli_moe_roof_mfma_i8), TOPS.
+    Median of five timed repetitions after one untimed one."""
+    import torch
+    sink = torch.empty(q.coli_moe_roof_sink_words(), dtype=torch.int32, device="cuda")
+    st = torch.cuda.current_stream()
+
+    def timed(fn, stream):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(5):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b) * 1e-3)
+        return sorted(ts)[2]
+
+    if kind == "hbm":
+        n = 4 << 30
+        buf = torch.empty(n, dtype=torch.uint8, device="cuda")
+        t = timed(lambda: q.coli_moe_roof_stream_read(buf, sink, st), st)
+        val, unit, how = n / t / 1e9, "GB/s", "streaming read of 4 GiB, 16-byte loads"
+        del buf
+    elif kind == "mfma":
+        iters = 200
+        t = timed(lambda: q.coli_moe_roof_mfma_i8(iters, sink, st), st)
+        ops = 2048 * 4 * iters * 4 * 2 * 32 * 32 * 32
+        val, unit, how = ops / t / 1e12, "TOPS", "v_mfma_i32_32x32x32_i8 loop, 8192 wavefronts, register operands"
+    else:
+        raise ValueError(kind)
+    r = res["roofline"]
+    r["measured_peak"] = {"value": round(val, 1), "unit": unit, "how": how}
+    if r.get("unit") == unit and val > 0:
+        r["frac_of_measured"] = round(r["achieved"] / val, 4)
 
 
 def kernel_times(q, run):
@@ -417,6 +460,7 @@ def run_prefill(args, q, synth):
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_prefill(args, spec, xs_host[0], d, host.numpy(), routed[0])
+    add_measured_roof(res, q, "mfma")
     print(json.dumps(res), flush=True)
 
 
@@ -565,7 +609,8 @@ def run_tiered(args, q, synth):
         "roofline": {
             "bound": "pcie", "kernel": "coli_moe_stage_experts (hipMemcpyAsync host to device)",
             "achieved": round(copy_gbs, 2), "peak": PCIE_PEAK_GBS, "unit": "GB/s",
-            "frac": round(copy_gbs / PCIE_PEAK_GBS, 4), "traffic": staged / max(1, len(copies_timed)),
+            "frac": round(copy_gbs / PCIE_PEAK_GBS, 4), "traffic": None,
+            "bytes_per_copy_batch": round(staged / max(1, len(copies_timed))),
             "copy_batches": len(copies_timed), "copy_busy_ms": round(copy_ms, 3),
         },
         "staged_gb_per_token": round(staged / steps / 1e9, 3),

@@ -213,6 +213,26 @@ int coli_moe_debug_mfma_i8(const int8_t *a, const int8_t *b, int32_t *c, void *s
 int coli_moe_debug_q8_0(int32_t n_rows, int32_t cols, const float *v, int8_t *q, float *d,
                         void *stream);
 
+/* ---- measured roofs (benchmarking) ----------------------------------
+ * Reference kernels for the ceilings the layer's kernels are compared
+ * with: a plain streaming read of HBM and the int8 matrix cores alone.
+ * Both run 2048 workgroups of 256 threads and write one 32-bit word per
+ * thread to a device `sink` of coli_moe_roof_sink_words() words (the
+ * values are meaningless; they keep the work alive).  Enqueued on
+ * `stream`; time them with events around the call. */
+size_t coli_moe_roof_sink_words(void);
+
+/* Reads `bytes` (a multiple of 16) of device memory at `src` once, with
+ * 16-byte non-temporal loads, eight per thread in flight.  COLI_EINVAL on
+ * NULL pointers or a size that is not a multiple of 16. */
+int coli_moe_roof_stream_read(const void *src, size_t bytes, uint32_t *sink, void *stream);
+
+/* Every wavefront runs `iters` (>= 1) rounds of four independent
+ * v_mfma_i32_32x32x32_i8 accumulations on register operands:
+ * 2048 * 4 * iters * 4 * 65536 integer operations (multiply and add
+ * counted apart).  COLI_EINVAL on iters < 1 or a NULL sink. */
+int coli_moe_roof_mfma_i8(int32_t iters, int32_t *sink, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

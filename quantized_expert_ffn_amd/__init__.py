@@ -29,6 +29,7 @@ EXPORTS = (
     "coli_moe_timing_read", "coli_moe_debug_unpack", "coli_moe_debug_block_dots",
     "coli_moe_debug_logits", "coli_moe_debug_expf", "coli_moe_debug_q8_0",
     "coli_moe_debug_force_path", "coli_moe_layer", "coli_moe_debug_mfma_i8",
+    "coli_moe_roof_sink_words", "coli_moe_roof_stream_read", "coli_moe_roof_mfma_i8",
 )
 
 KIND_ROUTER_LOGITS, KIND_ROUTER_SELECT, KIND_GATEUP, KIND_DOWN, KIND_COMBINE = 0, 1, 2, 3, 4
@@ -73,6 +74,9 @@ _sigs = {
     "coli_moe_debug_force_path": (ctypes.c_int, [_I32]),
     "coli_moe_layer": (ctypes.c_int, [_D, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "coli_moe_debug_mfma_i8": (ctypes.c_int, [_P, _P, _P, _P]),
+    "coli_moe_roof_sink_words": (_SZ, []),
+    "coli_moe_roof_stream_read": (ctypes.c_int, [_P, _SZ, _P, _P]),
+    "coli_moe_roof_mfma_i8": (ctypes.c_int, [_I32, _P, _P]),
 }
 for _name, (_res, _args) in _sigs.items():
     _f = getattr(_lib, _name)
@@ -264,3 +268,21 @@ def coli_moe_debug_mfma_i8(a, b, c, stream=None):
         raise ValueError("a, b and c hold 64 lanes x 16 registers")
     _check(_lib.coli_moe_debug_mfma_i8(_dev(a, torch.int8, "a"), _dev(b, torch.int8, "b"),
                                        _dev(c, torch.int32, "c"), _stream(stream)), "coli_moe_debug_mfma_i8")
+
+
+def coli_moe_roof_sink_words() -> int:
+    return int(_lib.coli_moe_roof_sink_words())
+
+
+def coli_moe_roof_stream_read(src, sink, stream=None):
+    """Streaming read of the whole device tensor `src` (bytes a multiple of 16)."""
+    import torch
+    nbytes = src.numel() * src.element_size()
+    _check(_lib.coli_moe_roof_stream_read(_ptr(src, None, "src"), nbytes, _dev(sink, torch.int32, "sink"),
+                                          _stream(stream)), "coli_moe_roof_stream_read")
+
+
+def coli_moe_roof_mfma_i8(iters: int, sink, stream=None):
+    import torch
+    _check(_lib.coli_moe_roof_mfma_i8(int(iters), _dev(sink, torch.int32, "sink"), _stream(stream)),
+           "coli_moe_roof_mfma_i8")

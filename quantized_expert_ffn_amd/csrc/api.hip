@@ -600,4 +600,23 @@ int coli_moe_debug_mfma_i8(const int8_t *a, const int8_t *b, int32_t *c, void *s
     return e == hipSuccess ? COLI_OK : hip_fail(e, "debug_mfma_i8 launch");
 }
 
+size_t coli_moe_roof_sink_words(void) { return (size_t)ROOF_GRID * 256; }
+
+int coli_moe_roof_stream_read(const void *src, size_t bytes, uint32_t *sink, void *stream) {
+    if (!src || !sink || bytes % 16) return fail(COLI_EINVAL, "roof_stream_read: bad arguments");
+    if (bytes == 0) return COLI_OK;
+    int rc = check_device();
+    if (rc) return rc;
+    hipError_t e = launch_roof_stream(src, bytes, sink, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? COLI_OK : hip_fail(e, "roof_stream_read launch");
+}
+
+int coli_moe_roof_mfma_i8(int32_t iters, int32_t *sink, void *stream) {
+    if (iters < 1 || !sink) return fail(COLI_EINVAL, "roof_mfma_i8: bad arguments");
+    int rc = check_device();
+    if (rc) return rc;
+    hipError_t e = launch_roof_mfma(iters, sink, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? COLI_OK : hip_fail(e, "roof_mfma_i8 launch");
+}
+
 }  // extern "C"

@@ -109,6 +109,63 @@ hipError_t launch_debug_mfma_i8(const int8_t *a, const int8_t *b, int32_t *c, hi
     return hipGetLastError();
 }
 
+// ---- measured roofs ------------------------------------------------------
+// A streaming read of n16 16-byte words (ROOF_SR_UNROLL loads per thread in
+// flight, grid-stride), every thread XOR-folding what it read into one sink
+// word so that no load is dead.
+constexpr int ROOF_SR_UNROLL = 8;
+__global__ __launch_bounds__(256) void k_roof_stream(const i32x4 *__restrict__ src, uint64_t n16,
+                                                     uint32_t *__restrict__ sink) {
+    const uint64_t stride = (uint64_t)gridDim.x * 256;
+    uint64_t i = (uint64_t)blockIdx.x * 256 + threadIdx.x;
+    i32x4 acc = {0, 0, 0, 0};
+    for (; i + (ROOF_SR_UNROLL - 1) * stride < n16; i += ROOF_SR_UNROLL * stride) {
+        i32x4 v[ROOF_SR_UNROLL];
+#pragma unroll
+        for (int k = 0; k < ROOF_SR_UNROLL; ++k) v[k] = __builtin_nontemporal_load(src + i + k * stride);
+#pragma unroll
+        for (int k = 0; k < ROOF_SR_UNROLL; ++k) acc ^= v[k];
+    }
+    for (; i < n16; i += stride) acc ^= __builtin_nontemporal_load(src + i);
+    sink[(size_t)blockIdx.x * 256 + threadIdx.x] = (uint32_t)(acc.x ^ acc.y ^ acc.z ^ acc.w);
+}
+
+// The int8 matrix cores alone: each wavefront runs `iters` rounds of four
+// independent v_mfma_i32_32x32x32_i8 accumulations on register operands.
+__global__ __launch_bounds__(256) void k_roof_mfma(int iters, int32_t *__restrict__ sink) {
+    const int t = (int)threadIdx.x;
+    const i32x4 a = {t, t + 1, t + 2, t + 3};
+    i32x4 b[4];   // a different B per chain, so that no two chains are the same computation
+#pragma unroll
+    for (int k = 0; k < 4; ++k) b[k] = i32x4{3 * t + k, 5 * t + k, 7 * t + k, 11 * t + k};
+    i32x16 c[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) c[k][r] = 0;
+    for (int i = 0; i < iters; ++i) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) c[k] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b[k], c[k], 0, 0, 0);
+    }
+    int32_t x = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) x ^= c[k][r];
+    sink[(size_t)blockIdx.x * 256 + t] = x;
+}
+
+hipError_t launch_roof_stream(const void *src, uint64_t bytes, uint32_t *sink, hipStream_t st) {
+    hipLaunchKernelGGL(k_roof_stream, dim3(ROOF_GRID), dim3(256), 0, st, static_cast<const i32x4 *>(src),
+                       bytes / 16, sink);
+    return hipGetLastError();
+}
+
+hipError_t launch_roof_mfma(int iters, int32_t *sink, hipStream_t st) {
+    hipLaunchKernelGGL(k_roof_mfma, dim3(ROOF_GRID), dim3(256), 0, st, iters, sink);
+    return hipGetLastError();
+}
+
 hipError_t launch_debug_q8_0(int rows, int cols, const float *v, int8_t *q, float *d,
                              hipStream_t st) {
     hipLaunchKernelGGL(k_debug_q8_0, dim3(rows), dim3(64), 0, st, v, q, d, cols);

@@ -222,6 +222,10 @@ hipError_t launch_debug_block_dots(int bits, int rows, int cols, const void *src
                                    int32_t *out, hipStream_t st);
 hipError_t launch_debug_expf(int64_t n, const float *x, float *y, hipStream_t st);
 hipError_t launch_debug_mfma_i8(const int8_t *a, const int8_t *b, int32_t *c, hipStream_t st);
+// Measured roofs: ROOF_GRID workgroups of 256 threads, one sink word per thread.
+constexpr int ROOF_GRID = 2048;
+hipError_t launch_roof_stream(const void *src, uint64_t bytes, uint32_t *sink, hipStream_t st);
+hipError_t launch_roof_mfma(int iters, int32_t *sink, hipStream_t st);
 hipError_t launch_debug_q8_0(int rows, int cols, const float *v, int8_t *q, float *d,
                              hipStream_t st);
 

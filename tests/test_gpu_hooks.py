@@ -131,3 +131,60 @@ def test_mfma_i8_lane_layout(torch):
     if not np.array_equal(got, want):
         np.save("gpurun_out/mfma_raw.npy", np.stack([a_raw.astype(np.int32), b_raw.astype(np.int32), got]))
     assert np.array_equal(got, want)
+
+
+def test_roof_stream_read_reads_every_word(torch):
+    """The streaming-read roof kernel really reads the whole buffer: thread g
+    of the grid XOR-folds the 16-byte words g, g + T, g + 2T, ... (T threads)."""
+    say("roof stream read 16 MiB")
+    qm = q()
+    T = qm.coli_moe_roof_sink_words()
+    n16 = (16 << 20) // 16 + 5           # a ragged tail past whole grid strides
+    rng = np.random.default_rng(7)
+    words = rng.integers(0, 2**32, size=(n16, 4), dtype=np.uint64).astype(np.uint32)
+    src = torch.from_numpy(words.view(np.int32).reshape(-1)).cuda()
+    sink = torch.full((T,), -1, dtype=torch.int32, device="cuda")
+    qm.coli_moe_roof_stream_read(src, sink)
+    got = sink.cpu().numpy().view(np.uint32)
+    per_word = words[:, 0] ^ words[:, 1] ^ words[:, 2] ^ words[:, 3]
+    want = np.zeros(T, np.uint32)
+    for k in range(0, n16, T):
+        part = per_word[k:k + T]
+        want[:len(part)] ^= part
+    assert np.array_equal(got, want)
+
+
+def test_roof_mfma_counts_real_products(torch):
+    """The int8 matrix-core roof kernel computes what its lane layout says:
+    every thread's sink word is the XOR of its four chains' 16 result
+    registers, each chain iters times A * B_k with A and B_k taken from the
+    lanes' registers (the layout of the prefill kernels)."""
+    say("roof mfma iters=3")
+    qm = q()
+    T = qm.coli_moe_roof_sink_words()
+    iters = 3
+    sink = torch.zeros((T,), dtype=torch.int32, device="cuda")
+    qm.coli_moe_roof_mfma_i8(iters, sink)
+    got = sink.cpu().numpy()[:256]    # every workgroup computes the same words
+    want = np.zeros(256, np.int64)
+    for w in range(4):
+        t = 64 * w + np.arange(64)
+        a = np.stack([t, t + 1, t + 2, t + 3], 1).astype(np.int32).view(np.int8).reshape(64, 16).astype(np.int64)
+        l = np.arange(64)
+        A = np.zeros((32, 32), np.int64)
+        for j in range(16):
+            A[l % 32, 16 * (l // 32) + j] = a[:, j]
+        acc = np.zeros(64, np.int64)
+        for k in range(4):
+            bk = np.stack([3 * t + k, 5 * t + k, 7 * t + k, 11 * t + k], 1).astype(np.int32)
+            bk = bk.view(np.int8).reshape(64, 16).astype(np.int64)
+            B = np.zeros((32, 32), np.int64)
+            for j in range(16):
+                B[16 * (l // 32) + j, l % 32] = bk[:, j]
+            C = (iters * (A @ B)).astype(np.int32)
+            for r in range(16):
+                i = 8 * (r // 4) + 4 * (l // 32) + r % 4
+                acc ^= C[i, l % 32].astype(np.int64)
+        want[64 * w:64 * w + 64] = acc
+    assert np.array_equal(got.astype(np.int64), want.astype(np.int32).astype(np.int64))
+    assert np.array_equal(sink.cpu().numpy().reshape(-1, 256), np.tile(got, (T // 256, 1)))
