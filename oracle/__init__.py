@@ -69,6 +69,10 @@ def lib():
             "oq_expert": (I32, [P, I32, I32, I32, P, P, P, P, P, P, P, P]),
             "oq_moe_route": (I32, [I32, I32, I32, F32, I32, I32, P, P, P, P, P, P, P]),
             "oq_moe_forward": (I32, [I32, I32, I32, I32, I32, I32, I32, P, P, P, P, P, P]),
+            "oq_blob_layout_g": (None, [I32, I32, I32, I32, P]),
+            "oq_row_dot_g": (F32, [P, P, P, I32, P, I32]),
+            "oq_expert_g": (I32, [P, I32, I32, I32, I32, P, P, P, P, P, P, P, P]),
+            "oq_moe_forward_g": (I32, [I32, I32, I32, I32, I32, I32, I32, I32, P, P, P, P, P, P]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -138,9 +142,10 @@ def unpack(src, n: int, bits: int) -> np.ndarray:
     return out
 
 
-def blob_layout(H: int, I: int, bits: int) -> dict:
+def blob_layout(H: int, I: int, bits: int, group: int = 0) -> dict:
+    """Section offsets of an expert blob; group > 0: group-scaled scales."""
     off = np.zeros(7, np.uint64)
-    lib().oq_blob_layout(H, I, bits, _p(off))
+    lib().oq_blob_layout_g(H, I, bits, group, _p(off))
     keys = ("gate", "up", "down", "s_gate", "s_up", "s_down", "total")
     return {k: int(v) for k, v in zip(keys, off)}
 
@@ -156,6 +161,14 @@ def row_dot(w, q, d, scale: float) -> np.float32:
     n = w.size
     assert q.size == n and d.size == n // 32
     return np.float32(lib().oq_row_dot(_p(w), _p(q), _p(d), n, float(scale)))
+
+
+def row_dot_g(w, q, d, gs, group: int) -> np.float32:
+    """Row dot with one scale per `group` codes (gs[n / group])."""
+    w, q, d, gs = _c(w, np.int8), _c(q, np.int8), _c(d, np.float32), _c(gs, np.float32)
+    n = w.size
+    assert q.size == n and d.size == n // 32 and gs.size == n // group
+    return np.float32(lib().oq_row_dot_g(_p(w), _p(q), _p(d), n, _p(gs), int(group)))
 
 
 def router_logit(x, w) -> np.float32:
@@ -176,14 +189,14 @@ def select(logits, bias, K: int, rsf: float, norm: int = 1):
     return idx, w, sig
 
 
-def expert(blob, H: int, I: int, bits: int, qx, dx) -> dict:
+def expert(blob, H: int, I: int, bits: int, qx, dx, group: int = 0) -> dict:
     """One SwiGLU expert on one token; returns y and the intermediates."""
     blob = _c(blob, np.uint8)
     qx, dx = _c(qx, np.int8), _c(dx, np.float32)
     out = {"y": np.empty(H, np.float32), "g": np.empty(I, np.float32), "u": np.empty(I, np.float32),
            "h": np.empty(I, np.float32), "qh": np.empty(I, np.int8), "dh": np.empty(I // 32, np.float32)}
-    rc = lib().oq_expert(_p(blob), H, I, bits, _p(qx), _p(dx), _p(out["y"]), _p(out["g"]),
-                         _p(out["u"]), _p(out["h"]), _p(out["qh"]), _p(out["dh"]))
+    rc = lib().oq_expert_g(_p(blob), H, I, bits, int(group), _p(qx), _p(dx), _p(out["y"]), _p(out["g"]),
+                           _p(out["u"]), _p(out["h"]), _p(out["qh"]), _p(out["dh"]))
     _check(rc, "expert")
     return out
 
@@ -217,8 +230,9 @@ def forward(spec, x, idx, w, blobs, shared_blob):
     ptrs = (ctypes.c_void_p * spec.n_experts)(*[None if b is None else b.ctypes.data for b in keep])
     sh = None if shared_blob is None else _c(shared_blob, np.uint8)
     out = np.empty((S, spec.hidden), np.float32)
-    rc = lib().oq_moe_forward(spec.hidden, spec.inter, spec.n_experts, spec.top_k, spec.n_shared,
-                              spec.wbits, S, _p(x), _p(idx), _p(w), ptrs, _p(sh), _p(out))
+    rc = lib().oq_moe_forward_g(spec.hidden, spec.inter, spec.n_experts, spec.top_k, spec.n_shared,
+                                spec.wbits, int(getattr(spec, "group", 0)), S, _p(x), _p(idx), _p(w), ptrs,
+                                _p(sh), _p(out))
     _check(rc, "forward")
     return out
 

@@ -21,6 +21,9 @@
  *            mechanics)": the sigmoid noaux_tc router and its self-test.
  *  [LAYOUT]  JustVugg/colibri (topgit.dev), the repository layout: the shared
  *            routed-expert FFN kernel header (SwiGLU experts).
+ *  [GS64]    JustVugg/colibri (topgit.dev), "Get started" and "Other
+ *            supported models": the group-scaled int4 containers (one scale
+ *            per 64 weights of a row, "int4-g64"), preferred to per-row int4.
  */
 #include <math.h>
 #include <stdint.h>
@@ -160,6 +163,28 @@ void oq_blob_layout(int H, int I, int bits, uint64_t off[7]) {
     off[6] = al256(off[5] + 4u * (uint64_t)H);
 }
 
+/* Group-scaled blobs [GS64]: the same code sections, then one f32 scale per
+ * `group` consecutive codes of each row, row-major: gate and up scales
+ * [I][H / group], down scales [H][I / group].  group = 0 is the per-row
+ * layout above.  Reading: the group scale replaces the per-row scale (the
+ * pages compare the two as alternatives), and groups start at column 0. */
+void oq_blob_layout_g(int H, int I, int bits, int group, uint64_t off[7]) {
+    if (group == 0) {
+        oq_blob_layout(H, I, bits, off);
+        return;
+    }
+    uint64_t gate = (uint64_t)I * (uint64_t)H * (uint64_t)bits / 8u;
+    uint64_t down = (uint64_t)H * (uint64_t)I * (uint64_t)bits / 8u;
+    uint64_t sgu = 4u * (uint64_t)I * (uint64_t)(H / group), sd = 4u * (uint64_t)H * (uint64_t)(I / group);
+    off[0] = 0;
+    off[1] = al256(off[0] + gate);
+    off[2] = al256(off[1] + gate);
+    off[3] = al256(off[2] + down);
+    off[4] = al256(off[3] + sgu);
+    off[5] = al256(off[4] + sgu);
+    off[6] = al256(off[5] + sd);
+}
+
 /* ------------------------------------------------------------------------
  * Row dot product of an integer weight row with a Q8_0 vector.
  * isum_b = sum_{j<32} w_{32b+j} * q_{32b+j} exactly in int32 (|isum| <=
@@ -178,6 +203,22 @@ float oq_row_dot(const int8_t *w, const int8_t *q, const float *d, int n, float 
     for (int b = 0; b < n / 32; ++b)
         acc = fmaf(d[b], (float)oq_block_isum(w + 32 * b, q + 32 * b), acc);
     return acc * row_scale;
+}
+
+/* Row dot with group scales [GS64]: gs[g] scales codes g*group ..
+ * (g+1)*group - 1 of the row (group a multiple of 32).  The weight of code j
+ * is gs[j / group] * w_j, so block b contributes d_b * gs[g(b)] * isum_b.
+ * Reading for the order: the same chain over blocks, the block's
+ * multiplier being the binary32 product d_b * gs[g(b)]:
+ *   acc = 0; for b ascending: acc = fmaf(d_b * gs[32 b / group], isum_b, acc)
+ * and no scale after the chain. */
+float oq_row_dot_g(const int8_t *w, const int8_t *q, const float *d, int n, const float *gs, int group) {
+    float acc = 0.0f;
+    for (int b = 0; b < n / 32; ++b) {
+        float m = d[b] * gs[(32 * b) / group];
+        acc = fmaf(m, (float)oq_block_isum(w + 32 * b, q + 32 * b), acc);
+    }
+    return acc;
 }
 
 /* ------------------------------------------------------------------------
@@ -267,10 +308,11 @@ int oq_select(const float *logit, const float *bias, int E, int K, float rsf, in
  * Reading: the down projection consumes Q8_0(h) like every other integer
  * dot in the layer.  Optional debug outputs may be NULL.
  * ---------------------------------------------------------------------- */
-int oq_expert(const uint8_t *blob, int H, int I, int bits, const int8_t *qx, const float *dx,
-              float *y, float *g_out, float *u_out, float *h_out, int8_t *qh_out, float *dh_out) {
+int oq_expert_g(const uint8_t *blob, int H, int I, int bits, int group, const int8_t *qx, const float *dx,
+                float *y, float *g_out, float *u_out, float *h_out, int8_t *qh_out, float *dh_out) {
+    if (group != 0 && (group % 32 != 0 || H % group != 0 || I % group != 0)) return OQ_EINVAL;
     uint64_t off[7];
-    oq_blob_layout(H, I, bits, off);
+    oq_blob_layout_g(H, I, bits, group, off);
     int n = H > I ? H : I;
     int8_t *row = (int8_t *)malloc((size_t)n);
     float *g = (float *)malloc(sizeof(float) * (size_t)I);
@@ -286,17 +328,18 @@ int oq_expert(const uint8_t *blob, int H, int I, int bits, const int8_t *qx, con
     const float *s_u = (const float *)(blob + off[4]);
     const float *s_d = (const float *)(blob + off[5]);
     uint64_t hrow = (uint64_t)H * (uint64_t)bits / 8u, irow = (uint64_t)I * (uint64_t)bits / 8u;
+    int hg = group ? H / group : 0, ig = group ? I / group : 0;
     for (int i = 0; i < I; ++i) {
         oq_unpack(blob + off[0] + (uint64_t)i * hrow, H, bits, row);
-        g[i] = oq_row_dot(row, qx, dx, H, s_g[i]);
+        g[i] = group ? oq_row_dot_g(row, qx, dx, H, s_g + (size_t)i * hg, group) : oq_row_dot(row, qx, dx, H, s_g[i]);
         oq_unpack(blob + off[1] + (uint64_t)i * hrow, H, bits, row);
-        u[i] = oq_row_dot(row, qx, dx, H, s_u[i]);
+        u[i] = group ? oq_row_dot_g(row, qx, dx, H, s_u + (size_t)i * hg, group) : oq_row_dot(row, qx, dx, H, s_u[i]);
         h[i] = oq_swiglu(g[i], u[i]);
     }
     oq_q8_0(h, I, qh, dh);
     for (int r = 0; r < H; ++r) {
         oq_unpack(blob + off[2] + (uint64_t)r * irow, I, bits, row);
-        y[r] = oq_row_dot(row, qh, dh, I, s_d[r]);
+        y[r] = group ? oq_row_dot_g(row, qh, dh, I, s_d + (size_t)r * ig, group) : oq_row_dot(row, qh, dh, I, s_d[r]);
     }
     if (g_out) memcpy(g_out, g, sizeof(float) * (size_t)I);
     if (u_out) memcpy(u_out, u, sizeof(float) * (size_t)I);
@@ -305,6 +348,11 @@ int oq_expert(const uint8_t *blob, int H, int I, int bits, const int8_t *qx, con
     if (dh_out) memcpy(dh_out, dh, sizeof(float) * (size_t)(I / 32));
     free(row); free(g); free(u); free(h); free(qh); free(dh);
     return OQ_OK;
+}
+
+int oq_expert(const uint8_t *blob, int H, int I, int bits, const int8_t *qx, const float *dx,
+              float *y, float *g_out, float *u_out, float *h_out, int8_t *qh_out, float *dh_out) {
+    return oq_expert_g(blob, H, I, bits, 0, qx, dx, y, g_out, u_out, h_out, qh_out, dh_out);
 }
 
 static int dims_ok(int H, int I, int E, int K, int n_shared, int bits) {
@@ -356,10 +404,11 @@ int oq_moe_route(int H, int E, int K, float rsf, int norm, int S, const float *x
  * after the routed sum; without a shared expert out is the routed sum.
  * blobs[e] == NULL marks expert e as not resident.
  * ---------------------------------------------------------------------- */
-int oq_moe_forward(int H, int I, int E, int K, int n_shared, int bits, int S, const float *x,
-                   const int32_t *idx, const float *w, const uint8_t *const *blobs,
-                   const uint8_t *shared_blob, float *out) {
+int oq_moe_forward_g(int H, int I, int E, int K, int n_shared, int bits, int group, int S, const float *x,
+                     const int32_t *idx, const float *w, const uint8_t *const *blobs,
+                     const uint8_t *shared_blob, float *out) {
     if (!dims_ok(H, I, E, K, n_shared, bits) || S < 0) return OQ_EINVAL;
+    if (group != 0 && (group % 32 != 0 || H % group != 0 || I % group != 0)) return OQ_EINVAL;
     if (n_shared && !shared_blob) return OQ_ENOTRESIDENT;
     if (!all_finite(x, (size_t)S * (size_t)H) || !all_finite(w, (size_t)S * (size_t)K))
         return OQ_ENONFINITE;
@@ -380,10 +429,10 @@ int oq_moe_forward(int H, int I, int E, int K, int n_shared, int bits, int S, co
     for (int t = 0; t < S && rc == OQ_OK; ++t) {
         oq_q8_0(x + (size_t)t * H, H, qx, dx);
         for (int k = 0; k < K && rc == OQ_OK; ++k)
-            rc = oq_expert(blobs[idx[(size_t)t * K + k]], H, I, bits, qx, dx, y + (size_t)k * H,
-                           NULL, NULL, NULL, NULL, NULL);
+            rc = oq_expert_g(blobs[idx[(size_t)t * K + k]], H, I, bits, group, qx, dx, y + (size_t)k * H,
+                             NULL, NULL, NULL, NULL, NULL);
         if (rc == OQ_OK && n_shared)
-            rc = oq_expert(shared_blob, H, I, bits, qx, dx, ysh, NULL, NULL, NULL, NULL, NULL);
+            rc = oq_expert_g(shared_blob, H, I, bits, group, qx, dx, ysh, NULL, NULL, NULL, NULL, NULL);
         for (int r = 0; r < H && rc == OQ_OK; ++r) {
             float acc = 0.0f;
             for (int k = 0; k < K; ++k) acc = fmaf(w[(size_t)t * K + k], y[(size_t)k * H + r], acc);
@@ -392,6 +441,12 @@ int oq_moe_forward(int H, int I, int E, int K, int n_shared, int bits, int S, co
     }
     free(qx); free(dx); free(y); free(ysh);
     return rc;
+}
+
+int oq_moe_forward(int H, int I, int E, int K, int n_shared, int bits, int S, const float *x,
+                   const int32_t *idx, const float *w, const uint8_t *const *blobs,
+                   const uint8_t *shared_blob, float *out) {
+    return oq_moe_forward_g(H, I, E, K, n_shared, bits, 0, S, x, idx, w, blobs, shared_blob, out);
 }
 
 /* Whole layer: routing then forward. */

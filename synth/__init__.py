@@ -108,36 +108,43 @@ class LayerSpec:
     wbits: int
     routed_scaling_factor: float = 2.5
     norm_topk_prob: int = 1
+    group: int = 0          # 0: one scale per row; 64: one per 64 codes of a row
 
     @property
     def blob_bytes(self) -> int:
-        return blob_layout(self.hidden, self.inter, self.wbits)["total"]
+        return blob_layout(self.hidden, self.inter, self.wbits, self.group)["total"]
 
 
 TINY = LayerSpec(hidden=256, inter=128, n_experts=16, top_k=2, n_shared=1, wbits=4)
 GLM = LayerSpec(hidden=6144, inter=2048, n_experts=256, top_k=8, n_shared=1, wbits=4)
 GLM_INT8 = dataclasses.replace(GLM, wbits=8)
 GLM_INT2 = dataclasses.replace(GLM, wbits=2)
+TINY_GS64 = dataclasses.replace(TINY, group=64)
+GLM_GS64 = dataclasses.replace(GLM, group=64)
 
 
-def blob_layout(hidden: int, inter: int, bits: int) -> dict:
+def blob_layout(hidden: int, inter: int, bits: int, group: int = 0) -> dict:
     """Byte offsets of the six sections of one expert blob.
 
     [gate codes: inter rows x hidden*bits/8][up codes: same][down codes:
     hidden rows x inter*bits/8][gate scales f32 x inter][up scales f32 x
     inter][down scales f32 x hidden]; every section starts on a 256-byte
-    boundary and the total is rounded up to 256 bytes.
+    boundary and the total is rounded up to 256 bytes.  With group > 0 the
+    scale sections hold one f32 per `group` codes of a row, row-major:
+    [inter][hidden/group], [inter][hidden/group], [hidden][inter/group].
     """
     a = lambda n: (n + 255) // 256 * 256  # noqa: E731
     gate = inter * hidden * bits // 8
     down = hidden * inter * bits // 8
+    sgu = 4 * inter * (hidden // group if group else 1)
+    sd = 4 * hidden * (inter // group if group else 1)
     off = {"gate": 0}
     off["up"] = a(gate)
     off["down"] = a(off["up"] + gate)
     off["s_gate"] = a(off["down"] + down)
-    off["s_up"] = a(off["s_gate"] + 4 * inter)
-    off["s_down"] = a(off["s_up"] + 4 * inter)
-    off["total"] = a(off["s_down"] + 4 * hidden)
+    off["s_up"] = a(off["s_gate"] + sgu)
+    off["s_down"] = a(off["s_up"] + sgu)
+    off["total"] = a(off["s_down"] + sd)
     return off
 
 
@@ -159,6 +166,14 @@ def quantize_rows(w: np.ndarray, bits: int) -> tuple[np.ndarray, np.ndarray]:
         q = np.where(s64[:, None] > 0, _round_half_away(w / s64[:, None]), 0.0)
     q = np.clip(q, lo, hi).astype(np.int8)
     return q, s
+
+
+def quantize_groups(w: np.ndarray, bits: int, group: int) -> tuple[np.ndarray, np.ndarray]:
+    """quantize_rows applied to every `group` consecutive weights of a row:
+    codes [rows, cols], scales [rows, cols / group]."""
+    rows, cols = w.shape
+    q, s = quantize_rows(np.asarray(w).reshape(rows * (cols // group), group), bits)
+    return q.reshape(rows, cols), s.reshape(rows, cols // group)
 
 
 def pack_codes(codes: np.ndarray, bits: int) -> np.ndarray:
@@ -187,8 +202,8 @@ def pack_codes(codes: np.ndarray, bits: int) -> np.ndarray:
     raise ValueError(bits)
 
 
-def assemble_blob(hidden, inter, bits, gate_codes, up_codes, down_codes, s_gate, s_up, s_down):
-    lay = blob_layout(hidden, inter, bits)
+def assemble_blob(hidden, inter, bits, gate_codes, up_codes, down_codes, s_gate, s_up, s_down, group=0):
+    lay = blob_layout(hidden, inter, bits, group)
     blob = np.zeros(lay["total"], dtype=np.uint8)
 
     def put(name, arr):
@@ -205,21 +220,22 @@ def assemble_blob(hidden, inter, bits, gate_codes, up_codes, down_codes, s_gate,
 
 
 def gaussian_expert(seed: int, layer: int, expert: int, spec: LayerSpec, sigma: float = 0.02):
-    """Expert weights w ~ N(0, sigma), per-row quantised.
+    """Expert weights w ~ N(0, sigma), per-row (or, with spec.group, per
+    row-group) quantised.
 
     Returns (blob, parts) where parts holds the codes and scales of the
     three matrices (gate/up [inter, hidden], down [hidden, inter]).
     """
-    H, I, b = spec.hidden, spec.inter, spec.wbits
+    H, I, b, G = spec.hidden, spec.inter, spec.wbits, spec.group
     parts = {}
     for m, (name, rows, cols) in enumerate((("gate", I, H), ("up", I, H), ("down", H, I))):
         key = stream_key(seed, K_WEIGHT, layer, expert, m)
         w = (normal(key, rows * cols) * sigma).astype(np.float32).reshape(rows, cols)
-        q, s = quantize_rows(w, b)
+        q, s = quantize_groups(w, b, G) if G else quantize_rows(w, b)
         parts[name] = q
         parts["s_" + name] = s
     blob = assemble_blob(H, I, b, parts["gate"], parts["up"], parts["down"],
-                         parts["s_gate"], parts["s_up"], parts["s_down"])
+                         parts["s_gate"], parts["s_up"], parts["s_down"], G)
     return blob, parts
 
 
@@ -246,9 +262,9 @@ def _load():
     global _lib
     if _lib is None:
         lib = ctypes.CDLL(build_lib())
-        lib.synth_fill_blob_cdf.restype = ctypes.c_uint64
-        lib.synth_fill_blob_cdf.argtypes = [
-            ctypes.POINTER(ctypes.c_uint64), ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        lib.synth_fill_blob_cdf_g.restype = ctypes.c_uint64
+        lib.synth_fill_blob_cdf_g.argtypes = [
+            ctypes.POINTER(ctypes.c_uint64), ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
             ctypes.c_void_p, ctypes.c_float, ctypes.c_float, ctypes.c_void_p, ctypes.c_int]
         _lib = lib
     return _lib
@@ -288,8 +304,8 @@ def cdf_expert_into(out_ptr: int, seed: int, layer: int, expert: int, spec: Laye
     nominal = 4.0 * sigma / QMAX[spec.wbits]
     if threads is None:
         threads = min(16, os.cpu_count() or 1)
-    n = lib.synth_fill_blob_cdf(keys, spec.hidden, spec.inter, spec.wbits,
-                                table.ctypes.data, nominal, 0.1, out_ptr, threads)
+    n = lib.synth_fill_blob_cdf_g(keys, spec.hidden, spec.inter, spec.wbits, spec.group,
+                                  table.ctypes.data, nominal, 0.1, out_ptr, threads)
     if n != spec.blob_bytes:
         raise RuntimeError("synth_fill_blob_cdf rejected the shape")
     return int(n)

@@ -13,7 +13,8 @@
  *
  * Codes are drawn i.i.d. from a caller-supplied 65536-entry table that maps a
  * 16-bit uniform to a signed code (the caller builds it from the CDF of a
- * quantised Gaussian).  Row scales are nominal * (1 + jitter * (u - 0.5)).
+ * quantised Gaussian).  Row (or row-group) scales are
+ * nominal * (1 + jitter * (u - 0.5)).
  */
 #include <stdint.h>
 #include <string.h>
@@ -55,13 +56,15 @@ static void pack_row(const int8_t *q, int ncols, int bits, uint8_t *dst) {
 }
 
 /*
- * Fills one matrix section (rows x cols codes) and its scale section.
- * key_codes / key_scales select the two random streams.
+ * Fills one matrix section (rows x cols codes) and its scale section: one
+ * scale per row, or with group > 0 one per `group` codes of a row (row-major
+ * [rows][cols / group]).  key_codes / key_scales select the two random streams.
  */
-static void fill_matrix(uint64_t key_codes, uint64_t key_scales, int rows, int cols, int bits,
+static void fill_matrix(uint64_t key_codes, uint64_t key_scales, int rows, int cols, int bits, int group,
                         const int8_t *table, float scale_nominal, float scale_jitter,
                         uint8_t *codes_out, float *scales_out, int nthreads) {
     int row_bytes = cols * bits / 8;
+    int ns = group ? cols / group : 1;
 #pragma omp parallel for schedule(static) num_threads(nthreads)
     for (int r = 0; r < rows; ++r) {
         int8_t q[32768];
@@ -74,9 +77,12 @@ static void fill_matrix(uint64_t key_codes, uint64_t key_scales, int rows, int c
             q[4 * g + 3] = table[(u >> 48) & 0xFFFF];
         }
         pack_row(q, cols, bits, codes_out + (uint64_t)r * (uint64_t)row_bytes);
-        uint64_t us = stream_at(key_scales, (uint64_t)r);
-        double uu = (double)(us >> 11) * (1.0 / 9007199254740992.0);
-        scales_out[r] = (float)((double)scale_nominal * (1.0 + (double)scale_jitter * (uu - 0.5)));
+        for (int g = 0; g < ns; ++g) {
+            uint64_t us = stream_at(key_scales, (uint64_t)r * (uint64_t)ns + (uint64_t)g);
+            double uu = (double)(us >> 11) * (1.0 / 9007199254740992.0);
+            scales_out[(uint64_t)r * (uint64_t)ns + (uint64_t)g] =
+                (float)((double)scale_nominal * (1.0 + (double)scale_jitter * (uu - 0.5)));
+        }
     }
 }
 
@@ -85,27 +91,37 @@ static void fill_matrix(uint64_t key_codes, uint64_t key_scales, int rows, int c
  * each section starting on a 256-byte boundary.  `keys` holds six stream keys:
  * codes and scales for gate, up and down.  Returns the number of bytes written.
  */
-uint64_t synth_fill_blob_cdf(const uint64_t *keys, int hidden, int inter, int bits,
-                             const int8_t *table, float scale_nominal, float scale_jitter,
-                             uint8_t *out, int nthreads) {
+uint64_t synth_fill_blob_cdf_g(const uint64_t *keys, int hidden, int inter, int bits, int group,
+                               const int8_t *table, float scale_nominal, float scale_jitter,
+                               uint8_t *out, int nthreads) {
     if (hidden <= 0 || inter <= 0 || hidden % 32 || inter % 32 || hidden > 32768 || inter > 32768)
         return 0;
     if (bits != 8 && bits != 4 && bits != 2) return 0;
+    if (group != 0 && (group % 32 || hidden % group || inter % group)) return 0;
     uint64_t gate_bytes = (uint64_t)inter * (uint64_t)(hidden * bits / 8);
     uint64_t down_bytes = (uint64_t)hidden * (uint64_t)(inter * bits / 8);
+    uint64_t sgu = 4ull * (uint64_t)inter * (uint64_t)(group ? hidden / group : 1);
+    uint64_t sd = 4ull * (uint64_t)hidden * (uint64_t)(group ? inter / group : 1);
     uint64_t off_g = 0;
     uint64_t off_u = align256(off_g + gate_bytes);
     uint64_t off_d = align256(off_u + gate_bytes);
     uint64_t off_sg = align256(off_d + down_bytes);
-    uint64_t off_su = align256(off_sg + 4ull * (uint64_t)inter);
-    uint64_t off_sd = align256(off_su + 4ull * (uint64_t)inter);
-    uint64_t total = align256(off_sd + 4ull * (uint64_t)hidden);
+    uint64_t off_su = align256(off_sg + sgu);
+    uint64_t off_sd = align256(off_su + sgu);
+    uint64_t total = align256(off_sd + sd);
     memset(out, 0, total);
-    fill_matrix(keys[0], keys[1], inter, hidden, bits, table, scale_nominal, scale_jitter,
+    fill_matrix(keys[0], keys[1], inter, hidden, bits, group, table, scale_nominal, scale_jitter,
                 out + off_g, (float *)(out + off_sg), nthreads);
-    fill_matrix(keys[2], keys[3], inter, hidden, bits, table, scale_nominal, scale_jitter,
+    fill_matrix(keys[2], keys[3], inter, hidden, bits, group, table, scale_nominal, scale_jitter,
                 out + off_u, (float *)(out + off_su), nthreads);
-    fill_matrix(keys[4], keys[5], hidden, inter, bits, table, scale_nominal, scale_jitter,
+    fill_matrix(keys[4], keys[5], hidden, inter, bits, group, table, scale_nominal, scale_jitter,
                 out + off_d, (float *)(out + off_sd), nthreads);
     return total;
+}
+
+uint64_t synth_fill_blob_cdf(const uint64_t *keys, int hidden, int inter, int bits,
+                             const int8_t *table, float scale_nominal, float scale_jitter,
+                             uint8_t *out, int nthreads) {
+    return synth_fill_blob_cdf_g(keys, hidden, inter, bits, 0, table, scale_nominal, scale_jitter, out,
+                                 nthreads);
 }

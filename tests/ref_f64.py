@@ -65,6 +65,27 @@ def matvec_q(codes, scales, q, d):
     return y, bound
 
 
+def matvec_qg(codes, gscales, q, d):
+    """Group-scaled rows: gscales [R, n / group], code j of row r weighted by
+    gscales[r, j / group]: y_r = sum_b d_b * s_{r, g(b)} * isum_{r,b} in
+    float64, with the bound of a binary32 fma chain over the blocks whose
+    multipliers d_b * s are themselves rounded:
+    |y32 - y64| <= ((nb + 2) * u) * sum_b |d_b s isum_b| (+ tiny)."""
+    isum = block_isums(codes, q[None, :]).astype(np.float64)     # [R, nb]
+    gs = np.asarray(gscales, np.float64)
+    nb = isum.shape[1]
+    per_block = np.repeat(gs, nb // gs.shape[1], axis=1)          # [R, nb]
+    terms = isum * np.asarray(d, np.float64)[None, :] * per_block
+    y = np.array([math.fsum(t) for t in terms])
+    bound = (nb + 3) * U32 * np.abs(terms).sum(1) + 2.0 ** -149
+    return y, bound
+
+
+def _matvec_any(codes, scales, q, d):
+    s = np.asarray(scales)
+    return matvec_qg(codes, s, q, d) if s.ndim == 2 else matvec_q(codes, s, q, d)
+
+
 def swiglu64(g, u):
     g = np.asarray(g, np.float64)
     u = np.asarray(u, np.float64)
@@ -86,12 +107,13 @@ def full_sort_topk(score, K):
 def expert64(parts, qx, dx, qh_override=None, near=1e-4):
     """One expert on one token in float64 from unpacked codes.
 
-    parts: dict with gate/up [I,H] codes, down [H,I] codes, s_gate/s_up/s_down.
+    parts: dict with gate/up [I,H] codes, down [H,I] codes, s_gate/s_up/s_down
+    (per-row vectors, or [rows, cols / group] arrays of group scales).
     Returns dict g, u, h, qh, dh, y, and nflips: the number of h codes taken
     from qh_override because the float64 value sits within `near` of a
     rounding boundary (only when qh_override is given)."""
-    g, _ = matvec_q(parts["gate"], parts["s_gate"], qx, dx)
-    u, _ = matvec_q(parts["up"], parts["s_up"], qx, dx)
+    g, _ = _matvec_any(parts["gate"], parts["s_gate"], qx, dx)
+    u, _ = _matvec_any(parts["up"], parts["s_up"], qx, dx)
     h = swiglu64(g, u)
     qh, dh, nt = q8_0_f64(h, near)
     nflips = 0
@@ -99,7 +121,7 @@ def expert64(parts, qx, dx, qh_override=None, near=1e-4):
         take = nt & (qh != qh_override)
         nflips = int(take.sum())
         qh = np.where(nt, qh_override, qh)
-    y, _ = matvec_q(parts["down"], parts["s_down"], qh, dh)
+    y, _ = _matvec_any(parts["down"], parts["s_down"], qh, dh)
     return {"g": g, "u": u, "h": h, "qh": qh, "dh": dh, "y": y, "nflips": nflips}
 
 
