@@ -59,6 +59,10 @@ typedef struct coli_moe_dims {
     int32_t wbits;                /* 8, 4 or 2: weight code width */
     float routed_scaling_factor;  /* multiplies the gate weights */
     int32_t norm_topk_prob;       /* 1: weights renormalised over the K selected */
+    int32_t group_size;           /* 0: one f32 scale per weight row; with wbits = 4, a power of two in 32..512
+                                     dividing H and I: one f32 scale per group_size consecutive codes
+                                     of a row (JustVugg/colibri, "Get started" / "Other supported
+                                     models": the group-scaled "int4-g64" containers) */
 } coli_moe_dims;
 
 /*
@@ -70,7 +74,12 @@ typedef struct coli_moe_dims {
  * Codes per 32-element block: int8 as bytes; int4 16 bytes, byte j = code j
  * (bits 0-3) | code j+16 (bits 4-7); int2 8 bytes, byte j = code j+8i in bits
  * 2i..2i+1.  Two's complement.  (README v1.0 "The idea": about 19 MB per
- * expert at int4; GLM-5.2 shape gives 18 915 328 bytes.)
+ * expert at int4; GLM-5.2 shape gives 18 915 328 bytes.)  With group_size
+ * G > 0 the three scale sections hold one f32 per G codes of a row,
+ * row-major: gate and up [I][H/G], down [H][I/G] (21 233 664 bytes at the
+ * GLM-5.2 shape with G = 64, int4).  A row's dot product is then
+ * acc = fmaf(d_b * s[row][32 b / G], isum_b, acc) over blocks b ascending
+ * (d_b the activation block scale), with no scale after the chain.
  * Returns 0 when dims are invalid.
  */
 size_t coli_moe_expert_bytes(const coli_moe_dims *dims);

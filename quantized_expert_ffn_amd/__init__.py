@@ -42,6 +42,7 @@ class coli_moe_dims(ctypes.Structure):
         ("hidden", ctypes.c_int32), ("inter", ctypes.c_int32), ("n_experts", ctypes.c_int32),
         ("top_k", ctypes.c_int32), ("n_shared", ctypes.c_int32), ("wbits", ctypes.c_int32),
         ("routed_scaling_factor", ctypes.c_float), ("norm_topk_prob", ctypes.c_int32),
+        ("group_size", ctypes.c_int32),
     ]
 
 
@@ -89,7 +90,7 @@ def make_dims(spec) -> coli_moe_dims:
     """coli_moe_dims from any object with the dims' field names."""
     return coli_moe_dims(int(spec.hidden), int(spec.inter), int(spec.n_experts), int(spec.top_k),
                          int(spec.n_shared), int(spec.wbits), float(spec.routed_scaling_factor),
-                         int(spec.norm_topk_prob))
+                         int(spec.norm_topk_prob), int(getattr(spec, "group", 0)))
 
 
 def _dims(d):

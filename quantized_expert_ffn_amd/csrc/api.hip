@@ -65,6 +65,10 @@ int check_dims(const coli_moe_dims *d) {
         return fail(COLI_EINVAL, "n_shared=%d: must be 0 or 1", d->n_shared);
     if (d->wbits != 8 && d->wbits != 4 && d->wbits != 2)
         return fail(COLI_EINVAL, "wbits=%d: must be 8, 4 or 2", d->wbits);
+    const int g = d->group_size;
+    if (g != 0 && (g < 32 || g > 512 || (g & (g - 1)) != 0 || d->hidden % g != 0 || d->inter % g != 0))
+        return fail(COLI_EINVAL, "group_size=%d: must be 0 or a power of two in 32..512 dividing hidden and inter", g);
+    if (g != 0 && d->wbits != 4) return fail(COLI_EINVAL, "group_size=%d needs wbits=4 (group-scaled int4)", g);
     return COLI_OK;
 }
 
@@ -95,17 +99,29 @@ int g_force_path = 0;
 // Batches of more than GROUPED_MIN_S - 1 tokens take the grouped kernels.
 constexpr int GROUPED_MIN_S = 9;
 
-bool use_grouped(int S) { return g_force_path == 3 || (g_force_path == 0 && S >= GROUPED_MIN_S); }
+// The grouped kernels take per-row scales only; group-scaled weights run the
+// multi-launch kernels at every batch size.
+bool use_grouped(int S, int group) {
+    return group == 0 && (g_force_path == 3 || (g_force_path == 0 && S >= GROUPED_MIN_S));
+}
 
 // LDS of the kernels a forward of S tokens launches.
 size_t forward_lds(const coli_moe_dims *d, int S) {
-    if (use_grouped(S)) return coli::pf_group_smem(S, d->top_k, d->n_experts);
-    return coli::forward_smem_max(S, d->hidden, d->inter, d->n_experts, d->top_k, d->n_shared);
+    if (use_grouped(S, d->group_size)) return coli::pf_group_smem(S, d->top_k, d->n_experts);
+    return coli::forward_smem_max(S, d->hidden, d->inter, d->n_experts, d->top_k, d->n_shared, d->group_size);
+}
+
+// A forced kernel family that does not take the call's weights.
+int forced_path_refused(const coli_moe_dims *d) {
+    if (d->group_size && (g_force_path == 2 || g_force_path == 3))
+        return fail(COLI_EINVAL, "group-scaled weights run the multi-launch kernels only (forced path %d)",
+                    g_force_path);
+    return COLI_OK;
 }
 
 // The persistent kernel takes small batches whose experts are all resident.
 bool persistent_fits(const coli_moe_dims *d, int S, bool pending) {
-    if (pending || S > 8) return false;
+    if (pending || S > 8 || d->group_size) return false;
     return coli::layer_smem(S, d->hidden, d->inter, d->n_experts, d->top_k, d->n_shared) <= 160 * 1024;
 }
 
@@ -179,6 +195,7 @@ FwdArgs fwd_args(const coli_moe_dims *d, int S, const float *x, const int32_t *i
     a.E = d->n_experts;
     a.K = d->top_k;
     a.n_shared = d->n_shared;
+    a.group = d->group_size;
     return a;
 }
 
@@ -231,7 +248,7 @@ int forward_launches(FwdArgs &a, int bits, bool any_pending, void *pending_ready
         timing_after(KK_QUANT_X, st);
         if (e != hipSuccess) return hip_fail(e, "Q8_0(x) launch");
     }
-    if (use_grouped(a.S)) {
+    if (use_grouped(a.S, a.group)) {
         // grouped kernels: the unit table and tiles, then gate/up and down as
         // int8 matrix-core products per (rows, tile), then the combine.  They
         // do not split resident from pending experts: all wait for the copies.
@@ -274,7 +291,7 @@ int forward_launches(FwdArgs &a, int bits, bool any_pending, void *pending_ready
     e = launch_gateup(a, bits, st);
     timing_after(KK_GATEUP, st);
     if (e != hipSuccess) return hip_fail(e, "gate/up launch");
-    if (a.S <= 8 && down_rows_smem(a.S, a.I, a.E, a.K, a.n_shared) <= 64 * 1024) {
+    if (a.S <= 8 && down_rows_smem(a.S, a.I, a.E, a.K, a.n_shared, a.group, bits) <= 64 * 1024) {
         timing_before(KK_DOWN, st);
         e = launch_down_rows(a, bits, st);
         timing_after(KK_DOWN, st);
@@ -298,7 +315,7 @@ extern "C" {
 
 size_t coli_moe_expert_bytes(const coli_moe_dims *d) {
     if (check_dims(d) != COLI_OK) return 0;
-    return blob_layout(d->hidden, d->inter, d->wbits).total;
+    return blob_layout(d->hidden, d->inter, d->wbits, d->group_size).total;
 }
 
 size_t coli_moe_workspace_bytes(const coli_moe_dims *d, int32_t max_tokens) {
@@ -340,6 +357,7 @@ int coli_moe_forward(const coli_moe_dims *d, int32_t S, const float *x, const in
     const WsLayout L = ws_layout(d->hidden, d->inter, d->n_experts, d->top_k, S);
     if (ws_bytes < L.total)
         return fail(COLI_EWORKSPACE, "workspace %zu bytes < %zu needed for %d tokens", ws_bytes, L.total, S);
+    if ((rc = forced_path_refused(d))) return rc;
     const size_t smem = forward_lds(d, S);
     if (smem > 160 * 1024)
         return fail(COLI_EINVAL, "shape needs %zu bytes of LDS per workgroup (> 160 KiB)", smem);
@@ -388,6 +406,7 @@ int coli_moe_layer(const coli_moe_dims *d, int32_t S, const float *x, const floa
     const WsLayout L = ws_layout(d->hidden, d->inter, d->n_experts, d->top_k, S);
     if (ws_bytes < L.total)
         return fail(COLI_EWORKSPACE, "workspace %zu bytes < %zu needed for %d tokens", ws_bytes, L.total, S);
+    if ((rc = forced_path_refused(d))) return rc;
     if (g_force_path == 2 && !persistent_fits(d, S, false))
         return fail(COLI_EINVAL, "persistent kernel forced but the call has more than 8 tokens or a shape beyond "
                                  "its LDS budget");
@@ -401,7 +420,7 @@ int coli_moe_layer(const coli_moe_dims *d, int32_t S, const float *x, const floa
             return fail(COLI_EINVAL, "shape needs %zu bytes of LDS per workgroup (> 160 KiB)", smem);
         // up to ROUTE_FUSE_MAX tokens: one router launch also selects the
         // routing and writes the call's unit table, which the expert kernels read
-        if (S <= ROUTE_FUSE_MAX && !use_grouped(S)) {
+        if (S <= ROUTE_FUSE_MAX && !use_grouped(S, d->group_size)) {
             RouteArgs r;
             std::memset(&r, 0, sizeof r);
             r.x = x;
@@ -428,6 +447,7 @@ int coli_moe_layer(const coli_moe_dims *d, int32_t S, const float *x, const floa
             r.dh = a.dh;
             r.I = d->inter;
             r.bits = d->wbits;
+            r.group = d->group_size;
             // the shared expert's gate/up tiles run in the router launch when
             // they are short enough to finish beside it (one pass over at
             // most 256 KiB of rows per workgroup) and their LDS fits there

@@ -346,17 +346,22 @@ struct BlobLayout {
     size_t gate, up, down, s_gate, s_up, s_down, total;
 };
 
-__host__ __device__ inline BlobLayout blob_layout(int H, int I, int bits) {
+// Expert blob sections.  group = 0: one f32 scale per row; group > 0: one
+// per `group` codes of a row, row-major ([I][H / group] for gate and up,
+// [H][I / group] for down).
+__host__ __device__ inline BlobLayout blob_layout(int H, int I, int bits, int group = 0) {
     BlobLayout L;
     const size_t gate = (size_t)I * (size_t)H * (size_t)bits / 8;
     const size_t down = (size_t)H * (size_t)I * (size_t)bits / 8;
+    const size_t sgu = 4 * (size_t)I * (size_t)(group ? H / group : 1);
+    const size_t sd = 4 * (size_t)H * (size_t)(group ? I / group : 1);
     L.gate = 0;
     L.up = align256(L.gate + gate);
     L.down = align256(L.up + gate);
     L.s_gate = align256(L.down + down);
-    L.s_up = align256(L.s_gate + 4 * (size_t)I);
-    L.s_down = align256(L.s_up + 4 * (size_t)I);
-    L.total = align256(L.s_down + 4 * (size_t)H);
+    L.s_up = align256(L.s_gate + sgu);
+    L.s_down = align256(L.s_up + sgu);
+    L.total = align256(L.s_down + sd);
     return L;
 }
 

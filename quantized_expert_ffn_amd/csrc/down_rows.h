@@ -40,9 +40,12 @@ struct DownRowsBatch {
 
 // LDS of one down tile (from `base`).
 struct DownTilePlan {
-    size_t qh, dh, isum, sdn, y, end;
+    size_t qh, dh, isum, sdn, y, gs, end;
 };
-__host__ __device__ inline DownTilePlan down_tile_plan(size_t base, int S, int K, int E, int n_shared, int I) {
+// group > 0: room for the group scales of one batch of units (UB units x
+// DR_ROWS rows x I / group scales).
+__host__ __device__ inline DownTilePlan down_tile_plan(size_t base, int S, int K, int E, int n_shared, int I,
+                                                       int group = 0, int ub = 0) {
     DownTilePlan p;
     const int P = S * K;
     const int umax = (P < E ? P : E) + 1;
@@ -53,13 +56,14 @@ __host__ __device__ inline DownTilePlan down_tile_plan(size_t base, int S, int K
     p.isum = a16(p.dh + 4 * (size_t)mpb * round_up(I / 32, 64));
     p.sdn = a16(p.isum + 4 * (size_t)DR_W * DR_RPW * mpb * ISUM_PITCH);
     p.y = a16(p.sdn + 4 * (size_t)umax * DR_ROWS);
-    p.end = a16(p.y + 4 * (size_t)slots * DR_ROWS);
+    p.gs = a16(p.y + 4 * (size_t)slots * DR_ROWS);
+    p.end = a16(p.gs + (group ? 4 * (size_t)ub * DR_ROWS * (I / group) : 0));
     return p;
 }
 
 // One down tile.  COHERENT: Q8_0(h) was written earlier in the same launch
 // by other workgroups, so it is read with device-scope loads.
-template <int BITS, bool ONE_TOKEN, bool COHERENT>
+template <int BITS, bool ONE_TOKEN, bool COHERENT, bool GROUPED = false>
 struct DownTile {
     static constexpr int UB = DownRowsBatch<BITS>::UB;
     const FwdArgs &a;
@@ -85,7 +89,7 @@ struct DownTile {
         dpitch = round_up(nbi, 64);
         m16 = fast_div_magic(a.I / 16);
         mnb = fast_div_magic(nbi);
-        BL = blob_layout(a.H, a.I, BITS);
+        BL = blob_layout(a.H, a.I, BITS, GROUPED ? a.group : 0);
         irow = (size_t)a.I * BITS / 8;
         ro = BL.down + (size_t)(rt * DR_ROWS + uniform(threadIdx.x >> 6) * DR_RPW) * irow;
     }
@@ -148,6 +152,17 @@ struct DownTile {
         const int npb = uniform(uoff[u1]) - pbase;
         const int cr = lane >> 4 >= DR_RPW ? 0 : lane >> 4, cp = lane & 15;   // chain lane (row, pair)
         const bool chain_lane = lane < DR_RPW * 16;
+        const int rl = wave * DR_RPW + cr;
+        // the chain lane's unit: the last one whose first pair is at or before its pair
+        auto unit_of_lane = [&]() {
+            int u = u0;
+            while (u + 1 < u1 && uoff[u + 1] <= pbase + cp) ++u;
+            return u;
+        };
+        const int ug = GROUPED ? unit_of_lane() : 0;
+        // group scales: one per 32 << lgb codes of a row, ngr per row
+        const int lgb = GROUPED ? group_lgb(a.group) : -1, ngr = GROUPED ? I / a.group : 0;
+        float *gsl = reinterpret_cast<float *>(smem + D.gs);
         float acc = 0.0f;
         // Q8_0(h) of the batch's pairs, their block scales and the down-row
         // scales of its units; the first round is issued before the weights
@@ -199,6 +214,14 @@ struct DownTile {
                 stage_store(qv, 0, nq, q_dst);
                 stage_store(dv, 0, nd, d_dst);
                 stage_store(sv, 0, ns, s_dst);
+                // the batch's group scales (rows r0 .. r0+7 of each unit),
+                // read after the weights were issued
+                for (int i = (int)threadIdx.x; GROUPED && i < (u1 - u0) * DR_ROWS * ngr; i += DR_T) {
+                    const int ur = i / ngr, g = i - ur * ngr;
+                    const uint8_t *blob = ublob[u0 + ur / DR_ROWS];
+                    gsl[i] = blob ? reinterpret_cast<const float *>(blob + BL.s_down)[(size_t)(r0 + ur % DR_ROWS) * ngr + g]
+                                  : 0.0f;
+                }
                 for (int rd = 1; !ONE && rd < nr; ++rd) {
                     stage_fetch(qv, rd, nq, q_src);
                     stage_fetch(dv, rd, nd, d_src);
@@ -227,17 +250,21 @@ struct DownTile {
                 }
             }
             wave_lds_sync();
-            if (chain_lane && cp < npb)
-                acc = chain_chunk(acc, isum + (cr * mpb + cp) * ISUM_PITCH, dh_l + cp * dpitch + c * 64,
-                                  min(64, nbi - c * 64));
+            if (chain_lane && cp < npb) {
+                if (GROUPED)
+                    acc = chain_chunk_g(acc, isum + (cr * mpb + cp) * ISUM_PITCH, dh_l + cp * dpitch + c * 64,
+                                        gsl + ((ug - u0) * DR_ROWS + rl) * ngr + c * (64 >> lgb), lgb,
+                                        min(64, nbi - c * 64));
+                else
+                    acc = chain_chunk(acc, isum + (cr * mpb + cp) * ISUM_PITCH, dh_l + cp * dpitch + c * 64,
+                                      min(64, nbi - c * 64));
+            }
             wave_lds_sync();
         }
         if (chain_lane && cp < npb) {
-            int ub = u0;   // the pair's unit: the last one whose first pair is at or before it
-            while (ub + 1 < u1 && uoff[ub + 1] <= pbase + cp) ++ub;
+            const int ub = GROUPED ? ug : unit_of_lane();
             const int slot = pairs[pbase + cp];
-            const int rl = wave * DR_RPW + cr;
-            y_l[slot * DR_ROWS + rl] = ublob[ub] ? acc * sdn[ub * DR_ROWS + rl] : 0.0f;
+            y_l[slot * DR_ROWS + rl] = ublob[ub] ? (GROUPED ? acc : acc * sdn[ub * DR_ROWS + rl]) : 0.0f;
         }
         __syncthreads();   // the next batch restages qh_l / dh_l
         return u1;

@@ -17,25 +17,27 @@ struct DownRowsPlan {
     size_t total;
 };
 
-__host__ __device__ inline DownRowsPlan down_rows_plan(int S, int K, int E, int n_shared, int I) {
+__host__ __device__ inline DownRowsPlan down_rows_plan(int S, int K, int E, int n_shared, int I, int group,
+                                                       int bits) {
     DownRowsPlan p;
     const int P = S * K;
     const int umax = (P < E ? P : E) + 1;
     p.T = smem_plan(S, K, E, 0, 0);
     p.ublob = a16(p.T.total);
     p.w = a16(p.ublob + 8 * (size_t)umax);
-    p.tile = down_tile_plan(p.w + 4 * (size_t)P, S, K, E, n_shared, I);
+    const int ub = bits == 8 ? DownRowsBatch<8>::UB : (bits == 4 ? DownRowsBatch<4>::UB : DownRowsBatch<2>::UB);
+    p.tile = down_tile_plan(p.w + 4 * (size_t)P, S, K, E, n_shared, I, group, ub);
     p.total = p.tile.end;
     return p;
 }
 
 // ONE_TOKEN: S == 1, so every unit has exactly one pair.
-template <int BITS, bool ONE_TOKEN>
-__global__ __launch_bounds__(DR_T) void k_down_rows(const FwdArgs a) {
+template <int BITS, bool ONE_TOKEN, bool GROUPED>
+__global__ __launch_bounds__(DR_T) __attribute__((amdgpu_waves_per_eu(3))) void k_down_rows(const FwdArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int tid = threadIdx.x;
     const int S = a.S, K = a.K, E = a.E, P = S * K;
-    const DownRowsPlan D = down_rows_plan(S, K, E, a.n_shared, a.I);
+    const DownRowsPlan D = down_rows_plan(S, K, E, a.n_shared, a.I, a.group, BITS);
     const uint8_t **ublob = reinterpret_cast<const uint8_t **>(smem + D.ublob);
     float *w_l = reinterpret_cast<float *>(smem + D.w);
     const int *uexp = reinterpret_cast<const int *>(smem + D.T.uexp);
@@ -67,16 +69,16 @@ __global__ __launch_bounds__(DR_T) void k_down_rows(const FwdArgs a) {
         __syncthreads();
     }
     if (tid < n_units && ublob[tid] == nullptr) raise_status(a.status, ST_NOTRESIDENT);
-    DownTile<BITS, ONE_TOKEN, false> tile(a, smem, D.tile, uoff, pairs, ublob, w_l, n_units, blockIdx.x);
+    DownTile<BITS, ONE_TOKEN, false, GROUPED> tile(a, smem, D.tile, uoff, pairs, ublob, w_l, n_units, blockIdx.x);
     tile.run(false);
 }
 
-size_t down_rows_smem(int S, int I, int E, int K, int n_shared) {
-    return down_rows_plan(S, K, E, n_shared, I).total;
+size_t down_rows_smem(int S, int I, int E, int K, int n_shared, int group, int bits) {
+    return down_rows_plan(S, K, E, n_shared, I, group, bits).total;
 }
 
 hipError_t launch_down_rows(const FwdArgs &a, int bits, hipStream_t st) {
-    const size_t smem = down_rows_plan(a.S, a.K, a.E, a.n_shared, a.I).total;
+    const size_t smem = down_rows_plan(a.S, a.K, a.E, a.n_shared, a.I, a.group, bits).total;
     const dim3 grid(a.H / DR_ROWS);
     auto go = [&](auto kern) {
         const hipError_t e = ensure_dyn_smem(reinterpret_cast<const void *>(kern), smem);
@@ -84,9 +86,10 @@ hipError_t launch_down_rows(const FwdArgs &a, int bits, hipStream_t st) {
         return launch(kern, grid, dim3(DR_T), smem, st, a);
     };
     const bool one = a.S == 1;
-    if (bits == 8) return one ? go(k_down_rows<8, true>) : go(k_down_rows<8, false>);
-    if (bits == 4) return one ? go(k_down_rows<4, true>) : go(k_down_rows<4, false>);
-    return one ? go(k_down_rows<2, true>) : go(k_down_rows<2, false>);
+    if (a.group) return one ? go(k_down_rows<4, true, true>) : go(k_down_rows<4, false, true>);
+    if (bits == 8) return one ? go(k_down_rows<8, true, false>) : go(k_down_rows<8, false, false>);
+    if (bits == 4) return one ? go(k_down_rows<4, true, false>) : go(k_down_rows<4, false, false>);
+    return one ? go(k_down_rows<2, true, false>) : go(k_down_rows<2, false, false>);
 }
 
 }  // namespace coli

@@ -51,7 +51,7 @@ __device__ __forceinline__ const uint8_t *load_unit_table(const uint8_t *units, 
 // routed unit y - 1, where y = blockIdx.y + shared_done (the router launch
 // may already have run the shared expert's tiles).  Otherwise every
 // workgroup builds the unit table from topk_idx and takes unit blockIdx.y.
-template <int BITS, int NT, bool TABLE>
+template <int BITS, int NT, bool TABLE, bool GROUPED>
 __global__ __launch_bounds__(256) void k_gateup(const FwdArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
@@ -135,13 +135,14 @@ __global__ __launch_bounds__(256) void k_gateup(const FwdArgs a) {
         }
         __syncthreads();
     };
-    gateup_unit<BITS, NT>(blob, H, I, blockIdx.x * 32, pairs + p0, np, smem, L, a.qh, a.dh, stage);
+    gateup_unit<BITS, NT, GROUPED>(blob, H, I, a.group, blockIdx.x * 32, pairs + p0, np, smem, L, L.total, a.qh,
+                                   a.dh, stage);
 }
 
 // Down projection: 64 rows of one unit per workgroup, y written to the
 // pair's slot of the workspace (the combine kernel reads it after this
 // kernel has finished, so no cross-workgroup signalling is needed).
-template <int BITS, int NT>
+template <int BITS, int NT, bool GROUPED>
 __global__ __launch_bounds__(256) void k_down(const FwdArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
@@ -169,7 +170,7 @@ __global__ __launch_bounds__(256) void k_down(const FwdArgs a) {
     int8_t *vq = reinterpret_cast<int8_t *>(smem + L.vq);
     float *vd = reinterpret_cast<float *>(smem + L.vd);
     int32_t *isum_wave = reinterpret_cast<int32_t *>(smem + L.isum) + wave * NT * ROWS_PER_WAVE * ISUM_PITCH;
-    const BlobLayout BL = blob_layout(H, I, BITS);
+    const BlobLayout BL = blob_layout(H, I, BITS, GROUPED ? a.group : 0);
     const size_t row_bytes = (size_t)I * BITS / 8;
     const int rw = r0 + wave * ROWS_PER_WAVE;
     const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(blob, (uint32_t)BL.total);
@@ -177,6 +178,14 @@ __global__ __launch_bounds__(256) void k_down(const FwdArgs a) {
 #pragma unroll
     for (int j = 0; j < ROWS_PER_WAVE; ++j) rowoff[j] = (uint32_t)(BL.down + (size_t)(rw + j) * row_bytes);
     const float *s_down = reinterpret_cast<const float *>(blob + BL.s_down);
+    RowGroups G;
+    G.lgb = GROUPED ? group_lgb(a.group) : -1;
+    if (GROUPED) {
+        G.rsrc = rsrc;
+        G.row_stride = (uint32_t)(4 * (I / a.group));
+        G.base = (uint32_t)(BL.s_down + (size_t)rw * G.row_stride);
+        G.lds = reinterpret_cast<float *>(smem + L.total) + wave * ROWS_PER_WAVE * (64 >> G.lgb);
+    }
     const int nb = I / 32;
     const int vds = vd_stride(nb);
     const int crow = lane & 15, cvec = lane >> 4;
@@ -194,10 +203,11 @@ __global__ __launch_bounds__(256) void k_down(const FwdArgs a) {
         };
         BlockBits<BITS> cur[ROWS_PER_WAVE];
         prime_rows<BITS, ROWS_PER_WAVE>(rsrc, rowoff, nb, cur);
-        const float acc = stream_rows<BITS, NT, ROWS_PER_WAVE>(rsrc, rowoff, nb, ng, vq, vd, isum_wave, I, stage, cur);
+        const float acc =
+            stream_rows<BITS, NT, ROWS_PER_WAVE, GROUPED>(rsrc, rowoff, nb, ng, vq, vd, isum_wave, I, stage, cur, G);
         if (cvec < ng) {
             const int slot = pairs[p0 + g0 + cvec];
-            a.Y[(size_t)slot * H + rw + crow] = acc * s_down[rw + crow];
+            a.Y[(size_t)slot * H + rw + crow] = GROUPED ? acc : acc * s_down[rw + crow];
         }
         __syncthreads();
     }
@@ -226,10 +236,10 @@ __global__ __launch_bounds__(256) void k_combine(const FwdArgs a) {
 // ---- launchers -----------------------------------------------------------
 static int pick_nt(int S) { return S >= 4 ? 4 : (S >= 2 ? 2 : 1); }
 
-size_t forward_smem_max(int S, int H, int I, int E, int K, int n_shared) {
+size_t forward_smem_max(int S, int H, int I, int E, int K, int n_shared, int group) {
     (void)n_shared;
     const int nt = pick_nt(S);
-    return std::max(smem_plan(S, K, E, nt, H).total, smem_plan(S, K, E, nt, I).total);
+    return std::max(smem_plan(S, K, E, nt, H).total, smem_plan(S, K, E, nt, I).total) + groups_lds_bytes(group, 4);
 }
 
 template <typename F>
@@ -239,32 +249,34 @@ static hipError_t launch_dyn(F kern, dim3 grid, size_t smem, hipStream_t st, con
     return launch(kern, grid, dim3(256), smem, st, a);
 }
 
-template <int BITS, bool TABLE>
+template <int BITS, bool TABLE, bool GROUPED = false>
 static hipError_t gateup_bits(const FwdArgs &a, hipStream_t st) {
     const int P = a.S * a.K;
     const int umax = std::min(P, a.E) + a.n_shared - (TABLE ? a.shared_done : 0);
     const dim3 grid(a.I / 32, umax);
     const int nt = pick_nt(a.S);
-    const size_t smem = smem_plan(a.S, a.K, a.E, nt, a.H).total;
-    if (nt == 1) return launch_dyn(k_gateup<BITS, 1, TABLE>, grid, smem, st, a);
-    if (nt == 2) return launch_dyn(k_gateup<BITS, 2, TABLE>, grid, smem, st, a);
-    return launch_dyn(k_gateup<BITS, 4, TABLE>, grid, smem, st, a);
+    const size_t smem = smem_plan(a.S, a.K, a.E, nt, a.H).total + groups_lds_bytes(a.group, 4);
+    if (nt == 1) return launch_dyn(k_gateup<BITS, 1, TABLE, GROUPED>, grid, smem, st, a);
+    if (nt == 2) return launch_dyn(k_gateup<BITS, 2, TABLE, GROUPED>, grid, smem, st, a);
+    return launch_dyn(k_gateup<BITS, 4, TABLE, GROUPED>, grid, smem, st, a);
 }
 
-template <int BITS>
+template <int BITS, bool GROUPED = false>
 static hipError_t down_bits(const FwdArgs &a, hipStream_t st) {
     const int P = a.S * a.K;
     const int umax = std::min(P, a.E) + a.n_shared;
     const dim3 grid(a.H / 64, umax);
     const int nt = pick_nt(a.S);
-    const size_t smem = smem_plan(a.S, a.K, a.E, nt, a.I).total;
-    if (nt == 1) return launch_dyn(k_down<BITS, 1>, grid, smem, st, a);
-    if (nt == 2) return launch_dyn(k_down<BITS, 2>, grid, smem, st, a);
-    return launch_dyn(k_down<BITS, 4>, grid, smem, st, a);
+    const size_t smem = smem_plan(a.S, a.K, a.E, nt, a.I).total + groups_lds_bytes(a.group, 4);
+    if (nt == 1) return launch_dyn(k_down<BITS, 1, GROUPED>, grid, smem, st, a);
+    if (nt == 2) return launch_dyn(k_down<BITS, 2, GROUPED>, grid, smem, st, a);
+    return launch_dyn(k_down<BITS, 4, GROUPED>, grid, smem, st, a);
 }
 
+// Group-scaled weights are int4 only (the dims check refuses the others).
 hipError_t launch_gateup(const FwdArgs &a, int bits, hipStream_t st) {
     const bool table = a.units != nullptr;
+    if (a.group) return table ? gateup_bits<4, true, true>(a, st) : gateup_bits<4, false, true>(a, st);
     if (bits == 8) return table ? gateup_bits<8, true>(a, st) : gateup_bits<8, false>(a, st);
     if (bits == 4) return table ? gateup_bits<4, true>(a, st) : gateup_bits<4, false>(a, st);
     return table ? gateup_bits<2, true>(a, st) : gateup_bits<2, false>(a, st);
@@ -275,6 +287,7 @@ hipError_t launch_combine(const FwdArgs &a, hipStream_t st) {
 }
 
 hipError_t launch_down(const FwdArgs &a, int bits, hipStream_t st) {
+    if (a.group) return down_bits<4, true>(a, st);
     if (bits == 8) return down_bits<8>(a, st);
     if (bits == 4) return down_bits<4>(a, st);
     return down_bits<2>(a, st);

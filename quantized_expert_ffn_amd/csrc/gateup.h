@@ -18,17 +18,19 @@ namespace coli {
 // vector) and vd (vd_stride(H / 32) scales per vector) and ends with a
 // workgroup barrier; it runs while the first weights are in flight.  Then
 // SwiGLU of each row pair and Q8_0(h) of the 32 values (one block), written
-// to qh / dh at the slot.  256 threads.
-template <int BITS, int NT, typename Stage>
-__device__ __forceinline__ void gateup_unit(const uint8_t *blob, int H, int I, int i0, const int *slots, int np,
-                                            uint8_t *smem, const SmemPlan &L, int8_t *__restrict__ qh,
-                                            float *__restrict__ dh, Stage stage) {
+// to qh / dh at the slot.  256 threads.  GROUPED: the blob has one scale per
+// `group` codes of a row, staged through the groups_lds_bytes(group, 4)
+// bytes of LDS at smem + gs_off.
+template <int BITS, int NT, bool GROUPED, typename Stage>
+__device__ __forceinline__ void gateup_unit(const uint8_t *blob, int H, int I, int group, int i0, const int *slots,
+                                            int np, uint8_t *smem, const SmemPlan &L, size_t gs_off,
+                                            int8_t *__restrict__ qh, float *__restrict__ dh, Stage stage) {
     const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
     int8_t *vq = reinterpret_cast<int8_t *>(smem + L.vq);
     float *vd = reinterpret_cast<float *>(smem + L.vd);
     int32_t *isum_wave = reinterpret_cast<int32_t *>(smem + L.isum) + wave * NT * ROWS_PER_WAVE * ISUM_PITCH;
     float *gu = reinterpret_cast<float *>(smem + L.gu);
-    const BlobLayout BL = blob_layout(H, I, BITS);
+    const BlobLayout BL = blob_layout(H, I, BITS, GROUPED ? group : 0);
     const size_t row_bytes = (size_t)H * BITS / 8;
     const int half = wave & 1;            // rows 0-15 or 16-31 of the tile
     const size_t mat = wave < 2 ? BL.gate : BL.up;
@@ -37,16 +39,26 @@ __device__ __forceinline__ void gateup_unit(const uint8_t *blob, int H, int I, i
 #pragma unroll
     for (int j = 0; j < ROWS_PER_WAVE; ++j)
         rowoff[j] = (uint32_t)(mat + (size_t)(i0 + 16 * half + j) * row_bytes);
-    const float *scale = reinterpret_cast<const float *>(blob + (wave < 2 ? BL.s_gate : BL.s_up));
+    const size_t ssec = wave < 2 ? BL.s_gate : BL.s_up;
+    const float *scale = reinterpret_cast<const float *>(blob + ssec);
+    RowGroups G;
+    G.lgb = GROUPED ? group_lgb(group) : -1;
+    if (GROUPED) {
+        G.rsrc = rsrc;
+        G.row_stride = (uint32_t)(4 * (H / group));
+        G.base = (uint32_t)(ssec + (size_t)(i0 + 16 * half) * G.row_stride);
+        G.lds = reinterpret_cast<float *>(smem + gs_off) + wave * ROWS_PER_WAVE * (64 >> G.lgb);
+    }
     const int nb = H / 32;
     const int crow = lane & 15, cvec = lane >> 4;
     for (int g0 = 0; g0 < np; g0 += NT) {
         const int ng = min(NT, np - g0);
         BlockBits<BITS> cur[ROWS_PER_WAVE];
         prime_rows<BITS, ROWS_PER_WAVE>(rsrc, rowoff, nb, cur);
-        const float acc = stream_rows<BITS, NT, ROWS_PER_WAVE>(rsrc, rowoff, nb, ng, vq, vd, isum_wave, H,
-                                                              [&]() { stage(g0, ng); }, cur);
-        if (cvec < ng) gu[cvec * 64 + wave * ROWS_PER_WAVE + crow] = acc * scale[i0 + 16 * half + crow];
+        const float acc = stream_rows<BITS, NT, ROWS_PER_WAVE, GROUPED>(rsrc, rowoff, nb, ng, vq, vd, isum_wave, H,
+                                                                       [&]() { stage(g0, ng); }, cur, G);
+        if (cvec < ng)
+            gu[cvec * 64 + wave * ROWS_PER_WAVE + crow] = GROUPED ? acc : acc * scale[i0 + 16 * half + crow];
         __syncthreads();
         // SwiGLU and Q8_0(h): half-wave (tid >> 5) handles one vector's 32 rows.
         const int vv = tid >> 5, i = tid & 31;

@@ -100,6 +100,7 @@ struct FwdArgs {
     int S, H, I, E, K, n_shared;
     int pend_mode;                 // 0: all units, 1: skip pending experts, 2: only pending
     int shared_done;               // 1: the router launch wrote the shared expert's Q8_0(h)
+    int group;                     // 0: per-row scales; else one scale per `group` codes of a row
     uint32_t pend[32];             // bit e: expert e pending
 };
 
@@ -121,7 +122,7 @@ struct RouteArgs {
     int8_t *qh;                    // with sg: the shared expert's Q8_0(h), slots S*K + t
     float *dh;
     int S, H, E, K, n_shared, norm;
-    int I, bits;                   // expert shape and code width (for sg)
+    int I, bits, group;            // expert shape, code width and scale group (for sg)
     int sg;                        // 1: the launch also runs the shared expert's gate/up tiles
     float rsf;
 };
@@ -200,7 +201,7 @@ struct LayerArgs {
 size_t route_fused_smem(int S, int K, int E);
 // Down projection + combine by output-row tiles (up to 8 tokens).
 hipError_t launch_down_rows(const FwdArgs &a, int bits, hipStream_t st);
-size_t down_rows_smem(int S, int I, int E, int K, int n_shared);
+size_t down_rows_smem(int S, int I, int E, int K, int n_shared, int group, int bits);
 hipError_t launch_layer(const FwdArgs &a, const LayerArgs &l, bool route, int bits, hipStream_t st);
 size_t layer_smem(int S, int H, int I, int E, int K, int n_shared);
 
@@ -214,7 +215,7 @@ hipError_t launch_group(const int32_t *idx, int S, int K, int E, int n_shared, u
 size_t pf_group_smem(int S, int K, int E);
 hipError_t launch_pf_gateup(const FwdArgs &a, const int32_t *tiles, int bits, hipStream_t st);
 hipError_t launch_pf_down(const FwdArgs &a, const int32_t *tiles, int bits, hipStream_t st);
-size_t forward_smem_max(int S, int H, int I, int E, int K, int n_shared);
+size_t forward_smem_max(int S, int H, int I, int E, int K, int n_shared, int group);
 
 hipError_t launch_debug_unpack(int bits, int rows, int cols, const void *src, int8_t *out,
                                hipStream_t st);

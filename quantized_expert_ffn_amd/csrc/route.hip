@@ -88,7 +88,7 @@ __global__ __launch_bounds__(64) void k_router_select(const float *__restrict__ 
 constexpr int RF_W = 4;
 
 // Shared expert, gate/up rows 32 tile .. 32 tile + 31, every token.
-template <int BITS, int NT>
+template <int BITS, int NT, bool GROUPED>
 __device__ __forceinline__ void shared_gateup_tile(const RouteArgs &r, uint8_t *smem, int tile) {
     const int tid = threadIdx.x, S = r.S, H = r.H, P = S * r.K;
     const SmemPlan L = smem_plan(S, r.K, r.E, NT, H);
@@ -106,10 +106,11 @@ __device__ __forceinline__ void shared_gateup_tile(const RouteArgs &r, uint8_t *
         }
         __syncthreads();
     };
-    gateup_unit<BITS, NT>(uniform_ptr(r.shared), H, r.I, 32 * tile, slots, S, smem, L, r.qh, r.dh, stage);
+    gateup_unit<BITS, NT, GROUPED>(uniform_ptr(r.shared), H, r.I, r.group, 32 * tile, slots, S, smem, L, L.total,
+                                   r.qh, r.dh, stage);
 }
 
-template <int MAXJ, int BITS, int NT>
+template <int MAXJ, int BITS, int NT, bool GROUPED>
 __global__ __launch_bounds__(64 * RF_W) void k_route_fused(const RouteArgs r) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     __shared__ int s_last;
@@ -117,7 +118,7 @@ __global__ __launch_bounds__(64 * RF_W) void k_route_fused(const RouteArgs r) {
     const int E = r.E, K = r.K, S = r.S, H = r.H;
     const int n_sg = r.sg ? r.I / 32 : 0;
     if ((int)blockIdx.x < n_sg) {
-        if (t == 0) shared_gateup_tile<BITS, NT>(r, smem, blockIdx.x);
+        if (t == 0) shared_gateup_tile<BITS, NT, GROUPED>(r, smem, blockIdx.x);
         return;
     }
     const int bx = (int)blockIdx.x - n_sg;
@@ -257,23 +258,25 @@ static int route_nt(int S) { return S >= 2 ? 2 : 1; }
 size_t route_fused_lds(const RouteArgs &r) {
     const size_t sel = route_fused_smem(r.S, r.K, r.E);
     if (!r.sg) return sel;
-    const size_t tile = smem_plan(r.S, r.K, r.E, route_nt(r.S), r.H).total;
+    const size_t tile = smem_plan(r.S, r.K, r.E, route_nt(r.S), r.H).total + groups_lds_bytes(r.group, 4);
     return sel > tile ? sel : tile;
 }
 
-template <int MAXJ, int BITS>
+template <int MAXJ, int BITS, bool GROUPED = false>
 static hipError_t route_fused_bits(const RouteArgs &r, dim3 grid, size_t smem, hipStream_t st) {
     auto go = [&](auto kern) {
         const hipError_t e = ensure_dyn_smem(reinterpret_cast<const void *>(kern), smem);
         if (e != hipSuccess) return e;
         return launch(kern, grid, dim3(64 * RF_W), smem, st, r);
     };
-    if (route_nt(r.S) == 1) return go(k_route_fused<MAXJ, BITS, 1>);
-    return go(k_route_fused<MAXJ, BITS, 2>);
+    if (route_nt(r.S) == 1) return go(k_route_fused<MAXJ, BITS, 1, GROUPED>);
+    return go(k_route_fused<MAXJ, BITS, 2, GROUPED>);
 }
 
+// Group-scaled weights are int4 only (the dims check refuses the others).
 template <int MAXJ>
 static hipError_t route_fused_maxj(const RouteArgs &r, dim3 grid, size_t smem, hipStream_t st) {
+    if (r.group) return route_fused_bits<MAXJ, 4, true>(r, grid, smem, st);
     if (r.bits == 8) return route_fused_bits<MAXJ, 8>(r, grid, smem, st);
     if (r.bits == 2) return route_fused_bits<MAXJ, 2>(r, grid, smem, st);
     return route_fused_bits<MAXJ, 4>(r, grid, smem, st);

@@ -247,6 +247,78 @@ __device__ __forceinline__ float chain_chunk(float acc, const int32_t *is, const
     return acc;
 }
 
+// The same chain with one scale per group of gb blocks of the row (gs: the
+// chunk's group scales of this lane's row): acc = fmaf(dv_b * gs[b / gb],
+// isum_b, acc), the multiplier being one binary32 product.  gb = 1 << lgb.
+__device__ __forceinline__ float chain_chunk_g(float acc, const int32_t *is, const float *dv, const float *gs,
+                                               int lgb, int nbc) {
+    if (nbc == 64) {
+#pragma unroll 1
+        for (int qq = 0; qq < 64; qq += 16) {
+            i32x4 iv[4];
+            f32x4 dd[4];
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                iv[q4] = *reinterpret_cast<const i32x4 *>(is + qq + 4 * q4);
+                dd[q4] = *reinterpret_cast<const f32x4 *>(dv + qq + 4 * q4);
+            }
+            float m[16];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) m[j] = gs[(qq + j) >> lgb];
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                acc = __builtin_fmaf(dd[q4].x * m[4 * q4], (float)iv[q4].x, acc);
+                acc = __builtin_fmaf(dd[q4].y * m[4 * q4 + 1], (float)iv[q4].y, acc);
+                acc = __builtin_fmaf(dd[q4].z * m[4 * q4 + 2], (float)iv[q4].z, acc);
+                acc = __builtin_fmaf(dd[q4].w * m[4 * q4 + 3], (float)iv[q4].w, acc);
+            }
+        }
+    } else {
+        for (int bb = 0; bb < nbc; ++bb) acc = __builtin_fmaf(dv[bb] * gs[bb >> lgb], (float)is[bb], acc);
+    }
+    return acc;
+}
+
+// Group scales of a wave's rows (one f32 per 32 << lgb codes), staged
+// through LDS one 64-block chunk at a time: the chunk's RPW x (64 >> lgb)
+// scales are 16-byte words w = lane + 64 k, word w holding scales
+// 4 p .. 4 p + 3 of the chunk of row w / (16 >> lgb), p = w % (16 >> lgb).
+// lgb <= 4 (groups of up to 512 codes), so a word never straddles rows.
+// Loads run through the blob's buffer resource (zeros past its end).
+struct RowGroups {
+    __amdgpu_buffer_rsrc_t rsrc;
+    uint32_t base;         // byte offset of the scales of the wave's first row
+    uint32_t row_stride;   // bytes of scales per row
+    int lgb;               // log2(blocks per group); -1: per-row scales, nothing staged
+    float *lds;            // RPW x (64 >> lgb) floats, private to the wave
+};
+
+template <int RPW>
+__device__ __forceinline__ void groups_load(const RowGroups &G, int c, i32x4 (&gw)[4]) {
+    const int lane = threadIdx.x & 63;
+    const int wpr = 16 >> G.lgb, words = RPW * wpr;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int w = lane + 64 * k;
+        if (w < words) {
+            const int row = w / wpr, p = w - row * wpr;
+            const uint32_t off = G.base + (uint32_t)row * G.row_stride + (uint32_t)(c * (64 >> G.lgb) + 4 * p) * 4u;
+            gw[k] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(G.rsrc, off, 0, 0));
+        }
+    }
+}
+
+template <int RPW>
+__device__ __forceinline__ void groups_store(const RowGroups &G, const i32x4 (&gw)[4]) {
+    const int lane = threadIdx.x & 63;
+    const int wpr = 16 >> G.lgb, words = RPW * wpr;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int w = lane + 64 * k;
+        if (w < words) reinterpret_cast<i32x4 *>(G.lds)[w] = gw[k];
+    }
+}
+
 // Issues the loads of chunk 0 (blocks 0..63) of this wave's RPW rows.
 template <int BITS, int RPW>
 __device__ __forceinline__ void prime_rows(__amdgpu_buffer_rsrc_t rsrc, const uint32_t rowoff[RPW],
@@ -266,19 +338,26 @@ __device__ __forceinline__ void prime_rows(__amdgpu_buffer_rsrc_t rsrc, const ui
 // works alone on its own LDS region (NT x RPW rows of ISUM_PITCH block
 // dots); for int4 / int2 the next chunk's weights are in flight while the
 // current chunk is reduced.
-template <int BITS, int NT, int RPW, typename Stage>
+// With GROUPED (G.lgb >= 0) the chain of chunk c uses the chunk's
+// group scales, loaded one chunk ahead with the weights and staged in the
+// wave's LDS region G.lds; the row scale is then not applied by the caller.
+template <int BITS, int NT, int RPW, bool GROUPED, typename Stage>
 __device__ __forceinline__ float stream_rows(__amdgpu_buffer_rsrc_t rsrc, const uint32_t rowoff[RPW],
                                              int nb, int ng, const int8_t *vq, const float *vd,
                                              int32_t *isum_wave, int vlen, Stage stage,
-                                             BlockBits<BITS> (&cur)[RPW]) {
+                                             BlockBits<BITS> (&cur)[RPW], const RowGroups &G) {
     static_assert(NT * RPW <= 64, "one chain per lane");
     constexpr bool PREFETCH = BITS < 8;
     const int lane = threadIdx.x & 63;
     const int crow = lane % RPW, cvec = lane / RPW;
     const int vds = vd_stride(nb);
+    constexpr bool grouped = GROUPED;
     float acc = 0.0f;
     const int nchunks = (nb + 63) / 64;
+    i32x4 gw[4];
+    if (grouped) groups_load<RPW>(G, 0, gw);
     stage();
+    if (grouped) groups_store<RPW>(G, gw);
     for (int c = 0; c < nchunks; ++c) {
         const int b = c * 64 + lane;
         const bool act = b < nb;
@@ -287,6 +366,7 @@ __device__ __forceinline__ float stream_rows(__amdgpu_buffer_rsrc_t rsrc, const 
 #pragma unroll
             for (int j = 0; j < RPW; ++j) nxt[j] = load_block<BITS>(rsrc, rowoff[j], b + 64);
         }
+        if (grouped && c + 1 < nchunks) groups_load<RPW>(G, c + 1, gw);
 #pragma unroll
         for (int it = 0; it < NT; ++it) {
             if (it < ng) {
@@ -298,10 +378,19 @@ __device__ __forceinline__ float stream_rows(__amdgpu_buffer_rsrc_t rsrc, const 
             }
         }
         wave_lds_sync();
-        if (cvec < ng)
-            acc = chain_chunk(acc, isum_wave + (cvec * RPW + crow) * ISUM_PITCH, vd + cvec * vds + c * 64,
-                              min(64, nb - c * 64));
+        if (cvec < ng) {
+            if (grouped)
+                acc = chain_chunk_g(acc, isum_wave + (cvec * RPW + crow) * ISUM_PITCH, vd + cvec * vds + c * 64,
+                                    G.lds + crow * (64 >> G.lgb), G.lgb, min(64, nb - c * 64));
+            else
+                acc = chain_chunk(acc, isum_wave + (cvec * RPW + crow) * ISUM_PITCH, vd + cvec * vds + c * 64,
+                                  min(64, nb - c * 64));
+        }
         wave_lds_sync();
+        if (grouped && c + 1 < nchunks) {
+            groups_store<RPW>(G, gw);
+            wave_lds_sync();
+        }
         if (PREFETCH) {
 #pragma unroll
             for (int j = 0; j < RPW; ++j) cur[j] = nxt[j];
@@ -311,6 +400,27 @@ __device__ __forceinline__ float stream_rows(__amdgpu_buffer_rsrc_t rsrc, const 
         }
     }
     return acc;
+}
+
+template <int BITS, int NT, int RPW, typename Stage>
+__device__ __forceinline__ float stream_rows(__amdgpu_buffer_rsrc_t rsrc, const uint32_t rowoff[RPW],
+                                             int nb, int ng, const int8_t *vq, const float *vd,
+                                             int32_t *isum_wave, int vlen, Stage stage,
+                                             BlockBits<BITS> (&cur)[RPW]) {
+    RowGroups G;
+    G.lgb = -1;
+    return stream_rows<BITS, NT, RPW, false>(rsrc, rowoff, nb, ng, vq, vd, isum_wave, vlen, stage, cur, G);
+}
+
+// LDS bytes of the group-scale staging of a workgroup of `waves` wavefronts
+// of 16 rows each (0 for per-row scales).
+__host__ __device__ inline size_t groups_lds_bytes(int group, int waves) {
+    return group ? (size_t)waves * 16 * (64 / (group / 32)) * 4 : 0;
+}
+__host__ __device__ inline int group_lgb(int group) {
+    int l = -1;
+    for (int g = group / 32; g > 0; g >>= 1) ++l;
+    return group ? l : -1;
 }
 
 }  // namespace coli
