@@ -59,6 +59,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--workload", choices=("decode", "verify", "prefill", "tiered"), default="decode")
     ap.add_argument("--tier-bits", type=int, choices=(4, 2), default=4, help="tiered: expert width")
+    ap.add_argument("--group-size", type=int, choices=(0, 64), default=0,
+                    help="decode / prefill: 64 = group-scaled int4 experts (one scale per 64 codes of a row)")
     ap.add_argument("--tier-layers", type=int, default=75, help="tiered: layers streamed")
     ap.add_argument("--host-layers", type=int, default=8,
                     help="tiered: distinct layers of expert bytes in pinned host memory (reused cyclically)")
@@ -125,6 +127,10 @@ def main():
         return
     verify = args.workload == "verify"
     spec = synth.GLM_INT8 if verify else synth.GLM
+    if args.group_size:
+        if verify:
+            raise SystemExit("--group-size applies to int4 experts (decode, prefill)")
+        spec = synth.GLM_GS64
     S = 4 if verify else 1  # tokens per step
     dims = q.make_dims(spec)
     H, E = spec.hidden, spec.n_experts
@@ -240,7 +246,8 @@ def main():
         in_router = args.path == "layer" and S <= 2 and 64 * H * spec.wbits // 8 <= 256 * 1024
         gu_units = n_units - (spec.n_shared if in_router else 0)
         dom, dom_kernel = "gateup", "k_gateup<%d,%d>" % (spec.wbits, min(S, 4))
-        dom_bytes = gu_units * (2 * spec.inter * H * spec.wbits // 8 + 2 * spec.inter * 4)
+        n_scales = H // spec.group if spec.group else 1   # per gate / up row
+        dom_bytes = gu_units * (2 * spec.inter * H * spec.wbits // 8 + 2 * spec.inter * 4 * n_scales)
     dom_us = kernel_us[dom]
     achieved = dom_bytes / (dom_us * 1e-6) / 1e9
     layer_gbs = lay_bytes / (ms_per_step * 1e-3) / 1e9
@@ -263,8 +270,10 @@ def main():
                          "int8 per-row-scaled weights (37.8 MB/expert), Q8_0 activations, fp32 router gate; "
                          f"{L} layers resident in HBM, step s uses layer s mod {L}") if verify else
                         ("GLM-5.2-shaped MoE decode layer, 1 token/step: hidden 6144, expert inter 2048, "
-                         "256 routed experts top-8 + 1 shared, int4 per-row-scaled weights (18.9 MB/expert), "
-                         f"Q8_0 activations, fp32 router gate; {L} layers resident in HBM, step s uses layer "
+                         "256 routed experts top-8 + 1 shared, "
+                         + ("int4 weights with one scale per 64 codes of a row (21.2 MB/expert), " if spec.group
+                            else "int4 per-row-scaled weights (18.9 MB/expert), ")
+                         + f"Q8_0 activations, fp32 router gate; {L} layers resident in HBM, step s uses layer "
                          f"s mod {L}"),
             "layers_resident": L, "resident_gb": round(L * nblob * bb / 1e9, 1),
             "tokens_per_step": S, "graph_steps": G, "entry": args.path, "kernels": args.kernels,

@@ -136,6 +136,47 @@ struct DownTile {
     }
     __device__ __forceinline__ float ld_dh(size_t i) const { return COHERENT ? ld_dev(a.dh + i) : a.dh[i]; }
 
+    // Group scales of this wave's DR_RPW rows for every unit of the batch
+    // into the wave's LDS region of gsl (UB x DR_RPW x ngr floats): all of
+    // the wave's loads are issued before the first is stored.
+    __device__ __forceinline__ void stage_groups(int u0, int u1, float *gsl) {
+        const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
+        const int ngr = a.I / a.group;
+        float *dst = gsl + wave * UB * DR_RPW * ngr;
+        const int rw0 = rt * DR_ROWS + wave * DR_RPW;
+        const int n = (u1 - u0) * DR_RPW * ngr;
+        if ((ngr & 3) == 0) {
+            const int wpr = ngr / 4, nw = n / 4;
+            for (int w0 = 0; w0 < nw; w0 += 4 * 64) {
+                i32x4 v[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const int w = w0 + lane + 64 * k;
+                    v[k] = i32x4{0, 0, 0, 0};
+                    if (w < nw) {
+                        const int ur = w / wpr, p = w - ur * wpr;
+                        const uint8_t *blob = ublob[u0 + ur / DR_RPW];
+                        if (blob)
+                            v[k] = *reinterpret_cast<const i32x4 *>(
+                                blob + BL.s_down + ((size_t)(rw0 + ur % DR_RPW) * ngr + 4 * p) * 4);
+                    }
+                }
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const int w = w0 + lane + 64 * k;
+                    if (w < nw) reinterpret_cast<i32x4 *>(dst)[w] = v[k];
+                }
+            }
+        } else {
+            for (int i = lane; i < n; i += 64) {
+                const int ur = i / ngr, g = i - ur * ngr;
+                const uint8_t *blob = ublob[u0 + ur / DR_RPW];
+                dst[i] = blob ? reinterpret_cast<const float *>(blob + BL.s_down)[(size_t)(rw0 + ur % DR_RPW) * ngr + g]
+                              : 0.0f;
+            }
+        }
+    }
+
     // One batch of units [u0, u1); ONE: single() holds and, with issued,
     // the batch's weights were issued ahead by issue(0, n_units, 0).
     template <bool ONE>
@@ -214,14 +255,7 @@ struct DownTile {
                 stage_store(qv, 0, nq, q_dst);
                 stage_store(dv, 0, nd, d_dst);
                 stage_store(sv, 0, ns, s_dst);
-                // the batch's group scales (rows r0 .. r0+7 of each unit),
-                // read after the weights were issued
-                for (int i = (int)threadIdx.x; GROUPED && i < (u1 - u0) * DR_ROWS * ngr; i += DR_T) {
-                    const int ur = i / ngr, g = i - ur * ngr;
-                    const uint8_t *blob = ublob[u0 + ur / DR_ROWS];
-                    gsl[i] = blob ? reinterpret_cast<const float *>(blob + BL.s_down)[(size_t)(r0 + ur % DR_ROWS) * ngr + g]
-                                  : 0.0f;
-                }
+                if (GROUPED) stage_groups(u0, u1, gsl);
                 for (int rd = 1; !ONE && rd < nr; ++rd) {
                     stage_fetch(qv, rd, nq, q_src);
                     stage_fetch(dv, rd, nd, d_src);
@@ -253,7 +287,8 @@ struct DownTile {
             if (chain_lane && cp < npb) {
                 if (GROUPED)
                     acc = chain_chunk_g(acc, isum + (cr * mpb + cp) * ISUM_PITCH, dh_l + cp * dpitch + c * 64,
-                                        gsl + ((ug - u0) * DR_ROWS + rl) * ngr + c * (64 >> lgb), lgb,
+                                        gsl + (wave * UB * DR_RPW + (ug - u0) * DR_RPW + cr) * ngr + c * (64 >> lgb),
+                                        lgb,
                                         min(64, nbi - c * 64));
                 else
                     acc = chain_chunk(acc, isum + (cr * mpb + cp) * ISUM_PITCH, dh_l + cp * dpitch + c * 64,

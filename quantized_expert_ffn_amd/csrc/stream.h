@@ -362,11 +362,15 @@ __device__ __forceinline__ float stream_rows(__amdgpu_buffer_rsrc_t rsrc, const 
         const int b = c * 64 + lane;
         const bool act = b < nb;
         BlockBits<BITS> nxt[RPW];
+        // the next chunk's group scales are issued before its weights: they
+        // are stored at the end of this chunk, and waiting for them must not
+        // wait for the weights (loads complete in issue order)
+        if (grouped && c + 1 < nchunks) groups_load<RPW>(G, c + 1, gw);
+        __builtin_amdgcn_sched_barrier(0);
         if (PREFETCH && b + 64 < nb) {
 #pragma unroll
             for (int j = 0; j < RPW; ++j) nxt[j] = load_block<BITS>(rsrc, rowoff[j], b + 64);
         }
-        if (grouped && c + 1 < nchunks) groups_load<RPW>(G, c + 1, gw);
 #pragma unroll
         for (int it = 0; it < NT; ++it) {
             if (it < ng) {
