@@ -31,6 +31,10 @@
  *    the outputs of the calls since the last read are unspecified.
  *  - There is no CPU fallback: without a usable gfx950 device every compute
  *    call fails with COLI_EHIP.
+ *  - Hidden states, router gate, outputs and expert blobs are accessed with
+ *    16-byte vector loads and stores: x, router_w, out and shared_blob must
+ *    be 16-byte aligned (COLI_EINVAL otherwise), and so must every pointer of
+ *    the expert blob table (not checked: the table lives on the device).
  */
 #ifndef COLI_MOE_H
 #define COLI_MOE_H

@@ -72,6 +72,10 @@ int check_dims(const coli_moe_dims *d) {
     return COLI_OK;
 }
 
+// Hidden states, router gate, outputs and blobs are read and written with
+// 16-byte vector accesses.
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
 // ---- kernel timing ------------------------------------------------------
 struct Timing {
     std::mutex mu;
@@ -334,6 +338,8 @@ int coli_moe_route(const coli_moe_dims *d, int32_t S, const float *x, const floa
     if (S == 0) return COLI_OK;
     if (!x || !router_w || !topk_idx || !topk_w || !ws)
         return fail(COLI_EINVAL, "coli_moe_route: NULL pointer argument");
+    if (!aligned16(x) || !aligned16(router_w))
+        return fail(COLI_EINVAL, "coli_moe_route: x and router_w must be 16-byte aligned");
     const WsLayout L = ws_layout(d->hidden, d->inter, d->n_experts, d->top_k, S);
     if (ws_bytes < L.total)
         return fail(COLI_EWORKSPACE, "workspace %zu bytes < %zu needed for %d tokens", ws_bytes, L.total, S);
@@ -352,6 +358,8 @@ int coli_moe_forward(const coli_moe_dims *d, int32_t S, const float *x, const in
     if (S == 0) return COLI_OK;
     if (!x || !topk_idx || !topk_w || !expert_blobs || !out || !ws)
         return fail(COLI_EINVAL, "coli_moe_forward: NULL pointer argument");
+    if (!aligned16(x) || !aligned16(out) || !aligned16(shared_blob))
+        return fail(COLI_EINVAL, "coli_moe_forward: x, out and shared_blob must be 16-byte aligned");
     if (d->n_shared && !shared_blob)
         return fail(COLI_ENOTRESIDENT, "n_shared=1 but shared_blob is NULL");
     const WsLayout L = ws_layout(d->hidden, d->inter, d->n_experts, d->top_k, S);
@@ -402,6 +410,8 @@ int coli_moe_layer(const coli_moe_dims *d, int32_t S, const float *x, const floa
     if (S == 0) return COLI_OK;
     if (!x || !router_w || !expert_blobs || !topk_idx || !topk_w || !out || !ws)
         return fail(COLI_EINVAL, "coli_moe_layer: NULL pointer argument");
+    if (!aligned16(x) || !aligned16(router_w) || !aligned16(out) || !aligned16(shared_blob))
+        return fail(COLI_EINVAL, "coli_moe_layer: x, router_w, out and shared_blob must be 16-byte aligned");
     if (d->n_shared && !shared_blob) return fail(COLI_ENOTRESIDENT, "n_shared=1 but shared_blob is NULL");
     const WsLayout L = ws_layout(d->hidden, d->inter, d->n_experts, d->top_k, S);
     if (ws_bytes < L.total)

@@ -214,22 +214,43 @@ __global__ __launch_bounds__(256) void k_down(const FwdArgs a) {
 }
 
 // Combine: out[t, r] = (fmaf chain over k in rank order of w[t,k] * y[t,k][r]
-// from 0) + y_shared[t][r].  One thread per output element, one writer.
-// Grid (H / 256, S).
+// from 0) + y_shared[t][r].  One writer per element, no atomics.  A thread
+// owns 4 consecutive elements (16-byte loads) and issues the loads of 8
+// ranks at a time before their chains.  Grid (ceil(H / 1024), S).
+constexpr int CB_K = 8;
 __global__ __launch_bounds__(256) void k_combine(const FwdArgs a) {
     const int t = blockIdx.y;
-    const int r = blockIdx.x * 256 + threadIdx.x;
+    const int r = 4 * (blockIdx.x * 256 + threadIdx.x);
     const int K = a.K, H = a.H, P = a.S * a.K;
+    if (r >= H) return;
     const float *w = a.w + (size_t)t * K;
-    float acc = 0.0f;
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
     bool ok = true;
-    for (int k = 0; k < K; ++k) {
-        const float wk = w[k];
-        ok = ok && finite_f32(wk);
-        acc = __builtin_fmaf(wk, a.Y[(size_t)(t * K + k) * H + r], acc);
+    for (int k0 = 0; k0 < K; k0 += CB_K) {
+        f32x4 y[CB_K];
+#pragma unroll
+        for (int k = 0; k < CB_K; ++k)
+            if (k0 + k < K) y[k] = *reinterpret_cast<const f32x4 *>(a.Y + (size_t)(t * K + k0 + k) * H + r);
+#pragma unroll
+        for (int k = 0; k < CB_K; ++k) {
+            if (k0 + k < K) {
+                const float wk = w[k0 + k];
+                ok = ok && finite_f32(wk);
+                acc.x = __builtin_fmaf(wk, y[k].x, acc.x);
+                acc.y = __builtin_fmaf(wk, y[k].y, acc.y);
+                acc.z = __builtin_fmaf(wk, y[k].z, acc.z);
+                acc.w = __builtin_fmaf(wk, y[k].w, acc.w);
+            }
+        }
     }
-    if (a.n_shared) acc = acc + a.Y[(size_t)(P + t) * H + r];
-    a.out[(size_t)t * H + r] = acc;
+    if (a.n_shared) {
+        const f32x4 ys = *reinterpret_cast<const f32x4 *>(a.Y + (size_t)(P + t) * H + r);
+        acc.x = acc.x + ys.x;
+        acc.y = acc.y + ys.y;
+        acc.z = acc.z + ys.z;
+        acc.w = acc.w + ys.w;
+    }
+    *reinterpret_cast<f32x4 *>(a.out + (size_t)t * H + r) = acc;
     if (!ok && r == 0) raise_status(a.status, ST_NONFINITE);
 }
 
@@ -283,7 +304,7 @@ hipError_t launch_gateup(const FwdArgs &a, int bits, hipStream_t st) {
 }
 
 hipError_t launch_combine(const FwdArgs &a, hipStream_t st) {
-    return launch(k_combine, dim3(a.H / 256, a.S), dim3(256), 0, st, a);
+    return launch(k_combine, dim3((a.H + 1023) / 1024, a.S), dim3(256), 0, st, a);
 }
 
 hipError_t launch_down(const FwdArgs &a, int bits, hipStream_t st) {

@@ -553,3 +553,41 @@ def test_graph_replay_matches_eager(torch, path, S):
         # eager work between replays
         gpu_layer(torch, dims, dl, ws)
     assert status(ws) == 0, qm.coli_moe_last_error()
+
+
+def test_misaligned_pointers_refused(torch):
+    """x, router_w, out and shared_blob are read and written 16 bytes at a
+    time: a pointer off by 4 bytes is refused on the host (COLI_EINVAL),
+    before anything is launched."""
+    from synth.device import upload_layer
+    qm = q()
+    spec = synth.TINY
+    d = _layer(spec, 2, seed=9)
+    dims = qm.make_dims(spec)
+    dl = upload_layer(d)
+    ws = workspace(dims, 2)
+    S, H = 2, spec.hidden
+    xbuf = torch.zeros(S * H + 4, dtype=torch.float32, device="cuda")
+    x_off = xbuf[1:1 + S * H].view(S, H)
+    x_off.copy_(dl["x"])
+    idx = torch.empty((S, spec.top_k), dtype=torch.int32, device="cuda")
+    w = torch.empty((S, spec.top_k), dtype=torch.float32, device="cuda")
+    obuf = torch.zeros(S * H + 4, dtype=torch.float32, device="cuda")
+    out_off = obuf[1:1 + S * H].view(S, H)
+    out = torch.zeros((S, H), dtype=torch.float32, device="cuda")
+    for call in (lambda: qm.coli_moe_route(dims, x_off, dl["router_w"], dl["bias"], idx, w, ws),
+                 lambda: qm.coli_moe_layer(dims, x_off, dl["router_w"], dl["bias"], dl["table"], dl["shared"],
+                                           idx, w, out, ws),
+                 lambda: qm.coli_moe_layer(dims, dl["x"], dl["router_w"], dl["bias"], dl["table"], dl["shared"],
+                                           idx, w, out_off, ws)):
+        with pytest.raises(qm.ColiError) as err:
+            call()
+        assert err.value.code == qm.COLI_EINVAL
+        assert "aligned" in str(err.value)
+    qm.coli_moe_route(dims, dl["x"], dl["router_w"], dl["bias"], idx, w, ws)
+    qm.coli_moe_forward(dims, dl["x"], idx, w, dl["table"], dl["shared"], out, ws)
+    with pytest.raises(qm.ColiError):
+        qm.coli_moe_forward(dims, dl["x"], idx, w, dl["table"], dl["shared"], out_off, ws)
+    assert status(ws) == 0
+    o_out, _, _ = oracle.layer(spec, d["x"], d["router_w"], d["bias"], d["blobs"], d["shared"])
+    parity(out.cpu().numpy(), o_out)
