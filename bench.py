@@ -367,7 +367,7 @@ def run_prefill(args, q, synth):
     import numpy as np
     import torch
 
-    spec = synth.GLM
+    spec = synth.GLM_GS64 if args.group_size else synth.GLM
     dims = q.make_dims(spec)
     S, H, I, E, K = args.tokens, spec.hidden, spec.inter, spec.n_experts, spec.top_k
     bb = spec.blob_bytes
@@ -450,7 +450,9 @@ def run_prefill(args, q, synth):
         "data": "synthetic (seeded; GLM-5.2-shaped random-code experts, Zipf(1.1)-routed tokens)",
         "config": {
             "workload": f"GLM-5.2-shaped MoE prefill layer, {S} tokens/step: hidden 6144, expert inter 2048, "
-                        "256 routed experts top-8 + 1 shared, int4 per-row-scaled weights, Q8_0 activations, "
+                        "256 routed experts top-8 + 1 shared, "
+                        + ("int4 weights with one scale per 64 codes of a row, " if spec.group
+                           else "int4 per-row-scaled weights, ") + "Q8_0 activations, "
                         "fp32 router gate, zero bias; Zipf(1.1) expert popularity; all 257 experts resident",
             "tokens_per_step": S, "graph_steps": G, "kernels": args.kernels,
             "routing": {"unique": int((counts > 0).sum()), "min": int(counts[counts > 0].min()),

@@ -103,10 +103,10 @@ int g_force_path = 0;
 // Batches of more than GROUPED_MIN_S - 1 tokens take the grouped kernels.
 constexpr int GROUPED_MIN_S = 9;
 
-// The grouped kernels take per-row scales only; group-scaled weights run the
-// multi-launch kernels at every batch size.
+// The grouped kernels take per-row scales or groups of 64; other group sizes
+// run the multi-launch kernels at every batch size.
 bool use_grouped(int S, int group) {
-    return group == 0 && (g_force_path == 3 || (g_force_path == 0 && S >= GROUPED_MIN_S));
+    return (group == 0 || group == 64) && (g_force_path == 3 || (g_force_path == 0 && S >= GROUPED_MIN_S));
 }
 
 // LDS of the kernels a forward of S tokens launches.
@@ -117,9 +117,11 @@ size_t forward_lds(const coli_moe_dims *d, int S) {
 
 // A forced kernel family that does not take the call's weights.
 int forced_path_refused(const coli_moe_dims *d) {
-    if (d->group_size && (g_force_path == 2 || g_force_path == 3))
-        return fail(COLI_EINVAL, "group-scaled weights run the multi-launch kernels only (forced path %d)",
-                    g_force_path);
+    if (d->group_size && g_force_path == 2)
+        return fail(COLI_EINVAL, "the persistent kernel takes per-row scales only");
+    if (d->group_size && d->group_size != 64 && g_force_path == 3)
+        return fail(COLI_EINVAL, "the grouped kernels take per-row scales or groups of 64 (group_size=%d)",
+                    d->group_size);
     return COLI_OK;
 }
 

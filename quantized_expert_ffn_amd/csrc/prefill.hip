@@ -166,6 +166,10 @@ struct PfStage {
     static constexpr int D_BYTES = 32 * C * 4;
     static constexpr int LDS = W_BYTES + A_BYTES + D_BYTES;
     static constexpr int SHIFT = BITS == 8 ? 0 : (BITS == 4 ? 4 : 6);
+    // group scales (one per 64 codes of a row, int4 only): G_PER groups per
+    // stage and matrix, stored group-major [m][g][row] after the scales
+    static constexpr int G_PER = C / 2;
+    static constexpr int GS_BYTES = NM * G_PER * PF_ROWS * 4;
 };
 
 // Weight operand of block j of the stage for lane half h, from the row's
@@ -195,10 +199,10 @@ __device__ __forceinline__ int slot_token(int slot, int P, int K) { return slot 
 // A scale that is 0 or at least 2^-120 qualifies (for SHIFT <= 6 its
 // product with 2^-SHIFT is a normal number or 0); smaller ones take the
 // shifting path, which is exact for every scale.
-template <int SHIFT>
+template <int SHIFT, bool GROUPED = false>
 __device__ __forceinline__ bool scales_fold(const float *d, int nb) {
-    if (SHIFT == 0) return true;
-    constexpr float LOW = 0x1p-120f;
+    if (SHIFT == 0 && !GROUPED) return true;
+    constexpr float LOW = GROUPED ? 0x1p-60f : 0x1p-120f;
     bool ok = true;
     if ((nb & 3) == 0 && (reinterpret_cast<uintptr_t>(d) & 15) == 0) {
         const f32x4 *v4 = reinterpret_cast<const f32x4 *>(d);
@@ -224,6 +228,8 @@ struct PfSrc {
     uint32_t mat[NM];
     uint32_t rb;
     int row0, n_rows, nb;
+    uint32_t smat[NM];   // group-scaled: byte offsets of the scale sections
+    uint32_t srow;       // and bytes of group scales per row
 };
 
 // Stage registers of one thread.
@@ -232,13 +238,23 @@ struct PfRegs {
     u32x4 w[PfStage<BITS, NM>::W_CHUNKS];
     u32x4 a[PfStage<BITS, NM>::A_CHUNKS];
     uint32_t d[PfStage<BITS, NM>::D_WORDS];
+    u32x4 g;   // group-scaled: the stage's 4 group scales of one row (threads < NM * PF_ROWS)
 };
 
-template <int BITS, int NM>
+template <int BITS, int NM, bool GROUPED = false>
 __device__ __forceinline__ void pf_load(PfRegs<BITS, NM> &R, const PfSrc<NM> &src, const uint32_t *col_voff,
                                         const uint32_t *col_doff, int stage) {
     using ST = PfStage<BITS, NM>;
     const int tid = threadIdx.x;
+    if constexpr (GROUPED) {
+        static_assert(ST::G_PER == 4, "group-scaled stages hold 4 groups of 64 codes");
+        if (tid < NM * PF_ROWS) {
+            const int m = tid / PF_ROWS, row = tid % PF_ROWS;
+            const int r = min(src.row0 + row, src.n_rows - 1);
+            R.g = __builtin_amdgcn_raw_buffer_load_b128(src.rw, src.smat[m] + (uint32_t)r * src.srow + 16u * stage,
+                                                        0, 0);
+        }
+    }
 #pragma unroll
     for (int i = 0; i < ST::W_CHUNKS; ++i) {
         // a matrix spans PF_ROWS * 8 / PF_T = 4 chunks of every thread
@@ -263,11 +279,30 @@ __device__ __forceinline__ void pf_load(PfRegs<BITS, NM> &R, const PfSrc<NM> &sr
     }
 }
 
-// FOLD: the scales are stored times 2^-SHIFT.
-template <int BITS, int NM, bool FOLD>
-__device__ __forceinline__ void pf_store(const PfRegs<BITS, NM> &R, uint8_t *lds) {
+// FOLD: the scales are stored times 2^-SHIFT.  GROUPED: the stage's group
+// scales go to LDS too; with FOLD, a nonzero one below 2^-60 sets *refold
+// (the folded chain is then not exact and the tile is recomputed).
+template <int BITS, int NM, bool FOLD, bool GROUPED = false>
+__device__ __forceinline__ void pf_store(const PfRegs<BITS, NM> &R, uint8_t *lds, int *refold = nullptr) {
     using ST = PfStage<BITS, NM>;
     const int tid = threadIdx.x;
+    if constexpr (GROUPED) {
+        if (tid < NM * PF_ROWS) {
+            const int m = tid / PF_ROWS, row = tid % PF_ROWS;
+            float *gs = reinterpret_cast<float *>(lds + ST::LDS) + m * ST::G_PER * PF_ROWS + row;
+            // (the whole vector is reinterpreted: a bit cast of one element of a
+            // vector register compiled to the first element for every one)
+            const f32x4 v4 = __builtin_bit_cast(f32x4, R.g);
+            const float v[4] = {v4.x, v4.y, v4.z, v4.w};
+            bool small = false;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                gs[g * PF_ROWS] = v[g];
+                small = small || (v[g] != 0.0f && __builtin_fabsf(v[g]) < 0x1p-60f);
+            }
+            if (FOLD && small) *refold = 1;
+        }
+    }
 #pragma unroll
     for (int i = 0; i < ST::W_CHUNKS; ++i) {
         const int g = i * PF_T + tid;
@@ -339,11 +374,15 @@ __device__ __forceinline__ i32x4 unpack_raw(typename RawW<BITS>::T w, int h) {
 // Blocks 0 .. nblk - 1 of a stage in LDS (all C of them when FULL).  The
 // raw operands of block j + 1 are read before the chains of block j and
 // unpacked after them, so the LDS latency overlaps the chains.
-template <int BITS, int NM, bool FOLD, int C, bool FULL>
+// GROUPED: lg points at the lane's first row (32 w + 4 h) of group 0 of
+// matrix 0 in the staged group scales; each block's multiplier is
+// d_b * s[row][group] (one binary32 product).
+template <int BITS, int NM, bool FOLD, int C, bool FULL, bool GROUPED = false>
 __device__ __forceinline__ void pf_blocks(float (&acc)[NM][16], const uint8_t *lw, const uint8_t *la,
-                                          const float *ld, int h, int nblk) {
+                                          const float *ld, int h, int nblk, const float *lg = nullptr) {
     using ST = PfStage<BITS, NM>;
     constexpr int SH = ST::SHIFT;
+    float sg[NM][16];
     typename RawW<BITS>::T wr[NM];
     i32x4 xa;
     float da;
@@ -364,12 +403,28 @@ __device__ __forceinline__ void pf_blocks(float (&acc)[NM][16], const uint8_t *l
             xa = *reinterpret_cast<const i32x4 *>(la + 32 * (j + 1));
             da = ld[32 * (j + 1)];
         }
+        if constexpr (GROUPED) {
+            if ((j & 1) == 0) {
+#pragma unroll
+                for (int m = 0; m < NM; ++m)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const f32x4 v =
+                            *reinterpret_cast<const f32x4 *>(lg + (m * ST::G_PER + j / 2) * PF_ROWS + 8 * q);
+                        sg[m][4 * q] = v.x;
+                        sg[m][4 * q + 1] = v.y;
+                        sg[m][4 * q + 2] = v.z;
+                        sg[m][4 * q + 3] = v.w;
+                    }
+            }
+        }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int m = 0; m < NM; ++m)
 #pragma unroll
             for (int r = 0; r < 16; ++r)
-                acc[m][r] = __builtin_fmaf(d, (float)(FOLD ? c[m][r] : c[m][r] >> SH), acc[m][r]);
+                acc[m][r] = __builtin_fmaf(GROUPED ? d * sg[m][r] : d, (float)(FOLD ? c[m][r] : c[m][r] >> SH),
+                                           acc[m][r]);
         __builtin_amdgcn_sched_barrier(0);
     }
 }
@@ -377,15 +432,17 @@ __device__ __forceinline__ void pf_blocks(float (&acc)[NM][16], const uint8_t *l
 // The staged product loop: acc[m][r] = chain over the nb blocks of
 // d_b * isum_b for row 32 w + mfma_c_row(lane, r) of matrix m and the lane's
 // column.  Every wave runs the loads and barriers; `active` waves compute.
-template <int BITS, int NM, bool FOLD, bool TAIL>
+template <int BITS, int NM, bool FOLD, bool TAIL, bool GROUPED = false>
 __device__ __forceinline__ void pf_run(float (&acc)[NM][16], uint8_t *lds, const PfSrc<NM> &src,
-                                       const uint32_t *col_voff, const uint32_t *col_doff, bool active) {
+                                       const uint32_t *col_voff, const uint32_t *col_doff, bool active,
+                                       int *refold = nullptr) {
     using ST = PfStage<BITS, NM>;
     constexpr int SH = ST::SHIFT;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, h = lane >> 5, n = lane & 31;
     const int n_stages = (src.nb + ST::C - 1) / ST::C;
+    const float *lg = reinterpret_cast<const float *>(lds + ST::LDS) + 32 * wave + 4 * h;
     PfRegs<BITS, NM> R;
-    pf_load<BITS, NM>(R, src, col_voff, col_doff, 0);
+    pf_load<BITS, NM, GROUPED>(R, src, col_voff, col_doff, 0);
     const uint8_t *la = lds + ST::W_BYTES + ST::AS * n + 16 * h;
     const float *ld = reinterpret_cast<const float *>(lds + ST::W_BYTES + ST::A_BYTES) + n;
     const uint8_t *lw = lds + ST::WS * (32 * wave + n);
@@ -394,14 +451,14 @@ __device__ __forceinline__ void pf_run(float (&acc)[NM][16], uint8_t *lds, const
     const int n_full = src.nb / ST::C;
     for (int s = 0; s < n_full; ++s) {
         if (s > 0) __syncthreads();  // every wave is done with the previous stage
-        pf_store<BITS, NM, FOLD>(R, lds);
+        pf_store<BITS, NM, FOLD, GROUPED>(R, lds, refold);
         __syncthreads();
-        if (s + 1 < n_stages) pf_load<BITS, NM>(R, src, col_voff, col_doff, s + 1);
-        if (active) pf_blocks<BITS, NM, FOLD, ST::C, true>(acc, lw, la, ld, h, ST::C);
+        if (s + 1 < n_stages) pf_load<BITS, NM, GROUPED>(R, src, col_voff, col_doff, s + 1);
+        if (active) pf_blocks<BITS, NM, FOLD, ST::C, true, GROUPED>(acc, lw, la, ld, h, ST::C, lg);
     }
     if (TAIL && n_full < n_stages) {
         if (n_full > 0) __syncthreads();
-        pf_store<BITS, NM, FOLD>(R, lds);
+        pf_store<BITS, NM, FOLD, GROUPED>(R, lds, refold);
         __syncthreads();
         const int nblk = src.nb - ST::C * n_full;
         if (active) {
@@ -413,8 +470,11 @@ __device__ __forceinline__ void pf_run(float (&acc)[NM][16], uint8_t *lds, const
                     const i32x16 c = mfma_i8_32x32x32(
                         unpack_raw<BITS>(lds_raw<BITS>(lw + m * PF_ROWS * ST::WS, j, h), h), xb);
 #pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        acc[m][r] = __builtin_fmaf(d, (float)(FOLD ? c[r] : c[r] >> SH), acc[m][r]);
+                    for (int r = 0; r < 16; ++r) {
+                        const float dm = GROUPED ? d * lg[(m * ST::G_PER + j / 2) * PF_ROWS + mfma_c_row(lane, r) - 4 * h]
+                                                 : d;
+                        acc[m][r] = __builtin_fmaf(dm, (float)(FOLD ? c[r] : c[r] >> SH), acc[m][r]);
+                    }
                 }
             }
         }
@@ -430,6 +490,27 @@ __device__ __forceinline__ void pf_dispatch(bool fold, float (&acc)[NM][16], uin
         pf_run<BITS, NM, true, TAIL>(acc, lds, src, col_voff, col_doff, active);
     else
         pf_run<BITS, NM, false, TAIL>(acc, lds, src, col_voff, col_doff, active);
+}
+
+// Group-scaled weights: the folded chain multiplies d * 2^-SHIFT by the group
+// scale, which equals (d * s) * 2^-SHIFT while that product stays normal; the
+// fold test admits block scales of at least 2^-60 and the stores check the
+// group scales, so every product is at least 2^-120.  A tile whose group
+// scales fail the check is recomputed with the shifting chain.
+template <int BITS, int NM, bool TAIL>
+__device__ __forceinline__ void pf_dispatch_grouped(bool fold, float (&acc)[NM][16], uint8_t *lds,
+                                                    const PfSrc<NM> &src, const uint32_t *col_voff,
+                                                    const uint32_t *col_doff, bool active, int *refold) {
+    if (fold) {
+        pf_run<BITS, NM, true, TAIL, true>(acc, lds, src, col_voff, col_doff, active, refold);
+        __syncthreads();
+        if (!*refold) return;
+#pragma unroll
+        for (int m = 0; m < NM; ++m)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[m][r] = 0.0f;
+    }
+    pf_run<BITS, NM, false, TAIL, true>(acc, lds, src, col_voff, col_doff, active, refold);
 }
 
 // Columns of the tile: the slot of pair n (the tile's first pair past its
@@ -449,11 +530,13 @@ __device__ __forceinline__ PfCols pf_col(const int32_t *pairs, const Tile &tl, i
 // ---- gate/up ------------------------------------------------------------
 // Grid (ceil(I / PF_ROWS), tile bound).  Epilogue: row scales, SwiGLU and
 // Q8_0 over each wave's 32 rows (one block of h) for every live column.
-template <int BITS>
+// GROUPED: int4 with one scale per 64 codes of a row (no row scale).
+template <int BITS, bool GROUPED>
 __global__ __launch_bounds__(PF_T, 3) void k_pf_gateup(const FwdArgs a, const int32_t *__restrict__ tiles) {
     using ST = PfStage<BITS, 2>;
-    __shared__ __attribute__((aligned(16))) uint8_t lds[ST::LDS];
+    __shared__ __attribute__((aligned(16))) uint8_t lds[ST::LDS + (GROUPED ? ST::GS_BYTES : 0)];
     __shared__ uint32_t col_voff[32], col_doff[32];
+    __shared__ int refold;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, h = lane >> 5, n = lane & 31;
     const int H = a.H, I = a.I, P = a.S * a.K, nb = H / 32;
     if ((int)blockIdx.y >= tiles[0]) return;
@@ -467,12 +550,13 @@ __global__ __launch_bounds__(PF_T, 3) void k_pf_gateup(const FwdArgs a, const in
         if (threadIdx.x == 0 && blockIdx.x == 0) raise_status(a.status, ST_NOTRESIDENT);
         return;
     }
-    const BlobLayout BL = blob_layout(H, I, BITS);
+    const BlobLayout BL = blob_layout(H, I, BITS, GROUPED ? 64 : 0);
     const PfCols col = pf_col(tab + U.pairs, tl, n, P, a.K);
     if (threadIdx.x < 32) {
         col_voff[n] = (uint32_t)col.tok * (uint32_t)H;
         col_doff[n] = (uint32_t)col.tok * (uint32_t)nb * 4u;
     }
+    if (threadIdx.x == 0) refold = 0;
     PfSrc<2> src;
     src.rw = make_rsrc(blob, (uint32_t)BL.total);
     src.ra = make_rsrc(a.qx, (uint32_t)a.S * (uint32_t)H);
@@ -483,6 +567,9 @@ __global__ __launch_bounds__(PF_T, 3) void k_pf_gateup(const FwdArgs a, const in
     src.row0 = blockIdx.x * PF_ROWS;
     src.n_rows = I;
     src.nb = nb;
+    src.smat[0] = (uint32_t)BL.s_gate;
+    src.smat[1] = (uint32_t)BL.s_up;
+    src.srow = (uint32_t)(4 * (H / 64));
     __syncthreads();
     const int i0 = src.row0 + 32 * wave;
     const bool active = i0 < I;
@@ -492,11 +579,18 @@ __global__ __launch_bounds__(PF_T, 3) void k_pf_gateup(const FwdArgs a, const in
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[m][r] = 0.0f;
     // every wave has the same 32 columns, hence the same choice
-    const bool fold = scales_fold<ST::SHIFT>(a.dx + (size_t)col.tok * nb, nb);
-    if (nb % ST::C != 0)
-        pf_dispatch<BITS, 2, true>(fold, acc, lds, src, col_voff, col_doff, active);
-    else
-        pf_dispatch<BITS, 2, false>(fold, acc, lds, src, col_voff, col_doff, active);
+    const bool fold = scales_fold<ST::SHIFT, GROUPED>(a.dx + (size_t)col.tok * nb, nb);
+    if constexpr (GROUPED) {
+        if (nb % ST::C != 0)
+            pf_dispatch_grouped<BITS, 2, true>(fold, acc, lds, src, col_voff, col_doff, active, &refold);
+        else
+            pf_dispatch_grouped<BITS, 2, false>(fold, acc, lds, src, col_voff, col_doff, active, &refold);
+    } else {
+        if (nb % ST::C != 0)
+            pf_dispatch<BITS, 2, true>(fold, acc, lds, src, col_voff, col_doff, active);
+        else
+            pf_dispatch<BITS, 2, false>(fold, acc, lds, src, col_voff, col_doff, active);
+    }
     if (!active || !col.live) return;
     const float *sg = reinterpret_cast<const float *>(blob + BL.s_gate) + i0;
     const float *su = reinterpret_cast<const float *>(blob + BL.s_up) + i0;
@@ -504,7 +598,7 @@ __global__ __launch_bounds__(PF_T, 3) void k_pf_gateup(const FwdArgs a, const in
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         const int row = mfma_c_row(lane, r);
-        hv[r] = swiglu_f32(acc[0][r] * sg[row], acc[1][r] * su[row]);
+        hv[r] = GROUPED ? swiglu_f32(acc[0][r], acc[1][r]) : swiglu_f32(acc[0][r] * sg[row], acc[1][r] * su[row]);
         amax = __builtin_fmaxf(amax, __builtin_fabsf(hv[r]));
     }
     // Q8_0 over the 32 rows of the column, held by lanes n and n + 32
@@ -531,11 +625,12 @@ __global__ __launch_bounds__(PF_T, 3) void k_pf_gateup(const FwdArgs a, const in
 // ---- down ---------------------------------------------------------------
 // Grid (ceil(H / PF_ROWS), tile bound): Y[slot][row] = s_d[row] * chain over
 // the I / 32 blocks of Q8_0(h) of the slot.
-template <int BITS>
+template <int BITS, bool GROUPED>
 __global__ __launch_bounds__(PF_T, 4) void k_pf_down(const FwdArgs a, const int32_t *__restrict__ tiles) {
     using ST = PfStage<BITS, 1>;
-    __shared__ __attribute__((aligned(16))) uint8_t lds[ST::LDS];
+    __shared__ __attribute__((aligned(16))) uint8_t lds[ST::LDS + (GROUPED ? ST::GS_BYTES : 0)];
     __shared__ uint32_t col_voff[32], col_doff[32];
+    __shared__ int refold;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, h = lane >> 5, n = lane & 31;
     const int H = a.H, I = a.I, P = a.S * a.K, nb = I / 32;
     if ((int)blockIdx.y >= tiles[0]) return;
@@ -546,12 +641,13 @@ __global__ __launch_bounds__(PF_T, 4) void k_pf_down(const FwdArgs a, const int3
     const int e = tab[U.uexp + tl.u];
     const uint8_t *blob = e < 0 ? a.shared : a.blobs[e];
     if (!blob) return;  // reported by the gate/up kernel
-    const BlobLayout BL = blob_layout(H, I, BITS);
+    const BlobLayout BL = blob_layout(H, I, BITS, GROUPED ? 64 : 0);
     const PfCols col = pf_col(tab + U.pairs, tl, n, P, a.K);
     if (threadIdx.x < 32) {
         col_voff[n] = (uint32_t)col.slot * (uint32_t)I;
         col_doff[n] = (uint32_t)col.slot * (uint32_t)nb * 4u;
     }
+    if (threadIdx.x == 0) refold = 0;
     const uint32_t slots = (uint32_t)a.S * (uint32_t)(a.K + 1);
     PfSrc<1> src;
     src.rw = make_rsrc(blob, (uint32_t)BL.total);
@@ -562,17 +658,26 @@ __global__ __launch_bounds__(PF_T, 4) void k_pf_down(const FwdArgs a, const int3
     src.row0 = blockIdx.x * PF_ROWS;
     src.n_rows = H;
     src.nb = nb;
+    src.smat[0] = (uint32_t)BL.s_down;
+    src.srow = (uint32_t)(4 * (I / 64));
     __syncthreads();
     const int r0 = src.row0 + 32 * wave;
     const bool active = r0 < H;
     float acc[1][16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[0][r] = 0.0f;
-    const bool fold = scales_fold<ST::SHIFT>(a.dh + (size_t)col.slot * nb, nb);
-    if (nb % ST::C != 0)
-        pf_dispatch<BITS, 1, true>(fold, acc, lds, src, col_voff, col_doff, active);
-    else
-        pf_dispatch<BITS, 1, false>(fold, acc, lds, src, col_voff, col_doff, active);
+    const bool fold = scales_fold<ST::SHIFT, GROUPED>(a.dh + (size_t)col.slot * nb, nb);
+    if constexpr (GROUPED) {
+        if (nb % ST::C != 0)
+            pf_dispatch_grouped<BITS, 1, true>(fold, acc, lds, src, col_voff, col_doff, active, &refold);
+        else
+            pf_dispatch_grouped<BITS, 1, false>(fold, acc, lds, src, col_voff, col_doff, active, &refold);
+    } else {
+        if (nb % ST::C != 0)
+            pf_dispatch<BITS, 1, true>(fold, acc, lds, src, col_voff, col_doff, active);
+        else
+            pf_dispatch<BITS, 1, false>(fold, acc, lds, src, col_voff, col_doff, active);
+    }
     if (!active || !col.live) return;
     const float *sd = reinterpret_cast<const float *>(blob + BL.s_down) + r0;
     float *yrow = a.Y + (size_t)col.slot * H + r0;
@@ -580,10 +685,10 @@ __global__ __launch_bounds__(PF_T, 4) void k_pf_down(const FwdArgs a, const int3
     for (int g = 0; g < 4; ++g) {
         const int rr = 8 * g + 4 * h;
         f32x4 v;
-        v.x = acc[0][4 * g + 0] * sd[rr + 0];
-        v.y = acc[0][4 * g + 1] * sd[rr + 1];
-        v.z = acc[0][4 * g + 2] * sd[rr + 2];
-        v.w = acc[0][4 * g + 3] * sd[rr + 3];
+        v.x = GROUPED ? acc[0][4 * g + 0] : acc[0][4 * g + 0] * sd[rr + 0];
+        v.y = GROUPED ? acc[0][4 * g + 1] : acc[0][4 * g + 1] * sd[rr + 1];
+        v.z = GROUPED ? acc[0][4 * g + 2] : acc[0][4 * g + 2] * sd[rr + 2];
+        v.w = GROUPED ? acc[0][4 * g + 3] : acc[0][4 * g + 3] * sd[rr + 3];
         *reinterpret_cast<f32x4 *>(yrow + rr) = v;
     }
 }
@@ -605,25 +710,29 @@ hipError_t launch_group(const int32_t *idx, int S, int K, int E, int n_shared, u
     return launch(k_group, dim3(1), dim3(1024), smem, st, idx, S, K, E, n_shared, units, tiles, status);
 }
 
-template <int BITS>
+template <int BITS, bool GROUPED = false>
 static hipError_t pf_gateup_bits(const FwdArgs &a, const int32_t *tiles, hipStream_t st) {
     const dim3 grid((a.I + PF_ROWS - 1) / PF_ROWS, pf_tile_bound(a.S, a.K, a.E, a.n_shared));
-    return launch(k_pf_gateup<BITS>, grid, dim3(PF_T), 0, st, a, tiles);
+    return launch(k_pf_gateup<BITS, GROUPED>, grid, dim3(PF_T), 0, st, a, tiles);
 }
 
-template <int BITS>
+template <int BITS, bool GROUPED = false>
 static hipError_t pf_down_bits(const FwdArgs &a, const int32_t *tiles, hipStream_t st) {
     const dim3 grid((a.H + PF_ROWS - 1) / PF_ROWS, pf_tile_bound(a.S, a.K, a.E, a.n_shared));
-    return launch(k_pf_down<BITS>, grid, dim3(PF_T), 0, st, a, tiles);
+    return launch(k_pf_down<BITS, GROUPED>, grid, dim3(PF_T), 0, st, a, tiles);
 }
 
+// Group-scaled weights: int4 with groups of 64 (the API routes other group
+// sizes to the decode kernels).
 hipError_t launch_pf_gateup(const FwdArgs &a, const int32_t *tiles, int bits, hipStream_t st) {
+    if (a.group) return pf_gateup_bits<4, true>(a, tiles, st);
     if (bits == 8) return pf_gateup_bits<8>(a, tiles, st);
     if (bits == 4) return pf_gateup_bits<4>(a, tiles, st);
     return pf_gateup_bits<2>(a, tiles, st);
 }
 
 hipError_t launch_pf_down(const FwdArgs &a, const int32_t *tiles, int bits, hipStream_t st) {
+    if (a.group) return pf_down_bits<4, true>(a, tiles, st);
     if (bits == 8) return pf_down_bits<8>(a, tiles, st);
     if (bits == 4) return pf_down_bits<4>(a, tiles, st);
     return pf_down_bits<2>(a, tiles, st);

@@ -2,8 +2,8 @@
 row; JustVugg/colibri, "Get started" and "Other supported models") through
 the C ABI against the CPU oracle: the router launch's shared-expert tiles
 (up to two tokens), gate/up, down + combine by output rows, the down and
-combine kernels of larger batches, and the error contract of the kernel
-families that take per-row scales only."""
+combine kernels, the grouped matrix-core kernels of large batches (with the
+exact fallback for tiny group scales), and the error contract."""
 import dataclasses
 
 import numpy as np
@@ -100,20 +100,109 @@ def test_glm_gs64_layer_entry(torch, S):
     say("gs64 glm parity", parity(out, want))
 
 
+MID_GS64 = synth.LayerSpec(hidden=512, inter=256, n_experts=64, top_k=8, n_shared=1, wbits=4, group=64)
+
+
+def _zipf_layer(spec, S, seed=0):
+    d = synth.layer_inputs(seed, 0, spec, S)
+    d["x"] = synth.prefill_hidden_states(seed, 0, spec, S)
+    d["bias"] = np.zeros(spec.n_experts, np.float32)
+    d["blobs"] = [synth.expert_blob(seed, 0, e, spec) for e in range(spec.n_experts)]
+    d["shared"] = synth.expert_blob(seed, 0, spec.n_experts, spec)
+    return d
+
+
+@pytest.mark.parametrize("S", [160])
+def test_mid_gs64_grouped_prefill(torch, S):
+    """Batches of 9 or more tokens take the int8 matrix-core kernels with the
+    group scales staged per stage: a Zipf-routed mid-size layer, every output
+    element against the oracle."""
+    from synth.device import upload_layer
+    spec = MID_GS64
+    say(f"gs64 grouped mid layer S={S}")
+    d = _zipf_layer(spec, S, seed=3)
+    dims = q().make_dims(spec)
+    dl = upload_layer(d)
+    ws = workspace(dims, S)
+    idx, w, out = _layer_call(torch, dims, dl, ws)
+    assert status(ws) == 0, q().coli_moe_last_error()
+    o_out, o_idx, o_w = oracle.layer(spec, d["x"], d["router_w"], d["bias"], d["blobs"], d["shared"])
+    assert np.array_equal(idx, o_idx)
+    assert int(np.bincount(idx.ravel()).max()) > 64   # one expert spans three tiles
+    say("parity", parity(out, o_out))
+
+
+@pytest.mark.parametrize("S", [3, 40])
+def test_tiny_gs64_forced_grouped(torch, S):
+    """The grouped kernels forced at small and ragged batches (tiles of one
+    to a few pairs), against the oracle."""
+    from synth.device import upload_layer
+    qm = q()
+    spec = synth.TINY_GS64
+    say(f"gs64 forced grouped tiny S={S}")
+    d = synth.tiny_layer(seed=8, S=S, spec=spec)
+    dims = qm.make_dims(spec)
+    dl = upload_layer(d)
+    ws = workspace(dims, S)
+    qm.coli_moe_debug_force_path(qm.PATH_GROUPED)
+    try:
+        idx, w, out = _layer_call(torch, dims, dl, ws)
+    finally:
+        qm.coli_moe_debug_force_path(qm.PATH_AUTO)
+    assert status(ws) == 0, qm.coli_moe_last_error()
+    o_out, o_idx, _ = oracle.layer(spec, d["x"], d["router_w"], d["bias"], d["blobs"], d["shared"])
+    assert np.array_equal(idx, o_idx)
+    parity(out, o_out)
+
+
+def test_gs64_grouped_tiny_group_scales_take_the_exact_path(torch):
+    """Group scales below 2^-60 would make the folded chain inexact: the
+    grouped kernels then recompute the tile with the shifting chain, and the
+    result still equals the oracle's."""
+    from synth.device import upload_layer
+    qm = q()
+    spec = synth.TINY_GS64
+    S = 20
+    say(f"gs64 grouped tiny group scales S={S}")
+    d = synth.tiny_layer(seed=10, S=S, spec=spec)
+    lay = oracle.blob_layout(spec.hidden, spec.inter, spec.wbits, spec.group)
+    blobs = []
+    for b in d["blobs"] + [d["shared"]]:
+        b = b.copy()
+        for sec in ("s_gate", "s_down"):
+            sc = b[lay[sec]:lay[sec] + 64].view(np.float32)   # the first 16 scales of the section
+            sc[:8] = sc[:8] * np.float32(2.0 ** -70)
+        blobs.append(b)
+    d["blobs"], d["shared"] = blobs[:-1], blobs[-1]
+    dims = qm.make_dims(spec)
+    dl = upload_layer(d)
+    ws = workspace(dims, S)
+    qm.coli_moe_debug_force_path(qm.PATH_GROUPED)
+    try:
+        idx, w, out = _layer_call(torch, dims, dl, ws)
+    finally:
+        qm.coli_moe_debug_force_path(qm.PATH_AUTO)
+    assert status(ws) == 0, qm.coli_moe_last_error()
+    o_out, o_idx, _ = oracle.layer(spec, d["x"], d["router_w"], d["bias"], d["blobs"], d["shared"])
+    assert np.array_equal(idx, o_idx)
+    parity(out, o_out)
+
+
 def test_gs_error_contract(torch):
     """Group scales need int4 and a power-of-two group dividing H and I; the
-    persistent and grouped kernel families refuse them when forced."""
+    persistent kernel refuses them when forced, the grouped kernels every
+    group size but 64."""
     from synth.device import upload_layer
     qm = q()
     for bad in (dataclasses.replace(synth.TINY_GS64, wbits=8), dataclasses.replace(synth.TINY_GS64, group=48),
                 dataclasses.replace(synth.TINY_GS64, group=256)):   # 256 does not divide inter 128
         assert qm.coli_moe_expert_bytes(qm.make_dims(bad)) == 0
-    spec = synth.TINY_GS64
-    d = synth.tiny_layer(seed=7, S=3, spec=spec)
-    dims = qm.make_dims(spec)
-    dl = upload_layer(d)
-    ws = workspace(dims, 3)
-    for path in (qm.PATH_PERSISTENT, qm.PATH_GROUPED):
+    for spec, path in ((synth.TINY_GS64, qm.PATH_PERSISTENT),
+                       (dataclasses.replace(synth.TINY_GS64, group=32), qm.PATH_GROUPED)):
+        d = synth.tiny_layer(seed=7, S=3, spec=spec)
+        dims = qm.make_dims(spec)
+        dl = upload_layer(d)
+        ws = workspace(dims, 3)
         qm.coli_moe_debug_force_path(path)
         try:
             with pytest.raises(qm.ColiError) as err:
@@ -121,4 +210,4 @@ def test_gs_error_contract(torch):
             assert err.value.code == qm.COLI_EINVAL
         finally:
             qm.coli_moe_debug_force_path(qm.PATH_AUTO)
-    assert status(ws) == 0
+        assert status(ws) == 0
