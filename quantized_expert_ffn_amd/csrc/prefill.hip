@@ -532,7 +532,7 @@ __device__ __forceinline__ PfCols pf_col(const int32_t *pairs, const Tile &tl, i
 // Q8_0 over each wave's 32 rows (one block of h) for every live column.
 // GROUPED: int4 with one scale per 64 codes of a row (no row scale).
 template <int BITS, bool GROUPED>
-__global__ __launch_bounds__(PF_T, 3) void k_pf_gateup(const FwdArgs a, const int32_t *__restrict__ tiles) {
+__global__ __launch_bounds__(PF_T) __attribute__((amdgpu_waves_per_eu(GROUPED ? 2 : 3))) void k_pf_gateup(const FwdArgs a, const int32_t *__restrict__ tiles) {
     using ST = PfStage<BITS, 2>;
     __shared__ __attribute__((aligned(16))) uint8_t lds[ST::LDS + (GROUPED ? ST::GS_BYTES : 0)];
     __shared__ uint32_t col_voff[32], col_doff[32];
