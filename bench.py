@@ -245,7 +245,7 @@ def main():
         # router launch; the gate/up launch then reads the routed experts only
         in_router = args.path == "layer" and S <= 2 and 64 * H * spec.wbits // 8 <= 256 * 1024
         gu_units = n_units - (spec.n_shared if in_router else 0)
-        dom, dom_kernel = "gateup", "k_gateup<%d,%d>" % (spec.wbits, min(S, 4))
+        dom, dom_kernel = "gateup", "k_gateup<%d,%d%s>" % (spec.wbits, min(S, 4), ",gs64" if spec.group else "")
         n_scales = H // spec.group if spec.group else 1   # per gate / up row
         dom_bytes = gu_units * (2 * spec.inter * H * spec.wbits // 8 + 2 * spec.inter * 4 * n_scales)
     dom_us = kernel_us[dom]
@@ -368,6 +368,7 @@ def run_prefill(args, q, synth):
     import torch
 
     spec = synth.GLM_GS64 if args.group_size else synth.GLM
+    pf_kernel = "k_pf_gateup<4,gs64>" if spec.group else "k_pf_gateup<4>"
     dims = q.make_dims(spec)
     S, H, I, E, K = args.tokens, spec.hidden, spec.inter, spec.n_experts, spec.top_k
     bb = spec.blob_bytes
@@ -459,9 +460,9 @@ def run_prefill(args, q, synth):
                         "median": float(np.median(counts[counts > 0])), "max": int(counts.max())},
         },
         "roofline": {
-            "bound": "mfma", "kernel": "k_pf_gateup<4>",
+            "bound": "mfma", "kernel": pf_kernel,
             "achieved": round(achieved, 1), "peak": INT8_PEAK_TOPS, "unit": "TOPS",
-            "frac": round(achieved / INT8_PEAK_TOPS, 4), "traffic": counted_traffic("k_pf_gateup<4>"),
+            "frac": round(achieved / INT8_PEAK_TOPS, 4), "traffic": counted_traffic(pf_kernel),
             "algorithmic_ops_per_launch": ops_gateup, "avg_launch_us": round(g_us, 3),
         },
         "layer_int8_tops": round(layer_tops, 1),
