@@ -19,6 +19,13 @@ if not os.path.exists(LIB_PATH):
         f"{LIB_PATH} is missing: build it with `python -m quantized_expert_ffn_amd.build` "
         "(or __graft_entry__.build()); the MoE layer has no non-HIP implementation")
 
+# torch's HIP runtime is loaded first, so that the library's libamdhip64.so.7
+# and libhsa-runtime64.so.1 resolve to the copies torch already holds (same
+# sonames): loaded the other way round, the process ends up with the
+# /opt/rocm runtime under torch as well, and the library's device queries
+# have been seen to report no device.
+import torch  # noqa: E402,F401
+
 _lib = ctypes.CDLL(LIB_PATH)
 
 COLI_OK, COLI_EINVAL, COLI_ENONFINITE, COLI_EHIP, COLI_ENOTRESIDENT, COLI_EWORKSPACE = 0, -1, -2, -3, -4, -5
