@@ -217,8 +217,7 @@ def main():
         graph.replay()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    for _ in range(reps):
-        graph.replay()
+    rep_ev = replay_timed(graph, reps)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t1
     steps = reps * G
@@ -227,6 +226,7 @@ def main():
         raise RuntimeError(f"device status after replay {rc}: {q.coli_moe_last_error()}")
     ms_per_step = 1e3 * elapsed / steps
     tokens_per_s = steps * S / elapsed
+    step_spread = replay_spread(rep_ev, G)
 
     # algorithmic bytes: each step reads W_r and each unique expert of its
     # tokens (8 routed + shared for one token) once
@@ -288,6 +288,7 @@ def main():
         "layer_hbm_frac": round(layer_gbs / HBM_PEAK_GBS, 4),
         "kernel_avg_us": {k: round(v, 3) for k, v in kernel_us.items()},
         "experts_read_per_step": n_units,
+        "ms_per_step_p10_p50_p90": step_spread,
     }
 
     if not args.no_cpu_baseline:
@@ -298,6 +299,27 @@ def main():
 
 KINDS = (("router_logits", 0), ("router_select", 1), ("quant_x", 7), ("group", 8), ("gateup", 2), ("down", 3),
          ("combine", 4), ("layer", 5), ("forward_persistent", 6))
+
+
+def replay_timed(graph, reps):
+    """Replays the captured graph reps times, with an event pair around each
+    replay; returns the pairs (read after the caller's synchronize)."""
+    import torch
+    evs = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        graph.replay()
+        b.record()
+        evs.append((a, b))
+    return evs
+
+
+def replay_spread(evs, steps_per_replay):
+    """10th, 50th and 90th percentile over the replays of ms per step."""
+    import numpy as np
+    v = np.array([a.elapsed_time(b) / steps_per_replay for a, b in evs])
+    return [round(float(x), 5) for x in np.percentile(v, [10, 50, 90])]
 
 
 def add_measured_roof(res, q, kind):
@@ -417,8 +439,7 @@ def run_prefill(args, q, synth):
         graph.replay()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    for _ in range(reps):
-        graph.replay()
+    rep_ev = replay_timed(graph, reps)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t1
     steps = reps * G
@@ -468,6 +489,7 @@ def run_prefill(args, q, synth):
         "layer_int8_tops": round(layer_tops, 1),
         "layer_int8_frac": round(layer_tops / INT8_PEAK_TOPS, 4),
         "layer_hbm_gbs": round(hbm_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+        "ms_per_step_p10_p50_p90": replay_spread(rep_ev, G),
         "kernel_avg_us": {k: round(v, 3) for k, v in kernel_us.items()},
     }
     if not args.no_cpu_baseline:

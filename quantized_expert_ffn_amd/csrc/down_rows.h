@@ -137,8 +137,10 @@ struct DownTile {
     __device__ __forceinline__ float ld_dh(size_t i) const { return COHERENT ? ld_dev(a.dh + i) : a.dh[i]; }
 
     // Group scales of this wave's DR_RPW rows for every unit of the batch
-    // into the wave's LDS region of gsl (UB x DR_RPW x ngr floats): all of
-    // the wave's loads are issued before the first is stored.
+    // into the wave's LDS region of gsl (UB x DR_RPW x ngr floats), by direct
+    // global-to-LDS loads (no registers held; the caller drains them before
+    // its barrier).  A unit that is not resident leaves its scales unset:
+    // its block dots are zero and its rows' results are replaced by 0.
     __device__ __forceinline__ void stage_groups(int u0, int u1, float *gsl) {
         const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
         const int ngr = a.I / a.group;
@@ -147,26 +149,17 @@ struct DownTile {
         const int n = (u1 - u0) * DR_RPW * ngr;
         if ((ngr & 3) == 0) {
             const int wpr = ngr / 4, nw = n / 4;
-            for (int w0 = 0; w0 < nw; w0 += 4 * 64) {
-                i32x4 v[4];
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    const int w = w0 + lane + 64 * k;
-                    v[k] = i32x4{0, 0, 0, 0};
-                    if (w < nw) {
-                        const int ur = w / wpr, p = w - ur * wpr;
-                        const uint8_t *blob = ublob[u0 + ur / DR_RPW];
-                        if (blob)
-                            v[k] = *reinterpret_cast<const i32x4 *>(
-                                blob + BL.s_down + ((size_t)(rw0 + ur % DR_RPW) * ngr + 4 * p) * 4);
-                    }
-                }
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    const int w = w0 + lane + 64 * k;
-                    if (w < nw) reinterpret_cast<i32x4 *>(dst)[w] = v[k];
+            for (int w0 = 0; w0 < nw; w0 += 64) {
+                const int w = w0 + lane;
+                if (w < nw) {
+                    const int ur = w / wpr, p = w - ur * wpr;
+                    const uint8_t *blob = ublob[u0 + ur / DR_RPW];
+                    if (blob)
+                        lds_dma16(blob + BL.s_down + ((size_t)(rw0 + ur % DR_RPW) * ngr + 4 * p) * 4,
+                                  dst + 4 * w0);
                 }
             }
+            drain_vm();
         } else {
             for (int i = lane; i < n; i += 64) {
                 const int ur = i / ngr, g = i - ur * ngr;

@@ -262,15 +262,13 @@ __device__ __forceinline__ float chain_chunk_g(float acc, const int32_t *is, con
                 iv[q4] = *reinterpret_cast<const i32x4 *>(is + qq + 4 * q4);
                 dd[q4] = *reinterpret_cast<const f32x4 *>(dv + qq + 4 * q4);
             }
-            float m[16];
-#pragma unroll
-            for (int j = 0; j < 16; ++j) m[j] = gs[(qq + j) >> lgb];
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
-                acc = __builtin_fmaf(dd[q4].x * m[4 * q4], (float)iv[q4].x, acc);
-                acc = __builtin_fmaf(dd[q4].y * m[4 * q4 + 1], (float)iv[q4].y, acc);
-                acc = __builtin_fmaf(dd[q4].z * m[4 * q4 + 2], (float)iv[q4].z, acc);
-                acc = __builtin_fmaf(dd[q4].w * m[4 * q4 + 3], (float)iv[q4].w, acc);
+                const int b = qq + 4 * q4;
+                acc = __builtin_fmaf(dd[q4].x * gs[b >> lgb], (float)iv[q4].x, acc);
+                acc = __builtin_fmaf(dd[q4].y * gs[(b + 1) >> lgb], (float)iv[q4].y, acc);
+                acc = __builtin_fmaf(dd[q4].z * gs[(b + 2) >> lgb], (float)iv[q4].z, acc);
+                acc = __builtin_fmaf(dd[q4].w * gs[(b + 3) >> lgb], (float)iv[q4].w, acc);
             }
         }
     } else {
