@@ -297,7 +297,10 @@ int forward_launches(FwdArgs &a, int bits, bool any_pending, void *pending_ready
     e = launch_gateup(a, bits, st);
     timing_after(KK_GATEUP, st);
     if (e != hipSuccess) return hip_fail(e, "gate/up launch");
-    if (a.S <= 8 && down_rows_smem(a.S, a.I, a.E, a.K, a.n_shared, a.group, bits) <= 64 * 1024) {
+    // down + combine by output rows up to 8 tokens while two workgroups fit a
+    // CU (the 4-token int8 verify step needs 76 KiB: 76 us against 91 us for
+    // the per-unit down and the combine)
+    if (a.S <= 8 && down_rows_smem(a.S, a.I, a.E, a.K, a.n_shared, a.group, bits) <= 80 * 1024) {
         timing_before(KK_DOWN, st);
         e = launch_down_rows(a, bits, st);
         timing_after(KK_DOWN, st);
