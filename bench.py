@@ -488,6 +488,11 @@ def run_prefill(args, q, synth):
         },
         "layer_int8_tops": round(layer_tops, 1),
         "layer_int8_frac": round(layer_tops / INT8_PEAK_TOPS, 4),
+        # the attainable roofline of the whole layer: min(int8 peak, its
+        # arithmetic intensity (ops per algorithmic HBM byte) x HBM peak)
+        "layer_ops_per_byte": round(ops_layer / hbm_bytes, 1),
+        "layer_attainable_tops": round(min(INT8_PEAK_TOPS, ops_layer / hbm_bytes * HBM_PEAK_GBS / 1e3), 1),
+        "layer_frac_of_attainable": round(layer_tops / min(INT8_PEAK_TOPS, ops_layer / hbm_bytes * HBM_PEAK_GBS / 1e3), 4),
         "layer_hbm_gbs": round(hbm_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         "ms_per_step_p10_p50_p90": replay_spread(rep_ev, G),
         "kernel_avg_us": {k: round(v, 3) for k, v in kernel_us.items()},
