@@ -128,9 +128,8 @@ def test_mfma_i8_lane_layout(torch):
     for lane in range(64):
         for r in range(16):
             want[lane, r] = C[8 * (r // 4) + 4 * (lane // 32) + r % 4, lane % 32]
-    if not np.array_equal(got, want):
-        np.save("gpurun_out/mfma_raw.npy", np.stack([a_raw.astype(np.int32), b_raw.astype(np.int32), got]))
-    assert np.array_equal(got, want)
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, f"{len(bad)} lane registers differ, first (lane, register) {bad[:4].tolist()}"
 
 
 def test_roof_stream_read_reads_every_word(torch):
