@@ -126,7 +126,10 @@ int coli_moe_route(const coli_moe_dims *dims, int32_t n_tokens, const float *x,
  *                batches of 9 or more tokens wait for the event first
  *   out          device f32 [n_tokens, H]; each element written once
  * Batches of up to 8 tokens run the decode kernels (GEMV-shaped, bound by
- * HBM bandwidth).  Larger batches run the grouped kernels: one launch builds
+ * HBM bandwidth; down and combine in one launch by output rows while its
+ * LDS stays within 80 KiB).  Larger batches run the grouped kernels (per-row
+ * scales or groups of 64; other group sizes keep the decode kernels): one
+ * launch builds
  * the unit table and its tiles of up to 32 (token, expert) pairs of one
  * expert, then gate/up and down are int8 matrix-core products per (32-row
  * tile, pair tile) with the exact per-block f32 chains, then the combine.
@@ -143,7 +146,11 @@ int coli_moe_forward(const coli_moe_dims *dims, int32_t n_tokens, const float *x
  * The whole layer in one call: the result of coli_moe_route followed by
  * coli_moe_forward (same bits), with the routing also written to topk_idx /
  * topk_w.  By default it runs the multi-launch kernels of those two calls,
- * with Q8_0(x) produced once by the router-logit launch.  A persistent
+ * with Q8_0(x) produced once by the router-logit launch; up to 8 tokens that
+ * launch also selects the routing and writes the call's unit table, and up
+ * to 2 tokens (when the shared expert's 32-row gate/up tiles hold at most
+ * 256 KiB of codes) it also runs the shared expert's gate/up, whose pairs do
+ * not depend on the routing.  A persistent
  * single-launch kernel (router, gate/up and down+combine phases separated
  * by grid barriers) serves up to 8 tokens when selected with
  * coli_moe_debug_force_path.  Arguments as for coli_moe_route and
