@@ -240,10 +240,11 @@ def main():
         dom, dom_kernel = "forward_persistent", "k_layer<%d,%d,0,24>" % (spec.wbits, S)
         dom_bytes = n_units * bb
     else:
-        # for up to 2 tokens with at most 256 KiB of shared gate/up rows per
-        # 32-row tile, the layer call runs the shared expert's gate/up in its
-        # router launch; the gate/up launch then reads the routed experts only
-        in_router = args.path == "layer" and S <= 2 and 64 * H * spec.wbits // 8 <= 256 * 1024
+        # for up to 2 tokens with at most 128 KiB of shared gate/up rows per
+        # 16-row half tile, the layer call runs the shared expert's gate/up in
+        # its router launch; the gate/up launch then reads the routed experts
+        # only
+        in_router = args.path == "layer" and S <= 2 and 32 * H * spec.wbits // 8 <= 128 * 1024
         gu_units = n_units - (spec.n_shared if in_router else 0)
         dom, dom_kernel = "gateup", "k_gateup<%d,%d%s>" % (spec.wbits, min(S, 4), ",gs64" if spec.group else "")
         n_scales = H // spec.group if spec.group else 1   # per gate / up row

@@ -148,9 +148,10 @@ int coli_moe_forward(const coli_moe_dims *dims, int32_t n_tokens, const float *x
  * topk_w.  By default it runs the multi-launch kernels of those two calls,
  * with Q8_0(x) produced once by the router-logit launch; up to 8 tokens that
  * launch also selects the routing and writes the call's unit table, and up
- * to 2 tokens (when the shared expert's 32-row gate/up tiles hold at most
- * 256 KiB of codes) it also runs the shared expert's gate/up, whose pairs do
- * not depend on the routing.  A persistent
+ * to 2 tokens (when the shared expert's 16-row gate/up half tiles hold at
+ * most 128 KiB of codes) it also runs the shared expert's gate/up, whose
+ * pairs do not depend on the routing, leaving its h in the workspace for the
+ * gate/up launch to quantise.  A persistent
  * single-launch kernel (router, gate/up and down+combine phases separated
  * by grid barriers) serves up to 8 tokens when selected with
  * coli_moe_debug_force_path.  Arguments as for coli_moe_route and

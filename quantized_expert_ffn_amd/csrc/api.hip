@@ -458,14 +458,13 @@ int coli_moe_layer(const coli_moe_dims *d, int32_t S, const float *x, const floa
             r.n_shared = d->n_shared;
             r.norm = d->norm_topk_prob;
             r.rsf = d->routed_scaling_factor;
-            r.qh = a.qh;
-            r.dh = a.dh;
+            r.hs = reinterpret_cast<float *>(w8 + L.hs);
             r.I = d->inter;
             r.bits = d->wbits;
             r.group = d->group_size;
-            // the shared expert's gate/up tiles run in the router launch when
-            // they are short enough to finish beside it (one pass over at
-            // most 256 KiB of rows per workgroup) and their LDS fits there
+            // the shared expert's gate/up half tiles run in the router launch
+            // when they are short enough to finish beside it (one pass over at
+            // most 128 KiB of rows per workgroup) and their LDS fits there
             r.sg = d->n_shared && route_shared_fits(S, d->hidden, d->wbits) ? 1 : 0;
             if (route_fused_lds(r) > 64 * 1024) r.sg = 0;
             if (route_fused_lds(r) <= 64 * 1024) {
@@ -475,6 +474,7 @@ int coli_moe_layer(const coli_moe_dims *d, int32_t S, const float *x, const floa
                 if (e != hipSuccess) return hip_fail(e, "router launch");
                 a.units = w8 + L.units;
                 a.shared_done = r.sg;
+                a.hs = r.hs;
                 return forward_launches(a, d->wbits, false, nullptr, true, w8 + L.units, st);
             }
         }

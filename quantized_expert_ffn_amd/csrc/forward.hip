@@ -49,8 +49,10 @@ __device__ __forceinline__ const uint8_t *load_unit_table(const uint8_t *units, 
 // call's unit table (coli_moe_layer): row y = 0 is the shared expert (its
 // pairs do not depend on the routing, so it needs no table) and row y > 0
 // routed unit y - 1, where y = blockIdx.y + shared_done (the router launch
-// may already have run the shared expert's tiles).  Otherwise every
-// workgroup builds the unit table from topk_idx and takes unit blockIdx.y.
+// may already have run the shared expert's gate/up: then the workgroups of
+// grid row 0 first quantise its h, one 32-row block each, to Q8_0(h) in the
+// shared expert's pair slots).  Otherwise every workgroup builds the unit
+// table from topk_idx and takes unit blockIdx.y.
 template <int BITS, int NT, bool TABLE, bool GROUPED>
 __global__ __launch_bounds__(256) void k_gateup(const FwdArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -61,6 +63,16 @@ __global__ __launch_bounds__(256) void k_gateup(const FwdArgs a) {
     const int *uoff = reinterpret_cast<const int *>(smem + L.uoff);
     const int *pairs = reinterpret_cast<const int *>(smem + L.pairs);
     const int y = (int)blockIdx.y + (TABLE ? a.shared_done : 0);
+    if (TABLE && a.shared_done && blockIdx.y == 0 && wave == 0) {
+        // half-wave t: block blockIdx.x of token t's h (S <= 2)
+        const int t = lane >> 5, i = 32 * (int)blockIdx.x + (lane & 31);
+        if (t < S) {
+            float d;
+            const int8_t q = q8_0_lane(a.hs[(size_t)t * I + i], &d);
+            a.qh[(size_t)(P + t) * I + i] = q;
+            if ((lane & 31) == 0) a.dh[(size_t)(P + t) * (I / 32) + blockIdx.x] = d;
+        }
+    }
     int u = y, e;
     const uint8_t *tblob = nullptr;
     if (TABLE && a.n_shared && y == 0) {

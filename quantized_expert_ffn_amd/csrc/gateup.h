@@ -74,4 +74,54 @@ __device__ __forceinline__ void gateup_unit(const uint8_t *blob, int H, int I, i
     }
 }
 
+// Gate/up of rows i0 .. i0+15 of one unit for the np <= NT pair slots
+// slots[0 .. np), with SwiGLU: h (binary32, not quantised) of slot v's row
+// i0 + i goes to hs[v * I + i0 + i].  Waves 0-1 stream 8 gate rows each,
+// waves 2-3 the matching up rows; otherwise as gateup_unit (the staging,
+// the block chains and the scales are the same).  Half a Q8_0 block of h:
+// whoever joins two such halves quantises them.  256 threads.
+template <int BITS, int NT, bool GROUPED, typename Stage>
+__device__ __forceinline__ void gateup_half_f32(const uint8_t *blob, int H, int I, int group, int i0,
+                                                int np, uint8_t *smem, const SmemPlan &L, size_t gs_off,
+                                                float *__restrict__ hs, Stage stage) {
+    constexpr int RPW = 8;
+    const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
+    int8_t *vq = reinterpret_cast<int8_t *>(smem + L.vq);
+    float *vd = reinterpret_cast<float *>(smem + L.vd);
+    int32_t *isum_wave = reinterpret_cast<int32_t *>(smem + L.isum) + wave * NT * RPW * ISUM_PITCH;
+    float *gu = reinterpret_cast<float *>(smem + L.gu);
+    const BlobLayout BL = blob_layout(H, I, BITS, GROUPED ? group : 0);
+    const size_t row_bytes = (size_t)H * BITS / 8;
+    const int r0 = i0 + RPW * (wave & 1);   // this wave's first row
+    const size_t mat = wave < 2 ? BL.gate : BL.up;
+    const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(blob, (uint32_t)BL.total);
+    uint32_t rowoff[RPW];
+#pragma unroll
+    for (int j = 0; j < RPW; ++j) rowoff[j] = (uint32_t)(mat + (size_t)(r0 + j) * row_bytes);
+    const size_t ssec = wave < 2 ? BL.s_gate : BL.s_up;
+    const float *scale = reinterpret_cast<const float *>(blob + ssec);
+    RowGroups G;
+    G.lgb = GROUPED ? group_lgb(group) : -1;
+    if (GROUPED) {
+        G.rsrc = rsrc;
+        G.row_stride = (uint32_t)(4 * (H / group));
+        G.base = (uint32_t)(ssec + (size_t)r0 * G.row_stride);
+        G.lds = reinterpret_cast<float *>(smem + gs_off) + wave * RPW * (64 >> G.lgb);
+    }
+    const int nb = H / 32;
+    const int crow = lane % RPW, cvec = lane / RPW;
+    const int ng = np;
+    BlockBits<BITS> cur[RPW];
+    prime_rows<BITS, RPW>(rsrc, rowoff, nb, cur);
+    const float acc = stream_rows<BITS, NT, RPW, GROUPED>(rsrc, rowoff, nb, ng, vq, vd, isum_wave, H,
+                                                         [&]() { stage(0, ng); }, cur, G);
+    // gu[v * 32 + k]: gate rows (k < 16) then up rows of vector v
+    if (cvec < ng) gu[cvec * 32 + wave * RPW + crow] = GROUPED ? acc : acc * scale[r0 + crow];
+    __syncthreads();
+    if (tid < ng * 16) {
+        const int v = tid >> 4, i = tid & 15;
+        hs[(size_t)v * I + i0 + i] = swiglu_f32(gu[v * 32 + i], gu[v * 32 + 16 + i]);
+    }
+}
+
 }  // namespace coli

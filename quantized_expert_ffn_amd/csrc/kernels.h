@@ -12,7 +12,7 @@ namespace coli {
 // Workspace carve-up for a call with S tokens.  The status word sits at a
 // fixed offset (it persists between calls); the rest is per call.
 struct WsLayout {
-    size_t status, flags, logits, units, tiles, qx, dx, qh, dh, Y, total;
+    size_t status, flags, logits, units, tiles, qx, dx, qh, dh, Y, hs, total;
 };
 
 // Tiles of the batch-union kernels for large batches: up to PF_TOK pairs of
@@ -77,7 +77,8 @@ inline WsLayout ws_layout(int H, int I, int E, int K, int S) {
     L.qh = al256h(L.dx + 4 * (size_t)S * (size_t)(H / 32));
     L.dh = al256h(L.qh + slots * (size_t)I);
     L.Y = al256h(L.dh + 4 * slots * (size_t)(I / 32));
-    L.total = al256h(L.Y + 4 * slots * (size_t)H);
+    L.hs = al256h(L.Y + 4 * slots * (size_t)H);
+    L.total = al256h(L.hs + 4 * (size_t)(S < 2 ? S : 2) * (size_t)I);
     return L;
 }
 
@@ -99,7 +100,8 @@ struct FwdArgs {
     uint32_t *status;
     int S, H, I, E, K, n_shared;
     int pend_mode;                 // 0: all units, 1: skip pending experts, 2: only pending
-    int shared_done;               // 1: the router launch wrote the shared expert's Q8_0(h)
+    int shared_done;               // 1: the router launch wrote the shared expert's h to hs
+    const float *hs;               // [S, I]  the shared expert's h, binary32 (with shared_done)
     int group;                     // 0: per-row scales; else one scale per `group` codes of a row
     uint32_t pend[32];             // bit e: expert e pending
 };
@@ -119,8 +121,7 @@ struct RouteArgs {
     const uint8_t *shared;
     uint8_t *units;
     uint32_t *sync;
-    int8_t *qh;                    // with sg: the shared expert's Q8_0(h), slots S*K + t
-    float *dh;
+    float *hs;                     // with sg: the shared expert's h [S, I], binary32
     int S, H, E, K, n_shared, norm;
     int I, bits, group;            // expert shape, code width and scale group (for sg)
     int sg;                        // 1: the launch also runs the shared expert's gate/up tiles
@@ -128,10 +129,11 @@ struct RouteArgs {
 };
 hipError_t launch_route_fused(const RouteArgs &r, hipStream_t st);
 size_t route_fused_lds(const RouteArgs &r);
-// Shared-expert tiles in the router launch: up to two tokens (one pass of
-// the tile's 64 rows) and at most 256 KiB of those rows per workgroup.
+// Shared-expert half tiles in the router launch: up to two tokens (one pass
+// over the half tile's 32 rows) and at most 128 KiB of those rows per
+// workgroup.
 inline bool route_shared_fits(int S, int H, int bits) {
-    return S <= 2 && (size_t)64 * H * bits / 8 <= 256 * 1024;
+    return S <= 2 && (size_t)32 * H * bits / 8 <= 128 * 1024;
 }
 
 // Router logits; with qx non-null the same launch writes Q8_0(x) to qx / dx.

@@ -67,34 +67,35 @@ __global__ __launch_bounds__(64) void k_router_select(const float *__restrict__ 
     if (!ok && lane == 0) raise_status(status, ST_NONFINITE);
 }
 
-// The fused router launch.  Grid (ceil(E / RF_W) [+ ceil(ceil(H / 2048) /
-// RF_W) with qx], S), RF_W wavefronts per workgroup.  Wave w of workgroup
-// (x < ceil(E / RF_W), t) computes logit (t, RF_W x + w) and publishes it
-// with a device-scope store; once all of its waves have drained their
-// stores, the workgroup counts itself in the token's arrival counter (one
-// atomic per workgroup).  In the workgroup that arrives last, wave 0 selects
-// the token's top-K from the published logits (device-scope loads); for one
-// token it writes the unit table straight from the selection, otherwise the
-// token counts itself done and the last token's workgroup builds the unit
-// table of the batch in LDS.  Each counter is reset by its last arriver, so
-// the next launch starts from zero.  Workgroups past the logits quantise x
-// (one 2048-element slice per wave).
+// The fused router launch.  Grid (ceil(E / L) [+ ceil(ceil(H / 2048) / RF_W)
+// with qx], S), RF_W wavefronts per workgroup, L = rf_lpw(S) logits per
+// workgroup.  Wave w < L of workgroup (x < ceil(E / L), t) computes logit
+// (t, L x + w) and publishes it with a device-scope store; once all of its
+// waves have drained their stores, the workgroup counts itself in the
+// token's arrival counter (one atomic per workgroup).  In the workgroup that
+// arrives last, wave 0 selects the token's top-K from the published logits
+// (device-scope loads); for one token it writes the unit table straight from
+// the selection, otherwise the token counts itself done and the last token's
+// workgroup builds the unit table of the batch in LDS.  Each counter is reset
+// by its last arriver, so the next launch starts from zero.  Workgroups past
+// the logits quantise x (one 2048-element slice per wave).
 //
-// With sg, the first I / 32 workgroups of grid row 0 (ahead of the logits,
-// being the longest) run the shared expert's gate/up tiles for all S tokens
-// — its pairs do not depend on the routing — quantising x into their own
-// LDS with the same Q8_0 as the workspace copy; the gate/up launch then
-// skips the shared expert.
+// For one token the launch spreads its reads over more compute units (two
+// logits per workgroup of four waves).  With sg, the first I / 16
+// workgroups of grid row 0 (ahead of the logits, being the longest) run the
+// shared expert's gate/up for all S tokens in half tiles of 16 rows — its
+// pairs do not depend on the routing — quantising x into their own LDS with
+// the same Q8_0 as the workspace copy, and write h unquantised to hs; the
+// gate/up launch quantises it and skips the shared expert.
 constexpr int RF_W = 4;
+// logits per workgroup: two for one token, four (one per wave) for more
+__host__ __device__ inline int rf_lpw(int S) { return S == 1 ? 2 : RF_W; }
 
-// Shared expert, gate/up rows 32 tile .. 32 tile + 31, every token.
+// Shared expert, gate/up rows 16 half .. 16 half + 15, every token; h to hs.
 template <int BITS, int NT, bool GROUPED>
-__device__ __forceinline__ void shared_gateup_tile(const RouteArgs &r, uint8_t *smem, int tile) {
-    const int tid = threadIdx.x, S = r.S, H = r.H, P = S * r.K;
+__device__ __forceinline__ void shared_gateup_half(const RouteArgs &r, uint8_t *smem, int half) {
+    const int tid = threadIdx.x, S = r.S, H = r.H;
     const SmemPlan L = smem_plan(S, r.K, r.E, NT, H);
-    int *slots = reinterpret_cast<int *>(smem + L.pairs);
-    for (int t = tid; t < S; t += blockDim.x) slots[t] = P + t;
-    __syncthreads();
     const int nb = H / 32, vds = vd_stride(nb);
     auto stage = [&](int g0, int ng) {
         int8_t *vq = reinterpret_cast<int8_t *>(smem + L.vq);
@@ -106,8 +107,8 @@ __device__ __forceinline__ void shared_gateup_tile(const RouteArgs &r, uint8_t *
         }
         __syncthreads();
     };
-    gateup_unit<BITS, NT, GROUPED>(uniform_ptr(r.shared), H, r.I, r.group, 32 * tile, slots, S, smem, L, L.total,
-                                   r.qh, r.dh, stage);
+    gateup_half_f32<BITS, NT, GROUPED>(uniform_ptr(r.shared), H, r.I, r.group, 16 * half, S, smem, L, L.total, r.hs,
+                                       stage);
 }
 
 template <int MAXJ, int BITS, int NT, bool GROUPED>
@@ -116,19 +117,32 @@ __global__ __launch_bounds__(64 * RF_W) void k_route_fused(const RouteArgs r) {
     __shared__ int s_last;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, t = blockIdx.y;
     const int E = r.E, K = r.K, S = r.S, H = r.H;
-    const int n_sg = r.sg ? r.I / 32 : 0;
+    const int n_sg = r.sg ? r.I / 16 : 0;
     if ((int)blockIdx.x < n_sg) {
-        if (t == 0) shared_gateup_tile<BITS, NT, GROUPED>(r, smem, blockIdx.x);
+        if (t == 0) shared_gateup_half<BITS, NT, GROUPED>(r, smem, blockIdx.x);
         return;
     }
     const int bx = (int)blockIdx.x - n_sg;
-    const int n_lw = (E + RF_W - 1) / RF_W;
+    const int lpw = rf_lpw(S), n_lw = (E + lpw - 1) / lpw;
     if (bx >= n_lw) {
         quant_x_wave(r.x, r.qx, r.dx, r.status, H, t, (bx - n_lw) * RF_W + wave);
         return;
     }
-    const int e = bx * RF_W + wave;
-    if (e < E) {
+    // wave 0 fetches what the selection needs besides the logits (the bias
+    // and the first 256 blob pointers, for the unit table) now, so that the
+    // workgroup arriving last waits only for the logits
+    float bpre[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    const uint8_t *bl[4] = {nullptr, nullptr, nullptr, nullptr};
+    if (wave == 0) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int ee = min(lane + 64 * m, E - 1);
+            if (r.bias) bpre[m] = r.bias[ee];
+            bl[m] = r.blobs[ee];
+        }
+    }
+    const int e = bx * lpw + wave;
+    if (wave < lpw && e < E) {
         bool ok;
         const float p = logit_wave<MAXJ>(r.x + (size_t)t * H, r.W + (size_t)e * H, H, &ok);
         if (!ok) raise_status(r.status, ST_NONFINITE);
@@ -144,21 +158,18 @@ __global__ __launch_bounds__(64 * RF_W) void k_route_fused(const RouteArgs r) {
     __syncthreads();
     if (!s_last) return;
 
-    // last workgroup of token t: wave 0 selects (the blob pointers of the
-    // first 256 experts are fetched meanwhile, for the unit table)
+    // last workgroup of token t: wave 0 selects
     const int P = S * K;
     const SmemPlan T = smem_plan(S, K, E, 0, 0);
     int32_t *idx_l = reinterpret_cast<int32_t *>(smem + T.total);
     const uint8_t **btab = reinterpret_cast<const uint8_t **>(smem + a16(T.total + 4 * (size_t)P));
-    const uint8_t *bl[4];
     int32_t si = 0;
     float sw = 0.0f;
     if (wave == 0) {
-#pragma unroll
-        for (int m = 0; m < 4; ++m) bl[m] = r.blobs[min(lane + 64 * m, E - 1)];
         const float *lg = r.logits + (size_t)t * E;
         auto ld = [&](int q) { return ld_dev(lg + q); };
-        const bool sok = E <= 256 ? select_wave<4>(ld, r.bias, E, K, r.rsf, r.norm, &si, &sw)
+        const bool sok = E <= 256 ? select_wave_b<4>(ld, [&](int m, int) { return bpre[m]; }, E, K, r.rsf, r.norm,
+                                                     &si, &sw)
                                   : select_wave<16>(ld, r.bias, E, K, r.rsf, r.norm, &si, &sw);
         if (!sok && lane == 0) raise_status(r.status, ST_NONFINITE);
     }
@@ -283,8 +294,8 @@ static hipError_t route_fused_maxj(const RouteArgs &r, dim3 grid, size_t smem, h
 }
 
 hipError_t launch_route_fused(const RouteArgs &r, hipStream_t st) {
-    const int n_lw = (r.E + RF_W - 1) / RF_W, n_q = ((r.H / 32 + 63) / 64 + RF_W - 1) / RF_W;
-    const int n_sg = r.sg ? r.I / 32 : 0;
+    const int lpw = rf_lpw(r.S), n_lw = (r.E + lpw - 1) / lpw, n_q = ((r.H / 32 + 63) / 64 + RF_W - 1) / RF_W;
+    const int n_sg = r.sg ? r.I / 16 : 0;
     const dim3 grid(n_sg + n_lw + (r.qx ? n_q : 0), r.S);
     const size_t smem = route_fused_lds(r);
     if (r.H <= 24 * 256) return route_fused_maxj<24>(r, grid, smem, st);

@@ -86,11 +86,11 @@ __device__ __forceinline__ int wave_min_i32(int v) {
 // it (a ballot settles the usual single-holder case; exact ties take a
 // minimum reduction).  Gate weights: (sig_k / ((sig_0 + sig_1) + ...)) * rsf,
 // or sig_k * rsf without renormalisation.  Lane k < K receives the k-th pick
-// in *idx / *w.  load_logit(e) returns the token's logit e.  E <= 64 * MAXM,
-// K <= 32.  Returns false on a non-finite input or zero weights.
-template <int MAXM, typename LoadLogit>
-__device__ __forceinline__ bool select_wave(LoadLogit load_logit, const float *__restrict__ bias,
-                                            int E, int K, float rsf, int norm, int32_t *idx, float *w) {
+// in *idx / *w.  load_logit(e) returns the token's logit e, load_bias(m, e)
+// the bias of expert e = lane + 64 m.  E <= 64 * MAXM, K <= 32.  Returns false on a non-finite input or zero weights.
+template <int MAXM, typename LoadLogit, typename LoadBias>
+__device__ __forceinline__ bool select_wave_b(LoadLogit load_logit, LoadBias load_bias, int E, int K, float rsf,
+                                              int norm, int32_t *idx, float *w) {
     const int lane = threadIdx.x & 63;
     const int mcount = (E + 63) / 64;
     float score[MAXM], sig[MAXM], lv[MAXM], bv[MAXM];
@@ -102,7 +102,7 @@ __device__ __forceinline__ bool select_wave(LoadLogit load_logit, const float *_
         const int e = min(lane + 64 * m, E - 1);
         if (m < mcount) {
             lv[m] = load_logit(e);
-            bv[m] = bias ? bias[e] : 0.0f;
+            bv[m] = load_bias(m, e);
         }
     }
 #pragma unroll
@@ -155,6 +155,14 @@ __device__ __forceinline__ bool select_wave(LoadLogit load_logit, const float *_
     *idx = my_idx;
     *w = norm ? (my_sig / denom) * rsf : my_sig * rsf;
     return __builtin_amdgcn_readfirstlane((int)(ok && wok)) != 0;
+}
+
+// select_wave_b with the bias read from memory (null: no bias).
+template <int MAXM, typename LoadLogit>
+__device__ __forceinline__ bool select_wave(LoadLogit load_logit, const float *__restrict__ bias, int E, int K,
+                                            float rsf, int norm, int32_t *idx, float *w) {
+    return select_wave_b<MAXM>(load_logit, [&](int, int e) { return bias ? bias[e] : 0.0f; }, E, K, rsf, norm, idx,
+                               w);
 }
 
 }  // namespace coli
