@@ -23,7 +23,6 @@ __device__ __forceinline__ float logit_wave(const float *__restrict__ xrow,
     const f32x4 *wr = reinterpret_cast<const f32x4 *>(wrow);
     const int steps = H / 256;
     float p = 0.0f;
-    bool good = true;
     for (int j0 = 0; j0 < steps; j0 += MAXJ) {
         f32x4 xv[MAXJ], wv[MAXJ];
 #pragma unroll
@@ -39,15 +38,15 @@ __device__ __forceinline__ float logit_wave(const float *__restrict__ xrow,
                 p = __builtin_fmaf(xv[jj].y, wv[jj].y, p);
                 p = __builtin_fmaf(xv[jj].z, wv[jj].z, p);
                 p = __builtin_fmaf(xv[jj].w, wv[jj].w, p);
-                good = good && finite_f32(xv[jj].x) && finite_f32(xv[jj].y) &&
-                       finite_f32(xv[jj].z) && finite_f32(xv[jj].w) && finite_f32(wv[jj].x) &&
-                       finite_f32(wv[jj].y) && finite_f32(wv[jj].z) && finite_f32(wv[jj].w);
             }
         }
     }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) p = p + __shfl_xor(p, o, 64);
-    *ok = good && finite_f32(p);
+    // a non-finite x or W_r element makes the logit non-finite (an infinity
+    // times zero or an opposite infinity gives NaN; NaN and infinities
+    // survive the chain and the sums), so this checks the inputs too
+    *ok = finite_f32(p);
     return p;
 }
 
