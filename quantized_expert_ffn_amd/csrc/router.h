@@ -57,15 +57,32 @@ __device__ __forceinline__ int dpp(int v) {
     return __builtin_amdgcn_update_dpp(v, v, CTRL, ROWS, 0xF, false);
 }
 
+// Order-preserving map of non-NaN binary32 values to uint32 (sign-magnitude
+// to offset binary; -0 sorts just below +0), and its inverse.
+__device__ __forceinline__ uint32_t f32_key(float f) {
+    const uint32_t b = __float_as_uint(f);
+    return b ^ ((uint32_t)((int32_t)b >> 31) | 0x80000000u);
+}
+__device__ __forceinline__ float key_f32(uint32_t k) { return __uint_as_float(k ^ ((k >> 31) ? 0x80000000u : ~0u)); }
+
+// DPP move whose disabled or out-of-row source lanes read 0 (the identity of
+// an unsigned maximum), so that the compiler folds it into the v_max_u32.
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ uint32_t dpp_u0(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWS, 0xF, true);
+}
+
+// Wavefront maximum of non-NaN values: one of the lanes' values (bit for bit),
+// through the unsigned maximum of their keys.
 __device__ __forceinline__ float wave_max_f32(float v) {
-    int i = __float_as_int(v);
-    i = __float_as_int(__builtin_fmaxf(__int_as_float(i), __int_as_float(dpp<0xB1>(i))));  // quad [1,0,3,2]
-    i = __float_as_int(__builtin_fmaxf(__int_as_float(i), __int_as_float(dpp<0x4E>(i))));  // quad [2,3,0,1]
-    i = __float_as_int(__builtin_fmaxf(__int_as_float(i), __int_as_float(dpp<0x141>(i)))); // row half mirror
-    i = __float_as_int(__builtin_fmaxf(__int_as_float(i), __int_as_float(dpp<0x140>(i)))); // row mirror
-    i = __float_as_int(__builtin_fmaxf(__int_as_float(i), __int_as_float(dpp<0x142, 0xA>(i))));  // row bcast 15
-    i = __float_as_int(__builtin_fmaxf(__int_as_float(i), __int_as_float(dpp<0x143, 0xC>(i))));  // row bcast 31
-    return __int_as_float(__builtin_amdgcn_readlane(i, 63));
+    uint32_t k = f32_key(v);
+    k = max(k, dpp_u0<0xB1>(k));        // quad [1,0,3,2]
+    k = max(k, dpp_u0<0x4E>(k));        // quad [2,3,0,1]
+    k = max(k, dpp_u0<0x141>(k));       // row half mirror
+    k = max(k, dpp_u0<0x140>(k));       // row mirror
+    k = max(k, dpp_u0<0x142, 0xA>(k));  // row bcast 15
+    k = max(k, dpp_u0<0x143, 0xC>(k));  // row bcast 31
+    return key_f32(__builtin_amdgcn_readlane(k, 63));
 }
 
 __device__ __forceinline__ int wave_min_i32(int v) {
