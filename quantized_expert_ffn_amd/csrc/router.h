@@ -58,12 +58,11 @@ __device__ __forceinline__ int dpp(int v) {
 }
 
 // Order-preserving map of non-NaN binary32 values to uint32 (sign-magnitude
-// to offset binary; -0 sorts just below +0), and its inverse.
+// to offset binary; -0 sorts just below +0).
 __device__ __forceinline__ uint32_t f32_key(float f) {
     const uint32_t b = __float_as_uint(f);
     return b ^ ((uint32_t)((int32_t)b >> 31) | 0x80000000u);
 }
-__device__ __forceinline__ float key_f32(uint32_t k) { return __uint_as_float(k ^ ((k >> 31) ? 0x80000000u : ~0u)); }
 
 // DPP move whose disabled or out-of-row source lanes read 0 (the identity of
 // an unsigned maximum), so that the compiler folds it into the v_max_u32.
@@ -72,17 +71,15 @@ __device__ __forceinline__ uint32_t dpp_u0(uint32_t v) {
     return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWS, 0xF, true);
 }
 
-// Wavefront maximum of non-NaN values: one of the lanes' values (bit for bit),
-// through the unsigned maximum of their keys.
-__device__ __forceinline__ float wave_max_f32(float v) {
-    uint32_t k = f32_key(v);
+// Wavefront maximum (uniform): each DPP step folds into one v_max_u32.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t k) {
     k = max(k, dpp_u0<0xB1>(k));        // quad [1,0,3,2]
     k = max(k, dpp_u0<0x4E>(k));        // quad [2,3,0,1]
     k = max(k, dpp_u0<0x141>(k));       // row half mirror
     k = max(k, dpp_u0<0x140>(k));       // row mirror
     k = max(k, dpp_u0<0x142, 0xA>(k));  // row bcast 15
     k = max(k, dpp_u0<0x143, 0xC>(k));  // row bcast 31
-    return key_f32(__builtin_amdgcn_readlane(k, 63));
+    return __builtin_amdgcn_readlane(k, 63);
 }
 
 __device__ __forceinline__ int wave_min_i32(int v) {
@@ -110,7 +107,6 @@ __device__ __forceinline__ bool select_wave_b(LoadLogit load_logit, LoadBias loa
     const int lane = threadIdx.x & 63;
     const int mcount = (E + 63) / 64;
     float score[MAXM], sig[MAXM], lv[MAXM], bv[MAXM];
-    uint32_t taken = 0;
     bool ok = true;
     // all loads first (in flight together), then the arithmetic
 #pragma unroll
@@ -132,29 +128,42 @@ __device__ __forceinline__ bool select_wave_b(LoadLogit load_logit, LoadBias loa
             score[m] = sig[m] + bv[m];
         }
     }
+    // The rounds compare order-preserving keys of the scores (f32_key): a
+    // candidate's key is 0 once taken, or when it is missing or its score is
+    // not above -inf (NaN included), so it never wins a round, as a score
+    // that is not above the running best never does.  Scores are never -0
+    // (sig >= +0), so key order is score order.
+    uint32_t key[MAXM];
+#pragma unroll
+    for (int m = 0; m < MAXM; ++m) key[m] = score[m] > -__builtin_inff() ? f32_key(score[m]) : 0u;
     int32_t my_idx = 0;
     float my_sig = 0.0f;
     for (int k = 0; k < K; ++k) {
-        float bs = -__builtin_inff(), bsig = 0.0f;
+        uint32_t bk = 0;
+        float bsig = 0.0f;
         int be = 0x7fffffff;
 #pragma unroll
         for (int m = 0; m < MAXM; ++m) {
-            if (m < mcount && !((taken >> m) & 1u) && score[m] > bs) {
-                bs = score[m];
+            if (key[m] > bk) {
+                bk = key[m];
                 bsig = sig[m];
                 be = lane + 64 * m;
             }
         }
-        const float M = wave_max_f32(bs);
-        const uint64_t hit = __builtin_amdgcn_ballot_w64(bs == M);
+        const uint32_t M = wave_max_u32(bk);
+        const uint64_t hit = __builtin_amdgcn_ballot_w64(bk == M);
         int sel;
         if (__builtin_popcountll(hit) == 1)
             sel = __builtin_amdgcn_readlane(be, (int)__builtin_ctzll(hit));
         else
-            sel = wave_min_i32(bs == M ? be : 0x7fffffff);
+            sel = wave_min_i32(bk == M ? be : 0x7fffffff);
         if (sel >= E) sel = k;  // only reachable with NaN scores, flagged below
         const float s = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bsig), sel & 63));
-        if ((sel & 63) == lane) taken |= 1u << (sel >> 6);
+        if ((sel & 63) == lane) {
+#pragma unroll
+            for (int m = 0; m < MAXM; ++m)
+                if (m == (sel >> 6)) key[m] = 0u;
+        }
         if (lane == k) {
             my_idx = sel;
             my_sig = s;
