@@ -30,7 +30,9 @@
  *    coli_moe_status() reads and clears them.  When the status is non-zero
  *    the outputs of the calls since the last read are unspecified.
  *  - There is no CPU fallback: without a usable gfx950 device every compute
- *    call fails with COLI_EHIP.
+ *    call fails with COLI_EHIP (colibrì README v1.0, "Experimental resident
+ *    CUDA backend": a requested GPU backend that cannot run fails at startup
+ *    instead of silently falling back to the CPU).
  *  - Hidden states, router gate, outputs and expert blobs are accessed with
  *    16-byte vector loads and stores: x, router_w, out and shared_blob must
  *    be 16-byte aligned (COLI_EINVAL otherwise), and so must every pointer of
@@ -88,9 +90,16 @@ typedef struct coli_moe_dims {
  */
 size_t coli_moe_expert_bytes(const coli_moe_dims *dims);
 
-/* Workspace bytes needed for calls with up to max_tokens tokens.  The
- * workspace must be zero-filled once before its first use (the status word
- * lives in it); afterwards the library keeps it consistent. 0 if invalid. */
+/* Workspace bytes needed for calls with up to max_tokens tokens.  The pages
+ * define no scratch memory: the workspace is this library's way of keeping
+ * every device allocation with the caller (colibrì README v1.0,
+ * "Experimental resident CUDA backend": resident tensors are uploaded once
+ * and reused, and the runtime keeps a fixed per-device reserve).  It holds
+ * the status word, the router's logits, the call's unit table, Q8_0(x),
+ * Q8_0(h) and the per-pair expert outputs.  It must be zero-filled once
+ * before its first use (the status word lives in it); afterwards the
+ * library keeps it consistent.  Returns 0 if dims are invalid or
+ * max_tokens < 0. */
 size_t coli_moe_workspace_bytes(const coli_moe_dims *dims, int32_t max_tokens);
 
 /*
@@ -175,10 +184,20 @@ int coli_moe_stage_experts(int32_t n, const void *const *host_src, void *const *
                            size_t bytes_each, void *copy_stream, void *done_event);
 
 /* Synchronises `stream`, returns the status recorded in the workspace since
- * the last read (0 or the most severe COLI_E* code) and clears it. */
+ * the last read (0 or the most severe COLI_E* code) and clears it.  This is
+ * how conditions only the kernels see reach the caller: non-finite input is
+ * rejected ("Colibri (colibrì): GLM-5.2 local inference on 25 GB of RAM",
+ * "How it works (validated core mechanics)": the router's self-test refuses
+ * NaN), and a failure is reported, never hidden behind a fallback (colibrì
+ * README v1.0, "Experimental resident CUDA backend").  COLI_EINVAL when ws
+ * is NULL, COLI_EHIP when the synchronisation or the read fails. */
 int coli_moe_status(void *ws, void *stream);
 
-/* Message of the last failure on the calling thread ("" if none). */
+/* Message of the last failure on the calling thread ("" if none): the text
+ * behind a non-zero return, so that a refused call says why (colibrì README
+ * v1.0, "Experimental resident CUDA backend": failures are reported rather
+ * than silently worked around).  The pointer stays valid until the thread's
+ * next failing call. */
 const char *coli_moe_last_error(void);
 
 /*

@@ -4,10 +4,14 @@ TEST INFRASTRUCTURE.  Only the test suite, the smoke check and the
 benchmark's CPU-baseline leg may import this package.  The product path never
 imports it, and it shares no code with the HIP library.
 
-Functions take and return numpy arrays; every call is a plain single-threaded
-C loop over the definitions in moe_oracle.c.  Errors come back as
-OracleError carrying the C return code (-1 invalid argument, -2 non-finite
-input, -4 expert not resident).
+Functions take and return numpy arrays; every call is a plain C loop over
+the definitions in moe_oracle.c.  Two builds of that one source exist:
+liboracle.so (single-threaded) and liboracle_omp.so (OpenMP: the loops over
+independent tokens of route / forward run on several threads; each token's
+arithmetic is the same sequential code, so the bits are the same).  The
+layer-level calls take parallel=True to use the second build.  Errors come
+back as OracleError carrying the C return code (-1 invalid argument, -2
+non-finite input, -4 expert not resident).
 """
 from __future__ import annotations
 
@@ -19,9 +23,12 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "_build", "liboracle.so")
+OMP_LIB_PATH = os.path.join(_HERE, "_build", "liboracle_omp.so")
 # a test may point the wrapper at another build of the same source
 LIB_OVERRIDE = os.environ.get("ORACLE_LIB_OVERRIDE")
 CFLAGS = ["-std=c11", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared", "-Wall"]
+# the multi-threaded build: the same flags plus OpenMP (the token loops)
+OMP_CFLAGS = CFLAGS + ["-fopenmp"]
 
 EINVAL, ENONFINITE, ENOTRESIDENT = -1, -2, -4
 
@@ -32,54 +39,78 @@ class OracleError(RuntimeError):
         self.rc = rc
 
 
+def _compile(path: str, flags, force: bool) -> str:
+    if force or not os.path.exists(path):
+        os.makedirs(os.path.dirname(path), exist_ok=True)
+        tmp = path + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", *flags, os.path.join(_HERE, "moe_oracle.c"), "-lm", "-o", tmp])
+        os.replace(tmp, path)
+    return path
+
+
 def build(force: bool = False) -> str:
-    """Compiles moe_oracle.c into oracle/_build/liboracle.so."""
-    if force or not os.path.exists(LIB_PATH):
-        os.makedirs(os.path.dirname(LIB_PATH), exist_ok=True)
-        tmp = LIB_PATH + ".tmp%d" % os.getpid()
-        subprocess.check_call(["gcc", *CFLAGS, os.path.join(_HERE, "moe_oracle.c"), "-lm", "-o", tmp])
-        os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    """Compiles moe_oracle.c into oracle/_build/liboracle.so and, with
+    OpenMP, liboracle_omp.so; returns the first."""
+    _compile(OMP_LIB_PATH, OMP_CFLAGS, force)
+    return _compile(LIB_PATH, CFLAGS, force)
 
 
 _lib = None
+_omp_lib = None
 P = ctypes.c_void_p
 I32 = ctypes.c_int
 F32 = ctypes.c_float
 
 
-def lib():
-    global _lib
+def lib(parallel: bool = False):
+    """The single-threaded build, or with parallel the OpenMP build."""
+    global _lib, _omp_lib
+    if parallel:
+        if _omp_lib is None:
+            build()
+            _omp_lib = _bind(ctypes.CDLL(OMP_LIB_PATH))
+        return _omp_lib
     if _lib is None:
-        L = ctypes.CDLL(LIB_OVERRIDE or build())
-        sig = {
-            "oq_expf": (F32, [F32]),
-            "oq_sigmoid": (F32, [F32]),
-            "oq_swiglu": (F32, [F32, F32]),
-            "oq_expf_n": (None, [P, P, ctypes.c_uint64]),
-            "oq_sigmoid_n": (None, [P, P, ctypes.c_uint64]),
-            "oq_swiglu_n": (None, [P, P, P, ctypes.c_uint64]),
-            "oq_q8_0": (None, [P, I32, P, P]),
-            "oq_unpack": (None, [P, I32, I32, P]),
-            "oq_blob_layout": (None, [I32, I32, I32, P]),
-            "oq_block_isum": (ctypes.c_int32, [P, P]),
-            "oq_row_dot": (F32, [P, P, P, I32, F32]),
-            "oq_router_logit": (F32, [P, P, I32]),
-            "oq_select": (I32, [P, P, I32, I32, F32, I32, P, P, P]),
-            "oq_expert": (I32, [P, I32, I32, I32, P, P, P, P, P, P, P, P]),
-            "oq_moe_route": (I32, [I32, I32, I32, F32, I32, I32, P, P, P, P, P, P, P]),
-            "oq_moe_forward": (I32, [I32, I32, I32, I32, I32, I32, I32, P, P, P, P, P, P]),
-            "oq_blob_layout_g": (None, [I32, I32, I32, I32, P]),
-            "oq_row_dot_g": (F32, [P, P, P, I32, P, I32]),
-            "oq_expert_g": (I32, [P, I32, I32, I32, I32, P, P, P, P, P, P, P, P]),
-            "oq_moe_forward_g": (I32, [I32, I32, I32, I32, I32, I32, I32, I32, P, P, P, P, P, P]),
-        }
-        for name, (res, args) in sig.items():
-            f = getattr(L, name)
-            f.restype = res
-            f.argtypes = args
-        _lib = L
+        _lib = _bind(ctypes.CDLL(LIB_OVERRIDE or build()))
     return _lib
+
+
+def threads(n: int = 0) -> int:
+    """Threads of the OpenMP build's token loops: n > 0 sets them; returns
+    the count in use."""
+    return int(lib(True).oq_threads(int(n)))
+
+
+def _bind(L):
+    """Declares the C signatures on a loaded build."""
+    sig = {
+        "oq_expf": (F32, [F32]),
+        "oq_sigmoid": (F32, [F32]),
+        "oq_swiglu": (F32, [F32, F32]),
+        "oq_expf_n": (None, [P, P, ctypes.c_uint64]),
+        "oq_sigmoid_n": (None, [P, P, ctypes.c_uint64]),
+        "oq_swiglu_n": (None, [P, P, P, ctypes.c_uint64]),
+        "oq_q8_0": (None, [P, I32, P, P]),
+        "oq_unpack": (None, [P, I32, I32, P]),
+        "oq_blob_layout": (None, [I32, I32, I32, P]),
+        "oq_block_isum": (ctypes.c_int32, [P, P]),
+        "oq_row_dot": (F32, [P, P, P, I32, F32]),
+        "oq_router_logit": (F32, [P, P, I32]),
+        "oq_select": (I32, [P, P, I32, I32, F32, I32, P, P, P]),
+        "oq_expert": (I32, [P, I32, I32, I32, P, P, P, P, P, P, P, P]),
+        "oq_moe_route": (I32, [I32, I32, I32, F32, I32, I32, P, P, P, P, P, P, P]),
+        "oq_moe_forward": (I32, [I32, I32, I32, I32, I32, I32, I32, P, P, P, P, P, P]),
+        "oq_blob_layout_g": (None, [I32, I32, I32, I32, P]),
+        "oq_row_dot_g": (F32, [P, P, P, I32, P, I32]),
+        "oq_expert_g": (I32, [P, I32, I32, I32, I32, P, P, P, P, P, P, P, P]),
+        "oq_moe_forward_g": (I32, [I32, I32, I32, I32, I32, I32, I32, I32, P, P, P, P, P, P]),
+        "oq_threads": (I32, [I32]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(L, name)
+        f.restype = res
+        f.argtypes = args
+    return L
 
 
 def _p(a):
@@ -202,7 +233,7 @@ def expert(blob, H: int, I: int, bits: int, qx, dx, group: int = 0) -> dict:
 
 
 # ---------------------------------------------------------------- layer
-def route(spec, x, router_w, bias):
+def route(spec, x, router_w, bias, parallel: bool = False):
     """Routing of x [S,H]: (idx [S,K] int32, w [S,K] f32, logits [S,E], sig [S,E])."""
     x = _c(x, np.float32)
     S = x.shape[0]
@@ -213,14 +244,14 @@ def route(spec, x, router_w, bias):
     w = np.empty((S, K), np.float32)
     logits = np.empty((S, E), np.float32)
     sig = np.empty((S, E), np.float32)
-    rc = lib().oq_moe_route(spec.hidden, E, K, float(spec.routed_scaling_factor),
+    rc = lib(parallel).oq_moe_route(spec.hidden, E, K, float(spec.routed_scaling_factor),
                             int(spec.norm_topk_prob), S, _p(x), _p(router_w), _p(bias),
                             _p(idx), _p(w), _p(logits), _p(sig))
     _check(rc, "route")
     return idx, w, logits, sig
 
 
-def forward(spec, x, idx, w, blobs, shared_blob):
+def forward(spec, x, idx, w, blobs, shared_blob, parallel: bool = False):
     """Expert FFNs + combine for x [S,H] with given routing; blobs[e] may be None."""
     x = _c(x, np.float32)
     S = x.shape[0]
@@ -230,14 +261,14 @@ def forward(spec, x, idx, w, blobs, shared_blob):
     ptrs = (ctypes.c_void_p * spec.n_experts)(*[None if b is None else b.ctypes.data for b in keep])
     sh = None if shared_blob is None else _c(shared_blob, np.uint8)
     out = np.empty((S, spec.hidden), np.float32)
-    rc = lib().oq_moe_forward_g(spec.hidden, spec.inter, spec.n_experts, spec.top_k, spec.n_shared,
+    rc = lib(parallel).oq_moe_forward_g(spec.hidden, spec.inter, spec.n_experts, spec.top_k, spec.n_shared,
                                 spec.wbits, int(getattr(spec, "group", 0)), S, _p(x), _p(idx), _p(w), ptrs,
                                 _p(sh), _p(out))
     _check(rc, "forward")
     return out
 
 
-def layer(spec, x, router_w, bias, blobs, shared_blob):
+def layer(spec, x, router_w, bias, blobs, shared_blob, parallel: bool = False):
     """Whole layer: returns (out [S,H], idx [S,K], w [S,K])."""
-    idx, w, _, _ = route(spec, x, router_w, bias)
-    return forward(spec, x, idx, w, blobs, shared_blob), idx, w
+    idx, w, _, _ = route(spec, x, router_w, bias, parallel)
+    return forward(spec, x, idx, w, blobs, shared_blob, parallel), idx, w

@@ -6,10 +6,13 @@
  * HIP library and its Python binding) never links, imports or calls it, and
  * this file shares no code, header or table with that path.
  *
- * Plain, single-threaded C11, built with -O2 -ffp-contract=off and without
- * -ffast-math: every floating-point operation below is one IEEE-754 binary32
- * operation rounded to nearest-even, and every fused multiply-add is an
- * explicit fmaf().  Where the pages leave an operation order or a rounding
+ * Plain C11, built with -O2 -ffp-contract=off and without -ffast-math:
+ * every floating-point operation below is one IEEE-754 binary32 operation
+ * rounded to nearest-even, and every fused multiply-add is an explicit
+ * fmaf().  Each token's arithmetic is single-threaded and sequential.  The
+ * same source is also built with OpenMP: then the loops over tokens, which
+ * share no data, run their iterations on several threads, and nothing else
+ * changes, so both builds give the same bits (a CPU test checks this).  Where the pages leave an operation order or a rounding
  * rule open, the reading taken is stated at the function; the layer's output
  * is then one exactly defined binary32 value per element.
  *
@@ -29,6 +32,9 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 #define OQ_OK 0
 #define OQ_EINVAL (-1)
@@ -380,17 +386,30 @@ int oq_moe_route(int H, int E, int K, float rsf, int norm, int S, const float *x
     if (!all_finite(x, (size_t)S * (size_t)H) || !all_finite(router_w, (size_t)E * (size_t)H) ||
         (bias && !all_finite(bias, (size_t)E)))
         return OQ_ENONFINITE;
-    float *lg = (float *)malloc(sizeof(float) * (size_t)E);
-    if (!lg) return OQ_ENOMEM;
     int rc = OQ_OK;
-    for (int t = 0; t < S && rc == OQ_OK; ++t) {
-        for (int e = 0; e < E; ++e)
-            lg[e] = oq_router_logit(x + (size_t)t * H, router_w + (size_t)e * H, H);
-        if (logits_out) memcpy(logits_out + (size_t)t * E, lg, sizeof(float) * (size_t)E);
-        rc = oq_select(lg, bias, E, K, rsf, norm, idx + (size_t)t * K, w + (size_t)t * K,
-                       sig_out ? sig_out + (size_t)t * E : NULL);
+    /* tokens are independent: each iteration reads its own x row and writes
+     * its own rows of the outputs */
+#ifdef _OPENMP
+#pragma omp parallel for schedule(dynamic, 1)
+#endif
+    for (int t = 0; t < S; ++t) {
+        float *lg = (float *)malloc(sizeof(float) * (size_t)E);
+        int r = lg ? OQ_OK : OQ_ENOMEM;
+        if (r == OQ_OK) {
+            for (int e = 0; e < E; ++e)
+                lg[e] = oq_router_logit(x + (size_t)t * H, router_w + (size_t)e * H, H);
+            if (logits_out) memcpy(logits_out + (size_t)t * E, lg, sizeof(float) * (size_t)E);
+            r = oq_select(lg, bias, E, K, rsf, norm, idx + (size_t)t * K, w + (size_t)t * K,
+                          sig_out ? sig_out + (size_t)t * E : NULL);
+        }
+        free(lg);
+        if (r != OQ_OK) {
+#ifdef _OPENMP
+#pragma omp critical(oq_rc)
+#endif
+            if (rc == OQ_OK) rc = r;
+        }
     }
-    free(lg);
     return rc;
 }
 
@@ -404,6 +423,30 @@ int oq_moe_route(int H, int E, int K, float rsf, int norm, int S, const float *x
  * after the routed sum; without a shared expert out is the routed sum.
  * blobs[e] == NULL marks expert e as not resident.
  * ---------------------------------------------------------------------- */
+/* One token of oq_moe_forward_g: out_t[r] for r < H (inputs validated). */
+static int forward_token(int H, int I, int K, int n_shared, int bits, int group, const float *x_t,
+                         const int32_t *idx_t, const float *w_t, const uint8_t *const *blobs,
+                         const uint8_t *shared_blob, float *out_t) {
+    int8_t *qx = (int8_t *)malloc((size_t)H);
+    float *dx = (float *)malloc(sizeof(float) * (size_t)(H / 32));
+    float *y = (float *)malloc(sizeof(float) * (size_t)H * (size_t)K);
+    float *ysh = (float *)malloc(sizeof(float) * (size_t)H);
+    int rc = (qx && dx && y && ysh) ? OQ_OK : OQ_ENOMEM;
+    if (rc == OQ_OK) oq_q8_0(x_t, H, qx, dx);
+    for (int k = 0; k < K && rc == OQ_OK; ++k)
+        rc = oq_expert_g(blobs[idx_t[k]], H, I, bits, group, qx, dx, y + (size_t)k * H, NULL, NULL, NULL, NULL,
+                         NULL);
+    if (rc == OQ_OK && n_shared)
+        rc = oq_expert_g(shared_blob, H, I, bits, group, qx, dx, ysh, NULL, NULL, NULL, NULL, NULL);
+    for (int r = 0; r < H && rc == OQ_OK; ++r) {
+        float acc = 0.0f;
+        for (int k = 0; k < K; ++k) acc = fmaf(w_t[k], y[(size_t)k * H + r], acc);
+        out_t[r] = n_shared ? acc + ysh[r] : acc;
+    }
+    free(qx); free(dx); free(y); free(ysh);
+    return rc;
+}
+
 int oq_moe_forward_g(int H, int I, int E, int K, int n_shared, int bits, int group, int S, const float *x,
                      const int32_t *idx, const float *w, const uint8_t *const *blobs,
                      const uint8_t *shared_blob, float *out) {
@@ -420,26 +463,22 @@ int oq_moe_forward_g(int H, int I, int E, int K, int n_shared, int bits, int gro
                 if (idx[(size_t)t * K + k2] == e) return OQ_EINVAL;
             if (!blobs[e]) return OQ_ENOTRESIDENT;
         }
-    int8_t *qx = (int8_t *)malloc((size_t)H);
-    float *dx = (float *)malloc(sizeof(float) * (size_t)(H / 32));
-    float *y = (float *)malloc(sizeof(float) * (size_t)H * (size_t)K);
-    float *ysh = (float *)malloc(sizeof(float) * (size_t)H);
-    if (!qx || !dx || !y || !ysh) { free(qx); free(dx); free(y); free(ysh); return OQ_ENOMEM; }
     int rc = OQ_OK;
-    for (int t = 0; t < S && rc == OQ_OK; ++t) {
-        oq_q8_0(x + (size_t)t * H, H, qx, dx);
-        for (int k = 0; k < K && rc == OQ_OK; ++k)
-            rc = oq_expert_g(blobs[idx[(size_t)t * K + k]], H, I, bits, group, qx, dx, y + (size_t)k * H,
-                             NULL, NULL, NULL, NULL, NULL);
-        if (rc == OQ_OK && n_shared)
-            rc = oq_expert_g(shared_blob, H, I, bits, group, qx, dx, ysh, NULL, NULL, NULL, NULL, NULL);
-        for (int r = 0; r < H && rc == OQ_OK; ++r) {
-            float acc = 0.0f;
-            for (int k = 0; k < K; ++k) acc = fmaf(w[(size_t)t * K + k], y[(size_t)k * H + r], acc);
-            out[(size_t)t * H + r] = n_shared ? acc + ysh[r] : acc;
+    /* tokens are independent: each iteration reads its own x, idx and w rows
+     * and writes its own out row */
+#ifdef _OPENMP
+#pragma omp parallel for schedule(dynamic, 1)
+#endif
+    for (int t = 0; t < S; ++t) {
+        int r = forward_token(H, I, K, n_shared, bits, group, x + (size_t)t * H, idx + (size_t)t * K,
+                              w + (size_t)t * K, blobs, shared_blob, out + (size_t)t * H);
+        if (r != OQ_OK) {
+#ifdef _OPENMP
+#pragma omp critical(oq_rc)
+#endif
+            if (rc == OQ_OK) rc = r;
         }
     }
-    free(qx); free(dx); free(y); free(ysh);
     return rc;
 }
 
@@ -471,4 +510,16 @@ void oq_sigmoid_n(const float *x, float *y, uint64_t n) {
 
 void oq_swiglu_n(const float *g, const float *u, float *h, uint64_t n) {
     for (uint64_t i = 0; i < n; ++i) h[i] = oq_swiglu(g[i], u[i]);
+}
+
+/* Threads of the token loops: n > 0 sets them (OpenMP build); returns the
+ * number the loops will use (1 in the single-threaded build). */
+int oq_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+    return omp_get_max_threads();
+#else
+    (void)n;
+    return 1;
+#endif
 }

@@ -135,6 +135,26 @@ def _stream(stream):
     return stream.cuda_stream
 
 
+def _event_handle(ev, what, create_on=None):
+    """hipEvent_t of a torch.cuda.Event (or a raw address, or None).  torch
+    creates an event's HIP handle lazily, at its first record(); until then
+    the handle is 0, which the library would read as "no event".  An event
+    the library is to record is therefore created here first, by recording
+    it on the stream it will be recorded on (create_on; the library records
+    it again after its own work); an event the library is to wait for must
+    already have been recorded."""
+    if ev is None or isinstance(ev, int):
+        return ev
+    if not ev.cuda_event:
+        if create_on is None:
+            raise ValueError(f"{what}: this torch.cuda.Event has never been recorded, so it has no HIP event "
+                             "to wait for")
+        ev.record(create_on if not isinstance(create_on, int) else None)
+        if not ev.cuda_event:
+            raise RuntimeError(f"{what}: torch did not create the HIP event on record()")
+    return ev.cuda_event
+
+
 def _check(rc, where):
     if rc != COLI_OK:
         raise ColiError(rc, where)
@@ -175,9 +195,7 @@ def coli_moe_forward(dims, x, topk_idx, topk_w, expert_blobs, shared_blob, out, 
     if pending_mask is not None:
         mask = np.ascontiguousarray(np.asarray(pending_mask, dtype=np.uint8))
         mask_ptr = mask.ctypes.data
-    ev = pending_ready
-    if ev is not None and not isinstance(ev, int):
-        ev = ev.cuda_event
+    ev = _event_handle(pending_ready, "pending_ready")
     _check(_lib.coli_moe_forward(
         _dims(dims), S, _dev(x, torch.float32, "x"), _dev(topk_idx, torch.int32, "topk_idx"),
         _dev(topk_w, torch.float32, "topk_w"), _dev(expert_blobs, torch.int64, "expert_blobs"),
@@ -204,9 +222,7 @@ def coli_moe_stage_experts(host_src, dev_dst, bytes_each: int, copy_stream=None,
         raise ValueError("host_src and dev_dst differ in length")
     src = (ctypes.c_void_p * max(n, 1))(*[_ptr(s, None, "host_src") for s in host_src])
     dst = (ctypes.c_void_p * max(n, 1))(*[_ptr(d, None, "dev_dst") for d in dev_dst])
-    ev = done_event
-    if ev is not None and not isinstance(ev, int):
-        ev = ev.cuda_event
+    ev = _event_handle(done_event, "done_event", create_on=copy_stream)
     _check(_lib.coli_moe_stage_experts(n, src, dst, int(bytes_each), _stream(copy_stream), ev),
            "coli_moe_stage_experts")
 

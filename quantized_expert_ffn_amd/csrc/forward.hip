@@ -4,18 +4,21 @@
 // over Q8_0 activations, batch-union MoE with each unique expert read once).
 //
 // Work decomposition.  A "unit" is one unique routed expert of the call (in
-// ascending id) or the shared expert (last).  Every workgroup rebuilds the
-// unit table from topk_idx in LDS (a few hundred integer operations), takes
-// unit blockIdx.y and a tile of weight rows blockIdx.x, and streams those
-// rows once for all tokens routed to the unit.
+// ascending id) or the shared expert (last).  A workgroup takes unit
+// blockIdx.y and a tile of weight rows blockIdx.x, and streams those rows
+// once for all tokens routed to the unit; the unit table comes from the
+// router launch (the workspace) or is rebuilt from topk_idx in LDS (a few
+// hundred integer operations).
 //
-//   k_gateup: 32 gate rows + the 32 matching up rows (rows i0..i0+31) ->
-//             SwiGLU -> one Q8_0 block of h per token, written to the
-//             workspace slot of the (token, rank) pair.
-//   k_down:   64 down rows -> y per pair slot in the workspace; the last of
-//             the units to finish a row tile (integer arrival counter) then
-//             combines that tile for every token in rank order.  Each output
-//             element has exactly one writer; no floating-point atomics.
+//   k_gateup:  32 gate rows + the 32 matching up rows (rows i0..i0+31) ->
+//              SwiGLU -> one Q8_0 block of h per token, written to the
+//              workspace slot of the (token, rank) pair.
+//   k_down:    64 down rows -> y per pair slot in the workspace (Y).
+//   k_combine: out[t] = rank-order fmaf chain over the routed y of token t,
+//              plus its shared y, once k_down has finished: each output
+//              element has exactly one writer; no floating-point atomics.
+// Batches whose down+combine tile fits 80 KiB of LDS take k_down_rows
+// (down_rows.hip) instead of k_down + k_combine.
 //
 // Inner loop (both kernels).  Wave w owns 16 rows.  A row is read in chunks
 // of 64 Q8_0 blocks: lane l loads block 64c+l of each of its 16 rows

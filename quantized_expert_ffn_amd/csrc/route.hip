@@ -165,12 +165,12 @@ __global__ __launch_bounds__(64 * RF_W) void k_route_fused(const RouteArgs r) {
     const uint8_t **btab = reinterpret_cast<const uint8_t **>(smem + a16(T.total + 4 * (size_t)P));
     int32_t si = 0;
     float sw = 0.0f;
+    bool sok = true;
     if (wave == 0) {
         const float *lg = r.logits + (size_t)t * E;
         auto ld = [&](int q) { return ld_dev(lg + q); };
-        const bool sok = E <= 256 ? select_wave_b<4>(ld, [&](int m, int) { return bpre[m]; }, E, K, r.rsf, r.norm,
-                                                     &si, &sw)
-                                  : select_wave<16>(ld, r.bias, E, K, r.rsf, r.norm, &si, &sw);
+        sok = E <= 256 ? select_wave_b<4>(ld, [&](int m, int) { return bpre[m]; }, E, K, r.rsf, r.norm, &si, &sw)
+                       : select_wave<16>(ld, r.bias, E, K, r.rsf, r.norm, &si, &sw);
         if (!sok && lane == 0) raise_status(r.status, ST_NONFINITE);
     }
     if (S == 1) {
@@ -182,6 +182,30 @@ __global__ __launch_bounds__(64 * RF_W) void k_route_fused(const RouteArgs r) {
         const UnitTable U = unit_table(1, K, E);
         int32_t *tab = reinterpret_cast<int32_t *>(r.units);
         const uint8_t **ublob = reinterpret_cast<const uint8_t **>(r.units + U.ublob);
+        if (!sok) {
+            // Non-finite scores (reported above): the picks may repeat an
+            // expert, so no routed unit is listed; the table holds the shared
+            // expert alone and the expert kernels read no routed blob.
+            if (lane < K) {
+                r.idx_out[lane] = si;
+                r.w_out[lane] = sw;
+            }
+            if (lane == 0) {
+                const int ns = r.n_shared;
+                tab[0] = ns;
+                tab[1] = 0;
+                tab[2] = 0;
+                tab[3] = 0;
+                if (ns) {
+                    tab[U.uexp] = -1;
+                    tab[U.pairs] = K;
+                    ublob[0] = r.shared;
+                }
+                tab[U.uoff] = 0;
+                tab[U.uoff + ns] = ns;
+            }
+            return;
+        }
         int rank = 0;
         for (int j = 0; j < K; ++j) rank += __builtin_amdgcn_readlane(si, j) < si ? 1 : 0;
         // blob pointer of expert si: prefetched by lane si % 64 in bl[si / 64]

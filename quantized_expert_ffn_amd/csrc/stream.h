@@ -280,9 +280,13 @@ __device__ __forceinline__ float chain_chunk_g(float acc, const int32_t *is, con
 // Group scales of a wave's rows (one f32 per 32 << lgb codes), staged
 // through LDS one 64-block chunk at a time: the chunk's RPW x (64 >> lgb)
 // scales are 16-byte words w = lane + 64 k, word w holding scales
-// 4 p .. 4 p + 3 of the chunk of row w / (16 >> lgb), p = w % (16 >> lgb).
-// lgb <= 4 (groups of up to 512 codes), so a word never straddles rows.
-// Loads run through the blob's buffer resource (zeros past its end).
+// 4 p .. 4 p + 3 of the chunk of row w / (16 >> lgb), p = w % (16 >> lgb)
+// (lgb <= 4, groups of up to 512 codes, so a row's chunk is whole words).
+// A row shorter than a chunk has fewer than 64 >> lgb scales there: its
+// words then run on into the next row's scales (or past the blob's end,
+// where the buffer resource returns zeros), values that belong to blocks
+// past the row's end and are never used.  Loads run through the blob's
+// buffer resource.
 struct RowGroups {
     __amdgpu_buffer_rsrc_t rsrc;
     uint32_t base;         // byte offset of the scales of the wave's first row

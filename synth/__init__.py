@@ -240,6 +240,96 @@ def gaussian_expert(seed: int, layer: int, expert: int, spec: LayerSpec, sigma: 
 
 
 # --------------------------------------------------------------------------
+# edge-case inputs: the code range's extremes
+# --------------------------------------------------------------------------
+# every code the formats admit, the minimum included (the quantisers above
+# never produce int4 -8 or int8 -128, but the blob format holds them)
+FULL_RANGE = {8: (-128, 127), 4: (-8, 7), 2: (-2, 1)}
+
+
+def extreme_codes(key: int, rows: int, cols: int, bits: int, flat_rows: tuple = ()) -> np.ndarray:
+    """Codes [rows, cols] built around the range's minimum lo and maximum hi:
+    row r % 4 == 0 holds lo at position (r // 4) % 32 of every 32-code block
+    and hi elsewhere, r % 4 == 2 the same at position (r // 4 + 16) % 32 (so
+    that every position gets the minimum alone in some row of any matrix of
+    at least 64 rows outside flat_rows); r % 4 == 1 is lo everywhere; r % 4
+    == 3 alternates lo and hi when r // 4 is even and is uniform over the
+    whole range when it is odd.  Rows in flat_rows (a range) are lo
+    everywhere, so that their dot products with one vector are equal."""
+    lo, hi = FULL_RANGE[bits]
+    u = uniform_u64(key, rows * cols).reshape(rows, cols)
+    codes = (lo + (u % np.uint64(hi - lo + 1)).astype(np.int64)).astype(np.int8)
+    pos = np.arange(cols) % 32
+    for r in range(rows):
+        m, j = r % 4, r // 4
+        if m == 0:
+            codes[r] = np.where(pos == j % 32, lo, hi)
+        elif m == 2:
+            codes[r] = np.where(pos == (j + 16) % 32, lo, hi)
+        elif m == 1:
+            codes[r] = lo
+        elif j % 2 == 0:
+            codes[r] = np.where(pos % 2 == 0, lo, hi)
+    if flat_rows:
+        codes[flat_rows[0]:flat_rows[1]] = lo
+    return codes
+
+
+def extreme_parts(seed: int, layer: int, expert: int, spec: LayerSpec) -> dict:
+    """Codes and scales of an edge-case expert (see extreme_expert)."""
+    H, I, b, G = spec.hidden, spec.inter, spec.wbits, spec.group
+    flat = (32, 64) if I >= 64 else ()
+    parts = {}
+    for m, (name, rows, cols) in enumerate((("gate", I, H), ("up", I, H), ("down", H, I))):
+        key = stream_key(seed, K_WEIGHT, layer, expert, m, 7)
+        parts[name] = extreme_codes(key, rows, cols, b, flat if name != "down" else ())
+        ns = cols // G if G else 1
+        s = (0.0025 + 0.005 * uniform01(stream_key(seed, K_WEIGHT, layer, expert, m, 8), rows * ns))
+        s = s.astype(np.float32).reshape(rows, ns)
+        if flat and name != "down":
+            s[flat[0]:flat[1]] = s[flat[0]]
+        parts["s_" + name] = s if G else s[:, 0].copy()
+    return parts
+
+
+def extreme_expert(seed: int, layer: int, expert: int, spec: LayerSpec) -> np.ndarray:
+    """A blob whose codes come from extreme_codes: gate and up rows 32..63
+    are all lo with one common scale, so that a token's h is the same over
+    that block of 32 and its Q8_0 codes are all +-127; scales (per row or per
+    group) are seeded uniforms in [0.0025, 0.0075)."""
+    p = extreme_parts(seed, layer, expert, spec)
+    return assemble_blob(spec.hidden, spec.inter, spec.wbits, p["gate"], p["up"], p["down"],
+                         p["s_gate"], p["s_up"], p["s_down"], spec.group)
+
+
+def extreme_hidden_states(seed: int, layer: int, S: int, H: int) -> np.ndarray:
+    """x [S, H] f32 whose 32-value blocks each hold one magnitude (a seeded
+    uniform in [0.5, 2)), so that every Q8_0 code is +-127: block b of a
+    token is all positive when (b + t) % 3 == 0, all negative when it is 1,
+    and of seeded random signs when it is 2."""
+    nb = H // 32
+    mag = 0.5 + 1.5 * uniform01(stream_key(seed, K_X, layer, 900), S * nb).reshape(S, nb)
+    rnd = uniform01(stream_key(seed, K_X, layer, 901), S * H).reshape(S, nb, 32) < 0.5
+    mode = (np.arange(nb)[None, :] + np.arange(S)[:, None]) % 3
+    sign = np.where(mode[:, :, None] == 0, 1.0, np.where(mode[:, :, None] == 1, -1.0, np.where(rnd, 1.0, -1.0)))
+    return (sign * mag[:, :, None]).reshape(S, H).astype(np.float32)
+
+
+def extreme_layer(seed: int, S: int, spec: LayerSpec, layer: int = 0) -> dict:
+    """A small layer of extreme_expert blobs and extreme_hidden_states (router
+    gate and bias as tiny_layer)."""
+    blobs = [extreme_expert(seed, layer, e, spec) for e in range(spec.n_experts + spec.n_shared)]
+    return {
+        "spec": spec,
+        "x": extreme_hidden_states(seed, layer, S, spec.hidden),
+        "router_w": router_weights(seed, layer, spec),
+        "bias": router_bias(seed, layer, spec),
+        "blobs": blobs[:spec.n_experts],
+        "shared": blobs[spec.n_experts] if spec.n_shared else None,
+    }
+
+
+# --------------------------------------------------------------------------
 # fast large-blob recipe (C helper)
 # --------------------------------------------------------------------------
 _HERE = os.path.dirname(os.path.abspath(__file__))

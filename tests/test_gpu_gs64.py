@@ -54,6 +54,33 @@ def test_tiny_gs_layer_entry(torch, S, group):
     parity(out, o_out)
 
 
+@pytest.mark.parametrize("group,H,I", [(256, 256, 256), (256, 512, 256), (512, 512, 512), (512, 1024, 512)],
+                         ids=["g256-h256", "g256-h512", "g512-h512", "g512-h1024"])
+@pytest.mark.parametrize("S", [1, 3, 12])
+def test_large_groups(torch, S, group, H, I):
+    """Groups of 256 and 512 codes (one or two scales per gate/up row, and
+    fewer scales per row than a 64-block chunk holds) through
+    coli_moe_layer and coli_moe_route + coli_moe_forward; these group sizes
+    run the decode kernels at every batch size."""
+    from synth.device import upload_layer
+    spec = dataclasses.replace(synth.TINY_GS64, group=group, hidden=H, inter=I)
+    say(f"gs large groups S={S} group={group} H={H} I={I}")
+    d = synth.tiny_layer(seed=15, S=S, spec=spec)
+    dims = q().make_dims(spec)
+    dl = upload_layer(d)
+    ws = workspace(dims, S)
+    idx, w, out = _layer_call(torch, dims, dl, ws)
+    assert status(ws) == 0, q().coli_moe_last_error()
+    o_out, o_idx, o_w = oracle.layer(spec, d["x"], d["router_w"], d["bias"], d["blobs"], d["shared"])
+    assert np.array_equal(idx, o_idx)
+    assert np.array_equal(w.view(np.uint32), o_w.view(np.uint32))
+    parity(out, o_out)
+    idx2, w2 = gpu_route(dims, dl, ws)
+    out2 = gpu_forward(dims, dl, idx2, w2, ws).cpu().numpy()
+    assert status(ws) == 0, q().coli_moe_last_error()
+    parity(out2, o_out)
+
+
 @pytest.mark.parametrize("S", [1, 4, 40])
 def test_tiny_gs64_forward_entry(torch, S):
     """coli_moe_route + coli_moe_forward (the gate/up launch runs the shared

@@ -232,6 +232,35 @@ def test_pending_experts_run_after_the_event(torch):
     assert np.array_equal(out.view(np.uint32), ref.view(np.uint32))
 
 
+@pytest.mark.parametrize("S", [1, 2])
+def test_nonfinite_router_rows_leave_a_safe_unit_table(torch, S):
+    """At least E - K + 1 router rows of NaN: no token has K finite scores,
+    so the selection fails and may repeat an expert.  coli_moe_layer (its
+    router launch selects and writes the unit table) must report
+    COLI_ENONFINITE and leave a table the expert kernels can run; the next,
+    valid call on the same workspace is bitwise the oracle's."""
+    from synth.device import upload_layer
+    say(f"NaN router rows, layer call S={S}")
+    spec = synth.TINY
+    qm = q()
+    d = _layer(spec, S, seed=31)
+    dims = qm.make_dims(spec)
+    dl = upload_layer(d)
+    bad = dl["router_w"].clone()
+    bad[: spec.n_experts - spec.top_k + 1] = float("nan")
+    ws = workspace(dims, S)
+    idx = torch.empty((S, spec.top_k), dtype=torch.int32, device="cuda")
+    w = torch.empty((S, spec.top_k), dtype=torch.float32, device="cuda")
+    out = torch.empty((S, spec.hidden), dtype=torch.float32, device="cuda")
+    qm.coli_moe_layer(dims, dl["x"], bad, dl["bias"], dl["table"], dl["shared"], idx, w, out, ws)
+    assert status(ws) == qm.COLI_ENONFINITE
+    qm.coli_moe_layer(dims, dl["x"], dl["router_w"], dl["bias"], dl["table"], dl["shared"], idx, w, out, ws)
+    assert status(ws) == 0, qm.coli_moe_last_error()
+    o_out, o_idx, _ = _oracle(spec, d)
+    assert np.array_equal(idx.cpu().numpy(), o_idx)
+    parity(out.cpu().numpy(), o_out)
+
+
 def test_stage_experts_copies_bytes(torch):
     say("stage experts")
     spec = synth.TINY
