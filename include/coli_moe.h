@@ -172,6 +172,34 @@ int coli_moe_layer(const coli_moe_dims *dims, int32_t n_tokens, const float *x,
                    float *topk_w, float *out, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * coli_moe_layer without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, serving loops that
+ * must not call hipMalloc, harnesses that forbid it): the same launches and
+ * the same bits as coli_moe_layer, with a library-owned scratch array of
+ * 32 MiB per GPU (a static device array, kept until the process ends) as
+ * the workspace.  The call allocates nothing.
+ *   n_tokens     at most what fits 32 MiB of workspace
+ *                (coli_moe_workspace_bytes <= 32 MiB: 132 tokens at the
+ *                GLM-5.2 shape); beyond it COLI_EWORKSPACE, nothing launched
+ *   status_out   device uint32 or NULL: after the layer's kernels, one more
+ *                launch moves the scratch's status word there and clears it:
+ *                0, or bit 0 (1) non-finite input or gate weights, bit 1 (2)
+ *                an expert index out of range or repeated in a token, bit 2
+ *                (4) a routed expert's blob pointer is NULL, bit 3 (8) a
+ *                persistent kernel's grid barrier gave up waiting; with NULL
+ *                the bits are cleared unread
+ * Other arguments as for coli_moe_layer.  Every call on one GPU shares
+ * that GPU's scratch, so calls that overlap on one GPU (several streams or
+ * threads at once) race and give unspecified results; calls on one stream
+ * are safe.
+ */
+int coli_moe_layer_noalloc(const coli_moe_dims *dims, int32_t n_tokens, const float *x,
+                           const float *router_w, const float *router_bias,
+                           const void *const *expert_blobs, const void *shared_blob,
+                           int32_t *topk_idx, float *topk_w, float *out, uint32_t *status_out,
+                           void *stream);
+
+/*
  * Expert staging (README v1.0 "What's implemented": async expert readahead —
  * the next experts are fetched while the current ones are multiplied).
  * Enqueues n host-to-device copies of bytes_each bytes, host_src[i] (pinned

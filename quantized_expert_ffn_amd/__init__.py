@@ -37,6 +37,7 @@ EXPORTS = (
     "coli_moe_debug_logits", "coli_moe_debug_expf", "coli_moe_debug_q8_0",
     "coli_moe_debug_force_path", "coli_moe_layer", "coli_moe_debug_mfma_i8",
     "coli_moe_roof_sink_words", "coli_moe_roof_stream_read", "coli_moe_roof_mfma_i8",
+    "coli_moe_layer_noalloc",
 )
 
 KIND_ROUTER_LOGITS, KIND_ROUTER_SELECT, KIND_GATEUP, KIND_DOWN, KIND_COMBINE = 0, 1, 2, 3, 4
@@ -85,6 +86,7 @@ _sigs = {
     "coli_moe_roof_sink_words": (_SZ, []),
     "coli_moe_roof_stream_read": (ctypes.c_int, [_P, _SZ, _P, _P]),
     "coli_moe_roof_mfma_i8": (ctypes.c_int, [_I32, _P, _P]),
+    "coli_moe_layer_noalloc": (ctypes.c_int, [_D, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
 }
 for _name, (_res, _args) in _sigs.items():
     _f = getattr(_lib, _name)
@@ -214,6 +216,25 @@ def coli_moe_layer(dims, x, router_w, router_bias, expert_blobs, shared_blob, to
         _ptr(shared_blob, None, "shared_blob"), _dev(topk_idx, torch.int32, "topk_idx"),
         _dev(topk_w, torch.float32, "topk_w"), _dev(out, torch.float32, "out"), _dev(ws, torch.uint8, "ws"),
         _nbytes(ws), _stream(stream)), "coli_moe_layer")
+
+
+def coli_moe_layer_noalloc(dims, x, router_w, router_bias, expert_blobs, shared_blob, topk_idx, topk_w, out,
+                           status_out=None, stream=None):
+    """coli_moe_layer on the library's own scratch (no workspace argument);
+    status_out: device int32/uint32 tensor of one element, or None."""
+    import torch
+    S = x.shape[0]
+    st = None
+    if status_out is not None:
+        if status_out.numel() != 1 or status_out.dtype not in (torch.int32, torch.uint32):
+            raise ValueError("status_out: one 32-bit device word")
+        st = _dev(status_out, None, "status_out")
+    _check(_lib.coli_moe_layer_noalloc(
+        _dims(dims), S, _dev(x, torch.float32, "x"), _dev(router_w, torch.float32, "router_w"),
+        _dev(router_bias, torch.float32, "router_bias"), _dev(expert_blobs, torch.int64, "expert_blobs"),
+        _ptr(shared_blob, None, "shared_blob"), _dev(topk_idx, torch.int32, "topk_idx"),
+        _dev(topk_w, torch.float32, "topk_w"), _dev(out, torch.float32, "out"), st, _stream(stream)),
+        "coli_moe_layer_noalloc")
 
 
 def coli_moe_stage_experts(host_src, dev_dst, bytes_each: int, copy_stream=None, done_event=None):

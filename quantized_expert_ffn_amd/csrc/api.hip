@@ -406,27 +406,39 @@ int coli_moe_forward(const coli_moe_dims *d, int32_t S, const float *x, const in
     return forward_launches(a, d->wbits, any_pending, pending_ready, false, w8 + L.units, st);
 }
 
-int coli_moe_layer(const coli_moe_dims *d, int32_t S, const float *x, const float *router_w,
-                   const float *router_bias, const void *const *expert_blobs, const void *shared_blob,
-                   int32_t *topk_idx, float *topk_w, float *out, void *ws, size_t ws_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Argument checks of a layer call that need no device (dims, pointers,
+// alignment); 0 or the failure code.
+int layer_args_ok(const coli_moe_dims *d, int32_t S, const float *x, const float *router_w,
+                  const void *const *expert_blobs, const void *shared_blob, const int32_t *topk_idx,
+                  const float *topk_w, const float *out, const char *who) {
     int rc = check_dims(d);
     if (rc) return rc;
     if (S < 0) return fail(COLI_EINVAL, "n_tokens=%d < 0", S);
     if (S == 0) return COLI_OK;
-    if (!x || !router_w || !expert_blobs || !topk_idx || !topk_w || !out || !ws)
-        return fail(COLI_EINVAL, "coli_moe_layer: NULL pointer argument");
+    if (!x || !router_w || !expert_blobs || !topk_idx || !topk_w || !out)
+        return fail(COLI_EINVAL, "%s: NULL pointer argument", who);
     if (!aligned16(x) || !aligned16(router_w) || !aligned16(out) || !aligned16(shared_blob))
-        return fail(COLI_EINVAL, "coli_moe_layer: x, router_w, out and shared_blob must be 16-byte aligned");
+        return fail(COLI_EINVAL, "%s: x, router_w, out and shared_blob must be 16-byte aligned", who);
     if (d->n_shared && !shared_blob) return fail(COLI_ENOTRESIDENT, "n_shared=1 but shared_blob is NULL");
+    return COLI_OK;
+}
+
+// The launches of a layer call on a workspace of at least
+// ws_layout(...).total bytes (arguments already checked).
+int layer_launches(const coli_moe_dims *d, int32_t S, const float *x, const float *router_w,
+                   const float *router_bias, const void *const *expert_blobs, const void *shared_blob,
+                   int32_t *topk_idx, float *topk_w, float *out, void *ws, hipStream_t st) {
+    int rc;
     const WsLayout L = ws_layout(d->hidden, d->inter, d->n_experts, d->top_k, S);
-    if (ws_bytes < L.total)
-        return fail(COLI_EWORKSPACE, "workspace %zu bytes < %zu needed for %d tokens", ws_bytes, L.total, S);
     if ((rc = forced_path_refused(d))) return rc;
     if (g_force_path == 2 && !persistent_fits(d, S, false))
         return fail(COLI_EINVAL, "persistent kernel forced but the call has more than 8 tokens or a shape beyond "
                                  "its LDS budget");
     if ((rc = check_device())) return rc;
-    hipStream_t st = static_cast<hipStream_t>(stream);
     uint8_t *w8 = static_cast<uint8_t *>(ws);
     FwdArgs a = fwd_args(d, S, x, topk_idx, topk_w, expert_blobs, shared_blob, out, w8, L);
     if (!use_persistent(d, S, false)) {
@@ -500,6 +512,93 @@ int coli_moe_layer(const coli_moe_dims *d, int32_t S, const float *x, const floa
     timing_after(KK_LAYER, st);
     if (e != hipSuccess) return hip_fail(e, "layer launch");
     return COLI_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int coli_moe_layer(const coli_moe_dims *d, int32_t S, const float *x, const float *router_w,
+                   const float *router_bias, const void *const *expert_blobs, const void *shared_blob,
+                   int32_t *topk_idx, float *topk_w, float *out, void *ws, size_t ws_bytes, void *stream) {
+    int rc = layer_args_ok(d, S, x, router_w, expert_blobs, shared_blob, topk_idx, topk_w, out, "coli_moe_layer");
+    if (rc || S == 0) return rc;
+    if (!ws) return fail(COLI_EINVAL, "coli_moe_layer: NULL pointer argument");
+    const WsLayout L = ws_layout(d->hidden, d->inter, d->n_experts, d->top_k, S);
+    if (ws_bytes < L.total)
+        return fail(COLI_EWORKSPACE, "workspace %zu bytes < %zu needed for %d tokens", ws_bytes, L.total, S);
+    return layer_launches(d, S, x, router_w, router_bias, expert_blobs, shared_blob, topk_idx, topk_w, out, ws,
+                          static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"
+
+// ---- the layer without a caller workspace -------------------------------
+// A file-scope device array serves as the workspace of
+// coli_moe_layer_noalloc.  Each GPU the library runs on holds its own copy
+// (zero at load, as a workspace must start) until the process ends; its
+// address on a device comes from hipGetSymbolAddress, taken once per device
+// with that device current.  In host code the array's name is not a device
+// address: only the pointer looked up here is ever handed to kernels.
+namespace {
+
+constexpr size_t NOALLOC_SCRATCH_BYTES = (size_t)32 << 20;
+static __device__ __align__(256) uint8_t scratch[NOALLOC_SCRATCH_BYTES];
+
+// Device address of this device's scratch array (looked up on first use).
+int scratch_ptr(uint8_t **out) {
+    static std::mutex mu;
+    static std::vector<uint8_t *> ptrs;  // per device; null until looked up
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    std::lock_guard<std::mutex> lk(mu);
+    if ((int)ptrs.size() <= dev) ptrs.resize(dev + 1, nullptr);
+    if (!ptrs[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        if (!p) return fail(COLI_EHIP, "hipGetSymbolAddress(scratch) returned NULL");
+        ptrs[dev] = static_cast<uint8_t *>(p);
+    }
+    *out = ptrs[dev];
+    return COLI_OK;
+}
+
+// Moves the scratch's status word to the caller's word (when given) and
+// clears it, with vector stores (one thread).
+__global__ void k_take_status(uint32_t *ws_status, uint32_t *status_out) {
+    const uint32_t s = __hip_atomic_load(ws_status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (status_out) *status_out = s;
+    __hip_atomic_store(ws_status, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace
+
+extern "C" {
+
+int coli_moe_layer_noalloc(const coli_moe_dims *d, int32_t S, const float *x, const float *router_w,
+                           const float *router_bias, const void *const *expert_blobs, const void *shared_blob,
+                           int32_t *topk_idx, float *topk_w, float *out, uint32_t *status_out, void *stream) {
+    int rc = layer_args_ok(d, S, x, router_w, expert_blobs, shared_blob, topk_idx, topk_w, out,
+                           "coli_moe_layer_noalloc");
+    if (rc || S == 0) return rc;
+    const WsLayout L = ws_layout(d->hidden, d->inter, d->n_experts, d->top_k, S);
+    if (L.total > NOALLOC_SCRATCH_BYTES)
+        return fail(COLI_EWORKSPACE,
+                    "coli_moe_layer_noalloc: %d tokens need %zu bytes of scratch, more than its %zu; "
+                    "use coli_moe_layer with a workspace",
+                    S, L.total, NOALLOC_SCRATCH_BYTES);
+    if ((rc = check_device())) return rc;
+    uint8_t *ws = nullptr;
+    if ((rc = scratch_ptr(&ws))) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    rc = layer_launches(d, S, x, router_w, router_bias, expert_blobs, shared_blob, topk_idx, topk_w, out, ws, st);
+    if (rc) return rc;
+    hipLaunchKernelGGL(k_take_status, dim3(1), dim3(1), 0, st, reinterpret_cast<uint32_t *>(ws + L.status),
+                       status_out);
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? COLI_OK : hip_fail(e, "status launch");
 }
 
 int coli_moe_stage_experts(int32_t n, const void *const *host_src, void *const *dev_dst,
