@@ -72,6 +72,9 @@ def parse():
     ap.add_argument("--graph-steps", type=int, default=240, help="steps per captured HIP graph")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU-oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill-record", action="store_true",
+                    help="decode: skip the prefill record the default run adds to its line")
+    ap.add_argument("--prefill-steps", type=int, default=50, help="decode: timed steps of the added prefill record")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
                     help="only run a device copy of MB megabytes ten times (counter calibration)")
@@ -165,7 +168,7 @@ def main():
         log(f"layer {l}: {nblob} experts generated and staged ({time.time() - t0:.1f} s)")
     torch.cuda.synchronize()
     del staging
-    G = max(1, min(args.graph_steps, args.steps))
+    G, reps, reps_w, warm_eager = graph_plan(args.steps, args.warmup, args.graph_steps)
     if verify:
         # step s: 4 tokens of layer s mod L sharing experts (independent draws per step)
         xs_host = np.concatenate([synth.verify_hidden_states(args.seed, s % L, spec, S, batch=1 + s // L,
@@ -211,10 +214,10 @@ def main():
         for s in range(G):
             step(s)
     torch.cuda.synchronize()
-    reps_w = max(1, args.warmup // G)
-    reps = max(1, args.steps // G)
     for _ in range(reps_w):
         graph.replay()
+    for s in range(warm_eager):
+        step(s)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     rep_ev = replay_timed(graph, reps)
@@ -258,7 +261,7 @@ def main():
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": steps,
-        "warmup": reps_w * G,
+        "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -277,7 +280,8 @@ def main():
                          + f"Q8_0 activations, fp32 router gate; {L} layers resident in HBM, step s uses layer "
                          f"s mod {L}"),
             "layers_resident": L, "resident_gb": round(L * nblob * bb / 1e9, 1),
-            "tokens_per_step": S, "graph_steps": G, "entry": args.path, "kernels": args.kernels,
+            "tokens_per_step": S, "graph_steps": G, "graph_replays": reps, "entry": args.path,
+            "kernels": args.kernels,
         },
         "roofline": {
             "bound": "hbm", "kernel": dom_kernel,
@@ -295,7 +299,28 @@ def main():
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(args, spec, xs_host, layers, L, S)
     add_measured_roof(res, q, "hbm")
+    if args.workload == "decode" and not args.group_size and not args.no_prefill_record:
+        # the prefill half of the metric, on the same GPU in the same run
+        del layers, graph, xs, ws, idx, wts, out
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        pa = argparse.Namespace(**vars(args))
+        pa.steps, pa.warmup, pa.tokens, pa.kernels = args.prefill_steps, 10, 2048, "auto"
+        q.coli_moe_debug_force_path(0)
+        res["prefill"] = run_prefill(pa, q, synth, embedded=True)
     print(json.dumps(res), flush=True)
+
+
+def graph_plan(steps, warmup, graph_steps):
+    """Steps per captured graph G and replays: G divides the timed steps K
+    exactly (K = reps * G), leaves at least five replays when K allows (so
+    the per-replay spread has several samples) and is at most the warmup W
+    when W > 0 (so that the graph has been replayed once before the timed
+    replays).  Warmup: exactly W steps, as whole replays of the graph while
+    they fit, then single eager steps."""
+    cap = max(1, min(graph_steps, steps // 5 if steps >= 5 else steps, warmup if warmup > 0 else steps))
+    G = max(g for g in range(1, cap + 1) if steps % g == 0)
+    return G, steps // G, warmup // G, warmup % G
 
 
 KINDS = (("router_logits", 0), ("router_select", 1), ("quant_x", 7), ("group", 8), ("gateup", 2), ("down", 3),
@@ -383,10 +408,11 @@ def kernel_times(q, run):
     return us, n_l
 
 
-def run_prefill(args, q, synth):
+def run_prefill(args, q, synth, embedded=False):
     """Batch-union prefill: GLM-5.2-shaped layer, all experts resident, one
     step = coli_moe_layer over a batch of args.tokens Zipf-routed tokens
-    (two batches alternate)."""
+    (two batches alternate).  embedded: return the record (for the default
+    run's line) instead of printing it."""
     import numpy as np
     import torch
 
@@ -426,7 +452,7 @@ def run_prefill(args, q, synth):
     counts = np.bincount(routed[0].ravel(), minlength=E)
     kernel_us, launches = kernel_times(q, lambda: [step(s) for s in range(2)])
 
-    G = 10
+    G, reps, reps_w, warm_eager = graph_plan(args.steps, args.warmup, 10)
     cap = torch.cuda.Stream()
     cap.wait_stream(torch.cuda.current_stream())
     graph = torch.cuda.CUDAGraph()
@@ -434,10 +460,10 @@ def run_prefill(args, q, synth):
         for s in range(G):
             step(s)
     torch.cuda.synchronize()
-    reps_w = max(1, args.warmup // G)
-    reps = max(1, args.steps // G)
     for _ in range(reps_w):
         graph.replay()
+    for s in range(warm_eager):
+        step(s)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     rep_ev = replay_timed(graph, reps)
@@ -464,7 +490,7 @@ def run_prefill(args, q, synth):
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": steps,
-        "warmup": reps_w * G,
+        "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -477,7 +503,7 @@ def run_prefill(args, q, synth):
                         + ("int4 weights with one scale per 64 codes of a row, " if spec.group
                            else "int4 per-row-scaled weights, ") + "Q8_0 activations, "
                         "fp32 router gate, zero bias; Zipf(1.1) expert popularity; all 257 experts resident",
-            "tokens_per_step": S, "graph_steps": G, "kernels": args.kernels,
+            "tokens_per_step": S, "graph_steps": G, "graph_replays": reps, "kernels": args.kernels,
             "routing": {"unique": int((counts > 0).sum()), "min": int(counts[counts > 0].min()),
                         "median": float(np.median(counts[counts > 0])), "max": int(counts.max())},
         },
@@ -501,6 +527,15 @@ def run_prefill(args, q, synth):
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_prefill(args, spec, xs_host[0], d, host.numpy(), routed[0])
     add_measured_roof(res, q, "mfma")
+    if embedded:
+        for k in ("metric", "n_gpus", "higher_is_better", "scaling", "vs_baseline"):
+            res.pop(k)
+        res["tokens_per_s"] = res.pop("value")
+        res.pop("unit")
+        del graph, dev, host, xs, ws, idx, wts, out
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        return res
     print(json.dumps(res), flush=True)
 
 
@@ -662,9 +697,16 @@ def run_tiered(args, q, synth):
     print(json.dumps(res), flush=True)
 
 
+def _oracle_threads():
+    import oracle
+    return oracle.threads()
+
+
 def cpu_baseline_prefill(args, spec, x, d, host, routed):
-    """The CPU oracle on the first tokens of the prefill batch, as many as fit
-    the time budget (each token's output depends on that token only)."""
+    """The CPU oracle on the first tokens of the prefill batch (each token's
+    output depends on that token only): the multi-threaded build over
+    tokens on all of this host's threads, as many tokens as fit the time
+    budget at its rate, and the single-threaded build on a few tokens."""
     import numpy as np
 
     import oracle
@@ -672,15 +714,23 @@ def cpu_baseline_prefill(args, spec, x, d, host, routed):
     blobs = [host[e * bb:(e + 1) * bb] for e in range(E)]
     shared = host[E * bb:(E + 1) * bb]
     bias = np.zeros(E, np.float32)
-    n, spent = 0, 0.0
-    while spent < args.cpu_seconds and n < x.shape[0]:
+    n1, spent1 = 0, 0.0
+    while spent1 < args.cpu_seconds / 4 and n1 < x.shape[0]:
         t = time.perf_counter()
-        oracle.layer(spec, x[n:n + 1], d["router_w"], bias, blobs, shared)
-        spent += time.perf_counter() - t
-        n += 1
-    return {"value": round(n / spent, 4), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {n} tokens of the 2048-token batch, one at a time (route + 9 experts + combine), "
-                      f"{spent:.1f} s single-threaded"}
+        oracle.layer(spec, x[n1:n1 + 1], d["router_w"], bias, blobs, shared)
+        spent1 += time.perf_counter() - t
+        n1 += 1
+    rate1 = n1 / spent1
+    thr = _oracle_threads()
+    n = int(min(x.shape[0], max(thr, int(round(rate1 * thr * args.cpu_seconds / thr)) * thr)))
+    t = time.perf_counter()
+    oracle.layer(spec, x[:n], d["router_w"], bias, blobs, shared, parallel=True)
+    spent = time.perf_counter() - t
+    return {"value": round(n / spent, 4), "unit": "tokens/s", "cores": thr, "kind": "oracle",
+            "sample": f"first {n} tokens of the 2048-token batch (route + 9 experts + combine each) through the "
+                      f"oracle's OpenMP build, tokens spread over {thr} threads, {spent:.1f} s",
+            "single_core": {"value": round(rate1, 4), "unit": "tokens/s", "cores": 1,
+                            "sample": f"first {n1} tokens one at a time, single-threaded build, {spent1:.1f} s"}}
 
 
 def _hipbuild():
@@ -718,18 +768,22 @@ def counted_traffic(kernel):
 
 
 def cpu_baseline(args, spec, xs_host, layers, L, S=1):
-    """The CPU oracle (plain single-threaded C) on a bounded sample: whole
-    layer steps (route + 8 experts + shared + combine) of the same workload,
-    as many as fit the time budget."""
+    """The CPU oracle on a bounded sample of the same workload: whole
+    token-layer steps (route + the token's experts + shared + combine).  The
+    single-threaded build runs the benchmark's own steps (their layers) one
+    at a time; the multi-threaded build (the same source, its loop over
+    independent tokens on all of this host's threads) runs a batch of
+    hidden states of layer 0 drawn the same way, as many as fit the time
+    budget at that rate.  Expert generation is excluded from both."""
     import numpy as np
 
     import oracle
     import synth
-    n, spent = 0, 0.0
-    while spent < args.cpu_seconds and n < xs_host.shape[0]:
-        l = (n // S) % L
+    n1, spent1 = 0, 0.0
+    while spent1 < args.cpu_seconds / 3 and n1 < xs_host.shape[0]:
+        l = (n1 // S) % L
         d = synth.layer_inputs(args.seed, l, spec, 1)
-        x = xs_host[n:n + 1]
+        x = xs_host[n1:n1 + 1]
         idx, w, _, _ = oracle.route(spec, x, d["router_w"], d["bias"])
         blobs = [None] * spec.n_experts
         for e in idx[0]:
@@ -737,11 +791,33 @@ def cpu_baseline(args, spec, xs_host, layers, L, S=1):
         shared = synth.cdf_expert(args.seed, l, spec.n_experts, spec)
         t = time.perf_counter()
         oracle.layer(spec, x, d["router_w"], d["bias"], blobs, shared)
-        spent += time.perf_counter() - t
-        n += 1
-    return {"value": round(n / spent, 4), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n} token-layer steps of the same workload (route + 9 experts + combine), "
-                      f"{spent:.1f} s single-threaded; expert generation excluded"}
+        spent1 += time.perf_counter() - t
+        n1 += 1
+    rate1 = n1 / spent1
+    thr = _oracle_threads()
+    # as many tokens as the budget allows at the single-threaded rate on
+    # every thread, a whole number of tokens per thread
+    n = int(round(rate1 * thr * args.cpu_seconds / thr)) * thr
+    n = int(max(thr, min(n, 16 * thr)))
+    d = synth.layer_inputs(args.seed, 0, spec, 1)
+    x = synth.hidden_states(args.seed, 2000, n, spec.hidden)
+    idx, w, _, _ = oracle.route(spec, x, d["router_w"], d["bias"], parallel=True)
+    used = sorted(set(idx.ravel().tolist()))
+    blobs = [None] * spec.n_experts
+    for e in used:
+        blobs[e] = synth.cdf_expert(args.seed, 0, e, spec)
+    shared = synth.cdf_expert(args.seed, 0, spec.n_experts, spec)
+    t = time.perf_counter()
+    oracle.layer(spec, x, d["router_w"], d["bias"], blobs, shared, parallel=True)
+    spent = time.perf_counter() - t
+    del blobs
+    return {"value": round(n / spent, 4), "unit": "tokens/s", "cores": thr, "kind": "oracle",
+            "sample": f"{n} token-layer steps of the same workload (layer 0, N(0,1) hidden states; route + 9 "
+                      f"experts + combine each) through the oracle's OpenMP build, tokens spread over {thr} "
+                      f"threads, {spent:.1f} s; expert generation excluded",
+            "single_core": {"value": round(rate1, 4), "unit": "tokens/s", "cores": 1,
+                            "sample": f"{n1} of the benchmark's token-layer steps one at a time, single-threaded "
+                                      f"build, {spent1:.1f} s"}}
 
 
 if __name__ == "__main__":
