@@ -105,6 +105,13 @@ def _bind(L):
         "oq_expert_g": (I32, [P, I32, I32, I32, I32, P, P, P, P, P, P, P, P]),
         "oq_moe_forward_g": (I32, [I32, I32, I32, I32, I32, I32, I32, I32, P, P, P, P, P, P]),
         "oq_threads": (I32, [I32]),
+        "oq_e2m1": (F32, [I32]),
+        "oq_e8m0": (F32, [I32]),
+        "oq_unpack_mx": (None, [P, I32, P]),
+        "oq_row_dot_mx": (F32, [P, P, P, I32, P]),
+        "oq_blob_layout_mx": (None, [I32, I32, P]),
+        "oq_expert_f": (I32, [P, I32, I32, I32, I32, I32, P, P, P, P, P, P, P, P]),
+        "oq_moe_forward_f": (I32, [I32, I32, I32, I32, I32, I32, I32, I32, I32, P, P, P, P, P, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -173,10 +180,14 @@ def unpack(src, n: int, bits: int) -> np.ndarray:
     return out
 
 
-def blob_layout(H: int, I: int, bits: int, group: int = 0) -> dict:
-    """Section offsets of an expert blob; group > 0: group-scaled scales."""
+def blob_layout(H: int, I: int, bits: int, group: int = 0, fmt: int = 0) -> dict:
+    """Section offsets of an expert blob; group > 0: group-scaled scales;
+    fmt = 1: MXFP4 (4-bit codes, one E8M0 byte per 32 codes of a row)."""
     off = np.zeros(7, np.uint64)
-    lib().oq_blob_layout_g(H, I, bits, group, _p(off))
+    if fmt == 1:
+        lib().oq_blob_layout_mx(H, I, _p(off))
+    else:
+        lib().oq_blob_layout_g(H, I, bits, group, _p(off))
     keys = ("gate", "up", "down", "s_gate", "s_up", "s_down", "total")
     return {k: int(v) for k, v in zip(keys, off)}
 
@@ -202,6 +213,34 @@ def row_dot_g(w, q, d, gs, group: int) -> np.float32:
     return np.float32(lib().oq_row_dot_g(_p(w), _p(q), _p(d), n, _p(gs), int(group)))
 
 
+def e2m1(code: int) -> np.float32:
+    """Value of a 4-bit E2M1 code."""
+    return np.float32(lib().oq_e2m1(int(code)))
+
+
+def e8m0(x: int) -> np.float32:
+    """Value of an E8M0 scale byte (NaN for 255)."""
+    return np.float32(lib().oq_e8m0(int(x)))
+
+
+def unpack_mx(src, n: int) -> np.ndarray:
+    """Twice the E2M1 values of the n codes of an MXFP4 row, as int8."""
+    src = _c(src, np.uint8)
+    assert src.size * 2 >= n
+    out = np.empty(n, np.int8)
+    lib().oq_unpack_mx(_p(src), n, _p(out))
+    return out
+
+
+def row_dot_mx(t, q, d, x) -> np.float32:
+    """Row dot of an MXFP4 row (t from unpack_mx) with a Q8_0 vector; x the
+    row's E8M0 bytes, one per 32 codes."""
+    t, q, d, x = _c(t, np.int8), _c(q, np.int8), _c(d, np.float32), _c(x, np.uint8)
+    n = t.size
+    assert q.size == n and d.size == n // 32 and x.size == n // 32
+    return np.float32(lib().oq_row_dot_mx(_p(t), _p(q), _p(d), n, _p(x)))
+
+
 def router_logit(x, w) -> np.float32:
     x, w = _c(x, np.float32), _c(w, np.float32)
     return np.float32(lib().oq_router_logit(_p(x), _p(w), x.size))
@@ -220,14 +259,14 @@ def select(logits, bias, K: int, rsf: float, norm: int = 1):
     return idx, w, sig
 
 
-def expert(blob, H: int, I: int, bits: int, qx, dx, group: int = 0) -> dict:
+def expert(blob, H: int, I: int, bits: int, qx, dx, group: int = 0, fmt: int = 0) -> dict:
     """One SwiGLU expert on one token; returns y and the intermediates."""
     blob = _c(blob, np.uint8)
     qx, dx = _c(qx, np.int8), _c(dx, np.float32)
     out = {"y": np.empty(H, np.float32), "g": np.empty(I, np.float32), "u": np.empty(I, np.float32),
            "h": np.empty(I, np.float32), "qh": np.empty(I, np.int8), "dh": np.empty(I // 32, np.float32)}
-    rc = lib().oq_expert_g(_p(blob), H, I, bits, int(group), _p(qx), _p(dx), _p(out["y"]), _p(out["g"]),
-                           _p(out["u"]), _p(out["h"]), _p(out["qh"]), _p(out["dh"]))
+    rc = lib().oq_expert_f(_p(blob), H, I, bits, int(group), int(fmt), _p(qx), _p(dx), _p(out["y"]),
+                           _p(out["g"]), _p(out["u"]), _p(out["h"]), _p(out["qh"]), _p(out["dh"]))
     _check(rc, "expert")
     return out
 
@@ -261,9 +300,9 @@ def forward(spec, x, idx, w, blobs, shared_blob, parallel: bool = False):
     ptrs = (ctypes.c_void_p * spec.n_experts)(*[None if b is None else b.ctypes.data for b in keep])
     sh = None if shared_blob is None else _c(shared_blob, np.uint8)
     out = np.empty((S, spec.hidden), np.float32)
-    rc = lib(parallel).oq_moe_forward_g(spec.hidden, spec.inter, spec.n_experts, spec.top_k, spec.n_shared,
-                                spec.wbits, int(getattr(spec, "group", 0)), S, _p(x), _p(idx), _p(w), ptrs,
-                                _p(sh), _p(out))
+    rc = lib(parallel).oq_moe_forward_f(spec.hidden, spec.inter, spec.n_experts, spec.top_k, spec.n_shared,
+                                        spec.wbits, int(getattr(spec, "group", 0)), int(getattr(spec, "fmt", 0)), S,
+                                        _p(x), _p(idx), _p(w), ptrs, _p(sh), _p(out))
     _check(rc, "forward")
     return out
 

@@ -27,6 +27,11 @@
  *  [GS64]    JustVugg/colibri (topgit.dev), "Get started" and "Other
  *            supported models": the group-scaled int4 containers (one scale
  *            per 64 weights of a row, "int4-g64"), preferred to per-row int4.
+ *  [MXFP4]   JustVugg/colibri (topgit.dev), "Other supported models": models
+ *            whose routed experts are streamed in their checkpoints' native
+ *            4-bit floating-point format, MXFP4, without conversion.  The
+ *            format itself is the OCP Microscaling (MX) specification's:
+ *            E2M1 elements, one E8M0 power-of-two scale per 32 elements.
  */
 #include <math.h>
 #include <stdint.h>
@@ -227,6 +232,70 @@ float oq_row_dot_g(const int8_t *w, const int8_t *q, const float *d, int n, cons
     return acc;
 }
 
+/* MXFP4 blobs [MXFP4]: code sections of 4 bits per weight, then one E8M0
+ * byte per 32 codes of a row, row-major: gate and up [I][H / 32], down
+ * [H][I / 32]; each section 256-byte aligned. */
+void oq_blob_layout_mx(int H, int I, uint64_t off[7]) {
+    uint64_t gate = (uint64_t)I * (uint64_t)H / 2u;
+    uint64_t down = (uint64_t)H * (uint64_t)I / 2u;
+    uint64_t sgu = (uint64_t)I * (uint64_t)(H / 32), sd = (uint64_t)H * (uint64_t)(I / 32);
+    off[0] = 0;
+    off[1] = al256(off[0] + gate);
+    off[2] = al256(off[1] + gate);
+    off[3] = al256(off[2] + down);
+    off[4] = al256(off[3] + sgu);
+    off[5] = al256(off[4] + sgu);
+    off[6] = al256(off[5] + sd);
+}
+
+/* ------------------------------------------------------------------------
+ * MXFP4 elements [MXFP4].  An E2M1 code c (4 bits) has sign s = bit 3,
+ * exponent field e = bits 2-1 and mantissa bit m = bit 0; its value is
+ * (-1)^s * (m / 2) when e == 0 (zero or the subnormal 0.5) and
+ * (-1)^s * (1 + m / 2) * 2^(e - 1) otherwise: magnitudes 0, 0.5, 1, 1.5,
+ * 2, 3, 4, 6.  An E8M0 byte x scales by 2^(x - 127); x = 255 is NaN.
+ * Twice an E2M1 value is an integer in [-12, 12]; the unpacking below
+ * returns that integer so that block sums stay exact integers.
+ * Row layout (reading: the element order of checkpoints that store MXFP4
+ * two codes per byte): byte j of a row holds element 2j in bits 0-3 and
+ * element 2j + 1 in bits 4-7.
+ * ---------------------------------------------------------------------- */
+float oq_e2m1(int code) {
+    int s = (code >> 3) & 1, e = (code >> 1) & 3, m = code & 1;
+    float mag = e == 0 ? 0.5f * (float)m : (1.0f + 0.5f * (float)m) * ldexpf(1.0f, e - 1);
+    return s ? -mag : mag;
+}
+
+float oq_e8m0(int x) {
+    if (x == 255) return NAN;
+    return ldexpf(1.0f, x - 127);
+}
+
+void oq_unpack_mx(const uint8_t *src, int n, int8_t *out) {
+    for (int j = 0; j < n; ++j) {
+        int byte = src[j / 2];
+        int code = (j % 2 == 0) ? (byte & 0xF) : (byte >> 4);
+        out[j] = (int8_t)(2.0f * oq_e2m1(code));
+    }
+}
+
+/* Row dot of an MXFP4 row (t = twice the element values, from
+ * oq_unpack_mx) with a Q8_0 vector.  Block b's weights are
+ * 2^(x_b - 127) * t_j / 2, so its term is d_b * 2^(x_b - 128) * isum_b with
+ * isum_b = sum_j t_j q_j exact.  Reading for the order (that of the
+ * group-scaled rows): the block's multiplier is the binary32 product
+ * d_b * (e8m0(x_b) / 2) (the halving exact), then
+ *   acc = 0; for b ascending: acc = fmaf(multiplier_b, isum_b, acc)
+ * and no scale after the chain. */
+float oq_row_dot_mx(const int8_t *t, const int8_t *q, const float *d, int n, const uint8_t *x) {
+    float acc = 0.0f;
+    for (int b = 0; b < n / 32; ++b) {
+        float m = d[b] * (oq_e8m0(x[b]) * 0.5f);
+        acc = fmaf(m, (float)oq_block_isum(t + 32 * b, q + 32 * b), acc);
+    }
+    return acc;
+}
+
 /* ------------------------------------------------------------------------
  * Router logit  [README "What's implemented" and [ROUTER]: logits of the
  * hidden state against the router gate].  logit = sum_h x_h * w_h in
@@ -314,11 +383,19 @@ int oq_select(const float *logit, const float *bias, int E, int K, float rsf, in
  * Reading: the down projection consumes Q8_0(h) like every other integer
  * dot in the layer.  Optional debug outputs may be NULL.
  * ---------------------------------------------------------------------- */
-int oq_expert_g(const uint8_t *blob, int H, int I, int bits, int group, const int8_t *qx, const float *dx,
-                float *y, float *g_out, float *u_out, float *h_out, int8_t *qh_out, float *dh_out) {
+/* fmt = 0: integer codes of `bits` bits with per-row (group = 0) or
+ * group scales; fmt = 1: MXFP4 (bits 4, group 0: one E8M0 scale per 32
+ * codes is part of the format). */
+int oq_expert_f(const uint8_t *blob, int H, int I, int bits, int group, int fmt, const int8_t *qx,
+                const float *dx, float *y, float *g_out, float *u_out, float *h_out, int8_t *qh_out,
+                float *dh_out) {
     if (group != 0 && (group % 32 != 0 || H % group != 0 || I % group != 0)) return OQ_EINVAL;
+    if (fmt != 0 && (fmt != 1 || bits != 4 || group != 0)) return OQ_EINVAL;
     uint64_t off[7];
-    oq_blob_layout_g(H, I, bits, group, off);
+    if (fmt == 1)
+        oq_blob_layout_mx(H, I, off);
+    else
+        oq_blob_layout_g(H, I, bits, group, off);
     int n = H > I ? H : I;
     int8_t *row = (int8_t *)malloc((size_t)n);
     float *g = (float *)malloc(sizeof(float) * (size_t)I);
@@ -330,22 +407,41 @@ int oq_expert_g(const uint8_t *blob, int H, int I, int bits, int group, const in
         free(row); free(g); free(u); free(h); free(qh); free(dh);
         return OQ_ENOMEM;
     }
-    const float *s_g = (const float *)(blob + off[3]);
-    const float *s_u = (const float *)(blob + off[4]);
-    const float *s_d = (const float *)(blob + off[5]);
     uint64_t hrow = (uint64_t)H * (uint64_t)bits / 8u, irow = (uint64_t)I * (uint64_t)bits / 8u;
-    int hg = group ? H / group : 0, ig = group ? I / group : 0;
-    for (int i = 0; i < I; ++i) {
-        oq_unpack(blob + off[0] + (uint64_t)i * hrow, H, bits, row);
-        g[i] = group ? oq_row_dot_g(row, qx, dx, H, s_g + (size_t)i * hg, group) : oq_row_dot(row, qx, dx, H, s_g[i]);
-        oq_unpack(blob + off[1] + (uint64_t)i * hrow, H, bits, row);
-        u[i] = group ? oq_row_dot_g(row, qx, dx, H, s_u + (size_t)i * hg, group) : oq_row_dot(row, qx, dx, H, s_u[i]);
-        h[i] = oq_swiglu(g[i], u[i]);
-    }
-    oq_q8_0(h, I, qh, dh);
-    for (int r = 0; r < H; ++r) {
-        oq_unpack(blob + off[2] + (uint64_t)r * irow, I, bits, row);
-        y[r] = group ? oq_row_dot_g(row, qh, dh, I, s_d + (size_t)r * ig, group) : oq_row_dot(row, qh, dh, I, s_d[r]);
+    if (fmt == 1) {
+        const uint8_t *x_g = blob + off[3], *x_u = blob + off[4], *x_d = blob + off[5];
+        for (int i = 0; i < I; ++i) {
+            oq_unpack_mx(blob + off[0] + (uint64_t)i * hrow, H, row);
+            g[i] = oq_row_dot_mx(row, qx, dx, H, x_g + (size_t)i * (H / 32));
+            oq_unpack_mx(blob + off[1] + (uint64_t)i * hrow, H, row);
+            u[i] = oq_row_dot_mx(row, qx, dx, H, x_u + (size_t)i * (H / 32));
+            h[i] = oq_swiglu(g[i], u[i]);
+        }
+        oq_q8_0(h, I, qh, dh);
+        for (int r = 0; r < H; ++r) {
+            oq_unpack_mx(blob + off[2] + (uint64_t)r * irow, I, row);
+            y[r] = oq_row_dot_mx(row, qh, dh, I, x_d + (size_t)r * (I / 32));
+        }
+    } else {
+        const float *s_g = (const float *)(blob + off[3]);
+        const float *s_u = (const float *)(blob + off[4]);
+        const float *s_d = (const float *)(blob + off[5]);
+        int hg = group ? H / group : 0, ig = group ? I / group : 0;
+        for (int i = 0; i < I; ++i) {
+            oq_unpack(blob + off[0] + (uint64_t)i * hrow, H, bits, row);
+            g[i] = group ? oq_row_dot_g(row, qx, dx, H, s_g + (size_t)i * hg, group)
+                         : oq_row_dot(row, qx, dx, H, s_g[i]);
+            oq_unpack(blob + off[1] + (uint64_t)i * hrow, H, bits, row);
+            u[i] = group ? oq_row_dot_g(row, qx, dx, H, s_u + (size_t)i * hg, group)
+                         : oq_row_dot(row, qx, dx, H, s_u[i]);
+            h[i] = oq_swiglu(g[i], u[i]);
+        }
+        oq_q8_0(h, I, qh, dh);
+        for (int r = 0; r < H; ++r) {
+            oq_unpack(blob + off[2] + (uint64_t)r * irow, I, bits, row);
+            y[r] = group ? oq_row_dot_g(row, qh, dh, I, s_d + (size_t)r * ig, group)
+                         : oq_row_dot(row, qh, dh, I, s_d[r]);
+        }
     }
     if (g_out) memcpy(g_out, g, sizeof(float) * (size_t)I);
     if (u_out) memcpy(u_out, u, sizeof(float) * (size_t)I);
@@ -354,6 +450,11 @@ int oq_expert_g(const uint8_t *blob, int H, int I, int bits, int group, const in
     if (dh_out) memcpy(dh_out, dh, sizeof(float) * (size_t)(I / 32));
     free(row); free(g); free(u); free(h); free(qh); free(dh);
     return OQ_OK;
+}
+
+int oq_expert_g(const uint8_t *blob, int H, int I, int bits, int group, const int8_t *qx, const float *dx,
+                float *y, float *g_out, float *u_out, float *h_out, int8_t *qh_out, float *dh_out) {
+    return oq_expert_f(blob, H, I, bits, group, 0, qx, dx, y, g_out, u_out, h_out, qh_out, dh_out);
 }
 
 int oq_expert(const uint8_t *blob, int H, int I, int bits, const int8_t *qx, const float *dx,
@@ -424,7 +525,7 @@ int oq_moe_route(int H, int E, int K, float rsf, int norm, int S, const float *x
  * blobs[e] == NULL marks expert e as not resident.
  * ---------------------------------------------------------------------- */
 /* One token of oq_moe_forward_g: out_t[r] for r < H (inputs validated). */
-static int forward_token(int H, int I, int K, int n_shared, int bits, int group, const float *x_t,
+static int forward_token(int H, int I, int K, int n_shared, int bits, int group, int fmt, const float *x_t,
                          const int32_t *idx_t, const float *w_t, const uint8_t *const *blobs,
                          const uint8_t *shared_blob, float *out_t) {
     int8_t *qx = (int8_t *)malloc((size_t)H);
@@ -434,10 +535,10 @@ static int forward_token(int H, int I, int K, int n_shared, int bits, int group,
     int rc = (qx && dx && y && ysh) ? OQ_OK : OQ_ENOMEM;
     if (rc == OQ_OK) oq_q8_0(x_t, H, qx, dx);
     for (int k = 0; k < K && rc == OQ_OK; ++k)
-        rc = oq_expert_g(blobs[idx_t[k]], H, I, bits, group, qx, dx, y + (size_t)k * H, NULL, NULL, NULL, NULL,
-                         NULL);
+        rc = oq_expert_f(blobs[idx_t[k]], H, I, bits, group, fmt, qx, dx, y + (size_t)k * H, NULL, NULL, NULL,
+                         NULL, NULL);
     if (rc == OQ_OK && n_shared)
-        rc = oq_expert_g(shared_blob, H, I, bits, group, qx, dx, ysh, NULL, NULL, NULL, NULL, NULL);
+        rc = oq_expert_f(shared_blob, H, I, bits, group, fmt, qx, dx, ysh, NULL, NULL, NULL, NULL, NULL);
     for (int r = 0; r < H && rc == OQ_OK; ++r) {
         float acc = 0.0f;
         for (int k = 0; k < K; ++k) acc = fmaf(w_t[k], y[(size_t)k * H + r], acc);
@@ -447,11 +548,12 @@ static int forward_token(int H, int I, int K, int n_shared, int bits, int group,
     return rc;
 }
 
-int oq_moe_forward_g(int H, int I, int E, int K, int n_shared, int bits, int group, int S, const float *x,
-                     const int32_t *idx, const float *w, const uint8_t *const *blobs,
+int oq_moe_forward_f(int H, int I, int E, int K, int n_shared, int bits, int group, int fmt, int S,
+                     const float *x, const int32_t *idx, const float *w, const uint8_t *const *blobs,
                      const uint8_t *shared_blob, float *out) {
     if (!dims_ok(H, I, E, K, n_shared, bits) || S < 0) return OQ_EINVAL;
     if (group != 0 && (group % 32 != 0 || H % group != 0 || I % group != 0)) return OQ_EINVAL;
+    if (fmt != 0 && (fmt != 1 || bits != 4 || group != 0)) return OQ_EINVAL;
     if (n_shared && !shared_blob) return OQ_ENOTRESIDENT;
     if (!all_finite(x, (size_t)S * (size_t)H) || !all_finite(w, (size_t)S * (size_t)K))
         return OQ_ENONFINITE;
@@ -470,7 +572,7 @@ int oq_moe_forward_g(int H, int I, int E, int K, int n_shared, int bits, int gro
 #pragma omp parallel for schedule(dynamic, 1)
 #endif
     for (int t = 0; t < S; ++t) {
-        int r = forward_token(H, I, K, n_shared, bits, group, x + (size_t)t * H, idx + (size_t)t * K,
+        int r = forward_token(H, I, K, n_shared, bits, group, fmt, x + (size_t)t * H, idx + (size_t)t * K,
                               w + (size_t)t * K, blobs, shared_blob, out + (size_t)t * H);
         if (r != OQ_OK) {
 #ifdef _OPENMP
@@ -480,6 +582,12 @@ int oq_moe_forward_g(int H, int I, int E, int K, int n_shared, int bits, int gro
         }
     }
     return rc;
+}
+
+int oq_moe_forward_g(int H, int I, int E, int K, int n_shared, int bits, int group, int S, const float *x,
+                     const int32_t *idx, const float *w, const uint8_t *const *blobs,
+                     const uint8_t *shared_blob, float *out) {
+    return oq_moe_forward_f(H, I, E, K, n_shared, bits, group, 0, S, x, idx, w, blobs, shared_blob, out);
 }
 
 int oq_moe_forward(int H, int I, int E, int K, int n_shared, int bits, int S, const float *x,

@@ -109,10 +109,11 @@ class LayerSpec:
     routed_scaling_factor: float = 2.5
     norm_topk_prob: int = 1
     group: int = 0          # 0: one scale per row; 64: one per 64 codes of a row
+    fmt: int = 0            # 0: integer codes; 1: MXFP4 (E2M1 codes, one E8M0 scale per 32)
 
     @property
     def blob_bytes(self) -> int:
-        return blob_layout(self.hidden, self.inter, self.wbits, self.group)["total"]
+        return blob_layout(self.hidden, self.inter, self.wbits, self.group, self.fmt)["total"]
 
 
 TINY = LayerSpec(hidden=256, inter=128, n_experts=16, top_k=2, n_shared=1, wbits=4)
@@ -121,9 +122,11 @@ GLM_INT8 = dataclasses.replace(GLM, wbits=8)
 GLM_INT2 = dataclasses.replace(GLM, wbits=2)
 TINY_GS64 = dataclasses.replace(TINY, group=64)
 GLM_GS64 = dataclasses.replace(GLM, group=64)
+TINY_MX = dataclasses.replace(TINY, fmt=1)
+GLM_MX = dataclasses.replace(GLM, fmt=1)
 
 
-def blob_layout(hidden: int, inter: int, bits: int, group: int = 0) -> dict:
+def blob_layout(hidden: int, inter: int, bits: int, group: int = 0, fmt: int = 0) -> dict:
     """Byte offsets of the six sections of one expert blob.
 
     [gate codes: inter rows x hidden*bits/8][up codes: same][down codes:
@@ -138,6 +141,9 @@ def blob_layout(hidden: int, inter: int, bits: int, group: int = 0) -> dict:
     down = hidden * inter * bits // 8
     sgu = 4 * inter * (hidden // group if group else 1)
     sd = 4 * hidden * (inter // group if group else 1)
+    if fmt == 1:   # MXFP4: 4-bit codes, one E8M0 byte per 32 codes of a row
+        gate, down = inter * hidden // 2, hidden * inter // 2
+        sgu, sd = inter * (hidden // 32), hidden * (inter // 32)
     off = {"gate": 0}
     off["up"] = a(gate)
     off["down"] = a(off["up"] + gate)
@@ -237,6 +243,107 @@ def gaussian_expert(seed: int, layer: int, expert: int, spec: LayerSpec, sigma: 
     blob = assemble_blob(H, I, b, parts["gate"], parts["up"], parts["down"],
                          parts["s_gate"], parts["s_up"], parts["s_down"], G)
     return blob, parts
+
+
+# --------------------------------------------------------------------------
+# MXFP4 experts (offline quantiser and packer; data preparation only)
+# --------------------------------------------------------------------------
+# magnitudes of the E2M1 codes 0..7 (code 8 + m is the negative of code m)
+E2M1_MAG = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
+
+
+def e2m1_round(x: np.ndarray) -> np.ndarray:
+    """E2M1 code (0..15) nearest to each value (ties to the even magnitude
+    index), saturating at +-6."""
+    x = np.asarray(x, np.float64)
+    mag = np.asarray(E2M1_MAG)
+    a = np.minimum(np.abs(x), 6.0)
+    d = np.abs(a[..., None] - mag)
+    best = np.argmin(d + 1e-12 * (np.arange(8) % 2), axis=-1)
+    return (best + np.where((x < 0) & (best > 0), 8, 0)).astype(np.uint8)
+
+
+def quantize_mx_rows(w: np.ndarray):
+    """MXFP4 quantiser (OCP Microscaling): per 32 values of a row, the shared
+    exponent floor(log2(amax)) - 2 (6 = 1.5 * 2^2 is the largest element),
+    E8M0 byte = exponent + 127 clamped to [0, 254] (0 when amax is 0), codes
+    the nearest E2M1 of w / 2^exponent.  Returns (codes [rows, cols] 0..15,
+    scale bytes [rows, cols / 32])."""
+    w = np.asarray(w, np.float64)
+    rows, cols = w.shape
+    wb = w.reshape(rows, cols // 32, 32)
+    amax = np.abs(wb).max(-1)
+    with np.errstate(divide="ignore"):
+        e = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 2, -127)
+    xb = np.clip(e + 127, 0, 254).astype(np.uint8)
+    codes = e2m1_round(wb / np.exp2(xb.astype(np.float64) - 127)[..., None])
+    return codes.reshape(rows, cols), xb
+
+
+def pack_mx(codes: np.ndarray) -> np.ndarray:
+    """Two E2M1 codes per byte: element 2j in bits 0-3, element 2j+1 in bits 4-7."""
+    c = np.asarray(codes, np.uint8)
+    return (c[:, 0::2] & 0x0F) | ((c[:, 1::2] & 0x0F) << 4)
+
+
+def assemble_mx_blob(hidden, inter, gate_codes, up_codes, down_codes, x_gate, x_up, x_down):
+    lay = blob_layout(hidden, inter, 4, 0, 1)
+    blob = np.zeros(lay["total"], dtype=np.uint8)
+    for name, arr in (("gate", pack_mx(gate_codes)), ("up", pack_mx(up_codes)), ("down", pack_mx(down_codes)),
+                      ("s_gate", x_gate), ("s_up", x_up), ("s_down", x_down)):
+        b = np.ascontiguousarray(arr, dtype=np.uint8).ravel()
+        blob[lay[name]:lay[name] + b.size] = b
+    return blob
+
+
+def mx_expert(seed: int, layer: int, expert: int, spec: LayerSpec, sigma: float = 0.02):
+    """MXFP4 expert: w ~ N(0, sigma) quantised by quantize_mx_rows.
+    Returns (blob, parts) with the codes and scale bytes of each matrix."""
+    H, I = spec.hidden, spec.inter
+    parts = {}
+    for m, (name, rows, cols) in enumerate((("gate", I, H), ("up", I, H), ("down", H, I))):
+        key = stream_key(seed, K_WEIGHT, layer, expert, m)
+        w = (normal(key, rows * cols) * sigma).reshape(rows, cols)
+        parts[name], parts["s_" + name] = quantize_mx_rows(w)
+    blob = assemble_mx_blob(H, I, parts["gate"], parts["up"], parts["down"],
+                            parts["s_gate"], parts["s_up"], parts["s_down"])
+    return blob, parts
+
+
+def mx_cdf_table(ratio: float = 2.56) -> np.ndarray:
+    """65536-entry table mapping a 16-bit uniform to an E2M1 code, distributed
+    as the nearest E2M1 of z * ratio for z ~ N(0, 1) (ratio: the weights'
+    standard deviation over the block scale; 0.02 / 2^-7 by default)."""
+    mag = np.asarray(E2M1_MAG)
+    mids = (mag[:-1] + mag[1:]) / 2                     # thresholds between magnitudes
+    # P(|x| < mid_k), x = z * ratio
+    cdf_abs = np.array([math.erf(t / ratio / math.sqrt(2.0)) for t in mids])
+    probs = np.diff(np.concatenate([[0.0], cdf_abs, [1.0]]))   # magnitude 0..7
+    # signed codes: magnitude 0 once (code 0), others split evenly by sign
+    p = np.zeros(16)
+    p[0] = probs[0]
+    p[1:8] = probs[1:] / 2
+    p[9:16] = probs[1:] / 2
+    edges = np.round(np.cumsum(p) * 65536.0).astype(np.int64)
+    u = np.arange(65536)
+    idx = np.searchsorted(edges, u, side="right")
+    return np.minimum(idx, 15).astype(np.uint8)
+
+
+def mx_cdf_expert_into(out_ptr: int, seed: int, layer: int, expert: int, spec: LayerSpec,
+                       threads: int | None = None) -> int:
+    """Writes one GLM-sized MXFP4 blob (codes from mx_cdf_table, E8M0 scale
+    bytes uniform over 119..121) at host address out_ptr; returns its size."""
+    lib = _load()
+    table = mx_cdf_table()
+    keys = (ctypes.c_uint64 * 6)(*[stream_key(seed, K_WEIGHT, layer, expert, m, part, 11)
+                                   for m in range(3) for part in (0, 1)])
+    if threads is None:
+        threads = min(16, os.cpu_count() or 1)
+    n = lib.synth_fill_blob_mx(keys, spec.hidden, spec.inter, table.ctypes.data, 119, 3, out_ptr, threads)
+    if n != spec.blob_bytes:
+        raise RuntimeError("synth_fill_blob_mx rejected the shape")
+    return int(n)
 
 
 # --------------------------------------------------------------------------
@@ -356,6 +463,10 @@ def _load():
         lib.synth_fill_blob_cdf_g.argtypes = [
             ctypes.POINTER(ctypes.c_uint64), ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
             ctypes.c_void_p, ctypes.c_float, ctypes.c_float, ctypes.c_void_p, ctypes.c_int]
+        lib.synth_fill_blob_mx.restype = ctypes.c_uint64
+        lib.synth_fill_blob_mx.argtypes = [
+            ctypes.POINTER(ctypes.c_uint64), ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
+            ctypes.c_int, ctypes.c_void_p, ctypes.c_int]
         _lib = lib
     return _lib
 
@@ -403,7 +514,10 @@ def cdf_expert_into(out_ptr: int, seed: int, layer: int, expert: int, spec: Laye
 
 def cdf_expert(seed: int, layer: int, expert: int, spec: LayerSpec, sigma: float = 0.02) -> np.ndarray:
     blob = np.empty(spec.blob_bytes, dtype=np.uint8)
-    cdf_expert_into(blob.ctypes.data, seed, layer, expert, spec, sigma)
+    if spec.fmt == 1:
+        mx_cdf_expert_into(blob.ctypes.data, seed, layer, expert, spec)
+    else:
+        cdf_expert_into(blob.ctypes.data, seed, layer, expert, spec, sigma)
     return blob
 
 
@@ -411,6 +525,8 @@ def expert_blob(seed: int, layer: int, expert: int, spec: LayerSpec) -> np.ndarr
     """The blob of routed expert `expert` (or the shared expert, expert ==
     n_experts) of `layer`, with the recipe chosen by size."""
     if spec.hidden * spec.inter <= 1 << 20:
+        if spec.fmt == 1:
+            return mx_expert(seed, layer, expert, spec)[0]
         return gaussian_expert(seed, layer, expert, spec)[0]
     return cdf_expert(seed, layer, expert, spec)
 
@@ -458,8 +574,10 @@ def shaped_hidden_states(W_r: np.ndarray, target_logits: np.ndarray, seed: int, 
 
 
 def tiny_layer(seed: int = 0, S: int = 4, spec: LayerSpec = TINY, layer: int = 0) -> dict:
-    """All inputs of one small layer (gaussian recipe)."""
-    blobs = [gaussian_expert(seed, layer, e, spec)[0] for e in range(spec.n_experts + spec.n_shared)]
+    """All inputs of one small layer (gaussian recipe; MXFP4 quantiser for
+    spec.fmt == 1)."""
+    make = mx_expert if spec.fmt == 1 else gaussian_expert
+    blobs = [make(seed, layer, e, spec)[0] for e in range(spec.n_experts + spec.n_shared)]
     return {
         "spec": spec,
         "x": hidden_states(seed, layer, S, spec.hidden),

@@ -125,3 +125,53 @@ uint64_t synth_fill_blob_cdf(const uint64_t *keys, int hidden, int inter, int bi
     return synth_fill_blob_cdf_g(keys, hidden, inter, bits, 0, table, scale_nominal, scale_jitter, out,
                                  nthreads);
 }
+
+/*
+ * MXFP4 blob (OCP Microscaling FP4): [gate codes][up codes][down codes]
+ * [gate scales][up scales][down scales], each section 256-byte aligned.
+ * Codes are 4-bit E2M1 codes drawn i.i.d. from a 65536-entry table (16-bit
+ * uniform -> code), two per byte (element 2j in bits 0-3, 2j+1 in bits 4-7);
+ * scales are one E8M0 byte per 32 codes of a row, uniform over
+ * scale_lo .. scale_lo + scale_span - 1.  Returns the bytes written.
+ */
+static void fill_matrix_mx(uint64_t key_codes, uint64_t key_scales, int rows, int cols, const uint8_t *table,
+                           int scale_lo, int scale_span, uint8_t *codes_out, uint8_t *scales_out, int nthreads) {
+    int row_bytes = cols / 2, nb = cols / 32;
+#pragma omp parallel for schedule(static) num_threads(nthreads)
+    for (int r = 0; r < rows; ++r) {
+        uint8_t *o = codes_out + (uint64_t)r * (uint64_t)row_bytes;
+        uint64_t base = (uint64_t)r * (uint64_t)(cols / 4);
+        for (int g = 0; g < cols / 4; ++g) {
+            uint64_t u = stream_at(key_codes, base + (uint64_t)g);
+            uint8_t c0 = table[(u >> 0) & 0xFFFF], c1 = table[(u >> 16) & 0xFFFF];
+            uint8_t c2 = table[(u >> 32) & 0xFFFF], c3 = table[(u >> 48) & 0xFFFF];
+            o[2 * g] = (uint8_t)((c0 & 0xF) | ((c1 & 0xF) << 4));
+            o[2 * g + 1] = (uint8_t)((c2 & 0xF) | ((c3 & 0xF) << 4));
+        }
+        for (int b = 0; b < nb; ++b) {
+            uint64_t us = stream_at(key_scales, (uint64_t)r * (uint64_t)nb + (uint64_t)b);
+            scales_out[(uint64_t)r * (uint64_t)nb + (uint64_t)b] = (uint8_t)(scale_lo + (int)(us % (uint64_t)scale_span));
+        }
+    }
+}
+
+uint64_t synth_fill_blob_mx(const uint64_t *keys, int hidden, int inter, const uint8_t *table, int scale_lo,
+                            int scale_span, uint8_t *out, int nthreads) {
+    if (hidden <= 0 || inter <= 0 || hidden % 32 || inter % 32 || hidden > 32768 || inter > 32768) return 0;
+    if (scale_lo < 0 || scale_span < 1 || scale_lo + scale_span > 255) return 0;
+    uint64_t gate_bytes = (uint64_t)inter * (uint64_t)(hidden / 2);
+    uint64_t down_bytes = (uint64_t)hidden * (uint64_t)(inter / 2);
+    uint64_t sgu = (uint64_t)inter * (uint64_t)(hidden / 32), sd = (uint64_t)hidden * (uint64_t)(inter / 32);
+    uint64_t off_g = 0;
+    uint64_t off_u = align256(off_g + gate_bytes);
+    uint64_t off_d = align256(off_u + gate_bytes);
+    uint64_t off_sg = align256(off_d + down_bytes);
+    uint64_t off_su = align256(off_sg + sgu);
+    uint64_t off_sd = align256(off_su + sgu);
+    uint64_t total = align256(off_sd + sd);
+    memset(out, 0, total);
+    fill_matrix_mx(keys[0], keys[1], inter, hidden, table, scale_lo, scale_span, out + off_g, out + off_sg, nthreads);
+    fill_matrix_mx(keys[2], keys[3], inter, hidden, table, scale_lo, scale_span, out + off_u, out + off_su, nthreads);
+    fill_matrix_mx(keys[4], keys[5], hidden, inter, table, scale_lo, scale_span, out + off_d, out + off_sd, nthreads);
+    return total;
+}
