@@ -61,6 +61,8 @@ def parse():
     ap.add_argument("--tier-bits", type=int, choices=(4, 2), default=4, help="tiered: expert width")
     ap.add_argument("--group-size", type=int, choices=(0, 64), default=0,
                     help="decode / prefill: 64 = group-scaled int4 experts (one scale per 64 codes of a row)")
+    ap.add_argument("--wformat", choices=("int", "mxfp4"), default="int",
+                    help="decode: mxfp4 = MXFP4 experts (E2M1 codes, one E8M0 scale per 32 codes of a row)")
     ap.add_argument("--tier-layers", type=int, default=75, help="tiered: layers streamed")
     ap.add_argument("--host-layers", type=int, default=8,
                     help="tiered: distinct layers of expert bytes in pinned host memory (reused cyclically)")
@@ -134,6 +136,10 @@ def main():
         if verify:
             raise SystemExit("--group-size applies to int4 experts (decode, prefill)")
         spec = synth.GLM_GS64
+    if args.wformat == "mxfp4":
+        if verify or args.group_size:
+            raise SystemExit("--wformat mxfp4 applies to the decode workload without --group-size")
+        spec = synth.GLM_MX
     S = 4 if verify else 1  # tokens per step
     dims = q.make_dims(spec)
     H, E = spec.hidden, spec.n_experts
@@ -153,7 +159,10 @@ def main():
             done[l % 2].synchronize()
         base = buf.data_ptr()
         for e in range(nblob):
-            synth.cdf_expert_into(base + e * bb, args.seed, l, e, spec)
+            if spec.fmt == 1:
+                synth.mx_cdf_expert_into(base + e * bb, args.seed, l, e, spec)
+            else:
+                synth.cdf_expert_into(base + e * bb, args.seed, l, e, spec)
         dev = torch.empty(nblob * bb, dtype=torch.uint8, device="cuda")
         with torch.cuda.stream(copy_stream):
             dev.copy_(buf, non_blocking=True)
@@ -249,9 +258,11 @@ def main():
         # only
         in_router = args.path == "layer" and S <= 2 and 32 * H * spec.wbits // 8 <= 128 * 1024
         gu_units = n_units - (spec.n_shared if in_router else 0)
-        dom, dom_kernel = "gateup", "k_gateup<%d,%d%s>" % (spec.wbits, min(S, 4), ",gs64" if spec.group else "")
+        dom, dom_kernel = "gateup", "k_gateup<%d,%d%s>" % (spec.wbits, min(S, 4),
+                                                            ",gs64" if spec.group else (",mxfp4" if spec.fmt else ""))
         n_scales = H // spec.group if spec.group else 1   # per gate / up row
-        dom_bytes = gu_units * (2 * spec.inter * H * spec.wbits // 8 + 2 * spec.inter * 4 * n_scales)
+        scale_bytes = 2 * spec.inter * (H // 32) if spec.fmt == 1 else 2 * spec.inter * 4 * n_scales
+        dom_bytes = gu_units * (2 * spec.inter * H * spec.wbits // 8 + scale_bytes)
     dom_us = kernel_us[dom]
     achieved = dom_bytes / (dom_us * 1e-6) / 1e9
     layer_gbs = lay_bytes / (ms_per_step * 1e-3) / 1e9
@@ -266,7 +277,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "i8xi8->i32,f32" if verify else "i8xi4->i32,f32",
+        "dtype": "i8xi8->i32,f32" if verify else ("i8xe2m1->i32,f32" if spec.fmt == 1 else "i8xi4->i32,f32"),
         "data": "synthetic (seeded; GLM-5.2-shaped random-code experts)",
         "config": {
             "workload": ("GLM-5.2-shaped speculative-verify batch, 4 tokens/step routed jointly (about 40% "
@@ -276,7 +287,8 @@ def main():
                         ("GLM-5.2-shaped MoE decode layer, 1 token/step: hidden 6144, expert inter 2048, "
                          "256 routed experts top-8 + 1 shared, "
                          + ("int4 weights with one scale per 64 codes of a row (21.2 MB/expert), " if spec.group
-                            else "int4 per-row-scaled weights (18.9 MB/expert), ")
+                            else "MXFP4 weights: E2M1 codes, one E8M0 scale per 32 codes of a row (20.05 MB/expert), "
+                            if spec.fmt == 1 else "int4 per-row-scaled weights (18.9 MB/expert), ")
                          + f"Q8_0 activations, fp32 router gate; {L} layers resident in HBM, step s uses layer "
                          f"s mod {L}"),
             "layers_resident": L, "resident_gb": round(L * nblob * bb / 1e9, 1),
@@ -299,7 +311,7 @@ def main():
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(args, spec, xs_host, layers, L, S)
     add_measured_roof(res, q, "hbm")
-    if args.workload == "decode" and not args.group_size and not args.no_prefill_record:
+    if args.workload == "decode" and not args.group_size and args.wformat == "int" and not args.no_prefill_record:
         # the prefill half of the metric, on the same GPU in the same run
         del layers, graph, xs, ws, idx, wts, out
         torch.cuda.synchronize()

@@ -55,6 +55,12 @@ extern "C" {
 #define COLI_ENOTRESIDENT (-4)  /* a routed expert's blob pointer is NULL */
 #define COLI_EWORKSPACE (-5)    /* workspace too small for this call */
 
+/* coli_moe_dims.wformat */
+#define COLI_WFMT_INT 0         /* integer codes of wbits bits, per-row or group f32 scales */
+#define COLI_WFMT_MXFP4 1       /* MXFP4: E2M1 codes, one E8M0 scale per 32 codes of a row */
+/* the debug hooks' `bits` value selecting MXFP4 codes */
+#define COLI_MXFP4 (-4)
+
 /* Layer shape.  All fields are preconditions checked on every call. */
 typedef struct coli_moe_dims {
     int32_t hidden;               /* H: multiple of 256 (router order) */
@@ -69,6 +75,10 @@ typedef struct coli_moe_dims {
                                      dividing H and I: one f32 scale per group_size consecutive codes
                                      of a row (JustVugg/colibri, "Get started" / "Other supported
                                      models": the group-scaled "int4-g64" containers) */
+    int32_t wformat;              /* COLI_WFMT_INT, or COLI_WFMT_MXFP4 (JustVugg/colibri, "Other supported
+                                     models": routed experts streamed in their checkpoints' native MXFP4,
+                                     without conversion), which needs wbits = 4, group_size = 0 and I a
+                                     multiple of 128 */
 } coli_moe_dims;
 
 /*
@@ -86,6 +96,14 @@ typedef struct coli_moe_dims {
  * GLM-5.2 shape with G = 64, int4).  A row's dot product is then
  * acc = fmaf(d_b * s[row][32 b / G], isum_b, acc) over blocks b ascending
  * (d_b the activation block scale), with no scale after the chain.
+ * With wformat = COLI_WFMT_MXFP4 (OCP Microscaling FP4) the code sections
+ * hold 4-bit E2M1 codes, byte j of a row = element 2j (bits 0-3) | element
+ * 2j + 1 (bits 4-7), and the three scale sections one E8M0 byte per 32
+ * codes of a row, row-major: gate and up [I][H/32], down [H][I/32]
+ * (20 054 016 bytes at the GLM-5.2 shape).  With t_j = 2 v_j (an integer in
+ * [-12, 12]) and x_b the block's scale byte, a row's dot product is
+ * acc = fmaf(d_b * 2^(x_b - 128), sum_j t_j q_j, acc) over blocks b ascending,
+ * the multiplier one binary32 product, no scale after the chain.
  * Returns 0 when dims are invalid.
  */
 size_t coli_moe_expert_bytes(const coli_moe_dims *dims);
@@ -252,7 +270,9 @@ int coli_moe_timing_read(int32_t kind, double *total_ms, int64_t *launches);
 int coli_moe_debug_force_path(int32_t path);
 
 /* Unpacks n_rows packed rows of `cols` codes (device src, row stride
- * cols*bits/8 bytes) into device int8 out [n_rows, cols]. */
+ * cols*bits/8 bytes) into device int8 out [n_rows, cols].  bits = COLI_MXFP4
+ * reads MXFP4 rows (4 bits a code) and gives twice each E2M1 value; the
+ * block dots then use those doubled values. */
 int coli_moe_debug_unpack(int32_t bits, int32_t n_rows, int32_t cols, const void *src,
                           int8_t *out, void *stream);
 

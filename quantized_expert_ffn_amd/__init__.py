@@ -29,6 +29,7 @@ import torch  # noqa: E402,F401
 _lib = ctypes.CDLL(LIB_PATH)
 
 COLI_OK, COLI_EINVAL, COLI_ENONFINITE, COLI_EHIP, COLI_ENOTRESIDENT, COLI_EWORKSPACE = 0, -1, -2, -3, -4, -5
+COLI_WFMT_INT, COLI_WFMT_MXFP4, COLI_MXFP4 = 0, 1, -4
 
 EXPORTS = (
     "coli_moe_expert_bytes", "coli_moe_workspace_bytes", "coli_moe_route", "coli_moe_forward",
@@ -50,7 +51,7 @@ class coli_moe_dims(ctypes.Structure):
         ("hidden", ctypes.c_int32), ("inter", ctypes.c_int32), ("n_experts", ctypes.c_int32),
         ("top_k", ctypes.c_int32), ("n_shared", ctypes.c_int32), ("wbits", ctypes.c_int32),
         ("routed_scaling_factor", ctypes.c_float), ("norm_topk_prob", ctypes.c_int32),
-        ("group_size", ctypes.c_int32),
+        ("group_size", ctypes.c_int32), ("wformat", ctypes.c_int32),
     ]
 
 
@@ -99,7 +100,7 @@ def make_dims(spec) -> coli_moe_dims:
     """coli_moe_dims from any object with the dims' field names."""
     return coli_moe_dims(int(spec.hidden), int(spec.inter), int(spec.n_experts), int(spec.top_k),
                          int(spec.n_shared), int(spec.wbits), float(spec.routed_scaling_factor),
-                         int(spec.norm_topk_prob), int(getattr(spec, "group", 0)))
+                         int(spec.norm_topk_prob), int(getattr(spec, "group", 0)), int(getattr(spec, "fmt", 0)))
 
 
 def _dims(d):

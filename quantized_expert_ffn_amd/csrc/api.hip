@@ -69,8 +69,15 @@ int check_dims(const coli_moe_dims *d) {
     if (g != 0 && (g < 32 || g > 512 || (g & (g - 1)) != 0 || d->hidden % g != 0 || d->inter % g != 0))
         return fail(COLI_EINVAL, "group_size=%d: must be 0 or a power of two in 32..512 dividing hidden and inter", g);
     if (g != 0 && d->wbits != 4) return fail(COLI_EINVAL, "group_size=%d needs wbits=4 (group-scaled int4)", g);
+    if (d->wformat != COLI_WFMT_INT && d->wformat != COLI_WFMT_MXFP4)
+        return fail(COLI_EINVAL, "wformat=%d: must be COLI_WFMT_INT (0) or COLI_WFMT_MXFP4 (1)", d->wformat);
+    if (d->wformat == COLI_WFMT_MXFP4 && (d->wbits != 4 || g != 0 || d->inter % 128 != 0))
+        return fail(COLI_EINVAL, "MXFP4 experts need wbits=4, group_size=0 and inter a multiple of 128 "
+                                 "(wbits=%d, group_size=%d, inter=%d)", d->wbits, g, d->inter);
     return COLI_OK;
 }
+
+bool is_mx(const coli_moe_dims *d) { return d->wformat == COLI_WFMT_MXFP4; }
 
 // Hidden states, router gate, outputs and blobs are read and written with
 // 16-byte vector accesses.
@@ -103,31 +110,36 @@ int g_force_path = 0;
 // Batches of more than GROUPED_MIN_S - 1 tokens take the grouped kernels.
 constexpr int GROUPED_MIN_S = 9;
 
-// The grouped kernels take per-row scales or groups of 64; other group sizes
-// run the multi-launch kernels at every batch size.
-bool use_grouped(int S, int group) {
-    return (group == 0 || group == 64) && (g_force_path == 3 || (g_force_path == 0 && S >= GROUPED_MIN_S));
+// The grouped kernels take integer codes with per-row scales or groups of
+// 64; other group sizes and MXFP4 run the multi-launch kernels at every
+// batch size.
+bool use_grouped(int S, int group, bool mx) {
+    return !mx && (group == 0 || group == 64) && (g_force_path == 3 || (g_force_path == 0 && S >= GROUPED_MIN_S));
 }
+
+// The group size the kernels see: MXFP4 has one (E8M0) scale per 32 codes.
+int kernel_group(const coli_moe_dims *d) { return is_mx(d) ? 32 : d->group_size; }
 
 // LDS of the kernels a forward of S tokens launches.
 size_t forward_lds(const coli_moe_dims *d, int S) {
-    if (use_grouped(S, d->group_size)) return coli::pf_group_smem(S, d->top_k, d->n_experts);
-    return coli::forward_smem_max(S, d->hidden, d->inter, d->n_experts, d->top_k, d->n_shared, d->group_size);
+    if (use_grouped(S, d->group_size, is_mx(d))) return coli::pf_group_smem(S, d->top_k, d->n_experts);
+    return coli::forward_smem_max(S, d->hidden, d->inter, d->n_experts, d->top_k, d->n_shared, kernel_group(d));
 }
 
 // A forced kernel family that does not take the call's weights.
 int forced_path_refused(const coli_moe_dims *d) {
-    if (d->group_size && g_force_path == 2)
-        return fail(COLI_EINVAL, "the persistent kernel takes per-row scales only");
+    if ((d->group_size || is_mx(d)) && g_force_path == 2)
+        return fail(COLI_EINVAL, "the persistent kernel takes integer codes with per-row scales only");
     if (d->group_size && d->group_size != 64 && g_force_path == 3)
         return fail(COLI_EINVAL, "the grouped kernels take per-row scales or groups of 64 (group_size=%d)",
                     d->group_size);
+    if (is_mx(d) && g_force_path == 3) return fail(COLI_EINVAL, "the grouped kernels take integer codes only");
     return COLI_OK;
 }
 
 // The persistent kernel takes small batches whose experts are all resident.
 bool persistent_fits(const coli_moe_dims *d, int S, bool pending) {
-    if (pending || S > 8 || d->group_size) return false;
+    if (pending || S > 8 || d->group_size || is_mx(d)) return false;
     return coli::layer_smem(S, d->hidden, d->inter, d->n_experts, d->top_k, d->n_shared) <= 160 * 1024;
 }
 
@@ -201,7 +213,8 @@ FwdArgs fwd_args(const coli_moe_dims *d, int S, const float *x, const int32_t *i
     a.E = d->n_experts;
     a.K = d->top_k;
     a.n_shared = d->n_shared;
-    a.group = d->group_size;
+    a.group = kernel_group(d);
+    a.mx = is_mx(d) ? 1 : 0;
     return a;
 }
 
@@ -254,7 +267,7 @@ int forward_launches(FwdArgs &a, int bits, bool any_pending, void *pending_ready
         timing_after(KK_QUANT_X, st);
         if (e != hipSuccess) return hip_fail(e, "Q8_0(x) launch");
     }
-    if (use_grouped(a.S, a.group)) {
+    if (use_grouped(a.S, a.group, a.mx != 0)) {
         // grouped kernels: the unit table and tiles, then gate/up and down as
         // int8 matrix-core products per (rows, tile), then the combine.  They
         // do not split resident from pending experts: all wait for the copies.
@@ -324,7 +337,7 @@ extern "C" {
 
 size_t coli_moe_expert_bytes(const coli_moe_dims *d) {
     if (check_dims(d) != COLI_OK) return 0;
-    return blob_layout(d->hidden, d->inter, d->wbits, d->group_size).total;
+    return blob_layout(d->hidden, d->inter, d->wbits, d->group_size, is_mx(d)).total;
 }
 
 size_t coli_moe_workspace_bytes(const coli_moe_dims *d, int32_t max_tokens) {
@@ -447,7 +460,7 @@ int layer_launches(const coli_moe_dims *d, int32_t S, const float *x, const floa
             return fail(COLI_EINVAL, "shape needs %zu bytes of LDS per workgroup (> 160 KiB)", smem);
         // up to ROUTE_FUSE_MAX tokens: one router launch also selects the
         // routing and writes the call's unit table, which the expert kernels read
-        if (S <= ROUTE_FUSE_MAX && !use_grouped(S, d->group_size)) {
+        if (S <= ROUTE_FUSE_MAX && !use_grouped(S, d->group_size, is_mx(d))) {
             RouteArgs r;
             std::memset(&r, 0, sizeof r);
             r.x = x;
@@ -473,7 +486,8 @@ int layer_launches(const coli_moe_dims *d, int32_t S, const float *x, const floa
             r.hs = reinterpret_cast<float *>(w8 + L.hs);
             r.I = d->inter;
             r.bits = d->wbits;
-            r.group = d->group_size;
+            r.group = kernel_group(d);
+            r.mx = is_mx(d) ? 1 : 0;
             // the shared expert's gate/up half tiles run in the router launch
             // when they are short enough to finish beside it (one pass over at
             // most 128 KiB of rows per workgroup) and their LDS fits there
@@ -673,8 +687,8 @@ int coli_moe_debug_force_path(int32_t path) {
 
 int coli_moe_debug_unpack(int32_t bits, int32_t n_rows, int32_t cols, const void *src, int8_t *out,
                           void *stream) {
-    if ((bits != 8 && bits != 4 && bits != 2) || n_rows < 0 || cols <= 0 || cols % 32 || !src || !out ||
-        (uint64_t)n_rows * (uint64_t)cols * (uint64_t)bits / 8 >= (1ull << 31))
+    if ((bits != 8 && bits != 4 && bits != 2 && bits != COLI_MXFP4) || n_rows < 0 || cols <= 0 || cols % 32 || !src || !out ||
+        (uint64_t)n_rows * (uint64_t)cols * (uint64_t)(bits == COLI_MXFP4 ? 4 : bits) / 8 >= (1ull << 31))
         return fail(COLI_EINVAL, "debug_unpack: bad arguments");
     if (n_rows == 0) return COLI_OK;
     int rc = check_device();
@@ -685,8 +699,8 @@ int coli_moe_debug_unpack(int32_t bits, int32_t n_rows, int32_t cols, const void
 
 int coli_moe_debug_block_dots(int32_t bits, int32_t n_rows, int32_t cols, const void *src,
                               const int8_t *q, int32_t *out, void *stream) {
-    if ((bits != 8 && bits != 4 && bits != 2) || n_rows < 0 || cols <= 0 || cols % 32 || !src || !q || !out ||
-        (uint64_t)n_rows * (uint64_t)cols * (uint64_t)bits / 8 >= (1ull << 31))
+    if ((bits != 8 && bits != 4 && bits != 2 && bits != COLI_MXFP4) || n_rows < 0 || cols <= 0 || cols % 32 || !src || !q || !out ||
+        (uint64_t)n_rows * (uint64_t)cols * (uint64_t)(bits == COLI_MXFP4 ? 4 : bits) / 8 >= (1ull << 31))
         return fail(COLI_EINVAL, "debug_block_dots: bad arguments");
     if (n_rows == 0) return COLI_OK;
     int rc = check_device();

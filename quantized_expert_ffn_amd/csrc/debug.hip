@@ -42,6 +42,50 @@ __global__ __launch_bounds__(64) void k_debug_block_dots(const uint8_t *__restri
     }
 }
 
+// MXFP4 rows (16 bytes per block): twice the E2M1 value of each code, and
+// the exact block dots, through the forward kernels' decode.
+__global__ __launch_bounds__(64) void k_debug_unpack_mx(const uint8_t *__restrict__ src,
+                                                        int8_t *__restrict__ out, int cols) {
+    const int r = blockIdx.x;
+    const int nb = cols / 32;
+    const uint32_t row_bytes = (uint32_t)cols / 2;
+    const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(src, row_bytes * gridDim.x);
+    for (int b = threadIdx.x; b < nb; b += 64) {
+        const BlockBits<4> w = load_block<4>(rsrc, (uint32_t)r * row_bytes, b);
+        const uint32_t ws[4] = {w.w.x, w.w.y, w.w.z, w.w.w};
+        int8_t *o = out + (size_t)r * cols + 32 * b;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t lo = mx_twice(ws[k]), hi = mx_twice(ws[k] >> 4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                o[8 * k + 2 * i] = (int8_t)(lo >> (8 * i));
+                o[8 * k + 2 * i + 1] = (int8_t)(hi >> (8 * i));
+            }
+        }
+    }
+}
+
+__global__ __launch_bounds__(64) void k_debug_block_dots_mx(const uint8_t *__restrict__ src,
+                                                            const int8_t *__restrict__ q,
+                                                            int32_t *__restrict__ out, int cols) {
+    const int r = blockIdx.x;
+    const int nb = cols / 32;
+    const uint32_t row_bytes = (uint32_t)cols / 2;
+    const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(src, row_bytes * gridDim.x);
+    for (int b = threadIdx.x; b < nb; b += 64) {
+        const BlockBits<4> w = load_block<4>(rsrc, (uint32_t)r * row_bytes, b);
+        int32_t a[8], ae[4], ao[4];
+        for (int k = 0; k < 8; ++k) {
+            const int8_t *p = q + 32 * b + 4 * k;
+            a[k] = (int32_t)((uint32_t)(uint8_t)p[0] | ((uint32_t)(uint8_t)p[1] << 8) |
+                             ((uint32_t)(uint8_t)p[2] << 16) | ((uint32_t)(uint8_t)p[3] << 24));
+        }
+        mx_split_act(a, ae, ao);
+        out[(size_t)r * nb + b] = block_dot_mx(w.w, ae, ao);
+    }
+}
+
 __global__ void k_debug_expf(const float *__restrict__ x, float *__restrict__ y, int64_t n) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n) y[i] = exp_f32(x[i]);
@@ -67,7 +111,8 @@ __global__ __launch_bounds__(64) void k_debug_q8_0(const float *__restrict__ v,
 hipError_t launch_debug_unpack(int bits, int rows, int cols, const void *src, int8_t *out,
                                hipStream_t st) {
     const uint8_t *s = static_cast<const uint8_t *>(src);
-    if (bits == 8) hipLaunchKernelGGL(k_debug_unpack<8>, dim3(rows), dim3(64), 0, st, s, out, cols);
+    if (bits == COLI_MXFP4) hipLaunchKernelGGL(k_debug_unpack_mx, dim3(rows), dim3(64), 0, st, s, out, cols);
+    else if (bits == 8) hipLaunchKernelGGL(k_debug_unpack<8>, dim3(rows), dim3(64), 0, st, s, out, cols);
     else if (bits == 4) hipLaunchKernelGGL(k_debug_unpack<4>, dim3(rows), dim3(64), 0, st, s, out, cols);
     else hipLaunchKernelGGL(k_debug_unpack<2>, dim3(rows), dim3(64), 0, st, s, out, cols);
     return hipGetLastError();
@@ -76,7 +121,9 @@ hipError_t launch_debug_unpack(int bits, int rows, int cols, const void *src, in
 hipError_t launch_debug_block_dots(int bits, int rows, int cols, const void *src, const int8_t *q,
                                    int32_t *out, hipStream_t st) {
     const uint8_t *s = static_cast<const uint8_t *>(src);
-    if (bits == 8)
+    if (bits == COLI_MXFP4)
+        hipLaunchKernelGGL(k_debug_block_dots_mx, dim3(rows), dim3(64), 0, st, s, q, out, cols);
+    else if (bits == 8)
         hipLaunchKernelGGL(k_debug_block_dots<8>, dim3(rows), dim3(64), 0, st, s, q, out, cols);
     else if (bits == 4)
         hipLaunchKernelGGL(k_debug_block_dots<4>, dim3(rows), dim3(64), 0, st, s, q, out, cols);

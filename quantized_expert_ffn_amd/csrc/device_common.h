@@ -219,6 +219,55 @@ __device__ __forceinline__ int32_t block_dot_int8(u32x4 w0, u32x4 w1, const int3
     return s;
 }
 
+// MXFP4 (OCP Microscaling FP4): a block's 32 E2M1 codes in 16 bytes, byte j
+// = element 2j (bits 0-3) | element 2j + 1 (bits 4-7); code bits: sign (3),
+// exponent (2-1), mantissa (0); magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6.
+// Twice a value is an integer in [-12, 12], so the block dot
+// isum = sum_j 2 v_j q_j is an exact int32 and feeds v_dot4.
+//
+// Bits 0-3 of each byte of x as four signed bytes 2 v: the magnitude index
+// (bits 0-2) looks up 2|v| and -2|v| in two 8-byte tables (v_perm), and a
+// third v_perm takes each byte from the table its sign bit names.
+__device__ __forceinline__ uint32_t mx_twice(uint32_t x) {
+    const uint32_t m = x & 0x07070707u;
+    const uint32_t pos = __builtin_amdgcn_perm(0x0C080604u, 0x03020100u, m);   // 0 1 2 3 | 4 6 8 12
+    const uint32_t neg = __builtin_amdgcn_perm(0xF4F8FAFCu, 0xFDFEFF00u, m);   // -(the same)
+    const uint32_t sel = ((x >> 1) & 0x04040404u) | 0x03020100u;               // byte i: i, or 4 + i if negative
+    return __builtin_amdgcn_perm(neg, pos, sel);
+}
+
+// Activation codes of a block (8 words, elements in order) rearranged to
+// pair with the MXFP4 bytes: even[k] holds elements 8k, 8k+2, 8k+4, 8k+6 and
+// odd[k] elements 8k+1, 8k+3, 8k+5, 8k+7 (the low and high nibbles of weight
+// word k).
+__device__ __forceinline__ void mx_split_act(const int32_t a[8], int32_t even[4], int32_t odd[4]) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        even[k] = (int32_t)__builtin_amdgcn_perm((uint32_t)a[2 * k + 1], (uint32_t)a[2 * k], 0x06040200u);
+        odd[k] = (int32_t)__builtin_amdgcn_perm((uint32_t)a[2 * k + 1], (uint32_t)a[2 * k], 0x07050301u);
+    }
+}
+
+// isum = sum_j 2 v_j q_j of one MXFP4 block against activations split by
+// mx_split_act.
+__device__ __forceinline__ int32_t block_dot_mx(u32x4 w, const int32_t even[4], const int32_t odd[4]) {
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+    int32_t s = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        s = __builtin_amdgcn_sdot4((int)mx_twice(ws[k]), even[k], s, false);
+        s = __builtin_amdgcn_sdot4((int)mx_twice(ws[k] >> 4), odd[k], s, false);
+    }
+    return s;
+}
+
+// Half the value of an E8M0 scale byte, 2^(x - 128), as binary32 (exact:
+// 2^-128 and 2^-127 are subnormal numbers); x = 255 (NaN in E8M0) gives NaN.
+__device__ __forceinline__ float e8m0_half(uint32_t x) {
+    const uint32_t bits = x >= 2u ? (x - 1u) << 23 : 0x00200000u << x;
+    return __uint_as_float(x == 255u ? 0x7FC00000u : bits);
+}
+
 // Raw bytes of one block of a packed row, as loaded by one lane.
 template <int BITS>
 struct BlockBits;
@@ -348,13 +397,14 @@ struct BlobLayout {
 
 // Expert blob sections.  group = 0: one f32 scale per row; group > 0: one
 // per `group` codes of a row, row-major ([I][H / group] for gate and up,
-// [H][I / group] for down).
-__host__ __device__ inline BlobLayout blob_layout(int H, int I, int bits, int group = 0) {
+// [H][I / group] for down).  mx: MXFP4, 4-bit codes and one E8M0 byte per 32
+// codes of a row, row-major ([I][H / 32], [I][H / 32], [H][I / 32]).
+__host__ __device__ inline BlobLayout blob_layout(int H, int I, int bits, int group = 0, bool mx = false) {
     BlobLayout L;
     const size_t gate = (size_t)I * (size_t)H * (size_t)bits / 8;
     const size_t down = (size_t)H * (size_t)I * (size_t)bits / 8;
-    const size_t sgu = 4 * (size_t)I * (size_t)(group ? H / group : 1);
-    const size_t sd = 4 * (size_t)H * (size_t)(group ? I / group : 1);
+    const size_t sgu = mx ? (size_t)I * (size_t)(H / 32) : 4 * (size_t)I * (size_t)(group ? H / group : 1);
+    const size_t sd = mx ? (size_t)H * (size_t)(I / 32) : 4 * (size_t)H * (size_t)(group ? I / group : 1);
     L.gate = 0;
     L.up = align256(L.gate + gate);
     L.down = align256(L.up + gate);

@@ -63,8 +63,11 @@ __host__ __device__ inline DownTilePlan down_tile_plan(size_t base, int S, int K
 
 // One down tile.  COHERENT: Q8_0(h) was written earlier in the same launch
 // by other workgroups, so it is read with device-scope loads.
-template <int BITS, bool ONE_TOKEN, bool COHERENT, bool GROUPED = false>
+// MX: MXFP4 down rows (4-bit E2M1 codes, one E8M0 byte per block; GROUPED
+// with group 32).
+template <int BITS, bool ONE_TOKEN, bool COHERENT, bool GROUPED = false, bool MX = false>
 struct DownTile {
+    static_assert(!MX || (BITS == 4 && GROUPED), "MXFP4 rows are 4-bit codes with a scale per block");
     static constexpr int UB = DownRowsBatch<BITS>::UB;
     const FwdArgs &a;
     uint8_t *smem;
@@ -89,7 +92,7 @@ struct DownTile {
         dpitch = round_up(nbi, 64);
         m16 = fast_div_magic(a.I / 16);
         mnb = fast_div_magic(nbi);
-        BL = blob_layout(a.H, a.I, BITS, GROUPED ? a.group : 0);
+        BL = blob_layout(a.H, a.I, BITS, GROUPED && !MX ? a.group : 0, MX);
         irow = (size_t)a.I * BITS / 8;
         ro = BL.down + (size_t)(rt * DR_ROWS + uniform(threadIdx.x >> 6) * DR_RPW) * irow;
     }
@@ -147,7 +150,14 @@ struct DownTile {
         float *dst = gsl + wave * UB * DR_RPW * ngr;
         const int rw0 = rt * DR_ROWS + wave * DR_RPW;
         const int n = (u1 - u0) * DR_RPW * ngr;
-        if ((ngr & 3) == 0) {
+        if (MX) {
+            // one E8M0 byte per block, converted to 2^(x - 128)
+            for (int i = lane; i < n; i += 64) {
+                const int ur = i / ngr, g = i - ur * ngr;
+                const uint8_t *blob = ublob[u0 + ur / DR_RPW];
+                dst[i] = blob ? e8m0_half(blob[BL.s_down + (size_t)(rw0 + ur % DR_RPW) * ngr + g]) : 0.0f;
+            }
+        } else if ((ngr & 3) == 0) {
             const int wpr = ngr / 4, nw = n / 4;
             for (int w0 = 0; w0 < nw; w0 += 64) {
                 const int w = w0 + lane;
@@ -269,10 +279,19 @@ struct DownTile {
                     for (int q = q0; q < q1; ++q) {
                         int32_t av[8] = {0, 0, 0, 0, 0, 0, 0, 0};
                         if (act) load_act(qh_l + (size_t)(q - pbase) * qpitch, b, av);
+                        if constexpr (MX) {
+                            int32_t ae[4], ao[4];
+                            mx_split_act(av, ae, ao);
 #pragma unroll
-                        for (int r = 0; r < DR_RPW; ++r)
-                            isum[(r * mpb + (q - pbase)) * ISUM_PITCH + lane] =
-                                (act && live) ? block_dot(wv[ui][r], av) : 0;
+                            for (int r = 0; r < DR_RPW; ++r)
+                                isum[(r * mpb + (q - pbase)) * ISUM_PITCH + lane] =
+                                    (act && live) ? block_dot_mx(wv[ui][r].w, ae, ao) : 0;
+                        } else {
+#pragma unroll
+                            for (int r = 0; r < DR_RPW; ++r)
+                                isum[(r * mpb + (q - pbase)) * ISUM_PITCH + lane] =
+                                    (act && live) ? block_dot(wv[ui][r], av) : 0;
+                        }
                     }
                 }
             }

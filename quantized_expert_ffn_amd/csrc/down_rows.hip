@@ -32,7 +32,7 @@ __host__ __device__ inline DownRowsPlan down_rows_plan(int S, int K, int E, int 
 }
 
 // ONE_TOKEN: S == 1, so every unit has exactly one pair.
-template <int BITS, bool ONE_TOKEN, bool GROUPED>
+template <int BITS, bool ONE_TOKEN, bool GROUPED, bool MX = false>
 __global__ __launch_bounds__(DR_T) __attribute__((amdgpu_waves_per_eu(3))) void k_down_rows(const FwdArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int tid = threadIdx.x;
@@ -69,7 +69,8 @@ __global__ __launch_bounds__(DR_T) __attribute__((amdgpu_waves_per_eu(3))) void 
         __syncthreads();
     }
     if (tid < n_units && ublob[tid] == nullptr) raise_status(a.status, ST_NOTRESIDENT);
-    DownTile<BITS, ONE_TOKEN, false, GROUPED> tile(a, smem, D.tile, uoff, pairs, ublob, w_l, n_units, blockIdx.x);
+    DownTile<BITS, ONE_TOKEN, false, GROUPED, MX> tile(a, smem, D.tile, uoff, pairs, ublob, w_l, n_units,
+                                                      blockIdx.x);
     tile.run(false);
 }
 
@@ -86,6 +87,7 @@ hipError_t launch_down_rows(const FwdArgs &a, int bits, hipStream_t st) {
         return launch(kern, grid, dim3(DR_T), smem, st, a);
     };
     const bool one = a.S == 1;
+    if (a.mx) return one ? go(k_down_rows<4, true, true, true>) : go(k_down_rows<4, false, true, true>);
     if (a.group) return one ? go(k_down_rows<4, true, true>) : go(k_down_rows<4, false, true>);
     if (bits == 8) return one ? go(k_down_rows<8, true, false>) : go(k_down_rows<8, false, false>);
     if (bits == 4) return one ? go(k_down_rows<4, true, false>) : go(k_down_rows<4, false, false>);

@@ -56,7 +56,7 @@ __device__ __forceinline__ const uint8_t *load_unit_table(const uint8_t *units, 
 // grid row 0 first quantise its h, one 32-row block each, to Q8_0(h) in the
 // shared expert's pair slots).  Otherwise every workgroup builds the unit
 // table from topk_idx and takes unit blockIdx.y.
-template <int BITS, int NT, bool TABLE, bool GROUPED>
+template <int BITS, int NT, bool TABLE, bool GROUPED, bool MX = false>
 __global__ __launch_bounds__(256) void k_gateup(const FwdArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
@@ -150,14 +150,14 @@ __global__ __launch_bounds__(256) void k_gateup(const FwdArgs a) {
         }
         __syncthreads();
     };
-    gateup_unit<BITS, NT, GROUPED>(blob, H, I, a.group, blockIdx.x * 32, pairs + p0, np, smem, L, L.total, a.qh,
-                                   a.dh, stage);
+    gateup_unit<BITS, NT, GROUPED, MX>(blob, H, I, a.group, blockIdx.x * 32, pairs + p0, np, smem, L, L.total, a.qh,
+                                       a.dh, stage);
 }
 
 // Down projection: 64 rows of one unit per workgroup, y written to the
 // pair's slot of the workspace (the combine kernel reads it after this
 // kernel has finished, so no cross-workgroup signalling is needed).
-template <int BITS, int NT, bool GROUPED>
+template <int BITS, int NT, bool GROUPED, bool MX = false>
 __global__ __launch_bounds__(256) void k_down(const FwdArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
@@ -185,7 +185,7 @@ __global__ __launch_bounds__(256) void k_down(const FwdArgs a) {
     int8_t *vq = reinterpret_cast<int8_t *>(smem + L.vq);
     float *vd = reinterpret_cast<float *>(smem + L.vd);
     int32_t *isum_wave = reinterpret_cast<int32_t *>(smem + L.isum) + wave * NT * ROWS_PER_WAVE * ISUM_PITCH;
-    const BlobLayout BL = blob_layout(H, I, BITS, GROUPED ? a.group : 0);
+    const BlobLayout BL = blob_layout(H, I, BITS, GROUPED && !MX ? a.group : 0, MX);
     const size_t row_bytes = (size_t)I * BITS / 8;
     const int rw = r0 + wave * ROWS_PER_WAVE;
     const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(blob, (uint32_t)BL.total);
@@ -197,7 +197,7 @@ __global__ __launch_bounds__(256) void k_down(const FwdArgs a) {
     G.lgb = GROUPED ? group_lgb(a.group) : -1;
     if (GROUPED) {
         G.rsrc = rsrc;
-        G.row_stride = (uint32_t)(4 * (I / a.group));
+        G.row_stride = MX ? (uint32_t)(I / 32) : (uint32_t)(4 * (I / a.group));
         G.base = (uint32_t)(BL.s_down + (size_t)rw * G.row_stride);
         G.lds = reinterpret_cast<float *>(smem + L.total) + wave * ROWS_PER_WAVE * (64 >> G.lgb);
     }
@@ -219,7 +219,7 @@ __global__ __launch_bounds__(256) void k_down(const FwdArgs a) {
         BlockBits<BITS> cur[ROWS_PER_WAVE];
         prime_rows<BITS, ROWS_PER_WAVE>(rsrc, rowoff, nb, cur);
         const float acc =
-            stream_rows<BITS, NT, ROWS_PER_WAVE, GROUPED>(rsrc, rowoff, nb, ng, vq, vd, isum_wave, I, stage, cur, G);
+            stream_rows<BITS, NT, ROWS_PER_WAVE, GROUPED, MX>(rsrc, rowoff, nb, ng, vq, vd, isum_wave, I, stage, cur, G);
         if (cvec < ng) {
             const int slot = pairs[p0 + g0 + cvec];
             a.Y[(size_t)slot * H + rw + crow] = GROUPED ? acc : acc * s_down[rw + crow];
@@ -285,33 +285,35 @@ static hipError_t launch_dyn(F kern, dim3 grid, size_t smem, hipStream_t st, con
     return launch(kern, grid, dim3(256), smem, st, a);
 }
 
-template <int BITS, bool TABLE, bool GROUPED = false>
+template <int BITS, bool TABLE, bool GROUPED = false, bool MX = false>
 static hipError_t gateup_bits(const FwdArgs &a, hipStream_t st) {
     const int P = a.S * a.K;
     const int umax = std::min(P, a.E) + a.n_shared - (TABLE ? a.shared_done : 0);
     const dim3 grid(a.I / 32, umax);
     const int nt = pick_nt(a.S);
     const size_t smem = smem_plan(a.S, a.K, a.E, nt, a.H).total + groups_lds_bytes(a.group, 4);
-    if (nt == 1) return launch_dyn(k_gateup<BITS, 1, TABLE, GROUPED>, grid, smem, st, a);
-    if (nt == 2) return launch_dyn(k_gateup<BITS, 2, TABLE, GROUPED>, grid, smem, st, a);
-    return launch_dyn(k_gateup<BITS, 4, TABLE, GROUPED>, grid, smem, st, a);
+    if (nt == 1) return launch_dyn(k_gateup<BITS, 1, TABLE, GROUPED, MX>, grid, smem, st, a);
+    if (nt == 2) return launch_dyn(k_gateup<BITS, 2, TABLE, GROUPED, MX>, grid, smem, st, a);
+    return launch_dyn(k_gateup<BITS, 4, TABLE, GROUPED, MX>, grid, smem, st, a);
 }
 
-template <int BITS, bool GROUPED = false>
+template <int BITS, bool GROUPED = false, bool MX = false>
 static hipError_t down_bits(const FwdArgs &a, hipStream_t st) {
     const int P = a.S * a.K;
     const int umax = std::min(P, a.E) + a.n_shared;
     const dim3 grid(a.H / 64, umax);
     const int nt = pick_nt(a.S);
     const size_t smem = smem_plan(a.S, a.K, a.E, nt, a.I).total + groups_lds_bytes(a.group, 4);
-    if (nt == 1) return launch_dyn(k_down<BITS, 1, GROUPED>, grid, smem, st, a);
-    if (nt == 2) return launch_dyn(k_down<BITS, 2, GROUPED>, grid, smem, st, a);
-    return launch_dyn(k_down<BITS, 4, GROUPED>, grid, smem, st, a);
+    if (nt == 1) return launch_dyn(k_down<BITS, 1, GROUPED, MX>, grid, smem, st, a);
+    if (nt == 2) return launch_dyn(k_down<BITS, 2, GROUPED, MX>, grid, smem, st, a);
+    return launch_dyn(k_down<BITS, 4, GROUPED, MX>, grid, smem, st, a);
 }
 
-// Group-scaled weights are int4 only (the dims check refuses the others).
+// Group-scaled and MXFP4 weights are 4-bit codes only (the dims check
+// refuses the others).
 hipError_t launch_gateup(const FwdArgs &a, int bits, hipStream_t st) {
     const bool table = a.units != nullptr;
+    if (a.mx) return table ? gateup_bits<4, true, true, true>(a, st) : gateup_bits<4, false, true, true>(a, st);
     if (a.group) return table ? gateup_bits<4, true, true>(a, st) : gateup_bits<4, false, true>(a, st);
     if (bits == 8) return table ? gateup_bits<8, true>(a, st) : gateup_bits<8, false>(a, st);
     if (bits == 4) return table ? gateup_bits<4, true>(a, st) : gateup_bits<4, false>(a, st);
@@ -323,6 +325,7 @@ hipError_t launch_combine(const FwdArgs &a, hipStream_t st) {
 }
 
 hipError_t launch_down(const FwdArgs &a, int bits, hipStream_t st) {
+    if (a.mx) return down_bits<4, true, true>(a, st);
     if (a.group) return down_bits<4, true>(a, st);
     if (bits == 8) return down_bits<8>(a, st);
     if (bits == 4) return down_bits<4>(a, st);

@@ -21,7 +21,9 @@ namespace coli {
 // to qh / dh at the slot.  256 threads.  GROUPED: the blob has one scale per
 // `group` codes of a row, staged through the groups_lds_bytes(group, 4)
 // bytes of LDS at smem + gs_off.
-template <int BITS, int NT, bool GROUPED, typename Stage>
+// MX: the blob is MXFP4 (4-bit E2M1 codes, one E8M0 byte per block; group
+// is then 32).
+template <int BITS, int NT, bool GROUPED, bool MX = false, typename Stage>
 __device__ __forceinline__ void gateup_unit(const uint8_t *blob, int H, int I, int group, int i0, const int *slots,
                                             int np, uint8_t *smem, const SmemPlan &L, size_t gs_off,
                                             int8_t *__restrict__ qh, float *__restrict__ dh, Stage stage) {
@@ -30,7 +32,7 @@ __device__ __forceinline__ void gateup_unit(const uint8_t *blob, int H, int I, i
     float *vd = reinterpret_cast<float *>(smem + L.vd);
     int32_t *isum_wave = reinterpret_cast<int32_t *>(smem + L.isum) + wave * NT * ROWS_PER_WAVE * ISUM_PITCH;
     float *gu = reinterpret_cast<float *>(smem + L.gu);
-    const BlobLayout BL = blob_layout(H, I, BITS, GROUPED ? group : 0);
+    const BlobLayout BL = blob_layout(H, I, BITS, GROUPED && !MX ? group : 0, MX);
     const size_t row_bytes = (size_t)H * BITS / 8;
     const int half = wave & 1;            // rows 0-15 or 16-31 of the tile
     const size_t mat = wave < 2 ? BL.gate : BL.up;
@@ -45,7 +47,7 @@ __device__ __forceinline__ void gateup_unit(const uint8_t *blob, int H, int I, i
     G.lgb = GROUPED ? group_lgb(group) : -1;
     if (GROUPED) {
         G.rsrc = rsrc;
-        G.row_stride = (uint32_t)(4 * (H / group));
+        G.row_stride = MX ? (uint32_t)(H / 32) : (uint32_t)(4 * (H / group));
         G.base = (uint32_t)(ssec + (size_t)(i0 + 16 * half) * G.row_stride);
         G.lds = reinterpret_cast<float *>(smem + gs_off) + wave * ROWS_PER_WAVE * (64 >> G.lgb);
     }
@@ -55,7 +57,7 @@ __device__ __forceinline__ void gateup_unit(const uint8_t *blob, int H, int I, i
         const int ng = min(NT, np - g0);
         BlockBits<BITS> cur[ROWS_PER_WAVE];
         prime_rows<BITS, ROWS_PER_WAVE>(rsrc, rowoff, nb, cur);
-        const float acc = stream_rows<BITS, NT, ROWS_PER_WAVE, GROUPED>(rsrc, rowoff, nb, ng, vq, vd, isum_wave, H,
+        const float acc = stream_rows<BITS, NT, ROWS_PER_WAVE, GROUPED, MX>(rsrc, rowoff, nb, ng, vq, vd, isum_wave, H,
                                                                        [&]() { stage(g0, ng); }, cur, G);
         if (cvec < ng)
             gu[cvec * 64 + wave * ROWS_PER_WAVE + crow] = GROUPED ? acc : acc * scale[i0 + 16 * half + crow];
@@ -80,7 +82,7 @@ __device__ __forceinline__ void gateup_unit(const uint8_t *blob, int H, int I, i
 // waves 2-3 the matching up rows; otherwise as gateup_unit (the staging,
 // the block chains and the scales are the same).  Half a Q8_0 block of h:
 // whoever joins two such halves quantises them.  256 threads.
-template <int BITS, int NT, bool GROUPED, typename Stage>
+template <int BITS, int NT, bool GROUPED, bool MX = false, typename Stage>
 __device__ __forceinline__ void gateup_half_f32(const uint8_t *blob, int H, int I, int group, int i0,
                                                 int np, uint8_t *smem, const SmemPlan &L, size_t gs_off,
                                                 float *__restrict__ hs, Stage stage) {
@@ -90,7 +92,7 @@ __device__ __forceinline__ void gateup_half_f32(const uint8_t *blob, int H, int 
     float *vd = reinterpret_cast<float *>(smem + L.vd);
     int32_t *isum_wave = reinterpret_cast<int32_t *>(smem + L.isum) + wave * NT * RPW * ISUM_PITCH;
     float *gu = reinterpret_cast<float *>(smem + L.gu);
-    const BlobLayout BL = blob_layout(H, I, BITS, GROUPED ? group : 0);
+    const BlobLayout BL = blob_layout(H, I, BITS, GROUPED && !MX ? group : 0, MX);
     const size_t row_bytes = (size_t)H * BITS / 8;
     const int r0 = i0 + RPW * (wave & 1);   // this wave's first row
     const size_t mat = wave < 2 ? BL.gate : BL.up;
@@ -104,7 +106,7 @@ __device__ __forceinline__ void gateup_half_f32(const uint8_t *blob, int H, int 
     G.lgb = GROUPED ? group_lgb(group) : -1;
     if (GROUPED) {
         G.rsrc = rsrc;
-        G.row_stride = (uint32_t)(4 * (H / group));
+        G.row_stride = MX ? (uint32_t)(H / 32) : (uint32_t)(4 * (H / group));
         G.base = (uint32_t)(ssec + (size_t)r0 * G.row_stride);
         G.lds = reinterpret_cast<float *>(smem + gs_off) + wave * RPW * (64 >> G.lgb);
     }
@@ -113,7 +115,7 @@ __device__ __forceinline__ void gateup_half_f32(const uint8_t *blob, int H, int 
     const int ng = np;
     BlockBits<BITS> cur[RPW];
     prime_rows<BITS, RPW>(rsrc, rowoff, nb, cur);
-    const float acc = stream_rows<BITS, NT, RPW, GROUPED>(rsrc, rowoff, nb, ng, vq, vd, isum_wave, H,
+    const float acc = stream_rows<BITS, NT, RPW, GROUPED, MX>(rsrc, rowoff, nb, ng, vq, vd, isum_wave, H,
                                                          [&]() { stage(0, ng); }, cur, G);
     // gu[v * 32 + k]: gate rows (k < 16) then up rows of vector v
     if (cvec < ng) gu[cvec * 32 + wave * RPW + crow] = GROUPED ? acc : acc * scale[r0 + crow];

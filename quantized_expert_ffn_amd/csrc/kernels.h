@@ -103,6 +103,7 @@ struct FwdArgs {
     int shared_done;               // 1: the router launch wrote the shared expert's h to hs
     const float *hs;               // [S, I]  the shared expert's h, binary32 (with shared_done)
     int group;                     // 0: per-row scales; else one scale per `group` codes of a row
+    int mx;                        // 1: MXFP4 codes and E8M0 scales (group is then 32)
     uint32_t pend[32];             // bit e: expert e pending
 };
 
@@ -123,7 +124,7 @@ struct RouteArgs {
     uint32_t *sync;
     float *hs;                     // with sg: the shared expert's h [S, I], binary32
     int S, H, E, K, n_shared, norm;
-    int I, bits, group;            // expert shape, code width and scale group (for sg)
+    int I, bits, group, mx;        // expert shape, code width, scale group, MXFP4 (for sg)
     int sg;                        // 1: the launch also runs the shared expert's gate/up tiles
     float rsf;
 };

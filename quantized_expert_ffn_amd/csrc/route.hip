@@ -92,7 +92,7 @@ constexpr int RF_W = 4;
 __host__ __device__ inline int rf_lpw(int S) { return S == 1 ? 2 : RF_W; }
 
 // Shared expert, gate/up rows 16 half .. 16 half + 15, every token; h to hs.
-template <int BITS, int NT, bool GROUPED>
+template <int BITS, int NT, bool GROUPED, bool MX = false>
 __device__ __forceinline__ void shared_gateup_half(const RouteArgs &r, uint8_t *smem, int half) {
     const int tid = threadIdx.x, S = r.S, H = r.H;
     const SmemPlan L = smem_plan(S, r.K, r.E, NT, H);
@@ -107,11 +107,11 @@ __device__ __forceinline__ void shared_gateup_half(const RouteArgs &r, uint8_t *
         }
         __syncthreads();
     };
-    gateup_half_f32<BITS, NT, GROUPED>(uniform_ptr(r.shared), H, r.I, r.group, 16 * half, S, smem, L, L.total, r.hs,
+    gateup_half_f32<BITS, NT, GROUPED, MX>(uniform_ptr(r.shared), H, r.I, r.group, 16 * half, S, smem, L, L.total, r.hs,
                                        stage);
 }
 
-template <int MAXJ, int BITS, int NT, bool GROUPED>
+template <int MAXJ, int BITS, int NT, bool GROUPED, bool MX = false>
 __global__ __launch_bounds__(64 * RF_W) void k_route_fused(const RouteArgs r) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     __shared__ int s_last;
@@ -119,7 +119,7 @@ __global__ __launch_bounds__(64 * RF_W) void k_route_fused(const RouteArgs r) {
     const int E = r.E, K = r.K, S = r.S, H = r.H;
     const int n_sg = r.sg ? r.I / 16 : 0;
     if ((int)blockIdx.x < n_sg) {
-        if (t == 0) shared_gateup_half<BITS, NT, GROUPED>(r, smem, blockIdx.x);
+        if (t == 0) shared_gateup_half<BITS, NT, GROUPED, MX>(r, smem, blockIdx.x);
         return;
     }
     const int bx = (int)blockIdx.x - n_sg;
@@ -297,20 +297,22 @@ size_t route_fused_lds(const RouteArgs &r) {
     return sel > tile ? sel : tile;
 }
 
-template <int MAXJ, int BITS, bool GROUPED = false>
+template <int MAXJ, int BITS, bool GROUPED = false, bool MX = false>
 static hipError_t route_fused_bits(const RouteArgs &r, dim3 grid, size_t smem, hipStream_t st) {
     auto go = [&](auto kern) {
         const hipError_t e = ensure_dyn_smem(reinterpret_cast<const void *>(kern), smem);
         if (e != hipSuccess) return e;
         return launch(kern, grid, dim3(64 * RF_W), smem, st, r);
     };
-    if (route_nt(r.S) == 1) return go(k_route_fused<MAXJ, BITS, 1, GROUPED>);
-    return go(k_route_fused<MAXJ, BITS, 2, GROUPED>);
+    if (route_nt(r.S) == 1) return go(k_route_fused<MAXJ, BITS, 1, GROUPED, MX>);
+    return go(k_route_fused<MAXJ, BITS, 2, GROUPED, MX>);
 }
 
-// Group-scaled weights are int4 only (the dims check refuses the others).
+// Group-scaled and MXFP4 weights are 4-bit codes only (the dims check
+// refuses the others).
 template <int MAXJ>
 static hipError_t route_fused_maxj(const RouteArgs &r, dim3 grid, size_t smem, hipStream_t st) {
+    if (r.mx) return route_fused_bits<MAXJ, 4, true, true>(r, grid, smem, st);
     if (r.group) return route_fused_bits<MAXJ, 4, true>(r, grid, smem, st);
     if (r.bits == 8) return route_fused_bits<MAXJ, 8>(r, grid, smem, st);
     if (r.bits == 2) return route_fused_bits<MAXJ, 2>(r, grid, smem, st);

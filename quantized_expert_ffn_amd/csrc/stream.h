@@ -321,6 +321,39 @@ __device__ __forceinline__ void groups_store(const RowGroups &G, const i32x4 (&g
     }
 }
 
+// MXFP4 rows: one E8M0 byte per block (lgb = 0), row_stride = H / 32 bytes
+// (a multiple of 4), staged the same way as floats 2^(x - 128): the chunk's
+// 64 bytes of a row are 16 dwords, dword w = lane + 64 k of the wave holding
+// bytes 4 p .. 4 p + 3 of row w / 16, p = w % 16, converted on the store.
+template <int RPW>
+__device__ __forceinline__ void groups_load_mx(const RowGroups &G, int c, uint32_t (&gb)[4]) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int w = lane + 64 * k;
+        if (w < RPW * 16) {
+            const int row = w >> 4, p = w & 15;
+            gb[k] = __builtin_amdgcn_raw_buffer_load_b32(G.rsrc, G.base + (uint32_t)row * G.row_stride +
+                                                                     (uint32_t)(64 * c + 4 * p), 0, 0);
+        }
+    }
+}
+
+template <int RPW>
+__device__ __forceinline__ void groups_store_mx(const RowGroups &G, const uint32_t (&gb)[4]) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int w = lane + 64 * k;
+        if (w < RPW * 16) {
+            const uint32_t v = gb[k];
+            reinterpret_cast<f32x4 *>(G.lds)[w] =
+                f32x4{e8m0_half(v & 0xFFu), e8m0_half((v >> 8) & 0xFFu), e8m0_half((v >> 16) & 0xFFu),
+                      e8m0_half(v >> 24)};
+        }
+    }
+}
+
 // Issues the loads of chunk 0 (blocks 0..63) of this wave's RPW rows.
 template <int BITS, int RPW>
 __device__ __forceinline__ void prime_rows(__amdgpu_buffer_rsrc_t rsrc, const uint32_t rowoff[RPW],
@@ -343,12 +376,14 @@ __device__ __forceinline__ void prime_rows(__amdgpu_buffer_rsrc_t rsrc, const ui
 // With GROUPED (G.lgb >= 0) the chain of chunk c uses the chunk's
 // group scales, loaded one chunk ahead with the weights and staged in the
 // wave's LDS region G.lds; the row scale is then not applied by the caller.
-template <int BITS, int NT, int RPW, bool GROUPED, typename Stage>
+// MX: the rows are MXFP4 (BITS 4, GROUPED with lgb 0, E8M0 scale bytes).
+template <int BITS, int NT, int RPW, bool GROUPED, bool MX = false, typename Stage>
 __device__ __forceinline__ float stream_rows(__amdgpu_buffer_rsrc_t rsrc, const uint32_t rowoff[RPW],
                                              int nb, int ng, const int8_t *vq, const float *vd,
                                              int32_t *isum_wave, int vlen, Stage stage,
                                              BlockBits<BITS> (&cur)[RPW], const RowGroups &G) {
     static_assert(NT * RPW <= 64, "one chain per lane");
+    static_assert(!MX || (BITS == 4 && GROUPED), "MXFP4 rows are 4-bit codes with a scale per block");
     constexpr bool PREFETCH = BITS < 8;
     const int lane = threadIdx.x & 63;
     const int crow = lane % RPW, cvec = lane / RPW;
@@ -357,9 +392,12 @@ __device__ __forceinline__ float stream_rows(__amdgpu_buffer_rsrc_t rsrc, const 
     float acc = 0.0f;
     const int nchunks = (nb + 63) / 64;
     i32x4 gw[4];
-    if (grouped) groups_load<RPW>(G, 0, gw);
+    uint32_t gb[4];
+    if (MX) groups_load_mx<RPW>(G, 0, gb);
+    else if (grouped) groups_load<RPW>(G, 0, gw);
     stage();
-    if (grouped) groups_store<RPW>(G, gw);
+    if (MX) groups_store_mx<RPW>(G, gb);
+    else if (grouped) groups_store<RPW>(G, gw);
     for (int c = 0; c < nchunks; ++c) {
         const int b = c * 64 + lane;
         const bool act = b < nb;
@@ -367,7 +405,8 @@ __device__ __forceinline__ float stream_rows(__amdgpu_buffer_rsrc_t rsrc, const 
         // the next chunk's group scales are issued before its weights: they
         // are stored at the end of this chunk, and waiting for them must not
         // wait for the weights (loads complete in issue order)
-        if (grouped && c + 1 < nchunks) groups_load<RPW>(G, c + 1, gw);
+        if (MX && c + 1 < nchunks) groups_load_mx<RPW>(G, c + 1, gb);
+        else if (grouped && c + 1 < nchunks) groups_load<RPW>(G, c + 1, gw);
         __builtin_amdgcn_sched_barrier(0);
         if (PREFETCH && b + 64 < nb) {
 #pragma unroll
@@ -379,8 +418,15 @@ __device__ __forceinline__ float stream_rows(__amdgpu_buffer_rsrc_t rsrc, const 
                 int32_t av[8] = {0, 0, 0, 0, 0, 0, 0, 0};
                 if (act) load_act(vq + (size_t)it * vlen, b, av);
                 int32_t *dst = isum_wave + it * RPW * ISUM_PITCH + lane;
+                if constexpr (MX) {
+                    int32_t ae[4], ao[4];
+                    mx_split_act(av, ae, ao);
 #pragma unroll
-                for (int j = 0; j < RPW; ++j) dst[j * ISUM_PITCH] = act ? block_dot(cur[j], av) : 0;
+                    for (int j = 0; j < RPW; ++j) dst[j * ISUM_PITCH] = act ? block_dot_mx(cur[j].w, ae, ao) : 0;
+                } else {
+#pragma unroll
+                    for (int j = 0; j < RPW; ++j) dst[j * ISUM_PITCH] = act ? block_dot(cur[j], av) : 0;
+                }
             }
         }
         wave_lds_sync();
@@ -394,7 +440,10 @@ __device__ __forceinline__ float stream_rows(__amdgpu_buffer_rsrc_t rsrc, const 
         }
         wave_lds_sync();
         if (grouped && c + 1 < nchunks) {
-            groups_store<RPW>(G, gw);
+            if (MX)
+                groups_store_mx<RPW>(G, gb);
+            else
+                groups_store<RPW>(G, gw);
             wave_lds_sync();
         }
         if (PREFETCH) {

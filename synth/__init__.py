@@ -310,6 +310,44 @@ def mx_expert(seed: int, layer: int, expert: int, spec: LayerSpec, sigma: float 
     return blob, parts
 
 
+def extreme_mx_parts(seed: int, layer: int, expert: int, spec: LayerSpec) -> dict:
+    """Edge-case MXFP4 codes and scales: every code 0..15 (the negative zero
+    8 and both ends +-6 included) at every position of a block (row r holds
+    code (j + r) % 16 at position j), with rows 32..63 of gate and up equal
+    and at -6 throughout (h constant over that block, so Q8_0(h) is +-127);
+    scale bytes drawn from 0, 1, 2 (subnormal and smallest normal
+    multipliers), 100, 120, 127 and 130, one common byte per flat row."""
+    H, I = spec.hidden, spec.inter
+    choices = np.array([0, 1, 2, 100, 120, 127, 130], np.uint8)
+    parts = {}
+    for m, (name, rows, cols) in enumerate((("gate", I, H), ("up", I, H), ("down", H, I))):
+        c = ((np.arange(cols)[None, :] + np.arange(rows)[:, None]) % 16).astype(np.uint8)
+        u = uniform_u64(stream_key(seed, K_WEIGHT, layer, expert, m, 9), rows * (cols // 32))
+        x = choices[(u % np.uint64(len(choices))).astype(np.int64)].reshape(rows, cols // 32)
+        if name != "down" and rows >= 64:
+            c[32:64] = 15
+            x[32:64] = x[32, 0]
+        parts[name], parts["s_" + name] = c, x
+    return parts
+
+
+def extreme_mx_layer(seed: int, S: int, spec: LayerSpec, layer: int = 0) -> dict:
+    """A small MXFP4 layer of extreme_mx_parts blobs with extreme_hidden_states."""
+    blobs = []
+    for e in range(spec.n_experts + spec.n_shared):
+        p = extreme_mx_parts(seed, layer, e, spec)
+        blobs.append(assemble_mx_blob(spec.hidden, spec.inter, p["gate"], p["up"], p["down"],
+                                      p["s_gate"], p["s_up"], p["s_down"]))
+    return {
+        "spec": spec,
+        "x": extreme_hidden_states(seed, layer, S, spec.hidden),
+        "router_w": router_weights(seed, layer, spec),
+        "bias": router_bias(seed, layer, spec),
+        "blobs": blobs[:spec.n_experts],
+        "shared": blobs[spec.n_experts] if spec.n_shared else None,
+    }
+
+
 def mx_cdf_table(ratio: float = 2.56) -> np.ndarray:
     """65536-entry table mapping a 16-bit uniform to an E2M1 code, distributed
     as the nearest E2M1 of z * ratio for z ~ N(0, 1) (ratio: the weights'
