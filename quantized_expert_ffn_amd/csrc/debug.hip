@@ -82,7 +82,13 @@ __global__ __launch_bounds__(64) void k_debug_block_dots_mx(const uint8_t *__res
                              ((uint32_t)(uint8_t)p[2] << 16) | ((uint32_t)(uint8_t)p[3] << 24));
         }
         mx_split_act(a, ae, ao);
-        out[(size_t)r * nb + b] = block_dot_mx(w.w, ae, ao);
+        // both device sums (int8 lookups and the f16 conversion path) must
+        // agree; a disagreement is reported as INT32_MIN
+        f16x2 h[16];
+        mx_act_f16(a, h);
+        const int32_t si = block_dot_mx(w.w, ae, ao);
+        const float sf = block_dot_mx_f16(w.w, h);
+        out[(size_t)r * nb + b] = (float)si == sf ? si : INT32_MIN;
     }
 }
 

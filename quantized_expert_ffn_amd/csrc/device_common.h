@@ -261,6 +261,41 @@ __device__ __forceinline__ int32_t block_dot_mx(u32x4 w, const int32_t even[4], 
     return s;
 }
 
+// The same block sum through the hardware FP4 conversion: each byte's two
+// codes become two f16 values 2 v (v_cvt_scalef32_pk_f16_fp4 with scale 2,
+// exact) and v_dot2 multiplies them with the activation pair in f32.  Every
+// product and partial sum is an integer of magnitude below 2^16, so the f32
+// result is exactly isum whatever the order of its additions.
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// The 32 activation codes of a block (8 words, in order) as 16 f16 pairs
+// (q_2j, q_2j+1), exact: each byte is flipped to offset binary, placed under
+// the f16 exponent of 1024 (0x64) and 1024 + 128 is subtracted.
+__device__ __forceinline__ void mx_act_f16(const int32_t a[8], f16x2 h[16]) {
+    const f16x2 off = {(_Float16)-1152.0f, (_Float16)-1152.0f};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const uint32_t u = (uint32_t)a[k] ^ 0x80808080u;
+        const uint32_t p0 = __builtin_amdgcn_perm(0x64646464u, u, 0x05010400u);   // bytes u0, 64, u1, 64
+        const uint32_t p1 = __builtin_amdgcn_perm(0x64646464u, u, 0x05030402u);   // bytes u2, 64, u3, 64
+        h[2 * k] = __builtin_bit_cast(f16x2, p0) + off;
+        h[2 * k + 1] = __builtin_bit_cast(f16x2, p1) + off;
+    }
+}
+
+__device__ __forceinline__ float block_dot_mx_f16(u32x4 w, const f16x2 h[16]) {
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+    float s = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        s = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(ws[k], 2.0f, 0), h[4 * k], s, false);
+        s = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(ws[k], 2.0f, 1), h[4 * k + 1], s, false);
+        s = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(ws[k], 2.0f, 2), h[4 * k + 2], s, false);
+        s = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(ws[k], 2.0f, 3), h[4 * k + 3], s, false);
+    }
+    return s;
+}
+
 // Half the value of an E8M0 scale byte, 2^(x - 128), as binary32 (exact:
 // 2^-128 and 2^-127 are subnormal numbers); x = 255 (NaN in E8M0) gives NaN.
 __device__ __forceinline__ float e8m0_half(uint32_t x) {

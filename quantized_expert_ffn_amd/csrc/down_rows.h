@@ -140,25 +140,47 @@ struct DownTile {
     __device__ __forceinline__ float ld_dh(size_t i) const { return COHERENT ? ld_dev(a.dh + i) : a.dh[i]; }
 
     // Group scales of this wave's DR_RPW rows for every unit of the batch
-    // into the wave's LDS region of gsl (UB x DR_RPW x ngr floats), by direct
-    // global-to-LDS loads (no registers held; the caller drains them before
-    // its barrier).  A unit that is not resident leaves its scales unset:
-    // its block dots are zero and its rows' results are replaced by 0.
-    __device__ __forceinline__ void stage_groups(int u0, int u1, float *gsl) {
-        const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
-        const int ngr = a.I / a.group;
-        float *dst = gsl + wave * UB * DR_RPW * ngr;
-        const int rw0 = rt * DR_ROWS + wave * DR_RPW;
-        const int n = (u1 - u0) * DR_RPW * ngr;
+    // into the wave's LDS region of gsl (UB x DR_RPW x ngr floats).  In two
+    // parts, so that the loads go out before the batch's weight loads and the
+    // caller's wait for its staged data (loads complete in issue order) also
+    // covers them: groups_issue sends direct global-to-LDS loads (f32 group
+    // scales) or, for MXFP4, loads the first GW_MX words of E8M0 bytes per
+    // lane into registers; groups_finish converts and stores those words
+    // (2^(x - 128)) and does whatever did not fit, after the weights.  A unit
+    // that is not resident leaves zeros (f32 scales: unset): its block dots
+    // are zero and its rows' results are replaced by 0.
+    static constexpr int GW_MX = 8;
+    __device__ __forceinline__ int groups_ngr() const { return a.I / a.group; }
+    __device__ __forceinline__ float *groups_dst(float *gsl) const {
+        return gsl + uniform(threadIdx.x >> 6) * UB * DR_RPW * groups_ngr();
+    }
+    __device__ __forceinline__ int groups_row0() const { return rt * DR_ROWS + uniform(threadIdx.x >> 6) * DR_RPW; }
+    __device__ __forceinline__ uint32_t mx_word(int u0, int w) const {
+        const int wpr = groups_ngr() / 4, ur = w / wpr, p = w - ur * wpr;
+        const uint8_t *blob = ublob[u0 + ur / DR_RPW];
+        return blob ? *reinterpret_cast<const uint32_t *>(
+                          blob + BL.s_down + (size_t)(groups_row0() + ur % DR_RPW) * groups_ngr() + 4 * p)
+                    : 0u;
+    }
+    __device__ __forceinline__ void mx_store(int u0, int w, uint32_t v, float *dst) const {
+        const bool live = ublob[u0 + w / (groups_ngr() / 4) / DR_RPW] != nullptr;
+        reinterpret_cast<f32x4 *>(dst)[w] = live ? f32x4{e8m0_half(v & 0xFFu), e8m0_half((v >> 8) & 0xFFu),
+                                                         e8m0_half((v >> 16) & 0xFFu), e8m0_half(v >> 24)}
+                                                 : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+
+    __device__ __forceinline__ void groups_issue(int u0, int u1, float *gsl, uint32_t (&mxv)[GW_MX]) {
+        const int lane = threadIdx.x & 63, ngr = groups_ngr();
+        const int nw = (u1 - u0) * DR_RPW * ngr / 4;
         if (MX) {
-            // one E8M0 byte per block, converted to 2^(x - 128)
-            for (int i = lane; i < n; i += 64) {
-                const int ur = i / ngr, g = i - ur * ngr;
-                const uint8_t *blob = ublob[u0 + ur / DR_RPW];
-                dst[i] = blob ? e8m0_half(blob[BL.s_down + (size_t)(rw0 + ur % DR_RPW) * ngr + g]) : 0.0f;
+#pragma unroll
+            for (int k = 0; k < GW_MX; ++k) {
+                const int w = lane + 64 * k;
+                mxv[k] = w < nw ? mx_word(u0, w) : 0u;
             }
         } else if ((ngr & 3) == 0) {
-            const int wpr = ngr / 4, nw = n / 4;
+            float *dst = groups_dst(gsl);
+            const int wpr = ngr / 4, rw0 = groups_row0();
             for (int w0 = 0; w0 < nw; w0 += 64) {
                 const int w = w0 + lane;
                 if (w < nw) {
@@ -169,8 +191,34 @@ struct DownTile {
                                   dst + 4 * w0);
                 }
             }
-            drain_vm();
-        } else {
+        }
+    }
+
+    __device__ __forceinline__ void groups_finish(int u0, int u1, float *gsl, const uint32_t (&mxv)[GW_MX]) {
+        const int lane = threadIdx.x & 63, ngr = groups_ngr();
+        float *dst = groups_dst(gsl);
+        const int n = (u1 - u0) * DR_RPW * ngr, nw = n / 4;
+        if (MX) {
+#pragma unroll
+            for (int k = 0; k < GW_MX; ++k) {
+                const int w = lane + 64 * k;
+                if (w < nw) mx_store(u0, w, mxv[k], dst);
+            }
+            for (int w0 = 64 * GW_MX; w0 < nw; w0 += 64 * GW_MX) {
+                uint32_t v[GW_MX];
+#pragma unroll
+                for (int k = 0; k < GW_MX; ++k) {
+                    const int w = w0 + lane + 64 * k;
+                    v[k] = w < nw ? mx_word(u0, w) : 0u;
+                }
+#pragma unroll
+                for (int k = 0; k < GW_MX; ++k) {
+                    const int w = w0 + lane + 64 * k;
+                    if (w < nw) mx_store(u0, w, v[k], dst);
+                }
+            }
+        } else if ((ngr & 3) != 0) {
+            const int rw0 = groups_row0();
             for (int i = lane; i < n; i += 64) {
                 const int ur = i / ngr, g = i - ur * ngr;
                 const uint8_t *blob = ublob[u0 + ur / DR_RPW];
@@ -178,6 +226,8 @@ struct DownTile {
                               : 0.0f;
             }
         }
+        // (f32 scales in whole 16-byte words: the direct loads of
+        // groups_issue completed with the caller's wait)
     }
 
     // One batch of units [u0, u1); ONE: single() holds and, with issued,
@@ -239,9 +289,11 @@ struct DownTile {
         const int nr = max(stage_rounds(nq, DR_MQ * DR_T), max(stage_rounds(nd, DR_MD * DR_T), stage_rounds(ns, DR_T)));
         i32x4 qv[DR_MQ];
         float dv[DR_MD], sv[1];
+        uint32_t mxv[GW_MX];
         stage_fetch(qv, 0, nq, q_src);
         stage_fetch(dv, 0, nd, d_src);
         stage_fetch(sv, 0, ns, s_src);
+        if (GROUPED) groups_issue(u0, u1, gsl, mxv);
         __builtin_amdgcn_sched_barrier(0);
         for (int c = 0; c < (ONE ? 1 : nch); ++c) {
             const int b = c * 64 + lane;
@@ -258,7 +310,7 @@ struct DownTile {
                 stage_store(qv, 0, nq, q_dst);
                 stage_store(dv, 0, nd, d_dst);
                 stage_store(sv, 0, ns, s_dst);
-                if (GROUPED) stage_groups(u0, u1, gsl);
+                if (GROUPED) groups_finish(u0, u1, gsl, mxv);
                 for (int rd = 1; !ONE && rd < nr; ++rd) {
                     stage_fetch(qv, rd, nq, q_src);
                     stage_fetch(dv, rd, nd, d_src);
@@ -280,12 +332,13 @@ struct DownTile {
                         int32_t av[8] = {0, 0, 0, 0, 0, 0, 0, 0};
                         if (act) load_act(qh_l + (size_t)(q - pbase) * qpitch, b, av);
                         if constexpr (MX) {
-                            int32_t ae[4], ao[4];
-                            mx_split_act(av, ae, ao);
+                            // exact block sums in binary32 (see block_dot_mx_f16)
+                            f16x2 h[16];
+                            mx_act_f16(av, h);
 #pragma unroll
                             for (int r = 0; r < DR_RPW; ++r)
                                 isum[(r * mpb + (q - pbase)) * ISUM_PITCH + lane] =
-                                    (act && live) ? block_dot_mx(wv[ui][r].w, ae, ao) : 0;
+                                    (act && live) ? __float_as_int(block_dot_mx_f16(wv[ui][r].w, h)) : 0;
                         } else {
 #pragma unroll
                             for (int r = 0; r < DR_RPW; ++r)
@@ -298,7 +351,7 @@ struct DownTile {
             wave_lds_sync();
             if (chain_lane && cp < npb) {
                 if (GROUPED)
-                    acc = chain_chunk_g(acc, isum + (cr * mpb + cp) * ISUM_PITCH, dh_l + cp * dpitch + c * 64,
+                    acc = chain_chunk_g<MX>(acc, isum + (cr * mpb + cp) * ISUM_PITCH, dh_l + cp * dpitch + c * 64,
                                         gsl + (wave * UB * DR_RPW + (ug - u0) * DR_RPW + cr) * ngr + c * (64 >> lgb),
                                         lgb,
                                         min(64, nbi - c * 64));

@@ -32,8 +32,10 @@ __host__ __device__ inline DownRowsPlan down_rows_plan(int S, int K, int E, int 
 }
 
 // ONE_TOKEN: S == 1, so every unit has exactly one pair.
+// Three workgroups per CU except for MXFP4, whose f16 activation pairs do
+// not fit 168 registers beside the batch's weights (two per CU, no spills).
 template <int BITS, bool ONE_TOKEN, bool GROUPED, bool MX = false>
-__global__ __launch_bounds__(DR_T) __attribute__((amdgpu_waves_per_eu(3))) void k_down_rows(const FwdArgs a) {
+__global__ __launch_bounds__(DR_T) __attribute__((amdgpu_waves_per_eu(MX ? 2 : 3))) void k_down_rows(const FwdArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int tid = threadIdx.x;
     const int S = a.S, K = a.K, E = a.E, P = S * K;

@@ -250,6 +250,13 @@ __device__ __forceinline__ float chain_chunk(float acc, const int32_t *is, const
 // The same chain with one scale per group of gb blocks of the row (gs: the
 // chunk's group scales of this lane's row): acc = fmaf(dv_b * gs[b / gb],
 // isum_b, acc), the multiplier being one binary32 product.  gb = 1 << lgb.
+// ISF: the block sums are stored as binary32 bits (exact integers) instead
+// of int32.
+template <bool ISF = false>
+__device__ __forceinline__ float isum_f(int32_t v) {
+    return ISF ? __int_as_float(v) : (float)v;
+}
+template <bool ISF = false>
 __device__ __forceinline__ float chain_chunk_g(float acc, const int32_t *is, const float *dv, const float *gs,
                                                int lgb, int nbc) {
     if (nbc == 64) {
@@ -265,14 +272,14 @@ __device__ __forceinline__ float chain_chunk_g(float acc, const int32_t *is, con
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
                 const int b = qq + 4 * q4;
-                acc = __builtin_fmaf(dd[q4].x * gs[b >> lgb], (float)iv[q4].x, acc);
-                acc = __builtin_fmaf(dd[q4].y * gs[(b + 1) >> lgb], (float)iv[q4].y, acc);
-                acc = __builtin_fmaf(dd[q4].z * gs[(b + 2) >> lgb], (float)iv[q4].z, acc);
-                acc = __builtin_fmaf(dd[q4].w * gs[(b + 3) >> lgb], (float)iv[q4].w, acc);
+                acc = __builtin_fmaf(dd[q4].x * gs[b >> lgb], isum_f<ISF>(iv[q4].x), acc);
+                acc = __builtin_fmaf(dd[q4].y * gs[(b + 1) >> lgb], isum_f<ISF>(iv[q4].y), acc);
+                acc = __builtin_fmaf(dd[q4].z * gs[(b + 2) >> lgb], isum_f<ISF>(iv[q4].z), acc);
+                acc = __builtin_fmaf(dd[q4].w * gs[(b + 3) >> lgb], isum_f<ISF>(iv[q4].w), acc);
             }
         }
     } else {
-        for (int bb = 0; bb < nbc; ++bb) acc = __builtin_fmaf(dv[bb] * gs[bb >> lgb], (float)is[bb], acc);
+        for (int bb = 0; bb < nbc; ++bb) acc = __builtin_fmaf(dv[bb] * gs[bb >> lgb], isum_f<ISF>(is[bb]), acc);
     }
     return acc;
 }
@@ -419,10 +426,12 @@ __device__ __forceinline__ float stream_rows(__amdgpu_buffer_rsrc_t rsrc, const 
                 if (act) load_act(vq + (size_t)it * vlen, b, av);
                 int32_t *dst = isum_wave + it * RPW * ISUM_PITCH + lane;
                 if constexpr (MX) {
-                    int32_t ae[4], ao[4];
-                    mx_split_act(av, ae, ao);
+                    // exact block sums in binary32 (see block_dot_mx_f16)
+                    f16x2 h[16];
+                    mx_act_f16(av, h);
 #pragma unroll
-                    for (int j = 0; j < RPW; ++j) dst[j * ISUM_PITCH] = act ? block_dot_mx(cur[j].w, ae, ao) : 0;
+                    for (int j = 0; j < RPW; ++j)
+                        dst[j * ISUM_PITCH] = act ? __float_as_int(block_dot_mx_f16(cur[j].w, h)) : 0;
                 } else {
 #pragma unroll
                     for (int j = 0; j < RPW; ++j) dst[j * ISUM_PITCH] = act ? block_dot(cur[j], av) : 0;
@@ -432,8 +441,8 @@ __device__ __forceinline__ float stream_rows(__amdgpu_buffer_rsrc_t rsrc, const 
         wave_lds_sync();
         if (cvec < ng) {
             if (grouped)
-                acc = chain_chunk_g(acc, isum_wave + (cvec * RPW + crow) * ISUM_PITCH, vd + cvec * vds + c * 64,
-                                    G.lds + crow * (64 >> G.lgb), G.lgb, min(64, nb - c * 64));
+                acc = chain_chunk_g<MX>(acc, isum_wave + (cvec * RPW + crow) * ISUM_PITCH, vd + cvec * vds + c * 64,
+                                        G.lds + crow * (64 >> G.lgb), G.lgb, min(64, nb - c * 64));
             else
                 acc = chain_chunk(acc, isum_wave + (cvec * RPW + crow) * ISUM_PITCH, vd + cvec * vds + c * 64,
                                   min(64, nb - c * 64));

@@ -16,6 +16,15 @@ experts live in pinned host memory.  For one layer step the host
      the forward call, which runs the hits first and the misses after the
      event (its pending mask).
 
+With look-ahead (README v1.0, "What's implemented": router-lookahead
+prefetch, the next layer's router applied to the current layer's state
+predicts 71.6% of its top-8; README v1.12, "Other supported models": the
+next layer's expert set prefetched into a second bank while the current
+layer computes), the host also plans copies for the experts predicted for
+the next layer while the current one computes; they land in that layer's
+own slots (its bank), and when its real routing arrives the predicted
+experts that were right are hits whose copies may still be in flight.
+
 This module holds the bookkeeping only; every byte moves through the C ABI.
 """
 from __future__ import annotations
@@ -77,18 +86,50 @@ class ExpertTier:
         self.lru = [LayerLRU(slots_per_layer) for _ in range(n_layers)]
         self.hits = 0
         self.misses = 0
+        # look-ahead: experts copied ahead for each layer and not yet used
+        self.ahead = [set() for _ in range(n_layers)]
+        self.prefetched = 0
+        self.prefetch_used = 0
+
+    def _table(self, layer):
+        table = [0] * self.n_experts
+        for e, s in self.lru[layer].resident().items():
+            table[e] = self.slot_addr(layer, s)
+        return table
 
     def plan(self, layer: int, experts):
         """Slot assignment for one step; returns (table, misses) where table
         is a list of E device addresses (0 = not resident) and misses the
         (expert, host address, device address) copies to make."""
-        lru = self.lru[layer]
-        _, misses, _ = lru.assign(experts)
-        n_req = len(set(int(e) for e in experts))
-        self.misses += len(misses)
-        self.hits += n_req - len(misses)
-        table = [0] * self.n_experts
-        for e, s in lru.resident().items():
-            table[e] = self.slot_addr(layer, s)
-        copies = [(e, self.host_addr(layer, e), self.slot_addr(layer, s)) for e, s in misses]
+        table, copies, _ = self.plan_with_ahead(layer, experts)
         return table, copies
+
+    def plan_with_ahead(self, layer: int, experts):
+        """As plan, and also the requested experts that a look-ahead copied
+        for this layer and that are used for the first time now (their copies
+        may still be in flight: the forward treats them as pending)."""
+        lru = self.lru[layer]
+        _, misses, evicted = lru.assign(experts)
+        req = set(int(e) for e in experts)
+        self.misses += len(misses)
+        self.hits += len(req) - len(misses)
+        early = sorted(req & self.ahead[layer])
+        self.prefetch_used += len(early)
+        self.ahead[layer] -= req
+        self.ahead[layer] -= set(evicted)
+        copies = [(e, self.host_addr(layer, e), self.slot_addr(layer, s)) for e, s in misses]
+        return self._table(layer), copies, early
+
+    def prefetch(self, layer: int, experts):
+        """Look-ahead for `layer`: makes the predicted experts resident in its
+        slots (least recently used victims first, as a step would) and
+        returns the (expert, host address, device address) copies to make.
+        Not counted as hits or misses; the predicted experts count as used
+        now for the LRU order."""
+        lru = self.lru[layer]
+        _, misses, evicted = lru.assign(experts)
+        self.ahead[layer] -= set(evicted)
+        for e, _ in misses:
+            self.ahead[layer].add(e)
+        self.prefetched += len(misses)
+        return [(e, self.host_addr(layer, e), self.slot_addr(layer, s)) for e, s in misses]

@@ -702,6 +702,41 @@ def trace_target_logits(seed: int, layer: int, spec: LayerSpec, trace: np.ndarra
     return t
 
 
+def predicted_sets(seed: int, layer: int, spec: LayerSpec, truth: np.ndarray, recall: float = 0.716) -> np.ndarray:
+    """A prediction [steps, K] of the expert sets `truth` [steps, K]: slot k
+    keeps the true expert with probability `recall`, else takes an expert
+    drawn uniformly from those outside the true set and the step's earlier
+    picks (so the expected overlap is recall * K)."""
+    steps, K = truth.shape
+    E = spec.n_experts
+    u = uniform01(stream_key(seed, K_ROUTING, layer, 400), steps * K * 2).reshape(steps, K, 2)
+    out = np.zeros((steps, K), np.int64)
+    for s in range(steps):
+        tset = set(int(e) for e in truth[s])
+        cur: list[int] = []
+        for k in range(K):
+            if u[s, k, 0] < recall:
+                cur.append(int(truth[s, k]))
+                continue
+            pool = [e for e in range(E) if e not in tset and e not in cur]
+            cur.append(pool[int(u[s, k, 1] * len(pool))])
+        out[s] = cur
+    return out
+
+
+def lookahead_hidden_states(W_here: np.ndarray, W_next: np.ndarray, t_here: np.ndarray, t_next: np.ndarray,
+                            seed: int, layer: int, stream: int = 0) -> np.ndarray:
+    """x [S, H] with W_here x_t = t_here[t] and W_next x_t = t_next[t] (the
+    minimum-norm solution of the stacked system, f64) plus N(0,1) noise
+    projected onto the null space of both gates; stored as f32.  With zero
+    bias the layer's router then picks the top-K of t_here, and the next
+    layer's router applied to this layer's state picks the top-K of t_next
+    (a look-ahead prediction of chosen quality)."""
+    W = np.concatenate([W_here, W_next]).astype(np.float64)
+    t = np.concatenate([t_here, t_next], axis=1)
+    return shaped_hidden_states(W, t, seed, layer, stream)
+
+
 def verify_hidden_states(seed: int, layer: int, spec: LayerSpec, S: int, union_frac: float = 0.6,
                          batch: int = 0, W: np.ndarray | None = None) -> np.ndarray:
     """Hidden states of S tokens that share experts: x_t = sqrt(rho) c +

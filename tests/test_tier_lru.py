@@ -78,3 +78,46 @@ def test_tier_table_and_copies():
     table, copies = tier.plan(1, [2, 5])   # 4 is evicted, 5 takes its slot
     assert copies == [(5, 51005, 2000)] and table[4] == 0 and table[5] == 2000
     assert (tier.hits, tier.misses) == (1, 3)
+
+
+def test_lookahead_bookkeeping():
+    """prefetch() makes predicted experts resident and remembers them; the
+    next plan_with_ahead() reports the predicted experts it uses as early
+    (their copies may still be in flight) and counts them as hits; a wrong
+    prediction costs a demand copy; evicted prefetches are forgotten."""
+    addr = {}
+    tier = ExpertTier(2, 16, 4, 100, slot_addr=lambda l, s: 1000 * (l + 1) + s,
+                      host_addr=lambda l, e: addr.setdefault((l, e), 50000 + 100 * e))
+    copies = tier.prefetch(1, [3, 5])
+    assert [c[0] for c in copies] == [3, 5] and tier.prefetched == 2
+    table, demand, early = tier.plan_with_ahead(1, [5, 7])
+    assert early == [5] and [c[0] for c in demand] == [7]
+    assert tier.hits == 1 and tier.misses == 1 and tier.prefetch_used == 1
+    assert table[5] and table[7] and table[3]           # 3 still resident (prefetched, unused)
+    # fill the layer so that the unused prefetch of 3 is evicted, then ask for it again
+    tier.plan_with_ahead(1, [8, 9, 10])
+    assert 3 not in tier.ahead[1]
+    _, demand, early = tier.plan_with_ahead(1, [3])
+    assert early == [] and [c[0] for c in demand] == [3]
+    # a prefetch of an expert already resident copies nothing
+    assert tier.prefetch(1, [3]) == []
+    # layers are independent banks
+    assert tier.prefetch(0, [3]) and tier.ahead[0] == {3}
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_lookahead_never_changes_which_experts_are_resident_for_a_step(seed):
+    """Whatever is prefetched, every requested expert has a slot afterwards,
+    slots stay distinct, and at most n_slots experts are resident."""
+    rng = random.Random(seed)
+    E, K, n_slots = 32, 4, 9
+    tier = ExpertTier(1, E, n_slots, 10, slot_addr=lambda l, s: 100 + s, host_addr=lambda l, e: 5000 + e)
+    for _ in range(300):
+        if rng.random() < 0.7:
+            tier.prefetch(0, rng.sample(range(E), K))
+        step = rng.sample(range(E), K)
+        table, _, early = tier.plan_with_ahead(0, step)
+        assert all(table[e] for e in step)
+        res = tier.lru[0].resident()
+        assert len(res) <= n_slots and len(set(res.values())) == len(res)
+        assert set(early) <= set(step)
