@@ -61,6 +61,12 @@ extern "C" {
 /* the debug hooks' `bits` value selecting MXFP4 codes */
 #define COLI_MXFP4 (-4)
 
+/* Most tokens one call takes (n_tokens, max_tokens): the workspace's int32
+ * pair and unit counts stay far from overflow below it.  Larger batches are
+ * split by the caller; COLI_EINVAL (0 from coli_moe_workspace_bytes)
+ * beyond it. */
+#define COLI_MAX_TOKENS 65536
+
 /* Layer shape.  All fields are preconditions checked on every call. */
 typedef struct coli_moe_dims {
     int32_t hidden;               /* H: multiple of 256 (router order) */
@@ -117,7 +123,7 @@ size_t coli_moe_expert_bytes(const coli_moe_dims *dims);
  * Q8_0(h) and the per-pair expert outputs.  It must be zero-filled once
  * before its first use (the status word lives in it); afterwards the
  * library keeps it consistent.  Returns 0 if dims are invalid or
- * max_tokens < 0. */
+ * max_tokens is outside 0..COLI_MAX_TOKENS. */
 size_t coli_moe_workspace_bytes(const coli_moe_dims *dims, int32_t max_tokens);
 
 /*

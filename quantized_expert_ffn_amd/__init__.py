@@ -30,6 +30,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 COLI_OK, COLI_EINVAL, COLI_ENONFINITE, COLI_EHIP, COLI_ENOTRESIDENT, COLI_EWORKSPACE = 0, -1, -2, -3, -4, -5
 COLI_WFMT_INT, COLI_WFMT_MXFP4, COLI_MXFP4 = 0, 1, -4
+COLI_MAX_TOKENS = 65536  # most tokens one call takes
 
 EXPORTS = (
     "coli_moe_expert_bytes", "coli_moe_workspace_bytes", "coli_moe_route", "coli_moe_forward",

@@ -341,7 +341,7 @@ size_t coli_moe_expert_bytes(const coli_moe_dims *d) {
 }
 
 size_t coli_moe_workspace_bytes(const coli_moe_dims *d, int32_t max_tokens) {
-    if (check_dims(d) != COLI_OK || max_tokens < 0) return 0;
+    if (check_dims(d) != COLI_OK || max_tokens < 0 || max_tokens > COLI_MAX_TOKENS) return 0;
     return ws_layout(d->hidden, d->inter, d->n_experts, d->top_k, max_tokens).total;
 }
 
@@ -352,7 +352,7 @@ int coli_moe_route(const coli_moe_dims *d, int32_t S, const float *x, const floa
                    size_t ws_bytes, void *stream) {
     int rc = check_dims(d);
     if (rc) return rc;
-    if (S < 0) return fail(COLI_EINVAL, "n_tokens=%d < 0", S);
+    if (S < 0 || S > COLI_MAX_TOKENS) return fail(COLI_EINVAL, "n_tokens=%d: must be in 0..%d", S, COLI_MAX_TOKENS);
     if (S == 0) return COLI_OK;
     if (!x || !router_w || !topk_idx || !topk_w || !ws)
         return fail(COLI_EINVAL, "coli_moe_route: NULL pointer argument");
@@ -372,7 +372,7 @@ int coli_moe_forward(const coli_moe_dims *d, int32_t S, const float *x, const in
                      size_t ws_bytes, void *stream) {
     int rc = check_dims(d);
     if (rc) return rc;
-    if (S < 0) return fail(COLI_EINVAL, "n_tokens=%d < 0", S);
+    if (S < 0 || S > COLI_MAX_TOKENS) return fail(COLI_EINVAL, "n_tokens=%d: must be in 0..%d", S, COLI_MAX_TOKENS);
     if (S == 0) return COLI_OK;
     if (!x || !topk_idx || !topk_w || !expert_blobs || !out || !ws)
         return fail(COLI_EINVAL, "coli_moe_forward: NULL pointer argument");
@@ -430,7 +430,7 @@ int layer_args_ok(const coli_moe_dims *d, int32_t S, const float *x, const float
                   const float *topk_w, const float *out, const char *who) {
     int rc = check_dims(d);
     if (rc) return rc;
-    if (S < 0) return fail(COLI_EINVAL, "n_tokens=%d < 0", S);
+    if (S < 0 || S > COLI_MAX_TOKENS) return fail(COLI_EINVAL, "n_tokens=%d: must be in 0..%d", S, COLI_MAX_TOKENS);
     if (S == 0) return COLI_OK;
     if (!x || !router_w || !expert_blobs || !topk_idx || !topk_w || !out)
         return fail(COLI_EINVAL, "%s: NULL pointer argument", who);
@@ -713,7 +713,7 @@ int coli_moe_debug_logits(const coli_moe_dims *d, int32_t S, const float *x, con
                           float *logits, void *stream) {
     int rc = check_dims(d);
     if (rc) return rc;
-    if (S < 0 || !x || !router_w || !logits) return fail(COLI_EINVAL, "debug_logits: bad arguments");
+    if (S < 0 || S > COLI_MAX_TOKENS || !x || !router_w || !logits) return fail(COLI_EINVAL, "debug_logits: bad arguments");
     if (S == 0) return COLI_OK;
     if ((rc = check_device())) return rc;
     // no workspace here: the kernel skips its status report when given none
