@@ -49,6 +49,15 @@ __device__ __forceinline__ int32_t ld_dev(const int32_t *p) {
 // Waits for every outstanding memory operation of this thread.
 __device__ __forceinline__ void drain() { __builtin_amdgcn_s_waitcnt(0); }
 
+// Hand-offs between workgroups of one launch follow the release/acquire
+// pattern: the producers' stores, a workgroup barrier, an agent-scope
+// release fence, then the relaxed arrival atomic; the consumer that sees the
+// last arrival (or a released flag) issues an agent-scope acquire fence
+// before it reads.  The data itself moves with device-scope accesses
+// (st_dev / ld_dev) and each writer drains before the barrier.
+__device__ __forceinline__ void fence_release_agent() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
+__device__ __forceinline__ void fence_acquire_agent() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
+
 __device__ __forceinline__ void raise_status(uint32_t *status, uint32_t bit) {
     // vector-memory atomic; the address is a plain global pointer
     __hip_atomic_fetch_or(status, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

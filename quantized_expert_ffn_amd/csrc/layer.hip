@@ -23,7 +23,8 @@
 //   -- barrier B: Q8_0(h) --
 //   2  down tiles of 8 output rows for every unit, combined in the
 //      workgroup (one writer per output element).
-// A workgroup drains its stores (s_waitcnt) before it arrives at a barrier.
+// A workgroup drains its stores (s_waitcnt) before it arrives at a barrier;
+// arrivals are agent-scope releases and the waits end in agent-scope acquires.
 // Barrier waits are bounded: a grid that could not be fully resident ends
 // with a status error, never a hang; the host sizes the grid from the
 // kernel's occupancy.
@@ -52,19 +53,26 @@ __device__ __forceinline__ uint32_t *flag_word(uint8_t *flags, int k, int copy) 
     return reinterpret_cast<uint32_t *>(flags + ((size_t)k * FLAG_COPIES + copy) * FLAG_STRIDE);
 }
 
-// Releases flag k of every workgroup (all lanes of the calling wave).
+// Releases flag k of every workgroup (all lanes of the calling wave, which
+// has acquired every arrival).
 __device__ __forceinline__ void release(uint8_t *flags, int k) {
     const int lane = threadIdx.x & 63;
+    fence_release_agent();
     for (int c = lane; c < (int)gridDim.x; c += 64) st_dev(flag_word(flags, k, c), 1u);
 }
 
-// Counts one arrival of the calling wave at counter k; the arrival that
-// completes `target` releases flag k.
+// Counts one arrival of the calling wave at counter k (a release of its
+// workgroup's drained stores); the arrival that completes `target`
+// acquires the others and releases flag k.
 __device__ __forceinline__ void signal(uint32_t *sync, uint8_t *flags, int k, uint32_t target) {
     uint32_t prev = 0;
+    fence_release_agent();
     if ((threadIdx.x & 63) == 0)
         prev = __hip_atomic_fetch_add(&sync[k], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (__builtin_amdgcn_readfirstlane(prev) == target - 1) release(flags, k);
+    if (__builtin_amdgcn_readfirstlane(prev) == target - 1) {
+        fence_acquire_agent();
+        release(flags, k);
+    }
 }
 
 // Workgroup arrival at barrier k (callers drain() their stores first).
@@ -85,6 +93,7 @@ __device__ __forceinline__ void wait_flag(uint8_t *flags, int k, uint32_t *statu
                 break;
             }
         }
+        fence_acquire_agent();
     }
     __syncthreads();
 }
@@ -94,8 +103,11 @@ __device__ __forceinline__ void wait_flag(uint8_t *flags, int k, uint32_t *statu
 __device__ __forceinline__ void grid_exit(uint32_t *sync, uint8_t *flags, int nbar, uint32_t nwg) {
     __shared__ int last;
     __syncthreads();
-    if (threadIdx.x == 0)
+    if (threadIdx.x == 0) {
+        fence_release_agent();
         last = __hip_atomic_fetch_add(&sync[nbar], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nwg - 1;
+        if (last) fence_acquire_agent();
+    }
     __syncthreads();
     if (last) {
         for (int c = threadIdx.x; c < N_FLAGS * (int)nwg; c += blockDim.x)

@@ -151,9 +151,13 @@ __global__ __launch_bounds__(64 * RF_W) void k_route_fused(const RouteArgs r) {
     drain();
     __syncthreads();
     if (tid == 0) {
+        fence_release_agent();
         const uint32_t prev = __hip_atomic_fetch_add(&r.sync[t], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         s_last = prev == (uint32_t)(n_lw - 1);
-        if (s_last) st_dev(&r.sync[t], 0u);
+        if (s_last) {
+            fence_acquire_agent();
+            st_dev(&r.sync[t], 0u);
+        }
     }
     __syncthreads();
     if (!s_last) return;
@@ -247,10 +251,14 @@ __global__ __launch_bounds__(64 * RF_W) void k_route_fused(const RouteArgs r) {
     drain();
     __syncthreads();
     if (tid == 0) {
+        fence_release_agent();
         const uint32_t prev =
             __hip_atomic_fetch_add(&r.sync[ROUTE_FUSE_MAX], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         s_last = prev == (uint32_t)(S - 1);
-        if (s_last) st_dev(&r.sync[ROUTE_FUSE_MAX], 0u);
+        if (s_last) {
+            fence_acquire_agent();
+            st_dev(&r.sync[ROUTE_FUSE_MAX], 0u);
+        }
     }
     __syncthreads();
     if (!s_last) return;
