@@ -38,6 +38,19 @@ struct DownRowsBatch {
     static constexpr int UB = BITS == 8 ? 4 : (BITS == 4 ? 9 : 16);  // units per batch
 };
 
+// Whether every pair slot of a call fits one batch and one staging round of
+// a down tile whatever the routing (a unit has at least one pair, so there
+// are no more units than slots), with rows of one 64-block chunk, and the
+// unit table and routing weights one word per thread: the condition of
+// slot-order staging (DownTile::slots_fetch / run_staged).
+__host__ __device__ inline bool down_slots_fit(int S, int K, int E, int n_shared, int I, int bits) {
+    const int slots = S * K + S * n_shared, nbi = I / 32;
+    const int ub = bits == 8 ? DownRowsBatch<8>::UB : (bits == 4 ? DownRowsBatch<4>::UB : DownRowsBatch<2>::UB);
+    const UnitTable U = unit_table(S, K, E);
+    return nbi <= 64 && slots <= ub && slots <= DR_MAXPB && slots * (I / 16) <= DR_MQ * DR_T &&
+           slots * nbi <= DR_MD * DR_T && U.words <= DR_T && U.umax <= DR_T && S * K <= DR_T;
+}
+
 // LDS of one down tile (from `base`).
 struct DownTilePlan {
     size_t qh, dh, isum, sdn, y, gs, end;
@@ -370,6 +383,92 @@ struct DownTile {
         return u1;
     }
 
+    // Q8_0(h) codes and block scales of every pair slot, in slot order
+    // (qh_l[slot], dh_l[slot]): the loads, then (after the caller's other
+    // loads of the same round) the stores.
+    __device__ __forceinline__ void slots_fetch(i32x4 (&qv)[DR_MQ], float (&dv)[DR_MD]) const {
+        const int slots = a.S * a.K + a.S * a.n_shared, w16 = a.I / 16;
+        stage_fetch(qv, 0, slots * w16, [&](int i) {
+            const int sl = fast_div(i, m16);
+            return ld_qh((uint32_t)sl * (uint32_t)a.I + 16u * (uint32_t)(i - sl * w16));
+        });
+        stage_fetch(dv, 0, slots * nbi, [&](int i) {
+            const int sl = fast_div(i, mnb);
+            return ld_dh((size_t)sl * nbi + (i - sl * nbi));
+        });
+    }
+    __device__ __forceinline__ void slots_store(const i32x4 (&qv)[DR_MQ], const float (&dv)[DR_MD]) const {
+        const int slots = a.S * a.K + a.S * a.n_shared, w16 = a.I / 16;
+        int8_t *qh_l = reinterpret_cast<int8_t *>(smem + D.qh);
+        float *dh_l = reinterpret_cast<float *>(smem + D.dh);
+        stage_store(qv, 0, slots * w16, [&](int i) {
+            const int sl = fast_div(i, m16);
+            return reinterpret_cast<i32x4 *>(qh_l + (size_t)sl * qpitch) + (i - sl * w16);
+        });
+        stage_store(dv, 0, slots * nbi, [&](int i) {
+            const int sl = fast_div(i, mnb);
+            return dh_l + sl * dpitch + (i - sl * nbi);
+        });
+    }
+
+    // Zeroes the per-slot results (a slot without a chain lane, as when a
+    // non-finite routing left only the shared expert in the table, reads 0).
+    __device__ __forceinline__ void zero_y() const {
+        float *y_l = reinterpret_cast<float *>(smem + D.y);
+        const int slots = a.S * a.K + a.S * a.n_shared;
+        for (int q = threadIdx.x; q < slots * DR_ROWS; q += DR_T) y_l[q] = 0.0f;
+    }
+
+    // The whole tile when slots_fit() holds and the slots' Q8_0(h) is in LDS
+    // (slots_store, then a workgroup barrier): the weights of every unit go
+    // out at once with the down-row scales right behind them (needed only at
+    // the end, so waiting for them waits for nothing the block dots have not
+    // already waited for), then the block dots, the chains and the combine.
+    __device__ __forceinline__ void run_staged() {
+        const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
+        const int r0 = rt * DR_ROWS;
+        const int8_t *qh_l = reinterpret_cast<const int8_t *>(smem + D.qh);
+        const float *dh_l = reinterpret_cast<const float *>(smem + D.dh);
+        int32_t *isum = reinterpret_cast<int32_t *>(smem + D.isum) + wave * DR_RPW * mpb * ISUM_PITCH;
+        float *y_l = reinterpret_cast<float *>(smem + D.y);
+        const int npb = uniform(uoff[n_units]);
+        const int cr = lane >> 4 >= DR_RPW ? 0 : lane >> 4, cp = lane & 15;
+        const bool chain = lane < DR_RPW * 16 && cp < npb;
+        const int rl = wave * DR_RPW + cr;
+        int ub = 0;
+        while (ub + 1 < n_units && uoff[ub + 1] <= cp) ++ub;
+        issue(0, n_units, 0);
+        float sd = 0.0f;
+        const uint8_t *my_blob = chain ? ublob[ub] : nullptr;
+        if (my_blob) sd = reinterpret_cast<const float *>(my_blob + BL.s_down)[r0 + rl];
+        const int b = lane;
+        const bool act = b < nbi;
+#pragma unroll
+        for (int ui = 0; ui < UB; ++ui) {
+            if (ui < n_units) {
+                const bool live = ublob[ui] != nullptr;
+                const int q0 = uniform(uoff[ui]);
+                const int q1 = ONE_TOKEN ? q0 + 1 : uniform(uoff[ui + 1]);
+#pragma unroll
+                for (int q = q0; q < q1; ++q) {
+                    int32_t av[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+                    if (act) load_act(qh_l + (size_t)pairs[q] * qpitch, b, av);
+#pragma unroll
+                    for (int r = 0; r < DR_RPW; ++r)
+                        isum[(r * mpb + q) * ISUM_PITCH + lane] = (act && live) ? block_dot(wv[ui][r], av) : 0;
+                }
+            }
+        }
+        wave_lds_sync();
+        if (chain) {
+            const int slot = pairs[cp];
+            const float acc = chain_chunk(0.0f, isum + (cr * mpb + cp) * ISUM_PITCH, dh_l + slot * dpitch, nbi);
+            y_l[slot * DR_ROWS + rl] = my_blob ? acc * sd : 0.0f;
+        }
+        __syncthreads();
+        combine();
+    }
+
     // Every unit of the tile, then the combine.  issued: single() holds and
     // issue(0, n_units, 0) was called.
     __device__ __forceinline__ void run(bool issued) {
@@ -385,6 +484,26 @@ struct DownTile {
         } else {
             for (int u0 = 0; u0 < n_units;) u0 = batch<false>(u0, false);
         }
+        const int r0 = rt * DR_ROWS;
+        for (int q = tid; q < S * DR_ROWS; q += DR_T) {
+            const int t = q / DR_ROWS, rl = q - t * DR_ROWS;
+            float acc = 0.0f;
+            for (int k = 0; k < K; ++k) {
+                const float wk = w[t * K + k];
+                if (rt == 0 && rl == 0 && !finite_f32(wk)) raise_status(a.status, ST_NONFINITE);
+                acc = __builtin_fmaf(wk, y_l[(t * K + k) * DR_ROWS + rl], acc);
+            }
+            if (a.n_shared) acc = acc + y_l[(P + t) * DR_ROWS + rl];
+            a.out[(size_t)t * a.H + r0 + rl] = acc;
+        }
+    }
+
+    // out[t, rows] = rank-order fmaf chain of w[t, k] * y[t, k] from 0, plus
+    // the shared expert's y (y_l complete, after a workgroup barrier).
+    __device__ __forceinline__ void combine() {
+        const int tid = threadIdx.x;
+        const int S = a.S, K = a.K, P = S * K;
+        const float *y_l = reinterpret_cast<const float *>(smem + D.y);
         const int r0 = rt * DR_ROWS;
         for (int q = tid; q < S * DR_ROWS; q += DR_T) {
             const int t = q / DR_ROWS, rl = q - t * DR_ROWS;

@@ -76,6 +76,39 @@ __global__ __launch_bounds__(DR_T) __attribute__((amdgpu_waves_per_eu(MX ? 2 : 3
     tile.run(false);
 }
 
+// The same tile when every pair slot of the call fits one staging round
+// (down_slots_fit, per-row scales, the call's unit table in the workspace):
+// the slots' Q8_0(h) is fetched in the same memory round trip as the table
+// (in slot order: its addresses do not depend on the routing), and the
+// weights go out as soon as the blob pointers are in (DownTile::run_staged).
+template <int BITS, bool ONE_TOKEN>
+__global__ __launch_bounds__(DR_T) __attribute__((amdgpu_waves_per_eu(3))) void k_down_rows_staged(const FwdArgs a) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int tid = threadIdx.x;
+    const int S = a.S, K = a.K, E = a.E, P = S * K;
+    const DownRowsPlan D = down_rows_plan(S, K, E, a.n_shared, a.I, 0, BITS);
+    const uint8_t **ublob = reinterpret_cast<const uint8_t **>(smem + D.ublob);
+    float *w_l = reinterpret_cast<float *>(smem + D.w);
+    const UnitTable U = unit_table(S, K, E);
+    int *tab = reinterpret_cast<int *>(smem);
+    DownTile<BITS, ONE_TOKEN, false> tile(a, smem, D.tile, tab + U.uoff, tab + U.pairs, ublob, w_l, 0, blockIdx.x);
+    const int32_t tw = tid < U.words ? reinterpret_cast<const int32_t *>(a.units)[tid] : 0;
+    const uint8_t *tb = tid < U.umax ? reinterpret_cast<const uint8_t *const *>(a.units + U.ublob)[tid] : nullptr;
+    const float wt = tid < P ? a.w[tid] : 0.0f;
+    i32x4 qv[DR_MQ];
+    float dv[DR_MD];
+    tile.slots_fetch(qv, dv);
+    if (tid < U.words) tab[tid] = tw;
+    if (tid < U.umax) ublob[tid] = tb;
+    if (tid < P) w_l[tid] = wt;
+    tile.slots_store(qv, dv);
+    tile.zero_y();
+    __syncthreads();
+    tile.n_units = uniform(tab[0]);
+    if (tid < tile.n_units && ublob[tid] == nullptr) raise_status(a.status, ST_NOTRESIDENT);
+    tile.run_staged();
+}
+
 size_t down_rows_smem(int S, int I, int E, int K, int n_shared, int group, int bits) {
     return down_rows_plan(S, K, E, n_shared, I, group, bits).total;
 }
@@ -89,6 +122,11 @@ hipError_t launch_down_rows(const FwdArgs &a, int bits, hipStream_t st) {
         return launch(kern, grid, dim3(DR_T), smem, st, a);
     };
     const bool one = a.S == 1;
+    if (a.units && !a.mx && !a.group && down_slots_fit(a.S, a.K, a.E, a.n_shared, a.I, bits)) {
+        if (bits == 8) return one ? go(k_down_rows_staged<8, true>) : go(k_down_rows_staged<8, false>);
+        if (bits == 4) return one ? go(k_down_rows_staged<4, true>) : go(k_down_rows_staged<4, false>);
+        return one ? go(k_down_rows_staged<2, true>) : go(k_down_rows_staged<2, false>);
+    }
     if (a.mx) return one ? go(k_down_rows<4, true, true, true>) : go(k_down_rows<4, false, true, true>);
     if (a.group) return one ? go(k_down_rows<4, true, true>) : go(k_down_rows<4, false, true>);
     if (bits == 8) return one ? go(k_down_rows<8, true, false>) : go(k_down_rows<8, false, false>);

@@ -28,6 +28,7 @@
 // acc = fmaf(d_b, isum_b, acc) over the chunk's blocks in ascending order —
 // the layer's defined order — and finally multiplies by the row scale.
 #include <algorithm>
+#include <type_traits>
 
 #include "device_common.h"
 #include "gateup.h"
@@ -150,6 +151,28 @@ __global__ __launch_bounds__(256) void k_gateup(const FwdArgs a) {
         }
         __syncthreads();
     };
+    if constexpr (BITS < 8 && !GROUPED && !MX) {
+        const int nch = (nb + 63) / 64;
+        if (np <= NT && H <= 8192 && nch >= 2) {
+            // all of the unit's vectors in one pass: their activations are
+            // loaded ahead of the weights (gateup_unit_primed)
+            auto tok = [&](int it) {
+                const int v = pairs[p0 + it];
+                return v < P ? v / K : v - P;
+            };
+            auto go = [&](auto nch_c) {
+                gateup_unit_primed<BITS, NT, decltype(nch_c)::value>(blob, H, I, blockIdx.x * 32, pairs + p0, np,
+                                                                     smem, L, a.qx, a.dx, tok, a.qh, a.dh);
+            };
+            if (nch == 2)
+                go(std::integral_constant<int, 2>());
+            else if (nch == 3)
+                go(std::integral_constant<int, 3>());
+            else
+                go(std::integral_constant<int, 4>());
+            return;
+        }
+    }
     gateup_unit<BITS, NT, GROUPED, MX>(blob, H, I, a.group, blockIdx.x * 32, pairs + p0, np, smem, L, L.total, a.qh,
                                        a.dh, stage);
 }

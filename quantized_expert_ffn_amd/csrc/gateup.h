@@ -76,6 +76,136 @@ __device__ __forceinline__ void gateup_unit(const uint8_t *blob, int H, int I, i
     }
 }
 
+// Chunk c (blocks 64 c .. 64 c + 63) of this wave's RPW rows: RPW buffer
+// loads, issued whatever the lane (a block past the row's end reads the next
+// row, or zeros past the blob; its dot is not used), so that the count of
+// memory operations in flight is known to the waits.
+template <int BITS, int RPW>
+__device__ __forceinline__ void issue_chunk(__amdgpu_buffer_rsrc_t rsrc, const uint32_t (&rowoff)[RPW], int c,
+                                            BlockBits<BITS> (&X)[RPW]) {
+    const int b = c * 64 + (int)(threadIdx.x & 63);
+#pragma unroll
+    for (int j = 0; j < RPW; ++j) X[j] = load_block<BITS>(rsrc, rowoff[j], b);
+}
+
+// Block dots of chunk c (in X) against the np staged vectors, then the
+// chain lanes' binary32 chain over the chunk's blocks in ascending order.
+template <int BITS, int NT, int RPW>
+__device__ __forceinline__ float reduce_chunk(const BlockBits<BITS> (&X)[RPW], int c, int nb, int np,
+                                              const int8_t *vq, const float *vd, int vds, int vlen,
+                                              int32_t *isum_wave, float acc) {
+    const int lane = threadIdx.x & 63, crow = lane % RPW, cvec = lane / RPW;
+    const int b = c * 64 + lane;
+    const bool act = b < nb;
+#pragma unroll
+    for (int it = 0; it < NT; ++it) {
+        if (it < np) {
+            int32_t av[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+            if (act) load_act(vq + (size_t)it * vlen, b, av);
+            int32_t *dst = isum_wave + it * RPW * ISUM_PITCH + lane;
+#pragma unroll
+            for (int j = 0; j < RPW; ++j) dst[j * ISUM_PITCH] = act ? block_dot(X[j], av) : 0;
+        }
+    }
+    wave_lds_sync();
+    if (cvec < np)
+        acc = chain_chunk(acc, isum_wave + (cvec * RPW + crow) * ISUM_PITCH, vd + cvec * vds + c * 64,
+                          min(64, nb - c * 64));
+    wave_lds_sync();
+    return acc;
+}
+
+// gateup_unit for a unit whose pairs fit one pass (np <= NT), with packed
+// codes (BITS 4 or 2), per-row scales and rows of NCH = (H / 32 + 63) / 64
+// chunks (at least two; H at most 8192).  The order of the memory
+// operations is the point: the activations (Q8_0(x) of the vectors' tokens,
+// token tok(v) for vector v) are loaded first, into registers, then each
+// lane's row scale, then chunks 0 and 1 of the wave's rows; storing the
+// activations to LDS then waits for none of the weights, the workgroup
+// barrier orders LDS only, and from there on two chunks are in flight
+// (chunk c + 2 is issued once chunk c has been reduced).  The chunks are
+// unrolled so that the waits the compiler places for each chunk's
+// registers leave the next chunk in flight.  Results as gateup_unit.
+template <int BITS, int NT, int NCH, typename Tok>
+__device__ __forceinline__ void gateup_unit_primed(const uint8_t *blob, int H, int I, int i0, const int *slots,
+                                                   int np, uint8_t *smem, const SmemPlan &L,
+                                                   const int8_t *__restrict__ qx, const float *__restrict__ dx, Tok tok,
+                                                   int8_t *__restrict__ qh, float *__restrict__ dh) {
+    static_assert(BITS == 4 || BITS == 2, "one buffer load per block");
+    constexpr int RPW = ROWS_PER_WAVE;
+    const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
+    int8_t *vq = reinterpret_cast<int8_t *>(smem + L.vq);
+    float *vd = reinterpret_cast<float *>(smem + L.vd);
+    int32_t *isum_wave = reinterpret_cast<int32_t *>(smem + L.isum) + wave * NT * RPW * ISUM_PITCH;
+    float *gu = reinterpret_cast<float *>(smem + L.gu);
+    const BlobLayout BL = blob_layout(H, I, BITS, 0, false);
+    const size_t row_bytes = (size_t)H * BITS / 8;
+    const int half = wave & 1;
+    const size_t mat = wave < 2 ? BL.gate : BL.up;
+    const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(blob, (uint32_t)BL.total);
+    uint32_t rowoff[RPW];
+#pragma unroll
+    for (int j = 0; j < RPW; ++j) rowoff[j] = (uint32_t)(mat + (size_t)(i0 + 16 * half + j) * row_bytes);
+    const int nb = H / 32, vds = vd_stride(nb), w16 = H / 16;
+    const uint32_t mw = fast_div_magic(w16), mb = fast_div_magic(nb);
+    const int crow = lane % RPW, cvec = lane / RPW;
+    // 1. activations (np * H / 16 code words, np * H / 32 scales: at most
+    //    2 NT and NT per thread for H <= 8192)
+    i32x4 xq[2 * NT];
+    float xd[NT];
+    stage_fetch(xq, 0, np * w16, [&](int i) {
+        const int it = fast_div(i, mw);
+        return *reinterpret_cast<const i32x4 *>(qx + (size_t)tok(it) * H + 16 * (i - it * w16));
+    });
+    stage_fetch(xd, 0, np * nb, [&](int i) {
+        const int it = fast_div(i, mb);
+        return dx[(size_t)tok(it) * nb + (i - it * nb)];
+    });
+    // 2. the row scale of this lane's chain row, 3. chunks 0 and 1
+    const uint32_t soff = (uint32_t)((wave < 2 ? BL.s_gate : BL.s_up) + 4 * (size_t)(i0 + 16 * half + crow));
+    __builtin_amdgcn_sched_barrier(0);
+    const float rs = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsrc, soff, 0, 0));
+    BlockBits<BITS> A[RPW], B[RPW];
+    issue_chunk<BITS, RPW>(rsrc, rowoff, 0, A);
+    __builtin_amdgcn_sched_barrier(0);   // chunk 0's loads ahead of chunk 1's
+    issue_chunk<BITS, RPW>(rsrc, rowoff, 1, B);
+    __builtin_amdgcn_sched_barrier(0);
+    stage_store(xq, 0, np * w16, [&](int i) {
+        const int it = fast_div(i, mw);
+        return reinterpret_cast<i32x4 *>(vq + (size_t)it * H) + (i - it * w16);
+    });
+    stage_store(xd, 0, np * nb, [&](int i) {
+        const int it = fast_div(i, mb);
+        return vd + it * vds + (i - it * nb);
+    });
+    lds_barrier();
+    float acc = 0.0f;
+#pragma unroll
+    for (int c = 0; c < NCH; c += 2) {
+        acc = reduce_chunk<BITS, NT, RPW>(A, c, nb, np, vq, vd, vds, H, isum_wave, acc);
+        __builtin_amdgcn_sched_barrier(0);
+        if (c + 2 < NCH) issue_chunk<BITS, RPW>(rsrc, rowoff, c + 2, A);
+        __builtin_amdgcn_sched_barrier(0);
+        if (c + 1 < NCH) {
+            acc = reduce_chunk<BITS, NT, RPW>(B, c + 1, nb, np, vq, vd, vds, H, isum_wave, acc);
+            __builtin_amdgcn_sched_barrier(0);
+            if (c + 3 < NCH) issue_chunk<BITS, RPW>(rsrc, rowoff, c + 3, B);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    if (cvec < np) gu[cvec * 64 + wave * RPW + crow] = acc * rs;
+    __syncthreads();
+    const int vv = tid >> 5, i = tid & 31;
+    if (vv < np) {
+        const float h = swiglu_f32(gu[vv * 64 + i], gu[vv * 64 + 32 + i]);
+        float d;
+        const int8_t q = q8_0_lane(h, &d);
+        const int slot = slots[vv];
+        qh[(size_t)slot * I + i0 + i] = q;
+        if (i == 0) dh[(size_t)slot * (I / 32) + i0 / 32] = d;
+    }
+}
+
 // Gate/up of rows i0 .. i0+15 of one unit for the np <= NT pair slots
 // slots[0 .. np), with SwiGLU: h (binary32, not quantised) of slot v's row
 // i0 + i goes to hs[v * I + i0 + i].  Waves 0-1 stream 8 gate rows each,

@@ -213,9 +213,18 @@ __device__ __forceinline__ void load_act(const int8_t *vq, int b, int32_t a[8]) 
 // operations of one wave complete in order; the fence orders them for the
 // compiler and waits for outstanding LDS traffic).
 __device__ __forceinline__ void wave_lds_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
     __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Workgroup barrier that orders LDS accesses only: global loads in flight
+// stay in flight across it (__syncthreads() waits for every one of them).
+// Direct global-to-LDS loads are not covered: wait for them (wait_vm) first.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 // Binary32 chain of one chunk for one (row, vector): acc = fmaf(d_b, isum_b,
