@@ -210,8 +210,8 @@ int coli_moe_layer(const coli_moe_dims *dims, int32_t n_tokens, const float *x,
  *                0, or bit 0 (1) non-finite input or gate weights, bit 1 (2)
  *                an expert index out of range or repeated in a token, bit 2
  *                (4) a routed expert's blob pointer is NULL, bit 3 (8) a
- *                persistent kernel's grid barrier gave up waiting; with NULL
- *                the bits are cleared unread
+ *                kernel's bounded wait for the other workgroups of its launch
+ *                gave up; with NULL the bits are cleared unread
  * Other arguments as for coli_moe_layer.  Every call on one GPU shares
  * that GPU's scratch, so calls that overlap on one GPU (several streams or
  * threads at once) race and give unspecified results; calls on one stream

@@ -484,6 +484,8 @@ int layer_launches(const coli_moe_dims *d, int32_t S, const float *x, const floa
             r.norm = d->norm_topk_prob;
             r.rsf = d->routed_scaling_factor;
             r.hs = reinterpret_cast<float *>(w8 + L.hs);
+            r.slots = reinterpret_cast<uint64_t *>(w8 + L.slots);
+            r.epoch = reinterpret_cast<uint32_t *>(w8) + WS_EPOCH;
             r.I = d->inter;
             r.bits = d->wbits;
             r.group = kernel_group(d);
@@ -644,7 +646,8 @@ int coli_moe_status(void *ws, void *stream) {
     e = hipMemset(ws, 0, sizeof s);
     if (e != hipSuccess) return hip_fail(e, "status clear");
     if (s & ST_TIMEOUT)
-        return fail(COLI_EHIP, "a persistent kernel's grid barrier timed out: not all workgroups were resident (status 0x%x)", s);
+        return fail(COLI_EHIP, "a kernel's wait for the other workgroups of its launch timed out: not all of them "
+                               "were resident (status 0x%x)", s);
     if (s & ST_BADINDEX) return fail(COLI_EINVAL, "expert index out of range or repeated within a token (status 0x%x)", s);
     if (s & ST_NONFINITE) return fail(COLI_ENONFINITE, "non-finite input or undefined gate weights (status 0x%x)", s);
     return fail(COLI_ENOTRESIDENT, "a routed expert blob was NULL (status 0x%x)", s);

@@ -24,7 +24,7 @@ enum : uint32_t {
     ST_NONFINITE = 1u,     // NaN/Inf in x, W_r, bias, logits or gate weights
     ST_BADINDEX = 2u,      // expert index out of range or repeated in a token
     ST_NOTRESIDENT = 4u,   // routed expert blob pointer is NULL
-    ST_TIMEOUT = 8u,       // a grid barrier of a persistent kernel gave up waiting
+    ST_TIMEOUT = 8u,       // a wait for other workgroups of the launch gave up (bounded spin)
 };
 
 // Device-scope (all L2 slices) relaxed accesses, for data exchanged between
@@ -38,6 +38,15 @@ __device__ __forceinline__ void st_dev(int32_t *p, int32_t v) {
 }
 __device__ __forceinline__ void st_dev(float *p, float v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev64(uint64_t *p, uint64_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_dev64(const uint64_t *p) {
+    return __hip_atomic_load(const_cast<uint64_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ld_dev(const uint32_t *p) {
+    return __hip_atomic_load(const_cast<uint32_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ float ld_dev(const float *p) {
     return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -206,6 +206,53 @@ __device__ __forceinline__ void gateup_unit_primed(const uint8_t *blob, int H, i
     }
 }
 
+// gateup_half_f32 with packed codes (BITS 4 or 2), per-row scales and rows
+// of NCH = (H / 32 + 63) / 64 <= 4 chunks: the activations are staged first
+// (stage(0, np): Q8_0 of x into LDS, ending with a workgroup barrier), then
+// every chunk of the wave's 8 rows goes out at once with the row scale — one
+// memory round trip for the whole half tile — and the chunks are reduced in
+// order as they arrive.  Results as gateup_half_f32.
+template <int BITS, int NT, int NCH, typename Stage>
+__device__ __forceinline__ void gateup_half_primed(const uint8_t *blob, int H, int I, int i0, int np, uint8_t *smem,
+                                                   const SmemPlan &L, float *__restrict__ hs, Stage stage) {
+    static_assert(BITS == 4 || BITS == 2, "one buffer load per block");
+    constexpr int RPW = 8;
+    const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
+    const int8_t *vq = reinterpret_cast<const int8_t *>(smem + L.vq);
+    const float *vd = reinterpret_cast<const float *>(smem + L.vd);
+    int32_t *isum_wave = reinterpret_cast<int32_t *>(smem + L.isum) + wave * NT * RPW * ISUM_PITCH;
+    float *gu = reinterpret_cast<float *>(smem + L.gu);
+    const BlobLayout BL = blob_layout(H, I, BITS, 0, false);
+    const size_t row_bytes = (size_t)H * BITS / 8;
+    const int r0 = i0 + RPW * (wave & 1);
+    const size_t mat = wave < 2 ? BL.gate : BL.up;
+    const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(blob, (uint32_t)BL.total);
+    uint32_t rowoff[RPW];
+#pragma unroll
+    for (int j = 0; j < RPW; ++j) rowoff[j] = (uint32_t)(mat + (size_t)(r0 + j) * row_bytes);
+    const int nb = H / 32, vds = vd_stride(nb);
+    const int crow = lane % RPW, cvec = lane / RPW;
+    stage(0, np);
+    const uint32_t soff = (uint32_t)((wave < 2 ? BL.s_gate : BL.s_up) + 4 * (size_t)(r0 + crow));
+    const float rs = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsrc, soff, 0, 0));
+    BlockBits<BITS> X[NCH][RPW];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        issue_chunk<BITS, RPW>(rsrc, rowoff, c, X[c]);
+        __builtin_amdgcn_sched_barrier(0);   // chunks in order
+    }
+    float acc = 0.0f;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) acc = reduce_chunk<BITS, NT, RPW>(X[c], c, nb, np, vq, vd, vds, H, isum_wave, acc);
+    // gu[v * 32 + k]: gate rows (k < 16) then up rows of vector v
+    if (cvec < np) gu[cvec * 32 + wave * RPW + crow] = acc * rs;
+    __syncthreads();
+    if (tid < np * 16) {
+        const int v = tid >> 4, i = tid & 15;
+        hs[(size_t)v * I + i0 + i] = swiglu_f32(gu[v * 32 + i], gu[v * 32 + 16 + i]);
+    }
+}
+
 // Gate/up of rows i0 .. i0+15 of one unit for the np <= NT pair slots
 // slots[0 .. np), with SwiGLU: h (binary32, not quantised) of slot v's row
 // i0 + i goes to hs[v * I + i0 + i].  Waves 0-1 stream 8 gate rows each,

@@ -12,7 +12,7 @@ namespace coli {
 // Workspace carve-up for a call with S tokens.  The status word sits at a
 // fixed offset (it persists between calls); the rest is per call.
 struct WsLayout {
-    size_t status, flags, logits, units, tiles, qx, dx, qh, dh, Y, hs, total;
+    size_t status, flags, logits, units, tiles, qx, dx, qh, dh, Y, hs, slots, total;
 };
 
 // Tiles of the batch-union kernels for large batches: up to PF_TOK pairs of
@@ -39,6 +39,10 @@ constexpr int WS_SYNC_LAYER = 32;
 // ROUTE_FUSE_MAX tokens), then one for the tokens whose selection is done.
 constexpr int WS_SYNC_ROUTE = 48;
 constexpr int ROUTE_FUSE_MAX = 8;
+// Word index of the one-token router's epoch: the number of one-token router
+// launches on this workspace so far (mod 2^32); a launch tags its published
+// logits with epoch + 1 and its selecting workgroup stores epoch + 1.
+constexpr int WS_EPOCH = 60;
 
 inline size_t al256h(size_t v) { return (v + 255) & ~(size_t)255; }
 
@@ -78,7 +82,8 @@ inline WsLayout ws_layout(int H, int I, int E, int K, int S) {
     L.dh = al256h(L.qh + slots * (size_t)I);
     L.Y = al256h(L.dh + 4 * slots * (size_t)(I / 32));
     L.hs = al256h(L.Y + 4 * slots * (size_t)H);
-    L.total = al256h(L.hs + 4 * (size_t)(S < 2 ? S : 2) * (size_t)I);
+    L.slots = al256h(L.hs + 4 * (size_t)(S < 2 ? S : 2) * (size_t)I);
+    L.total = al256h(L.slots + 8 * (size_t)E);
     return L;
 }
 
@@ -123,6 +128,8 @@ struct RouteArgs {
     uint8_t *units;
     uint32_t *sync;
     float *hs;                     // with sg: the shared expert's h [S, I], binary32
+    uint64_t *slots;               // one token: [E] published logits, (tag << 32) | binary32 bits
+    uint32_t *epoch;               // one token: the workspace's router epoch (WS_EPOCH)
     int S, H, E, K, n_shared, norm;
     int I, bits, group, mx;        // expert shape, code width, scale group, MXFP4 (for sg)
     int sg;                        // 1: the launch also runs the shared expert's gate/up tiles

@@ -2,6 +2,8 @@
 // one launch that also selects and builds the unit table of the call
 // (coli_moe_layer, up to ROUTE_FUSE_MAX tokens).  The device routines are
 // in router.h.
+#include <type_traits>
+
 #include "device_common.h"
 #include "gateup.h"
 #include "kernels.h"
@@ -107,8 +109,167 @@ __device__ __forceinline__ void shared_gateup_half(const RouteArgs &r, uint8_t *
         }
         __syncthreads();
     };
+    if constexpr ((BITS == 4 || BITS == 2) && !GROUPED && !MX) {
+        const int nch = (nb + 63) / 64;
+        if (S <= NT && nch <= 4) {
+            auto go = [&](auto nch_c) {
+                gateup_half_primed<BITS, NT, decltype(nch_c)::value>(uniform_ptr(r.shared), H, r.I, 16 * half, S,
+                                                                     smem, L, r.hs, stage);
+            };
+            if (nch == 1)
+                go(std::integral_constant<int, 1>());
+            else if (nch == 2)
+                go(std::integral_constant<int, 2>());
+            else if (nch == 3)
+                go(std::integral_constant<int, 3>());
+            else
+                go(std::integral_constant<int, 4>());
+            return;
+        }
+    }
     gateup_half_f32<BITS, NT, GROUPED, MX>(uniform_ptr(r.shared), H, r.I, r.group, 16 * half, S, smem, L, L.total, r.hs,
                                        stage);
+}
+
+// Spin bound of the one-token selection's wait for the published logits.
+constexpr uint32_t ROUTE_SPIN_LIMIT = 1u << 22;
+
+// The logit workgroups of a one-token launch with at most 256 experts
+// ("Colibri (colibrì): GLM-5.2 local inference on 25 GB of RAM", "How it
+// works (validated core mechanics)": sigmoid scores, the bias ranks only,
+// lower id wins a tie, the weights are the unbiased sigmoids renormalised).
+// Wave w < lpw of logit workgroup bx computes logit lpw bx + w and publishes
+// it as one 64-bit word (tag << 32) | bits, the tag being the workspace's
+// epoch + 1, so that no arrival counter is needed.  Logit workgroup 0 then
+// selects.  Thread e waits (bounded) until slot e carries the tag and forms
+// expert e's sort key (order-preserving key of its score) << 32 | ~e, which
+// orders the experts as the selection does (score desc, id asc) with no two
+// equal.  The top-K come from ranks: each thread counts the keys of its own
+// wavefront above its own (the wavefront's K best are candidates, 4 K in
+// all), then each candidate counts the candidates above it; the K
+// candidates of rank < K are the selection, in rank order.  It writes idx /
+// w (weights: (sig_k / ((sig_0 + sig_1) + ...)) * rsf, or sig_k * rsf), the
+// unit table (unit j: the selected expert of the j-th smallest id, its pair
+// slot its rank; then the shared expert) and the next epoch.  On a
+// non-finite input or weight sum, or a wait that gave up, the table holds
+// the shared expert alone.
+template <int MAXJ>
+__device__ __forceinline__ void route_one(const RouteArgs &r, int bx, int lpw) {
+    __shared__ __attribute__((aligned(16))) uint64_t s_key[256];
+    __shared__ __attribute__((aligned(16))) uint64_t s_ck[4 * 32];
+    __shared__ int32_t s_cid[4 * 32];
+    __shared__ float s_sig[256];
+    __shared__ int32_t s_sel[32];
+    __shared__ const uint8_t *s_blob[256];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int E = r.E, K = r.K, H = r.H;
+    const uint32_t tag = ld_dev(r.epoch) + 1u;
+    const bool selector = bx == 0;
+    // the selector's inputs besides the logits, fetched ahead of them
+    float my_bias = 0.0f;
+    const uint8_t *my_blob = nullptr;
+    if (selector && tid < E) {
+        if (r.bias) my_bias = r.bias[tid];
+        my_blob = r.blobs[tid];
+    }
+    const int e = bx * lpw + wave;
+    if (wave < lpw && e < E) {
+        bool ok;
+        const float p = logit_wave<MAXJ>(r.x, r.W + (size_t)e * H, H, &ok);
+        if (!ok) raise_status(r.status, ST_NONFINITE);
+        if (lane == 0) st_dev64(&r.slots[e], ((uint64_t)tag << 32) | __float_as_uint(p));
+    }
+    if (!selector) return;
+    bool late = false;
+    float lg = 0.0f;
+    const bool valid = tid < E;
+    if (valid) {
+        uint32_t spins = 0;
+        uint64_t v = ld_dev64(&r.slots[tid]);
+        while ((uint32_t)(v >> 32) != tag) {
+            __builtin_amdgcn_s_sleep(1);
+            if (++spins >= ROUTE_SPIN_LIMIT) {
+                late = true;
+                break;
+            }
+            v = ld_dev64(&r.slots[tid]);
+        }
+        lg = __uint_as_float((uint32_t)v);
+    }
+    const float sig = sigmoid_f32(lg);
+    const float score = sig + my_bias;
+    const bool finite_in = !valid || (finite_f32(lg) && finite_f32(my_bias));
+    // the score part is 0 for a missing expert and for a score not above
+    // -inf (NaN included); the id part keeps every key distinct and puts the
+    // missing experts (ids E and up) last
+    const uint32_t sk = valid && score > -__builtin_inff() ? f32_key(score) : 0u;
+    const uint64_t key = ((uint64_t)sk << 32) | (uint32_t)~(uint32_t)tid;
+    s_key[tid] = key;
+    s_sig[tid] = sig;
+    s_blob[tid] = my_blob;
+    const int bad_in = __syncthreads_or(!finite_in);
+    const int timed_out = __syncthreads_or(late);
+    // rank within the wavefront
+    int c1 = 0;
+    const uint64_t *wk = s_key + wave * 64;
+#pragma unroll 8
+    for (int j = 0; j < 64; ++j) c1 += wk[j] > key ? 1 : 0;
+    if (c1 < K) {
+        s_ck[wave * K + c1] = key;
+        s_cid[wave * K + c1] = tid;
+    }
+    __syncthreads();
+    if (tid < 4 * K) {
+        int c2 = 0;
+        const uint64_t ck = s_ck[tid];
+        for (int j = 0; j < 4 * K; ++j) c2 += s_ck[j] > ck ? 1 : 0;
+        if (c2 < K) s_sel[c2] = s_cid[tid];
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    const int32_t si = lane < K ? s_sel[lane] : 0;
+    const float ssig = lane < K ? s_sig[si] : 0.0f;
+    float denom = 1.0f;
+    bool wok = true;
+    if (r.norm) {
+        denom = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ssig), 0));
+        for (int k = 1; k < K; ++k) denom = denom + __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ssig), k));
+        wok = denom > 0.0f && finite_f32(denom);
+    }
+    const float sw = r.norm ? (ssig / denom) * r.rsf : ssig * r.rsf;
+    const UnitTable U = unit_table(1, K, E);
+    int32_t *tab = reinterpret_cast<int32_t *>(r.units);
+    const uint8_t **ublob = reinterpret_cast<const uint8_t **>(r.units + U.ublob);
+    if (lane < K) {
+        r.idx_out[lane] = si;
+        r.w_out[lane] = sw;
+    }
+    const bool good = !bad_in && !timed_out && wok;
+    int u = 0;   // position of si among the selected ids, ascending
+    for (int j = 0; j < K; ++j) u += __builtin_amdgcn_readlane(si, j) < si ? 1 : 0;
+    if (good && lane < K) {
+        tab[U.uexp + u] = si;
+        tab[U.uoff + u] = u;
+        tab[U.pairs + u] = lane;
+        ublob[u] = s_blob[si];
+    }
+    if (lane == 0) {
+        const int ns = r.n_shared;
+        if (!good) raise_status(r.status, timed_out ? ST_TIMEOUT : ST_NONFINITE);
+        const int nr = good ? K : 0;   // routed units
+        tab[0] = nr + ns;
+        tab[1] = nr;
+        tab[2] = nr;
+        tab[3] = 0;
+        if (ns) {
+            tab[U.uexp + nr] = -1;
+            tab[U.uoff + nr] = nr;
+            tab[U.pairs + nr] = K;
+            ublob[nr] = r.shared;
+        }
+        tab[U.uoff + nr + ns] = nr + ns;
+        st_dev(r.epoch, tag);
+    }
 }
 
 template <int MAXJ, int BITS, int NT, bool GROUPED, bool MX = false>
@@ -126,6 +287,10 @@ __global__ __launch_bounds__(64 * RF_W) void k_route_fused(const RouteArgs r) {
     const int lpw = rf_lpw(S), n_lw = (E + lpw - 1) / lpw;
     if (bx >= n_lw) {
         quant_x_wave(r.x, r.qx, r.dx, r.status, H, t, (bx - n_lw) * RF_W + wave);
+        return;
+    }
+    if (S == 1 && E <= 256) {
+        route_one<MAXJ>(r, bx, lpw);
         return;
     }
     // wave 0 fetches what the selection needs besides the logits (the bias
