@@ -302,6 +302,16 @@ int coli_moe_debug_expf(int64_t n, const float *x, float *y, void *stream);
  * lane layout of the prefill kernels is checked against a host matmul). */
 int coli_moe_debug_mfma_i8(const int8_t *a, const int8_t *b, int32_t *c, void *stream);
 
+/* One v_mfma_scale_f32_32x32x64_f8f6f4 on raw lane registers: lane l (of
+ * 64) takes its A and B registers from bytes 32 l .. 32 l + 31 of device a
+ * and b and its E8M0 scales from byte l of device sa and sb, and writes its
+ * 16 binary32 results to device c[16 l .. 16 l + 15].  fmt_a / fmt_b: 0 FP8
+ * E4M3, 4 FP4 E2M1 (A only); COLI_EINVAL for other pairs.  The lane layout
+ * and scaling the MXFP4 prefill kernels assume are checked against a host
+ * model through it. */
+int coli_moe_debug_mfma_f8f6f4(int32_t fmt_a, int32_t fmt_b, const uint8_t *a, const uint8_t *b,
+                               const uint8_t *sa, const uint8_t *sb, float *c, void *stream);
+
 /* Q8_0 of device f32 v [n_rows, cols] into device int8 q and f32 d
  * [n_rows, cols/32], with the device quantiser the kernels use. */
 int coli_moe_debug_q8_0(int32_t n_rows, int32_t cols, const float *v, int8_t *q, float *d,

@@ -39,7 +39,7 @@ EXPORTS = (
     "coli_moe_debug_logits", "coli_moe_debug_expf", "coli_moe_debug_q8_0",
     "coli_moe_debug_force_path", "coli_moe_layer", "coli_moe_debug_mfma_i8",
     "coli_moe_roof_sink_words", "coli_moe_roof_stream_read", "coli_moe_roof_mfma_i8",
-    "coli_moe_layer_noalloc",
+    "coli_moe_layer_noalloc", "coli_moe_debug_mfma_f8f6f4",
 )
 
 KIND_ROUTER_LOGITS, KIND_ROUTER_SELECT, KIND_GATEUP, KIND_DOWN, KIND_COMBINE = 0, 1, 2, 3, 4
@@ -85,6 +85,7 @@ _sigs = {
     "coli_moe_debug_force_path": (ctypes.c_int, [_I32]),
     "coli_moe_layer": (ctypes.c_int, [_D, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "coli_moe_debug_mfma_i8": (ctypes.c_int, [_P, _P, _P, _P]),
+    "coli_moe_debug_mfma_f8f6f4": (ctypes.c_int, [_I32, _I32, _P, _P, _P, _P, _P, _P]),
     "coli_moe_roof_sink_words": (_SZ, []),
     "coli_moe_roof_stream_read": (ctypes.c_int, [_P, _SZ, _P, _P]),
     "coli_moe_roof_mfma_i8": (ctypes.c_int, [_I32, _P, _P]),
@@ -315,6 +316,18 @@ def coli_moe_debug_mfma_i8(a, b, c, stream=None):
         raise ValueError("a, b and c hold 64 lanes x 16 registers")
     _check(_lib.coli_moe_debug_mfma_i8(_dev(a, torch.int8, "a"), _dev(b, torch.int8, "b"),
                                        _dev(c, torch.int32, "c"), _stream(stream)), "coli_moe_debug_mfma_i8")
+
+
+def coli_moe_debug_mfma_f8f6f4(fmt_a: int, fmt_b: int, a, b, sa, sb, c, stream=None):
+    """a, b: device uint8 [64, 32] raw lane registers; sa, sb: device uint8
+    [64] E8M0 scales; c: device float32 [64, 16]."""
+    import torch
+    if a.numel() != 2048 or b.numel() != 2048 or sa.numel() != 64 or sb.numel() != 64 or c.numel() != 1024:
+        raise ValueError("a, b: 64 lanes x 32 bytes; sa, sb: 64 bytes; c: 64 lanes x 16 floats")
+    _check(_lib.coli_moe_debug_mfma_f8f6f4(int(fmt_a), int(fmt_b), _dev(a, torch.uint8, "a"), _dev(b, torch.uint8, "b"),
+                                           _dev(sa, torch.uint8, "sa"), _dev(sb, torch.uint8, "sb"),
+                                           _dev(c, torch.float32, "c"), _stream(stream)),
+           "coli_moe_debug_mfma_f8f6f4")
 
 
 def coli_moe_roof_sink_words() -> int:

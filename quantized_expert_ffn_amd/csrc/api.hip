@@ -751,6 +751,17 @@ int coli_moe_debug_mfma_i8(const int8_t *a, const int8_t *b, int32_t *c, void *s
     return e == hipSuccess ? COLI_OK : hip_fail(e, "debug_mfma_i8 launch");
 }
 
+int coli_moe_debug_mfma_f8f6f4(int32_t fmt_a, int32_t fmt_b, const uint8_t *a, const uint8_t *b, const uint8_t *sa,
+                               const uint8_t *sb, float *c, void *stream) {
+    if (!a || !b || !sa || !sb || !c) return fail(COLI_EINVAL, "debug_mfma_f8f6f4: NULL pointer argument");
+    if (!((fmt_a == 0 || fmt_a == 4) && fmt_b == 0))
+        return fail(COLI_EINVAL, "debug_mfma_f8f6f4: formats (A, B) must be (0, 0) or (4, 0)");
+    int rc = check_device();
+    if (rc) return rc;
+    hipError_t e = launch_debug_mfma_f8f6f4(fmt_a, fmt_b, a, b, sa, sb, c, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? COLI_OK : hip_fail(e, "debug_mfma_f8f6f4 launch");
+}
+
 size_t coli_moe_roof_sink_words(void) { return (size_t)ROOF_GRID * 256; }
 
 int coli_moe_roof_stream_read(const void *src, size_t bytes, uint32_t *sink, void *stream) {

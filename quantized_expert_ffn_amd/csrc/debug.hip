@@ -162,6 +162,33 @@ hipError_t launch_debug_mfma_i8(const int8_t *a, const int8_t *b, int32_t *c, hi
     return hipGetLastError();
 }
 
+// One scaled f8f6f4 MFMA on raw lane registers: lane l's A and B registers
+// are bytes 32 l .. 32 l + 31 of a and b, its scales bytes l of sa and sb;
+// its 16 results go to c[16 l .. 16 l + 15].  FA / FB: operand formats.
+template <int FA, int FB>
+__global__ __launch_bounds__(64) void k_debug_mfma_f8f6f4(const uint8_t *__restrict__ a,
+                                                          const uint8_t *__restrict__ b,
+                                                          const uint8_t *__restrict__ sa,
+                                                          const uint8_t *__restrict__ sb, float *__restrict__ c) {
+    const int l = threadIdx.x;
+    const i32x8 av = reinterpret_cast<const i32x8 *>(a)[l];
+    const i32x8 bv = reinterpret_cast<const i32x8 *>(b)[l];
+    const f32x16 cv = mfma_scale_f8f6f4<FA, FB>(av, bv, (int)sa[l], (int)sb[l]);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) c[16 * l + r] = cv[r];
+}
+
+hipError_t launch_debug_mfma_f8f6f4(int fa, int fb, const uint8_t *a, const uint8_t *b, const uint8_t *sa,
+                                    const uint8_t *sb, float *c, hipStream_t st) {
+    if (fa == 0 && fb == 0)
+        hipLaunchKernelGGL((k_debug_mfma_f8f6f4<0, 0>), dim3(1), dim3(64), 0, st, a, b, sa, sb, c);
+    else if (fa == 4 && fb == 0)
+        hipLaunchKernelGGL((k_debug_mfma_f8f6f4<4, 0>), dim3(1), dim3(64), 0, st, a, b, sa, sb, c);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
 // ---- measured roofs ------------------------------------------------------
 // A streaming read of n16 16-byte words (ROOF_SR_UNROLL loads per thread in
 // flight, grid-stride), every thread XOR-folding what it read into one sink

@@ -132,6 +132,143 @@ def test_mfma_i8_lane_layout(torch):
     assert bad.size == 0, f"{len(bad)} lane registers differ, first (lane, register) {bad[:4].tolist()}"
 
 
+def _e4m3(byte: int, bias: int = 7) -> float:
+    """OCP FP8 E4M3 (bias 7; S.1111.111 is NaN), or with bias 8 the older
+    variant, for the diagnostics."""
+    s = -1.0 if byte & 0x80 else 1.0
+    e, m = (byte >> 3) & 15, byte & 7
+    if e == 15 and m == 7:
+        return float("nan")
+    if e == 0:
+        return s * (m / 8.0) * 2.0 ** (1 - bias)
+    return s * (1.0 + m / 8.0) * 2.0 ** (e - bias)
+
+
+def _e2m1(code: int) -> float:
+    s = -1.0 if code & 8 else 1.0
+    e, m = (code >> 1) & 3, code & 1
+    return s * (m * 0.5 if e == 0 else (1.0 + m / 2.0) * 2.0 ** (e - 1))
+
+
+def _k_fp8(half: int, j: int) -> int:
+    """K of byte j of an FP8 operand in lane half `half`: bytes 0-15 belong
+    to the first 32-deep scale block, bytes 16-31 to the second, and the two
+    lane halves hold the two 16-element halves of each block."""
+    return 32 * (j // 16) + 16 * half + j % 16
+
+
+def _mfma_f8f6f4_model(fmt_a, a_raw, b_raw, sa, sb, bias=7):
+    """C of one scaled 32x32x64 MFMA under the assumed lane layout (float64).
+    FP4 A: lane half h holds scale block h, its 32 elements as the nibbles of
+    its first 16 bytes (element j: byte j / 2, even j in the low nibble).
+    The scale of row (column) i and block kb comes from lane 32 kb + i."""
+    A = np.zeros((32, 64))
+    B = np.zeros((64, 32))
+    SA = np.zeros((32, 2))
+    SB = np.zeros((32, 2))
+    for lane in range(64):
+        i, half = lane % 32, lane // 32
+        for j in range(32):
+            if fmt_a == 4:
+                byte = int(a_raw[lane, j // 2])
+                A[i, 32 * half + j] = _e2m1(byte & 15 if j % 2 == 0 else byte >> 4)
+            else:
+                A[i, _k_fp8(half, j)] = _e4m3(int(a_raw[lane, j]), bias)
+            B[_k_fp8(half, j), i] = _e4m3(int(b_raw[lane, j]), bias)
+        SA[i, half] = 2.0 ** (int(sa[lane]) - 127)
+        SB[i, half] = 2.0 ** (int(sb[lane]) - 127)
+    C = np.zeros((32, 32))
+    for kb in range(2):
+        C += (SA[:, kb:kb + 1] * SB[:, kb][None, :]) * (A[:, 32 * kb:32 * kb + 32] @ B[32 * kb:32 * kb + 32, :])
+    want = np.zeros((64, 16))
+    for lane in range(64):
+        for r in range(16):
+            want[lane, r] = C[8 * (r // 4) + 4 * (lane // 32) + r % 4, lane % 32]
+    return want
+
+
+@pytest.mark.parametrize("fmt_a", [0, 4])
+def test_mfma_f8f6f4_lane_layout_and_scales(torch, fmt_a):
+    """The lane layout and E8M0 scaling the MXFP4 prefill kernels assume for
+    v_mfma_scale_f32_32x32x64_f8f6f4 (A FP8 E4M3 or FP4 E2M1, B FP8 E4M3)
+    reproduce a float64 host model exactly: the operands are small integers
+    and halves and the scales powers of two, so every sum is exact.  With
+    FP4 A the last four registers of every lane hold random bytes, which must
+    not matter."""
+    say(f"mfma scale f8f6f4 32x32x64 layout, A format {fmt_a}")
+    rng = np.random.default_rng(12 + fmt_a)
+    # E4M3 bytes of the integers -16 .. 16 (and the halves -2 .. 2)
+    vals = sorted({b for b in range(256) if not np.isnan(_e4m3(b)) and abs(_e4m3(b)) <= 16
+                   and (2 * _e4m3(b)).is_integer()})
+    b_raw = rng.choice(np.array(vals, np.uint8), size=(64, 32))
+    if fmt_a == 4:
+        a_raw = rng.integers(0, 256, size=(64, 32), dtype=np.uint8)
+    else:
+        a_raw = rng.choice(np.array(vals, np.uint8), size=(64, 32))
+    # the two blocks' partial sums differ in scale by at most 2^8, so every
+    # sum stays within binary32's 24 bits
+    sa = rng.integers(125, 130, size=64, dtype=np.uint8)
+    sb = rng.integers(125, 130, size=64, dtype=np.uint8)
+    c = torch.zeros((64, 16), dtype=torch.float32, device="cuda")
+    q().coli_moe_debug_mfma_f8f6f4(fmt_a, 0, torch.from_numpy(a_raw).cuda(), torch.from_numpy(b_raw).cuda(),
+                                   torch.from_numpy(sa).cuda(), torch.from_numpy(sb).cuda(), c)
+    got = c.cpu().numpy().astype(np.float64)
+    want = _mfma_f8f6f4_model(fmt_a, a_raw, b_raw, sa, sb)
+    bad = np.argwhere(got != want)
+    if bad.size:
+        alt = _mfma_f8f6f4_model(fmt_a, a_raw, b_raw, sa, sb, bias=8)
+        unscaled = _mfma_f8f6f4_model(fmt_a, a_raw, b_raw, np.full(64, 127), np.full(64, 127))
+        raise AssertionError(f"{len(bad)} lane registers differ, first {bad[:4].tolist()}: got "
+                             f"{got[tuple(bad[0])]}, want {want[tuple(bad[0])]}; bias-8 model matches "
+                             f"{int((got == alt).sum())}/1024, unscaled model {int((got == unscaled).sum())}/1024")
+
+
+def test_mfma_fp4_times_split_activations_is_the_block_sum(torch):
+    """The MXFP4 prefill product: A = a row's 32 E2M1 codes of one block in
+    both scale blocks with the row's E8M0 scale x; B = the Q8_0 codes q of a
+    column split as q = 16 hi + lo, E4M3 hi in the first scale block (scale
+    2^4) and E4M3 lo in the second (scale 1), laid out as the kernels stage
+    them.  Every result must be 2^(x - 128) * sum_j t_j q_j exactly, t_j
+    twice the E2M1 value (the block sum of the MXFP4 chain)."""
+    say("mfma fp4 x split activations")
+    rng = np.random.default_rng(21)
+    enc = {}
+    for byte in range(128):
+        v = _e4m3(byte)
+        if float(v).is_integer() and 0 <= v <= 15:
+            enc.setdefault(int(v), byte)
+    for v in range(-8, 0):
+        enc[v] = enc[-v] | 0x80 if -v <= 15 else None
+    e2m1 = np.array([_e2m1(c) for c in range(16)])
+    sb = np.concatenate([np.full(32, 131, np.uint8), np.full(32, 127, np.uint8)])
+    for trial in range(8):
+        codes = rng.integers(0, 16, size=(32, 32))              # [row][j]
+        qv = rng.integers(-127, 128, size=(32, 32))             # [column][j]
+        if trial == 0:
+            codes[:] = 15                                       # -6 everywhere
+            qv[:] = 127
+        x = rng.integers(40, 200, size=32).astype(np.uint8)
+        hi, lo = qv >> 4, qv & 15
+        a = rng.integers(0, 256, size=(64, 32)).astype(np.uint8)  # bytes 16-31 unused
+        b = np.zeros((64, 32), np.uint8)
+        for lane in range(64):
+            i, half = lane % 32, lane // 32
+            a[lane, :16] = [codes[i, 2 * j] | (codes[i, 2 * j + 1] << 4) for j in range(16)]
+            js = range(16 * half, 16 * half + 16)
+            b[lane, :16] = [enc[int(hi[i, j])] for j in js]
+            b[lane, 16:] = [enc[int(lo[i, j])] for j in js]
+        c = torch.zeros((64, 16), dtype=torch.float32, device="cuda")
+        q().coli_moe_debug_mfma_f8f6f4(4, 0, torch.from_numpy(a).cuda(), torch.from_numpy(b).cuda(),
+                                       torch.from_numpy(np.concatenate([x, x])).cuda(), torch.from_numpy(sb).cuda(), c)
+        got = c.cpu().numpy().astype(np.float64)
+        isum = (2 * e2m1[codes]) @ qv.T                          # [row][column], exact integers
+        C = isum * 2.0 ** (x.astype(np.float64)[:, None] - 128)
+        want = np.array([[C[8 * (r // 4) + 4 * (lane // 32) + r % 4, lane % 32] for r in range(16)]
+                         for lane in range(64)])
+        bad = np.argwhere(got != want)
+        assert bad.size == 0, f"trial {trial}: {len(bad)} differ, first {bad[0].tolist()}: {got[tuple(bad[0])]} vs {want[tuple(bad[0])]}"
+
+
 def test_roof_stream_read_reads_every_word(torch):
     """The streaming-read roof kernel really reads the whole buffer: thread g
     of the grid XOR-folds the 16-byte words g, g + T, g + 2T, ... (T threads)."""
