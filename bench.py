@@ -62,7 +62,7 @@ def parse():
     ap.add_argument("--group-size", type=int, choices=(0, 64), default=0,
                     help="decode / prefill: 64 = group-scaled int4 experts (one scale per 64 codes of a row)")
     ap.add_argument("--wformat", choices=("int", "mxfp4"), default="int",
-                    help="decode: mxfp4 = MXFP4 experts (E2M1 codes, one E8M0 scale per 32 codes of a row)")
+                    help="decode, prefill: mxfp4 = MXFP4 experts (E2M1 codes, one E8M0 scale per 32 codes of a row)")
     ap.add_argument("--tier-layers", type=int, default=75, help="tiered: layers streamed")
     ap.add_argument("--host-layers", type=int, default=8,
                     help="tiered: distinct layers of expert bytes in pinned host memory (reused cyclically)")
@@ -99,6 +99,7 @@ def parse():
 
 PATHS = {"auto": 0, "multi": 1, "persistent": 2, "grouped": 3}
 INT8_PEAK_TOPS = 5000.0   # MI355X dense int8 matrix-core peak
+FP8_PEAK_TOPS = 5000.0    # MI355X dense FP8 matrix-core peak (TFLOP/s)
 
 
 def main():
@@ -432,15 +433,23 @@ def run_prefill(args, q, synth, embedded=False):
     import numpy as np
     import torch
 
-    spec = synth.GLM_GS64 if args.group_size else synth.GLM
-    pf_kernel = "k_pf_gateup<4,gs64>" if spec.group else "k_pf_gateup<4>"
+    mx = args.wformat == "mxfp4"
+    if mx and args.group_size:
+        raise SystemExit("--wformat mxfp4 takes no --group-size")
+    spec = synth.GLM_MX if mx else (synth.GLM_GS64 if args.group_size else synth.GLM)
+    pf_kernel = "k_pf_gateup_mx" if mx else ("k_pf_gateup<4,gs64>" if spec.group else "k_pf_gateup<4>")
+    # the peak of the products' own format: int8, or FP8 for the MXFP4
+    # kernels' E2M1 x E4M3 products (the FP8 rate; the split of each Q8_0
+    # code into two E4M3 parts doubles their matrix-core work)
+    peak = FP8_PEAK_TOPS if mx else INT8_PEAK_TOPS
     dims = q.make_dims(spec)
     S, H, I, E, K = args.tokens, spec.hidden, spec.inter, spec.n_experts, spec.top_k
     bb = spec.blob_bytes
     t0 = time.time()
     host = torch.empty((E + 1) * bb, dtype=torch.uint8, pin_memory=True)
+    fill = synth.mx_cdf_expert_into if mx else synth.cdf_expert_into
     for e in range(E + 1):
-        synth.cdf_expert_into(host.data_ptr() + e * bb, args.seed, 0, e, spec)
+        fill(host.data_ptr() + e * bb, args.seed, 0, e, spec)
     dev = host.cuda()
     table = torch.tensor([dev.data_ptr() + e * bb for e in range(E)], dtype=torch.int64, device="cuda")
     shared = dev.data_ptr() + E * bb
@@ -511,13 +520,14 @@ def run_prefill(args, q, synth, embedded=False):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "i8xi4->i32,f32",
+        "dtype": "e2m1xe4m3->f32" if mx else "i8xi4->i32,f32",
         "data": "synthetic (seeded; GLM-5.2-shaped random-code experts, Zipf(1.1)-routed tokens)",
         "config": {
             "workload": f"GLM-5.2-shaped MoE prefill layer, {S} tokens/step: hidden 6144, expert inter 2048, "
                         "256 routed experts top-8 + 1 shared, "
-                        + ("int4 weights with one scale per 64 codes of a row, " if spec.group
-                           else "int4 per-row-scaled weights, ") + "Q8_0 activations, "
+                        + ("MXFP4 weights (E2M1 codes, one E8M0 scale per 32 codes of a row) on the FP4 "
+                           "matrix cores, " if mx else "int4 weights with one scale per 64 codes of a row, "
+                           if spec.group else "int4 per-row-scaled weights, ") + "Q8_0 activations, "
                         "fp32 router gate, zero bias; Zipf(1.1) expert popularity; all 257 experts resident",
             "tokens_per_step": S, "graph_steps": G, "graph_replays": reps, "kernels": args.kernels,
             "routing": {"unique": int((counts > 0).sum()), "min": int(counts[counts > 0].min()),
@@ -525,17 +535,17 @@ def run_prefill(args, q, synth, embedded=False):
         },
         "roofline": {
             "bound": "mfma", "kernel": pf_kernel,
-            "achieved": round(achieved, 1), "peak": INT8_PEAK_TOPS, "unit": "TOPS",
-            "frac": round(achieved / INT8_PEAK_TOPS, 4), "traffic": counted_traffic(pf_kernel),
+            "achieved": round(achieved, 1), "peak": peak, "unit": "TOPS",
+            "frac": round(achieved / peak, 4), "traffic": counted_traffic(pf_kernel),
             "algorithmic_ops_per_launch": ops_gateup, "avg_launch_us": round(g_us, 3),
         },
-        "layer_int8_tops": round(layer_tops, 1),
-        "layer_int8_frac": round(layer_tops / INT8_PEAK_TOPS, 4),
-        # the attainable roofline of the whole layer: min(int8 peak, its
+        "layer_tops": round(layer_tops, 1),
+        "layer_frac": round(layer_tops / peak, 4),
+        # the attainable roofline of the whole layer: min(peak, its
         # arithmetic intensity (ops per algorithmic HBM byte) x HBM peak)
         "layer_ops_per_byte": round(ops_layer / hbm_bytes, 1),
-        "layer_attainable_tops": round(min(INT8_PEAK_TOPS, ops_layer / hbm_bytes * HBM_PEAK_GBS / 1e3), 1),
-        "layer_frac_of_attainable": round(layer_tops / min(INT8_PEAK_TOPS, ops_layer / hbm_bytes * HBM_PEAK_GBS / 1e3), 4),
+        "layer_attainable_tops": round(min(peak, ops_layer / hbm_bytes * HBM_PEAK_GBS / 1e3), 1),
+        "layer_frac_of_attainable": round(layer_tops / min(peak, ops_layer / hbm_bytes * HBM_PEAK_GBS / 1e3), 4),
         "layer_hbm_gbs": round(hbm_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         "ms_per_step_p10_p50_p90": replay_spread(rep_ev, G),
         "kernel_avg_us": {k: round(v, 3) for k, v in kernel_us.items()},

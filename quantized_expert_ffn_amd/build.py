@@ -16,7 +16,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(OUT_DIR, "libcolimoe.so")
-SOURCES = ["route.hip", "forward.hip", "down_rows.hip", "prefill.hip", "layer.hip", "debug.hip", "api.hip"]
+SOURCES = ["route.hip", "forward.hip", "down_rows.hip", "prefill.hip", "prefill_mx.hip", "layer.hip", "debug.hip",
+           "api.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -111,10 +111,10 @@ int g_force_path = 0;
 constexpr int GROUPED_MIN_S = 9;
 
 // The grouped kernels take integer codes with per-row scales or groups of
-// 64; other group sizes and MXFP4 run the multi-launch kernels at every
-// batch size.
+// 64, and MXFP4 codes; other group sizes run the multi-launch kernels at
+// every batch size.
 bool use_grouped(int S, int group, bool mx) {
-    return !mx && (group == 0 || group == 64) && (g_force_path == 3 || (g_force_path == 0 && S >= GROUPED_MIN_S));
+    return (mx || group == 0 || group == 64) && (g_force_path == 3 || (g_force_path == 0 && S >= GROUPED_MIN_S));
 }
 
 // The group size the kernels see: MXFP4 has one (E8M0) scale per 32 codes.
@@ -133,7 +133,6 @@ int forced_path_refused(const coli_moe_dims *d) {
     if (d->group_size && d->group_size != 64 && g_force_path == 3)
         return fail(COLI_EINVAL, "the grouped kernels take per-row scales or groups of 64 (group_size=%d)",
                     d->group_size);
-    if (is_mx(d) && g_force_path == 3) return fail(COLI_EINVAL, "the grouped kernels take integer codes only");
     return COLI_OK;
 }
 
@@ -215,6 +214,8 @@ FwdArgs fwd_args(const coli_moe_dims *d, int S, const float *x, const int32_t *i
     a.n_shared = d->n_shared;
     a.group = kernel_group(d);
     a.mx = is_mx(d) ? 1 : 0;
+    a.qxs = is_mx(d) ? w8 + L.qxs : nullptr;
+    a.qhs = is_mx(d) ? w8 + L.qhs : nullptr;
     return a;
 }
 
@@ -235,17 +236,26 @@ int route_launches(const coli_moe_dims *d, int S, const float *x, const float *r
         if (quant_x) {
             timing_before(KK_QUANT_X, st);
             e = launch_quant_x(x, reinterpret_cast<int8_t *>(w8 + L.qx), reinterpret_cast<float *>(w8 + L.dx),
-                               status, S, d->hidden, st);
+                               is_mx(d) ? w8 + L.qxs : nullptr, status, S, d->hidden, st);
             timing_after(KK_QUANT_X, st);
             if (e != hipSuccess) return hip_fail(e, "Q8_0(x) launch");
         }
     } else {
+        // (MXFP4 experts also need the split codes of Q8_0(x): k_quant_x)
+        const bool fused_qx = quant_x && !is_mx(d);
         timing_before(KK_ROUTER_LOGITS, st);
         e = launch_router_logits(x, router_w, logits, status, S, d->hidden, d->n_experts,
-                                 quant_x ? reinterpret_cast<int8_t *>(w8 + L.qx) : nullptr,
-                                 quant_x ? reinterpret_cast<float *>(w8 + L.dx) : nullptr, st);
+                                 fused_qx ? reinterpret_cast<int8_t *>(w8 + L.qx) : nullptr,
+                                 fused_qx ? reinterpret_cast<float *>(w8 + L.dx) : nullptr, st);
         timing_after(KK_ROUTER_LOGITS, st);
         if (e != hipSuccess) return hip_fail(e, "router logits launch");
+        if (quant_x && !fused_qx) {
+            timing_before(KK_QUANT_X, st);
+            e = launch_quant_x(x, reinterpret_cast<int8_t *>(w8 + L.qx), reinterpret_cast<float *>(w8 + L.dx),
+                               w8 + L.qxs, status, S, d->hidden, st);
+            timing_after(KK_QUANT_X, st);
+            if (e != hipSuccess) return hip_fail(e, "Q8_0(x) launch");
+        }
     }
     if (!select) return COLI_OK;
     timing_before(KK_ROUTER_SELECT, st);
@@ -263,7 +273,7 @@ int forward_launches(FwdArgs &a, int bits, bool any_pending, void *pending_ready
     hipError_t e;
     if (!qx_ready) {
         timing_before(KK_QUANT_X, st);
-        e = launch_quant_x(a.x, const_cast<int8_t *>(a.qx), const_cast<float *>(a.dx), a.status, a.S, a.H, st);
+        e = launch_quant_x(a.x, const_cast<int8_t *>(a.qx), const_cast<float *>(a.dx), a.qxs, a.status, a.S, a.H, st);
         timing_after(KK_QUANT_X, st);
         if (e != hipSuccess) return hip_fail(e, "Q8_0(x) launch");
     }
@@ -342,7 +352,7 @@ size_t coli_moe_expert_bytes(const coli_moe_dims *d) {
 
 size_t coli_moe_workspace_bytes(const coli_moe_dims *d, int32_t max_tokens) {
     if (check_dims(d) != COLI_OK || max_tokens < 0 || max_tokens > COLI_MAX_TOKENS) return 0;
-    return ws_layout(d->hidden, d->inter, d->n_experts, d->top_k, max_tokens).total;
+    return ws_layout(d->hidden, d->inter, d->n_experts, d->top_k, max_tokens, is_mx(d)).total;
 }
 
 const char *coli_moe_last_error(void) { return g_err.c_str(); }
@@ -358,7 +368,7 @@ int coli_moe_route(const coli_moe_dims *d, int32_t S, const float *x, const floa
         return fail(COLI_EINVAL, "coli_moe_route: NULL pointer argument");
     if (!aligned16(x) || !aligned16(router_w))
         return fail(COLI_EINVAL, "coli_moe_route: x and router_w must be 16-byte aligned");
-    const WsLayout L = ws_layout(d->hidden, d->inter, d->n_experts, d->top_k, S);
+    const WsLayout L = ws_layout(d->hidden, d->inter, d->n_experts, d->top_k, S, is_mx(d));
     if (ws_bytes < L.total)
         return fail(COLI_EWORKSPACE, "workspace %zu bytes < %zu needed for %d tokens", ws_bytes, L.total, S);
     if ((rc = check_device())) return rc;
@@ -380,7 +390,7 @@ int coli_moe_forward(const coli_moe_dims *d, int32_t S, const float *x, const in
         return fail(COLI_EINVAL, "coli_moe_forward: x, out and shared_blob must be 16-byte aligned");
     if (d->n_shared && !shared_blob)
         return fail(COLI_ENOTRESIDENT, "n_shared=1 but shared_blob is NULL");
-    const WsLayout L = ws_layout(d->hidden, d->inter, d->n_experts, d->top_k, S);
+    const WsLayout L = ws_layout(d->hidden, d->inter, d->n_experts, d->top_k, S, is_mx(d));
     if (ws_bytes < L.total)
         return fail(COLI_EWORKSPACE, "workspace %zu bytes < %zu needed for %d tokens", ws_bytes, L.total, S);
     if ((rc = forced_path_refused(d))) return rc;
@@ -446,7 +456,7 @@ int layer_launches(const coli_moe_dims *d, int32_t S, const float *x, const floa
                    const float *router_bias, const void *const *expert_blobs, const void *shared_blob,
                    int32_t *topk_idx, float *topk_w, float *out, void *ws, hipStream_t st) {
     int rc;
-    const WsLayout L = ws_layout(d->hidden, d->inter, d->n_experts, d->top_k, S);
+    const WsLayout L = ws_layout(d->hidden, d->inter, d->n_experts, d->top_k, S, is_mx(d));
     if ((rc = forced_path_refused(d))) return rc;
     if (g_force_path == 2 && !persistent_fits(d, S, false))
         return fail(COLI_EINVAL, "persistent kernel forced but the call has more than 8 tokens or a shape beyond "
@@ -540,7 +550,7 @@ int coli_moe_layer(const coli_moe_dims *d, int32_t S, const float *x, const floa
     int rc = layer_args_ok(d, S, x, router_w, expert_blobs, shared_blob, topk_idx, topk_w, out, "coli_moe_layer");
     if (rc || S == 0) return rc;
     if (!ws) return fail(COLI_EINVAL, "coli_moe_layer: NULL pointer argument");
-    const WsLayout L = ws_layout(d->hidden, d->inter, d->n_experts, d->top_k, S);
+    const WsLayout L = ws_layout(d->hidden, d->inter, d->n_experts, d->top_k, S, is_mx(d));
     if (ws_bytes < L.total)
         return fail(COLI_EWORKSPACE, "workspace %zu bytes < %zu needed for %d tokens", ws_bytes, L.total, S);
     return layer_launches(d, S, x, router_w, router_bias, expert_blobs, shared_blob, topk_idx, topk_w, out, ws,
@@ -599,7 +609,7 @@ int coli_moe_layer_noalloc(const coli_moe_dims *d, int32_t S, const float *x, co
     int rc = layer_args_ok(d, S, x, router_w, expert_blobs, shared_blob, topk_idx, topk_w, out,
                            "coli_moe_layer_noalloc");
     if (rc || S == 0) return rc;
-    const WsLayout L = ws_layout(d->hidden, d->inter, d->n_experts, d->top_k, S);
+    const WsLayout L = ws_layout(d->hidden, d->inter, d->n_experts, d->top_k, S, is_mx(d));
     if (L.total > NOALLOC_SCRATCH_BYTES)
         return fail(COLI_EWORKSPACE,
                     "coli_moe_layer_noalloc: %d tokens need %zu bytes of scratch, more than its %zu; "

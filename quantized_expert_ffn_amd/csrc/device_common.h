@@ -175,6 +175,41 @@ __device__ __forceinline__ float q8_0_block_words(const float *__restrict__ x, u
     return d;
 }
 
+// E4M3 byte (OCP FP8: 1 sign, 4 exponent bits of bias 7, 3 mantissa bits)
+// of an integer v in -15 .. 15, exact: |v| = 1.m * 2^e with e = floor(log2 |v|).
+__device__ __forceinline__ uint32_t e4m3_small(int v) {
+    const uint32_t u = (uint32_t)(v < 0 ? -v : v);
+    if (u == 0) return 0u;
+    const int e = 31 - __builtin_clz(u);
+    return (v < 0 ? 0x80u : 0u) | ((uint32_t)(e + 7) << 3) | ((u << (3 - e)) & 7u);
+}
+
+// The Q8_0 codes of one block (w: 32 int8 codes, four per word) split for
+// the FP8 matrix cores: q = 16 hi + lo with hi = q >> 4 in -8 .. 7 and
+// lo = q & 15 in 0 .. 15, both exact in E4M3.  64 bytes: the E4M3 of hi for
+// codes 0-15, of lo for codes 0-15, of hi for 16-31, of lo for 16-31 — the
+// two 32-byte halves are the B operands of lane halves 0 and 1 (bytes 0-15
+// in the first scale block, scaled by 2^4, bytes 16-31 in the second).
+__device__ __forceinline__ void split_e4m3(const uint32_t w[8], u32x4 out[4]) {
+    uint32_t hw[8], lw[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        uint32_t h = 0, l = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int q = (int)(int8_t)(uint8_t)(w[i] >> (8 * j));
+            h |= e4m3_small(q >> 4) << (8 * j);
+            l |= e4m3_small(q & 15) << (8 * j);
+        }
+        hw[i] = h;
+        lw[i] = l;
+    }
+    out[0] = u32x4{hw[0], hw[1], hw[2], hw[3]};
+    out[1] = u32x4{lw[0], lw[1], lw[2], lw[3]};
+    out[2] = u32x4{hw[4], hw[5], hw[6], hw[7]};
+    out[3] = u32x4{lw[4], lw[5], lw[6], lw[7]};
+}
+
 // As q8_0_block_words, storing the codes to q[0..31] (16-byte aligned).
 __device__ __forceinline__ float q8_0_block_lane(const float *__restrict__ x, int8_t *__restrict__ q, bool *ok) {
     uint32_t w[8];

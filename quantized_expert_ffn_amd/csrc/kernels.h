@@ -12,7 +12,7 @@ namespace coli {
 // Workspace carve-up for a call with S tokens.  The status word sits at a
 // fixed offset (it persists between calls); the rest is per call.
 struct WsLayout {
-    size_t status, flags, logits, units, tiles, qx, dx, qh, dh, Y, hs, slots, total;
+    size_t status, flags, logits, units, tiles, qx, dx, qh, dh, Y, hs, slots, qxs, qhs, total;
 };
 
 // Tiles of the batch-union kernels for large batches: up to PF_TOK pairs of
@@ -68,7 +68,9 @@ __host__ __device__ inline UnitTable unit_table(int S, int K, int E) {
     return u;
 }
 
-inline WsLayout ws_layout(int H, int I, int E, int K, int S) {
+// mx: MXFP4 experts, whose grouped kernels also take the Q8_0 codes of x
+// and of h split for the matrix cores (split_e4m3: 64 bytes per block).
+inline WsLayout ws_layout(int H, int I, int E, int K, int S, bool mx = false) {
     WsLayout L;
     const size_t slots = (size_t)S * (size_t)(K + 1);
     L.status = 0;
@@ -83,7 +85,9 @@ inline WsLayout ws_layout(int H, int I, int E, int K, int S) {
     L.Y = al256h(L.dh + 4 * slots * (size_t)(I / 32));
     L.hs = al256h(L.Y + 4 * slots * (size_t)H);
     L.slots = al256h(L.hs + 4 * (size_t)(S < 2 ? S : 2) * (size_t)I);
-    L.total = al256h(L.slots + 8 * (size_t)E);
+    L.qxs = al256h(L.slots + 8 * (size_t)E);
+    L.qhs = al256h(L.qxs + (mx ? 2 * (size_t)S * (size_t)H : 0));
+    L.total = al256h(L.qhs + (mx ? 2 * slots * (size_t)I : 0));
     return L;
 }
 
@@ -109,6 +113,8 @@ struct FwdArgs {
     const float *hs;               // [S, I]  the shared expert's h, binary32 (with shared_done)
     int group;                     // 0: per-row scales; else one scale per `group` codes of a row
     int mx;                        // 1: MXFP4 codes and E8M0 scales (group is then 32)
+    uint8_t *qxs;                  // MXFP4 grouped kernels: Q8_0(x) split [S][H / 32][64] (split_e4m3)
+    uint8_t *qhs;                  // and Q8_0(h) split [S*(K+1)][I / 32][64]
     uint32_t pend[32];             // bit e: expert e pending
 };
 
@@ -147,7 +153,7 @@ inline bool route_shared_fits(int S, int H, int bits) {
 // Router logits; with qx non-null the same launch writes Q8_0(x) to qx / dx.
 hipError_t launch_router_logits(const float *x, const float *W, float *logits, uint32_t *status,
                                 int S, int H, int E, int8_t *qx, float *dx, hipStream_t st);
-hipError_t launch_quant_x(const float *x, int8_t *qx, float *dx, uint32_t *status, int S, int H,
+hipError_t launch_quant_x(const float *x, int8_t *qx, float *dx, uint8_t *qxs, uint32_t *status, int S, int H,
                           hipStream_t st);
 hipError_t launch_router_select(const float *logits, const float *bias, int32_t *idx, float *w,
                                 uint32_t *status, int S, int E, int K, float rsf, int norm,
@@ -225,6 +231,8 @@ hipError_t launch_group(const int32_t *idx, int S, int K, int E, int n_shared, u
 size_t pf_group_smem(int S, int K, int E);
 hipError_t launch_pf_gateup(const FwdArgs &a, const int32_t *tiles, int bits, hipStream_t st);
 hipError_t launch_pf_down(const FwdArgs &a, const int32_t *tiles, int bits, hipStream_t st);
+hipError_t launch_pf_gateup_mx(const FwdArgs &a, const int32_t *tiles, hipStream_t st);
+hipError_t launch_pf_down_mx(const FwdArgs &a, const int32_t *tiles, hipStream_t st);
 size_t forward_smem_max(int S, int H, int I, int E, int K, int n_shared, int group);
 
 hipError_t launch_debug_unpack(int bits, int rows, int cols, const void *src, int8_t *out,

@@ -719,8 +719,9 @@ static hipError_t pf_down_bits(const FwdArgs &a, const int32_t *tiles, hipStream
 }
 
 // Group-scaled weights: int4 with groups of 64 (the API routes other group
-// sizes to the decode kernels).
+// sizes to the decode kernels); MXFP4 weights: prefill_mx.hip.
 hipError_t launch_pf_gateup(const FwdArgs &a, const int32_t *tiles, int bits, hipStream_t st) {
+    if (a.mx) return launch_pf_gateup_mx(a, tiles, st);
     if (a.group) return pf_gateup_bits<4, true>(a, tiles, st);
     if (bits == 8) return pf_gateup_bits<8>(a, tiles, st);
     if (bits == 4) return pf_gateup_bits<4>(a, tiles, st);
@@ -728,6 +729,7 @@ hipError_t launch_pf_gateup(const FwdArgs &a, const int32_t *tiles, int bits, hi
 }
 
 hipError_t launch_pf_down(const FwdArgs &a, const int32_t *tiles, int bits, hipStream_t st) {
+    if (a.mx) return launch_pf_down_mx(a, tiles, st);
     if (a.group) return pf_down_bits<4, true>(a, tiles, st);
     if (bits == 8) return pf_down_bits<8>(a, tiles, st);
     if (bits == 4) return pf_down_bits<4>(a, tiles, st);

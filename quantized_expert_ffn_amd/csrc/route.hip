@@ -501,11 +501,35 @@ hipError_t launch_route_fused(const RouteArgs &r, hipStream_t st) {
     return route_fused_maxj<16>(r, grid, smem, st);
 }
 
-// Q8_0 of the hidden states alone.  Grid: (ceil(H / 2048), S), 64 threads.
+// Q8_0 of the hidden states alone, and with qxs also their split codes
+// (split_e4m3) for the MXFP4 grouped kernels.  Grid: (ceil(H / 2048), S),
+// 64 threads.
 __global__ __launch_bounds__(64) void k_quant_x(const float *__restrict__ x, int8_t *__restrict__ qx,
-                                                float *__restrict__ dx, uint32_t *__restrict__ status,
-                                                int H) {
-    quant_x_wave(x, qx, dx, status, H, blockIdx.y, blockIdx.x);
+                                                float *__restrict__ dx, uint8_t *__restrict__ qxs,
+                                                uint32_t *__restrict__ status, int H) {
+    const int t = blockIdx.y, nbx = H / 32;
+    const int b = (int)blockIdx.x * 64 + (int)(threadIdx.x & 63);
+    if (b >= nbx) return;
+    bool ok;
+    uint32_t w[8];
+    const float d = q8_0_block_words(x + (size_t)t * H + 32 * b, w, &ok);
+    u32x4 *qv = reinterpret_cast<u32x4 *>(qx + (size_t)t * H + 32 * b);
+    qv[0] = u32x4{w[0], w[1], w[2], w[3]};
+    qv[1] = u32x4{w[4], w[5], w[6], w[7]};
+    dx[(size_t)t * nbx + b] = d;
+    if (!ok) raise_status(status, ST_NONFINITE);
+    if (qxs) {
+        u32x4 sp[4];
+        split_e4m3(w, sp);
+        u32x4 *dst = reinterpret_cast<u32x4 *>(qxs + ((size_t)t * nbx + b) * 64);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) dst[k] = sp[k];
+    }
+}
+
+hipError_t launch_quant_x(const float *x, int8_t *qx, float *dx, uint8_t *qxs, uint32_t *status, int S, int H,
+                          hipStream_t st) {
+    return launch(k_quant_x, dim3((H / 32 + 63) / 64, S), dim3(64), 0, st, x, qx, dx, qxs, status, H);
 }
 
 hipError_t launch_router_logits(const float *x, const float *W, float *logits, uint32_t *status,
@@ -513,11 +537,6 @@ hipError_t launch_router_logits(const float *x, const float *W, float *logits, u
     const int gx = E + (qx ? (H / 32 + 63) / 64 : 0);
     if (H <= 24 * 256) return launch(k_router_logits<24>, dim3(gx, S), dim3(64), 0, st, x, W, logits, status, H, E, qx, dx);
     return launch(k_router_logits<16>, dim3(gx, S), dim3(64), 0, st, x, W, logits, status, H, E, qx, dx);
-}
-
-hipError_t launch_quant_x(const float *x, int8_t *qx, float *dx, uint32_t *status, int S, int H,
-                          hipStream_t st) {
-    return launch(k_quant_x, dim3((H / 32 + 63) / 64, S), dim3(64), 0, st, x, qx, dx, status, H);
 }
 
 hipError_t launch_router_select(const float *logits, const float *bias, int32_t *idx, float *w,

@@ -86,7 +86,7 @@ def test_mx_layer(torch, name, S):
     parity(out2, o_out)
 
 
-@pytest.mark.parametrize("S", [1, 2, 5, 12])
+@pytest.mark.parametrize("S", [1, 2, 5, 12, 40])
 def test_mx_extreme_codes_and_subnormal_scales(torch, S):
     from synth.device import upload_layer
     spec = synth.TINY_MX
@@ -135,14 +135,39 @@ def test_mx_refusals(torch):
     d = synth.tiny_layer(seed=78, S=2, spec=spec)
     dl = upload_layer(d)
     dims = qm.make_dims(spec)
-    for path in (qm.PATH_PERSISTENT, qm.PATH_GROUPED):
-        qm.coli_moe_debug_force_path(path)
-        try:
-            with pytest.raises(qm.ColiError) as e:
-                _layer_call(torch, dims, dl, 2)
-            assert e.value.code == qm.COLI_EINVAL
-        finally:
-            qm.coli_moe_debug_force_path(qm.PATH_AUTO)
+    qm.coli_moe_debug_force_path(qm.PATH_PERSISTENT)
+    try:
+        with pytest.raises(qm.ColiError) as e:
+            _layer_call(torch, dims, dl, 2)
+        assert e.value.code == qm.COLI_EINVAL
+    finally:
+        qm.coli_moe_debug_force_path(qm.PATH_AUTO)
+
+
+@pytest.mark.parametrize("S", [1, 3, 8])
+@pytest.mark.parametrize("extreme", [False, True])
+def test_mx_forced_grouped(torch, S, extreme):
+    """The MXFP4 grouped kernels (FP4 matrix cores) forced at small batch
+    sizes: tiles of one to a few pairs, with ordinary scales (the scaled
+    products) and with extreme codes and E8M0 bytes 0, 1 and 2 (the tiles
+    recomputed with unscaled products); bitwise equal to the oracle."""
+    from synth.device import upload_layer
+    qm = q()
+    spec = synth.TINY_MX
+    say(f"mx forced grouped S={S} extreme={extreme}")
+    d = (synth.extreme_mx_layer(seed=95 + S, S=S, spec=spec) if extreme
+         else synth.tiny_layer(seed=85 + S, S=S, spec=spec))
+    o_out, o_idx, o_w = oracle.layer(spec, d["x"], d["router_w"], d["bias"], d["blobs"], d["shared"])
+    dims = qm.make_dims(spec)
+    dl = upload_layer(d)
+    qm.coli_moe_debug_force_path(qm.PATH_GROUPED)
+    try:
+        ws, idx, w, out = _layer_call(torch, dims, dl, S)
+    finally:
+        qm.coli_moe_debug_force_path(qm.PATH_AUTO)
+    assert status(ws) == 0, qm.coli_moe_last_error()
+    assert np.array_equal(idx, o_idx)
+    parity(out, o_out)
 
 
 @pytest.mark.parametrize("S", [1, 4])

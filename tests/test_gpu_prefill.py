@@ -64,14 +64,16 @@ def _histogram(idx, E):
             "max": int(c.max())}
 
 
-@pytest.mark.parametrize("bits", [4, 8, 2])
-def test_mid_zipf_layer(torch, bits):
-    """coli_moe_layer at 160 tokens (grouped kernels by default): every
-    output element against the oracle."""
-    spec = dataclasses.replace(MID, wbits=bits)
+@pytest.mark.parametrize("fmt", ["int4", "int8", "int2", "mxfp4"])
+def test_mid_zipf_layer(torch, fmt):
+    """coli_moe_layer at 160 tokens (grouped kernels by default; MXFP4
+    experts on the FP4 matrix cores): every output element against the
+    oracle."""
+    bits = 4 if fmt == "mxfp4" else int(fmt[3:])
+    spec = dataclasses.replace(MID, wbits=bits, fmt=1 if fmt == "mxfp4" else 0)
     S = 160
-    say(f"grouped mid layer S={S} int{bits}")
-    d = _zipf_layer(spec, S, seed=bits)
+    say(f"grouped mid layer S={S} {fmt}")
+    d = _zipf_layer(spec, S, seed=bits + (10 if fmt == "mxfp4" else 0))
     dl = _upload(torch, d)
     ws = workspace(q().make_dims(spec), S)
     idx, w, out = _layer_call(torch, spec, dl, ws)
@@ -142,23 +144,25 @@ def test_pending_experts_grouped(torch):
 
 
 @pytest.mark.timeout(1500)
-def test_glm_prefill_2048_zipf(torch):
+@pytest.mark.parametrize("fmt", ["int4", "mxfp4"])
+def test_glm_prefill_2048_zipf(torch, fmt):
     """The batch-union prefill workload at its full size: GLM-5.2-shaped
-    layer (H 6144, I 2048, 256 experts top-8 + shared, int4), 2048 tokens with
-    Zipf(1.1) expert popularity, through coli_moe_layer as the benchmark
-    calls it.  Routing of all tokens against the oracle's router, and every
-    output row bitwise against the oracle's forward (the multi-threaded
-    build of the oracle, over chunks of tokens; it gives the same bits as the
-    single-threaded one)."""
-    spec, S = synth.GLM, 2048
-    say(f"glm prefill S={S} int4: generating inputs")
+    layer (H 6144, I 2048, 256 experts top-8 + shared, int4 or MXFP4), 2048
+    tokens with Zipf(1.1) expert popularity, through coli_moe_layer as the
+    benchmark calls it.  Routing of all tokens against the oracle's router,
+    and every output row bitwise against the oracle's forward (the
+    multi-threaded build of the oracle, over chunks of tokens; it gives the
+    same bits as the single-threaded one)."""
+    spec, S = (synth.GLM_MX if fmt == "mxfp4" else synth.GLM), 2048
+    say(f"glm prefill S={S} {fmt}: generating inputs")
     d = synth.layer_inputs(0, 0, spec, S)
     d["x"] = synth.prefill_hidden_states(0, 0, spec, S)
     d["bias"] = np.zeros(spec.n_experts, np.float32)
     E, bb = spec.n_experts, spec.blob_bytes
     host = np.empty((E + 1) * bb, np.uint8)
+    fill = synth.mx_cdf_expert_into if fmt == "mxfp4" else synth.cdf_expert_into
     for e in range(E + 1):
-        synth.cdf_expert_into(host.ctypes.data + e * bb, 0, 0, e, spec)
+        fill(host.ctypes.data + e * bb, 0, 0, e, spec)
     dev = torch.from_numpy(host).cuda()
     table = torch.tensor([dev.data_ptr() + e * bb for e in range(E)], dtype=torch.int64, device="cuda")
     dl = {"x": torch.from_numpy(d["x"]).cuda(), "router_w": torch.from_numpy(d["router_w"]).cuda(),
