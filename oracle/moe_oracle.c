@@ -272,10 +272,13 @@ float oq_e8m0(int x) {
 }
 
 void oq_unpack_mx(const uint8_t *src, int n, int8_t *out) {
+    /* the 16 values 2 * e2m1(code), taken from oq_e2m1 once per call */
+    int8_t twice[16];
+    for (int code = 0; code < 16; ++code) twice[code] = (int8_t)(2.0f * oq_e2m1(code));
     for (int j = 0; j < n; ++j) {
         int byte = src[j / 2];
         int code = (j % 2 == 0) ? (byte & 0xF) : (byte >> 4);
-        out[j] = (int8_t)(2.0f * oq_e2m1(code));
+        out[j] = twice[code];
     }
 }
 
