@@ -32,6 +32,10 @@ namespace coli {
 constexpr int MX_T = 256;      // threads per workgroup (4 waves)
 constexpr int MX_ROWS = 128;   // rows per workgroup (32 per wave)
 constexpr int MX_C = 8;        // blocks per stage
+// stages of loads in flight (two measured no faster than one: the kernels
+// are bound by LDS reads, not by the loads)
+template <int NM>
+constexpr int MX_DEPTH = 1;
 
 // Fast-path scale bounds (see above): x_lo <= x <= x_hi and d = 0 or
 // d_lo <= d <= d_hi give 2^-126 <= d * 2^(x - 128) and
@@ -205,21 +209,82 @@ __device__ __forceinline__ void mx_blocks(float (&acc)[NM][16], const uint8_t *l
     }
 }
 
+// A full stage on the fast path, in the order that keeps the matrix core
+// and the vector ALU busy together: the products of unit u = (block j,
+// matrix m) go to buffer u % 2, and unit u's product is issued before unit
+// u - 1's chain step reads its buffer.
+template <int NM>
+__device__ __forceinline__ void mx_blocks_full(float (&acc)[NM][16], const uint8_t *lds) {
+    using ST = MxStage<NM>;
+    constexpr int U = MX_C * NM;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, h = lane >> 5, n = lane & 31;
+    const int row = 32 * wave + n;
+    const uint8_t *lw = lds + ST::WS * row;
+    const uint32_t *lx = reinterpret_cast<const uint32_t *>(lds + ST::W_BYTES);
+    const uint8_t *la = lds + ST::W_BYTES + ST::X_BYTES + ST::AS * n + 32 * h;
+    const float *ld = reinterpret_cast<const float *>(lds + ST::W_BYTES + ST::X_BYTES + ST::A_BYTES) + n;
+    const int sb = h ? 127 : 131;
+    uint32_t xw[NM][2];
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+        xw[m][0] = lx[2 * (m * MX_ROWS + row)];
+        xw[m][1] = lx[2 * (m * MX_ROWS + row) + 1];
+    }
+    f32x16 P[2];
+    i32x8 bv;
+#pragma unroll
+    for (int u = 0; u <= U; ++u) {
+        if (u < U) {
+            const int j = u / NM, m = u % NM;
+            if (m == 0) {
+                const u32x4 b0 = *reinterpret_cast<const u32x4 *>(la + 64 * j);
+                const u32x4 b1 = *reinterpret_cast<const u32x4 *>(la + 64 * j + 16);
+                bv = i32x8{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+            }
+            const u32x4 a4 = *reinterpret_cast<const u32x4 *>(lw + m * MX_ROWS * ST::WS + 16 * j);
+            const i32x8 av = {(int)a4.x, (int)a4.y, (int)a4.z, (int)a4.w, 0, 0, 0, 0};
+            const int sa = (int)((xw[m][j >> 2] >> (8 * (j & 3))) & 0xFFu);
+            P[u & 1] = mfma_scale_f8f6f4<4, 0>(av, bv, sa, sb);
+        }
+        if (u > 0) {
+            const int v = u - 1, j = v / NM, m = v % NM;
+            const float d = ld[32 * j];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[m][r] = __builtin_fmaf(d, P[v & 1][r], acc[m][r]);
+        }
+    }
+}
+
 // Every stage of the tile.  All waves load, store and meet at the barriers;
-// `active` waves compute.
-template <int NM, bool FAST>
+// `active` waves compute.  The loads run DEPTH stages ahead, rotating over
+// DEPTH register sets (the barriers order LDS only, so every set stays in
+// flight across them).
+template <int NM, bool FAST, int DEPTH>
 __device__ __forceinline__ void mx_run(float (&acc)[NM][16], uint8_t *lds, const MxSrc<NM> &src,
                                        const uint32_t *col_aoff, const uint32_t *col_doff, bool active, int *bad) {
     const int n_stages = (src.nb + MX_C - 1) / MX_C;
-    MxRegs<NM> R;
-    mx_load<NM>(R, src, col_aoff, col_doff, 0);
-    for (int s = 0; s < n_stages; ++s) {
-        const int nblk = min(MX_C, src.nb - MX_C * s);
-        if (s > 0) __syncthreads();   // every wave is done with the previous stage
-        mx_store<NM>(R, lds, nblk, bad);
-        __syncthreads();
-        if (s + 1 < n_stages) mx_load<NM>(R, src, col_aoff, col_doff, s + 1);
-        if (active) mx_blocks<NM, FAST>(acc, lds, nblk);
+    MxRegs<NM> R[DEPTH];
+#pragma unroll
+    for (int k = 0; k < DEPTH; ++k)
+        if (k < n_stages) mx_load<NM>(R[k], src, col_aoff, col_doff, k);
+    for (int s0 = 0; s0 < n_stages; s0 += DEPTH) {
+#pragma unroll
+        for (int k = 0; k < DEPTH; ++k) {
+            const int s = s0 + k;
+            if (s < n_stages) {
+                const int nblk = min(MX_C, src.nb - MX_C * s);
+                if (s > 0) lds_barrier();   // every wave is done with the previous stage
+                mx_store<NM>(R[k], lds, nblk, bad);
+                lds_barrier();
+                if (s + DEPTH < n_stages) mx_load<NM>(R[k], src, col_aoff, col_doff, s + DEPTH);
+                if (active) {
+                    if (FAST && nblk == MX_C)
+                        mx_blocks_full<NM>(acc, lds);
+                    else
+                        mx_blocks<NM, FAST>(acc, lds, nblk);
+                }
+            }
+        }
     }
 }
 
@@ -229,13 +294,13 @@ template <int NM>
 __device__ __forceinline__ void mx_tile(float (&acc)[NM][16], uint8_t *lds, const MxSrc<NM> &src,
                                         const uint32_t *col_aoff, const uint32_t *col_doff, bool active) {
     int bad = 0;
-    mx_run<NM, true>(acc, lds, src, col_aoff, col_doff, active, &bad);
+    mx_run<NM, true, MX_DEPTH<NM>>(acc, lds, src, col_aoff, col_doff, active, &bad);
     if (!__syncthreads_or(bad)) return;
 #pragma unroll
     for (int m = 0; m < NM; ++m)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[m][r] = 0.0f;
-    mx_run<NM, false>(acc, lds, src, col_aoff, col_doff, active, &bad);
+    mx_run<NM, false, MX_DEPTH<NM>>(acc, lds, src, col_aoff, col_doff, active, &bad);
 }
 
 struct MxTile {
@@ -337,7 +402,7 @@ __global__ __launch_bounds__(MX_T) __attribute__((amdgpu_waves_per_eu(2))) void 
 // Grid (ceil(H / 128), tile bound): Y[slot][row] = chain over the I / 32
 // blocks of Q8_0(h) of the slot (no row scale: the E8M0 bytes are in the
 // chain).
-__global__ __launch_bounds__(MX_T) __attribute__((amdgpu_waves_per_eu(2))) void k_pf_down_mx(
+__global__ __launch_bounds__(MX_T) __attribute__((amdgpu_waves_per_eu(3))) void k_pf_down_mx(
     const FwdArgs a, const int32_t *__restrict__ tiles) {
     using ST = MxStage<1>;
     __shared__ __attribute__((aligned(16))) uint8_t lds[ST::LDS];
