@@ -57,8 +57,10 @@ struct DownTilePlan {
 };
 // group > 0: room for the group scales of one batch of units (UB units x
 // DR_ROWS rows x I / group scales).
+// gs_bytes: bytes per staged scale (4: binary32 group scales; 1: raw E8M0
+// bytes of the slot-staged MXFP4 tile).
 __host__ __device__ inline DownTilePlan down_tile_plan(size_t base, int S, int K, int E, int n_shared, int I,
-                                                       int group = 0, int ub = 0) {
+                                                       int group = 0, int ub = 0, int gs_bytes = 4) {
     DownTilePlan p;
     const int P = S * K;
     const int umax = (P < E ? P : E) + 1;
@@ -70,8 +72,26 @@ __host__ __device__ inline DownTilePlan down_tile_plan(size_t base, int S, int K
     p.sdn = a16(p.isum + 4 * (size_t)DR_W * DR_RPW * mpb * ISUM_PITCH);
     p.y = a16(p.sdn + 4 * (size_t)umax * DR_ROWS);
     p.gs = a16(p.y + 4 * (size_t)slots * DR_ROWS);
-    p.end = a16(p.gs + (group ? 4 * (size_t)ub * DR_ROWS * (I / group) : 0));
+    p.end = a16(p.gs + (group ? (size_t)gs_bytes * ub * DR_ROWS * (I / group) : 0));
     return p;
+}
+
+// The MXFP4 chain of one (row, pair) over nb blocks from 0 with the row's
+// E8M0 bytes as raw words (4 blocks each): acc = fmaf(d_b * 2^(x_b - 128),
+// S_b, acc), S_b the exact binary32 block sum stored as its bits; the same
+// operations as chain_chunk_g<true> with group 32.
+__device__ __forceinline__ float chain_mx_bytes(const int32_t *is, const float *dv, const uint32_t *xw, int nb) {
+    float acc = 0.0f;
+    for (int b = 0; b < nb; b += 4) {
+        const i32x4 iv = *reinterpret_cast<const i32x4 *>(is + b);
+        const f32x4 dd = *reinterpret_cast<const f32x4 *>(dv + b);
+        const uint32_t x = xw[b / 4];
+        acc = __builtin_fmaf(dd.x * e8m0_half(x & 0xFFu), __int_as_float(iv.x), acc);
+        acc = __builtin_fmaf(dd.y * e8m0_half((x >> 8) & 0xFFu), __int_as_float(iv.y), acc);
+        acc = __builtin_fmaf(dd.z * e8m0_half((x >> 16) & 0xFFu), __int_as_float(iv.z), acc);
+        acc = __builtin_fmaf(dd.w * e8m0_half(x >> 24), __int_as_float(iv.w), acc);
+    }
+    return acc;
 }
 
 // One down tile.  COHERENT: Q8_0(h) was written earlier in the same launch
@@ -437,10 +457,24 @@ struct DownTile {
         const int rl = wave * DR_RPW + cr;
         int ub = 0;
         while (ub + 1 < n_units && uoff[ub + 1] <= cp) ++ub;
+        // MXFP4: the E8M0 bytes of this wave's rows of every unit (UB x
+        // DR_RPW rows of nbi bytes, kept raw in LDS) go out first, the
+        // weights right behind them
+        static_assert(!MX || UB * DR_RPW * 64 / 4 <= 64 * GW_MX, "one round of scale words");
+        uint32_t *gsw = reinterpret_cast<uint32_t *>(smem + D.gs) + wave * UB * DR_RPW * (nbi / 4);
+        const int nsw = n_units * DR_RPW * (nbi / 4);
+        uint32_t mxv[GW_MX];
+        if (MX) {
+#pragma unroll
+            for (int k = 0; k < GW_MX; ++k) {
+                const int w = lane + 64 * k;
+                mxv[k] = w < nsw ? mx_word(0, w) : 0u;
+            }
+        }
         issue(0, n_units, 0);
         float sd = 0.0f;
         const uint8_t *my_blob = chain ? ublob[ub] : nullptr;
-        if (my_blob) sd = reinterpret_cast<const float *>(my_blob + BL.s_down)[r0 + rl];
+        if (!MX && my_blob) sd = reinterpret_cast<const float *>(my_blob + BL.s_down)[r0 + rl];
         const int b = lane;
         const bool act = b < nbi;
 #pragma unroll
@@ -453,17 +487,41 @@ struct DownTile {
                 for (int q = q0; q < q1; ++q) {
                     int32_t av[8] = {0, 0, 0, 0, 0, 0, 0, 0};
                     if (act) load_act(qh_l + (size_t)pairs[q] * qpitch, b, av);
+                    if constexpr (MX) {
+                        // exact block sums in binary32 (see block_dot_mx_f16)
+                        f16x2 h[16];
+                        mx_act_f16(av, h);
 #pragma unroll
-                    for (int r = 0; r < DR_RPW; ++r)
-                        isum[(r * mpb + q) * ISUM_PITCH + lane] = (act && live) ? block_dot(wv[ui][r], av) : 0;
+                        for (int r = 0; r < DR_RPW; ++r)
+                            isum[(r * mpb + q) * ISUM_PITCH + lane] =
+                                (act && live) ? __float_as_int(block_dot_mx_f16(wv[ui][r].w, h)) : 0;
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < DR_RPW; ++r)
+                            isum[(r * mpb + q) * ISUM_PITCH + lane] = (act && live) ? block_dot(wv[ui][r], av) : 0;
+                    }
                 }
+            }
+        }
+        if (MX) {
+#pragma unroll
+            for (int k = 0; k < GW_MX; ++k) {
+                const int w = lane + 64 * k;
+                if (w < nsw) gsw[w] = mxv[k];
             }
         }
         wave_lds_sync();
         if (chain) {
             const int slot = pairs[cp];
-            const float acc = chain_chunk(0.0f, isum + (cr * mpb + cp) * ISUM_PITCH, dh_l + slot * dpitch, nbi);
-            y_l[slot * DR_ROWS + rl] = my_blob ? acc * sd : 0.0f;
+            if constexpr (MX) {
+                // multiplier d_b * 2^(x_b - 128) per block, no row scale
+                const float acc = chain_mx_bytes(isum + (cr * mpb + cp) * ISUM_PITCH, dh_l + slot * dpitch,
+                                                 gsw + (ub * DR_RPW + cr) * (nbi / 4), nbi);
+                y_l[slot * DR_ROWS + rl] = my_blob ? acc : 0.0f;
+            } else {
+                const float acc = chain_chunk(0.0f, isum + (cr * mpb + cp) * ISUM_PITCH, dh_l + slot * dpitch, nbi);
+                y_l[slot * DR_ROWS + rl] = my_blob ? acc * sd : 0.0f;
+            }
         }
         __syncthreads();
         combine();

@@ -18,7 +18,7 @@ struct DownRowsPlan {
 };
 
 __host__ __device__ inline DownRowsPlan down_rows_plan(int S, int K, int E, int n_shared, int I, int group,
-                                                       int bits) {
+                                                       int bits, int gs_bytes = 4) {
     DownRowsPlan p;
     const int P = S * K;
     const int umax = (P < E ? P : E) + 1;
@@ -26,7 +26,7 @@ __host__ __device__ inline DownRowsPlan down_rows_plan(int S, int K, int E, int 
     p.ublob = a16(p.T.total);
     p.w = a16(p.ublob + 8 * (size_t)umax);
     const int ub = bits == 8 ? DownRowsBatch<8>::UB : (bits == 4 ? DownRowsBatch<4>::UB : DownRowsBatch<2>::UB);
-    p.tile = down_tile_plan(p.w + 4 * (size_t)P, S, K, E, n_shared, I, group, ub);
+    p.tile = down_tile_plan(p.w + 4 * (size_t)P, S, K, E, n_shared, I, group, ub, gs_bytes);
     p.total = p.tile.end;
     return p;
 }
@@ -81,17 +81,18 @@ __global__ __launch_bounds__(DR_T) __attribute__((amdgpu_waves_per_eu(MX ? 2 : 3
 // the slots' Q8_0(h) is fetched in the same memory round trip as the table
 // (in slot order: its addresses do not depend on the routing), and the
 // weights go out as soon as the blob pointers are in (DownTile::run_staged).
-template <int BITS, bool ONE_TOKEN>
+template <int BITS, bool ONE_TOKEN, bool MX = false>
 __global__ __launch_bounds__(DR_T) __attribute__((amdgpu_waves_per_eu(3))) void k_down_rows_staged(const FwdArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int tid = threadIdx.x;
     const int S = a.S, K = a.K, E = a.E, P = S * K;
-    const DownRowsPlan D = down_rows_plan(S, K, E, a.n_shared, a.I, 0, BITS);
+    const DownRowsPlan D = down_rows_plan(S, K, E, a.n_shared, a.I, MX ? a.group : 0, BITS, 1);
     const uint8_t **ublob = reinterpret_cast<const uint8_t **>(smem + D.ublob);
     float *w_l = reinterpret_cast<float *>(smem + D.w);
     const UnitTable U = unit_table(S, K, E);
     int *tab = reinterpret_cast<int *>(smem);
-    DownTile<BITS, ONE_TOKEN, false> tile(a, smem, D.tile, tab + U.uoff, tab + U.pairs, ublob, w_l, 0, blockIdx.x);
+    DownTile<BITS, ONE_TOKEN, false, MX, MX> tile(a, smem, D.tile, tab + U.uoff, tab + U.pairs, ublob, w_l, 0,
+                                                  blockIdx.x);
     const int32_t tw = tid < U.words ? reinterpret_cast<const int32_t *>(a.units)[tid] : 0;
     const uint8_t *tb = tid < U.umax ? reinterpret_cast<const uint8_t *const *>(a.units + U.ublob)[tid] : nullptr;
     const float wt = tid < P ? a.w[tid] : 0.0f;
@@ -114,7 +115,8 @@ size_t down_rows_smem(int S, int I, int E, int K, int n_shared, int group, int b
 }
 
 hipError_t launch_down_rows(const FwdArgs &a, int bits, hipStream_t st) {
-    const size_t smem = down_rows_plan(a.S, a.K, a.E, a.n_shared, a.I, a.group, bits).total;
+    const bool staged = a.units && (a.mx || !a.group) && down_slots_fit(a.S, a.K, a.E, a.n_shared, a.I, bits);
+    const size_t smem = down_rows_plan(a.S, a.K, a.E, a.n_shared, a.I, a.group, bits, staged ? 1 : 4).total;
     const dim3 grid(a.H / DR_ROWS);
     auto go = [&](auto kern) {
         const hipError_t e = ensure_dyn_smem(reinterpret_cast<const void *>(kern), smem);
@@ -122,7 +124,8 @@ hipError_t launch_down_rows(const FwdArgs &a, int bits, hipStream_t st) {
         return launch(kern, grid, dim3(DR_T), smem, st, a);
     };
     const bool one = a.S == 1;
-    if (a.units && !a.mx && !a.group && down_slots_fit(a.S, a.K, a.E, a.n_shared, a.I, bits)) {
+    if (staged) {
+        if (a.mx) return one ? go(k_down_rows_staged<4, true, true>) : go(k_down_rows_staged<4, false, true>);
         if (bits == 8) return one ? go(k_down_rows_staged<8, true>) : go(k_down_rows_staged<8, false>);
         if (bits == 4) return one ? go(k_down_rows_staged<4, true>) : go(k_down_rows_staged<4, false>);
         return one ? go(k_down_rows_staged<2, true>) : go(k_down_rows_staged<2, false>);
