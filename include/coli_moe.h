@@ -275,6 +275,19 @@ int coli_moe_timing_read(int32_t kind, double *total_ms, int64_t *launches);
  * a shape beyond 160 KiB of LDS) — 3 grouped kernels at any batch size. */
 int coli_moe_debug_force_path(int32_t path);
 
+/* Failure-path hook for later calls in this process (not for concurrent
+ * calls).  The one-token router launch (at most 256 experts) selects in one
+ * workgroup that waits, bounded, for every logit of the launch; the wait
+ * gives up after `spins` polls (0: the default bound, 2^22).  With
+ * unreachable = 1 (spins must then be nonzero) it waits for a tag that no
+ * workgroup writes, so it always gives up: coli_moe_status then reports
+ * COLI_EHIP (a timed-out wait), the router writes a unit table holding the
+ * shared expert alone, and every launch still ends normally, so `out` is
+ * the shared expert's output.  unreachable = 0 restores the normal wait.
+ * Returns COLI_EINVAL
+ * for unreachable outside {0, 1} or an unreachable wait without a bound. */
+int coli_moe_debug_route_wait(uint32_t spins, int32_t unreachable);
+
 /* Unpacks n_rows packed rows of `cols` codes (device src, row stride
  * cols*bits/8 bytes) into device int8 out [n_rows, cols].  bits = COLI_MXFP4
  * reads MXFP4 rows (4 bits a code) and gives twice each E2M1 value; the

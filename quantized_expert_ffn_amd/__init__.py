@@ -39,7 +39,7 @@ EXPORTS = (
     "coli_moe_debug_logits", "coli_moe_debug_expf", "coli_moe_debug_q8_0",
     "coli_moe_debug_force_path", "coli_moe_layer", "coli_moe_debug_mfma_i8",
     "coli_moe_roof_sink_words", "coli_moe_roof_stream_read", "coli_moe_roof_mfma_i8",
-    "coli_moe_layer_noalloc", "coli_moe_debug_mfma_f8f6f4",
+    "coli_moe_layer_noalloc", "coli_moe_debug_mfma_f8f6f4", "coli_moe_debug_route_wait",
 )
 
 KIND_ROUTER_LOGITS, KIND_ROUTER_SELECT, KIND_GATEUP, KIND_DOWN, KIND_COMBINE = 0, 1, 2, 3, 4
@@ -83,6 +83,7 @@ _sigs = {
     "coli_moe_debug_expf": (ctypes.c_int, [ctypes.c_int64, _P, _P, _P]),
     "coli_moe_debug_q8_0": (ctypes.c_int, [_I32, _I32, _P, _P, _P, _P]),
     "coli_moe_debug_force_path": (ctypes.c_int, [_I32]),
+    "coli_moe_debug_route_wait": (ctypes.c_int, [ctypes.c_uint32, _I32]),
     "coli_moe_layer": (ctypes.c_int, [_D, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "coli_moe_debug_mfma_i8": (ctypes.c_int, [_P, _P, _P, _P]),
     "coli_moe_debug_mfma_f8f6f4": (ctypes.c_int, [_I32, _I32, _P, _P, _P, _P, _P, _P]),
@@ -307,6 +308,10 @@ def coli_moe_debug_q8_0(v, q, d, stream=None):
 
 def coli_moe_debug_force_path(path: int) -> None:
     _check(_lib.coli_moe_debug_force_path(int(path)), "coli_moe_debug_force_path")
+
+
+def coli_moe_debug_route_wait(spins: int, unreachable: int) -> None:
+    _check(_lib.coli_moe_debug_route_wait(int(spins), int(unreachable)), "coli_moe_debug_route_wait")
 
 
 def coli_moe_debug_mfma_i8(a, b, c, stream=None):

@@ -106,6 +106,10 @@ hipEvent_t take_event() {
 // 2: persistent kernels only, 3: grouped (matrix-core) kernels at any batch
 // size.
 int g_force_path = 0;
+// coli_moe_debug_route_wait: polls of the one-token selection's wait (0:
+// ROUTE_SPIN_LIMIT) and whether it waits for a tag no workgroup writes
+uint32_t g_route_spins = 0;
+uint32_t g_route_skew = 0;
 
 // Batches of more than GROUPED_MIN_S - 1 tokens take the grouped kernels.
 constexpr int GROUPED_MIN_S = 9;
@@ -496,6 +500,8 @@ int layer_launches(const coli_moe_dims *d, int32_t S, const float *x, const floa
             r.hs = reinterpret_cast<float *>(w8 + L.hs);
             r.slots = reinterpret_cast<uint64_t *>(w8 + L.slots);
             r.epoch = reinterpret_cast<uint32_t *>(w8) + WS_EPOCH;
+            r.spin_limit = g_route_spins ? g_route_spins : ROUTE_SPIN_LIMIT;
+            r.tag_skew = g_route_skew;
             r.I = d->inter;
             r.bits = d->wbits;
             r.group = kernel_group(d);
@@ -695,6 +701,14 @@ int coli_moe_timing_read(int32_t kind, double *total_ms, int64_t *launches) {
 int coli_moe_debug_force_path(int32_t path) {
     if (path < 0 || path > 3) return fail(COLI_EINVAL, "path must be 0, 1, 2 or 3");
     g_force_path = path;
+    return COLI_OK;
+}
+
+int coli_moe_debug_route_wait(uint32_t spins, int32_t unreachable) {
+    if (unreachable != 0 && unreachable != 1) return fail(COLI_EINVAL, "unreachable must be 0 or 1");
+    if (unreachable && spins == 0) return fail(COLI_EINVAL, "an unreachable wait needs a spin bound");
+    g_route_spins = spins;
+    g_route_skew = (uint32_t)unreachable;
     return COLI_OK;
 }
 

@@ -43,6 +43,9 @@ constexpr int ROUTE_FUSE_MAX = 8;
 // launches on this workspace so far (mod 2^32); a launch tags its published
 // logits with epoch + 1 and its selecting workgroup stores epoch + 1.
 constexpr int WS_EPOCH = 60;
+// Polls before the one-token selection's bounded wait for the published
+// logits gives up (a test hook can lower it).
+constexpr uint32_t ROUTE_SPIN_LIMIT = 1u << 22;
 
 inline size_t al256h(size_t v) { return (v + 255) & ~(size_t)255; }
 
@@ -136,6 +139,8 @@ struct RouteArgs {
     float *hs;                     // with sg: the shared expert's h [S, I], binary32
     uint64_t *slots;               // one token: [E] published logits, (tag << 32) | binary32 bits
     uint32_t *epoch;               // one token: the workspace's router epoch (WS_EPOCH)
+    uint32_t spin_limit;           // one token: polls before the selection's wait gives up
+    uint32_t tag_skew;             // one token: 0, or (test hook) 1 to wait for a tag no one writes
     int S, H, E, K, n_shared, norm;
     int I, bits, group, mx;        // expert shape, code width, scale group, MXFP4 (for sg)
     int sg;                        // 1: the launch also runs the shared expert's gate/up tiles

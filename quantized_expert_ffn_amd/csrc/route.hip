@@ -131,9 +131,6 @@ __device__ __forceinline__ void shared_gateup_half(const RouteArgs &r, uint8_t *
                                        stage);
 }
 
-// Spin bound of the one-token selection's wait for the published logits.
-constexpr uint32_t ROUTE_SPIN_LIMIT = 1u << 22;
-
 // The logit workgroups of a one-token launch with at most 256 experts
 // ("Colibri (colibrì): GLM-5.2 local inference on 25 GB of RAM", "How it
 // works (validated core mechanics)": sigmoid scores, the bias ranks only,
@@ -184,11 +181,12 @@ __device__ __forceinline__ void route_one(const RouteArgs &r, int bx, int lpw) {
     float lg = 0.0f;
     const bool valid = tid < E;
     if (valid) {
+        const uint32_t want = tag + r.tag_skew;
         uint32_t spins = 0;
         uint64_t v = ld_dev64(&r.slots[tid]);
-        while ((uint32_t)(v >> 32) != tag) {
+        while ((uint32_t)(v >> 32) != want) {
             __builtin_amdgcn_s_sleep(1);
-            if (++spins >= ROUTE_SPIN_LIMIT) {
+            if (++spins >= r.spin_limit) {
                 late = true;
                 break;
             }

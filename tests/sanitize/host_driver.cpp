@@ -133,6 +133,10 @@ int main() {
     expect(coli_moe_status(nullptr, nullptr) == COLI_EINVAL, "status(NULL)");
     expect(coli_moe_debug_force_path(4) == COLI_EINVAL, "force_path 4");
     expect(coli_moe_debug_force_path(-1) == COLI_EINVAL, "force_path -1");
+    expect(coli_moe_debug_route_wait(0, 1) == COLI_EINVAL, "route_wait unbounded unreachable");
+    expect(coli_moe_debug_route_wait(16, 2) == COLI_EINVAL, "route_wait unreachable 2");
+    expect(coli_moe_debug_route_wait(16, 1) == COLI_OK && coli_moe_debug_route_wait(0, 0) == COLI_OK,
+           "route_wait set and restore");
     expect(coli_moe_timing_read(99, nullptr, nullptr) == COLI_EINVAL, "timing_read bad kind");
     double ms = -1.0;
     int64_t n = -1;
