@@ -54,18 +54,24 @@ __host__ __device__ inline bool down_slots_fit(int S, int K, int E, int n_shared
 // LDS of one down tile (from `base`).
 struct DownTilePlan {
     size_t qh, dh, isum, sdn, y, gs, end;
+    int mpb;   // pair slots per batch
 };
 // group > 0: room for the group scales of one batch of units (UB units x
 // DR_ROWS rows x I / group scales).
 // gs_bytes: bytes per staged scale (4: binary32 group scales; 1: raw E8M0
-// bytes of the slot-staged MXFP4 tile).
+// bytes of the slot-staged MXFP4 tile).  A batch holds at most 2 ub pair
+// slots (ub units of a batch, 0: no such bound): with int8 codes (4 units a
+// batch) that keeps the tile of a 4-token verify step within a third of a
+// CU's LDS, so all H / 8 workgroups are resident at once.
 __host__ __device__ inline DownTilePlan down_tile_plan(size_t base, int S, int K, int E, int n_shared, int I,
                                                        int group = 0, int ub = 0, int gs_bytes = 4) {
     DownTilePlan p;
     const int P = S * K;
     const int umax = (P < E ? P : E) + 1;
     const int slots = P + S * n_shared;
-    const int mpb = slots < DR_MAXPB ? slots : DR_MAXPB;
+    const int cap = ub > 0 && 2 * ub < DR_MAXPB ? 2 * ub : DR_MAXPB;
+    const int mpb = slots < cap ? slots : cap;
+    p.mpb = mpb;
     p.qh = a16(base);
     p.dh = a16(p.qh + (size_t)mpb * round_up(I, 1024));
     p.isum = a16(p.dh + 4 * (size_t)mpb * round_up(I / 32, 64));
@@ -117,8 +123,7 @@ struct DownTile {
     __device__ __forceinline__ DownTile(const FwdArgs &a_, uint8_t *smem_, const DownTilePlan &D_, const int *uoff_,
                         const int *pairs_, const uint8_t *const *ublob_, const float *w_, int n_units_, int rt_)
         : a(a_), smem(smem_), D(D_), uoff(uoff_), pairs(pairs_), ublob(ublob_), w(w_), n_units(n_units_), rt(rt_) {
-        const int slots = a.S * a.K + a.S * a.n_shared;
-        mpb = slots < DR_MAXPB ? slots : DR_MAXPB;
+        mpb = D.mpb;
         nbi = a.I / 32;
         nch = (nbi + 63) / 64;
         qpitch = round_up(a.I, 1024);
