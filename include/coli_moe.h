@@ -315,6 +315,13 @@ int coli_moe_debug_expf(int64_t n, const float *x, float *y, void *stream);
  * lane layout of the prefill kernels is checked against a host matmul). */
 int coli_moe_debug_mfma_i8(const int8_t *a, const int8_t *b, int32_t *c, void *stream);
 
+/* One v_mfma_i32_16x16x32_i8 on raw lane registers: lane l (of 64) takes
+ * its A and B registers from bytes 8 l .. 8 l + 7 of device a and b and
+ * writes its 4 int32 result registers to device c[4 l .. 4 l + 3] (the lane
+ * layout of the prefill kernels' tiles of at most 16 pairs is checked
+ * against a host matmul). */
+int coli_moe_debug_mfma_i8_16(const int8_t *a, const int8_t *b, int32_t *c, void *stream);
+
 /* One v_mfma_scale_f32_32x32x64_f8f6f4 on raw lane registers: lane l (of
  * 64) takes its A and B registers from bytes 32 l .. 32 l + 31 of device a
  * and b and its E8M0 scales from byte l of device sa and sb, and writes its

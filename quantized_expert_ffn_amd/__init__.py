@@ -40,6 +40,7 @@ EXPORTS = (
     "coli_moe_debug_force_path", "coli_moe_layer", "coli_moe_debug_mfma_i8",
     "coli_moe_roof_sink_words", "coli_moe_roof_stream_read", "coli_moe_roof_mfma_i8",
     "coli_moe_layer_noalloc", "coli_moe_debug_mfma_f8f6f4", "coli_moe_debug_route_wait",
+    "coli_moe_debug_mfma_i8_16",
 )
 
 KIND_ROUTER_LOGITS, KIND_ROUTER_SELECT, KIND_GATEUP, KIND_DOWN, KIND_COMBINE = 0, 1, 2, 3, 4
@@ -86,6 +87,7 @@ _sigs = {
     "coli_moe_debug_route_wait": (ctypes.c_int, [ctypes.c_uint32, _I32]),
     "coli_moe_layer": (ctypes.c_int, [_D, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "coli_moe_debug_mfma_i8": (ctypes.c_int, [_P, _P, _P, _P]),
+    "coli_moe_debug_mfma_i8_16": (ctypes.c_int, [_P, _P, _P, _P]),
     "coli_moe_debug_mfma_f8f6f4": (ctypes.c_int, [_I32, _I32, _P, _P, _P, _P, _P, _P]),
     "coli_moe_roof_sink_words": (_SZ, []),
     "coli_moe_roof_stream_read": (ctypes.c_int, [_P, _SZ, _P, _P]),
@@ -321,6 +323,15 @@ def coli_moe_debug_mfma_i8(a, b, c, stream=None):
         raise ValueError("a, b and c hold 64 lanes x 16 registers")
     _check(_lib.coli_moe_debug_mfma_i8(_dev(a, torch.int8, "a"), _dev(b, torch.int8, "b"),
                                        _dev(c, torch.int32, "c"), _stream(stream)), "coli_moe_debug_mfma_i8")
+
+
+def coli_moe_debug_mfma_i8_16(a, b, c, stream=None):
+    """a, b: device int8 [64, 8] raw lane registers; c: device int32 [64, 4]."""
+    import torch
+    if a.numel() != 512 or b.numel() != 512 or c.numel() != 256:
+        raise ValueError("a, b hold 64 lanes x 8 bytes and c 64 lanes x 4 words")
+    _check(_lib.coli_moe_debug_mfma_i8_16(_dev(a, torch.int8, "a"), _dev(b, torch.int8, "b"),
+                                          _dev(c, torch.int32, "c"), _stream(stream)), "coli_moe_debug_mfma_i8_16")
 
 
 def coli_moe_debug_mfma_f8f6f4(fmt_a: int, fmt_b: int, a, b, sa, sb, c, stream=None):

@@ -775,6 +775,14 @@ int coli_moe_debug_mfma_i8(const int8_t *a, const int8_t *b, int32_t *c, void *s
     return e == hipSuccess ? COLI_OK : hip_fail(e, "debug_mfma_i8 launch");
 }
 
+int coli_moe_debug_mfma_i8_16(const int8_t *a, const int8_t *b, int32_t *c, void *stream) {
+    if (!a || !b || !c) return fail(COLI_EINVAL, "debug_mfma_i8_16: NULL pointer argument");
+    int rc = check_device();
+    if (rc) return rc;
+    hipError_t e = launch_debug_mfma_i8_16(a, b, c, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? COLI_OK : hip_fail(e, "debug_mfma_i8_16 launch");
+}
+
 int coli_moe_debug_mfma_f8f6f4(int32_t fmt_a, int32_t fmt_b, const uint8_t *a, const uint8_t *b, const uint8_t *sa,
                                const uint8_t *sb, float *c, void *stream) {
     if (!a || !b || !sa || !sb || !c) return fail(COLI_EINVAL, "debug_mfma_f8f6f4: NULL pointer argument");

@@ -162,6 +162,23 @@ hipError_t launch_debug_mfma_i8(const int8_t *a, const int8_t *b, int32_t *c, hi
     return hipGetLastError();
 }
 
+// One v_mfma_i32_16x16x32_i8 on raw lane registers: lane l's A and B
+// registers are bytes 8 l .. 8 l + 7 of a and b; its 4 results go to
+// c[4 l .. 4 l + 3].
+__global__ __launch_bounds__(64) void k_debug_mfma_i8_16(const int8_t *__restrict__ a, const int8_t *__restrict__ b,
+                                                          int32_t *__restrict__ c) {
+    const int l = threadIdx.x;
+    const int64_t av = reinterpret_cast<const int64_t *>(a)[l];
+    const int64_t bv = reinterpret_cast<const int64_t *>(b)[l];
+    const i32x4 cv = mfma_i8_16x16x32(av, bv);
+    reinterpret_cast<i32x4 *>(c)[l] = cv;
+}
+
+hipError_t launch_debug_mfma_i8_16(const int8_t *a, const int8_t *b, int32_t *c, hipStream_t st) {
+    hipLaunchKernelGGL(k_debug_mfma_i8_16, dim3(1), dim3(64), 0, st, a, b, c);
+    return hipGetLastError();
+}
+
 // One scaled f8f6f4 MFMA on raw lane registers: lane l's A and B registers
 // are bytes 32 l .. 32 l + 31 of a and b, its scales bytes l of sa and sb;
 // its 16 results go to c[16 l .. 16 l + 15].  FA / FB: operand formats.

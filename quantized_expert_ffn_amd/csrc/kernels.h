@@ -246,6 +246,7 @@ hipError_t launch_debug_block_dots(int bits, int rows, int cols, const void *src
                                    int32_t *out, hipStream_t st);
 hipError_t launch_debug_expf(int64_t n, const float *x, float *y, hipStream_t st);
 hipError_t launch_debug_mfma_i8(const int8_t *a, const int8_t *b, int32_t *c, hipStream_t st);
+hipError_t launch_debug_mfma_i8_16(const int8_t *a, const int8_t *b, int32_t *c, hipStream_t st);
 hipError_t launch_debug_mfma_f8f6f4(int fa, int fb, const uint8_t *a, const uint8_t *b, const uint8_t *sa,
                                     const uint8_t *sb, float *c, hipStream_t st);
 // Measured roofs: ROOF_GRID workgroups of 256 threads, one sink word per thread.

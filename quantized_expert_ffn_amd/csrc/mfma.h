@@ -22,6 +22,18 @@ __device__ __forceinline__ i32x16 mfma_i8_32x32x32(i32x4 a, i32x4 b) {
 
 __host__ __device__ inline int mfma_c_row(int lane, int r) { return 8 * (r / 4) + 4 * (lane / 32) + (r % 4); }
 
+// v_mfma_i32_16x16x32_i8: C[16x16] = A[16x32] * B[32x16], one Q8_0 block
+// per instruction over 16 rows and 16 columns.  Lane layout (checked by the
+// debug hook coli_moe_debug_mfma_i8_16 against a host matmul):
+//   A: lane l holds A[i][k], i = l % 16, k = 8 (l / 16) + j, in byte j of
+//      its two registers;
+//   B: lane l holds B[k][n], n = l % 16, k = 8 (l / 16) + j, likewise;
+//   C: register r of lane l holds C[i][n], n = l % 16, i = 4 (l / 16) + r.
+__device__ __forceinline__ i32x4 mfma_i8_16x16x32(int64_t a, int64_t b) {
+    const i32x4 zero = {0, 0, 0, 0};
+    return __builtin_amdgcn_mfma_i32_16x16x32_i8(a, b, zero, 0, 0, 0);
+}
+
 // The scaled low-precision matrix-core operation of gfx950,
 // v_mfma_scale_f32_32x32x64_f8f6f4: C[32x32] = sum over K = 64 of A * B, in
 // binary32, each 32-deep half of K multiplied by the E8M0 scales of its A

@@ -509,6 +509,93 @@ __device__ __forceinline__ void pf_dispatch_grouped(bool fold, float (&acc)[NM][
     pf_run<BITS, NM, false, TAIL, true>(acc, lds, src, col_voff, col_doff, active, refold);
 }
 
+// ---- tiles of at most 16 pairs -----------------------------------------
+// The same stages, with two v_mfma_i32_16x16x32_i8 per block and matrix
+// (rows 0-15 and 16-31 of the wave) over the tile's first 16 columns: half
+// the conversions and chain steps of a 32-column product, the rest being
+// padding.  Lane l takes column l % 16 and, of each block, the 8 codes of
+// quarter q = l / 16: int8 codes 8 q .. 8 q + 7; int4 the low and high
+// nibbles of bytes 4 q .. 4 q + 3 (codes 4 q .. 4 q + 3 and 16 + 4 q ..
+// 16 + 4 q + 3, each as 16 * code), with the activations read in the
+// matching order from their LDS order (0-7, 16-23, 8-15, 24-31).  A
+// block's sum is exact whatever the order, so the chain is R-DOT's.
+template <int BITS>
+__device__ __forceinline__ int64_t narrow_w(const uint8_t *row_lds, int j, int q) {
+    if constexpr (BITS == 8) {
+        return *reinterpret_cast<const int64_t *>(row_lds + 32 * j + 8 * q);
+    } else {
+        const uint32_t w = *reinterpret_cast<const uint32_t *>(row_lds + 16 * j + 4 * q);
+        const uint32_t lo = (w << 4) & 0xF0F0F0F0u, hi = w & 0xF0F0F0F0u;
+        return (int64_t)(((uint64_t)hi << 32) | lo);
+    }
+}
+
+template <int BITS>
+__device__ __forceinline__ int64_t narrow_a(const uint8_t *col_lds, int j, int q) {
+    if constexpr (BITS == 8) {
+        return *reinterpret_cast<const int64_t *>(col_lds + 32 * j + 8 * q);
+    } else {
+        const int o = q < 2 ? 4 * q : 16 + 4 * (q - 2);
+        const uint32_t lo = *reinterpret_cast<const uint32_t *>(col_lds + 32 * j + o);
+        const uint32_t hi = *reinterpret_cast<const uint32_t *>(col_lds + 32 * j + o + 8);
+        return (int64_t)(((uint64_t)hi << 32) | lo);
+    }
+}
+
+// Blocks 0 .. nblk - 1 of a stage in LDS (all C when FULL); acc[m][4 g + i]
+// is row 16 g + 4 q + i of the wave's 32 rows of matrix m.
+template <int BITS, int NM, bool FOLD, int C, bool FULL>
+__device__ __forceinline__ void pf_blocks_narrow(float (&acc)[NM][8], const uint8_t *lw, const uint8_t *la,
+                                                 const float *ld, int q, int nblk) {
+    using ST = PfStage<BITS, NM>;
+    constexpr int SH = ST::SHIFT;
+#pragma unroll
+    for (int j = 0; j < C; ++j) {
+        if (FULL || j < nblk) {
+            const int64_t b = narrow_a<BITS>(la, j, q);
+            const float d = ld[32 * j];
+#pragma unroll
+            for (int m = 0; m < NM; ++m)
+#pragma unroll
+                for (int g = 0; g < 2; ++g) {
+                    const i32x4 c =
+                        mfma_i8_16x16x32(narrow_w<BITS>(lw + (m * PF_ROWS + 16 * g) * ST::WS, j, q), b);
+                    acc[m][4 * g + 0] = __builtin_fmaf(d, (float)(FOLD ? c.x : c.x >> SH), acc[m][4 * g + 0]);
+                    acc[m][4 * g + 1] = __builtin_fmaf(d, (float)(FOLD ? c.y : c.y >> SH), acc[m][4 * g + 1]);
+                    acc[m][4 * g + 2] = __builtin_fmaf(d, (float)(FOLD ? c.z : c.z >> SH), acc[m][4 * g + 2]);
+                    acc[m][4 * g + 3] = __builtin_fmaf(d, (float)(FOLD ? c.w : c.w >> SH), acc[m][4 * g + 3]);
+                }
+        }
+    }
+}
+
+// pf_run for a tile of at most 16 pairs.
+template <int BITS, int NM, bool FOLD>
+__device__ __forceinline__ void pf_run_narrow(float (&acc)[NM][8], uint8_t *lds, const PfSrc<NM> &src,
+                                              const uint32_t *col_voff, const uint32_t *col_doff, bool active) {
+    using ST = PfStage<BITS, NM>;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, q = lane >> 4, c = lane & 15;
+    const int n_stages = (src.nb + ST::C - 1) / ST::C;
+    PfRegs<BITS, NM> R;
+    pf_load<BITS, NM>(R, src, col_voff, col_doff, 0);
+    const uint8_t *la = lds + ST::W_BYTES + ST::AS * c;
+    const float *ld = reinterpret_cast<const float *>(lds + ST::W_BYTES + ST::A_BYTES) + c;
+    const uint8_t *lw = lds + ST::WS * (32 * wave + c);
+    for (int s = 0; s < n_stages; ++s) {
+        if (s > 0) __syncthreads();  // every wave is done with the previous stage
+        pf_store<BITS, NM, FOLD>(R, lds);
+        __syncthreads();
+        if (s + 1 < n_stages) pf_load<BITS, NM>(R, src, col_voff, col_doff, s + 1);
+        const int nblk = min(ST::C, src.nb - ST::C * s);
+        if (active) {
+            if (nblk == ST::C)
+                pf_blocks_narrow<BITS, NM, FOLD, ST::C, true>(acc, lw, la, ld, q, nblk);
+            else
+                pf_blocks_narrow<BITS, NM, FOLD, ST::C, false>(acc, lw, la, ld, q, nblk);
+        }
+    }
+}
+
 // Columns of the tile: the slot of pair n (the tile's first pair past its
 // end) and that slot's token.
 struct PfCols {
@@ -569,13 +656,61 @@ __global__ __launch_bounds__(PF_T) __attribute__((amdgpu_waves_per_eu(GROUPED ? 
     __syncthreads();
     const int i0 = src.row0 + 32 * wave;
     const bool active = i0 < I;
+    // every wave has the same 32 columns, hence the same choice
+    const bool fold = scales_fold<ST::SHIFT, GROUPED>(a.dx + (size_t)col.tok * nb, nb);
+    if constexpr (!GROUPED && (BITS == 4 || BITS == 8)) {
+        if (tl.n <= 16) {
+            float an[2][8];
+#pragma unroll
+            for (int m = 0; m < 2; ++m)
+#pragma unroll
+                for (int r = 0; r < 8; ++r) an[m][r] = 0.0f;
+            if (fold)
+                pf_run_narrow<BITS, 2, true>(an, lds, src, col_voff, col_doff, active);
+            else
+                pf_run_narrow<BITS, 2, false>(an, lds, src, col_voff, col_doff, active);
+            if (!active) return;
+            // lane (column c, quarter q) holds rows 16 g + 4 q + i
+            const int c = lane & 15, qq = lane >> 4;
+            const PfCols cc = pf_col(tab + U.pairs, tl, c, P, a.K);
+            const float *sg = reinterpret_cast<const float *>(blob + BL.s_gate) + i0;
+            const float *su = reinterpret_cast<const float *>(blob + BL.s_up) + i0;
+            float hv[8], amax = 0.0f;
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                const int row = 16 * (r / 4) + 4 * qq + r % 4;
+                hv[r] = swiglu_f32(an[0][r] * sg[row], an[1][r] * su[row]);
+                amax = __builtin_fmaxf(amax, __builtin_fabsf(hv[r]));
+            }
+            // Q8_0 over the 32 rows of the column, held by its four lanes
+            amax = __builtin_fmaxf(amax, __shfl_xor(amax, 16, 64));
+            amax = __builtin_fmaxf(amax, __shfl_xor(amax, 32, 64));
+            if (!cc.live) return;
+            const float dq = amax / 127.0f;
+            int8_t *qrow = a.qh + (size_t)cc.slot * I + i0;
+#pragma unroll
+            for (int g = 0; g < 2; ++g) {
+                uint32_t word = 0;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float v = 0.0f;
+                    if (dq != 0.0f) {
+                        v = __builtin_roundf(hv[4 * g + i] / dq);
+                        v = __builtin_fminf(__builtin_fmaxf(v, -127.0f), 127.0f);
+                    }
+                    word |= (uint32_t)(uint8_t)(int8_t)(int)v << (8 * i);
+                }
+                *reinterpret_cast<uint32_t *>(qrow + 16 * g + 4 * qq) = word;
+            }
+            if (qq == 0) a.dh[(size_t)cc.slot * (I / 32) + i0 / 32] = dq;
+            return;
+        }
+    }
     float acc[2][16];
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[m][r] = 0.0f;
-    // every wave has the same 32 columns, hence the same choice
-    const bool fold = scales_fold<ST::SHIFT, GROUPED>(a.dx + (size_t)col.tok * nb, nb);
     if constexpr (GROUPED) {
         if (nb % ST::C != 0)
             pf_dispatch_grouped<BITS, 2, true>(fold, acc, lds, src, col_voff, col_doff, active, &refold);
@@ -659,10 +794,37 @@ __global__ __launch_bounds__(PF_T, 4) void k_pf_down(const FwdArgs a, const int3
     __syncthreads();
     const int r0 = src.row0 + 32 * wave;
     const bool active = r0 < H;
+    const bool fold = scales_fold<ST::SHIFT, GROUPED>(a.dh + (size_t)col.slot * nb, nb);
+    if constexpr (!GROUPED && (BITS == 4 || BITS == 8)) {
+        if (tl.n <= 16) {
+            float an[1][8];
+#pragma unroll
+            for (int r = 0; r < 8; ++r) an[0][r] = 0.0f;
+            if (fold)
+                pf_run_narrow<BITS, 1, true>(an, lds, src, col_voff, col_doff, active);
+            else
+                pf_run_narrow<BITS, 1, false>(an, lds, src, col_voff, col_doff, active);
+            const int c = lane & 15, qq = lane >> 4;
+            const PfCols cc = pf_col(tab + U.pairs, tl, c, P, a.K);
+            if (!active || !cc.live) return;
+            const float *sd = reinterpret_cast<const float *>(blob + BL.s_down) + r0;
+            float *yrow = a.Y + (size_t)cc.slot * H + r0;
+#pragma unroll
+            for (int g = 0; g < 2; ++g) {
+                const int rr = 16 * g + 4 * qq;
+                f32x4 v;
+                v.x = an[0][4 * g + 0] * sd[rr + 0];
+                v.y = an[0][4 * g + 1] * sd[rr + 1];
+                v.z = an[0][4 * g + 2] * sd[rr + 2];
+                v.w = an[0][4 * g + 3] * sd[rr + 3];
+                *reinterpret_cast<f32x4 *>(yrow + rr) = v;
+            }
+            return;
+        }
+    }
     float acc[1][16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[0][r] = 0.0f;
-    const bool fold = scales_fold<ST::SHIFT, GROUPED>(a.dh + (size_t)col.slot * nb, nb);
     if constexpr (GROUPED) {
         if (nb % ST::C != 0)
             pf_dispatch_grouped<BITS, 1, true>(fold, acc, lds, src, col_voff, col_doff, active, &refold);

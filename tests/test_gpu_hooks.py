@@ -132,6 +132,32 @@ def test_mfma_i8_lane_layout(torch):
     assert bad.size == 0, f"{len(bad)} lane registers differ, first (lane, register) {bad[:4].tolist()}"
 
 
+def test_mfma_i8_16x16_lane_layout(torch):
+    """The lane layout the prefill kernels' tiles of at most 16 pairs assume
+    for v_mfma_i32_16x16x32_i8 reproduces a host int matmul of the matrices
+    it implies."""
+    say("mfma i8 16x16x32 lane layout")
+    rng = np.random.default_rng(13)
+    a_raw = rng.integers(-128, 128, size=(64, 8), dtype=np.int8)
+    b_raw = rng.integers(-128, 128, size=(64, 8), dtype=np.int8)
+    c = torch.zeros((64, 4), dtype=torch.int32, device="cuda")
+    q().coli_moe_debug_mfma_i8_16(torch.from_numpy(a_raw).cuda(), torch.from_numpy(b_raw).cuda(), c)
+    got = c.cpu().numpy()
+    A = np.zeros((16, 32), np.int64)
+    B = np.zeros((32, 16), np.int64)
+    for lane in range(64):
+        for j in range(8):
+            A[lane % 16, 8 * (lane // 16) + j] = a_raw[lane, j]
+            B[8 * (lane // 16) + j, lane % 16] = b_raw[lane, j]
+    C = A @ B
+    want = np.zeros((64, 4), np.int64)
+    for lane in range(64):
+        for r in range(4):
+            want[lane, r] = C[4 * (lane // 16) + r, lane % 16]
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, f"{len(bad)} lane registers differ, first (lane, register) {bad[:4].tolist()}"
+
+
 def _e4m3(byte: int, bias: int = 7) -> float:
     """OCP FP8 E4M3 (bias 7; S.1111.111 is NaN), or with bias 8 the older
     variant, for the diagnostics."""
