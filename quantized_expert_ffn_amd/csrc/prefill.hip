@@ -543,57 +543,98 @@ __device__ __forceinline__ int64_t narrow_a(const uint8_t *col_lds, int j, int q
 }
 
 // Blocks 0 .. nblk - 1 of a stage in LDS (all C when FULL); acc[m][4 g + i]
-// is row 16 g + 4 q + i of the wave's 32 rows of matrix m.
-template <int BITS, int NM, bool FOLD, int C, bool FULL>
+// is row 16 g + 4 q + i of the wave's 32 rows of matrix m.  GROUPED: lg
+// points at the lane's first row (32 w + 4 q) of group 0 of matrix 0 in the
+// staged group scales, and each block's multiplier is d_b * s[row][group].
+template <int BITS, int NM, bool FOLD, int C, bool FULL, bool GROUPED = false>
 __device__ __forceinline__ void pf_blocks_narrow(float (&acc)[NM][8], const uint8_t *lw, const uint8_t *la,
-                                                 const float *ld, int q, int nblk) {
+                                                 const float *ld, int q, int nblk, const float *lg = nullptr) {
     using ST = PfStage<BITS, NM>;
     constexpr int SH = ST::SHIFT;
+    float sg[NM][8];
 #pragma unroll
     for (int j = 0; j < C; ++j) {
         if (FULL || j < nblk) {
             const int64_t b = narrow_a<BITS>(la, j, q);
             const float d = ld[32 * j];
+            if constexpr (GROUPED) {
+                if ((j & 1) == 0) {
+#pragma unroll
+                    for (int m = 0; m < NM; ++m)
+#pragma unroll
+                        for (int g = 0; g < 2; ++g) {
+                            const f32x4 v =
+                                *reinterpret_cast<const f32x4 *>(lg + (m * ST::G_PER + j / 2) * PF_ROWS + 16 * g);
+                            sg[m][4 * g] = v.x;
+                            sg[m][4 * g + 1] = v.y;
+                            sg[m][4 * g + 2] = v.z;
+                            sg[m][4 * g + 3] = v.w;
+                        }
+                }
+            }
 #pragma unroll
             for (int m = 0; m < NM; ++m)
 #pragma unroll
                 for (int g = 0; g < 2; ++g) {
                     const i32x4 c =
                         mfma_i8_16x16x32(narrow_w<BITS>(lw + (m * PF_ROWS + 16 * g) * ST::WS, j, q), b);
-                    acc[m][4 * g + 0] = __builtin_fmaf(d, (float)(FOLD ? c.x : c.x >> SH), acc[m][4 * g + 0]);
-                    acc[m][4 * g + 1] = __builtin_fmaf(d, (float)(FOLD ? c.y : c.y >> SH), acc[m][4 * g + 1]);
-                    acc[m][4 * g + 2] = __builtin_fmaf(d, (float)(FOLD ? c.z : c.z >> SH), acc[m][4 * g + 2]);
-                    acc[m][4 * g + 3] = __builtin_fmaf(d, (float)(FOLD ? c.w : c.w >> SH), acc[m][4 * g + 3]);
+                    const int32_t cv[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        acc[m][4 * g + i] = __builtin_fmaf(GROUPED ? d * sg[m][4 * g + i] : d,
+                                                           (float)(FOLD ? cv[i] : cv[i] >> SH), acc[m][4 * g + i]);
                 }
         }
     }
 }
 
 // pf_run for a tile of at most 16 pairs.
-template <int BITS, int NM, bool FOLD>
+template <int BITS, int NM, bool FOLD, bool GROUPED = false>
 __device__ __forceinline__ void pf_run_narrow(float (&acc)[NM][8], uint8_t *lds, const PfSrc<NM> &src,
-                                              const uint32_t *col_voff, const uint32_t *col_doff, bool active) {
+                                              const uint32_t *col_voff, const uint32_t *col_doff, bool active,
+                                              int *refold = nullptr) {
     using ST = PfStage<BITS, NM>;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, q = lane >> 4, c = lane & 15;
     const int n_stages = (src.nb + ST::C - 1) / ST::C;
     PfRegs<BITS, NM> R;
-    pf_load<BITS, NM>(R, src, col_voff, col_doff, 0);
+    pf_load<BITS, NM, GROUPED>(R, src, col_voff, col_doff, 0);
     const uint8_t *la = lds + ST::W_BYTES + ST::AS * c;
     const float *ld = reinterpret_cast<const float *>(lds + ST::W_BYTES + ST::A_BYTES) + c;
     const uint8_t *lw = lds + ST::WS * (32 * wave + c);
+    const float *lg = reinterpret_cast<const float *>(lds + ST::LDS) + 32 * wave + 4 * q;
     for (int s = 0; s < n_stages; ++s) {
         if (s > 0) __syncthreads();  // every wave is done with the previous stage
-        pf_store<BITS, NM, FOLD>(R, lds);
+        pf_store<BITS, NM, FOLD, GROUPED>(R, lds, refold);
         __syncthreads();
-        if (s + 1 < n_stages) pf_load<BITS, NM>(R, src, col_voff, col_doff, s + 1);
+        if (s + 1 < n_stages) pf_load<BITS, NM, GROUPED>(R, src, col_voff, col_doff, s + 1);
         const int nblk = min(ST::C, src.nb - ST::C * s);
         if (active) {
             if (nblk == ST::C)
-                pf_blocks_narrow<BITS, NM, FOLD, ST::C, true>(acc, lw, la, ld, q, nblk);
+                pf_blocks_narrow<BITS, NM, FOLD, ST::C, true, GROUPED>(acc, lw, la, ld, q, nblk, lg);
             else
-                pf_blocks_narrow<BITS, NM, FOLD, ST::C, false>(acc, lw, la, ld, q, nblk);
+                pf_blocks_narrow<BITS, NM, FOLD, ST::C, false, GROUPED>(acc, lw, la, ld, q, nblk, lg);
         }
     }
+}
+
+// pf_run_narrow with the folded or the shifting chain; group-scaled: a tile
+// whose group scales fail the fold check is recomputed with the shifting
+// chain (as pf_dispatch_grouped).
+template <int BITS, int NM, bool GROUPED>
+__device__ __forceinline__ void pf_dispatch_narrow(bool fold, float (&acc)[NM][8], uint8_t *lds,
+                                                   const PfSrc<NM> &src, const uint32_t *col_voff,
+                                                   const uint32_t *col_doff, bool active, int *refold) {
+    if (fold) {
+        pf_run_narrow<BITS, NM, true, GROUPED>(acc, lds, src, col_voff, col_doff, active, refold);
+        if (!GROUPED) return;
+        __syncthreads();
+        if (!*refold) return;
+#pragma unroll
+        for (int m = 0; m < NM; ++m)
+#pragma unroll
+            for (int r = 0; r < 8; ++r) acc[m][r] = 0.0f;
+    }
+    pf_run_narrow<BITS, NM, false, GROUPED>(acc, lds, src, col_voff, col_doff, active, refold);
 }
 
 // Columns of the tile: the slot of pair n (the tile's first pair past its
@@ -658,17 +699,14 @@ __global__ __launch_bounds__(PF_T) __attribute__((amdgpu_waves_per_eu(GROUPED ? 
     const bool active = i0 < I;
     // every wave has the same 32 columns, hence the same choice
     const bool fold = scales_fold<ST::SHIFT, GROUPED>(a.dx + (size_t)col.tok * nb, nb);
-    if constexpr (!GROUPED && (BITS == 4 || BITS == 8)) {
+    if constexpr (BITS == 4 || (BITS == 8 && !GROUPED)) {
         if (tl.n <= 16) {
             float an[2][8];
 #pragma unroll
             for (int m = 0; m < 2; ++m)
 #pragma unroll
                 for (int r = 0; r < 8; ++r) an[m][r] = 0.0f;
-            if (fold)
-                pf_run_narrow<BITS, 2, true>(an, lds, src, col_voff, col_doff, active);
-            else
-                pf_run_narrow<BITS, 2, false>(an, lds, src, col_voff, col_doff, active);
+            pf_dispatch_narrow<BITS, 2, GROUPED>(fold, an, lds, src, col_voff, col_doff, active, &refold);
             if (!active) return;
             // lane (column c, quarter q) holds rows 16 g + 4 q + i
             const int c = lane & 15, qq = lane >> 4;
@@ -679,7 +717,7 @@ __global__ __launch_bounds__(PF_T) __attribute__((amdgpu_waves_per_eu(GROUPED ? 
 #pragma unroll
             for (int r = 0; r < 8; ++r) {
                 const int row = 16 * (r / 4) + 4 * qq + r % 4;
-                hv[r] = swiglu_f32(an[0][r] * sg[row], an[1][r] * su[row]);
+                hv[r] = GROUPED ? swiglu_f32(an[0][r], an[1][r]) : swiglu_f32(an[0][r] * sg[row], an[1][r] * su[row]);
                 amax = __builtin_fmaxf(amax, __builtin_fabsf(hv[r]));
             }
             // Q8_0 over the 32 rows of the column, held by its four lanes
@@ -795,15 +833,12 @@ __global__ __launch_bounds__(PF_T, 4) void k_pf_down(const FwdArgs a, const int3
     const int r0 = src.row0 + 32 * wave;
     const bool active = r0 < H;
     const bool fold = scales_fold<ST::SHIFT, GROUPED>(a.dh + (size_t)col.slot * nb, nb);
-    if constexpr (!GROUPED && (BITS == 4 || BITS == 8)) {
+    if constexpr (BITS == 4 || (BITS == 8 && !GROUPED)) {
         if (tl.n <= 16) {
             float an[1][8];
 #pragma unroll
             for (int r = 0; r < 8; ++r) an[0][r] = 0.0f;
-            if (fold)
-                pf_run_narrow<BITS, 1, true>(an, lds, src, col_voff, col_doff, active);
-            else
-                pf_run_narrow<BITS, 1, false>(an, lds, src, col_voff, col_doff, active);
+            pf_dispatch_narrow<BITS, 1, GROUPED>(fold, an, lds, src, col_voff, col_doff, active, &refold);
             const int c = lane & 15, qq = lane >> 4;
             const PfCols cc = pf_col(tab + U.pairs, tl, c, P, a.K);
             if (!active || !cc.live) return;
@@ -813,10 +848,10 @@ __global__ __launch_bounds__(PF_T, 4) void k_pf_down(const FwdArgs a, const int3
             for (int g = 0; g < 2; ++g) {
                 const int rr = 16 * g + 4 * qq;
                 f32x4 v;
-                v.x = an[0][4 * g + 0] * sd[rr + 0];
-                v.y = an[0][4 * g + 1] * sd[rr + 1];
-                v.z = an[0][4 * g + 2] * sd[rr + 2];
-                v.w = an[0][4 * g + 3] * sd[rr + 3];
+                v.x = GROUPED ? an[0][4 * g + 0] : an[0][4 * g + 0] * sd[rr + 0];
+                v.y = GROUPED ? an[0][4 * g + 1] : an[0][4 * g + 1] * sd[rr + 1];
+                v.z = GROUPED ? an[0][4 * g + 2] : an[0][4 * g + 2] * sd[rr + 2];
+                v.w = GROUPED ? an[0][4 * g + 3] : an[0][4 * g + 3] * sd[rr + 3];
                 *reinterpret_cast<f32x4 *>(yrow + rr) = v;
             }
             return;
