@@ -138,12 +138,11 @@ __device__ __forceinline__ int8_t q8_0_lane(float v, float *d_out) {
     return (int8_t)(int)c;
 }
 
-// The same quantisation with one lane holding a whole 32-value block: reads
-// x[0..31] (16-byte aligned), returns d and the 32 codes as 8 little-endian
-// words in w.  *ok is cleared on a non-finite input.
-__device__ __forceinline__ float q8_0_block_words(const float *__restrict__ x, uint32_t w[8], bool *ok) {
+// The same quantisation with one lane holding a whole 32-value block v
+// (in registers): returns d and the 32 codes as 8 little-endian words in w.
+// *ok is cleared on a non-finite input.
+__device__ __forceinline__ float q8_0_words_of(const f32x4 (&xv)[8], uint32_t w[8], bool *ok) {
     float v[32];
-    const f32x4 *xv = reinterpret_cast<const f32x4 *>(x);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const f32x4 t = xv[i];
@@ -173,6 +172,15 @@ __device__ __forceinline__ float q8_0_block_words(const float *__restrict__ x, u
         w[i] = word;
     }
     return d;
+}
+
+// q8_0_words_of for the block at x[0..31] (16-byte aligned).
+__device__ __forceinline__ float q8_0_block_words(const float *__restrict__ x, uint32_t w[8], bool *ok) {
+    f32x4 xv[8];
+    const f32x4 *src = reinterpret_cast<const f32x4 *>(x);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) xv[i] = src[i];
+    return q8_0_words_of(xv, w, ok);
 }
 
 // E4M3 byte (OCP FP8: 1 sign, 4 exponent bits of bias 7, 3 mantissa bits)

@@ -207,19 +207,24 @@ __device__ __forceinline__ void gateup_unit_primed(const uint8_t *blob, int H, i
 }
 
 // gateup_half_f32 with packed codes (BITS 4 or 2), per-row scales and rows
-// of NCH = (H / 32 + 63) / 64 <= 4 chunks: the activations are staged first
-// (stage(0, np): Q8_0 of x into LDS, ending with a workgroup barrier), then
-// every chunk of the wave's 8 rows goes out at once with the row scale — one
-// memory round trip for the whole half tile — and the chunks are reduced in
-// order as they arrive.  Results as gateup_half_f32.
-template <int BITS, int NT, int NCH, typename Stage>
+// of NCH = (H / 32 + 63) / 64 <= 4 chunks, for np <= NT vectors x[v * H ..]
+// (binary32, not yet quantised).  The memory operations go out in this
+// order: each thread's 32-value blocks of x (block j = tid + 256 k of the
+// np * H / 32, at most NT per thread), the row scale, then every chunk of
+// the wave's 8 rows — one memory round trip for the whole half tile.  Q8_0
+// of the blocks (q8_0_words_of, as the quantisation of x everywhere else)
+// then waits for x alone and goes to LDS behind a barrier that orders LDS
+// only, and the chunks are reduced in order as they arrive.  Results as
+// gateup_half_f32.
+template <int BITS, int NT, int NCH>
 __device__ __forceinline__ void gateup_half_primed(const uint8_t *blob, int H, int I, int i0, int np, uint8_t *smem,
-                                                   const SmemPlan &L, float *__restrict__ hs, Stage stage) {
+                                                   const SmemPlan &L, const float *__restrict__ x,
+                                                   float *__restrict__ hs) {
     static_assert(BITS == 4 || BITS == 2, "one buffer load per block");
     constexpr int RPW = 8;
     const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
-    const int8_t *vq = reinterpret_cast<const int8_t *>(smem + L.vq);
-    const float *vd = reinterpret_cast<const float *>(smem + L.vd);
+    int8_t *vq = reinterpret_cast<int8_t *>(smem + L.vq);
+    float *vd = reinterpret_cast<float *>(smem + L.vd);
     int32_t *isum_wave = reinterpret_cast<int32_t *>(smem + L.isum) + wave * NT * RPW * ISUM_PITCH;
     float *gu = reinterpret_cast<float *>(smem + L.gu);
     const BlobLayout BL = blob_layout(H, I, BITS, 0, false);
@@ -230,9 +235,22 @@ __device__ __forceinline__ void gateup_half_primed(const uint8_t *blob, int H, i
     uint32_t rowoff[RPW];
 #pragma unroll
     for (int j = 0; j < RPW; ++j) rowoff[j] = (uint32_t)(mat + (size_t)(r0 + j) * row_bytes);
-    const int nb = H / 32, vds = vd_stride(nb);
+    const int nb = H / 32, vds = vd_stride(nb), nblk = np * nb;
     const int crow = lane % RPW, cvec = lane / RPW;
-    stage(0, np);
+    // 1. x: block tid + 256 k of the np vectors (a clamped index past the
+    //    end, so that every thread issues the same loads)
+    f32x4 xr[NT][8];
+#pragma unroll
+    for (int k = 0; k < NT; ++k) {
+        if (256 * k < nblk) {
+            const int j = min(tid + 256 * k, nblk - 1), it = j / nb, b = j - it * nb;
+            const f32x4 *src = reinterpret_cast<const f32x4 *>(x + (size_t)it * H + 32 * b);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) xr[k][i] = src[i];
+        }
+    }
+    // 2. the row scale, 3. every chunk, in order
+    __builtin_amdgcn_sched_barrier(0);
     const uint32_t soff = (uint32_t)((wave < 2 ? BL.s_gate : BL.s_up) + 4 * (size_t)(r0 + crow));
     const float rs = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsrc, soff, 0, 0));
     BlockBits<BITS> X[NCH][RPW];
@@ -241,6 +259,21 @@ __device__ __forceinline__ void gateup_half_primed(const uint8_t *blob, int H, i
         issue_chunk<BITS, RPW>(rsrc, rowoff, c, X[c]);
         __builtin_amdgcn_sched_barrier(0);   // chunks in order
     }
+    // 4. Q8_0(x) into LDS
+#pragma unroll
+    for (int k = 0; k < NT; ++k) {
+        const int j = tid + 256 * k;
+        if (j < nblk) {
+            const int it = j / nb, b = j - it * nb;
+            uint32_t w[8];
+            bool ok;   // a non-finite x is reported by the quantisation of x
+            vd[it * vds + b] = q8_0_words_of(xr[k], w, &ok);
+            u32x4 *qv = reinterpret_cast<u32x4 *>(vq + (size_t)it * H + 32 * b);
+            qv[0] = u32x4{w[0], w[1], w[2], w[3]};
+            qv[1] = u32x4{w[4], w[5], w[6], w[7]};
+        }
+    }
+    lds_barrier();
     float acc = 0.0f;
 #pragma unroll
     for (int c = 0; c < NCH; ++c) acc = reduce_chunk<BITS, NT, RPW>(X[c], c, nb, np, vq, vd, vds, H, isum_wave, acc);

@@ -114,7 +114,7 @@ __device__ __forceinline__ void shared_gateup_half(const RouteArgs &r, uint8_t *
         if (S <= NT && nch <= 4) {
             auto go = [&](auto nch_c) {
                 gateup_half_primed<BITS, NT, decltype(nch_c)::value>(uniform_ptr(r.shared), H, r.I, 16 * half, S,
-                                                                     smem, L, r.hs, stage);
+                                                                     smem, L, r.x, r.hs);
             };
             if (nch == 1)
                 go(std::integral_constant<int, 1>());
