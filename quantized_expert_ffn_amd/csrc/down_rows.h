@@ -156,15 +156,19 @@ struct DownTile {
 
     // Weight loads of units [u0, u1), chunk c, in one straight run.
     __device__ __forceinline__ void issue(int u0, int u1, int c) {
-        const int b = c * 64 + (int)(threadIdx.x & 63);
 #pragma unroll
         for (int ui = 0; ui < UB; ++ui) {
             const int uu = u0 + ui;
-            const uint8_t *blob = uniform_ptr(ublob[min(uu, n_units - 1)]);
-            const __amdgpu_buffer_rsrc_t rs = make_rsrc(blob, (uu < u1 && blob) ? (uint32_t)BL.total : 0u);
-#pragma unroll
-            for (int r = 0; r < DR_RPW; ++r) wv[ui][r] = load_block<BITS>(rs, (uint32_t)(ro + r * irow), b);
+            issue_unit(ui, uniform_ptr(ublob[min(uu, n_units - 1)]), uu < u1, c);
         }
+    }
+    // The loads of batch entry ui (unit blob, wave-uniform; live: part of
+    // the batch; a null or dead blob reads zeros).
+    __device__ __forceinline__ void issue_unit(int ui, const uint8_t *blob, bool live, int c) {
+        const int b = c * 64 + (int)(threadIdx.x & 63);
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(blob, (live && blob) ? (uint32_t)BL.total : 0u);
+#pragma unroll
+        for (int r = 0; r < DR_RPW; ++r) wv[ui][r] = load_block<BITS>(rs, (uint32_t)(ro + r * irow), b);
     }
 
     __device__ __forceinline__ i32x4 ld_qh(uint32_t off) const {
@@ -446,10 +450,11 @@ struct DownTile {
 
     // The whole tile when slots_fit() holds and the slots' Q8_0(h) is in LDS
     // (slots_store, then a workgroup barrier): the weights of every unit go
-    // out at once with the down-row scales right behind them (needed only at
-    // the end, so waiting for them waits for nothing the block dots have not
-    // already waited for), then the block dots, the chains and the combine.
-    __device__ __forceinline__ void run_staged() {
+    // out at once (unless the caller issued them already: issued) with the
+    // down-row scales right behind them (needed only at the end, so waiting
+    // for them waits for nothing the block dots have not already waited
+    // for), then the block dots, the chains and the combine.
+    __device__ __forceinline__ void run_staged(bool issued) {
         const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
         const int r0 = rt * DR_ROWS;
         const int8_t *qh_l = reinterpret_cast<const int8_t *>(smem + D.qh);
@@ -476,7 +481,7 @@ struct DownTile {
                 mxv[k] = w < nsw ? mx_word(0, w) : 0u;
             }
         }
-        issue(0, n_units, 0);
+        if (!issued) issue(0, n_units, 0);
         float sd = 0.0f;
         const uint8_t *my_blob = chain ? ublob[ub] : nullptr;
         if (!MX && my_blob) sd = reinterpret_cast<const float *>(my_blob + BL.s_down)[r0 + rl];

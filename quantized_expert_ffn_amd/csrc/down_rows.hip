@@ -77,10 +77,15 @@ __global__ __launch_bounds__(DR_T) __attribute__((amdgpu_waves_per_eu(MX ? 2 : 3
 }
 
 // The same tile when every pair slot of the call fits one staging round
-// (down_slots_fit, per-row scales, the call's unit table in the workspace):
-// the slots' Q8_0(h) is fetched in the same memory round trip as the table
-// (in slot order: its addresses do not depend on the routing), and the
-// weights go out as soon as the blob pointers are in (DownTile::run_staged).
+// (down_slots_fit, per-row scales or MXFP4, the call's unit table in the
+// workspace): the slots' Q8_0(h) is fetched in the same memory round trip as
+// the table (in slot order: its addresses do not depend on the routing).
+// With per-row scales every wave also reads the unit count and the blob
+// pointers through the scalar cache and issues its weights as soon as those
+// are in, before the staged data has arrived (loads complete in issue order,
+// so storing the staged data to LDS then waits for none of the weights);
+// MXFP4 tiles issue theirs from LDS after the staging
+// (DownTile::run_staged).
 template <int BITS, bool ONE_TOKEN, bool MX = false>
 __global__ __launch_bounds__(DR_T) __attribute__((amdgpu_waves_per_eu(3))) void k_down_rows_staged(const FwdArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -99,15 +104,33 @@ __global__ __launch_bounds__(DR_T) __attribute__((amdgpu_waves_per_eu(3))) void 
     i32x4 qv[DR_MQ];
     float dv[DR_MD];
     tile.slots_fetch(qv, dv);
+    if constexpr (!MX) {
+        constexpr int UB = DownRowsBatch<BITS>::UB;   // units <= slots <= UB
+        __builtin_amdgcn_sched_barrier(0);
+        const int nu = ld_scalar<int32_t>(a.units);
+        // every load unconditional (a clamped index), so that they go out
+        // back to back behind one wait
+        const uint8_t *bp[UB];
+#pragma unroll
+        for (int ui = 0; ui < UB; ++ui)
+            bp[ui] = ld_scalar<const uint8_t *>(a.units + U.ublob + 8 * (size_t)min(ui, U.umax - 1));
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int ui = 0; ui < UB; ++ui) tile.issue_unit(ui, bp[ui], ui < nu, 0);   // past nu: no records
+        __builtin_amdgcn_sched_barrier(0);
+    }
     if (tid < U.words) tab[tid] = tw;
     if (tid < U.umax) ublob[tid] = tb;
     if (tid < P) w_l[tid] = wt;
     tile.slots_store(qv, dv);
     tile.zero_y();
-    __syncthreads();
+    if (MX)
+        __syncthreads();
+    else
+        lds_barrier();   // orders LDS only: the weights stay in flight
     tile.n_units = uniform(tab[0]);
     if (tid < tile.n_units && ublob[tid] == nullptr) raise_status(a.status, ST_NOTRESIDENT);
-    tile.run_staged();
+    tile.run_staged(!MX);
 }
 
 size_t down_rows_smem(int S, int I, int E, int K, int n_shared, int group, int bits) {

@@ -28,6 +28,15 @@ __device__ __forceinline__ T *uniform_ptr(T *p) {
     return reinterpret_cast<T *>(((uint64_t)hi << 32) | lo);
 }
 
+// A load through the scalar cache of a value that no wave writes during the
+// launch (an earlier launch wrote it): the address must be the same in
+// every lane.  Scalar loads count on their own counter, so waiting for one
+// does not wait for the vector loads issued before it.
+template <typename T>
+__device__ __forceinline__ T ld_scalar(const void *p) {
+    return *reinterpret_cast<const __attribute__((address_space(4))) T *>(reinterpret_cast<uintptr_t>(p));
+}
+
 // Per-vector stride of the staged block scales (a multiple of 4 so every
 // chunk of 64 scales starts 16-byte aligned).
 __host__ __device__ inline int vd_stride(int nb) { return (nb + 3) & ~3; }
