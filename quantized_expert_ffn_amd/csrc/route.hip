@@ -207,20 +207,36 @@ __device__ __forceinline__ void route_one(const RouteArgs &r, int bx, int lpw) {
     s_blob[tid] = my_blob;
     const int bad_in = __syncthreads_or(!finite_in);
     const int timed_out = __syncthreads_or(late);
-    // rank within the wavefront
+    // rank within the wavefront: the wavefront's 64 keys read two per LDS
+    // access, every read of a half issued before its compares (the ranking
+    // is a chain of LDS latencies otherwise)
+    auto key_lo = [](u32x4 v) { return ((uint64_t)v.y << 32) | v.x; };
+    auto key_hi = [](u32x4 v) { return ((uint64_t)v.w << 32) | v.z; };
     int c1 = 0;
-    const uint64_t *wk = s_key + wave * 64;
-#pragma unroll 8
-    for (int j = 0; j < 64; ++j) c1 += wk[j] > key ? 1 : 0;
+    const u32x4 *wk = reinterpret_cast<const u32x4 *>(s_key + wave * 64);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        u32x4 kv[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) kv[j] = wk[16 * h + j];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) c1 += (key_lo(kv[j]) > key ? 1 : 0) + (key_hi(kv[j]) > key ? 1 : 0);
+    }
     if (c1 < K) {
         s_ck[wave * K + c1] = key;
         s_cid[wave * K + c1] = tid;
     }
     __syncthreads();
+    // each of the 4 K candidates against the others, two per LDS access
     if (tid < 4 * K) {
         int c2 = 0;
         const uint64_t ck = s_ck[tid];
-        for (int j = 0; j < 4 * K; ++j) c2 += s_ck[j] > ck ? 1 : 0;
+        const u32x4 *cv = reinterpret_cast<const u32x4 *>(s_ck);
+#pragma unroll 8
+        for (int j = 0; j < 2 * K; ++j) {
+            const u32x4 v = cv[j];
+            c2 += (key_lo(v) > ck ? 1 : 0) + (key_hi(v) > ck ? 1 : 0);
+        }
         if (c2 < K) s_sel[c2] = s_cid[tid];
     }
     __syncthreads();
