@@ -397,7 +397,8 @@ __device__ __forceinline__ void prime_rows(__amdgpu_buffer_rsrc_t rsrc, const ui
 // workgroup barrier; it runs while chunk 0 is in flight.  Each wave then
 // works alone on its own LDS region (NT x RPW rows of ISUM_PITCH block
 // dots); for int4 / int2 the next chunk's weights are in flight while the
-// current chunk is reduced.
+// current chunk is reduced, for int8 each row of the next chunk from the
+// moment the current chunk's row has been used.
 // With GROUPED (G.lgb >= 0) the chain of chunk c uses the chunk's
 // group scales, loaded one chunk ahead with the weights and staged in the
 // wave's LDS region G.lds; the row scale is then not applied by the caller.
@@ -437,8 +438,37 @@ __device__ __forceinline__ float stream_rows(__amdgpu_buffer_rsrc_t rsrc, const 
 #pragma unroll
             for (int j = 0; j < RPW; ++j) nxt[j] = load_block<BITS>(rsrc, rowoff[j], b + 64);
         }
+        if constexpr (!PREFETCH) {
+            // int8: no registers for a second chunk, so row j of the next
+            // chunk is requested as soon as row j's block dots are done (the
+            // vectors' activations of the block are read first), keeping
+            // about one chunk in flight through the reduction
+            int32_t av[NT][8];
+#pragma unroll
+            for (int it = 0; it < NT; ++it) {
+#pragma unroll
+                for (int k = 0; k < 8; ++k) av[it][k] = 0;
+                if (it < ng && act) load_act(vq + (size_t)it * vlen, b, av[it]);
+            }
+            // every lane issues the refill (after the last chunk through an
+            // empty resource, which reads zeros without a memory access), so
+            // that the count of loads in flight is the same on every path
+            // and the wait for row j + 1 leaves the refills in flight; a
+            // lane past the row's end reads bytes it does not use
+            const __amdgpu_buffer_rsrc_t rnext = c + 1 < nchunks ? rsrc : make_rsrc(nullptr, 0u);
+#pragma unroll
+            for (int j = 0; j < RPW; ++j) {
+#pragma unroll
+                for (int it = 0; it < NT; ++it)
+                    if (it < ng) isum_wave[(it * RPW + j) * ISUM_PITCH + lane] = act ? block_dot(cur[j], av[it]) : 0;
+                __builtin_amdgcn_sched_barrier(0);
+                cur[j] = load_block<BITS>(rnext, rowoff[j], b + 64);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
 #pragma unroll
         for (int it = 0; it < NT; ++it) {
+            if (!PREFETCH) break;
             if (it < ng) {
                 int32_t av[8] = {0, 0, 0, 0, 0, 0, 0, 0};
                 if (act) load_act(vq + (size_t)it * vlen, b, av);
@@ -476,9 +506,6 @@ __device__ __forceinline__ float stream_rows(__amdgpu_buffer_rsrc_t rsrc, const 
         if (PREFETCH) {
 #pragma unroll
             for (int j = 0; j < RPW; ++j) cur[j] = nxt[j];
-        } else if (c + 1 < nchunks && b + 64 < nb) {
-#pragma unroll
-            for (int j = 0; j < RPW; ++j) cur[j] = load_block<BITS>(rsrc, rowoff[j], b + 64);
         }
     }
     return acc;
