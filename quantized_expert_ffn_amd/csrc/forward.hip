@@ -151,18 +151,22 @@ __global__ __launch_bounds__(256) void k_gateup(const FwdArgs a) {
         }
         __syncthreads();
     };
-    if constexpr (BITS < 8 && !GROUPED && !MX) {
+    // (MXFP4 with one vector only: the f16 activation pairs of more do not
+    // fit the registers beside two chunks of weights)
+    if constexpr (BITS < 8 && (!MX || NT == 1)) {
         const int nch = (nb + 63) / 64;
-        if (np <= NT && H <= 8192 && nch >= 2) {
-            // all of the unit's vectors in one pass: their activations are
-            // loaded ahead of the weights (gateup_unit_primed)
+        if (np <= NT && H <= 8192 && nch >= 2 && (!GROUPED || primed_scales_fit(H, a.group, MX))) {
+            // all of the unit's vectors in one pass: their activations (and
+            // the rows' group scales) are loaded ahead of the weights
+            // (gateup_unit_primed)
             auto tok = [&](int it) {
                 const int v = pairs[p0 + it];
                 return v < P ? v / K : v - P;
             };
             auto go = [&](auto nch_c) {
-                gateup_unit_primed<BITS, NT, decltype(nch_c)::value>(blob, H, I, blockIdx.x * 32, pairs + p0, np,
-                                                                     smem, L, a.qx, a.dx, tok, a.qh, a.dh);
+                gateup_unit_primed<BITS, NT, decltype(nch_c)::value, decltype(tok), GROUPED, MX>(
+                    blob, H, I, blockIdx.x * 32, pairs + p0, np, smem, L, a.qx, a.dx, tok, a.qh, a.dh, a.group,
+                    L.total);
             };
             if (nch == 2)
                 go(std::integral_constant<int, 2>());
@@ -298,7 +302,12 @@ static int pick_nt(int S) { return S >= 4 ? 4 : (S >= 2 ? 2 : 1); }
 size_t forward_smem_max(int S, int H, int I, int E, int K, int n_shared, int group) {
     (void)n_shared;
     const int nt = pick_nt(S);
-    return std::max(smem_plan(S, K, E, nt, H).total, smem_plan(S, K, E, nt, I).total) + groups_lds_bytes(group, 4);
+    // group scales staged a chunk at a time, or every chunk's at once by the
+    // primed gate/up tile (group 32 may be MXFP4: one E8M0 byte per block)
+    const size_t gs = group ? std::max({groups_lds_bytes(group, 4), primed_scales_lds_bytes(H, group, false),
+                                        group == 32 ? primed_scales_lds_bytes(H, group, true) : (size_t)0})
+                            : 0;
+    return std::max(smem_plan(S, K, E, nt, H).total, smem_plan(S, K, E, nt, I).total) + gs;
 }
 
 template <typename F>
@@ -314,7 +323,9 @@ static hipError_t gateup_bits(const FwdArgs &a, hipStream_t st) {
     const int umax = std::min(P, a.E) + a.n_shared - (TABLE ? a.shared_done : 0);
     const dim3 grid(a.I / 32, umax);
     const int nt = pick_nt(a.S);
-    const size_t smem = smem_plan(a.S, a.K, a.E, nt, a.H).total + groups_lds_bytes(a.group, 4);
+    // group scales: a chunk at a time, or every chunk's at once (primed tile)
+    const size_t gs = GROUPED ? std::max(groups_lds_bytes(a.group, 4), primed_scales_lds_bytes(a.H, a.group, MX)) : 0;
+    const size_t smem = smem_plan(a.S, a.K, a.E, nt, a.H).total + gs;
     if (nt == 1) return launch_dyn(k_gateup<BITS, 1, TABLE, GROUPED, MX>, grid, smem, st, a);
     if (nt == 2) return launch_dyn(k_gateup<BITS, 2, TABLE, GROUPED, MX>, grid, smem, st, a);
     return launch_dyn(k_gateup<BITS, 4, TABLE, GROUPED, MX>, grid, smem, st, a);

@@ -90,10 +90,14 @@ __device__ __forceinline__ void issue_chunk(__amdgpu_buffer_rsrc_t rsrc, const u
 
 // Block dots of chunk c (in X) against the np staged vectors, then the
 // chain lanes' binary32 chain over the chunk's blocks in ascending order.
-template <int BITS, int NT, int RPW>
+// GROUPED: gs is the chain lane's row of scales in LDS (every chunk's: f32
+// group scales, one per 1 << lgb blocks, or with MX the row's E8M0 bytes),
+// and the chain takes them (no row scale follows).
+template <int BITS, int NT, int RPW, bool GROUPED = false, bool MX = false>
 __device__ __forceinline__ float reduce_chunk(const BlockBits<BITS> (&X)[RPW], int c, int nb, int np,
                                               const int8_t *vq, const float *vd, int vds, int vlen,
-                                              int32_t *isum_wave, float acc) {
+                                              int32_t *isum_wave, float acc, const uint8_t *gs = nullptr,
+                                              int lgb = 0) {
     const int lane = threadIdx.x & 63, crow = lane % RPW, cvec = lane / RPW;
     const int b = c * 64 + lane;
     const bool act = b < nb;
@@ -103,16 +107,50 @@ __device__ __forceinline__ float reduce_chunk(const BlockBits<BITS> (&X)[RPW], i
             int32_t av[8] = {0, 0, 0, 0, 0, 0, 0, 0};
             if (act) load_act(vq + (size_t)it * vlen, b, av);
             int32_t *dst = isum_wave + it * RPW * ISUM_PITCH + lane;
+            if constexpr (MX) {
+                // exact block sums in binary32 (see block_dot_mx_f16)
+                f16x2 h[16];
+                mx_act_f16(av, h);
 #pragma unroll
-            for (int j = 0; j < RPW; ++j) dst[j * ISUM_PITCH] = act ? block_dot(X[j], av) : 0;
+                for (int j = 0; j < RPW; ++j)
+                    dst[j * ISUM_PITCH] = act ? __float_as_int(block_dot_mx_f16(X[j].w, h)) : 0;
+            } else {
+#pragma unroll
+                for (int j = 0; j < RPW; ++j) dst[j * ISUM_PITCH] = act ? block_dot(X[j], av) : 0;
+            }
         }
     }
     wave_lds_sync();
-    if (cvec < np)
-        acc = chain_chunk(acc, isum_wave + (cvec * RPW + crow) * ISUM_PITCH, vd + cvec * vds + c * 64,
-                          min(64, nb - c * 64));
+    if (cvec < np) {
+        const int32_t *is = isum_wave + (cvec * RPW + crow) * ISUM_PITCH;
+        const float *dv = vd + cvec * vds + c * 64;
+        const int nbc = min(64, nb - c * 64);
+        if constexpr (MX)
+            acc = chain_chunk_mx_bytes(acc, is, dv, gs + 64 * c, nbc);
+        else if constexpr (GROUPED)
+            acc = chain_chunk_g(acc, is, dv, reinterpret_cast<const float *>(gs) + (c * 64 >> lgb), lgb, nbc);
+        else
+            acc = chain_chunk(acc, is, dv, nbc);
+    }
     wave_lds_sync();
     return acc;
+}
+
+// Bytes of scales per row that the primed tile stages whole (every chunk's
+// at once): binary32 group scales of a group-scaled row, or the E8M0 bytes
+// of an MXFP4 row; 0 for per-row scales.  The tile takes such rows when a
+// wave's 16 rows of them fit PRIMED_GW 16-byte words per lane.
+constexpr int PRIMED_GW = 6;
+__host__ __device__ inline int primed_scale_row_bytes(int H, int group, bool mx) {
+    return mx ? H / 32 : (group ? 4 * (H / group) : 0);
+}
+__host__ __device__ inline bool primed_scales_fit(int H, int group, bool mx) {
+    const int rb = primed_scale_row_bytes(H, group, mx);
+    return rb > 0 && rb % 16 == 0 && rb <= 4 * PRIMED_GW * 16;
+}
+// LDS of the staged scales of a workgroup (4 waves x 16 rows).
+__host__ __device__ inline size_t primed_scales_lds_bytes(int H, int group, bool mx) {
+    return primed_scales_fit(H, group, mx) ? (size_t)64 * primed_scale_row_bytes(H, group, mx) : 0;
 }
 
 // gateup_unit for a unit whose pairs fit one pass (np <= NT), with packed
@@ -126,19 +164,27 @@ __device__ __forceinline__ float reduce_chunk(const BlockBits<BITS> (&X)[RPW], i
 // (chunk c + 2 is issued once chunk c has been reduced).  The chunks are
 // unrolled so that the waits the compiler places for each chunk's
 // registers leave the next chunk in flight.  Results as gateup_unit.
-template <int BITS, int NT, int NCH, typename Tok>
+//
+// GROUPED (group-scaled int4, or MXFP4 with MX), when primed_scales_fit():
+// the scales of the wave's 16 rows for every chunk (16 x
+// primed_scale_row_bytes, contiguous in the blob) are loaded right after
+// the activations, into registers, and stored to LDS at gs_off with them;
+// the chain then takes them and no row scale follows.
+template <int BITS, int NT, int NCH, typename Tok, bool GROUPED = false, bool MX = false>
 __device__ __forceinline__ void gateup_unit_primed(const uint8_t *blob, int H, int I, int i0, const int *slots,
                                                    int np, uint8_t *smem, const SmemPlan &L,
                                                    const int8_t *__restrict__ qx, const float *__restrict__ dx, Tok tok,
-                                                   int8_t *__restrict__ qh, float *__restrict__ dh) {
+                                                   int8_t *__restrict__ qh, float *__restrict__ dh, int group = 0,
+                                                   size_t gs_off = 0) {
     static_assert(BITS == 4 || BITS == 2, "one buffer load per block");
+    static_assert(!MX || (BITS == 4 && GROUPED), "MXFP4 rows are 4-bit codes with a scale per block");
     constexpr int RPW = ROWS_PER_WAVE;
     const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
     int8_t *vq = reinterpret_cast<int8_t *>(smem + L.vq);
     float *vd = reinterpret_cast<float *>(smem + L.vd);
     int32_t *isum_wave = reinterpret_cast<int32_t *>(smem + L.isum) + wave * NT * RPW * ISUM_PITCH;
     float *gu = reinterpret_cast<float *>(smem + L.gu);
-    const BlobLayout BL = blob_layout(H, I, BITS, 0, false);
+    const BlobLayout BL = blob_layout(H, I, BITS, GROUPED && !MX ? group : 0, MX);
     const size_t row_bytes = (size_t)H * BITS / 8;
     const int half = wave & 1;
     const size_t mat = wave < 2 ? BL.gate : BL.up;
@@ -161,10 +207,25 @@ __device__ __forceinline__ void gateup_unit_primed(const uint8_t *blob, int H, i
         const int it = fast_div(i, mb);
         return dx[(size_t)tok(it) * nb + (i - it * nb)];
     });
-    // 2. the row scale of this lane's chain row, 3. chunks 0 and 1
-    const uint32_t soff = (uint32_t)((wave < 2 ? BL.s_gate : BL.s_up) + 4 * (size_t)(i0 + 16 * half + crow));
+    // 2. the wave's rows' scales: the row scale of this lane's chain row, or
+    //    (GROUPED) every scale of the wave's 16 rows, PRIMED_GW words per
+    //    lane, all issued (words past the rows read bytes that are not used),
+    //    3. chunks 0 and 1
+    const size_t ssec = wave < 2 ? BL.s_gate : BL.s_up;
+    const int rb = GROUPED ? primed_scale_row_bytes(H, group, MX) : 0;
     __builtin_amdgcn_sched_barrier(0);
-    const float rs = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsrc, soff, 0, 0));
+    float rs = 1.0f;
+    i32x4 gsw[GROUPED ? PRIMED_GW : 1];
+    if constexpr (GROUPED) {
+        const uint32_t gbase = (uint32_t)(ssec + (size_t)(i0 + 16 * half) * rb);
+#pragma unroll
+        for (int k = 0; k < PRIMED_GW; ++k)
+            gsw[k] = __builtin_bit_cast(
+                i32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, gbase + 16u * (uint32_t)(lane + 64 * k), 0, 0));
+    } else {
+        const uint32_t soff = (uint32_t)(ssec + 4 * (size_t)(i0 + 16 * half + crow));
+        rs = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsrc, soff, 0, 0));
+    }
     BlockBits<BITS> A[RPW], B[RPW];
     issue_chunk<BITS, RPW>(rsrc, rowoff, 0, A);
     __builtin_amdgcn_sched_barrier(0);   // chunk 0's loads ahead of chunk 1's
@@ -178,22 +239,32 @@ __device__ __forceinline__ void gateup_unit_primed(const uint8_t *blob, int H, i
         const int it = fast_div(i, mb);
         return vd + it * vds + (i - it * nb);
     });
+    uint8_t *gsl = smem + gs_off + (size_t)wave * RPW * rb;   // this wave's rows' scales
+    if constexpr (GROUPED) {
+#pragma unroll
+        for (int k = 0; k < PRIMED_GW; ++k) {
+            const int w = lane + 64 * k;
+            if (w < rb) reinterpret_cast<i32x4 *>(gsl)[w] = gsw[k];   // RPW x rb / 16 = rb words
+        }
+    }
     lds_barrier();
+    const uint8_t *gs = gsl + (size_t)crow * rb;   // the chain lane's row
+    const int lgb = GROUPED && !MX ? group_lgb(group) : 0;
     float acc = 0.0f;
 #pragma unroll
     for (int c = 0; c < NCH; c += 2) {
-        acc = reduce_chunk<BITS, NT, RPW>(A, c, nb, np, vq, vd, vds, H, isum_wave, acc);
+        acc = reduce_chunk<BITS, NT, RPW, GROUPED, MX>(A, c, nb, np, vq, vd, vds, H, isum_wave, acc, gs, lgb);
         __builtin_amdgcn_sched_barrier(0);
         if (c + 2 < NCH) issue_chunk<BITS, RPW>(rsrc, rowoff, c + 2, A);
         __builtin_amdgcn_sched_barrier(0);
         if (c + 1 < NCH) {
-            acc = reduce_chunk<BITS, NT, RPW>(B, c + 1, nb, np, vq, vd, vds, H, isum_wave, acc);
+            acc = reduce_chunk<BITS, NT, RPW, GROUPED, MX>(B, c + 1, nb, np, vq, vd, vds, H, isum_wave, acc, gs, lgb);
             __builtin_amdgcn_sched_barrier(0);
             if (c + 3 < NCH) issue_chunk<BITS, RPW>(rsrc, rowoff, c + 3, B);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
-    if (cvec < np) gu[cvec * 64 + wave * RPW + crow] = acc * rs;
+    if (cvec < np) gu[cvec * 64 + wave * RPW + crow] = GROUPED ? acc : acc * rs;
     __syncthreads();
     const int vv = tid >> 5, i = tid & 31;
     if (vv < np) {

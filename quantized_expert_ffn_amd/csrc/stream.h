@@ -302,6 +302,39 @@ __device__ __forceinline__ float chain_chunk_g(float acc, const int32_t *is, con
     return acc;
 }
 
+// The MXFP4 chain of one chunk with the row's E8M0 bytes xb (one per block,
+// raw, in LDS): the same operations as chain_chunk_g<true> with group 32,
+// the multiplier 2^(x_b - 128) formed from the byte.
+__device__ __forceinline__ float chain_chunk_mx_bytes(float acc, const int32_t *is, const float *dv, const uint8_t *xb,
+                                                      int nbc) {
+    if (nbc == 64) {
+#pragma unroll 1
+        for (int qq = 0; qq < 64; qq += 16) {
+            i32x4 iv[4];
+            f32x4 dd[4];
+            const u32x4 xw = *reinterpret_cast<const u32x4 *>(xb + qq);
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                iv[q4] = *reinterpret_cast<const i32x4 *>(is + qq + 4 * q4);
+                dd[q4] = *reinterpret_cast<const f32x4 *>(dv + qq + 4 * q4);
+            }
+            const uint32_t xs[4] = {xw.x, xw.y, xw.z, xw.w};
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const uint32_t x = xs[q4];
+                acc = __builtin_fmaf(dd[q4].x * e8m0_half(x & 0xFFu), __int_as_float(iv[q4].x), acc);
+                acc = __builtin_fmaf(dd[q4].y * e8m0_half((x >> 8) & 0xFFu), __int_as_float(iv[q4].y), acc);
+                acc = __builtin_fmaf(dd[q4].z * e8m0_half((x >> 16) & 0xFFu), __int_as_float(iv[q4].z), acc);
+                acc = __builtin_fmaf(dd[q4].w * e8m0_half(x >> 24), __int_as_float(iv[q4].w), acc);
+            }
+        }
+    } else {
+        for (int bb = 0; bb < nbc; ++bb)
+            acc = __builtin_fmaf(dv[bb] * e8m0_half(xb[bb]), __int_as_float(is[bb]), acc);
+    }
+    return acc;
+}
+
 // Group scales of a wave's rows (one f32 per 32 << lgb codes), staged
 // through LDS one 64-block chunk at a time: the chunk's RPW x (64 >> lgb)
 // scales are 16-byte words w = lane + 64 k, word w holding scales
