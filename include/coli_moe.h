@@ -276,14 +276,16 @@ int coli_moe_timing_read(int32_t kind, double *total_ms, int64_t *launches);
 int coli_moe_debug_force_path(int32_t path);
 
 /* Failure-path hook for later calls in this process (not for concurrent
- * calls).  The one-token router launch (at most 256 experts) selects in one
- * workgroup that waits, bounded, for every logit of the launch; the wait
+ * calls).  The router launch of one to four tokens (at most 256 experts)
+ * selects in one workgroup that waits, bounded, for every logit of the
+ * launch; the wait
  * gives up after `spins` polls (0: the default bound, 2^22).  With
  * unreachable = 1 (spins must then be nonzero) it waits for a tag that no
  * workgroup writes, so it always gives up: coli_moe_status then reports
  * COLI_EHIP (a timed-out wait), the router writes a unit table holding the
- * shared expert alone, and every launch still ends normally, so `out` is
- * the shared expert's output.  unreachable = 0 restores the normal wait.
+ * shared expert alone (with several tokens, every routing weight 0), and
+ * every launch still ends normally, so `out` is the shared expert's output.
+ * unreachable = 0 restores the normal wait.
  * Returns COLI_EINVAL
  * for unreachable outside {0, 1} or an unreachable wait without a bound. */
 int coli_moe_debug_route_wait(uint32_t spins, int32_t unreachable);

@@ -88,7 +88,7 @@ inline WsLayout ws_layout(int H, int I, int E, int K, int S, bool mx = false) {
     L.Y = al256h(L.dh + 4 * slots * (size_t)(I / 32));
     L.hs = al256h(L.Y + 4 * slots * (size_t)H);
     L.slots = al256h(L.hs + 4 * (size_t)(S < 2 ? S : 2) * (size_t)I);
-    L.qxs = al256h(L.slots + 8 * (size_t)E);
+    L.qxs = al256h(L.slots + 8 * (size_t)E * (size_t)(S < 4 ? S : 4));   // tagged logits of up to 4 tokens
     L.qhs = al256h(L.qxs + (mx ? 2 * (size_t)S * (size_t)H : 0));
     L.total = al256h(L.qhs + (mx ? 2 * slots * (size_t)I : 0));
     return L;
@@ -137,7 +137,7 @@ struct RouteArgs {
     uint8_t *units;
     uint32_t *sync;
     float *hs;                     // with sg: the shared expert's h [S, I], binary32
-    uint64_t *slots;               // one token: [E] published logits, (tag << 32) | binary32 bits
+    uint64_t *slots;               // up to 4 tokens: [S][E] published logits, (tag << 32) | binary32 bits
     uint32_t *epoch;               // one token: the workspace's router epoch (WS_EPOCH)
     uint32_t spin_limit;           // one token: polls before the selection's wait gives up
     uint32_t tag_skew;             // one token: 0, or (test hook) 1 to wait for a tag no one writes

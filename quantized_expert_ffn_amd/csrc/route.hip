@@ -286,6 +286,141 @@ __device__ __forceinline__ void route_one(const RouteArgs &r, int bx, int lpw) {
     }
 }
 
+// The unit table of a batch from its selections (idx_l: S x K ids in LDS,
+// btab: the first 256 experts' blob pointers in LDS): build_units in LDS,
+// then the table's words and blob pointers to the workspace.  Every thread
+// of the workgroup.
+__device__ __forceinline__ void write_unit_table(const RouteArgs &r, uint8_t *smem, const SmemPlan &T,
+                                                 const int32_t *idx_l, const uint8_t *const *btab) {
+    const int tid = threadIdx.x, S = r.S, K = r.K, E = r.E, P = S * K;
+    build_units(idx_l, S, K, E, r.n_shared, smem, T, r.status, false);
+    const UnitTable U = unit_table(S, K, E);
+    int32_t *tab = reinterpret_cast<int32_t *>(r.units);
+    const int *misc = reinterpret_cast<const int *>(smem + T.misc);
+    const int *uexp = reinterpret_cast<const int *>(smem + T.uexp);
+    const int *uoff = reinterpret_cast<const int *>(smem + T.uoff);
+    const int *pairs = reinterpret_cast<const int *>(smem + T.pairs);
+    const int n_units = misc[0];
+    if (tid < 4) tab[tid] = tid < 3 ? misc[tid] : 0;
+    for (int q = tid; q < n_units; q += blockDim.x) {
+        const int ex = uexp[q];
+        tab[U.uexp + q] = ex;
+        reinterpret_cast<const uint8_t **>(r.units + U.ublob)[q] =
+            ex < 0 ? r.shared : (ex < 256 ? btab[ex] : r.blobs[ex]);
+    }
+    for (int q = tid; q <= n_units; q += blockDim.x) tab[U.uoff + q] = uoff[q];
+    for (int q = tid; q < P + S * r.n_shared; q += blockDim.x) tab[U.pairs + q] = pairs[q];
+}
+
+// The logit and selecting workgroups of a launch of 2 .. 4 tokens with at
+// most 256 experts (the same selection rule as route_one): wave w of logit
+// workgroup bx of token t computes logit (t, lpw bx + w) and publishes it as
+// a tagged 64-bit slot (slot t E + e).  Workgroup 0 of token 0 then waits
+// (bounded) for all S x E slots, wavefront w selects token w with
+// select_wave_b from the logits in LDS, and the workgroup builds the unit
+// table: one workgroup, no arrival counters and no round trip of the
+// selections through memory.  A wait that gave up leaves the shared expert
+// alone in the table (status timed-out).
+template <int MAXJ>
+__device__ __forceinline__ void route_few(const RouteArgs &r, uint8_t *smem, int bx, int lpw, int t) {
+    __shared__ float s_lg[4][256];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int E = r.E, K = r.K, S = r.S, H = r.H, P = S * K;
+    const uint32_t tag = ld_dev(r.epoch) + 1u;
+    const bool selector = bx == 0 && t == 0;
+    // the selector's inputs besides the logits, fetched ahead of them: the
+    // bias (every wave selects) and the blob pointers
+    float bpre[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    const uint8_t *bl[4] = {nullptr, nullptr, nullptr, nullptr};
+    if (selector) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int ee = min(lane + 64 * m, E - 1);
+            if (r.bias) bpre[m] = r.bias[ee];
+            if (wave == 0) bl[m] = r.blobs[ee];
+        }
+    }
+    const int e = bx * lpw + wave;
+    if (wave < lpw && e < E) {
+        bool ok;
+        const float p = logit_wave<MAXJ>(r.x + (size_t)t * H, r.W + (size_t)e * H, H, &ok);
+        if (!ok) raise_status(r.status, ST_NONFINITE);
+        if (lane == 0) st_dev64(&r.slots[(size_t)t * E + e], ((uint64_t)tag << 32) | __float_as_uint(p));
+    }
+    if (!selector) return;
+    bool late = false;
+    if (tid < E) {
+        const uint32_t want = tag + r.tag_skew;
+        uint64_t v[4];
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+            if (tt < S) v[tt] = ld_dev64(&r.slots[(size_t)tt * E + tid]);
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+            if (tt < S) {
+                uint32_t spins = 0;
+                while (!late && (uint32_t)(v[tt] >> 32) != want) {
+                    __builtin_amdgcn_s_sleep(1);
+                    if (++spins >= r.spin_limit) late = true;
+                    else v[tt] = ld_dev64(&r.slots[(size_t)tt * E + tid]);
+                }
+                s_lg[tt][tid] = __uint_as_float((uint32_t)v[tt]);
+            }
+        }
+    }
+    const SmemPlan T = smem_plan(S, K, E, 0, 0);
+    int32_t *idx_l = reinterpret_cast<int32_t *>(smem + T.total);
+    const uint8_t **btab = reinterpret_cast<const uint8_t **>(smem + a16(T.total + 4 * (size_t)P));
+    if (wave == 0) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+            if (lane + 64 * m < E) btab[lane + 64 * m] = bl[m];
+    }
+    const int timed_out = __syncthreads_or(late);
+    if (timed_out) {
+        // the logits are not all in: no routed unit, the shared expert alone
+        // (every routing weight 0, so the combine adds no routed term)
+        for (int q = tid; q < P; q += blockDim.x) {
+            r.idx_out[q] = 0;
+            r.w_out[q] = 0.0f;
+        }
+        if (tid == 0) {
+            raise_status(r.status, ST_TIMEOUT);
+            const UnitTable U = unit_table(S, K, E);
+            int32_t *tab = reinterpret_cast<int32_t *>(r.units);
+            const int ns = r.n_shared;
+            tab[0] = ns;
+            tab[1] = 0;
+            tab[2] = 0;
+            tab[3] = 0;
+            for (int q = 0; q < ns * S; ++q) tab[U.pairs + q] = P + q;
+            if (ns) {
+                tab[U.uexp] = -1;
+                reinterpret_cast<const uint8_t **>(r.units + U.ublob)[0] = r.shared;
+            }
+            tab[U.uoff] = 0;
+            tab[U.uoff + ns] = ns * S;
+            st_dev(r.epoch, tag);
+        }
+        return;
+    }
+    if (wave < S) {
+        int32_t si = 0;
+        float sw = 0.0f;
+        const bool sok = select_wave_b<4>([&](int q) { return s_lg[wave][q]; }, [&](int m, int) { return bpre[m]; },
+                                          E, K, r.rsf, r.norm, &si, &sw);
+        if (!sok && lane == 0) raise_status(r.status, ST_NONFINITE);
+        if (lane < K) {
+            r.idx_out[(size_t)wave * K + lane] = si;
+            r.w_out[(size_t)wave * K + lane] = sw;
+            idx_l[wave * K + lane] = si;
+        }
+    }
+    __syncthreads();
+    write_unit_table(r, smem, T, idx_l, btab);
+    if (tid == 0) st_dev(r.epoch, tag);
+}
+
 template <int MAXJ, int BITS, int NT, bool GROUPED, bool MX = false>
 __global__ __launch_bounds__(64 * RF_W) void k_route_fused(const RouteArgs r) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -305,6 +440,10 @@ __global__ __launch_bounds__(64 * RF_W) void k_route_fused(const RouteArgs r) {
     }
     if (S == 1 && E <= 256) {
         route_one<MAXJ>(r, bx, lpw);
+        return;
+    }
+    if (S <= 4 && E <= 256) {
+        route_few<MAXJ>(r, smem, bx, lpw, t);
         return;
     }
     // wave 0 fetches what the selection needs besides the logits (the bias
@@ -449,23 +588,7 @@ __global__ __launch_bounds__(64 * RF_W) void k_route_fused(const RouteArgs r) {
             if (lane + 64 * m < E) btab[lane + 64 * m] = bl[m];
     }
     __syncthreads();
-    build_units(idx_l, S, K, E, r.n_shared, smem, T, r.status, false);
-    const UnitTable U = unit_table(S, K, E);
-    int32_t *tab = reinterpret_cast<int32_t *>(r.units);
-    const int *misc = reinterpret_cast<const int *>(smem + T.misc);
-    const int *uexp = reinterpret_cast<const int *>(smem + T.uexp);
-    const int *uoff = reinterpret_cast<const int *>(smem + T.uoff);
-    const int *pairs = reinterpret_cast<const int *>(smem + T.pairs);
-    const int n_units = misc[0];
-    if (tid < 4) tab[tid] = tid < 3 ? misc[tid] : 0;
-    for (int q = tid; q < n_units; q += blockDim.x) {
-        const int ex = uexp[q];
-        tab[U.uexp + q] = ex;
-        reinterpret_cast<const uint8_t **>(r.units + U.ublob)[q] =
-            ex < 0 ? r.shared : (ex < 256 ? btab[ex] : r.blobs[ex]);
-    }
-    for (int q = tid; q <= n_units; q += blockDim.x) tab[U.uoff + q] = uoff[q];
-    for (int q = tid; q < P + S * r.n_shared; q += blockDim.x) tab[U.pairs + q] = pairs[q];
+    write_unit_table(r, smem, T, idx_l, btab);
 }
 
 size_t route_fused_smem(int S, int K, int E) {

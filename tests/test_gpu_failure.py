@@ -1,7 +1,7 @@
 """A failure path forced from the host, with every kernel ending normally.
 
-The one-token router launch selects in one workgroup that waits, bounded,
-for the logits its other workgroups publish.  coli_moe_debug_route_wait
+The router launch of one to four tokens selects in one workgroup that
+waits, bounded, for the logits its other workgroups publish.  coli_moe_debug_route_wait
 makes that wait look for a tag no workgroup writes, with a short bound, so
 it always gives up.  The contract for that case (a failure is reported,
 never hidden behind a fallback: colibrì README v1.0, "Experimental resident
@@ -37,16 +37,16 @@ def _call(torch, dims, dl, ws):
     return idx, w, out
 
 
-@pytest.mark.parametrize("fmt", ["int4", "int8", "mxfp4"])
-def test_router_wait_gives_up_routes_the_shared_expert_alone(torch, fmt):
+@pytest.mark.parametrize("fmt,S", [("int4", 1), ("int8", 1), ("mxfp4", 1), ("int4", 2), ("int8", 4), ("mxfp4", 3)])
+def test_router_wait_gives_up_routes_the_shared_expert_alone(torch, fmt, S):
     from synth.device import upload_layer
     spec = {"int4": synth.TINY, "int8": dataclasses.replace(synth.TINY, wbits=8), "mxfp4": synth.TINY_MX}[fmt]
-    d = synth.tiny_layer(seed=31, S=1, spec=spec)
+    d = synth.tiny_layer(seed=31, S=S, spec=spec)
     dims = q().make_dims(spec)
     dl = upload_layer(d)
-    ws = workspace(dims, 1)
+    ws = workspace(dims, S)
     qm = q()
-    say(f"router wait forced to give up ({fmt})")
+    say(f"router wait forced to give up ({fmt}, {S} tokens)")
     qm.coli_moe_debug_route_wait(64, 1)
     try:
         _, _, out = _call(torch, dims, dl, ws)
@@ -54,12 +54,13 @@ def test_router_wait_gives_up_routes_the_shared_expert_alone(torch, fmt):
     finally:
         qm.coli_moe_debug_route_wait(0, 0)
     assert rc == qm.COLI_EHIP and "timed out" in qm.coli_moe_last_error()
-    qx, dx = oracle.q8_0(d["x"][0])
-    y = oracle.expert(d["shared"], spec.hidden, spec.inter, spec.wbits, qx, dx, spec.group, spec.fmt)["y"]
-    want = (np.float32(0.0) + y).astype(np.float32)
-    got = out.cpu().numpy()[0]
-    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
-    say(f"router wait restored ({fmt})")
+    got = out.cpu().numpy()
+    for t in range(S):
+        qx, dx = oracle.q8_0(d["x"][t])
+        y = oracle.expert(d["shared"], spec.hidden, spec.inter, spec.wbits, qx, dx, spec.group, spec.fmt)["y"]
+        want = (np.float32(0.0) + y).astype(np.float32)
+        assert np.array_equal(got[t].view(np.uint32), want.view(np.uint32)), t
+    say(f"router wait restored ({fmt}, {S} tokens)")
     idx, w, out = _call(torch, dims, dl, ws)
     assert status(ws) == 0, qm.coli_moe_last_error()
     o_out, o_idx, o_w = oracle.layer(spec, d["x"], d["router_w"], d["bias"], d["blobs"], d["shared"])
