@@ -65,7 +65,11 @@ __host__ __device__ inline SmemPlan smem_plan(int S, int K, int E, int NT, int v
 // topk_idx in ascending id, then the shared expert.  The order of pairs
 // inside a unit does not affect any value (every pair has its own output
 // slot and its own chain).  With `validate`, out-of-range and repeated
-// indices are flagged in the status word.
+// indices are flagged in the status word.  A thread takes whole tokens and
+// loads their indices BU_KC at a time, all in flight together (one memory
+// round trip per group, not one per pair), before counting and checking
+// them in registers.
+constexpr int BU_KC = 8;
 __device__ inline void build_units(const int32_t *__restrict__ idx, int S, int K, int E, int n_shared,
                             uint8_t *smem, const SmemPlan &L, uint32_t *status, bool validate) {
     int *cnt = reinterpret_cast<int *>(smem + L.cnt);
@@ -82,17 +86,41 @@ __device__ inline void build_units(const int32_t *__restrict__ idx, int S, int K
         fill[e] = 0;
     }
     __syncthreads();
-    for (int p = tid; p < P; p += nthr) {
-        const int e = idx[p];
-        if (e >= 0 && e < E) {
-            atomicAdd(&cnt[e], 1);
-            if (validate) {
-                const int t0 = (p / K) * K;
-                for (int q = t0; q < p; ++q)
-                    if (idx[q] == e) raise_status(status, ST_BADINDEX);
+    // indices k0 .. k0 + BU_KC - 1 of token t (-1 past K)
+    auto load_group = [&](int t, int k0, int (&v)[BU_KC]) {
+#pragma unroll
+        for (int j = 0; j < BU_KC; ++j) v[j] = k0 + j < K ? idx[(size_t)t * K + k0 + j] : -1;
+    };
+    for (int t = tid; t < S; t += nthr) {
+        for (int k0 = 0; k0 < K; k0 += BU_KC) {
+            int v[BU_KC];
+            load_group(t, k0, v);
+            bool bad = false;
+#pragma unroll
+            for (int j = 0; j < BU_KC; ++j) {
+                if (k0 + j >= K) break;
+                const int e = v[j];
+                if (e >= 0 && e < E)
+                    atomicAdd(&cnt[e], 1);
+                else
+                    bad = true;
+                if (validate) {
+#pragma unroll
+                    for (int i = 0; i < j; ++i) bad |= v[i] == e;   // a repeat within the group
+                }
             }
-        } else if (validate) {
-            raise_status(status, ST_BADINDEX);
+            if (validate) {
+                // a repeat of an earlier group of the token (top-k above BU_KC)
+                for (int q0 = 0; q0 < k0; q0 += BU_KC) {
+                    int u[BU_KC];
+                    load_group(t, q0, u);
+#pragma unroll
+                    for (int j = 0; j < BU_KC; ++j)
+#pragma unroll
+                        for (int i = 0; i < BU_KC; ++i) bad |= k0 + j < K && u[i] == v[j];
+                }
+                if (bad) raise_status(status, ST_BADINDEX);
+            }
         }
     }
     __syncthreads();
@@ -135,9 +163,16 @@ __device__ inline void build_units(const int32_t *__restrict__ idx, int S, int K
         }
     }
     __syncthreads();
-    for (int p = tid; p < P; p += nthr) {
-        const int e = idx[p];
-        if (e >= 0 && e < E) pairs[ustart[e] + atomicAdd(&fill[e], 1)] = p;
+    for (int t = tid; t < S; t += nthr) {
+        for (int k0 = 0; k0 < K; k0 += BU_KC) {
+            int v[BU_KC];
+            load_group(t, k0, v);
+#pragma unroll
+            for (int j = 0; j < BU_KC; ++j) {
+                const int e = v[j];
+                if (e >= 0 && e < E) pairs[ustart[e] + atomicAdd(&fill[e], 1)] = t * K + k0 + j;
+            }
+        }
     }
     const int nr = misc[1], pv = misc[2];
     if (n_shared)
