@@ -38,6 +38,14 @@ struct DownRowsBatch {
     static constexpr int UB = BITS == 8 ? 4 : (BITS == 4 ? 9 : 16);  // units per batch
 };
 
+// Whether the binary32 group scales (group > 0) of a wave's rows of a whole
+// batch fit the staged tile's round of registers (DownTile::GW_GS words per
+// lane) as whole 4-byte words.
+__host__ __device__ inline bool down_staged_groups_fit(int I, int group, int bits) {
+    const int ub = bits == 8 ? DownRowsBatch<8>::UB : (bits == 4 ? DownRowsBatch<4>::UB : DownRowsBatch<2>::UB);
+    return group > 0 && I % group == 0 && ub * DR_RPW * (I / group) <= 64 * 9;
+}
+
 // Whether every pair slot of a call fits one batch and one staging round of
 // a down tile whatever the routing (a unit has at least one pair, so there
 // are no more units than slots), with rows of one 64-block chunk, and the
@@ -202,6 +210,16 @@ struct DownTile {
         const uint8_t *blob = ublob[u0 + ur / DR_RPW];
         return blob ? *reinterpret_cast<const uint32_t *>(
                           blob + BL.s_down + (size_t)(groups_row0() + ur % DR_RPW) * groups_ngr() + 4 * p)
+                    : 0u;
+    }
+    // Word w of the binary32 group scales of this wave's rows of units
+    // u0 ..: row ur = w / ngr of them (unit u0 + ur / DR_RPW), scale w % ngr.
+    static constexpr int GW_GS = 9;
+    __device__ __forceinline__ uint32_t gs_word(int u0, int w) const {
+        const int ngr = groups_ngr(), ur = w / ngr, p = w - ur * ngr;
+        const uint8_t *blob = ublob[u0 + ur / DR_RPW];
+        return blob ? *reinterpret_cast<const uint32_t *>(
+                          blob + BL.s_down + ((size_t)(groups_row0() + ur % DR_RPW) * ngr + p) * 4)
                     : 0u;
     }
     __device__ __forceinline__ void mx_store(int u0, int w, uint32_t v, float *dst) const {
@@ -469,22 +487,32 @@ struct DownTile {
         while (ub + 1 < n_units && uoff[ub + 1] <= cp) ++ub;
         // MXFP4: the E8M0 bytes of this wave's rows of every unit (UB x
         // DR_RPW rows of nbi bytes, kept raw in LDS) go out first, the
-        // weights right behind them
+        // weights right behind them; group scales (binary32, ngr a row:
+        // down_staged_groups_fit) the same way, as raw words
         static_assert(!MX || UB * DR_RPW * 64 / 4 <= 64 * GW_MX, "one round of scale words");
-        uint32_t *gsw = reinterpret_cast<uint32_t *>(smem + D.gs) + wave * UB * DR_RPW * (nbi / 4);
-        const int nsw = n_units * DR_RPW * (nbi / 4);
-        uint32_t mxv[GW_MX];
+        constexpr bool GS = GROUPED && !MX;
+        const int ngr = GS ? groups_ngr() : 0;
+        const int wrow = MX ? nbi / 4 : ngr;   // scale words per row
+        uint32_t *gsw = reinterpret_cast<uint32_t *>(smem + D.gs) + wave * UB * DR_RPW * wrow;
+        const int nsw = n_units * DR_RPW * wrow;
+        uint32_t mxv[MX ? GW_MX : (GS ? GW_GS : 1)];
         if (MX) {
 #pragma unroll
             for (int k = 0; k < GW_MX; ++k) {
                 const int w = lane + 64 * k;
                 mxv[k] = w < nsw ? mx_word(0, w) : 0u;
             }
+        } else if (GS) {
+#pragma unroll
+            for (int k = 0; k < GW_GS; ++k) {
+                const int w = lane + 64 * k;
+                mxv[k] = w < nsw ? gs_word(0, w) : 0u;
+            }
         }
         if (!issued) issue(0, n_units, 0);
         float sd = 0.0f;
         const uint8_t *my_blob = chain ? ublob[ub] : nullptr;
-        if (!MX && my_blob) sd = reinterpret_cast<const float *>(my_blob + BL.s_down)[r0 + rl];
+        if (!GROUPED && my_blob) sd = reinterpret_cast<const float *>(my_blob + BL.s_down)[r0 + rl];
         const int b = lane;
         const bool act = b < nbi;
 #pragma unroll
@@ -513,9 +541,9 @@ struct DownTile {
                 }
             }
         }
-        if (MX) {
+        if (GROUPED) {
 #pragma unroll
-            for (int k = 0; k < GW_MX; ++k) {
+            for (int k = 0; k < (MX ? GW_MX : GW_GS); ++k) {
                 const int w = lane + 64 * k;
                 if (w < nsw) gsw[w] = mxv[k];
             }
@@ -523,7 +551,13 @@ struct DownTile {
         wave_lds_sync();
         if (chain) {
             const int slot = pairs[cp];
-            if constexpr (MX) {
+            if constexpr (GS) {
+                // multiplier d_b * s_g per block, no row scale
+                const float acc = chain_chunk_g(0.0f, isum + (cr * mpb + cp) * ISUM_PITCH, dh_l + slot * dpitch,
+                                                reinterpret_cast<const float *>(gsw) + (ub * DR_RPW + cr) * ngr,
+                                                group_lgb(a.group), nbi);
+                y_l[slot * DR_ROWS + rl] = my_blob ? acc : 0.0f;
+            } else if constexpr (MX) {
                 // multiplier d_b * 2^(x_b - 128) per block, no row scale
                 const float acc = chain_mx_bytes(isum + (cr * mpb + cp) * ISUM_PITCH, dh_l + slot * dpitch,
                                                  gsw + (ub * DR_RPW + cr) * (nbi / 4), nbi);

@@ -86,25 +86,25 @@ __global__ __launch_bounds__(DR_T) __attribute__((amdgpu_waves_per_eu(MX ? 2 : 3
 // so storing the staged data to LDS then waits for none of the weights);
 // MXFP4 tiles issue theirs from LDS after the staging
 // (DownTile::run_staged).
-template <int BITS, bool ONE_TOKEN, bool MX = false>
+template <int BITS, bool ONE_TOKEN, bool GROUPED = false, bool MX = false>
 __global__ __launch_bounds__(DR_T) __attribute__((amdgpu_waves_per_eu(3))) void k_down_rows_staged(const FwdArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int tid = threadIdx.x;
     const int S = a.S, K = a.K, E = a.E, P = S * K;
-    const DownRowsPlan D = down_rows_plan(S, K, E, a.n_shared, a.I, MX ? a.group : 0, BITS, 1);
+    const DownRowsPlan D = down_rows_plan(S, K, E, a.n_shared, a.I, GROUPED ? a.group : 0, BITS, MX ? 1 : 4);
     const uint8_t **ublob = reinterpret_cast<const uint8_t **>(smem + D.ublob);
     float *w_l = reinterpret_cast<float *>(smem + D.w);
     const UnitTable U = unit_table(S, K, E);
     int *tab = reinterpret_cast<int *>(smem);
-    DownTile<BITS, ONE_TOKEN, false, MX, MX> tile(a, smem, D.tile, tab + U.uoff, tab + U.pairs, ublob, w_l, 0,
-                                                  blockIdx.x);
+    DownTile<BITS, ONE_TOKEN, false, GROUPED, MX> tile(a, smem, D.tile, tab + U.uoff, tab + U.pairs, ublob, w_l, 0,
+                                                       blockIdx.x);
     const int32_t tw = tid < U.words ? reinterpret_cast<const int32_t *>(a.units)[tid] : 0;
     const uint8_t *tb = tid < U.umax ? reinterpret_cast<const uint8_t *const *>(a.units + U.ublob)[tid] : nullptr;
     const float wt = tid < P ? a.w[tid] : 0.0f;
     i32x4 qv[DR_MQ];
     float dv[DR_MD];
     tile.slots_fetch(qv, dv);
-    if constexpr (!MX) {
+    if constexpr (!GROUPED) {
         constexpr int UB = DownRowsBatch<BITS>::UB;   // units <= slots <= UB
         __builtin_amdgcn_sched_barrier(0);
         const int nu = ld_scalar<int32_t>(a.units);
@@ -124,13 +124,13 @@ __global__ __launch_bounds__(DR_T) __attribute__((amdgpu_waves_per_eu(3))) void 
     if (tid < P) w_l[tid] = wt;
     tile.slots_store(qv, dv);
     tile.zero_y();
-    if (MX)
+    if (GROUPED)
         __syncthreads();
     else
         lds_barrier();   // orders LDS only: the weights stay in flight
     tile.n_units = uniform(tab[0]);
     if (tid < tile.n_units && ublob[tid] == nullptr) raise_status(a.status, ST_NOTRESIDENT);
-    tile.run_staged(!MX);
+    tile.run_staged(!GROUPED);
 }
 
 size_t down_rows_smem(int S, int I, int E, int K, int n_shared, int group, int bits) {
@@ -138,8 +138,9 @@ size_t down_rows_smem(int S, int I, int E, int K, int n_shared, int group, int b
 }
 
 hipError_t launch_down_rows(const FwdArgs &a, int bits, hipStream_t st) {
-    const bool staged = a.units && (a.mx || !a.group) && down_slots_fit(a.S, a.K, a.E, a.n_shared, a.I, bits);
-    const size_t smem = down_rows_plan(a.S, a.K, a.E, a.n_shared, a.I, a.group, bits, staged ? 1 : 4).total;
+    const bool staged = a.units && (a.mx || !a.group || down_staged_groups_fit(a.I, a.group, bits)) &&
+                        down_slots_fit(a.S, a.K, a.E, a.n_shared, a.I, bits);
+    const size_t smem = down_rows_plan(a.S, a.K, a.E, a.n_shared, a.I, a.group, bits, staged && a.mx ? 1 : 4).total;
     const dim3 grid(a.H / DR_ROWS);
     auto go = [&](auto kern) {
         const hipError_t e = ensure_dyn_smem(reinterpret_cast<const void *>(kern), smem);
@@ -148,7 +149,8 @@ hipError_t launch_down_rows(const FwdArgs &a, int bits, hipStream_t st) {
     };
     const bool one = a.S == 1;
     if (staged) {
-        if (a.mx) return one ? go(k_down_rows_staged<4, true, true>) : go(k_down_rows_staged<4, false, true>);
+        if (a.mx) return one ? go(k_down_rows_staged<4, true, true, true>) : go(k_down_rows_staged<4, false, true, true>);
+        if (a.group) return one ? go(k_down_rows_staged<4, true, true>) : go(k_down_rows_staged<4, false, true>);
         if (bits == 8) return one ? go(k_down_rows_staged<8, true>) : go(k_down_rows_staged<8, false>);
         if (bits == 4) return one ? go(k_down_rows_staged<4, true>) : go(k_down_rows_staged<4, false>);
         return one ? go(k_down_rows_staged<2, true>) : go(k_down_rows_staged<2, false>);
