@@ -620,3 +620,31 @@ def test_misaligned_pointers_refused(torch):
     assert status(ws) == 0
     o_out, _, _ = oracle.layer(spec, d["x"], d["router_w"], d["bias"], d["blobs"], d["shared"])
     parity(out.cpu().numpy(), o_out)
+
+
+@pytest.mark.parametrize("S", [4, 12])
+def test_repeated_index_across_groups_top10(torch, S):
+    """Top-10 routing: the unit table reads each token's indices in groups of
+    eight, so a repeat within the second group and a repeat across the two
+    groups must both be reported (COLI_EINVAL), by the decode kernels (4
+    tokens) and the grouping kernel of the grouped path (12 tokens); the
+    unmodified indices give the oracle's layer again."""
+    from synth.device import upload_layer
+    spec = dataclasses.replace(synth.TINY, n_experts=32, top_k=10)
+    d = synth.tiny_layer(seed=77, S=S, spec=spec)
+    dims = q().make_dims(spec)
+    dl = upload_layer(d)
+    ws = workspace(dims, S)
+    qm = q()
+    o_out, o_idx, o_w = oracle.layer(spec, d["x"], d["router_w"], d["bias"], d["blobs"], d["shared"])
+    idx = torch.from_numpy(o_idx).cuda()
+    w = torch.from_numpy(o_w).cuda()
+    say(f"repeated top-10 indices, {S} tokens")
+    for k_dup, k_src in ((9, 8), (9, 1), (8, 0)):
+        bad = idx.clone()
+        bad[S - 1, k_dup] = bad[S - 1, k_src]
+        gpu_forward(dims, dl, bad, w, ws)
+        assert status(ws) == qm.COLI_EINVAL, (k_dup, k_src)
+    out = gpu_forward(dims, dl, idx, w, ws)
+    assert status(ws) == 0, qm.coli_moe_last_error()
+    parity(out.cpu().numpy(), o_out)
