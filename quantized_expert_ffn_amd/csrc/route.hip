@@ -72,26 +72,28 @@ __global__ __launch_bounds__(64) void k_router_select(const float *__restrict__ 
 // The fused router launch.  Grid (ceil(E / L) [+ ceil(ceil(H / 2048) / RF_W)
 // with qx], S), RF_W wavefronts per workgroup, L = rf_lpw(S) logits per
 // workgroup.  Wave w < L of workgroup (x < ceil(E / L), t) computes logit
-// (t, L x + w) and publishes it with a device-scope store; once all of its
-// waves have drained their stores, the workgroup counts itself in the
-// token's arrival counter (one atomic per workgroup).  In the workgroup that
-// arrives last, wave 0 selects the token's top-K from the published logits
-// (device-scope loads); for one token it writes the unit table straight from
-// the selection, otherwise the token counts itself done and the last token's
-// workgroup builds the unit table of the batch in LDS.  Each counter is reset
-// by its last arriver, so the next launch starts from zero.  Workgroups past
-// the logits quantise x (one 2048-element slice per wave).
+// (t, L x + w).  Up to four tokens with at most 256 experts (route_one,
+// route_few), each logit is published as a tagged 64-bit slot and one
+// workgroup, which waits (bounded) for every slot, selects and writes the
+// unit table.  Otherwise each logit goes out with a device-scope store and,
+// once all of its waves have drained their stores, the workgroup counts
+// itself in the token's arrival counter (one atomic per workgroup); in the
+// workgroup that arrives last, wave 0 selects the token's top-K from the
+// published logits (device-scope loads), the token counts itself done and
+// the last token's workgroup builds the unit table of the batch in LDS.
+// Each counter is reset by its last arriver, so the next launch starts from
+// zero.  Workgroups past the logits quantise x (one 2048-element slice per
+// wave).
 //
-// For one token the launch spreads its reads over more compute units (two
-// logits per workgroup of four waves).  With sg, the first I / 16
-// workgroups of grid row 0 (ahead of the logits, being the longest) run the
-// shared expert's gate/up for all S tokens in half tiles of 16 rows — its
-// pairs do not depend on the routing — quantising x into their own LDS with
-// the same Q8_0 as the workspace copy, and write h unquantised to hs; the
-// gate/up launch quantises it and skips the shared expert.
+// With sg, the first I / 16 workgroups of grid row 0 (ahead of the logits,
+// being the longest) run the shared expert's gate/up for all S tokens in
+// half tiles of 16 rows — its pairs do not depend on the routing —
+// quantising x into their own LDS with the same Q8_0 as the workspace copy,
+// and write h unquantised to hs; the gate/up launch quantises it and skips
+// the shared expert.
 constexpr int RF_W = 4;
-// logits per workgroup: two for one token, four (one per wave) for more
-__host__ __device__ inline int rf_lpw(int S) { return S == 1 ? 2 : RF_W; }
+// logits per workgroup: one per wave, at every batch size
+__host__ __device__ inline int rf_lpw(int) { return RF_W; }
 
 // Shared expert, gate/up rows 16 half .. 16 half + 15, every token; h to hs.
 template <int BITS, int NT, bool GROUPED, bool MX = false>
