@@ -648,3 +648,31 @@ def test_repeated_index_across_groups_top10(torch, S):
     out = gpu_forward(dims, dl, idx, w, ws)
     assert status(ws) == 0, qm.coli_moe_last_error()
     parity(out.cpu().numpy(), o_out)
+
+
+@pytest.mark.parametrize("S", [1, 2, 3, 4, 5])
+def test_top32_of_256_routing_and_layer(torch, S):
+    """The widest selection the boundary admits (top-32 of 256 experts, the
+    most the one-workgroup selections of one to four tokens rank) through
+    coli_moe_route and coli_moe_layer: indices and weights bitwise equal to
+    the oracle's, the layer output too (five tokens take the per-token
+    arrival path)."""
+    from synth.device import upload_layer
+    spec = dataclasses.replace(synth.TINY, n_experts=256, top_k=32, hidden=256, inter=64)
+    d = synth.tiny_layer(seed=91 + S, S=S, spec=spec)
+    dims = q().make_dims(spec)
+    dl = upload_layer(d)
+    ws = workspace(dims, S)
+    qm = q()
+    o_out, o_idx, o_w = oracle.layer(spec, d["x"], d["router_w"], d["bias"], d["blobs"], d["shared"])
+    say(f"top-32 of 256, {S} tokens")
+    idx, w = gpu_route(dims, dl, ws)
+    assert status(ws) == 0, qm.coli_moe_last_error()
+    assert np.array_equal(idx.cpu().numpy(), o_idx)
+    assert np.array_equal(w.cpu().numpy().view(np.uint32), o_w.view(np.uint32))
+    l_idx, l_w, out = gpu_layer(torch, dims, dl, ws)
+    assert status(ws) == 0, qm.coli_moe_last_error()
+    assert np.array_equal(l_idx, o_idx)
+    assert np.array_equal(l_w.view(np.uint32), o_w.view(np.uint32))
+    parity(out, o_out)
+    assert np.array_equal(out.view(np.uint32), o_out.view(np.uint32))
