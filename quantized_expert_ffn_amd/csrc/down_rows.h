@@ -116,6 +116,10 @@ template <int BITS, bool ONE_TOKEN, bool COHERENT, bool GROUPED = false, bool MX
 struct DownTile {
     static_assert(!MX || (BITS == 4 && GROUPED), "MXFP4 rows are 4-bit codes with a scale per block");
     static constexpr int UB = DownRowsBatch<BITS>::UB;
+    // Staged tiles with per-row scales: units whose weights are in flight
+    // ahead of the block dots.  Fewer loads out at once than the whole batch
+    // keeps the early burst short; three cover the latency of the next.
+    static constexpr int AHEAD = 3;
     const FwdArgs &a;
     uint8_t *smem;
     DownTilePlan D;
@@ -467,12 +471,14 @@ struct DownTile {
     }
 
     // The whole tile when slots_fit() holds and the slots' Q8_0(h) is in LDS
-    // (slots_store, then a workgroup barrier): the weights of every unit go
-    // out at once (unless the caller issued them already: issued) with the
-    // down-row scales right behind them (needed only at the end, so waiting
-    // for them waits for nothing the block dots have not already waited
-    // for), then the block dots, the chains and the combine.
-    __device__ __forceinline__ void run_staged(bool issued) {
+    // (slots_store, then a workgroup barrier).  Grouped and MXFP4 rows: the
+    // weights of every unit go out here at once.  Per-row scales: the caller
+    // has issued units [0, AHEAD), and unit ui + AHEAD goes out once unit
+    // ui's block dots are done.  The down-row scales come right after the
+    // first loads (needed only at the end, so waiting for them waits for
+    // nothing the block dots have not already waited for), then the block
+    // dots, the chains and the combine.
+    __device__ __forceinline__ void run_staged() {
         const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
         const int r0 = rt * DR_ROWS;
         const int8_t *qh_l = reinterpret_cast<const int8_t *>(smem + D.qh);
@@ -509,7 +515,7 @@ struct DownTile {
                 mxv[k] = w < nsw ? gs_word(0, w) : 0u;
             }
         }
-        if (!issued) issue(0, n_units, 0);
+        if constexpr (GROUPED) issue(0, n_units, 0);
         float sd = 0.0f;
         const uint8_t *my_blob = chain ? ublob[ub] : nullptr;
         if (!GROUPED && my_blob) sd = reinterpret_cast<const float *>(my_blob + BL.s_down)[r0 + rl];
@@ -538,6 +544,16 @@ struct DownTile {
                         for (int r = 0; r < DR_RPW; ++r)
                             isum[(r * mpb + q) * ISUM_PITCH + lane] = (act && live) ? block_dot(wv[ui][r], av) : 0;
                     }
+                }
+            }
+            if constexpr (!GROUPED) {
+                // unconditional (a clamped index, no records past n_units),
+                // so that no wait ahead of it covers the loads still in flight
+                const int uj = ui + AHEAD;
+                if (uj < UB) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    issue_unit(uj, uniform_ptr(ublob[min(uj, n_units - 1)]), uj < n_units, 0);
+                    __builtin_amdgcn_sched_barrier(0);
                 }
             }
         }

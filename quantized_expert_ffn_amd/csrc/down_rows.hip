@@ -81,11 +81,12 @@ __global__ __launch_bounds__(DR_T) __attribute__((amdgpu_waves_per_eu(MX ? 2 : 3
 // workspace): the slots' Q8_0(h) is fetched in the same memory round trip as
 // the table (in slot order: its addresses do not depend on the routing).
 // With per-row scales every wave also reads the unit count and the blob
-// pointers through the scalar cache and issues its weights as soon as those
-// are in, before the staged data has arrived (loads complete in issue order,
-// so storing the staged data to LDS then waits for none of the weights);
-// MXFP4 tiles issue theirs from LDS after the staging
-// (DownTile::run_staged).
+// pointers through the scalar cache and issues the weights of its first
+// DownTile::AHEAD units as soon as those are in, before the staged data has
+// arrived (loads complete in issue order, so storing the staged data to LDS
+// then waits for none of the weights); the rest follow one unit at a time
+// behind the block dots.  Grouped and MXFP4 tiles issue theirs from LDS after
+// the staging (DownTile::run_staged).
 template <int BITS, bool ONE_TOKEN, bool GROUPED = false, bool MX = false>
 __global__ __launch_bounds__(DR_T) __attribute__((amdgpu_waves_per_eu(3))) void k_down_rows_staged(const FwdArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -116,7 +117,8 @@ __global__ __launch_bounds__(DR_T) __attribute__((amdgpu_waves_per_eu(3))) void 
             bp[ui] = ld_scalar<const uint8_t *>(a.units + U.ublob + 8 * (size_t)min(ui, U.umax - 1));
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int ui = 0; ui < UB; ++ui) tile.issue_unit(ui, bp[ui], ui < nu, 0);   // past nu: no records
+        for (int ui = 0; ui < (UB < tile.AHEAD ? UB : tile.AHEAD); ++ui)
+            tile.issue_unit(ui, bp[ui], ui < nu, 0);   // past nu: no records
         __builtin_amdgcn_sched_barrier(0);
     }
     if (tid < U.words) tab[tid] = tw;
@@ -130,7 +132,7 @@ __global__ __launch_bounds__(DR_T) __attribute__((amdgpu_waves_per_eu(3))) void 
         lds_barrier();   // orders LDS only: the weights stay in flight
     tile.n_units = uniform(tab[0]);
     if (tid < tile.n_units && ublob[tid] == nullptr) raise_status(a.status, ST_NOTRESIDENT);
-    tile.run_staged(!GROUPED);
+    tile.run_staged();
 }
 
 size_t down_rows_smem(int S, int I, int E, int K, int n_shared, int group, int bits) {
