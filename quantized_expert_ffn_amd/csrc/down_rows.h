@@ -116,9 +116,9 @@ template <int BITS, bool ONE_TOKEN, bool COHERENT, bool GROUPED = false, bool MX
 struct DownTile {
     static_assert(!MX || (BITS == 4 && GROUPED), "MXFP4 rows are 4-bit codes with a scale per block");
     static constexpr int UB = DownRowsBatch<BITS>::UB;
-    // Staged tiles with per-row scales: units whose weights are in flight
-    // ahead of the block dots.  Fewer loads out at once than the whole batch
-    // keeps the early burst short; three cover the latency of the next.
+    // Staged tiles: units whose weights are in flight ahead of the block
+    // dots.  Fewer loads out at once than the whole batch keeps the early
+    // burst short; three cover the latency of the next.
     static constexpr int AHEAD = 3;
     const FwdArgs &a;
     uint8_t *smem;
@@ -471,13 +471,13 @@ struct DownTile {
     }
 
     // The whole tile when slots_fit() holds and the slots' Q8_0(h) is in LDS
-    // (slots_store, then a workgroup barrier).  Grouped and MXFP4 rows: the
-    // weights of every unit go out here at once.  Per-row scales: the caller
-    // has issued units [0, AHEAD), and unit ui + AHEAD goes out once unit
-    // ui's block dots are done.  The down-row scales come right after the
-    // first loads (needed only at the end, so waiting for them waits for
-    // nothing the block dots have not already waited for), then the block
-    // dots, the chains and the combine.
+    // (slots_store, then a workgroup barrier).  The weights of units [0,
+    // AHEAD) go out first (per-row scales: the caller has issued them;
+    // grouped and MXFP4 rows: here, behind the scale words), and unit ui +
+    // AHEAD once unit ui's block dots are done.  The down-row scales come
+    // right after the first loads (needed only at the end, so waiting for
+    // them waits for nothing the block dots have not already waited for),
+    // then the block dots, the chains and the combine.
     __device__ __forceinline__ void run_staged() {
         const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
         const int r0 = rt * DR_ROWS;
@@ -515,7 +515,11 @@ struct DownTile {
                 mxv[k] = w < nsw ? gs_word(0, w) : 0u;
             }
         }
-        if constexpr (GROUPED) issue(0, n_units, 0);
+        if constexpr (GROUPED) {
+#pragma unroll
+            for (int ui = 0; ui < (UB < AHEAD ? UB : AHEAD); ++ui)
+                issue_unit(ui, uniform_ptr(ublob[min(ui, n_units - 1)]), ui < n_units, 0);
+        }
         float sd = 0.0f;
         const uint8_t *my_blob = chain ? ublob[ub] : nullptr;
         if (!GROUPED && my_blob) sd = reinterpret_cast<const float *>(my_blob + BL.s_down)[r0 + rl];
@@ -546,15 +550,13 @@ struct DownTile {
                     }
                 }
             }
-            if constexpr (!GROUPED) {
-                // unconditional (a clamped index, no records past n_units),
-                // so that no wait ahead of it covers the loads still in flight
+            // unconditional (a clamped index, no records past n_units), so
+            // that no wait ahead of it covers the loads still in flight
+            if (ui + AHEAD < UB) {
                 const int uj = ui + AHEAD;
-                if (uj < UB) {
-                    __builtin_amdgcn_sched_barrier(0);
-                    issue_unit(uj, uniform_ptr(ublob[min(uj, n_units - 1)]), uj < n_units, 0);
-                    __builtin_amdgcn_sched_barrier(0);
-                }
+                __builtin_amdgcn_sched_barrier(0);
+                issue_unit(uj, uniform_ptr(ublob[min(uj, n_units - 1)]), uj < n_units, 0);
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
         if (GROUPED) {

@@ -85,8 +85,8 @@ __global__ __launch_bounds__(DR_T) __attribute__((amdgpu_waves_per_eu(MX ? 2 : 3
 // DownTile::AHEAD units as soon as those are in, before the staged data has
 // arrived (loads complete in issue order, so storing the staged data to LDS
 // then waits for none of the weights); the rest follow one unit at a time
-// behind the block dots.  Grouped and MXFP4 tiles issue theirs from LDS after
-// the staging (DownTile::run_staged).
+// behind the block dots.  Grouped and MXFP4 tiles issue theirs the same way
+// from LDS after the staging (DownTile::run_staged).
 template <int BITS, bool ONE_TOKEN, bool GROUPED = false, bool MX = false>
 __global__ __launch_bounds__(DR_T) __attribute__((amdgpu_waves_per_eu(3))) void k_down_rows_staged(const FwdArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
