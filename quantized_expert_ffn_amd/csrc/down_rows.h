@@ -118,8 +118,9 @@ struct DownTile {
     static constexpr int UB = DownRowsBatch<BITS>::UB;
     // Staged tiles: units whose weights are in flight ahead of the block
     // dots.  Fewer loads out at once than the whole batch keeps the early
-    // burst short; three cover the latency of the next.
-    static constexpr int AHEAD = 3;
+    // burst short; three cover the latency of the next (two for MXFP4 rows,
+    // whose block dots take longer).
+    static constexpr int AHEAD = MX ? 2 : 3;
     const FwdArgs &a;
     uint8_t *smem;
     DownTilePlan D;
