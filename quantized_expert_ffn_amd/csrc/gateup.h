@@ -281,12 +281,13 @@ __device__ __forceinline__ void gateup_unit_primed(const uint8_t *blob, int H, i
 // of NCH = (H / 32 + 63) / 64 <= 4 chunks, for np <= NT vectors x[v * H ..]
 // (binary32, not yet quantised).  The memory operations go out in this
 // order: each thread's 32-value blocks of x (block j = tid + 256 k of the
-// np * H / 32, at most NT per thread), the row scale, then every chunk of
-// the wave's 8 rows — one memory round trip for the whole half tile.  Q8_0
-// of the blocks (q8_0_words_of, as the quantisation of x everywhere else)
-// then waits for x alone and goes to LDS behind a barrier that orders LDS
-// only, and the chunks are reduced in order as they arrive.  Results as
-// gateup_half_f32.
+// np * H / 32, at most NT per thread), the row scale, then the first chunk
+// of the wave's 8 rows.  Q8_0 of the blocks (q8_0_words_of, as the
+// quantisation of x everywhere else) then waits for x alone and goes to LDS
+// behind a barrier that orders LDS only, and the chunks are reduced in
+// order, each one's successor requested as soon as it is reduced: one chunk
+// in flight per wave keeps these tiles' loads from crowding out the router
+// rows that run beside them.  Results as gateup_half_f32.
 template <int BITS, int NT, int NCH>
 __device__ __forceinline__ void gateup_half_primed(const uint8_t *blob, int H, int I, int i0, int np, uint8_t *smem,
                                                    const SmemPlan &L, const float *__restrict__ x,
@@ -320,16 +321,13 @@ __device__ __forceinline__ void gateup_half_primed(const uint8_t *blob, int H, i
             for (int i = 0; i < 8; ++i) xr[k][i] = src[i];
         }
     }
-    // 2. the row scale, 3. every chunk, in order
+    // 2. the row scale, 3. the first chunk
     __builtin_amdgcn_sched_barrier(0);
     const uint32_t soff = (uint32_t)((wave < 2 ? BL.s_gate : BL.s_up) + 4 * (size_t)(r0 + crow));
     const float rs = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsrc, soff, 0, 0));
     BlockBits<BITS> X[NCH][RPW];
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-        issue_chunk<BITS, RPW>(rsrc, rowoff, c, X[c]);
-        __builtin_amdgcn_sched_barrier(0);   // chunks in order
-    }
+    issue_chunk<BITS, RPW>(rsrc, rowoff, 0, X[0]);
+    __builtin_amdgcn_sched_barrier(0);
     // 4. Q8_0(x) into LDS
 #pragma unroll
     for (int k = 0; k < NT; ++k) {
@@ -347,7 +345,14 @@ __device__ __forceinline__ void gateup_half_primed(const uint8_t *blob, int H, i
     lds_barrier();
     float acc = 0.0f;
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) acc = reduce_chunk<BITS, NT, RPW>(X[c], c, nb, np, vq, vd, vds, H, isum_wave, acc);
+    for (int c = 0; c < NCH; ++c) {
+        acc = reduce_chunk<BITS, NT, RPW>(X[c], c, nb, np, vq, vd, vds, H, isum_wave, acc);
+        if (c + 1 < NCH) {
+            __builtin_amdgcn_sched_barrier(0);
+            issue_chunk<BITS, RPW>(rsrc, rowoff, c + 1, X[c + 1]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
     // gu[v * 32 + k]: gate rows (k < 16) then up rows of vector v
     if (cvec < np) gu[cvec * 32 + wave * RPW + crow] = acc * rs;
     __syncthreads();
