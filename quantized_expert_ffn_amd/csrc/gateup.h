@@ -210,7 +210,9 @@ __device__ __forceinline__ void gateup_unit_primed(const uint8_t *blob, int H, i
     // 2. the wave's rows' scales: the row scale of this lane's chain row, or
     //    (GROUPED) every scale of the wave's 16 rows, PRIMED_GW words per
     //    lane, all issued (words past the rows read bytes that are not used),
-    //    3. chunks 0 and 1
+    //    3. chunk 0, and chunk 1 with per-row scales (grouped and MXFP4 rows,
+    //    whose block sums take longer, request chunk 1 once chunk 0 is
+    //    reduced: fewer loads out at once)
     const size_t ssec = wave < 2 ? BL.s_gate : BL.s_up;
     const int rb = GROUPED ? primed_scale_row_bytes(H, group, MX) : 0;
     __builtin_amdgcn_sched_barrier(0);
@@ -229,7 +231,7 @@ __device__ __forceinline__ void gateup_unit_primed(const uint8_t *blob, int H, i
     BlockBits<BITS> A[RPW], B[RPW];
     issue_chunk<BITS, RPW>(rsrc, rowoff, 0, A);
     __builtin_amdgcn_sched_barrier(0);   // chunk 0's loads ahead of chunk 1's
-    issue_chunk<BITS, RPW>(rsrc, rowoff, 1, B);
+    if constexpr (!GROUPED) issue_chunk<BITS, RPW>(rsrc, rowoff, 1, B);
     __builtin_amdgcn_sched_barrier(0);
     stage_store(xq, 0, np * w16, [&](int i) {
         const int it = fast_div(i, mw);
@@ -254,6 +256,8 @@ __device__ __forceinline__ void gateup_unit_primed(const uint8_t *blob, int H, i
 #pragma unroll
     for (int c = 0; c < NCH; c += 2) {
         acc = reduce_chunk<BITS, NT, RPW, GROUPED, MX>(A, c, nb, np, vq, vd, vds, H, isum_wave, acc, gs, lgb);
+        __builtin_amdgcn_sched_barrier(0);
+        if (GROUPED && c == 0 && NCH > 1) issue_chunk<BITS, RPW>(rsrc, rowoff, 1, B);
         __builtin_amdgcn_sched_barrier(0);
         if (c + 2 < NCH) issue_chunk<BITS, RPW>(rsrc, rowoff, c + 2, A);
         __builtin_amdgcn_sched_barrier(0);
