@@ -121,6 +121,10 @@ struct DownTile {
     // burst short; three cover the latency of the next (two for MXFP4 rows,
     // whose block dots take longer).
     static constexpr int AHEAD = MX ? 2 : 3;
+    // Batched tiles with per-row scales (batch()): units of a batch whose
+    // weights go out with its staged data; the rest follow one at a time
+    // behind the block dots.
+    static constexpr int BATCH_AHEAD = UB < 2 ? UB : 2;
     const FwdArgs &a;
     uint8_t *smem;
     DownTilePlan D;
@@ -363,7 +367,15 @@ struct DownTile {
         for (int c = 0; c < (ONE ? 1 : nch); ++c) {
             const int b = c * 64 + lane;
             const bool act = b < nbi;
-            if (!(ONE && issued)) issue(u0, u1, c);
+            if (!(ONE && issued)) {
+                if constexpr (GROUPED) {
+                    issue(u0, u1, c);
+                } else {
+#pragma unroll
+                    for (int ui = 0; ui < BATCH_AHEAD; ++ui)
+                        issue_unit(ui, uniform_ptr(ublob[min(u0 + ui, n_units - 1)]), u0 + ui < u1, c);
+                }
+            }
             if (c == 0) {
                 // the staged data are in once no more than the weight loads
                 // issued after them are outstanding
@@ -371,7 +383,7 @@ struct DownTile {
                 if (ONE && issued)
                     wait_vm<0>();
                 else
-                    wait_vm<UB * DR_RPW * BlockLoads<BITS>::N>();
+                    wait_vm<(GROUPED ? UB : BATCH_AHEAD) * DR_RPW * BlockLoads<BITS>::N>();
                 stage_store(qv, 0, nq, q_dst);
                 stage_store(dv, 0, nd, d_dst);
                 stage_store(sv, 0, ns, s_dst);
@@ -410,6 +422,16 @@ struct DownTile {
                                 isum[(r * mpb + (q - pbase)) * ISUM_PITCH + lane] =
                                     (act && live) ? block_dot(wv[ui][r], av) : 0;
                         }
+                    }
+                }
+                // unconditional within the batch (no records past u1), so
+                // that no wait ahead of it covers the loads still in flight
+                if constexpr (!GROUPED) {
+                    if (!(ONE && issued) && ui + BATCH_AHEAD < UB) {
+                        const int uj = ui + BATCH_AHEAD;
+                        __builtin_amdgcn_sched_barrier(0);
+                        issue_unit(uj, uniform_ptr(ublob[min(u0 + uj, n_units - 1)]), u0 + uj < u1, c);
+                        __builtin_amdgcn_sched_barrier(0);
                     }
                 }
             }
